@@ -1,0 +1,231 @@
+/* fp64 CPU oracle for the RVQ-LUT MoE expert forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this library.  It shares no
+ * code, header, table or helper with the GPU path.
+ *
+ * It computes the plain definitions, slowly and in double precision:
+ *  - RVQ decode: a weight sub-vector of 8 consecutive columns of one row is
+ *    the sum of three code vectors, one from each of three 256-entry stage
+ *    codebooks, chosen by that group's three code bytes (stage-minor).
+ *    (WASTE Inference Engine: Running Kimi K3 2.78T on Consumer Hardware,
+ *    section "Residual Vector Quantization (RVQ)"; news.hada.io topic 32035,
+ *    section on quantization and accuracy: 3 stages x 256 entries x 8 dims.)
+ *  - Expert output: y = W x with W rebuilt element by element (never the
+ *    table form), then down(silu(gate x) * (up x)).
+ *  - Partial-dot tables (for checking only): T[g][s][c] = C_s[c] . x[8g:8g+8],
+ *    the per-codebook, per-position tables of "Running a 2.78-Trillion-
+ *    Parameter Model on a Laptop: Inside WASTE's NVMe-Streaming Engine",
+ *    section "Technical Insight".
+ *  - Router: logits = W_r x with bf16 weights widened exactly; top-k by
+ *    (logit descending, expert id ascending); gates = softmax over the k
+ *    selected logits (news.hada.io topic 32035, read-ahead section: 16
+ *    experts per layer).
+ *  - RMSNorm: h / sqrt(mean(h^2) + eps), unit weight.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- threads */
+typedef void (*range_fn)(void *ctx, int64_t lo, int64_t hi);
+typedef struct { range_fn fn; void *ctx; int64_t lo, hi; } range_job;
+
+static void *range_worker(void *arg) {
+  range_job *j = (range_job *)arg;
+  j->fn(j->ctx, j->lo, j->hi);
+  return 0;
+}
+
+static void parallel_for(int64_t n, int threads, range_fn fn, void *ctx) {
+  if (threads < 1) threads = 1;
+  if (threads > 128) threads = 128;
+  if (threads == 1 || n < 2) { fn(ctx, 0, n); return; }
+  pthread_t th[128];
+  range_job jobs[128];
+  int64_t per = (n + threads - 1) / threads;
+  int used = 0;
+  for (int t = 0; t < threads; ++t) {
+    int64_t lo = t * per, hi = lo + per;
+    if (lo >= n) break;
+    if (hi > n) hi = n;
+    jobs[t].fn = fn; jobs[t].ctx = ctx; jobs[t].lo = lo; jobs[t].hi = hi;
+    pthread_create(&th[t], 0, range_worker, &jobs[t]);
+    ++used;
+  }
+  for (int t = 0; t < used; ++t) pthread_join(th[t], 0);
+}
+
+/* ---------------------------------------------------------------- RVQ decode */
+/* One row of W, rebuilt in double: W[r][8g+j] = C0[c0][j] + C1[c1][j] + C2[c2][j]. */
+static void decode_row(const uint8_t *codes, const float *cb, int64_t cols, int64_t r, double *w) {
+  int64_t groups = cols / 8;
+  const uint8_t *row = codes + r * groups * 3;
+  for (int64_t g = 0; g < groups; ++g) {
+    const float *v0 = cb + (0 * 256 + row[3 * g + 0]) * 8;
+    const float *v1 = cb + (1 * 256 + row[3 * g + 1]) * 8;
+    const float *v2 = cb + (2 * 256 + row[3 * g + 2]) * 8;
+    for (int j = 0; j < 8; ++j) w[8 * g + j] = (double)v0[j] + (double)v1[j] + (double)v2[j];
+  }
+}
+
+void orc_dequant(const uint8_t *codes, const float *cb, int64_t rows, int64_t cols, double *W) {
+  for (int64_t r = 0; r < rows; ++r) decode_row(codes, cb, cols, r, W + r * cols);
+}
+
+/* ---------------------------------------------------------------- matvec */
+typedef struct {
+  const uint8_t *codes; const float *cb; int64_t rows, cols;
+  const double *X; int64_t ntok;            /* X[t][cols] */
+  const int64_t *rowsel;                    /* NULL = all rows */
+  double *Y;                                /* Y[t][nrows_out] */
+  int64_t nout;
+} gemv_ctx;
+
+static void gemv_range(void *vctx, int64_t lo, int64_t hi) {
+  gemv_ctx *c = (gemv_ctx *)vctx;
+  double *w = (double *)malloc(sizeof(double) * c->cols);
+  for (int64_t i = lo; i < hi; ++i) {
+    int64_t r = c->rowsel ? c->rowsel[i] : i;
+    decode_row(c->codes, c->cb, c->cols, r, w);
+    for (int64_t t = 0; t < c->ntok; ++t) {
+      const double *x = c->X + t * c->cols;
+      double acc = 0.0;
+      for (int64_t k = 0; k < c->cols; ++k) acc += w[k] * x[k];
+      c->Y[t * c->nout + i] = acc;
+    }
+  }
+  free(w);
+}
+
+/* Y[t][i] = sum_k W[row_i][k] X[t][k] for the selected rows (all rows if rowsel == NULL). */
+void orc_gemv_batch(const uint8_t *codes, const float *cb, int64_t rows, int64_t cols,
+                    const double *X, int64_t ntok, const int64_t *rowsel, int64_t nsel,
+                    double *Y, int threads) {
+  gemv_ctx c = {codes, cb, rows, cols, X, ntok, rowsel, Y, rowsel ? nsel : rows};
+  parallel_for(c.nout, threads, gemv_range, &c);
+}
+
+void orc_gemv(const uint8_t *codes, const float *cb, int64_t rows, int64_t cols, const double *x,
+              const int64_t *rowsel, int64_t nsel, double *y, int threads) {
+  orc_gemv_batch(codes, cb, rows, cols, x, 1, rowsel, nsel, y, threads);
+}
+
+/* ---------------------------------------------------------------- partial-dot tables */
+/* T[g][s][c] = sum_j C_s[c][j] * x[8g+j]  (groups = cols/8). */
+void orc_lut(const float *cb, const double *x, int64_t cols, double *T) {
+  int64_t groups = cols / 8;
+  for (int64_t g = 0; g < groups; ++g)
+    for (int s = 0; s < 3; ++s)
+      for (int c = 0; c < 256; ++c) {
+        double acc = 0.0;
+        for (int j = 0; j < 8; ++j) acc += (double)cb[(s * 256 + c) * 8 + j] * x[8 * g + j];
+        T[(g * 3 + s) * 256 + c] = acc;
+      }
+}
+
+/* The table form of the same product: y[r] = sum_g sum_s T[g][s][codes[r][g][s]]. */
+void orc_gemv_via_lut(const uint8_t *codes, const double *T, int64_t rows, int64_t cols, double *y) {
+  int64_t groups = cols / 8;
+  for (int64_t r = 0; r < rows; ++r) {
+    double acc = 0.0;
+    for (int64_t g = 0; g < groups; ++g)
+      for (int s = 0; s < 3; ++s) acc += T[(g * 3 + s) * 256 + codes[(r * groups + g) * 3 + s]];
+    y[r] = acc;
+  }
+}
+
+/* ---------------------------------------------------------------- SwiGLU expert */
+double orc_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Y[t] = down( silu(gate X[t]) * (up X[t]) ) for ntok tokens; output rows of down
+ * restricted to rowsel if given.  gate/up are [inter x hidden], down is [hidden x inter]. */
+void orc_expert_batch(const uint8_t *gate_codes, const float *gate_cb,
+                      const uint8_t *up_codes, const float *up_cb,
+                      const uint8_t *down_codes, const float *down_cb,
+                      int64_t hidden, int64_t inter, const double *X, int64_t ntok,
+                      const int64_t *rowsel, int64_t nsel, double *Y, int threads) {
+  double *g = (double *)malloc(sizeof(double) * ntok * inter);
+  double *u = (double *)malloc(sizeof(double) * ntok * inter);
+  orc_gemv_batch(gate_codes, gate_cb, inter, hidden, X, ntok, 0, 0, g, threads);
+  orc_gemv_batch(up_codes, up_cb, inter, hidden, X, ntok, 0, 0, u, threads);
+  for (int64_t i = 0; i < ntok * inter; ++i) g[i] = orc_silu(g[i]) * u[i];
+  orc_gemv_batch(down_codes, down_cb, hidden, inter, g, ntok, rowsel, nsel, Y, threads);
+  free(g);
+  free(u);
+}
+
+/* ---------------------------------------------------------------- router */
+static double bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+typedef struct { const uint16_t *w; const double *X; int64_t ntok, E, H; double *L; } router_ctx;
+
+static void router_range(void *vctx, int64_t lo, int64_t hi) {
+  router_ctx *c = (router_ctx *)vctx;
+  for (int64_t e = lo; e < hi; ++e)
+    for (int64_t t = 0; t < c->ntok; ++t) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < c->H; ++k) acc += bf16_to_double(c->w[e * c->H + k]) * c->X[t * c->H + k];
+      c->L[t * c->E + e] = acc;
+    }
+}
+
+/* L[t][e] = sum_k Wr[e][k] X[t][k], Wr given as bf16 bit patterns. */
+void orc_router_logits(const uint16_t *w_bf16, const double *X, int64_t ntok, int64_t E, int64_t H,
+                       double *L, int threads) {
+  router_ctx c = {w_bf16, X, ntok, E, H, L};
+  parallel_for(E, threads, router_range, &c);
+}
+
+/* Selection by sorting the whole list with the key (logit descending, id ascending),
+ * then keeping the first k.  gates = exp(l - l_max) / sum over the k kept.
+ * gap_out[0] = l[k-th] - l[(k+1)-th] (inf if k == E); gap_out[1] = smallest
+ * difference between consecutive kept logits (inf if k == 1). */
+static const double *g_sort_logits;
+static int cmp_rank(const void *a, const void *b) {
+  int32_t i = *(const int32_t *)a, j = *(const int32_t *)b;
+  double li = g_sort_logits[i], lj = g_sort_logits[j];
+  if (li > lj) return -1;
+  if (li < lj) return 1;
+  return (i < j) ? -1 : (i > j);
+}
+
+void orc_topk(const double *logits, int64_t E, int64_t k, int32_t *ids, double *gates, double *gap_out) {
+  int32_t *order = (int32_t *)malloc(sizeof(int32_t) * E);
+  for (int64_t e = 0; e < E; ++e) order[e] = (int32_t)e;
+  g_sort_logits = logits;
+  qsort(order, (size_t)E, sizeof(int32_t), cmp_rank);
+  double m = logits[order[0]];
+  double z = 0.0;
+  for (int64_t i = 0; i < k; ++i) {
+    ids[i] = order[i];
+    gates[i] = exp(logits[order[i]] - m);
+    z += gates[i];
+  }
+  for (int64_t i = 0; i < k; ++i) gates[i] /= z;
+  if (gap_out) {
+    gap_out[0] = (k < E) ? logits[order[k - 1]] - logits[order[k]] : INFINITY;
+    double mg = INFINITY;
+    for (int64_t i = 1; i < k; ++i) {
+      double d = logits[order[i - 1]] - logits[order[i]];
+      if (d < mg) mg = d;
+    }
+    gap_out[1] = mg;
+  }
+  free(order);
+}
+
+/* ---------------------------------------------------------------- RMSNorm */
+void orc_rmsnorm(const double *h, int64_t H, double eps, double *out) {
+  double ss = 0.0;
+  for (int64_t k = 0; k < H; ++k) ss += h[k] * h[k];
+  double inv = 1.0 / sqrt(ss / (double)H + eps);
+  for (int64_t k = 0; k < H; ++k) out[k] = h[k] * inv;
+}

@@ -1,0 +1,317 @@
+"""Pins for the fp64 oracle: each test ties an oracle function to something
+other than itself (page-printed constants, closed forms, an independent
+encoding, a library routine, brute force, or an invariant), chosen so that a
+plausible slip (dropped stage, swapped stage order, transposed group layout,
+wrong sign, wrong tie order) fails at least one of them.
+
+Pinned functions and what pins them:
+  dequant / gemv   : page constants (3 B per 8 weights), binary-digit encoding
+                     (exact integers), stage-0-only dense reduction to numpy
+                     matmul, linearity, power-of-two scaling, relabelling
+  lut / via_lut    : closed form on digit codebooks (T_s[c] = 16c, 4c, c),
+                     brute force over all 256^3 triples, exact equality with
+                     gemv on small integers
+  expert           : torch fp64 dense SwiGLU on independently built weights,
+                     zero input, k=1 mixing
+  router / topk    : numpy matmul on widened bf16, lexsort order, scipy softmax
+                     (k = E), gate = 1 at k = 1, exact ties -> lower id
+  rmsnorm          : torch rms_norm, closed-form RMS of the output
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")
+
+
+def _digit_codebooks():
+    """Stage s codebook entry c = weight_s * (bit j of c) for j = 0..7, weights (16, 4, 1)."""
+    bits = ((np.arange(256)[:, None] >> np.arange(8)[None, :]) & 1).astype(np.float32)
+    return np.stack([16.0 * bits, 4.0 * bits, 1.0 * bits]).astype(np.float32)
+
+
+def _digit_encode(W):
+    """Encode W (entries 16a+4b+c, a,b,c in {0,1}) into codes [rows, cols/8, 3]: stage s's
+    code for a group is the 8-bit pattern of that digit across the group's 8 columns."""
+    rows, cols = W.shape
+    Wi = W.astype(np.int64)
+    digits = [(Wi >> 4) & 1, (Wi >> 2) & 1, Wi & 1]
+    assert np.array_equal(16 * digits[0] + 4 * digits[1] + digits[2], Wi)
+    codes = np.zeros((rows, cols // 8, 3), dtype=np.uint8)
+    for s in range(3):
+        d = digits[s].reshape(rows, cols // 8, 8)
+        codes[:, :, s] = (d << np.arange(8)[None, None, :]).sum(axis=2).astype(np.uint8)
+    return codes
+
+
+def _digit_matrix(rng, rows, cols):
+    vals = np.array([16 * a + 4 * b + c for a in (0, 1) for b in (0, 1) for c in (0, 1)])
+    return vals[rng.integers(0, 8, size=(rows, cols))].astype(np.float64)
+
+
+# ---------------------------------------------------------------- format (page constants)
+
+def test_page_constants_and_code_bytes():
+    g = json.load(open(GOLDEN))
+    stages, entries, dim = g["stages"]["value"], g["codebook_entries"]["value"], g["subvector_dim"]["value"]
+    assert (stages, entries, dim) == (3, 256, 8)
+    # one code byte per stage per 8-weight group, each byte indexing a 256-entry codebook
+    assert 2 ** 8 == entries
+    bpw = stages * 8 / dim
+    assert bpw == g["bits_per_weight"]["value"]
+    for rows, cols in [(256, 512), (2048, 7168), (7168, 2048)]:
+        codes = synth.matrix_codes(1, 0, 0, synth.SINGLE, rows, cols)
+        assert codes.dtype == np.uint8 and codes.shape == (rows, cols // dim, stages)
+        assert codes.nbytes * 8 / (rows * cols) == bpw
+    ex = synth.Expert(synth.SEED_EXPERT, 0, 0, 7168, 2048)
+    assert ex.record_bytes().nbytes == 16_515_072
+    assert 256 * 16_515_072 == 4_227_858_432
+    assert 92 * 64 * 16_515_072 == 97_240_743_936
+    assert g["table_reads_per_row_group"]["value"] == stages
+    assert g["additions_per_row_group"]["value"] == stages - 1
+
+
+# ---------------------------------------------------------------- decode + matvec
+
+def test_digit_encoding_decodes_exactly():
+    rng = np.random.default_rng(1)
+    rows, cols = 37, 64
+    W = _digit_matrix(rng, rows, cols)
+    codes = _digit_encode(W)
+    cb = _digit_codebooks()
+    assert np.array_equal(oracle.dequant(codes, cb, rows, cols), W)
+    x = rng.integers(-3, 4, size=cols).astype(np.float64)
+    assert np.array_equal(oracle.gemv(codes, cb, rows, cols, x), W @ x)
+    xr = rng.standard_normal(cols)
+    np.testing.assert_allclose(oracle.gemv(codes, cb, rows, cols, xr), W @ xr, rtol=1e-13, atol=1e-12)
+
+
+def test_stage0_only_reduces_to_dense_matmul():
+    rng = np.random.default_rng(2)
+    rows, cols = 20, 48
+    # dense W whose 8-vectors come from a pool of 256 distinct vectors
+    pool = rng.standard_normal((256, 8)).astype(np.float32)
+    pick = rng.integers(0, 256, size=(rows, cols // 8))
+    W = pool[pick].reshape(rows, cols).astype(np.float64)
+    cb = np.zeros((3, 256, 8), dtype=np.float32)
+    cb[0] = pool
+    codes = np.zeros((rows, cols // 8, 3), dtype=np.uint8)
+    codes[:, :, 0] = pick
+    codes[:, :, 1:] = rng.integers(0, 256, size=(rows, cols // 8, 2))  # indexes zero vectors
+    x = rng.standard_normal(cols)
+    np.testing.assert_allclose(oracle.gemv(codes, cb, rows, cols, x), W @ x, rtol=1e-13, atol=1e-13)
+
+
+def test_linearity_and_power_of_two_scaling():
+    codes = synth.matrix_codes(5, 0, 0, synth.SINGLE, 64, 256)
+    cb = synth.matrix_codebooks(5, 0, 0, synth.SINGLE)
+    x1 = synth.activation_f32(5, 1, 256).astype(np.float64)
+    x2 = synth.activation_f32(5, 2, 256).astype(np.float64)
+    y = oracle.gemv(codes, cb, 64, 256, 0.75 * x1 - 2.5 * x2)
+    y1, y2 = oracle.gemv(codes, cb, 64, 256, x1), oracle.gemv(codes, cb, 64, 256, x2)
+    np.testing.assert_allclose(y, 0.75 * y1 - 2.5 * y2, rtol=1e-12, atol=1e-12)
+    ys = oracle.gemv(codes, (cb * np.float32(8.0)).astype(np.float32), 64, 256, x1)
+    assert np.array_equal(ys, 8.0 * y1)
+
+
+def test_codebook_relabelling_invariance():
+    rng = np.random.default_rng(3)
+    codes = synth.matrix_codes(6, 0, 0, synth.SINGLE, 32, 128)
+    cb = synth.matrix_codebooks(6, 0, 0, synth.SINGLE)
+    x = synth.activation_f32(6, 0, 128)
+    cb2 = np.empty_like(cb)
+    codes2 = np.empty_like(codes)
+    for s in range(3):
+        perm = rng.permutation(256)          # new entry i holds old entry perm[i]
+        inv = np.argsort(perm)               # old code c -> new code inv[c]
+        cb2[s] = cb[s][perm]
+        codes2[:, :, s] = inv[codes[:, :, s]]
+    assert np.array_equal(oracle.gemv(codes2, cb2, 32, 128, x), oracle.gemv(codes, cb, 32, 128, x))
+
+
+def test_row_selection_matches_full():
+    codes = synth.matrix_codes(7, 0, 0, synth.SINGLE, 100, 80)
+    cb = synth.matrix_codebooks(7, 0, 0, synth.SINGLE)
+    x = synth.activation_f32(7, 0, 80)
+    full = oracle.gemv(codes, cb, 100, 80, x)
+    sel = np.array([99, 0, 17, 17, 50])
+    assert np.array_equal(oracle.gemv(codes, cb, 100, 80, x, rowsel=sel), full[sel])
+
+
+# ---------------------------------------------------------------- partial-dot tables
+
+def test_lut_closed_form_on_digit_codebooks():
+    cb = _digit_codebooks()
+    x = np.tile(2.0 ** np.arange(8), 3)          # every group sees (1, 2, 4, ..., 128)
+    T = oracle.lut(cb, x)
+    c = np.arange(256, dtype=np.float64)
+    for g in range(3):
+        assert np.array_equal(T[g, 0], 16 * c)
+        assert np.array_equal(T[g, 1], 4 * c)
+        assert np.array_equal(T[g, 2], c)
+
+
+def test_lut_brute_force_all_code_triples():
+    cb = synth.matrix_codebooks(8, 0, 0, synth.SINGLE).astype(np.float64)
+    xg = synth.activation_f32(8, 0, 8).astype(np.float64)
+    T = oracle.lut(cb.astype(np.float32), xg)[0]            # [3, 256]
+    table_sum = T[0][:, None, None] + T[1][None, :, None] + T[2][None, None, :]
+    # decoded sub-vector for every (c0, c1, c2), then its dot with x_g
+    d0, d1, d2 = cb[0] @ xg, cb[1] @ xg, cb[2] @ xg
+    assert np.abs(T[0] - d0).max() < 1e-14 * 8
+    dense = np.einsum("abcj,j->abc", cb[0][:, None, None, :] + cb[1][None, :, None, :]
+                      + cb[2][None, None, :, :], xg, optimize=True)
+    assert np.abs(table_sum - dense).max() <= 1e-13 * np.abs(dense).max()
+    del d1, d2
+
+
+def test_lut_form_equals_decode_exactly_on_small_integers():
+    rng = np.random.default_rng(4)
+    rows, cols = 50, 96
+    cb = rng.integers(-4, 5, size=(3, 256, 8)).astype(np.float32)
+    codes = rng.integers(0, 256, size=(rows, cols // 8, 3)).astype(np.uint8)
+    x = rng.integers(-3, 4, size=cols).astype(np.float64)
+    y_dec = oracle.gemv(codes, cb, rows, cols, x)
+    y_lut = oracle.gemv_via_lut(codes, oracle.lut(cb, x), rows, cols)
+    assert np.array_equal(y_dec, y_lut)
+    W = oracle.dequant(codes, cb, rows, cols)
+    assert np.array_equal(W @ x, y_dec)
+
+
+def test_lut_form_equals_decode_on_random_data():
+    codes = synth.matrix_codes(synth.SEED_MATVEC, 0, 0, synth.SINGLE, 256, 512)
+    cb = synth.matrix_codebooks(synth.SEED_MATVEC, 0, 0, synth.SINGLE)
+    x = synth.activation_f32(synth.SEED_MATVEC, 0, 512)
+    y_dec = oracle.gemv(codes, cb, 256, 512, x)
+    y_lut = oracle.gemv_via_lut(codes, oracle.lut(cb, x), 256, 512)
+    assert np.linalg.norm(y_dec - y_lut) <= 1e-12 * np.linalg.norm(y_dec)
+
+
+# ---------------------------------------------------------------- SwiGLU expert
+
+def _digit_expert(rng, H, I):
+    Wg, Wu, Wd = _digit_matrix(rng, I, H), _digit_matrix(rng, I, H), _digit_matrix(rng, H, I)
+    # centre the weights so activations stay moderate: subtract via codebooks is not possible,
+    # so scale x instead (the expert is linear in each matrix)
+    cb = _digit_codebooks()
+    ex = {"hidden": H, "inter": I, "gate": (_digit_encode(Wg), cb), "up": (_digit_encode(Wu), cb),
+          "down": (_digit_encode(Wd), cb)}
+    return ex, Wg, Wu, Wd
+
+
+def test_expert_matches_dense_torch_swiglu():
+    rng = np.random.default_rng(5)
+    H, I = 64, 40
+    ex, Wg, Wu, Wd = _digit_expert(rng, H, I)
+    x = rng.standard_normal(H) * 0.01
+    y = oracle.expert(ex, x)
+    xt = torch.tensor(x, dtype=torch.float64)
+    ref = torch.tensor(Wd) @ (torch.nn.functional.silu(torch.tensor(Wg) @ xt) * (torch.tensor(Wu) @ xt))
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(oracle.expert(ex, np.zeros(H)), np.zeros(H))
+    sel = np.array([3, 63, 0])
+    np.testing.assert_allclose(oracle.expert(ex, x, rowsel=sel), y[sel], rtol=0, atol=0)
+
+
+def test_silu_special_values():
+    assert oracle.silu(0.0) == 0.0
+    for z in (-30.0, -2.5, -1e-3, 0.5, 3.0, 40.0):
+        assert abs(oracle.silu(z) - z * scipy.special.expit(z)) <= 1e-15 * max(1.0, abs(z))
+    assert abs(oracle.silu(60.0) / 60.0 - 1.0) < 1e-20 + 1e-15
+    assert abs(oracle.silu(-60.0)) < 1e-20
+    # odd-even identity of z*sigmoid(z): silu(z) - silu(-z) = z
+    for z in (0.3, 1.7, 9.0):
+        assert abs(oracle.silu(z) - oracle.silu(-z) - z) < 1e-14 * max(1.0, z)
+
+
+# ---------------------------------------------------------------- router
+
+def test_router_logits_match_numpy_on_widened_bf16():
+    bits = synth.router_bf16_bits(synth.SEED_LAYER, 0, 64, 512)
+    X = np.stack([synth.activation_f32(synth.SEED_LAYER, t, 512) for t in range(3)]).astype(np.float64)
+    L = oracle.router_logits(bits, X)
+    Wf = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    np.testing.assert_allclose(L, X @ Wf.T, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("E,k", [(256, 16), (64, 16), (16, 16), (10, 1), (300, 7)])
+def test_topk_invariants(E, k):
+    rng = np.random.default_rng(E * 31 + k)
+    logits = rng.standard_normal(E) * 1.7
+    ids, gates, gaps = oracle.topk(logits, k)
+    assert len(set(ids.tolist())) == k and ids.min() >= 0 and ids.max() < E
+    order = np.lexsort((np.arange(E), -logits))
+    assert np.array_equal(ids, order[:k])
+    if k < E:
+        assert logits[ids].min() >= np.delete(logits, ids).max()
+        assert gaps[0] == logits[order[k - 1]] - logits[order[k]]
+    assert (gates > 0).all() and abs(gates.sum() - 1.0) < 1e-12
+    assert (np.diff(gates) <= 0).all()
+    np.testing.assert_allclose(gates, scipy.special.softmax(logits[ids]), rtol=1e-13)
+    if k == E:
+        np.testing.assert_allclose(gates, scipy.special.softmax(logits)[ids], rtol=1e-13)
+    if k == 1:
+        assert gates[0] == 1.0
+
+
+def test_topk_exact_ties_prefer_lower_id():
+    logits = np.array([0.5, 2.0, 1.0, 2.0, 1.0, 1.0, -3.0, 2.0])
+    ids, gates, gaps = oracle.topk(logits, 5)
+    assert ids.tolist() == [1, 3, 7, 2, 4]
+    assert gates[0] == gates[1] == gates[2] and gates[3] == gates[4]
+    assert gaps == (0.0, 0.0)
+
+
+def test_topk_softmax_renormalisation_equals_softmax_then_renormalise():
+    rng = np.random.default_rng(9)
+    logits = rng.standard_normal(256) * 1.7
+    ids, gates, _ = oracle.topk(logits, 16)
+    p = scipy.special.softmax(logits)
+    np.testing.assert_allclose(gates, p[ids] / p[ids].sum(), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- MoE composition
+
+def _small_expert(seed, e, H, I):
+    ex = synth.Expert(seed, 0, e, H, I)
+    return {"hidden": H, "inter": I, "gate": (ex.codes(synth.GATE), ex.codebooks(synth.GATE)),
+            "up": (ex.codes(synth.UP), ex.codebooks(synth.UP)),
+            "down": (ex.codes(synth.DOWN), ex.codebooks(synth.DOWN))}
+
+
+def test_moe_layer_k1_and_duplicate_experts():
+    H, I, E = 64, 32, 8
+    experts = {e: _small_expert(11, e, H, I) for e in range(E)}
+    bits = synth.router_bf16_bits(11, 0, E, H)
+    x = synth.activation_f32(11, 0, H).astype(np.float64)
+    y1, ids1, g1, _ = oracle.moe_layer(lambda e: experts[e], bits, x, 1)
+    assert g1[0] == 1.0
+    assert np.array_equal(y1, oracle.expert(experts[int(ids1[0])], x))
+    # every id maps to the same expert: output = (sum of gates) * expert = expert (gates sum to 1)
+    y4, ids4, g4, _ = oracle.moe_layer(lambda e: experts[0], bits, x, 4)
+    np.testing.assert_allclose(y4, oracle.expert(experts[0], x), rtol=1e-13, atol=1e-12)
+    # residual is added once
+    r = np.arange(H, dtype=np.float64)
+    yr, _, _, _ = oracle.moe_layer(lambda e: experts[e], bits, x, 3, residual=r)
+    y3, _, _, _ = oracle.moe_layer(lambda e: experts[e], bits, x, 3)
+    np.testing.assert_allclose(yr - r, y3, rtol=1e-13, atol=1e-12)
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_matches_torch_and_closed_form():
+    h = synth.activation_f32(12, 0, 7168).astype(np.float64) * 3.0
+    eps = 1e-6
+    out = oracle.rmsnorm(h, eps)
+    ref = torch.nn.functional.rms_norm(torch.tensor(h), (h.size,), eps=eps).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-14, atol=1e-15)
+    ms = np.mean(h * h)
+    assert abs(np.sqrt(np.mean(out * out)) - np.sqrt(ms / (ms + eps))) < 1e-14
+    np.testing.assert_allclose(oracle.rmsnorm(7.0 * h, 0.0), oracle.rmsnorm(h, 0.0), rtol=1e-14)
