@@ -1,0 +1,189 @@
+/* rvq.h - C ABI of librvq.so: the RVQ-LUT Mixture-of-Experts expert forward
+ * on MI355X (gfx950).
+ *
+ * The method (from the WASTE engine pages):
+ *  - Expert weights are stored with three-stage residual vector quantization:
+ *    every run of 8 consecutive columns of a weight row (a "group") is coded by
+ *    three bytes, one per stage, each choosing an 8-dim vector from that stage's
+ *    256-entry codebook; the decoded sub-vector is the sum of the three chosen
+ *    vectors.  3 bytes per 8 weights = exactly 3.00 bits per weight.
+ *    ("WASTE Inference Engine: Running Kimi K3 2.78T on Consumer Hardware",
+ *    section "Residual Vector Quantization (RVQ)"; news.hada.io topic 32035,
+ *    quantization-and-accuracy section.)
+ *  - The product W x is computed without rebuilding W: per codebook stage and
+ *    per group position a table of partial dot products
+ *        T[g][s][c] = C_s[c] . x[8g .. 8g+7]
+ *    is built from the activation, and each row then needs, per group, three
+ *    table reads and two additions.  ("Running a 2.78-Trillion-Parameter Model
+ *    on a Laptop: Inside WASTE's NVMe-Streaming Engine", section "Technical
+ *    Insight".)
+ *  - An expert is a gate, an up and a down matrix stored next to each other
+ *    (same page, same section); the router picks 16 experts per layer
+ *    (news.hada.io topic 32035, read-ahead and router-prediction section).
+ *
+ * Conventions for every entry point:
+ *  - Data pointers are DEVICE pointers unless stated otherwise; the caller
+ *    owns every buffer.  The library never allocates, frees or synchronises,
+ *    except rvq_check_device_status, which synchronises `stream`.
+ *  - Work is enqueued on `stream` (0 = the null stream).  Calls on distinct
+ *    streams with distinct workspaces may run concurrently; the library has no
+ *    global mutable state.
+ *  - Return value: RVQ_OK (0) or an rvq_status_t error.  Every host-visible
+ *    argument is validated before anything is enqueued: a call that returns an
+ *    error other than RVQ_ERR_HIP has enqueued nothing.
+ *  - Descriptor structs are read during the call only.
+ *  - Sizes are element counts unless named *_bytes.
+ */
+#ifndef RVQ_H_
+#define RVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RVQ_OK = 0,
+  RVQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  RVQ_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  RVQ_ERR_DTYPE = 3,       /* unsupported dtype for this argument */
+  RVQ_ERR_ALIGN = 4,       /* a pointer or stride violates the stated alignment */
+  RVQ_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returned */
+  RVQ_ERR_EXPERT_ID = 6,   /* (device status) an expert id outside [0, num_experts) was seen */
+  RVQ_ERR_HIP = 7          /* a HIP runtime call failed */
+} rvq_status_t;
+
+typedef enum { RVQ_F32 = 0, RVQ_F16 = 1, RVQ_BF16 = 2 } rvq_dtype_t;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *rvq_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Code layout.
+ *
+ * Canonical codes (what a converter produces and what the synthetic
+ * generators emit): uint8 [rows][cols/8][3], stage-minor, row-major, i.e. the
+ * three stage bytes of group g of row r sit at byte 3*(r*(cols/8) + g).
+ *
+ * Packed codes (what the kernels stream; a pure byte permutation, same 3.00
+ * bits per weight):  the matrix is cut into slabs of 64 rows x 16 groups
+ * (3072 bytes).  Slab (t, b) covers groups [16t, 16t+16) of rows
+ * [64b, 64b+64); slabs are ordered t-major: slab index = t*ceil(rows/64) + b.
+ * Inside a slab, byte 1024*j + 16*l + i (j < 3, l < 64, i < 16) is byte
+ * 16*j + i of row 64b+l's 48-byte run for those 16 groups (so one 16-byte
+ * load per lane, 64 lanes, reads one contiguous KiB).  Rows past `rows` and
+ * groups past cols/8 are zero-filled.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of the packed form of a rows x cols matrix:
+ * ceil(cols/8 / 16) * ceil(rows / 64) * 3072.  Equals 3*rows*cols/8 when rows
+ * is a multiple of 64 and cols of 128.  Returns 0 for invalid sizes. */
+size_t rvq_packed_bytes(int32_t rows, int32_t cols);
+
+/* Canonical -> packed.  src: [rows][cols/8][3] uint8 (device, any alignment);
+ * dst: rvq_packed_bytes(rows, cols) bytes, 16-byte aligned; src and dst must
+ * not overlap.  rows >= 1, cols >= 8, cols % 8 == 0. */
+int rvq_pack_codes(const uint8_t *src, int32_t rows, int32_t cols, uint8_t *dst, hipStream_t stream);
+
+/* One RVQ matrix W [rows x cols] in packed layout with its codebooks. */
+typedef struct {
+  const uint8_t *codes;      /* packed codes, 16-byte aligned */
+  const float *codebooks;    /* [3 stages][256 entries][8] fp32, 16-byte aligned */
+  int32_t rows, cols;        /* cols % 8 == 0 */
+} rvq_matrix_t;
+
+/* ------------------------------------------------------------------------
+ * Partial-dot tables (the "lookup tables per codebook and position").
+ *
+ * lut[g][s][c] = sum_{j<8} codebooks[s][c][j] * x[8g+j],  g < cols/8.
+ * lut_dtype RVQ_F32: float lut[cols/8][3][256]; *log2_scale is set to 0.
+ * lut_dtype RVQ_F16: _Float16 lut[cols/8][3][256] holding
+ *   fp16_rne(lut * 2^-e) with one power-of-two exponent e for the whole table,
+ *   chosen from the bound |lut| <= max_{s,c} ||C_s[c]||_2 * max_g ||x_g||_2 so
+ *   that no entry overflows; e is written to *log2_scale (device int32).
+ * x: fp32 [cols]; lut: 16-byte aligned, 4*cols/8*768 (F32) or 2*cols/8*768
+ * (F16) bytes; log2_scale: device int32.  No workspace.
+ * ------------------------------------------------------------------------ */
+int rvq_lut_build(const float *x, int32_t cols, const float *codebooks, int32_t lut_dtype, void *lut,
+                  int32_t *log2_scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Single-matrix LUT GEMV: y = W x through the table path, tables built on
+ * chip per K-tile (16 groups for RVQ_F32, 32 groups for RVQ_F16 tables, each
+ * F16 tile with its own power-of-two scale), W never rebuilt.
+ * x: fp32 [cols]; y: fp32 [rows].  workspace: device, 256-byte aligned, at
+ * least rvq_expert_gemv_workspace_bytes(rows, cols, lut_dtype) bytes; its
+ * contents need no initialisation.
+ * ------------------------------------------------------------------------ */
+size_t rvq_expert_gemv_workspace_bytes(int32_t rows, int32_t cols, int32_t lut_dtype);
+int rvq_expert_gemv(const rvq_matrix_t *W, const float *x, int32_t lut_dtype, float *y, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Router: logits[t][e] = sum_h w_router[e][h] * x[t][h], accumulated in fp64
+ * (bf16 x fp32 products are exact in fp64), then the k experts with the
+ * largest logits in the order (logit descending, expert id ascending) and
+ * gates = softmax over those k logits (= softmax over all E renormalised to
+ * the selected k).
+ * w_router: bf16 [E][H]; x: [T][H] of x_dtype RVQ_F32 or RVQ_BF16;
+ * ids: int32 [T][k]; gates: fp32 [T][k]; logits: double [T][E] or NULL.
+ * 1 <= k <= E <= 4096, k <= 64, H >= 1, T >= 1.  No workspace.
+ * ------------------------------------------------------------------------ */
+int rvq_router_topk(const void *w_router_bf16, const void *x, int32_t x_dtype, int32_t T, int32_t E, int32_t H,
+                    int32_t k, int32_t *ids, float *gates, double *logits, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Expert bank: E SwiGLU experts sharing (hidden H, inter I).  Record e starts
+ * at codes + e*record_stride and holds, back to back, the packed gate [I x H],
+ * packed up [I x H] and packed down [H x I] codes (each of
+ * rvq_packed_bytes(...) bytes).  codebooks: fp32 [E][3 (gate, up, down)][3][256][8].
+ * record_stride: multiple of 256, >= rvq_bank_record_bytes(H, I).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  const uint8_t *codes;
+  const float *codebooks;
+  int64_t record_stride;
+  int32_t num_experts, hidden, inter;
+} rvq_expert_bank_t;
+
+size_t rvq_bank_record_bytes(int32_t hidden, int32_t inter);
+
+/* ------------------------------------------------------------------------
+ * MoE layer forward for T tokens:
+ *   y[t] = residual[t] + sum_{i<k} gates[t][i] * down( silu(gate x_t) * (up x_t) )
+ * of expert ids[t][i], silu(z) = z / (1 + exp(-z)).
+ * T == 1 (decode): table path; compute_dtype RVQ_F32 or RVQ_F16 (table
+ * precision; accumulation is fp32); x_dtype RVQ_F32.
+ * ids, gates: device [T][k] (as written by rvq_router_topk); residual: fp32
+ * [T][H] or NULL; y: fp32 [T][H] (may alias residual).
+ * An id outside [0, num_experts) contributes zero and sets the sticky device
+ * status RVQ_ERR_EXPERT_ID in the workspace (see rvq_check_device_status).
+ * workspace: 256-byte aligned, >= rvq_moe_layer_workspace_bytes(...), and
+ * zero-filled once by rvq_workspace_init before its first use.
+ * ------------------------------------------------------------------------ */
+size_t rvq_moe_layer_workspace_bytes(const rvq_expert_bank_t *bank, int32_t T, int32_t k, int32_t compute_dtype);
+int rvq_moe_layer_forward(const rvq_expert_bank_t *bank, const void *x, int32_t x_dtype, int32_t T,
+                          const int32_t *ids, const float *gates, int32_t k, const float *residual, float *y,
+                          int32_t compute_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Zero-fill a workspace (with a kernel, so the call can be graph-captured). */
+int rvq_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * RMSNorm with unit weight: out[t] = x[t] / sqrt(mean(x[t]^2) + eps).
+ * x, out: fp32 [T][H] (may alias).  T >= 1, H >= 1, eps >= 0.
+ * ------------------------------------------------------------------------ */
+int rvq_rmsnorm(const float *x, int32_t T, int32_t H, float eps, float *out, hipStream_t stream);
+
+/* Synchronises `stream`, returns the sticky device status held in the
+ * workspace of rvq_moe_layer_forward (RVQ_OK or RVQ_ERR_EXPERT_ID) and clears
+ * it.  Returns RVQ_ERR_HIP if the synchronisation or copy fails. */
+int rvq_check_device_status(void *workspace, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RVQ_H_ */

@@ -1,0 +1,286 @@
+"""ctypes binding of librvq.so (include/rvq.h).
+
+Argument marshalling only: PyTorch supplies device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.
+There is no CPU fallback: if librvq.so is missing, or no GPU is visible, the
+calls raise.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librvq.so")
+
+F32, F16, BF16 = 0, 1, 2
+_DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
+
+RVQ_OK = 0
+RVQ_ERR_EXPERT_ID = 6
+
+
+class RvqError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+class Matrix(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("codebooks", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+class BankDesc(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("codebooks", ctypes.c_void_p), ("record_stride", ctypes.c_int64),
+                ("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32)]
+
+
+_lib = None
+
+EXPORTS = [
+    "rvq_status_string", "rvq_packed_bytes", "rvq_pack_codes", "rvq_lut_build",
+    "rvq_expert_gemv_workspace_bytes", "rvq_expert_gemv", "rvq_router_topk", "rvq_bank_record_bytes",
+    "rvq_moe_layer_workspace_bytes", "rvq_moe_layer_forward", "rvq_workspace_init", "rvq_rmsnorm",
+    "rvq_check_device_status",
+]
+
+
+def lib():
+    """Loads librvq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m rvq_quantized_moe_amd.build` "
+                              "(or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.rvq_status_string.argtypes = [ctypes.c_int]
+        L.rvq_status_string.restype = ctypes.c_char_p
+        L.rvq_packed_bytes.argtypes = [i32, i32]
+        L.rvq_packed_bytes.restype = sz
+        L.rvq_pack_codes.argtypes = [p, i32, i32, p, p]
+        L.rvq_lut_build.argtypes = [p, i32, p, i32, p, p, p]
+        L.rvq_expert_gemv_workspace_bytes.argtypes = [i32, i32, i32]
+        L.rvq_expert_gemv_workspace_bytes.restype = sz
+        L.rvq_expert_gemv.argtypes = [ctypes.POINTER(Matrix), p, i32, p, p, sz, p]
+        L.rvq_router_topk.argtypes = [p, p, i32, i32, i32, i32, i32, p, p, p, p]
+        L.rvq_bank_record_bytes.argtypes = [i32, i32]
+        L.rvq_bank_record_bytes.restype = sz
+        L.rvq_moe_layer_workspace_bytes.argtypes = [ctypes.POINTER(BankDesc), i32, i32, i32]
+        L.rvq_moe_layer_workspace_bytes.restype = sz
+        L.rvq_moe_layer_forward.argtypes = [ctypes.POINTER(BankDesc), p, i32, i32, p, p, i32, p, p, i32, p, sz, p]
+        L.rvq_workspace_init.argtypes = [p, sz, p]
+        L.rvq_rmsnorm.argtypes = [p, i32, i32, ctypes.c_float, p, p]
+        L.rvq_check_device_status.argtypes = [p, p]
+        for name in ("rvq_pack_codes", "rvq_lut_build", "rvq_expert_gemv", "rvq_router_topk",
+                     "rvq_moe_layer_forward", "rvq_workspace_init", "rvq_rmsnorm", "rvq_check_device_status"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().rvq_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status != RVQ_OK:
+        raise RvqError(status, status_string(status))
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dev(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _table_dtype(d):
+    if d in ("f32", torch.float32, F32):
+        return F32
+    if d in ("f16", torch.float16, F16):
+        return F16
+    raise ValueError(f"table dtype must be f32 or f16, got {d!r}")
+
+
+# ---------------------------------------------------------------------------------------------
+
+def packed_bytes(rows, cols):
+    n = lib().rvq_packed_bytes(rows, cols)
+    if n == 0:
+        raise ValueError(f"invalid matrix shape {rows}x{cols}")
+    return n
+
+
+def pack_codes(codes, rows, cols, out=None):
+    """Canonical uint8 codes [rows, cols/8, 3] (device) -> packed slab layout (device uint8)."""
+    _dev(codes, torch.uint8, "codes")
+    if codes.numel() != rows * (cols // 8) * 3:
+        raise ValueError("codes must hold 3 bytes per 8 weights")
+    n = packed_bytes(rows, cols)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=codes.device)
+    _dev(out, torch.uint8, "out")
+    if out.numel() < n:
+        raise ValueError("out too small")
+    _check(lib().rvq_pack_codes(_ptr(codes), rows, cols, _ptr(out), _stream(codes)))
+    return out
+
+
+def lut_build(x, codebooks, dtype="f32"):
+    """Partial-dot tables [cols/8, 3, 256] (fp32, or fp16 scaled by 2^-e) and e (int32 device scalar)."""
+    _dev(x, torch.float32, "x")
+    _dev(codebooks, torch.float32, "codebooks")
+    d = _table_dtype(dtype)
+    cols = x.numel()
+    lut = torch.empty((cols // 8, 3, 256), dtype=torch.float32 if d == F32 else torch.float16, device=x.device)
+    e = torch.empty(1, dtype=torch.int32, device=x.device)
+    _check(lib().rvq_lut_build(_ptr(x), cols, _ptr(codebooks), d, _ptr(lut), _ptr(e), _stream(x)))
+    return lut, e
+
+
+def gemv_workspace_bytes(rows, cols, dtype="f32"):
+    return lib().rvq_expert_gemv_workspace_bytes(rows, cols, _table_dtype(dtype))
+
+
+def expert_gemv(packed, codebooks, rows, cols, x, dtype="f32", y=None, workspace=None):
+    """y = W x through the table path for one packed RVQ matrix."""
+    _dev(packed, torch.uint8, "packed")
+    _dev(codebooks, torch.float32, "codebooks")
+    _dev(x, torch.float32, "x")
+    d = _table_dtype(dtype)
+    if y is None:
+        y = torch.empty(rows, dtype=torch.float32, device=x.device)
+    need = gemv_workspace_bytes(rows, cols, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    m = Matrix(packed.data_ptr(), codebooks.data_ptr(), rows, cols)
+    _check(lib().rvq_expert_gemv(ctypes.byref(m), _ptr(x), d, _ptr(y), _ptr(workspace), workspace.numel(),
+                                 _stream(x)))
+    return y
+
+
+def router_topk(w_router, x, k, ids=None, gates=None, logits=None):
+    """Top-k routing: w_router bf16 [E, H]; x fp32 or bf16 [T, H] (or [H]).
+
+    Returns (ids int32 [T, k], gates fp32 [T, k], logits fp64 [T, E])."""
+    _dev(w_router, torch.bfloat16, "w_router")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _dev(x, x.dtype, "x")
+    E, H = w_router.shape
+    x2 = x.reshape(-1, H)
+    T = x2.shape[0]
+    dev = x.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev) if gates is None else gates
+    logits = torch.empty((T, E), dtype=torch.float64, device=dev) if logits is None else logits
+    xd = F32 if x.dtype == torch.float32 else BF16
+    _check(lib().rvq_router_topk(_ptr(w_router), _ptr(x2), xd, T, E, H, k, _ptr(ids), _ptr(gates), _ptr(logits),
+                                 _stream(x)))
+    return ids, gates, logits
+
+
+def rmsnorm(x, eps=1e-6, out=None):
+    _dev(x, torch.float32, "x")
+    H = x.shape[-1]
+    T = x.numel() // H
+    out = torch.empty_like(x) if out is None else out
+    _check(lib().rvq_rmsnorm(_ptr(x), T, H, float(eps), _ptr(out), _stream(x)))
+    return out
+
+
+def workspace_init(ws):
+    _check(lib().rvq_workspace_init(_ptr(ws), ws.numel(), _stream(ws)))
+
+
+def check_device_status(ws):
+    """Synchronises the current stream; returns the sticky device status (0 = OK) and clears it."""
+    return lib().rvq_check_device_status(_ptr(ws), _stream(ws))
+
+
+class ExpertBank:
+    """E SwiGLU experts (hidden H, inter I) resident on the device in packed layout.
+
+    codes: uint8 [E * record_stride]; codebooks: fp32 [E, 3, 3, 256, 8] (gate, up, down)."""
+
+    def __init__(self, num_experts, hidden, inter, device="cuda", record_stride=None):
+        self.E, self.H, self.I = num_experts, hidden, inter
+        rec = lib().rvq_bank_record_bytes(hidden, inter)
+        if rec == 0:
+            raise ValueError("invalid expert shape")
+        self.record_bytes = rec
+        self.stride = record_stride or ((rec + 255) // 256) * 256
+        self.gate_bytes = packed_bytes(inter, hidden)
+        self.down_bytes = packed_bytes(hidden, inter)
+        self.codes = torch.empty(num_experts * self.stride, dtype=torch.uint8, device=device)
+        self.codebooks = torch.empty((num_experts, 3, 3, 256, 8), dtype=torch.float32, device=device)
+        self._staging = None
+
+    def desc(self):
+        return BankDesc(self.codes.data_ptr(), self.codebooks.data_ptr(), self.stride, self.E, self.H, self.I)
+
+    def matrix_offset(self, e, m):
+        return e * self.stride + m * self.gate_bytes
+
+    def load_expert(self, e, gate_codes, up_codes, down_codes, codebooks):
+        """Uploads one expert given canonical numpy codes ([I, H/8, 3], [I, H/8, 3], [H, I/8, 3]) and
+        codebooks [3, 3, 256, 8], packing each matrix into record e."""
+        dev = self.codes.device
+        n = max(gate_codes.size, down_codes.size)
+        if self._staging is None or self._staging.numel() < n:
+            self._staging = torch.empty(n, dtype=torch.uint8, device=dev)
+        for m, (c, rows, cols) in enumerate(((gate_codes, self.I, self.H), (up_codes, self.I, self.H),
+                                             (down_codes, self.H, self.I))):
+            st = self._staging[:c.size]
+            st.copy_(torch.from_numpy(c.reshape(-1)))
+            nbytes = packed_bytes(rows, cols)
+            off = self.matrix_offset(e, m)
+            pack_codes(st, rows, cols, out=self.codes[off:off + nbytes])
+        self.codebooks[e].copy_(torch.from_numpy(codebooks))
+
+
+def moe_workspace_bytes(bank, T=1, k=16, dtype="f32"):
+    d = bank.desc()
+    return lib().rvq_moe_layer_workspace_bytes(ctypes.byref(d), T, k, _table_dtype(dtype))
+
+
+def make_moe_workspace(bank, T=1, k=16, dtype="f32"):
+    n = moe_workspace_bytes(bank, T, k, dtype)
+    if n == 0:
+        raise ValueError("unsupported MoE layer configuration")
+    ws = torch.empty(n, dtype=torch.uint8, device=bank.codes.device)
+    workspace_init(ws)
+    return ws
+
+
+def moe_layer_forward(bank, x, ids, gates, residual=None, dtype="f32", y=None, workspace=None):
+    """y = [residual +] sum_i gates[i] * expert_{ids[i]}(x) for one decode token (x fp32 [H])."""
+    _dev(x, torch.float32, "x")
+    _dev(ids, torch.int32, "ids")
+    _dev(gates, torch.float32, "gates")
+    d = _table_dtype(dtype)
+    k = ids.numel()
+    T = 1
+    if residual is not None:
+        _dev(residual, torch.float32, "residual")
+    if y is None:
+        y = torch.empty(bank.H, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = make_moe_workspace(bank, T, k, d)
+    desc = bank.desc()
+    _check(lib().rvq_moe_layer_forward(ctypes.byref(desc), _ptr(x), F32, T, _ptr(ids), _ptr(gates), k,
+                                       _ptr(residual), _ptr(y), d, _ptr(workspace), workspace.numel(), _stream(x)))
+    return y

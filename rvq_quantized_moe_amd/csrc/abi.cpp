@@ -1,0 +1,162 @@
+// extern "C" entry points of librvq.so (declared in include/rvq.h): argument validation, workspace
+// layout, and calls into the kernel launchers.  Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/rvq.h"
+#include "device.hpp"
+#include "launch.hpp"
+
+using namespace rvq;
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? RVQ_OK : RVQ_ERR_HIP; }
+
+// Largest element count the kernels index with 32-bit row/column arithmetic.
+constexpr int64_t kMaxDim = 1 << 24;
+
+inline bool valid_matrix_shape(int64_t rows, int64_t cols) {
+  return rows >= 1 && cols >= 8 && cols % 8 == 0 && rows <= kMaxDim && cols <= kMaxDim;
+}
+
+inline bool table_dtype(int32_t d) { return d == RVQ_F32 || d == RVQ_F16; }
+
+int check_bank(const rvq_expert_bank_t* bank) {
+  if (!bank || !bank->codes || !bank->codebooks) return RVQ_ERR_NULL;
+  if (bank->num_experts < 1 || bank->num_experts > kMaxExperts) return RVQ_ERR_SHAPE;
+  if (!valid_matrix_shape(bank->inter, bank->hidden) || bank->inter % 8 != 0) return RVQ_ERR_SHAPE;
+  if (!aligned(bank->codes, 16) || !aligned(bank->codebooks, 16)) return RVQ_ERR_ALIGN;
+  if (bank->record_stride % 256 != 0) return RVQ_ERR_ALIGN;
+  if (bank->record_stride < (int64_t)rvq_bank_record_bytes(bank->hidden, bank->inter)) return RVQ_ERR_SHAPE;
+  return RVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rvq_status_string(int status) {
+  switch (status) {
+    case RVQ_OK: return "RVQ_OK";
+    case RVQ_ERR_NULL: return "RVQ_ERR_NULL: a required pointer is NULL";
+    case RVQ_ERR_SHAPE: return "RVQ_ERR_SHAPE: a size is out of range or inconsistent";
+    case RVQ_ERR_DTYPE: return "RVQ_ERR_DTYPE: unsupported dtype";
+    case RVQ_ERR_ALIGN: return "RVQ_ERR_ALIGN: pointer or stride misaligned";
+    case RVQ_ERR_WORKSPACE: return "RVQ_ERR_WORKSPACE: workspace too small";
+    case RVQ_ERR_EXPERT_ID: return "RVQ_ERR_EXPERT_ID: an expert id outside [0, num_experts) was seen";
+    case RVQ_ERR_HIP: return "RVQ_ERR_HIP: a HIP runtime call failed";
+    default: return "RVQ: unknown status";
+  }
+}
+
+size_t rvq_packed_bytes(int32_t rows, int32_t cols) {
+  if (!valid_matrix_shape(rows, cols)) return 0;
+  return (size_t)packed_bytes(rows, cols);
+}
+
+int rvq_pack_codes(const uint8_t* src, int32_t rows, int32_t cols, uint8_t* dst, hipStream_t stream) {
+  if (!src || !dst) return RVQ_ERR_NULL;
+  if (!valid_matrix_shape(rows, cols)) return RVQ_ERR_SHAPE;
+  if (!aligned(dst, 16)) return RVQ_ERR_ALIGN;
+  return hip_status(launch_pack(src, rows, cols, dst, stream));
+}
+
+int rvq_lut_build(const float* x, int32_t cols, const float* codebooks, int32_t lut_dtype, void* lut,
+                  int32_t* log2_scale, hipStream_t stream) {
+  if (!x || !codebooks || !lut || !log2_scale) return RVQ_ERR_NULL;
+  if (cols < 8 || cols % 8 != 0 || cols > kMaxDim) return RVQ_ERR_SHAPE;
+  if (!table_dtype(lut_dtype)) return RVQ_ERR_DTYPE;
+  if (!aligned(codebooks, 16) || !aligned(lut, 16) || !aligned(x, 4)) return RVQ_ERR_ALIGN;
+  return hip_status(launch_lut_build(x, cols, codebooks, lut_dtype == RVQ_F16, lut, log2_scale, stream));
+}
+
+size_t rvq_expert_gemv_workspace_bytes(int32_t rows, int32_t cols, int32_t lut_dtype) {
+  if (!valid_matrix_shape(rows, cols) || !table_dtype(lut_dtype)) return 0;
+  return gemv_workspace_bytes(rows, cols, lut_dtype == RVQ_F16);
+}
+
+int rvq_expert_gemv(const rvq_matrix_t* W, const float* x, int32_t lut_dtype, float* y, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  if (!W || !W->codes || !W->codebooks || !x || !y || !workspace) return RVQ_ERR_NULL;
+  if (!valid_matrix_shape(W->rows, W->cols)) return RVQ_ERR_SHAPE;
+  if (!table_dtype(lut_dtype)) return RVQ_ERR_DTYPE;
+  if (!aligned(W->codes, 16) || !aligned(W->codebooks, 16) || !aligned(workspace, 256) || !aligned(x, 4) ||
+      !aligned(y, 4))
+    return RVQ_ERR_ALIGN;
+  if (workspace_bytes < gemv_workspace_bytes(W->rows, W->cols, lut_dtype == RVQ_F16)) return RVQ_ERR_WORKSPACE;
+  return hip_status(
+      launch_gemv(W->codes, W->codebooks, W->rows, W->cols, x, lut_dtype == RVQ_F16, y, workspace, stream));
+}
+
+int rvq_router_topk(const void* w_router_bf16, const void* x, int32_t x_dtype, int32_t T, int32_t E, int32_t H,
+                    int32_t k, int32_t* ids, float* gates, double* logits, hipStream_t stream) {
+  if (!w_router_bf16 || !x || !ids || !gates || !logits) return RVQ_ERR_NULL;
+  if (T < 1 || E < 1 || E > kMaxExperts || H < 1 || H > kMaxDim || k < 1 || k > E || k > kMaxTopK)
+    return RVQ_ERR_SHAPE;
+  if ((int64_t)T * E > ((int64_t)1 << 31) || (int64_t)T * H > ((int64_t)1 << 40)) return RVQ_ERR_SHAPE;
+  if (x_dtype != RVQ_F32 && x_dtype != RVQ_BF16) return RVQ_ERR_DTYPE;
+  if (!aligned(w_router_bf16, 2) || !aligned(x, x_dtype == RVQ_F32 ? 4 : 2) || !aligned(logits, 8) ||
+      !aligned(ids, 4) || !aligned(gates, 4))
+    return RVQ_ERR_ALIGN;
+  return hip_status(launch_router_topk(static_cast<const uint16_t*>(w_router_bf16), x, x_dtype == RVQ_BF16, T, E, H,
+                                       k, ids, gates, logits, stream));
+}
+
+size_t rvq_bank_record_bytes(int32_t hidden, int32_t inter) {
+  if (!valid_matrix_shape(inter, hidden) || !valid_matrix_shape(hidden, inter)) return 0;
+  return (size_t)(2 * packed_bytes(inter, hidden) + packed_bytes(hidden, inter));
+}
+
+size_t rvq_moe_layer_workspace_bytes(const rvq_expert_bank_t* bank, int32_t T, int32_t k, int32_t compute_dtype) {
+  if (!bank || T != 1 || k < 1 || k > kMaxTopK || !table_dtype(compute_dtype)) return 0;
+  if (!valid_matrix_shape(bank->inter, bank->hidden) || bank->inter % 8 != 0) return 0;
+  return moe_workspace_layout(bank->hidden, bank->inter, k, compute_dtype == RVQ_F16).total;
+}
+
+int rvq_moe_layer_forward(const rvq_expert_bank_t* bank, const void* x, int32_t x_dtype, int32_t T,
+                          const int32_t* ids, const float* gates, int32_t k, const float* residual, float* y,
+                          int32_t compute_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_bank(bank);
+  if (st != RVQ_OK) return st;
+  if (!x || !ids || !gates || !y || !workspace) return RVQ_ERR_NULL;
+  if (T != 1 || k < 1 || k > kMaxTopK) return RVQ_ERR_SHAPE;
+  if (x_dtype != RVQ_F32 || !table_dtype(compute_dtype)) return RVQ_ERR_DTYPE;
+  if (!aligned(workspace, 256) || !aligned(x, 4) || !aligned(y, 4) || !aligned(ids, 4) || !aligned(gates, 4) ||
+      (residual && !aligned(residual, 4)))
+    return RVQ_ERR_ALIGN;
+  const bool f16 = compute_dtype == RVQ_F16;
+  if (workspace_bytes < moe_workspace_layout(bank->hidden, bank->inter, k, f16).total) return RVQ_ERR_WORKSPACE;
+  return hip_status(launch_moe_decode(bank->codes, bank->codebooks, bank->record_stride, bank->num_experts,
+                                      bank->hidden, bank->inter, static_cast<const float*>(x), ids, gates, k,
+                                      residual, y, f16, workspace, stream));
+}
+
+int rvq_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace) return RVQ_ERR_NULL;
+  if (!aligned(workspace, 256)) return RVQ_ERR_ALIGN;
+  if (workspace_bytes == 0) return RVQ_OK;
+  return hip_status(launch_zero(workspace, workspace_bytes, stream));
+}
+
+int rvq_rmsnorm(const float* x, int32_t T, int32_t H, float eps, float* out, hipStream_t stream) {
+  if (!x || !out) return RVQ_ERR_NULL;
+  if (T < 1 || H < 1 || H > kMaxDim || !(eps >= 0.f)) return RVQ_ERR_SHAPE;
+  if (!aligned(x, 4) || !aligned(out, 4)) return RVQ_ERR_ALIGN;
+  return hip_status(launch_rmsnorm(x, T, H, eps, out, stream));
+}
+
+int rvq_check_device_status(void* workspace, hipStream_t stream) {
+  if (!workspace) return RVQ_ERR_NULL;
+  if (!aligned(workspace, 256)) return RVQ_ERR_ALIGN;
+  if (hipStreamSynchronize(stream) != hipSuccess) return RVQ_ERR_HIP;
+  int32_t st = 0;
+  if (hipMemcpy(&st, workspace, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess) return RVQ_ERR_HIP;
+  const int32_t zero = 0;
+  if (hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return RVQ_ERR_HIP;
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,37 @@
+// Internal host-side launch interface between abi.cpp (validation) and kernels.hip (kernels).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rvq {
+
+constexpr int kMaxExperts = 4096;
+constexpr int kMaxTopK = 64;
+
+struct MoeWorkspace {
+  int nt_in, nt_out;              // K-tiles of gate/up (over H) and of down (over I)
+  size_t status_off;              // int32 sticky device status
+  size_t part_gu_off;             // fp32 [k][2][nt_in][I]
+  size_t part_d_off;              // fp32 [k][nt_out][H]
+  size_t total;
+};
+
+MoeWorkspace moe_workspace_layout(int H, int I, int k, bool f16);
+int gemv_tiles(int cols, bool f16);
+size_t gemv_workspace_bytes(int rows, int cols, bool f16);
+
+hipError_t launch_pack(const uint8_t* src, int rows, int cols, uint8_t* dst, hipStream_t stream);
+hipError_t launch_zero(void* p, size_t nbytes, hipStream_t stream);
+hipError_t launch_lut_build(const float* x, int cols, const float* cb, bool f16, void* lut, int32_t* log2_scale,
+                            hipStream_t stream);
+hipError_t launch_gemv(const uint8_t* codes, const float* cb, int rows, int cols, const float* x, bool f16, float* y,
+                       void* ws, hipStream_t stream);
+hipError_t launch_router_topk(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, int k, int32_t* ids,
+                              float* gates, double* logits, hipStream_t stream);
+hipError_t launch_rmsnorm(const float* x, int T, int H, float eps, float* out, hipStream_t stream);
+hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
+                             const float* x, const int32_t* ids, const float* gates, int k, const float* residual,
+                             float* y, bool f16, void* ws, hipStream_t stream);
+
+}  // namespace rvq

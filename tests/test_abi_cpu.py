@@ -1,0 +1,188 @@
+"""Host-side contract of librvq.so, runnable without a GPU: the library loads,
+exports every entry point include/rvq.h declares, and rejects invalid
+arguments with the documented status before anything is enqueued (fake
+non-NULL device pointers are used; no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rvq_quantized_moe_amd as rvq
+from rvq_quantized_moe_amd import _lib
+from workloads import pack_spec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rvq.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WS, EXPERT_ID, HIP = range(8)
+FAKE = 0x7f0000000000          # 256-byte aligned, never dereferenced by the validators
+FAKE2 = 0x7f0000100000
+
+
+@pytest.fixture(scope="module")
+def L():
+    return rvq.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(rvq_[a-z0-9_]+)\s*\(", text))
+    assert declared, "no declarations found"
+    assert set(_lib.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for s in range(8):
+        txt = rvq.status_string(s)
+        assert txt.startswith("RVQ_")
+    assert "unknown" in rvq.status_string(99)
+
+
+def test_packed_bytes(L):
+    assert rvq.packed_bytes(2048, 7168) == 5_505_024 == 2048 * 7168 * 3 // 8
+    assert rvq.packed_bytes(7168, 2048) == 5_505_024
+    assert rvq.packed_bytes(256, 512) == 49_152
+    assert rvq.packed_bytes(1, 8) == 3072
+    assert rvq.packed_bytes(65, 8 * 17) == 2 * 2 * 3072
+    assert L.rvq_packed_bytes(0, 8) == 0 and L.rvq_packed_bytes(4, 12) == 0
+    assert L.rvq_bank_record_bytes(7168, 2048) == 16_515_072
+    for rows, cols in [(1, 8), (65, 136), (256, 512), (300, 800)]:
+        assert pack_spec(np.zeros((rows, cols // 8, 3), np.uint8), rows, cols).size == rvq.packed_bytes(rows, cols)
+
+
+def test_pack_spec_is_a_zero_padded_permutation():
+    rng = np.random.default_rng(0)
+    rows, cols = 70, 8 * 21
+    codes = rng.integers(1, 256, size=(rows, cols // 8, 3)).astype(np.uint8)
+    p = pack_spec(codes, rows, cols)
+    assert np.array_equal(np.sort(p[p != 0]), np.sort(codes.reshape(-1)))
+    # first KiB of the first slab = rows 0..63, bytes 0..15 of each row's run
+    assert np.array_equal(p[:1024].reshape(64, 16), codes.reshape(rows, -1)[:64, :16])
+
+
+def test_pack_validation(L):
+    s = None
+    assert L.rvq_pack_codes(None, 4, 8, FAKE, s) == NULL
+    assert L.rvq_pack_codes(FAKE, 4, 8, None, s) == NULL
+    assert L.rvq_pack_codes(FAKE, 0, 8, FAKE2, s) == SHAPE
+    assert L.rvq_pack_codes(FAKE, 4, 12, FAKE2, s) == SHAPE
+    assert L.rvq_pack_codes(FAKE, 4, 0, FAKE2, s) == SHAPE
+    assert L.rvq_pack_codes(FAKE, 4, 8, FAKE2 + 8, s) == ALIGN
+
+
+def test_lut_validation(L):
+    s = None
+    assert L.rvq_lut_build(None, 8, FAKE, 0, FAKE2, FAKE2, s) == NULL
+    assert L.rvq_lut_build(FAKE, 8, FAKE, 0, FAKE2, None, s) == NULL
+    assert L.rvq_lut_build(FAKE, 9, FAKE, 0, FAKE2, FAKE2, s) == SHAPE
+    assert L.rvq_lut_build(FAKE, 8, FAKE, 2, FAKE2, FAKE2, s) == DTYPE
+    assert L.rvq_lut_build(FAKE, 8, FAKE + 4, 0, FAKE2, FAKE2, s) == ALIGN
+
+
+def _matrix(rows, cols, codes=FAKE, cb=FAKE2):
+    return ctypes.byref(_lib.Matrix(codes, cb, rows, cols))
+
+
+def test_gemv_validation(L):
+    s = None
+    need = L.rvq_expert_gemv_workspace_bytes(256, 512, 0)
+    assert need == 4 * 256 * 4
+    assert L.rvq_expert_gemv_workspace_bytes(256, 512, 1) == 2 * 256 * 4
+    assert L.rvq_expert_gemv_workspace_bytes(256, 500, 0) == 0
+    assert L.rvq_expert_gemv(None, FAKE, 0, FAKE, FAKE, need, s) == NULL
+    assert L.rvq_expert_gemv(_matrix(256, 512, codes=None), FAKE, 0, FAKE, FAKE, need, s) == NULL
+    assert L.rvq_expert_gemv(_matrix(256, 512), FAKE, 0, FAKE, None, need, s) == NULL
+    assert L.rvq_expert_gemv(_matrix(0, 512), FAKE, 0, FAKE, FAKE, need, s) == SHAPE
+    assert L.rvq_expert_gemv(_matrix(256, 511), FAKE, 0, FAKE, FAKE, need, s) == SHAPE
+    assert L.rvq_expert_gemv(_matrix(256, 512), FAKE, 2, FAKE, FAKE, need, s) == DTYPE
+    assert L.rvq_expert_gemv(_matrix(256, 512, codes=FAKE + 8), FAKE, 0, FAKE, FAKE, need, s) == ALIGN
+    assert L.rvq_expert_gemv(_matrix(256, 512), FAKE, 0, FAKE, FAKE + 16, need, s) == ALIGN
+    assert L.rvq_expert_gemv(_matrix(256, 512), FAKE, 0, FAKE, FAKE, need - 1, s) == WS
+
+
+def test_router_validation(L):
+    s = None
+    a = (FAKE, FAKE2)
+    assert L.rvq_router_topk(None, FAKE, 0, 1, 256, 7168, 16, FAKE, FAKE, FAKE, s) == NULL
+    assert L.rvq_router_topk(*a, 0, 1, 256, 7168, 16, FAKE, FAKE, None, s) == NULL
+    assert L.rvq_router_topk(*a, 0, 1, 256, 7168, 257, FAKE, FAKE, FAKE, s) == SHAPE
+    assert L.rvq_router_topk(*a, 0, 1, 256, 7168, 0, FAKE, FAKE, FAKE, s) == SHAPE
+    assert L.rvq_router_topk(*a, 0, 1, 5000, 7168, 16, FAKE, FAKE, FAKE, s) == SHAPE
+    assert L.rvq_router_topk(*a, 0, 1, 256, 7168, 65, FAKE, FAKE, FAKE, s) == SHAPE
+    assert L.rvq_router_topk(*a, 0, 0, 256, 7168, 16, FAKE, FAKE, FAKE, s) == SHAPE
+    assert L.rvq_router_topk(*a, 1, 1, 256, 7168, 16, FAKE, FAKE, FAKE, s) == DTYPE
+    assert L.rvq_router_topk(FAKE + 1, FAKE2, 0, 1, 256, 7168, 16, FAKE, FAKE, FAKE, s) == ALIGN
+    assert L.rvq_router_topk(*a, 0, 1, 256, 7168, 16, FAKE, FAKE, FAKE + 4, s) == ALIGN
+
+
+def _bank(E=256, H=7168, I=2048, stride=16_515_072, codes=FAKE, cb=FAKE2):
+    return ctypes.byref(_lib.BankDesc(codes, cb, stride, E, H, I))
+
+
+def test_moe_workspace_size(L):
+    n = L.rvq_moe_layer_workspace_bytes(_bank(), 1, 16, 0)
+    assert n == 256 + 16 * 2 * 56 * 2048 * 4 + 16 * 16 * 7168 * 4
+    assert L.rvq_moe_layer_workspace_bytes(_bank(), 1, 16, 1) == 256 + 16 * 2 * 28 * 2048 * 4 + 16 * 8 * 7168 * 4
+    assert L.rvq_moe_layer_workspace_bytes(_bank(), 1, 16, 2) == 0
+    assert L.rvq_moe_layer_workspace_bytes(None, 1, 16, 0) == 0
+
+
+def test_moe_validation(L):
+    s = None
+    n = L.rvq_moe_layer_workspace_bytes(_bank(), 1, 16, 0)
+    args = (FAKE, 0, 1, FAKE, FAKE, 16, None, FAKE, 0, FAKE, n, s)
+    assert L.rvq_moe_layer_forward(None, *args) == NULL
+    assert L.rvq_moe_layer_forward(_bank(codes=None), *args) == NULL
+    assert L.rvq_moe_layer_forward(_bank(stride=16_515_072 + 8), *args) == ALIGN
+    assert L.rvq_moe_layer_forward(_bank(stride=16_515_072 - 256), *args) == SHAPE
+    assert L.rvq_moe_layer_forward(_bank(E=0), *args) == SHAPE
+    assert L.rvq_moe_layer_forward(_bank(H=7170), *args) == SHAPE
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 2, FAKE, FAKE, 16, None, FAKE, 0, FAKE, n, s) == SHAPE
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 1, FAKE, FAKE, 65, None, FAKE, 0, FAKE, n, s) == SHAPE
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 2, 1, FAKE, FAKE, 16, None, FAKE, 0, FAKE, n, s) == DTYPE
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 1, FAKE, FAKE, 16, None, FAKE, 2, FAKE, n, s) == DTYPE
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 1, FAKE, FAKE, 16, None, FAKE, 0, FAKE + 64, n, s) == ALIGN
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 1, FAKE, FAKE, 16, None, FAKE, 0, FAKE, n - 1, s) == WS
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 1, None, FAKE, 16, None, FAKE, 0, FAKE, n, s) == NULL
+
+
+def test_misc_validation(L):
+    s = None
+    assert L.rvq_rmsnorm(None, 1, 8, 1e-6, FAKE, s) == NULL
+    assert L.rvq_rmsnorm(FAKE, 0, 8, 1e-6, FAKE, s) == SHAPE
+    assert L.rvq_rmsnorm(FAKE, 1, 8, -1.0, FAKE, s) == SHAPE
+    assert L.rvq_rmsnorm(FAKE, 1, 8, float("nan"), FAKE, s) == SHAPE
+    assert L.rvq_workspace_init(None, 16, s) == NULL
+    assert L.rvq_workspace_init(FAKE + 8, 16, s) == ALIGN
+    assert L.rvq_check_device_status(None, s) == NULL
+
+
+def test_validator_fuzz(L):
+    """Random argument sets with at least one invalid field never pass validation."""
+    rng = np.random.default_rng(1234)
+    s = None
+    bad_values = {"rows": [0, -1, -64], "cols": [0, 4, 12, 1001, -8], "dtype": [2, 3, -1, 7],
+                  "align": [1, 2, 4, 8]}
+    for _ in range(400):
+        rows = int(rng.integers(1, 5000))
+        cols = 8 * int(rng.integers(1, 1000))
+        dtype = int(rng.integers(0, 2))
+        codes = FAKE
+        which = rng.choice(list(bad_values))
+        if which == "rows":
+            rows = int(rng.choice(bad_values["rows"]))
+        elif which == "cols":
+            cols = int(rng.choice(bad_values["cols"]))
+        elif which == "dtype":
+            dtype = int(rng.choice(bad_values["dtype"]))
+        else:
+            codes = FAKE + int(rng.choice(bad_values["align"]))
+        st = L.rvq_expert_gemv(_matrix(rows, cols, codes=codes), FAKE, dtype, FAKE, FAKE, 1 << 40, s)
+        assert st in (SHAPE, DTYPE, ALIGN), (which, rows, cols, dtype, st)
+        st = L.rvq_pack_codes(FAKE, rows, cols, codes if which == "align" else FAKE2, s)
+        if which in ("rows", "cols", "align"):
+            assert st in (SHAPE, ALIGN), (which, st)

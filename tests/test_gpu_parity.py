@@ -1,0 +1,289 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Tolerances (relative L2 over the whole output unless stated):
+  fp32 tables: 1e-5;  fp16 tables: 2e-3;  router ids: bit-exact;
+  gates: 1e-6 relative;  logits (fp64 on both sides): 1e-12 relative.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rvq_quantized_moe_amd as rvq
+import synth
+from workloads import (HIDDEN, INTER, LAYER_EXPERTS, MATVEC_COLS, MATVEC_ROWS, TOP_K, oracle_expert, pack_spec,
+                       rel_l2, router, upload_bank)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {"f32": 1e-5, "f16": 2e-3}
+
+
+def say(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def packed_matrix(seed, rows, cols, matrix=synth.SINGLE, expert=0):
+    codes = synth.matrix_codes(seed, 0, expert, matrix, rows, cols)
+    cb = synth.matrix_codebooks(seed, 0, expert, matrix)
+    packed = rvq.pack_codes(to_dev(codes), rows, cols)
+    return codes, cb, packed, to_dev(cb)
+
+
+# ---------------------------------------------------------------- packing (byte permutation, exact)
+
+@pytest.mark.parametrize("rows,cols", [(256, 512), (1, 8), (65, 136), (300, 800), (2048, 7168), (7168, 2048)])
+def test_pack_matches_layout_spec(rows, cols):
+    say(f"pack {rows}x{cols}")
+    codes = synth.matrix_codes(0xA1, 0, 0, synth.SINGLE, rows, cols)
+    packed = rvq.pack_codes(to_dev(codes), rows, cols).cpu().numpy()
+    assert np.array_equal(packed, pack_spec(codes, rows, cols))
+
+
+# ---------------------------------------------------------------- partial-dot tables
+
+def test_lut_build_f32_matvec_config():
+    say("lut f32 256x512")
+    x = synth.activation_f32(synth.SEED_MATVEC, 0, MATVEC_COLS)
+    cb = synth.matrix_codebooks(synth.SEED_MATVEC, 0, 0, synth.SINGLE)
+    lut, e = rvq.lut_build(to_dev(x), to_dev(cb), "f32")
+    T = oracle.lut(cb, x)
+    absT = oracle.lut(np.abs(cb), np.abs(x))          # sum_j |C_s[c][j] x_j|
+    got = lut.cpu().numpy().astype(np.float64)
+    assert int(e.item()) == 0
+    assert (np.abs(got - T) <= 8 * 2.0 ** -24 * absT + 1e-30).all()
+
+
+@pytest.mark.parametrize("cols,scale", [(512, 1.0), (7168, 1.0), (2048, 3.0e4), (136, 1e-3)])
+def test_lut_build_f16(cols, scale):
+    say(f"lut f16 cols={cols} scale={scale}")
+    x = (synth.activation_f32(0xB2, 0, cols) * np.float32(scale)).astype(np.float32)
+    cb = synth.matrix_codebooks(0xB2, 0, 0, synth.SINGLE)
+    lut, e = rvq.lut_build(to_dev(x), to_dev(cb), "f16")
+    e = int(e.item())
+    got = lut.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    T = oracle.lut(cb, x)
+    assert np.abs(T).max() * 2.0 ** -e < 65504
+    absT = oracle.lut(np.abs(cb), np.abs(x))
+    err = np.abs(got * 2.0 ** e - T)
+    # fp16 rounding (half ulp = 2^-11 relative), fp32 dot error, and subnormal spacing 2^-24 (scaled)
+    bound = 2.0 ** -11 * np.abs(T) + 16 * 2.0 ** -24 * absT + 2.0 ** (e - 24)
+    assert (err <= bound).all()
+
+
+# ---------------------------------------------------------------- single-matrix GEMV
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_gemv_matvec_config(dtype):
+    say(f"gemv 256x512 {dtype}")
+    codes, cb, packed, cbd = packed_matrix(synth.SEED_MATVEC, MATVEC_ROWS, MATVEC_COLS)
+    x = synth.activation_f32(synth.SEED_MATVEC, 0, MATVEC_COLS)
+    y = rvq.expert_gemv(packed, cbd, MATVEC_ROWS, MATVEC_COLS, to_dev(x), dtype).cpu().numpy()
+    ref = oracle.gemv(codes, cb, MATVEC_ROWS, MATVEC_COLS, x)
+    err = rel_l2(y, ref)
+    say(f"  rel-L2 {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("rows,cols", [(1, 8), (7, 120), (64, 128), (65, 136), (300, 264), (129, 800), (5, 8 * 33)])
+def test_gemv_ragged_shapes(rows, cols, dtype):
+    say(f"gemv {rows}x{cols} {dtype}")
+    codes, cb, packed, cbd = packed_matrix(0xC3 + rows, rows, cols)
+    x = synth.activation_f32(0xC3, rows, cols)
+    y = rvq.expert_gemv(packed, cbd, rows, cols, to_dev(x), dtype).cpu().numpy()
+    ref = oracle.gemv(codes, cb, rows, cols, x)
+    assert rel_l2(y, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_gemv_full_size_sampled(dtype):
+    rows, cols = INTER, HIDDEN
+    say(f"gemv {rows}x{cols} {dtype}")
+    codes, cb, packed, cbd = packed_matrix(synth.SEED_EXPERT, rows, cols, synth.GATE)
+    x = synth.activation_f32(synth.SEED_EXPERT, 0, cols)
+    y = rvq.expert_gemv(packed, cbd, rows, cols, to_dev(x), dtype).cpu().numpy()
+    ref = oracle.gemv(codes, cb, rows, cols, x)
+    assert rel_l2(y, ref) <= TOL[dtype]
+
+
+def test_gemv_is_deterministic():
+    say("gemv determinism")
+    codes, cb, packed, cbd = packed_matrix(0xD4, 2048, 7168)
+    x = to_dev(synth.activation_f32(0xD4, 0, 7168))
+    a = rvq.expert_gemv(packed, cbd, 2048, 7168, x, "f32")
+    b = rvq.expert_gemv(packed, cbd, 2048, 7168, x, "f32")
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- router
+
+@pytest.mark.parametrize("E,H,k", [(LAYER_EXPERTS, HIDDEN, TOP_K), (64, HIDDEN, TOP_K), (300, 1000, 7), (16, 64, 16)])
+def test_router_topk_matches_oracle(E, H, k):
+    say(f"router E={E} H={H} k={k}")
+    bits, w = router(synth.SEED_LAYER, 0, E, H)
+    X = np.stack([synth.activation_f32(synth.SEED_LAYER, t, H) for t in range(8)])
+    ids, gates, logits = rvq.router_topk(w, to_dev(X), k)
+    ids, gates, logits = ids.cpu().numpy(), gates.cpu().numpy(), logits.cpu().numpy()
+    L = oracle.router_logits(bits, X)
+    np.testing.assert_allclose(logits, L, rtol=1e-12, atol=1e-12 * np.abs(L).max())
+    for t in range(X.shape[0]):
+        ids_o, gates_o, _ = oracle.topk(L[t], k)
+        assert np.array_equal(ids[t], ids_o), (t, ids[t], ids_o)
+        np.testing.assert_allclose(gates[t], gates_o, rtol=1e-6)
+
+
+def test_router_bf16_tokens():
+    say("router bf16 x")
+    E, H, k = LAYER_EXPERTS, HIDDEN, TOP_K
+    bits, w = router(synth.SEED_LAYER, 0, E, H)
+    xb = np.stack([synth.activation_bf16_bits(synth.SEED_CHUNK, t, H) for t in range(16)])
+    xt = to_dev(xb.view(np.int16)).view(torch.bfloat16)
+    ids, gates, logits = rvq.router_topk(w, xt, k)
+    L = oracle.router_logits(bits, synth.bf16_bits_to_f32(xb))
+    for t in range(16):
+        ids_o, gates_o, _ = oracle.topk(L[t], k)
+        assert np.array_equal(ids[t].cpu().numpy(), ids_o)
+        np.testing.assert_allclose(gates[t].cpu().numpy(), gates_o, rtol=1e-6)
+
+
+def test_router_exact_ties_and_edge_k():
+    say("router ties")
+    E, H = 12, 32
+    bits = synth.router_bf16_bits(0xE5, 0, E, H)
+    bits[5] = bits[2]          # identical rows -> identical logits -> lower id first
+    bits[9] = bits[2]
+    w = to_dev(bits.view(np.int16)).view(torch.bfloat16)
+    x = synth.activation_f32(0xE5, 0, H)
+    for k in (1, 3, E):
+        ids, gates, logits = rvq.router_topk(w, to_dev(x), k)
+        ids_o, gates_o, _ = oracle.topk(oracle.router_logits(bits, x[None, :])[0], k)
+        assert np.array_equal(ids[0].cpu().numpy(), ids_o)
+        np.testing.assert_allclose(gates[0].cpu().numpy(), gates_o, rtol=1e-6)
+        if k == 1:
+            assert gates[0, 0].item() == 1.0
+    l = logits[0].cpu().numpy()
+    assert l[5] == l[2] == l[9]
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_matches_oracle():
+    say("rmsnorm")
+    X = np.stack([synth.activation_f32(0xF6, t, HIDDEN) * np.float32(0.1 * (t + 1)) for t in range(4)])
+    out = rvq.rmsnorm(to_dev(X), 1e-6).cpu().numpy()
+    for t in range(4):
+        ref = oracle.rmsnorm(X[t].astype(np.float64), 1e-6)
+        assert rel_l2(out[t], ref) <= 1e-6
+
+
+# ---------------------------------------------------------------- one SwiGLU expert (k = 1)
+
+@pytest.fixture(scope="module")
+def expert_bank():
+    say("upload single-expert bank (7168/2048)")
+    bank = upload_bank(synth.SEED_EXPERT, 0, 4)
+    return bank
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_single_expert_decode(expert_bank, dtype):
+    say(f"expert 7168/2048 {dtype}")
+    x = synth.activation_f32(synth.SEED_EXPERT, 0, HIDDEN)
+    for e in (0, 3):
+        ids = torch.tensor([e], dtype=torch.int32, device=DEV)
+        gates = torch.ones(1, dtype=torch.float32, device=DEV)
+        y = rvq.moe_layer_forward(expert_bank, to_dev(x), ids, gates, dtype=dtype).cpu().numpy()
+        ref = oracle.expert(oracle_expert(synth.SEED_EXPERT, 0, e), x)
+        err = rel_l2(y, ref)
+        say(f"  expert {e} rel-L2 {err:.3e}")
+        assert err <= TOL[dtype]
+
+
+def test_single_expert_layer_equals_three_gemvs(expert_bank):
+    """Cross-path: the fused layer (k = 1) and three standalone GEMVs with a host-side SwiGLU agree."""
+    say("expert cross-path")
+    x = to_dev(synth.activation_f32(synth.SEED_EXPERT, 1, HIDDEN))
+    b = expert_bank
+    e = 1
+    def mat(m, rows, cols):
+        off = b.matrix_offset(e, m)
+        return b.codes[off:off + rvq.packed_bytes(rows, cols)], b.codebooks[e, m].contiguous()
+    g = rvq.expert_gemv(*mat(0, INTER, HIDDEN), INTER, HIDDEN, x)
+    u = rvq.expert_gemv(*mat(1, INTER, HIDDEN), INTER, HIDDEN, x)
+    h = (g.double() * torch.sigmoid(g.double()) * u.double()).float()
+    y3 = rvq.expert_gemv(*mat(2, HIDDEN, INTER), HIDDEN, INTER, h)
+    y1 = rvq.moe_layer_forward(b, x, torch.tensor([e], dtype=torch.int32, device=DEV),
+                               torch.ones(1, device=DEV))
+    assert rel_l2(y1.cpu().numpy(), y3.cpu().numpy()) <= 2e-6
+
+
+def test_invalid_expert_id_sets_status_and_is_skipped(expert_bank):
+    say("invalid expert id")
+    x = to_dev(synth.activation_f32(synth.SEED_EXPERT, 2, HIDDEN))
+    ws = rvq.make_moe_workspace(expert_bank, 1, 2, "f32")
+    assert rvq.check_device_status(ws) == 0
+    gates = torch.tensor([0.75, 0.25], device=DEV)
+    y_bad = rvq.moe_layer_forward(expert_bank, x, torch.tensor([2, 99], dtype=torch.int32, device=DEV), gates,
+                                  workspace=ws)
+    assert rvq.check_device_status(ws) == rvq._lib.RVQ_ERR_EXPERT_ID
+    assert rvq.check_device_status(ws) == 0          # cleared
+    y_one = rvq.moe_layer_forward(expert_bank, x, torch.tensor([2], dtype=torch.int32, device=DEV),
+                                  torch.tensor([0.75], device=DEV))
+    assert torch.equal(y_bad, y_one)
+    assert rvq.check_device_status(ws) == 0
+
+
+# ---------------------------------------------------------------- one MoE layer (256 experts, top-16)
+
+@pytest.fixture(scope="module")
+def layer_bank():
+    say("upload 256-expert layer bank (4.2 GB)")
+    bank = upload_bank(synth.SEED_LAYER, 0, LAYER_EXPERTS)
+    bits, w = router(synth.SEED_LAYER, 0, LAYER_EXPERTS, HIDDEN)
+    return bank, bits, w
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_moe_layer_decode(layer_bank, dtype):
+    bank, bits, w = layer_bank
+    ws = rvq.make_moe_workspace(bank, 1, TOP_K, dtype)
+    cache = {}
+    def get(e):
+        if e not in cache:
+            cache[e] = oracle_expert(synth.SEED_LAYER, 0, e)
+        return cache[e]
+    for t in (0, 1):
+        say(f"moe layer token {t} {dtype}")
+        x = synth.activation_f32(synth.SEED_LAYER, t, HIDDEN)
+        r = synth.activation_f32(synth.SEED_LAYER, 1000 + t, HIDDEN)
+        xd = to_dev(x)
+        ids, gates, _ = rvq.router_topk(w, xd, TOP_K)
+        y = rvq.moe_layer_forward(bank, xd, ids[0], gates[0], residual=to_dev(r), dtype=dtype, workspace=ws)
+        y = y.cpu().numpy()
+        y_ref, ids_ref, gates_ref, gaps = oracle.moe_layer(get, bits, x, TOP_K, residual=r)
+        assert np.array_equal(ids[0].cpu().numpy(), ids_ref)
+        np.testing.assert_allclose(gates[0].cpu().numpy(), gates_ref, rtol=1e-6)
+        err = rel_l2(y - r, y_ref - r)           # the MoE part alone
+        say(f"  rel-L2 {err:.3e} (boundary gap {gaps[0]:.2e})")
+        assert err <= TOL[dtype]
+        assert rel_l2(y, y_ref) <= TOL[dtype]
+    assert rvq.check_device_status(ws) == 0
+
+
+def test_moe_layer_is_deterministic(layer_bank):
+    say("moe layer determinism")
+    bank, bits, w = layer_bank
+    x = to_dev(synth.activation_f32(synth.SEED_LAYER, 5, HIDDEN))
+    ids, gates, _ = rvq.router_topk(w, x, TOP_K)
+    a = rvq.moe_layer_forward(bank, x, ids[0], gates[0])
+    b = rvq.moe_layer_forward(bank, x, ids[0], gates[0])
+    assert torch.equal(a, b)
