@@ -1,0 +1,314 @@
+"""Benchmark: one MoE layer, batch-1 decode, top-16 of 256 RVQ experts (7168/2048 SwiGLU), on one MI355X.
+
+A step is one decode token through the whole path: router logits (fp64 accumulate) + top-16 +
+renormalised softmax, then the table-path gate/up kernel, the SwiGLU + down kernel and the gated
+combine, on a token drawn from a pool of 64 seeded tokens (so routing changes every step and the
+256 MB last-level cache cannot hold the experts a step touches).  All 256 experts (4.23 GB of
+3-bit codes) are resident in HBM before timing starts.
+
+Prints ONE JSON line.  Roofline: the dominant kernel (gate/up, two thirds of the code bytes) is
+timed with HIP events recorded around it on its own stream inside the timed region; its
+algorithmic bytes per launch are the code bytes of 16 experts' gate and up matrices plus their
+codebooks.  cpu_baseline: the fp64 oracle on a bounded sample of the same workload.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+METRIC = "MoE-layer decode tokens/s + code-byte HBM GB/s (% of peak), batch 1, top-16"
+HBM_PEAK_GBPS = 8000.0
+E, H, I, K = 256, 7168, 2048, 16
+POOL = 64
+CODE_BYTES_PER_TOKEN = K * 3 * (H * I * 3 // 8)          # 264,241,152
+WEIGHTS_PER_TOKEN = K * 3 * H * I                         # 704,643,072
+GATEUP_CODE_BYTES = K * 2 * (H * I * 3 // 8)              # 176,160,768 per gate/up launch
+GATEUP_CODEBOOK_BYTES = K * 2 * 3 * 256 * 8 * 4           # 786,432
+DOWN_CODE_BYTES = K * (H * I * 3 // 8)
+KERNEL_SOURCES = ["rvq_quantized_moe_amd/csrc/kernels.hip", "rvq_quantized_moe_amd/csrc/device.hpp"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Hip:
+    """Raw HIP event API from the runtime already loaded by torch (events are handed to librvq)."""
+
+    def __init__(self):
+        path = None
+        for line in open("/proc/self/maps"):
+            m = re.search(r"(\S*libamdhip64\.so\S*)", line)
+            if m:
+                path = m.group(1)
+                break
+        self.L = ctypes.CDLL(path or "libamdhip64.so.7")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.L.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return out.value
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(e)
+
+
+def traffic_from_profiles(dtype):
+    """HBM bytes per gate/up launch from the committed rocprofv3 --pmc summary, if it was taken on
+    the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"moe_gateup_{dtype}_layer256_top16_pmc.txt")
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def run_variant(rvq, hip, bank, w, pool, steps, warmup, dtype):
+    import torch
+    dev = pool.device
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    ids = torch.empty((1, K), dtype=torch.int32, device=dev)
+    gates = torch.empty((1, K), dtype=torch.float32, device=dev)
+    logits = torch.empty((1, E), dtype=torch.float64, device=dev)
+    y = torch.empty(H, dtype=torch.float32, device=dev)
+    ws = rvq.make_moe_workspace(bank, 1, K, dtype)
+    L = rvq.lib()
+    d = rvq._lib._table_dtype(dtype)
+    desc = bank.desc()
+    # arguments marshalled once; each step passes the next pool token
+    xptrs = [ctypes.c_void_p(pool[i].data_ptr()) for i in range(POOL)]
+    router_args = lambda xp: (ctypes.c_void_p(w.data_ptr()), xp, rvq.F32, 1, E, H, K, ctypes.c_void_p(ids.data_ptr()),
+                              ctypes.c_void_p(gates.data_ptr()), ctypes.c_void_p(logits.data_ptr()), sptr)
+    rargs = [router_args(xp) for xp in xptrs]
+    margs = [(ctypes.byref(desc), xp, rvq.F32, 1, ctypes.c_void_p(ids.data_ptr()), ctypes.c_void_p(gates.data_ptr()),
+              K, None, ctypes.c_void_p(y.data_ptr()), d, ctypes.c_void_p(ws.data_ptr()), ws.numel(), sptr)
+             for xp in xptrs]
+    n_ev = steps
+    evs = [[hip.event() for _ in range(5)] for _ in range(n_ev)]
+    ev_arrays = [(ctypes.c_void_p * 4)(*ev[1:5]) for ev in evs]
+
+    def step(i, timed):
+        j = i % POOL
+        if timed:
+            hip.record(evs[i][0], sptr)
+        st = L.rvq_router_topk(*rargs[j])
+        if st:
+            raise RuntimeError(rvq.status_string(st))
+        if timed:
+            st = L.rvq_moe_layer_forward_timed(*margs[j], ev_arrays[i])
+        else:
+            st = L.rvq_moe_layer_forward(*margs[j])
+        if st:
+            raise RuntimeError(rvq.status_string(st))
+
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    status = rvq.check_device_status(ws)
+    if status:
+        raise RuntimeError(rvq.status_string(status))
+    router_ms = np.array([hip.ms(ev[0], ev[1]) for ev in evs])
+    gateup_ms = np.array([hip.ms(ev[1], ev[2]) for ev in evs])
+    down_ms = np.array([hip.ms(ev[2], ev[3]) for ev in evs])
+    comb_ms = np.array([hip.ms(ev[3], ev[4]) for ev in evs])
+    for ev in evs:
+        for e in ev:
+            hip.destroy(e)
+    elapsed = t1 - t0
+    tok_s = steps / elapsed
+    gu_s = float(np.mean(gateup_ms)) * 1e-3
+    return {
+        "tokens_per_s": tok_s,
+        "ms_per_step": elapsed / steps * 1e3,
+        "code_GBps": CODE_BYTES_PER_TOKEN * tok_s / 1e9,
+        "code_frac_of_hbm_peak": CODE_BYTES_PER_TOKEN * tok_s / 1e9 / HBM_PEAK_GBPS,
+        "decoded_weights_per_s": WEIGHTS_PER_TOKEN * tok_s,
+        "kernel_us": {"router_topk": float(np.mean(router_ms)) * 1e3, "gateup": float(np.mean(gateup_ms)) * 1e3,
+                      "swiglu_down": float(np.mean(down_ms)) * 1e3, "combine": float(np.mean(comb_ms)) * 1e3,
+                      "gateup_p10": float(np.percentile(gateup_ms, 10)) * 1e3,
+                      "gateup_p90": float(np.percentile(gateup_ms, 90)) * 1e3},
+        "gateup_GBps": (GATEUP_CODE_BYTES + GATEUP_CODEBOOK_BYTES) / gu_s / 1e9,
+        "down_GBps": DOWN_CODE_BYTES / (float(np.mean(down_ms)) * 1e-3) / 1e9,
+    }
+
+
+def stream_copy_peak(torch, dev):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 10
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del a, b
+    return 2 * n / dt / 1e9
+
+
+def cpu_baseline(budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample: whole tokens of the same layer."""
+    import oracle
+    import synth
+    from workloads import oracle_expert
+    bits = synth.router_bf16_bits(synth.SEED_LAYER, 0, E, H)
+    cache = {}
+
+    def get(e):
+        if e not in cache:
+            cache[e] = oracle_expert(synth.SEED_LAYER, 0, e)
+        return cache[e]
+
+    n, busy = 0, 0.0
+    while n == 0 or (busy < budget_s and n < POOL):
+        x = synth.activation_f32(synth.SEED_LAYER, n, H)
+        # the codes of the selected experts are regenerated outside the timed part
+        l = oracle.router_logits(bits, x[None, :])[0]
+        for e in oracle.topk(l, K)[0]:
+            get(int(e))
+        t0 = time.perf_counter()
+        oracle.moe_layer(get, bits, x, K)
+        busy += time.perf_counter() - t0
+        n += 1
+        if len(cache) > 64:
+            cache.clear()
+    return {"value": n / busy, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{n} decode tokens of the same 256-expert top-16 layer (router + 16 full experts, "
+                      f"all 7168 outputs), fp64, {busy:.1f} s of CPU time; input generation excluded",
+            "code_GBps": CODE_BYTES_PER_TOKEN * n / busy / 1e9,
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--dtype", choices=["f32", "f16"], default="f32", help="table precision of the headline run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip the other table precision")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sharded design is described in DESIGN.md, not run)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rvq_quantized_moe_amd as rvq
+    import synth
+    from workloads import router, upload_bank
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] uploading 256-expert bank ({E} x 16.5 MB)", file=sys.stderr, flush=True)
+    bank = upload_bank(synth.SEED_LAYER, 0, E, H, I, device=dev)
+    _, w = router(synth.SEED_LAYER, 0, E, H, device=dev)
+    pool = torch.from_numpy(np.stack([synth.activation_f32(synth.SEED_LAYER, t, H) for t in range(POOL)])).to(dev)
+    hip = Hip()
+    print("[bench] stream copy peak", file=sys.stderr, flush=True)
+    copy_gbps = stream_copy_peak(torch, dev)
+    print(f"[bench] timing {args.steps} steps ({args.dtype} tables)", file=sys.stderr, flush=True)
+    main_res = run_variant(rvq, hip, bank, w, pool, args.steps, args.warmup, args.dtype)
+    variants = {}
+    if not args.no_variants:
+        other = "f16" if args.dtype == "f32" else "f32"
+        print(f"[bench] timing {args.steps} steps ({other} tables)", file=sys.stderr, flush=True)
+        variants[other] = run_variant(rvq, hip, bank, w, pool, args.steps, args.warmup, other)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args.cpu_budget)
+
+    gu_us = main_res["kernel_us"]["gateup"]
+    achieved = (GATEUP_CODE_BYTES + GATEUP_CODEBOOK_BYTES) / (gu_us * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {"workload": "moe_layer_decode", "experts": E, "hidden": H, "inter": I, "top_k": K, "batch": 1,
+                   "table_dtype": args.dtype, "accumulate": "f32", "router_accumulate": "f64",
+                   "resident_code_bytes": E * 3 * (H * I * 3 // 8), "token_pool": POOL},
+        "code_GBps": main_res["code_GBps"],
+        "code_frac_of_hbm_peak": main_res["code_frac_of_hbm_peak"],
+        "code_frac_of_stream_copy": main_res["code_GBps"] / copy_gbps,
+        "stream_copy_GBps": copy_gbps,
+        "decoded_weights_per_s": main_res["decoded_weights_per_s"],
+        "kernel_us": main_res["kernel_us"],
+        "roofline": {"bound": "hbm", "kernel": f"k_moe_gateup_{args.dtype}", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic_from_profiles(args.dtype),
+                     "algorithmic_bytes_per_launch": GATEUP_CODE_BYTES + GATEUP_CODEBOOK_BYTES},
+        "cpu_baseline": cpu,
+        "variants": variants,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

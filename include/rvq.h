@@ -169,6 +169,16 @@ int rvq_moe_layer_forward(const rvq_expert_bank_t *bank, const void *x, int32_t 
                           const int32_t *ids, const float *gates, int32_t k, const float *residual, float *y,
                           int32_t compute_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Same as rvq_moe_layer_forward, and records events[0..3] on `stream`
+ * around its kernels: [0] before the gate/up table kernel, [1] between it
+ * and the SwiGLU+down kernel, [2] before the gated combine, [3] after it, so
+ * a caller can time each kernel with hipEventElapsedTime.  events: host array
+ * of 4 caller-created events (none NULL). */
+int rvq_moe_layer_forward_timed(const rvq_expert_bank_t *bank, const void *x, int32_t x_dtype, int32_t T,
+                                const int32_t *ids, const float *gates, int32_t k, const float *residual, float *y,
+                                int32_t compute_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t *events);
+
 /* Zero-fill a workspace (with a kernel, so the call can be graph-captured). */
 int rvq_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
 

@@ -41,7 +41,8 @@ _lib = None
 EXPORTS = [
     "rvq_status_string", "rvq_packed_bytes", "rvq_pack_codes", "rvq_lut_build",
     "rvq_expert_gemv_workspace_bytes", "rvq_expert_gemv", "rvq_router_topk", "rvq_bank_record_bytes",
-    "rvq_moe_layer_workspace_bytes", "rvq_moe_layer_forward", "rvq_workspace_init", "rvq_rmsnorm",
+    "rvq_moe_layer_workspace_bytes", "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed",
+    "rvq_workspace_init", "rvq_rmsnorm",
     "rvq_check_device_status",
 ]
 
@@ -70,11 +71,13 @@ def lib():
         L.rvq_moe_layer_workspace_bytes.argtypes = [ctypes.POINTER(BankDesc), i32, i32, i32]
         L.rvq_moe_layer_workspace_bytes.restype = sz
         L.rvq_moe_layer_forward.argtypes = [ctypes.POINTER(BankDesc), p, i32, i32, p, p, i32, p, p, i32, p, sz, p]
+        L.rvq_moe_layer_forward_timed.argtypes = [ctypes.POINTER(BankDesc), p, i32, i32, p, p, i32, p, p, i32, p,
+                                                  sz, p, ctypes.POINTER(ctypes.c_void_p)]
         L.rvq_workspace_init.argtypes = [p, sz, p]
         L.rvq_rmsnorm.argtypes = [p, i32, i32, ctypes.c_float, p, p]
         L.rvq_check_device_status.argtypes = [p, p]
         for name in ("rvq_pack_codes", "rvq_lut_build", "rvq_expert_gemv", "rvq_router_topk",
-                     "rvq_moe_layer_forward", "rvq_workspace_init", "rvq_rmsnorm", "rvq_check_device_status"):
+                     "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed", "rvq_workspace_init", "rvq_rmsnorm", "rvq_check_device_status"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -266,8 +269,10 @@ def make_moe_workspace(bank, T=1, k=16, dtype="f32"):
     return ws
 
 
-def moe_layer_forward(bank, x, ids, gates, residual=None, dtype="f32", y=None, workspace=None):
-    """y = [residual +] sum_i gates[i] * expert_{ids[i]}(x) for one decode token (x fp32 [H])."""
+def moe_layer_forward(bank, x, ids, gates, residual=None, dtype="f32", y=None, workspace=None, events=None):
+    """y = [residual +] sum_i gates[i] * expert_{ids[i]}(x) for one decode token (x fp32 [H]).
+
+    events: optional sequence of 4 raw hipEvent_t handles recorded around the layer's kernels."""
     _dev(x, torch.float32, "x")
     _dev(ids, torch.int32, "ids")
     _dev(gates, torch.float32, "gates")
@@ -281,6 +286,11 @@ def moe_layer_forward(bank, x, ids, gates, residual=None, dtype="f32", y=None, w
     if workspace is None:
         workspace = make_moe_workspace(bank, T, k, d)
     desc = bank.desc()
-    _check(lib().rvq_moe_layer_forward(ctypes.byref(desc), _ptr(x), F32, T, _ptr(ids), _ptr(gates), k,
-                                       _ptr(residual), _ptr(y), d, _ptr(workspace), workspace.numel(), _stream(x)))
+    args = (ctypes.byref(desc), _ptr(x), F32, T, _ptr(ids), _ptr(gates), k, _ptr(residual), _ptr(y), d,
+            _ptr(workspace), workspace.numel(), _stream(x))
+    if events is None:
+        _check(lib().rvq_moe_layer_forward(*args))
+    else:
+        arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(int(e)) for e in events])
+        _check(lib().rvq_moe_layer_forward_timed(*args, arr))
     return y

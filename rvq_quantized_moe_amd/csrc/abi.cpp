@@ -116,9 +116,11 @@ size_t rvq_moe_layer_workspace_bytes(const rvq_expert_bank_t* bank, int32_t T, i
   return moe_workspace_layout(bank->hidden, bank->inter, k, compute_dtype == RVQ_F16).total;
 }
 
-int rvq_moe_layer_forward(const rvq_expert_bank_t* bank, const void* x, int32_t x_dtype, int32_t T,
-                          const int32_t* ids, const float* gates, int32_t k, const float* residual, float* y,
-                          int32_t compute_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+int moe_layer_forward_impl(const rvq_expert_bank_t* bank, const void* x, int32_t x_dtype, int32_t T,
+                           const int32_t* ids, const float* gates, int32_t k, const float* residual, float* y,
+                           int32_t compute_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           hipEvent_t* events) {
   int st = check_bank(bank);
   if (st != RVQ_OK) return st;
   if (!x || !ids || !gates || !y || !workspace) return RVQ_ERR_NULL;
@@ -131,7 +133,26 @@ int rvq_moe_layer_forward(const rvq_expert_bank_t* bank, const void* x, int32_t 
   if (workspace_bytes < moe_workspace_layout(bank->hidden, bank->inter, k, f16).total) return RVQ_ERR_WORKSPACE;
   return hip_status(launch_moe_decode(bank->codes, bank->codebooks, bank->record_stride, bank->num_experts,
                                       bank->hidden, bank->inter, static_cast<const float*>(x), ids, gates, k,
-                                      residual, y, f16, workspace, stream));
+                                      residual, y, f16, workspace, stream, events));
+}
+}  // namespace
+
+int rvq_moe_layer_forward(const rvq_expert_bank_t* bank, const void* x, int32_t x_dtype, int32_t T,
+                          const int32_t* ids, const float* gates, int32_t k, const float* residual, float* y,
+                          int32_t compute_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return moe_layer_forward_impl(bank, x, x_dtype, T, ids, gates, k, residual, y, compute_dtype, workspace,
+                                workspace_bytes, stream, nullptr);
+}
+
+int rvq_moe_layer_forward_timed(const rvq_expert_bank_t* bank, const void* x, int32_t x_dtype, int32_t T,
+                                const int32_t* ids, const float* gates, int32_t k, const float* residual, float* y,
+                                int32_t compute_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t* events) {
+  if (!events) return RVQ_ERR_NULL;
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return RVQ_ERR_NULL;
+  return moe_layer_forward_impl(bank, x, x_dtype, T, ids, gates, k, residual, y, compute_dtype, workspace,
+                                workspace_bytes, stream, events);
 }
 
 int rvq_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {

@@ -31,7 +31,8 @@ constexpr int kSlabBytes = 3 * kSlabGroups * kSlabRows;       // 3072
 constexpr int kEntries = 256;                                 // codebook entries per stage
 constexpr int kCodebookFloats = 3 * kEntries * 8;             // 6144 floats per matrix
 constexpr int kLutBytes = 49152;                              // per-workgroup table tile
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;                                // threads of a table-path workgroup (8 waves)
+constexpr int kWaves = kThreads / 64;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -64,13 +65,16 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
-__device__ inline float block_max(float v, float* red4) {
+__device__ inline float block_max(float v, float* red) {
   v = wave_max(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
-  if (lane == 0) red4[wave] = v;
+  if (lane == 0) red[wave] = v;
   __syncthreads();
-  return fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
+  float m = red[0];
+  const int nw = blockDim.x >> 6;
+  for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
+  return m;
 }
 
 // Power-of-two exponent e with bound * 2^-e < 2^15 (so every fp16 table entry,
@@ -90,7 +94,7 @@ __device__ inline int f16_table_exponent(float bound) {
 // Entry (g, s, c) goes to lut[(3g + s) * 256 + c], scaled by `scale` (a power of two; 1 for fp32).
 template <bool F16>
 __device__ __forceinline__ void load_codebook_entry(const float* __restrict__ cb, float (&cv)[3][8]) {
-  const int c = threadIdx.x;
+  const int c = threadIdx.x & (kEntries - 1);
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(cb + (s * kEntries + c) * 8);
@@ -100,12 +104,14 @@ __device__ __forceinline__ void load_codebook_entry(const float* __restrict__ cb
   }
 }
 
+// With kThreads = 512 the two halves of the workgroup build alternate groups.
 template <bool F16>
 __device__ __forceinline__ void build_tile(typename Tile<F16>::entry_t* lut, const float (&cv)[3][8],
                                            const float* vs, float scale) {
-  const int c = threadIdx.x;
+  const int c = threadIdx.x & (kEntries - 1);
+  const int half = threadIdx.x >> 8;
 #pragma unroll 4
-  for (int g = 0; g < Tile<F16>::kGroups; ++g) {
+  for (int g = half; g < Tile<F16>::kGroups; g += kThreads / kEntries) {
     float xv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) xv[j] = vs[g * 8 + j];
@@ -175,14 +181,18 @@ struct SlabData {
   u32x4 d[6];
 };
 
+// Loads one row block (48 code bytes per lane, or 96 with fp16 tables) of slab base(s) s0/s1 at
+// byte offset `off` (< 4 GiB; lane part included): uniform 64-bit base + 32-bit lane offset, so
+// the address costs one VGPR.
 template <bool F16>
-__device__ __forceinline__ void load_slabs(SlabData& s, const uint8_t* __restrict__ p0, const uint8_t* __restrict__ p1) {
-  const u32x4* a = reinterpret_cast<const u32x4*>(p0);
+__device__ __forceinline__ void load_slabs(SlabData& s, const uint8_t* __restrict__ s0, const uint8_t* __restrict__ s1,
+                                           uint32_t off) {
+  const u32x4* a = reinterpret_cast<const u32x4*>(s0 + off);
   s.d[0] = __builtin_nontemporal_load(a);
   s.d[1] = __builtin_nontemporal_load(a + 64);
   s.d[2] = __builtin_nontemporal_load(a + 128);
   if constexpr (F16) {
-    const u32x4* b = reinterpret_cast<const u32x4*>(p1);
+    const u32x4* b = reinterpret_cast<const u32x4*>(s1 + off);
     s.d[3] = __builtin_nontemporal_load(b);
     s.d[4] = __builtin_nontemporal_load(b + 64);
     s.d[5] = __builtin_nontemporal_load(b + 128);
@@ -209,35 +219,83 @@ __device__ __forceinline__ float gather_slabs(const void* lut, const SlabData& s
   return acc;
 }
 
-// Streams row blocks [rb_begin, rb_end) of K-tile `tile` of one packed matrix through the tables
-// in `lut`, writing out[row] = out_scale * (sum over the tile) for rows < rows.  Waves take row
-// blocks round-robin; each wave keeps the next block's loads in flight while it gathers.
-template <bool F16>
-__device__ __forceinline__ void stream_tile(const void* lut, const uint8_t* __restrict__ codes, int nrb, int nt16,
-                                            int tile, int rb_begin, int rb_end, int rows, float out_scale,
-                                            float* __restrict__ out) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  int rb = rb_begin + wave;
-  if (rb >= rb_end) return;
-  const int slab0 = tile * Tile<F16>::kSlabs;
-  // the second slab of an fp16 tile may not exist (odd slab count): its tables are all zero then,
-  // so any valid code bytes do; re-read slab0 to stay in bounds.
-  const int slab1 = F16 ? (slab0 + 1 < nt16 ? slab0 + 1 : slab0) : slab0;
-  const uint8_t* base0 = codes + (int64_t)slab0 * nrb * kSlabBytes + lane * 16;
-  const uint8_t* base1 = codes + (int64_t)slab1 * nrb * kSlabBytes + lane * 16;
-  SlabData cur, nxt;
-  load_slabs<F16>(cur, base0 + (int64_t)rb * kSlabBytes, base1 + (int64_t)rb * kSlabBytes);
-  for (;;) {
-    const int nx = rb + nwaves;
-    const int pf = nx < rb_end ? nx : rb;
-    load_slabs<F16>(nxt, base0 + (int64_t)pf * kSlabBytes, base1 + (int64_t)pf * kSlabBytes);
-    const float acc = gather_slabs<F16>(lut, cur);
-    const int row = rb * kSlabRows + lane;
-    if (row < rows) out[row] = acc * out_scale;
-    if (nx >= rb_end) break;
-    rb = nx;
-    cur = nxt;
+// Streams row blocks [rb_begin, rb_end) of K-tile `tile` of one packed matrix through the tables in
+// LDS, writing out[row] = out_scale * (sum over the tile) for every row of those blocks (`out` has
+// its rows padded to a multiple of 64, so stores need no guard).  Waves take row blocks
+// round-robin.  Each wave keeps NB row blocks of codes in registers: the buffer just gathered is
+// refilled with the block NB steps ahead before the next buffer is gathered, so NB-1 blocks are
+// always in flight; buffers rotate by unrolling, never by register copies.  begin() issues the
+// first loads and may be called before the tables are built, so the first HBM round trip overlaps
+// the build.
+//
+// BPW > 0: every wave streams exactly BPW row blocks (the launcher checked this), so the loop is
+// straight-line code and the compiler's memory-counter waits are exact: a gather waits only for its
+// own buffer.  BPW == 0: any range, with data-dependent loads (correct, but the waits are
+// conservative, which costs overlap).
+template <bool F16, int BPW>
+struct RowStream {
+  static constexpr int kDepth = F16 ? 2 : 3;   // 12 KiB / 9 KiB of codes per wave in registers
+  static constexpr int NB = (BPW > 0 && BPW < kDepth) ? BPW : kDepth;
+  SlabData buf[NB];
+  const uint8_t* s0;       // slab bases of this tile (uniform)
+  const uint8_t* s1;
+  uint32_t lane_off;       // lane * 16
+  int rb, step, rb_end;    // wave-uniform
+
+  __device__ __forceinline__ void load(int i, int b) {
+    load_slabs<F16>(buf[i], s0, s1, (uint32_t)b * kSlabBytes + lane_off);
   }
-}
+
+  __device__ __forceinline__ void begin(const uint8_t* __restrict__ codes, int nrb, int nt16, int tile, int rb_begin,
+                                        int rb_end_) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    lane_off = (threadIdx.x & 63) * 16;
+    step = blockDim.x >> 6;
+    rb = rb_begin + wave;
+    rb_end = rb_end_;
+    const int slab0 = tile * Tile<F16>::kSlabs;
+    // the second slab of an fp16 tile may not exist (odd slab count): its tables are all zero then,
+    // so any valid code bytes do; re-read slab0 to stay in bounds.
+    const int slab1 = F16 ? (slab0 + 1 < nt16 ? slab0 + 1 : slab0) : slab0;
+    s0 = codes + (int64_t)slab0 * nrb * kSlabBytes;
+    s1 = codes + (int64_t)slab1 * nrb * kSlabBytes;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if constexpr (BPW > 0) {
+        load(i, rb + i * step);
+      } else {
+        if (rb + i * step < rb_end) load(i, rb + i * step);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void run(const void* lut, float out_scale, float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (BPW > 0) {
+#pragma unroll
+      for (int j = 0; j < BPW; ++j) {
+        const float acc = gather_slabs<F16>(lut, buf[j % NB]);
+        if (j + NB < BPW) load(j % NB, rb + (j + NB) * step);
+        out[(rb + j * step) * kSlabRows + lane] = acc * out_scale;
+      }
+    } else {
+      if (rb >= rb_end) return;
+      for (;;) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const float acc = gather_slabs<F16>(lut, buf[i]);
+          const int nb = rb + NB * step;
+          if (nb < rb_end) load(i, nb);
+          out[rb * kSlabRows + lane] = acc * out_scale;
+          rb += step;
+          if (rb >= rb_end) return;
+        }
+      }
+    }
+  }
+};
+
+// Row blocks per wave that have a straight-line specialisation.
+__host__ __device__ constexpr bool fixed_bpw(int b) { return b == 1 || b == 2 || b == 4 || b == 7 || b == 8 || b == 14; }
 
 }  // namespace rvq

@@ -131,13 +131,11 @@ hipError_t launch_lut_build(const float* x, int cols, const float* cb, bool half
 // Shared prologue of every table-path workgroup: stage the tile's activation values `vs` (already
 // in LDS), choose the fp16 exponent, build the tables.  Returns the output scale 2^e.
 template <bool F16>
-__device__ __forceinline__ float tile_tables(typename Tile<F16>::entry_t* lut, const float* __restrict__ cb,
+__device__ __forceinline__ float tile_tables(typename Tile<F16>::entry_t* lut, const float (&cv)[3][8],
                                              const float* vs, float my_v, float* red) {
-  float cv[3][8];
-  load_codebook_entry<F16>(cb, cv);
   float scale = 1.f, out_scale = 1.f;
   if constexpr (F16) {
-    // my_v = this thread's element of the tile vector (threads 0..255 cover the 32 groups)
+    // my_v = this thread's element of the tile vector (threads 0..8G-1; zero elsewhere)
     const float xmax2 = block_max(group_norm2(my_v), red);
     const float cmax2 = block_max(codebook_norm2(cv), red);
     const int e = f16_table_exponent(sqrtf(cmax2) * sqrtf(xmax2));
@@ -149,38 +147,82 @@ __device__ __forceinline__ float tile_tables(typename Tile<F16>::entry_t* lut, c
   return out_scale;
 }
 
+// Occupancy of the table kernels: with fp32 tables three 8-wave workgroups per CU (LDS allows
+// three), i.e. at most 512/6 VGPRs per lane; fp16 tables keep twice the code bytes in registers per
+// row block and run two workgroups per CU.
+#define RVQ_OCC_F32 __attribute__((amdgpu_waves_per_eu(6, 8)))
+#define RVQ_OCC_F16 __attribute__((amdgpu_waves_per_eu(4, 8)))
+
 // =============================================================================================
-// Single-matrix GEMV.  Grid: (tiles, parts).  part[t][row] = tile t's contribution.
-template <bool F16>
-__global__ __launch_bounds__(256) void k_gemv_tiles(const uint8_t* __restrict__ codes, const float* __restrict__ cb,
-                                                    int rows, int cols, const float* __restrict__ x,
-                                                    float* __restrict__ part, int nparts) {
+// Dispatch of the row-blocks-per-wave specialisation (see RowStream).
+#define RVQ_BPW_DISPATCH(bpw, ...)                 \
+  switch (bpw) {                                   \
+    case 1: { constexpr int B = 1; __VA_ARGS__; } break;   \
+    case 2: { constexpr int B = 2; __VA_ARGS__; } break;   \
+    case 4: { constexpr int B = 4; __VA_ARGS__; } break;   \
+    case 7: { constexpr int B = 7; __VA_ARGS__; } break;   \
+    case 8: { constexpr int B = 8; __VA_ARGS__; } break;   \
+    case 14: { constexpr int B = 14; __VA_ARGS__; } break; \
+    default: { constexpr int B = 0; __VA_ARGS__; } break;  \
+  }
+
+// Straight-line specialisation usable when `nparts` workgroups split nrb row blocks evenly over
+// their waves; 0 (the general loop) otherwise.
+static int pick_bpw(int nrb, int nparts) {
+  if (nrb % nparts != 0) return 0;
+  const int per = nrb / nparts;
+  if (per % kWaves != 0) return 0;
+  return fixed_bpw(per / kWaves) ? per / kWaves : 0;
+}
+
+__host__ __device__ inline int64_t pad_rows(int64_t rows) { return cdiv(rows, kSlabRows) * kSlabRows; }
+
+// =============================================================================================
+// Single-matrix GEMV.  Grid: (tiles, parts).  part[t][row] = tile t's contribution (rows padded).
+template <bool F16, int BPW>
+__device__ __forceinline__ void k_gemv_tiles_body(const uint8_t* __restrict__ codes, const float* __restrict__ cb,
+                                                         int rows, int cols, const float* __restrict__ x,
+                                                         float* __restrict__ part, int nparts) {
   constexpr int G = Tile<F16>::kGroups;
   __shared__ __attribute__((aligned(16))) typename Tile<F16>::entry_t lut[kLutBytes / sizeof(typename Tile<F16>::entry_t)];
   __shared__ float vs[256];
-  __shared__ float red[4];
+  __shared__ float red[kWaves];
   const int tile = blockIdx.x, p = blockIdx.y;
   const int groups = cols / 8;
   const int nt16 = (int)cdiv(groups, kSlabGroups);
   const int nrb = (int)cdiv(rows, kSlabRows);
   const int i = threadIdx.x;
   const int k0 = tile * G * 8;
-  const float v = (i < G * 8 && k0 + i < cols) ? x[k0 + i] : 0.f;
-  if (i < G * 8) vs[i] = v;
-  __syncthreads();
-  const float out_scale = tile_tables<F16>(lut, cb, vs, v, red);
   const int per = (int)cdiv(nrb, nparts);
   const int rb0 = p * per;
   const int rb1 = rb0 + per < nrb ? rb0 + per : nrb;
-  stream_tile<F16>(lut, codes, nrb, nt16, tile, rb0, rb1, rows, out_scale, part + (int64_t)tile * rows);
+  // loads the tables need are issued before the code prefetch: waits on memory counters are in order
+  const float v = (i < G * 8 && k0 + i < cols) ? x[k0 + i] : 0.f;
+  float cv[3][8];
+  load_codebook_entry<F16>(cb, cv);
+  RowStream<F16, BPW> rs;
+  rs.begin(codes, nrb, nt16, tile, rb0, rb1);
+  if (i < G * 8) vs[i] = v;
+  __syncthreads();
+  const float out_scale = tile_tables<F16>(lut, cv, vs, v, red);
+  rs.run(lut, out_scale, part + (int64_t)tile * pad_rows(rows));
+}
+
+template <int BPW>
+__global__ __launch_bounds__(kThreads) RVQ_OCC_F32 void k_gemv_tiles_f32(const uint8_t* __restrict__ codes, const float* __restrict__ cb, int rows, int cols, const float* __restrict__ x, float* __restrict__ part, int nparts) {
+  k_gemv_tiles_body<false, BPW>(codes, cb, rows, cols, x, part, nparts);
+}
+template <int BPW>
+__global__ __launch_bounds__(kThreads) RVQ_OCC_F16 void k_gemv_tiles_f16(const uint8_t* __restrict__ codes, const float* __restrict__ cb, int rows, int cols, const float* __restrict__ x, float* __restrict__ part, int nparts) {
+  k_gemv_tiles_body<true, BPW>(codes, cb, rows, cols, x, part, nparts);
 }
 
 __global__ __launch_bounds__(256) void k_sum_tiles(const float* __restrict__ part, int ntiles, int rows,
-                                                   float* __restrict__ y) {
+                                                   int64_t stride, float* __restrict__ y) {
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= rows) return;
   float acc = 0.f;
-  for (int t = 0; t < ntiles; ++t) acc += part[(int64_t)t * rows + r];
+  for (int t = 0; t < ntiles; ++t) acc += part[(int64_t)t * stride + r];
   y[r] = acc;
 }
 
@@ -189,7 +231,7 @@ int gemv_tiles(int cols, bool f16) {
 }
 
 size_t gemv_workspace_bytes(int rows, int cols, bool f16) {
-  return (size_t)gemv_tiles(cols, f16) * (size_t)rows * sizeof(float);
+  return (size_t)gemv_tiles(cols, f16) * (size_t)pad_rows(rows) * sizeof(float);
 }
 
 hipError_t launch_gemv(const uint8_t* codes, const float* cb, int rows, int cols, const float* x, bool f16,
@@ -198,17 +240,20 @@ hipError_t launch_gemv(const uint8_t* codes, const float* cb, int rows, int cols
   const int nrb = (int)cdiv(rows, kSlabRows);
   // enough workgroups to cover the chip: split rows when there are few tiles
   int nparts = 1;
-  while (nt * nparts < 512 && (nparts * 2) * 4 <= nrb) nparts *= 2;
+  while (nt * nparts < 512 && (nparts * 2) * kWaves <= nrb) nparts *= 2;
   float* part = static_cast<float*>(ws);
-  if (f16)
-    hipLaunchKernelGGL(k_gemv_tiles<true>, dim3(nt, nparts), dim3(256), 0, stream, codes, cb, rows, cols, x, part,
-                       nparts);
-  else
-    hipLaunchKernelGGL(k_gemv_tiles<false>, dim3(nt, nparts), dim3(256), 0, stream, codes, cb, rows, cols, x, part,
-                       nparts);
+  const int bpw = pick_bpw(nrb, nparts);
+  if (f16) {
+    RVQ_BPW_DISPATCH(bpw, hipLaunchKernelGGL((k_gemv_tiles_f16<B>), dim3(nt, nparts), dim3(kThreads), 0, stream,
+                                             codes, cb, rows, cols, x, part, nparts))
+  } else {
+    RVQ_BPW_DISPATCH(bpw, hipLaunchKernelGGL((k_gemv_tiles_f32<B>), dim3(nt, nparts), dim3(kThreads), 0, stream,
+                                             codes, cb, rows, cols, x, part, nparts))
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_sum_tiles, dim3((unsigned)cdiv(rows, 256)), dim3(256), 0, stream, part, nt, rows, y);
+  hipLaunchKernelGGL(k_sum_tiles, dim3((unsigned)cdiv(rows, 256)), dim3(256), 0, stream, part, nt, rows,
+                     (int64_t)pad_rows(rows), y);
   return hipGetLastError();
 }
 
@@ -220,32 +265,55 @@ __device__ inline double x_to_f64(float v) { return (double)v; }
 __device__ inline double x_to_f64(uint16_t v) { return bf16_to_f64(v); }
 
 template <typename XT>
+__device__ __forceinline__ void load8(const XT* p, double (&xv)[8]);
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, double (&xv)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w; xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, double (&xv)[8]) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    xv[2 * j] = bf16_to_f64((uint16_t)(a[j] & 0xffffu));
+    xv[2 * j + 1] = bf16_to_f64((uint16_t)(a[j] >> 16));
+  }
+}
+
+// One workgroup per (expert, token): 256 threads stride over H in 8-element (16/32-byte) pieces
+// with two fp64 accumulators each, then a fixed-order reduction.
+template <typename XT>
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ w, const XT* __restrict__ x, int T,
                                                        int E, int H, double* __restrict__ logits, int vec) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int t = blockIdx.y;
-  if (e >= E) return;
+  __shared__ double red[4];
+  const int e = blockIdx.x, t = blockIdx.y;
   const uint16_t* wr = w + (int64_t)e * H;
   const XT* xr = x + (int64_t)t * H;
-  double acc = 0.0;
+  double a0 = 0.0, a1 = 0.0;
   int h0 = 0;
   if (vec) {
     const int n8 = H / 8;
-    for (int q = lane; q < n8; q += 64) {
+    for (int q = threadIdx.x; q < n8; q += 256) {
       const u32x4 wv = *reinterpret_cast<const u32x4*>(wr + q * 8);
+      double xv[8];
+      load8<XT>(xr + q * 8, xv);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc = fma(bf16_to_f64((uint16_t)(wv[j] & 0xffffu)), x_to_f64(xr[q * 8 + 2 * j]), acc);
-        acc = fma(bf16_to_f64((uint16_t)(wv[j] >> 16)), x_to_f64(xr[q * 8 + 2 * j + 1]), acc);
+        a0 = fma(bf16_to_f64((uint16_t)(wv[j] & 0xffffu)), xv[2 * j], a0);
+        a1 = fma(bf16_to_f64((uint16_t)(wv[j] >> 16)), xv[2 * j + 1], a1);
       }
     }
     h0 = n8 * 8;
   }
-  for (int h = h0 + lane; h < H; h += 64) acc = fma(bf16_to_f64(wr[h]), x_to_f64(xr[h]), acc);
+  for (int h = h0 + threadIdx.x; h < H; h += 256) a0 = fma(bf16_to_f64(wr[h]), x_to_f64(xr[h]), a0);
+  double acc = a0 + a1;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) logits[(int64_t)t * E + e] = acc;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) logits[(int64_t)t * E + e] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 // Top-k by (logit desc, id asc): the rank of e is the number of experts that precede it in that
@@ -280,8 +348,9 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
 
 hipError_t launch_router_topk(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, int k, int32_t* ids,
                               float* gates, double* logits, hipStream_t stream) {
-  const int vec = (H % 8 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0);
-  dim3 grid((unsigned)cdiv(E, 4), (unsigned)T);
+  const int vec = (H % 8 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0) &&
+                  ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  dim3 grid((unsigned)E, (unsigned)T);
   if (x_bf16)
     hipLaunchKernelGGL(k_router_logits<uint16_t>, grid, dim3(256), 0, stream, w, static_cast<const uint16_t*>(x), T,
                        E, H, logits, vec);
@@ -330,14 +399,14 @@ struct BankArgs {
   int E, H, I;
 };
 
-template <bool F16>
-__global__ __launch_bounds__(256) void k_moe_gateup(BankArgs bank, const float* __restrict__ x,
+template <bool F16, int BPW>
+__device__ __forceinline__ void k_moe_gateup_body(BankArgs bank, const float* __restrict__ x,
                                                     const int32_t* __restrict__ ids, float* __restrict__ part_gu,
                                                     int32_t* __restrict__ status) {
   constexpr int G = Tile<F16>::kGroups;
   __shared__ __attribute__((aligned(16))) typename Tile<F16>::entry_t lut[kLutBytes / sizeof(typename Tile<F16>::entry_t)];
   __shared__ float vs[256];
-  __shared__ float red[4];
+  __shared__ float red[kWaves];
   const int H = bank.H, I = bank.I;
   const int groups = H / 8;
   const int nt = (int)cdiv(groups, G);
@@ -351,26 +420,42 @@ __global__ __launch_bounds__(256) void k_moe_gateup(BankArgs bank, const float* 
   }
   const uint8_t* codes = bank.codes + (int64_t)e * bank.stride + (int64_t)m * packed_bytes(I, H);
   const float* cb = bank.cb + ((int64_t)e * 3 + m) * kCodebookFloats;
-  const int i = threadIdx.x;
-  const int k0 = tile * G * 8;
-  const float v = (i < G * 8 && k0 + i < H) ? x[k0 + i] : 0.f;
-  if (i < G * 8) vs[i] = v;
-  __syncthreads();
-  const float out_scale = tile_tables<F16>(lut, cb, vs, v, red);
   const int nrb = (int)cdiv(I, kSlabRows);
   const int nt16 = (int)cdiv(groups, kSlabGroups);
-  stream_tile<F16>(lut, codes, nrb, nt16, tile, 0, nrb, I, out_scale,
-                   part_gu + (((int64_t)slot * 2 + m) * nt + tile) * I);
+  const int i = threadIdx.x;
+  const int k0 = tile * G * 8;
+  // loads the tables need are issued before the code prefetch: waits on memory counters are in order
+  const float v = (i < G * 8 && k0 + i < H) ? x[k0 + i] : 0.f;
+  float cv[3][8];
+  load_codebook_entry<F16>(cb, cv);
+  RowStream<F16, BPW> rs;
+  rs.begin(codes, nrb, nt16, tile, 0, nrb);
+  if (i < G * 8) vs[i] = v;
+  __syncthreads();
+  const float out_scale = tile_tables<F16>(lut, cv, vs, v, red);
+  rs.run(lut, out_scale, part_gu + (((int64_t)slot * 2 + m) * nt + tile) * pad_rows(I));
 }
 
-template <bool F16>
-__global__ __launch_bounds__(256) void k_moe_down(BankArgs bank, const int32_t* __restrict__ ids,
-                                                  const float* __restrict__ part_gu, float* __restrict__ part_d,
-                                                  int nparts) {
+template <int BPW>
+__global__ __launch_bounds__(kThreads) RVQ_OCC_F32 void k_moe_gateup_f32(BankArgs bank, const float* __restrict__ x, const int32_t* __restrict__ ids, float* __restrict__ part_gu, int32_t* __restrict__ status) {
+  k_moe_gateup_body<false, BPW>(bank, x, ids, part_gu, status);
+}
+template <int BPW>
+__global__ __launch_bounds__(kThreads) RVQ_OCC_F16 void k_moe_gateup_f16(BankArgs bank, const float* __restrict__ x, const int32_t* __restrict__ ids, float* __restrict__ part_gu, int32_t* __restrict__ status) {
+  k_moe_gateup_body<true, BPW>(bank, x, ids, part_gu, status);
+}
+
+template <bool F16, int BPW>
+__device__ __forceinline__ void k_moe_down_body(BankArgs bank, const int32_t* __restrict__ ids,
+                                                       const float* __restrict__ part_gu, float* __restrict__ part_d,
+                                                       int nparts) {
   constexpr int G = Tile<F16>::kGroups;
+  constexpr int V = G * 8;              // entries of h this tile consumes
+  constexpr int S = kThreads / V;       // threads cooperating on one entry's tile sums
   __shared__ __attribute__((aligned(16))) typename Tile<F16>::entry_t lut[kLutBytes / sizeof(typename Tile<F16>::entry_t)];
   __shared__ float vs[256];
-  __shared__ float red[4];
+  __shared__ float hg[S][V], hu[S][V];
+  __shared__ float red[kWaves];
   const int H = bank.H, I = bank.I;
   const int groups = I / 8;
   const int nt = (int)cdiv(groups, G);
@@ -381,47 +466,109 @@ __global__ __launch_bounds__(256) void k_moe_down(BankArgs bank, const int32_t* 
   const int e = ids[slot];
   if (e < 0 || e >= bank.E) return;  // gate/up kernel records the status
   const int i = threadIdx.x;
-  const int k0 = tile * G * 8;
-  float v = 0.f;
-  if (i < G * 8 && k0 + i < I) {
-    const float* pg = part_gu + ((int64_t)slot * 2 + 0) * nt_in * I + k0 + i;
-    const float* pu = part_gu + ((int64_t)slot * 2 + 1) * nt_in * I + k0 + i;
-    float gs = 0.f, us = 0.f;
-    for (int t = 0; t < nt_in; ++t) {
-      gs += pg[(int64_t)t * I];
-      us += pu[(int64_t)t * I];
-    }
-    v = gs / (1.f + expf(-gs)) * us;
-  }
-  if (i < G * 8) vs[i] = v;
-  __syncthreads();
+  const int k0 = tile * V;
   const uint8_t* codes = bank.codes + (int64_t)e * bank.stride + 2 * packed_bytes(I, H);
   const float* cb = bank.cb + ((int64_t)e * 3 + 2) * kCodebookFloats;
-  const float out_scale = tile_tables<F16>(lut, cb, vs, v, red);
   const int nrb = (int)cdiv(H, kSlabRows);
   const int nt16 = (int)cdiv(groups, kSlabGroups);
   const int per = (int)cdiv(nrb, nparts);
   const int rb0 = p * per;
   const int rb1 = rb0 + per < nrb ? rb0 + per : nrb;
-  stream_tile<F16>(lut, codes, nrb, nt16, tile, rb0, rb1, H, out_scale,
-                   part_d + ((int64_t)slot * nt + tile) * H);
+  const int64_t Ip = pad_rows(I);
+  // Loads the tables need (codebook entry, gate/up tile sums for h) are issued before the code
+  // prefetch, since waits on the memory counter are in issue order.  Thread (ei, q) sums tiles
+  // q, q+S, ... of entry ei; up to kHold tiles per thread are loaded at once (clamped addresses,
+  // masked values, so the loads are unconditional).
+  constexpr int kHold = 16;
+  float cv[3][8];
+  load_codebook_entry<F16>(cb, cv);
+  const int ei = i % V, q = i / V;
+  const bool live = k0 + ei < I;
+  const float* pg = part_gu + ((int64_t)slot * 2 + 0) * nt_in * Ip + (live ? k0 + ei : 0);
+  const float* pu = part_gu + ((int64_t)slot * 2 + 1) * nt_in * Ip + (live ? k0 + ei : 0);
+  float gv[kHold], uv[kHold];
+#pragma unroll
+  for (int j = 0; j < kHold; ++j) {
+    const int t = q + j * S;
+    const int tt = t < nt_in ? t : nt_in - 1;
+    gv[j] = pg[tt * Ip];
+    uv[j] = pu[tt * Ip];
+  }
+  RowStream<F16, BPW> rs;
+  rs.begin(codes, nrb, nt16, tile, rb0, rb1);
+  float gs = 0.f, us = 0.f;
+#pragma unroll
+  for (int j = 0; j < kHold; ++j) {
+    const bool in = q + j * S < nt_in;
+    gs += in ? gv[j] : 0.f;
+    us += in ? uv[j] : 0.f;
+  }
+  for (int t = q + kHold * S; t < nt_in; t += S) {  // only when H > 8 * G * S * kHold
+    gs += pg[t * Ip];
+    us += pu[t * Ip];
+  }
+  hg[q][ei] = live ? gs : 0.f;
+  hu[q][ei] = live ? us : 0.f;
+  __syncthreads();
+  float v = 0.f;
+  if (i < V) {
+    float g = hg[0][i], u = hu[0][i];
+#pragma unroll
+    for (int qq = 1; qq < S; ++qq) {
+      g += hg[qq][i];
+      u += hu[qq][i];
+    }
+    if (k0 + i < I) v = g / (1.f + expf(-g)) * u;
+    vs[i] = v;
+  }
+  __syncthreads();
+  const float out_scale = tile_tables<F16>(lut, cv, vs, v, red);
+  rs.run(lut, out_scale, part_d + ((int64_t)slot * nt + tile) * pad_rows(H));
 }
 
-__global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ part_d, int nt, int H,
+template <int BPW>
+__global__ __launch_bounds__(kThreads) RVQ_OCC_F32 void k_moe_down_f32(BankArgs bank, const int32_t* __restrict__ ids, const float* __restrict__ part_gu, float* __restrict__ part_d, int nparts) {
+  k_moe_down_body<false, BPW>(bank, ids, part_gu, part_d, nparts);
+}
+template <int BPW>
+__global__ __launch_bounds__(kThreads) RVQ_OCC_F16 void k_moe_down_f16(BankArgs bank, const int32_t* __restrict__ ids, const float* __restrict__ part_gu, float* __restrict__ part_d, int nparts) {
+  k_moe_down_body<true, BPW>(bank, ids, part_gu, part_d, nparts);
+}
+
+// Gated combine.  Workgroup = 64 rows x 8 waves; wave q sums slots q, q+8, ... over all tiles (loads
+// four tiles at a time), then wave 0 adds the 8 partial sums to the residual in a fixed order.
+__global__ __launch_bounds__(512) void k_moe_combine(const float* __restrict__ part_d, int nt, int H,
                                                      const int32_t* __restrict__ ids, const float* __restrict__ gates,
                                                      int k, int E, const float* residual, float* y) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
-  if (r >= H) return;
-  float acc = residual ? residual[r] : 0.f;
-  for (int slot = 0; slot < k; ++slot) {
-    const int e = ids[slot];
-    if (e < 0 || e >= E) continue;
-    float s = 0.f;
-    const float* pd = part_d + (int64_t)slot * nt * H + r;
-    for (int t = 0; t < nt; ++t) s += pd[(int64_t)t * H];
-    acc = fmaf(gates[slot], s, acc);
+  const int64_t Hp = pad_rows(H);
+  __shared__ float red[8][64];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int r = blockIdx.x * 64 + lane;
+  float acc = 0.f;
+  if (r < H) {
+    for (int slot = q; slot < k; slot += 8) {
+      const int e = ids[slot];
+      if (e < 0 || e >= E) continue;
+      const float* pd = part_d + (int64_t)slot * nt * Hp + r;
+      float s = 0.f;
+      int t = 0;
+      for (; t + 4 <= nt; t += 4) {
+        const float a = pd[t * Hp], b = pd[(t + 1) * Hp];
+        const float c = pd[(t + 2) * Hp], d = pd[(t + 3) * Hp];
+        s += a; s += b; s += c; s += d;
+      }
+      for (; t < nt; ++t) s += pd[t * Hp];
+      acc = fmaf(gates[slot], s, acc);
+    }
   }
-  y[r] = acc;
+  red[q][lane] = acc;
+  __syncthreads();
+  if (q == 0 && r < H) {
+    float o = residual ? residual[r] : 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) o += red[w][lane];
+    y[r] = o;
+  }
 }
 
 static int down_parts(int H) {
@@ -436,16 +583,16 @@ MoeWorkspace moe_workspace_layout(int H, int I, int k, bool f16) {
   w.nt_out = (int)cdiv(I / 8, G);
   w.status_off = 0;
   w.part_gu_off = 256;
-  const size_t gu = (size_t)k * 2 * w.nt_in * I * sizeof(float);
+  const size_t gu = (size_t)k * 2 * w.nt_in * pad_rows(I) * sizeof(float);
   w.part_d_off = w.part_gu_off + ((gu + 255) / 256) * 256;
-  const size_t d = (size_t)k * w.nt_out * H * sizeof(float);
+  const size_t d = (size_t)k * w.nt_out * pad_rows(H) * sizeof(float);
   w.total = w.part_d_off + ((d + 255) / 256) * 256;
   return w;
 }
 
 hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
                              const float* x, const int32_t* ids, const float* gates, int k, const float* residual,
-                             float* y, bool f16, void* ws, hipStream_t stream) {
+                             float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev) {
   const MoeWorkspace w = moe_workspace_layout(H, I, k, f16);
   uint8_t* base = static_cast<uint8_t*>(ws);
   int32_t* status = reinterpret_cast<int32_t*>(base + w.status_off);
@@ -453,19 +600,34 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
   float* part_d = reinterpret_cast<float*>(base + w.part_d_off);
   BankArgs bank{codes, cb, stride, E, H, I};
   const int nparts = down_parts(H);
+  hipError_t err = hipSuccess;
+  auto mark = [&](int i) {
+    if (ev && err == hipSuccess) err = hipEventRecord(ev[i], stream);
+  };
+  mark(0);
+  const int bpw_gu = pick_bpw((int)cdiv(I, kSlabRows), 1);
+  const int bpw_d = pick_bpw((int)cdiv(H, kSlabRows), nparts);
   if (f16) {
-    hipLaunchKernelGGL(k_moe_gateup<true>, dim3(k * 2 * w.nt_in), dim3(256), 0, stream, bank, x, ids, part_gu, status);
-    hipLaunchKernelGGL(k_moe_down<true>, dim3(k * w.nt_out * nparts), dim3(256), 0, stream, bank, ids, part_gu, part_d,
-                       nparts);
+    RVQ_BPW_DISPATCH(bpw_gu, hipLaunchKernelGGL((k_moe_gateup_f16<B>), dim3(k * 2 * w.nt_in), dim3(kThreads), 0,
+                                                stream, bank, x, ids, part_gu, status))
   } else {
-    hipLaunchKernelGGL(k_moe_gateup<false>, dim3(k * 2 * w.nt_in), dim3(256), 0, stream, bank, x, ids, part_gu,
-                       status);
-    hipLaunchKernelGGL(k_moe_down<false>, dim3(k * w.nt_out * nparts), dim3(256), 0, stream, bank, ids, part_gu,
-                       part_d, nparts);
+    RVQ_BPW_DISPATCH(bpw_gu, hipLaunchKernelGGL((k_moe_gateup_f32<B>), dim3(k * 2 * w.nt_in), dim3(kThreads), 0,
+                                                stream, bank, x, ids, part_gu, status))
   }
-  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)cdiv(H, 256)), dim3(256), 0, stream, part_d, w.nt_out, H, ids,
+  mark(1);
+  if (f16) {
+    RVQ_BPW_DISPATCH(bpw_d, hipLaunchKernelGGL((k_moe_down_f16<B>), dim3(k * w.nt_out * nparts), dim3(kThreads), 0,
+                                               stream, bank, ids, part_gu, part_d, nparts))
+  } else {
+    RVQ_BPW_DISPATCH(bpw_d, hipLaunchKernelGGL((k_moe_down_f32<B>), dim3(k * w.nt_out * nparts), dim3(kThreads), 0,
+                                               stream, bank, ids, part_gu, part_d, nparts))
+  }
+  mark(2);
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)cdiv(H, 64)), dim3(512), 0, stream, part_d, w.nt_out, H, ids,
                      gates, k, E, residual, y);
-  return hipGetLastError();
+  mark(3);
+  const hipError_t last = hipGetLastError();
+  return err != hipSuccess ? err : last;
 }
 
 }  // namespace rvq

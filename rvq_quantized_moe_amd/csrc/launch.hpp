@@ -32,6 +32,6 @@ hipError_t launch_router_topk(const uint16_t* w, const void* x, bool x_bf16, int
 hipError_t launch_rmsnorm(const float* x, int T, int H, float eps, float* out, hipStream_t stream);
 hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
                              const float* x, const int32_t* ids, const float* gates, int k, const float* residual,
-                             float* y, bool f16, void* ws, hipStream_t stream);
+                             float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev);
 
 }  // namespace rvq
