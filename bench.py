@@ -173,6 +173,40 @@ def run_variant(rvq, hip, bank, w, pool, steps, warmup, dtype):
     }
 
 
+def run_graphed(rvq, bank, w, pool, steps, warmup, dtype):
+    """The same step replayed from HIP graphs (one graph per pool token: router top-k + MoE layer),
+    which removes host launch overhead; returns tokens/s over `steps` replays."""
+    import torch
+    dev = pool.device
+    ids = torch.empty((1, K), dtype=torch.int32, device=dev)
+    gates = torch.empty((1, K), dtype=torch.float32, device=dev)
+    logits = torch.empty((1, E), dtype=torch.float64, device=dev)
+    y = torch.empty(H, dtype=torch.float32, device=dev)
+    ws = rvq.make_moe_workspace(bank, 1, K, dtype)
+    torch.cuda.synchronize()
+    graphs = []
+    side = torch.cuda.Stream()
+    for j in range(POOL):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            rvq.router_topk(w, pool[j], K, ids=ids, gates=gates, logits=logits)
+            rvq.moe_layer_forward(bank, pool[j], ids[0], gates[0], dtype=dtype, y=y, workspace=ws)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % POOL].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % POOL].replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    status = rvq.check_device_status(ws)
+    if status:
+        raise RuntimeError(rvq.status_string(status))
+    del graphs
+    return steps / (t1 - t0)
+
+
 def stream_copy_peak(torch, dev):
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -265,11 +299,14 @@ def main():
     copy_gbps = stream_copy_peak(torch, dev)
     print(f"[bench] timing {args.steps} steps ({args.dtype} tables)", file=sys.stderr, flush=True)
     main_res = run_variant(rvq, hip, bank, w, pool, args.steps, args.warmup, args.dtype)
+    print("[bench] graph replay", file=sys.stderr, flush=True)
+    graph_tok_s = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype)
     variants = {}
     if not args.no_variants:
         other = "f16" if args.dtype == "f32" else "f32"
         print(f"[bench] timing {args.steps} steps ({other} tables)", file=sys.stderr, flush=True)
         variants[other] = run_variant(rvq, hip, bank, w, pool, args.steps, args.warmup, other)
+        variants[other]["graph_replay_tokens_per_s"] = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, other)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -279,12 +316,12 @@ def main():
     achieved = (GATEUP_CODE_BYTES + GATEUP_CODEBOOK_BYTES) / (gu_us * 1e-6) / 1e9
     line = {
         "metric": METRIC,
-        "value": main_res["tokens_per_s"],
+        "value": graph_tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": main_res["ms_per_step"],
+        "ms_per_step": 1e3 / graph_tok_s,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -293,11 +330,14 @@ def main():
         "config": {"workload": "moe_layer_decode", "experts": E, "hidden": H, "inter": I, "top_k": K, "batch": 1,
                    "table_dtype": args.dtype, "accumulate": "f32", "router_accumulate": "f64",
                    "resident_code_bytes": E * 3 * (H * I * 3 // 8), "token_pool": POOL},
-        "code_GBps": main_res["code_GBps"],
-        "code_frac_of_hbm_peak": main_res["code_frac_of_hbm_peak"],
-        "code_frac_of_stream_copy": main_res["code_GBps"] / copy_gbps,
+        "code_GBps": CODE_BYTES_PER_TOKEN * graph_tok_s / 1e9,
+        "code_frac_of_hbm_peak": CODE_BYTES_PER_TOKEN * graph_tok_s / 1e9 / HBM_PEAK_GBPS,
+        "code_frac_of_stream_copy": CODE_BYTES_PER_TOKEN * graph_tok_s / 1e9 / copy_gbps,
         "stream_copy_GBps": copy_gbps,
-        "decoded_weights_per_s": main_res["decoded_weights_per_s"],
+        "decoded_weights_per_s": WEIGHTS_PER_TOKEN * graph_tok_s,
+        "timing": "value: HIP-graph replay of the step (one graph per pool token); kernel_us and roofline: "
+                  "HIP events recorded around each kernel in an eager timed pass of the same steps",
+        "eager_tokens_per_s": main_res["tokens_per_s"],
         "kernel_us": main_res["kernel_us"],
         "roofline": {"bound": "hbm", "kernel": f"k_moe_gateup_{args.dtype}", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,

@@ -104,14 +104,15 @@ __device__ __forceinline__ void load_codebook_entry(const float* __restrict__ cb
   }
 }
 
-// With kThreads = 512 the two halves of the workgroup build alternate groups.
+// Workgroups of 256*n threads: the n thread sets build interleaved groups.
 template <bool F16>
 __device__ __forceinline__ void build_tile(typename Tile<F16>::entry_t* lut, const float (&cv)[3][8],
                                            const float* vs, float scale) {
   const int c = threadIdx.x & (kEntries - 1);
-  const int half = threadIdx.x >> 8;
+  const int set = threadIdx.x >> 8;
+  const int nsets = blockDim.x >> 8;
 #pragma unroll 4
-  for (int g = half; g < Tile<F16>::kGroups; g += kThreads / kEntries) {
+  for (int g = set; g < Tile<F16>::kGroups; g += nsets) {
     float xv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) xv[j] = vs[g * 8 + j];

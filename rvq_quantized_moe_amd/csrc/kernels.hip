@@ -168,11 +168,11 @@ __device__ __forceinline__ float tile_tables(typename Tile<F16>::entry_t* lut, c
 
 // Straight-line specialisation usable when `nparts` workgroups split nrb row blocks evenly over
 // their waves; 0 (the general loop) otherwise.
-static int pick_bpw(int nrb, int nparts) {
+static int pick_bpw(int nrb, int nparts, int waves) {
   if (nrb % nparts != 0) return 0;
   const int per = nrb / nparts;
-  if (per % kWaves != 0) return 0;
-  return fixed_bpw(per / kWaves) ? per / kWaves : 0;
+  if (per % waves != 0) return 0;
+  return fixed_bpw(per / waves) ? per / waves : 0;
 }
 
 __host__ __device__ inline int64_t pad_rows(int64_t rows) { return cdiv(rows, kSlabRows) * kSlabRows; }
@@ -242,7 +242,7 @@ hipError_t launch_gemv(const uint8_t* codes, const float* cb, int rows, int cols
   int nparts = 1;
   while (nt * nparts < 512 && (nparts * 2) * kWaves <= nrb) nparts *= 2;
   float* part = static_cast<float*>(ws);
-  const int bpw = pick_bpw(nrb, nparts);
+  const int bpw = pick_bpw(nrb, nparts, kWaves);
   if (f16) {
     RVQ_BPW_DISPATCH(bpw, hipLaunchKernelGGL((k_gemv_tiles_f16<B>), dim3(nt, nparts), dim3(kThreads), 0, stream,
                                              codes, cb, rows, cols, x, part, nparts))
@@ -317,31 +317,45 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 }
 
 // Top-k by (logit desc, id asc): the rank of e is the number of experts that precede it in that
-// order; ranks < k are kept, at position rank.  gates = softmax over the kept logits (fp64).
-__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits, int E, int k,
-                                              int32_t* __restrict__ ids, float* __restrict__ gates) {
+// order; ranks < k are kept, at position rank.  P consecutive lanes share one expert's comparisons
+// (each compares against every P-th logit; their counts are summed by shuffles).  gates = softmax
+// over the kept logits in fp64, summed by a fixed shuffle tree.
+__global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ logits, int E, int k,
+                                               int32_t* __restrict__ ids, float* __restrict__ gates) {
   __shared__ double L[kMaxExperts];
   __shared__ int sel[kMaxTopK];
   const int t = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += 256) L[e] = logits[(int64_t)t * E + e];
+  if (threadIdx.x < kMaxTopK) sel[threadIdx.x] = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) L[e] = logits[(int64_t)t * E + e];
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) {
-    const double le = L[e];
+  int P = (int)(blockDim.x / E);
+  P = P >= 64 ? 64 : P >= 32 ? 32 : P >= 16 ? 16 : P >= 8 ? 8 : P >= 4 ? 4 : P >= 2 ? 2 : 1;
+  const int sub = threadIdx.x % P;
+  const int per_pass = blockDim.x / P;
+  for (int base = 0; base < E; base += per_pass) {
+    const int e = base + threadIdx.x / P;
     int rank = 0;
-    for (int j = 0; j < E; ++j) {
-      const double lj = L[j];
-      rank += (lj > le) || (lj == le && j < e);
+    if (e < E) {
+      const double le = L[e];
+      for (int j = sub; j < E; j += P) {
+        const double lj = L[j];
+        rank += (lj > le) || (lj == le && j < e);
+      }
     }
-    if (rank < k) sel[rank] = e;
+    for (int off = 1; off < P; off <<= 1) rank += __shfl_xor(rank, off, 64);
+    if (e < E && sub == 0 && rank < k) sel[rank] = e;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {
+    const int i = threadIdx.x;
     const double m = L[sel[0]];
-    double z = 0.0;
-    for (int i = 0; i < k; ++i) z += exp(L[sel[i]] - m);
-    for (int i = 0; i < k; ++i) {
+    const double ex = i < k ? exp(L[sel[i]] - m) : 0.0;
+    double z = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+    if (i < k) {
       ids[(int64_t)t * k + i] = sel[i];
-      gates[(int64_t)t * k + i] = (float)(exp(L[sel[i]] - m) / z);
+      gates[(int64_t)t * k + i] = (float)(ex / z);
     }
   }
 }
@@ -359,7 +373,7 @@ hipError_t launch_router_topk(const uint16_t* w, const void* x, bool x_bf16, int
                        logits, vec);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_topk, dim3((unsigned)T), dim3(256), 0, stream, logits, E, k, ids, gates);
+  hipLaunchKernelGGL(k_topk, dim3((unsigned)T), dim3(1024), 0, stream, logits, E, k, ids, gates);
   return hipGetLastError();
 }
 
@@ -445,17 +459,17 @@ __global__ __launch_bounds__(kThreads) RVQ_OCC_F16 void k_moe_gateup_f16(BankArg
   k_moe_gateup_body<true, BPW>(bank, x, ids, part_gu, status);
 }
 
-template <bool F16, int BPW>
+template <bool F16, int BPW, int NT>
 __device__ __forceinline__ void k_moe_down_body(BankArgs bank, const int32_t* __restrict__ ids,
                                                        const float* __restrict__ part_gu, float* __restrict__ part_d,
                                                        int nparts) {
   constexpr int G = Tile<F16>::kGroups;
   constexpr int V = G * 8;              // entries of h this tile consumes
-  constexpr int S = kThreads / V;       // threads cooperating on one entry's tile sums
+  constexpr int S = NT / V;             // threads cooperating on one entry's tile sums
   __shared__ __attribute__((aligned(16))) typename Tile<F16>::entry_t lut[kLutBytes / sizeof(typename Tile<F16>::entry_t)];
   __shared__ float vs[256];
   __shared__ float hg[S][V], hu[S][V];
-  __shared__ float red[kWaves];
+  __shared__ float red[NT / 64];
   const int H = bank.H, I = bank.I;
   const int groups = I / 8;
   const int nt = (int)cdiv(groups, G);
@@ -526,13 +540,126 @@ __device__ __forceinline__ void k_moe_down_body(BankArgs bank, const int32_t* __
   rs.run(lut, out_scale, part_d + ((int64_t)slot * nt + tile) * pad_rows(H));
 }
 
+// ---------------------------------------------------------------------------------------------
+// Persistent gate/up kernel with fp32 tables (the decode hot loop when the shape allows it).
+//
+// One 16-wave workgroup per CU processes ITEMS (expert slot, matrix, 16-group tile) items in turn.
+// Its tables are double-buffered in LDS (2 x 48 KiB): while the waves stream item n through one
+// buffer, each thread builds its share of item n+1's tables into the other (12 entries per thread,
+// split over the item's row blocks), so an item costs one barrier and no exposed prologue.  The
+// code stream runs across item boundaries (NB row blocks of loads in flight per wave).
+//
+// Item placement: workgroup b runs on XCD b % 8; the items of XCD x are a contiguous range of
+// 224 (= 4 matrices x 56 tiles at the 7168/2048 shape), so each XCD's L2 holds the codebooks of
+// only its own matrices.  Invalid expert ids are streamed as expert 0 (results never read) and
+// flagged in the device status.
+template <int ITEMS, int BPI>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_gateup_pipe_f32(
+    BankArgs bank, const float* __restrict__ x, const int32_t* __restrict__ ids, float* __restrict__ part_gu,
+    int32_t* __restrict__ status, int nt) {
+  constexpr int NW = 16;                           // waves
+  constexpr int NB = 3;                            // row blocks of codes in flight per wave
+  constexpr int NBLK = ITEMS * BPI;                // row blocks per wave over the whole kernel
+  constexpr int GPT = 4;                           // groups per thread per item (16 groups / 4 sets)
+  __shared__ __attribute__((aligned(16))) float lut[2][48 * kEntries];
+  const int H = bank.H, I = bank.I;
+  const int nrb = NW * BPI;
+  const int64_t Ip = pad_rows(I);
+  const int64_t mat_bytes = packed_bytes(I, H);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = threadIdx.x & (kEntries - 1);
+  const int set = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int wgs_per_xcd = gridDim.x >> 3;
+  const int per_xcd = wgs_per_xcd * ITEMS;
+
+  // per-item addressing (uniform)
+  const uint8_t* base[ITEMS];
+  const float* cbk[ITEMS];
+  float* outk[ITEMS];
+  int tilek[ITEMS];
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const int item = xcd * per_xcd + j + wgs_per_xcd * k;
+    const int gm = item / nt, tile = item - gm * nt;
+    const int slot = gm >> 1, m = gm & 1;
+    int e = ids[slot];
+    if (e < 0 || e >= bank.E) {
+      if (tile == 0 && m == 0 && threadIdx.x == 0) atomicExch(status, 6 /* RVQ_ERR_EXPERT_ID */);
+      e = 0;
+    }
+    base[k] = bank.codes + (int64_t)e * bank.stride + (int64_t)m * mat_bytes + (int64_t)tile * nrb * kSlabBytes;
+    cbk[k] = bank.cb + ((int64_t)e * 3 + m) * kCodebookFloats;
+    outk[k] = part_gu + ((int64_t)gm * nt + tile) * Ip;
+    tilek[k] = tile;
+  }
+  const uint32_t lane_off = lane * 16;
+  SlabData buf[NB];
+  auto load_blk = [&](int i, int s) {  // row block s of this wave's sequence
+    const int k = s / BPI, r = s % BPI;
+    load_slabs<false>(buf[i], base[k], base[k], (uint32_t)(wave + NW * r) * kSlabBytes + lane_off);
+  };
+  float cv[3][8];
+  float xv[GPT][8];
+  auto load_item_inputs = [&](int k) {
+    load_codebook_entry<false>(cbk[k], cv);
+#pragma unroll
+    for (int u = 0; u < GPT; ++u) {
+      const int g = tilek[k] * 16 + set + 4 * u;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) xv[u][jj] = x[g * 8 + jj];
+    }
+  };
+  auto build_part = [&](float* L, int u0, int u1) {  // entries of groups set + 4u, u in [u0, u1)
+#pragma unroll
+    for (int u = u0; u < u1; ++u) {
+      const int g = set + 4 * u;
+#pragma unroll
+      for (int st = 0; st < 3; ++st) {
+        float t = cv[st][0] * xv[u][0];
+#pragma unroll
+        for (int jj = 1; jj < 8; ++jj) t = fmaf(cv[st][jj], xv[u][jj], t);
+        L[(3 * g + st) * kEntries + c] = t;
+      }
+    }
+  };
+
+  load_item_inputs(0);
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    if (i < NBLK) load_blk(i, i);
+  build_part(lut[0], 0, GPT);
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    if (k + 1 < ITEMS) load_item_inputs(k + 1);
+#pragma unroll
+    for (int r = 0; r < BPI; ++r) {
+      const int s = k * BPI + r;
+      const float acc = gather_slabs<false>(lut[k & 1], buf[s % NB]);
+      if (s + NB < NBLK) load_blk(s % NB, s + NB);
+      outk[k][(wave + NW * r) * kSlabRows + lane] = acc;
+      if (k + 1 < ITEMS) build_part(lut[(k + 1) & 1], (GPT * r) / BPI, (GPT * (r + 1)) / BPI);
+    }
+    __syncthreads();
+  }
+}
+
+// The down kernel runs one 16-wave workgroup per CU (256 workgroups = 16 experts x 16 tiles), so
+// each (expert, tile) rebuilds its slice of h once.
+constexpr int kDownThreads = 1024;
 template <int BPW>
-__global__ __launch_bounds__(kThreads) RVQ_OCC_F32 void k_moe_down_f32(BankArgs bank, const int32_t* __restrict__ ids, const float* __restrict__ part_gu, float* __restrict__ part_d, int nparts) {
-  k_moe_down_body<false, BPW>(bank, ids, part_gu, part_d, nparts);
+__global__ __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_moe_down_f32(
+    BankArgs bank, const int32_t* __restrict__ ids, const float* __restrict__ part_gu, float* __restrict__ part_d,
+    int nparts) {
+  k_moe_down_body<false, BPW, kDownThreads>(bank, ids, part_gu, part_d, nparts);
 }
 template <int BPW>
-__global__ __launch_bounds__(kThreads) RVQ_OCC_F16 void k_moe_down_f16(BankArgs bank, const int32_t* __restrict__ ids, const float* __restrict__ part_gu, float* __restrict__ part_d, int nparts) {
-  k_moe_down_body<true, BPW>(bank, ids, part_gu, part_d, nparts);
+__global__ __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_moe_down_f16(
+    BankArgs bank, const int32_t* __restrict__ ids, const float* __restrict__ part_gu, float* __restrict__ part_d,
+    int nparts) {
+  k_moe_down_body<true, BPW, kDownThreads>(bank, ids, part_gu, part_d, nparts);
 }
 
 // Gated combine.  Workgroup = 64 rows x 8 waves; wave q sums slots q, q+8, ... over all tiles (loads
@@ -572,8 +699,8 @@ __global__ __launch_bounds__(512) void k_moe_combine(const float* __restrict__ p
 }
 
 static int down_parts(int H) {
-  const int nrb = (int)cdiv(H, kSlabRows);
-  return nrb >= 64 ? 2 : 1;
+  (void)H;
+  return 1;
 }
 
 MoeWorkspace moe_workspace_layout(int H, int I, int k, bool f16) {
@@ -605,9 +732,27 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
     if (ev && err == hipSuccess) err = hipEventRecord(ev[i], stream);
   };
   mark(0);
-  const int bpw_gu = pick_bpw((int)cdiv(I, kSlabRows), 1);
-  const int bpw_d = pick_bpw((int)cdiv(H, kSlabRows), nparts);
-  if (f16) {
+  const int nrb_gu = (int)cdiv(I, kSlabRows);
+  const int items = k * 2 * w.nt_in;
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess) ncu = 0;
+  const int pipe_items = (ncu > 0 && ncu % 8 == 0 && items % ncu == 0) ? items / ncu : 0;
+  const int pipe_bpi = nrb_gu % 16 == 0 ? nrb_gu / 16 : 0;
+  bool piped = false;
+  if (!f16 && (H / 8) % 16 == 0 && pipe_bpi == 2 && pipe_items >= 1 && pipe_items <= 8) {
+    piped = true;
+    switch (pipe_items) {
+#define RVQ_PIPE_CASE(n)   case n: hipLaunchKernelGGL((k_gateup_pipe_f32<n, 2>), dim3(ncu), dim3(1024), 0, stream, bank, x, ids, part_gu, status, w.nt_in); break;
+      RVQ_PIPE_CASE(1) RVQ_PIPE_CASE(2) RVQ_PIPE_CASE(3) RVQ_PIPE_CASE(4)
+      RVQ_PIPE_CASE(5) RVQ_PIPE_CASE(6) RVQ_PIPE_CASE(7) RVQ_PIPE_CASE(8)
+#undef RVQ_PIPE_CASE
+      default: piped = false;
+    }
+  }
+  const int bpw_gu = pick_bpw((int)cdiv(I, kSlabRows), 1, kWaves);
+  const int bpw_d = pick_bpw((int)cdiv(H, kSlabRows), nparts, kDownThreads / 64);
+  if (piped) {
+  } else if (f16) {
     RVQ_BPW_DISPATCH(bpw_gu, hipLaunchKernelGGL((k_moe_gateup_f16<B>), dim3(k * 2 * w.nt_in), dim3(kThreads), 0,
                                                 stream, bank, x, ids, part_gu, status))
   } else {
@@ -616,10 +761,10 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
   }
   mark(1);
   if (f16) {
-    RVQ_BPW_DISPATCH(bpw_d, hipLaunchKernelGGL((k_moe_down_f16<B>), dim3(k * w.nt_out * nparts), dim3(kThreads), 0,
+    RVQ_BPW_DISPATCH(bpw_d, hipLaunchKernelGGL((k_moe_down_f16<B>), dim3(k * w.nt_out * nparts), dim3(kDownThreads), 0,
                                                stream, bank, ids, part_gu, part_d, nparts))
   } else {
-    RVQ_BPW_DISPATCH(bpw_d, hipLaunchKernelGGL((k_moe_down_f32<B>), dim3(k * w.nt_out * nparts), dim3(kThreads), 0,
+    RVQ_BPW_DISPATCH(bpw_d, hipLaunchKernelGGL((k_moe_down_f32<B>), dim3(k * w.nt_out * nparts), dim3(kDownThreads), 0,
                                                stream, bank, ids, part_gu, part_d, nparts))
   }
   mark(2);
