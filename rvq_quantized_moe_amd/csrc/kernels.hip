@@ -413,14 +413,14 @@ struct BankArgs {
   int E, H, I;
 };
 
-template <bool F16, int BPW>
+template <bool F16, int BPW, int NT>
 __device__ __forceinline__ void k_moe_gateup_body(BankArgs bank, const float* __restrict__ x,
                                                     const int32_t* __restrict__ ids, float* __restrict__ part_gu,
                                                     int32_t* __restrict__ status) {
   constexpr int G = Tile<F16>::kGroups;
   __shared__ __attribute__((aligned(16))) typename Tile<F16>::entry_t lut[kLutBytes / sizeof(typename Tile<F16>::entry_t)];
   __shared__ float vs[256];
-  __shared__ float red[kWaves];
+  __shared__ float red[NT / 64];
   const int H = bank.H, I = bank.I;
   const int groups = H / 8;
   const int nt = (int)cdiv(groups, G);
@@ -450,13 +450,20 @@ __device__ __forceinline__ void k_moe_gateup_body(BankArgs bank, const float* __
   rs.run(lut, out_scale, part_gu + (((int64_t)slot * 2 + m) * nt + tile) * pad_rows(I));
 }
 
+// gate/up: 4-wave workgroups, three per CU (LDS-bound), so three workgroups' table builds and
+// streams interleave on each CU.
+constexpr int kGateUpThreads = 256;
 template <int BPW>
-__global__ __launch_bounds__(kThreads) RVQ_OCC_F32 void k_moe_gateup_f32(BankArgs bank, const float* __restrict__ x, const int32_t* __restrict__ ids, float* __restrict__ part_gu, int32_t* __restrict__ status) {
-  k_moe_gateup_body<false, BPW>(bank, x, ids, part_gu, status);
+__global__ __launch_bounds__(kGateUpThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_moe_gateup_f32(
+    BankArgs bank, const float* __restrict__ x, const int32_t* __restrict__ ids, float* __restrict__ part_gu,
+    int32_t* __restrict__ status) {
+  k_moe_gateup_body<false, BPW, kGateUpThreads>(bank, x, ids, part_gu, status);
 }
 template <int BPW>
-__global__ __launch_bounds__(kThreads) RVQ_OCC_F16 void k_moe_gateup_f16(BankArgs bank, const float* __restrict__ x, const int32_t* __restrict__ ids, float* __restrict__ part_gu, int32_t* __restrict__ status) {
-  k_moe_gateup_body<true, BPW>(bank, x, ids, part_gu, status);
+__global__ __launch_bounds__(kGateUpThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_moe_gateup_f16(
+    BankArgs bank, const float* __restrict__ x, const int32_t* __restrict__ ids, float* __restrict__ part_gu,
+    int32_t* __restrict__ status) {
+  k_moe_gateup_body<true, BPW, kGateUpThreads>(bank, x, ids, part_gu, status);
 }
 
 template <bool F16, int BPW, int NT>
@@ -538,112 +545,6 @@ __device__ __forceinline__ void k_moe_down_body(BankArgs bank, const int32_t* __
   __syncthreads();
   const float out_scale = tile_tables<F16>(lut, cv, vs, v, red);
   rs.run(lut, out_scale, part_d + ((int64_t)slot * nt + tile) * pad_rows(H));
-}
-
-// ---------------------------------------------------------------------------------------------
-// Persistent gate/up kernel with fp32 tables (the decode hot loop when the shape allows it).
-//
-// One 16-wave workgroup per CU processes ITEMS (expert slot, matrix, 16-group tile) items in turn.
-// Its tables are double-buffered in LDS (2 x 48 KiB): while the waves stream item n through one
-// buffer, each thread builds its share of item n+1's tables into the other (12 entries per thread,
-// split over the item's row blocks), so an item costs one barrier and no exposed prologue.  The
-// code stream runs across item boundaries (NB row blocks of loads in flight per wave).
-//
-// Item placement: workgroup b runs on XCD b % 8; the items of XCD x are a contiguous range of
-// 224 (= 4 matrices x 56 tiles at the 7168/2048 shape), so each XCD's L2 holds the codebooks of
-// only its own matrices.  Invalid expert ids are streamed as expert 0 (results never read) and
-// flagged in the device status.
-template <int ITEMS, int BPI>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_gateup_pipe_f32(
-    BankArgs bank, const float* __restrict__ x, const int32_t* __restrict__ ids, float* __restrict__ part_gu,
-    int32_t* __restrict__ status, int nt) {
-  constexpr int NW = 16;                           // waves
-  constexpr int NB = 3;                            // row blocks of codes in flight per wave
-  constexpr int NBLK = ITEMS * BPI;                // row blocks per wave over the whole kernel
-  constexpr int GPT = 4;                           // groups per thread per item (16 groups / 4 sets)
-  __shared__ __attribute__((aligned(16))) float lut[2][48 * kEntries];
-  const int H = bank.H, I = bank.I;
-  const int nrb = NW * BPI;
-  const int64_t Ip = pad_rows(I);
-  const int64_t mat_bytes = packed_bytes(I, H);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = threadIdx.x & (kEntries - 1);
-  const int set = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
-  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int wgs_per_xcd = gridDim.x >> 3;
-  const int per_xcd = wgs_per_xcd * ITEMS;
-
-  // per-item addressing (uniform)
-  const uint8_t* base[ITEMS];
-  const float* cbk[ITEMS];
-  float* outk[ITEMS];
-  int tilek[ITEMS];
-#pragma unroll
-  for (int k = 0; k < ITEMS; ++k) {
-    const int item = xcd * per_xcd + j + wgs_per_xcd * k;
-    const int gm = item / nt, tile = item - gm * nt;
-    const int slot = gm >> 1, m = gm & 1;
-    int e = ids[slot];
-    if (e < 0 || e >= bank.E) {
-      if (tile == 0 && m == 0 && threadIdx.x == 0) atomicExch(status, 6 /* RVQ_ERR_EXPERT_ID */);
-      e = 0;
-    }
-    base[k] = bank.codes + (int64_t)e * bank.stride + (int64_t)m * mat_bytes + (int64_t)tile * nrb * kSlabBytes;
-    cbk[k] = bank.cb + ((int64_t)e * 3 + m) * kCodebookFloats;
-    outk[k] = part_gu + ((int64_t)gm * nt + tile) * Ip;
-    tilek[k] = tile;
-  }
-  const uint32_t lane_off = lane * 16;
-  SlabData buf[NB];
-  auto load_blk = [&](int i, int s) {  // row block s of this wave's sequence
-    const int k = s / BPI, r = s % BPI;
-    load_slabs<false>(buf[i], base[k], base[k], (uint32_t)(wave + NW * r) * kSlabBytes + lane_off);
-  };
-  float cv[3][8];
-  float xv[GPT][8];
-  auto load_item_inputs = [&](int k) {
-    load_codebook_entry<false>(cbk[k], cv);
-#pragma unroll
-    for (int u = 0; u < GPT; ++u) {
-      const int g = tilek[k] * 16 + set + 4 * u;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) xv[u][jj] = x[g * 8 + jj];
-    }
-  };
-  auto build_part = [&](float* L, int u0, int u1) {  // entries of groups set + 4u, u in [u0, u1)
-#pragma unroll
-    for (int u = u0; u < u1; ++u) {
-      const int g = set + 4 * u;
-#pragma unroll
-      for (int st = 0; st < 3; ++st) {
-        float t = cv[st][0] * xv[u][0];
-#pragma unroll
-        for (int jj = 1; jj < 8; ++jj) t = fmaf(cv[st][jj], xv[u][jj], t);
-        L[(3 * g + st) * kEntries + c] = t;
-      }
-    }
-  };
-
-  load_item_inputs(0);
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-    if (i < NBLK) load_blk(i, i);
-  build_part(lut[0], 0, GPT);
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < ITEMS; ++k) {
-    if (k + 1 < ITEMS) load_item_inputs(k + 1);
-#pragma unroll
-    for (int r = 0; r < BPI; ++r) {
-      const int s = k * BPI + r;
-      const float acc = gather_slabs<false>(lut[k & 1], buf[s % NB]);
-      if (s + NB < NBLK) load_blk(s % NB, s + NB);
-      outk[k][(wave + NW * r) * kSlabRows + lane] = acc;
-      if (k + 1 < ITEMS) build_part(lut[(k + 1) & 1], (GPT * r) / BPI, (GPT * (r + 1)) / BPI);
-    }
-    __syncthreads();
-  }
 }
 
 // The down kernel runs one 16-wave workgroup per CU (256 workgroups = 16 experts x 16 tiles), so
@@ -732,31 +633,13 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
     if (ev && err == hipSuccess) err = hipEventRecord(ev[i], stream);
   };
   mark(0);
-  const int nrb_gu = (int)cdiv(I, kSlabRows);
-  const int items = k * 2 * w.nt_in;
-  int ncu = 0;
-  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess) ncu = 0;
-  const int pipe_items = (ncu > 0 && ncu % 8 == 0 && items % ncu == 0) ? items / ncu : 0;
-  const int pipe_bpi = nrb_gu % 16 == 0 ? nrb_gu / 16 : 0;
-  bool piped = false;
-  if (!f16 && (H / 8) % 16 == 0 && pipe_bpi == 2 && pipe_items >= 1 && pipe_items <= 8) {
-    piped = true;
-    switch (pipe_items) {
-#define RVQ_PIPE_CASE(n)   case n: hipLaunchKernelGGL((k_gateup_pipe_f32<n, 2>), dim3(ncu), dim3(1024), 0, stream, bank, x, ids, part_gu, status, w.nt_in); break;
-      RVQ_PIPE_CASE(1) RVQ_PIPE_CASE(2) RVQ_PIPE_CASE(3) RVQ_PIPE_CASE(4)
-      RVQ_PIPE_CASE(5) RVQ_PIPE_CASE(6) RVQ_PIPE_CASE(7) RVQ_PIPE_CASE(8)
-#undef RVQ_PIPE_CASE
-      default: piped = false;
-    }
-  }
-  const int bpw_gu = pick_bpw((int)cdiv(I, kSlabRows), 1, kWaves);
+  const int bpw_gu = pick_bpw((int)cdiv(I, kSlabRows), 1, kGateUpThreads / 64);
   const int bpw_d = pick_bpw((int)cdiv(H, kSlabRows), nparts, kDownThreads / 64);
-  if (piped) {
-  } else if (f16) {
-    RVQ_BPW_DISPATCH(bpw_gu, hipLaunchKernelGGL((k_moe_gateup_f16<B>), dim3(k * 2 * w.nt_in), dim3(kThreads), 0,
+  if (f16) {
+    RVQ_BPW_DISPATCH(bpw_gu, hipLaunchKernelGGL((k_moe_gateup_f16<B>), dim3(k * 2 * w.nt_in), dim3(kGateUpThreads), 0,
                                                 stream, bank, x, ids, part_gu, status))
   } else {
-    RVQ_BPW_DISPATCH(bpw_gu, hipLaunchKernelGGL((k_moe_gateup_f32<B>), dim3(k * 2 * w.nt_in), dim3(kThreads), 0,
+    RVQ_BPW_DISPATCH(bpw_gu, hipLaunchKernelGGL((k_moe_gateup_f32<B>), dim3(k * 2 * w.nt_in), dim3(kGateUpThreads), 0,
                                                 stream, bank, x, ids, part_gu, status))
   }
   mark(1);

@@ -58,3 +58,23 @@ def rel_l2(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+class Stack:
+    """92 MoE layers (64 experts each, 7168/2048) with per-layer bf16 routers, resident on the device."""
+
+    def __init__(self, seed=None, layers=None, experts=None, hidden=HIDDEN, inter=INTER, device="cuda"):
+        import synth as _s
+        self.seed = _s.SEED_STACK if seed is None else seed
+        self.L = STACK_LAYERS if layers is None else layers
+        self.E = STACK_EXPERTS if experts is None else experts
+        self.H, self.I = hidden, inter
+        self.banks, self.router_bits, self.routers = [], [], []
+        for l in range(self.L):
+            self.banks.append(upload_bank(self.seed, l, self.E, hidden, inter, device=device))
+            bits, w = router(self.seed, l, self.E, hidden, device=device)
+            self.router_bits.append(bits)
+            self.routers.append(w)
+
+    def oracle_expert(self, l, e):
+        return oracle_expert(self.seed, l, e, self.H, self.I)
