@@ -207,18 +207,20 @@ def run_graphed(rvq, bank, w, pool, steps, warmup, dtype):
     return steps / (t1 - t0)
 
 
-def stream_copy_peak(torch, dev):
+def stream_copy_peak(torch, rvq, dev):
+    """Read+write GB/s of rvq_stream_copy over 1 GiB (the code stream's load instruction); its
+    rocprofv3 FETCH_SIZE/WRITE_SIZE per dispatch (1 GiB each) calibrate the counters."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
     b = torch.empty(n, dtype=torch.uint8, device=dev)
     a.fill_(1)
     for _ in range(2):
-        b.copy_(a)
+        rvq.stream_copy(a, b)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     reps = 10
     for _ in range(reps):
-        b.copy_(a)
+        rvq.stream_copy(a, b)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / reps
     del a, b
@@ -296,7 +298,7 @@ def main():
     pool = torch.from_numpy(np.stack([synth.activation_f32(synth.SEED_LAYER, t, H) for t in range(POOL)])).to(dev)
     hip = Hip()
     print("[bench] stream copy peak", file=sys.stderr, flush=True)
-    copy_gbps = stream_copy_peak(torch, dev)
+    copy_gbps = stream_copy_peak(torch, rvq, dev)
     print(f"[bench] timing {args.steps} steps ({args.dtype} tables)", file=sys.stderr, flush=True)
     main_res = run_variant(rvq, hip, bank, w, pool, args.steps, args.warmup, args.dtype)
     print("[bench] graph replay", file=sys.stderr, flush=True)

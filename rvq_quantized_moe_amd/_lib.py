@@ -42,7 +42,7 @@ EXPORTS = [
     "rvq_status_string", "rvq_packed_bytes", "rvq_pack_codes", "rvq_lut_build",
     "rvq_expert_gemv_workspace_bytes", "rvq_expert_gemv", "rvq_router_topk", "rvq_bank_record_bytes",
     "rvq_moe_layer_workspace_bytes", "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed",
-    "rvq_workspace_init", "rvq_rmsnorm",
+    "rvq_workspace_init", "rvq_rmsnorm", "rvq_stream_copy",
     "rvq_check_device_status",
 ]
 
@@ -76,8 +76,10 @@ def lib():
         L.rvq_workspace_init.argtypes = [p, sz, p]
         L.rvq_rmsnorm.argtypes = [p, i32, i32, ctypes.c_float, p, p]
         L.rvq_check_device_status.argtypes = [p, p]
+        L.rvq_stream_copy.argtypes = [p, p, sz, p]
         for name in ("rvq_pack_codes", "rvq_lut_build", "rvq_expert_gemv", "rvq_router_topk",
-                     "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed", "rvq_workspace_init", "rvq_rmsnorm", "rvq_check_device_status"):
+                     "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed", "rvq_workspace_init", "rvq_rmsnorm",
+                     "rvq_check_device_status", "rvq_stream_copy"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -203,6 +205,12 @@ def rmsnorm(x, eps=1e-6, out=None):
     out = torch.empty_like(x) if out is None else out
     _check(lib().rvq_rmsnorm(_ptr(x), T, H, float(eps), _ptr(out), _stream(x)))
     return out
+
+
+def stream_copy(src, dst):
+    """dst <- src (uint8 device tensors, 16-byte multiples) with the code stream's load instruction."""
+    n = src.numel() * src.element_size()
+    _check(lib().rvq_stream_copy(_ptr(src), _ptr(dst), n, _stream(src)))
 
 
 def workspace_init(ws):

@@ -162,6 +162,14 @@ int rvq_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stre
   return hip_status(launch_zero(workspace, workspace_bytes, stream));
 }
 
+int rvq_stream_copy(const void* src, void* dst, size_t nbytes, hipStream_t stream) {
+  if (!src || !dst) return RVQ_ERR_NULL;
+  if (nbytes % 16 != 0) return RVQ_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return RVQ_ERR_ALIGN;
+  if (nbytes == 0) return RVQ_OK;
+  return hip_status(launch_stream_copy(src, dst, nbytes, stream));
+}
+
 int rvq_rmsnorm(const float* x, int32_t T, int32_t H, float eps, float* out, hipStream_t stream) {
   if (!x || !out) return RVQ_ERR_NULL;
   if (T < 1 || H < 1 || H > kMaxDim || !(eps >= 0.f)) return RVQ_ERR_SHAPE;

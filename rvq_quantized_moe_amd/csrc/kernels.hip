@@ -62,6 +62,26 @@ hipError_t launch_zero(void* p, size_t nbytes, hipStream_t stream) {
 }
 
 // =============================================================================================
+// Streaming copy with the code stream's load instruction (16-byte global loads): the
+// reference for the achievable read rate and for scaling memory-traffic counters.
+__global__ __launch_bounds__(256) void k_stream_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                     int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride)
+    dst[i] = src[i];
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, size_t nbytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(nbytes / 16);
+  int64_t grid = cdiv(n16, 256);
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(k_stream_copy, dim3((unsigned)grid), dim3(256), 0, stream, static_cast<const u32x4*>(src),
+                     static_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+
+// =============================================================================================
 // Standalone partial-dot tables lut[g][s][c] for all groups of x (global memory output).
 // Block b builds groups [b*G, b*G+G) with G = Tile<F16>::kGroups.  fp16: one exponent for the
 // whole table, from max_c ||C_s[c]|| * max_g ||x_g|| (each block recomputes the x maximum).

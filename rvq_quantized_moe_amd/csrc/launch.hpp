@@ -23,6 +23,7 @@ size_t gemv_workspace_bytes(int rows, int cols, bool f16);
 
 hipError_t launch_pack(const uint8_t* src, int rows, int cols, uint8_t* dst, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t nbytes, hipStream_t stream);
+hipError_t launch_stream_copy(const void* src, void* dst, size_t nbytes, hipStream_t stream);
 hipError_t launch_lut_build(const float* x, int cols, const float* cb, bool f16, void* lut, int32_t* log2_scale,
                             hipStream_t stream);
 hipError_t launch_gemv(const uint8_t* codes, const float* cb, int rows, int cols, const float* x, bool f16, float* y,

@@ -186,3 +186,12 @@ def test_validator_fuzz(L):
         st = L.rvq_pack_codes(FAKE, rows, cols, codes if which == "align" else FAKE2, s)
         if which in ("rows", "cols", "align"):
             assert st in (SHAPE, ALIGN), (which, st)
+
+
+def test_stream_copy_validation(L):
+    s = None
+    assert L.rvq_stream_copy(None, FAKE, 16, s) == NULL
+    assert L.rvq_stream_copy(FAKE, None, 16, s) == NULL
+    assert L.rvq_stream_copy(FAKE, FAKE2, 17, s) == SHAPE
+    assert L.rvq_stream_copy(FAKE + 4, FAKE2, 16, s) == ALIGN
+    assert L.rvq_stream_copy(FAKE, FAKE2, 0, s) == OK
