@@ -209,3 +209,32 @@ def moe_layer(get_expert, router_bits, x, k, residual=None, rowsel=None):
         r = np.asarray(residual, dtype=np.float64)
         y = y + (r if rowsel is None else r[np.asarray(rowsel)])
     return y, ids, gates, gaps
+
+
+def moe_chunk(get_expert, router_bits, X, k, residual=None, tokens=None):
+    """A chunk of tokens through one MoE layer: every token routed, then each expert rebuilt once and
+    applied to all of its tokens (the token's output is the same as moe_layer's, token by token).
+
+    X: fp64 [T, H] (exact widening of the bf16 chunk).  tokens: indices whose outputs are wanted
+    (all if None).  Returns (Y fp64 [len(tokens), H], ids [T, k], gates [T, k])."""
+    X = np.asarray(X, dtype=np.float64)
+    T, H = X.shape
+    L = router_logits(router_bits, X)
+    ids = np.empty((T, k), dtype=np.int32)
+    gates = np.empty((T, k), dtype=np.float64)
+    for t in range(T):
+        ids[t], gates[t], _ = topk(L[t], k)
+    want = np.arange(T) if tokens is None else np.asarray(tokens)
+    Y = np.zeros((want.size, H), dtype=np.float64)
+    by_expert = {}
+    for row, t in enumerate(want):
+        for i in range(k):
+            by_expert.setdefault(int(ids[t, i]), []).append((row, int(t), i))
+    for e in sorted(by_expert):
+        pairs = by_expert[e]
+        Ye = expert_batch(get_expert(e), X[[t for _, t, _ in pairs]])
+        for (row, t, i), y in zip(pairs, Ye):
+            Y[row] += gates[t, i] * y
+    if residual is not None:
+        Y += np.asarray(residual, dtype=np.float64)[want]
+    return Y, ids, gates

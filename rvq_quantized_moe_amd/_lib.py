@@ -263,9 +263,19 @@ class ExpertBank:
         self.codebooks[e].copy_(torch.from_numpy(codebooks))
 
 
+def _layer_dtype(d, T):
+    if T == 1:
+        return _table_dtype(d)
+    if d in ("f16", F16, torch.float16):
+        return F16
+    if d in ("bf16", BF16, torch.bfloat16):
+        return BF16
+    raise ValueError(f"chunk tile dtype must be f16 or bf16, got {d!r}")
+
+
 def moe_workspace_bytes(bank, T=1, k=16, dtype="f32"):
     d = bank.desc()
-    return lib().rvq_moe_layer_workspace_bytes(ctypes.byref(d), T, k, _table_dtype(dtype))
+    return lib().rvq_moe_layer_workspace_bytes(ctypes.byref(d), T, k, _layer_dtype(dtype, T))
 
 
 def make_moe_workspace(bank, T=1, k=16, dtype="f32"):
@@ -278,23 +288,36 @@ def make_moe_workspace(bank, T=1, k=16, dtype="f32"):
 
 
 def moe_layer_forward(bank, x, ids, gates, residual=None, dtype="f32", y=None, workspace=None, events=None):
-    """y = [residual +] sum_i gates[i] * expert_{ids[i]}(x) for one decode token (x fp32 [H]).
+    """y = [residual +] sum_i gates[i] * expert_{ids[i]}(x).
 
-    events: optional sequence of 4 raw hipEvent_t handles recorded around the layer's kernels."""
-    _dev(x, torch.float32, "x")
+    One decode token: x fp32 [H], ids/gates [k], dtype = table precision "f32" | "f16".
+    A chunk of T > 1 tokens: x bf16 [T, H], ids/gates [T, k], dtype = tile precision "f16" | "bf16";
+    returns fp32 [T, H].
+    events: optional sequence of 4 raw hipEvent_t handles recorded around the decode kernels."""
     _dev(ids, torch.int32, "ids")
     _dev(gates, torch.float32, "gates")
-    d = _table_dtype(dtype)
-    k = ids.numel()
-    T = 1
+    if x.dim() == 2 and x.shape[0] > 1:
+        _dev(x, torch.bfloat16, "x")
+        T = x.shape[0]
+        d = {"f16": F16, "bf16": BF16}[dtype]
+        k = ids.shape[-1]
+        out_shape = (T, bank.H)
+        xd = BF16
+    else:
+        _dev(x, torch.float32, "x")
+        T = 1
+        d = _table_dtype(dtype)
+        k = ids.numel()
+        out_shape = (bank.H,)
+        xd = F32
     if residual is not None:
         _dev(residual, torch.float32, "residual")
     if y is None:
-        y = torch.empty(bank.H, dtype=torch.float32, device=x.device)
+        y = torch.empty(out_shape, dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = make_moe_workspace(bank, T, k, d)
     desc = bank.desc()
-    args = (ctypes.byref(desc), _ptr(x), F32, T, _ptr(ids), _ptr(gates), k, _ptr(residual), _ptr(y), d,
+    args = (ctypes.byref(desc), _ptr(x), xd, T, _ptr(ids), _ptr(gates), k, _ptr(residual), _ptr(y), d,
             _ptr(workspace), workspace.numel(), _stream(x))
     if events is None:
         _check(lib().rvq_moe_layer_forward(*args))

@@ -110,10 +110,24 @@ size_t rvq_bank_record_bytes(int32_t hidden, int32_t inter) {
   return (size_t)(2 * packed_bytes(inter, hidden) + packed_bytes(hidden, inter));
 }
 
+// Largest chunk the bucketing workgroup handles (its per-expert token bitmaps live in 64 KiB of LDS).
+inline bool chunk_shape_ok(const rvq_expert_bank_t* bank, int32_t T, int32_t k) {
+  if (T < 2 || T > 4096 || k < 1 || k > kMaxTopK || k > bank->num_experts) return false;
+  if (bank->hidden % 64 != 0 || bank->inter % 64 != 0) return false;
+  const int64_t words = (int64_t)bank->num_experts * ((T + 31) / 32) + bank->num_experts + 1;
+  return words <= 16384;
+}
+
 size_t rvq_moe_layer_workspace_bytes(const rvq_expert_bank_t* bank, int32_t T, int32_t k, int32_t compute_dtype) {
-  if (!bank || T != 1 || k < 1 || k > kMaxTopK || !table_dtype(compute_dtype)) return 0;
+  if (!bank || k < 1 || k > kMaxTopK) return 0;
   if (!valid_matrix_shape(bank->inter, bank->hidden) || bank->inter % 8 != 0) return 0;
-  return moe_workspace_layout(bank->hidden, bank->inter, k, compute_dtype == RVQ_F16).total;
+  if (T == 1) {
+    if (!table_dtype(compute_dtype)) return 0;
+    return moe_workspace_layout(bank->hidden, bank->inter, k, compute_dtype == RVQ_F16).total;
+  }
+  if (compute_dtype != RVQ_F16 && compute_dtype != RVQ_BF16) return 0;
+  if (bank->num_experts < 1 || bank->num_experts > kMaxExperts || !chunk_shape_ok(bank, T, k)) return 0;
+  return chunk_workspace_bytes(bank->num_experts, bank->hidden, bank->inter, T, k);
 }
 
 namespace {
@@ -124,6 +138,19 @@ int moe_layer_forward_impl(const rvq_expert_bank_t* bank, const void* x, int32_t
   int st = check_bank(bank);
   if (st != RVQ_OK) return st;
   if (!x || !ids || !gates || !y || !workspace) return RVQ_ERR_NULL;
+  if (T > 1) {
+    if (events) return RVQ_ERR_SHAPE;
+    if (!chunk_shape_ok(bank, T, k)) return RVQ_ERR_SHAPE;
+    if (x_dtype != RVQ_BF16 || (compute_dtype != RVQ_F16 && compute_dtype != RVQ_BF16)) return RVQ_ERR_DTYPE;
+    if (!aligned(workspace, 256) || !aligned(x, 16) || !aligned(y, 4) || !aligned(ids, 4) || !aligned(gates, 4) ||
+        (residual && !aligned(residual, 4)))
+      return RVQ_ERR_ALIGN;
+    if (workspace_bytes < chunk_workspace_bytes(bank->num_experts, bank->hidden, bank->inter, T, k))
+      return RVQ_ERR_WORKSPACE;
+    return hip_status(launch_moe_chunk(bank->codes, bank->codebooks, bank->record_stride, bank->num_experts,
+                                       bank->hidden, bank->inter, static_cast<const uint16_t*>(x), T, ids, gates, k,
+                                       residual, y, compute_dtype == RVQ_F16, workspace, stream));
+  }
   if (T != 1 || k < 1 || k > kMaxTopK) return RVQ_ERR_SHAPE;
   if (x_dtype != RVQ_F32 || !table_dtype(compute_dtype)) return RVQ_ERR_DTYPE;
   if (!aligned(workspace, 256) || !aligned(x, 4) || !aligned(y, 4) || !aligned(ids, 4) || !aligned(gates, 4) ||

@@ -44,6 +44,14 @@ __host__ __device__ inline int64_t packed_bytes(int64_t rows, int64_t cols) {
   return cdiv(cols / 8, kSlabGroups) * cdiv(rows, kSlabRows) * kSlabBytes;
 }
 
+// Device view of an expert bank (see rvq_expert_bank_t in rvq.h).
+struct BankArgs {
+  const uint8_t* codes;
+  const float* cb;
+  int64_t stride;
+  int E, H, I;
+};
+
 // Table precision traits: fp32 tables cover 16 groups (one slab), fp16 tables 32 (two slabs).
 template <bool F16> struct Tile;
 template <> struct Tile<false> {

@@ -426,13 +426,6 @@ hipError_t launch_rmsnorm(const float* x, int T, int H, float eps, float* out, h
 //   down:     grid k * nt_out * P  -> part_d[slot][tile][row]        (rows of down = H)
 //             (each workgroup first rebuilds its 8*G entries of h = silu(g) * u from part_gu)
 //   combine:  y[r] = residual[r] + sum_slot gate[slot] * sum_tile part_d[slot][tile][r]
-struct BankArgs {
-  const uint8_t* codes;
-  const float* cb;
-  int64_t stride;
-  int E, H, I;
-};
-
 template <bool F16, int BPW, int NT>
 __device__ __forceinline__ void k_moe_gateup_body(BankArgs bank, const float* __restrict__ x,
                                                     const int32_t* __restrict__ ids, float* __restrict__ part_gu,

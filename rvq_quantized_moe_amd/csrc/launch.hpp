@@ -35,4 +35,9 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
                              const float* x, const int32_t* ids, const float* gates, int k, const float* residual,
                              float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev);
 
+size_t chunk_workspace_bytes(int E, int H, int I, int T, int k);
+hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
+                            const uint16_t* x, int T, const int32_t* ids, const float* gates, int k,
+                            const float* residual, float* y, bool f16, void* ws, hipStream_t stream);
+
 }  // namespace rvq

@@ -141,13 +141,35 @@ def test_moe_validation(L):
     assert L.rvq_moe_layer_forward(_bank(stride=16_515_072 - 256), *args) == SHAPE
     assert L.rvq_moe_layer_forward(_bank(E=0), *args) == SHAPE
     assert L.rvq_moe_layer_forward(_bank(H=7170), *args) == SHAPE
-    assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 2, FAKE, FAKE, 16, None, FAKE, 0, FAKE, n, s) == SHAPE
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 0, FAKE, FAKE, 16, None, FAKE, 0, FAKE, n, s) == SHAPE
     assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 1, FAKE, FAKE, 65, None, FAKE, 0, FAKE, n, s) == SHAPE
     assert L.rvq_moe_layer_forward(_bank(), FAKE, 2, 1, FAKE, FAKE, 16, None, FAKE, 0, FAKE, n, s) == DTYPE
     assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 1, FAKE, FAKE, 16, None, FAKE, 2, FAKE, n, s) == DTYPE
     assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 1, FAKE, FAKE, 16, None, FAKE, 0, FAKE + 64, n, s) == ALIGN
     assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 1, FAKE, FAKE, 16, None, FAKE, 0, FAKE, n - 1, s) == WS
     assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 1, None, FAKE, 16, None, FAKE, 0, FAKE, n, s) == NULL
+
+
+def test_chunk_workspace_and_validation(L):
+    """T > 1 selects the chunk path: bf16 tokens, f16 or bf16 tiles."""
+    s = None
+    E, H, I, T, k = 256, 7168, 2048, 512, 16
+    n = L.rvq_moe_layer_workspace_bytes(_bank(), T, k, 1)
+    P = T * k
+    up = lambda v: (v + 255) // 256 * 256
+    assert n == 256 + up((E + 1) * 4) + 3 * up(P * 4) + up(P * I * 4) + up(P * H * 4)
+    assert L.rvq_moe_layer_workspace_bytes(_bank(), T, k, 2) == n
+    assert L.rvq_moe_layer_workspace_bytes(_bank(), T, k, 0) == 0          # fp32 tiles: no
+    assert L.rvq_moe_layer_workspace_bytes(_bank(), 5000, k, 1) == 0       # too many tokens
+    assert L.rvq_moe_layer_workspace_bytes(_bank(H=7176), T, k, 1) == 0    # rows not a multiple of 64
+    ok = (FAKE, 2, T, FAKE, FAKE, k, None, FAKE, 1, FAKE, n, s)
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, T, FAKE, FAKE, k, None, FAKE, 1, FAKE, n, s) == DTYPE
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 2, T, FAKE, FAKE, k, None, FAKE, 0, FAKE, n, s) == DTYPE
+    assert L.rvq_moe_layer_forward(_bank(), FAKE + 2, 2, T, FAKE, FAKE, k, None, FAKE, 1, FAKE, n, s) == ALIGN
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 2, T, FAKE, FAKE, k, None, FAKE, 1, FAKE, n - 1, s) == WS
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 2, 5000, FAKE, FAKE, k, None, FAKE, 1, FAKE, n, s) == SHAPE
+    assert L.rvq_moe_layer_forward(_bank(), FAKE, 2, T, FAKE, None, k, None, FAKE, 1, FAKE, n, s) == NULL
+    del ok
 
 
 def test_misc_validation(L):
