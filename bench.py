@@ -207,6 +207,49 @@ def run_graphed(rvq, bank, w, pool, steps, warmup, dtype):
     return steps / (t1 - t0)
 
 
+def run_chunk(rvq, hip, bank, w, xt, steps, dtype):
+    """Chunked prefill of the 512-token bf16 chunk through the same layer: router top-16 for all tokens,
+    then the decode-to-MFMA path.  Returns tokens/s and the mean event time of the MoE part."""
+    import torch
+    dev = xt.device
+    T = xt.shape[0]
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, K), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float64, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = rvq.make_moe_workspace(bank, T, K, dtype)
+    sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    evs = [[hip.event() for _ in range(3)] for _ in range(steps)]
+
+    def step(i):
+        hip.record(evs[i][0], sptr)
+        rvq.router_topk(w, xt, K, ids=ids, gates=gates, logits=logits)
+        hip.record(evs[i][1], sptr)
+        rvq.moe_layer_forward(bank, xt, ids, gates, dtype=dtype, y=y, workspace=ws)
+        hip.record(evs[i][2], sptr)
+
+    step(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    status = rvq.check_device_status(ws)
+    if status:
+        raise RuntimeError(rvq.status_string(status))
+    router_ms = float(np.mean([hip.ms(e[0], e[1]) for e in evs]))
+    moe_ms = float(np.mean([hip.ms(e[1], e[2]) for e in evs]))
+    for ev in evs:
+        for e in ev:
+            hip.destroy(e)
+    tok_s = T * steps / (t1 - t0)
+    flops = 2.0 * T * K * 3 * H * I
+    return {"tokens_per_s": tok_s, "ms_per_chunk": (t1 - t0) / steps * 1e3, "router_ms": router_ms,
+            "moe_ms": moe_ms, "code_GBps": E * 3 * (H * I * 3 // 8) / (moe_ms * 1e-3) / 1e9,
+            "mfma_TFLOPs": flops / (moe_ms * 1e-3) / 1e12, "tile_dtype": dtype}
+
+
 def stream_copy_peak(torch, rvq, dev):
     """Read+write GB/s of rvq_stream_copy over 1 GiB (the code stream's load instruction); its
     rocprofv3 FETCH_SIZE/WRITE_SIZE per dispatch (1 GiB each) calibrate the counters."""
@@ -279,6 +322,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the other table precision")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-chunk", action="store_true", help="skip the 512-token chunked-prefill measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
@@ -309,6 +353,12 @@ def main():
         print(f"[bench] timing {args.steps} steps ({other} tables)", file=sys.stderr, flush=True)
         variants[other] = run_variant(rvq, hip, bank, w, pool, args.steps, args.warmup, other)
         variants[other]["graph_replay_tokens_per_s"] = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, other)
+    chunk = None
+    if not args.no_chunk:
+        print("[bench] chunked prefill (512 tokens)", file=sys.stderr, flush=True)
+        xb = np.stack([synth.activation_bf16_bits(synth.SEED_CHUNK, t, H) for t in range(512)])
+        xt = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+        chunk = {d: run_chunk(rvq, hip, bank, w, xt, 20, d) for d in ("f16", "bf16")}
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -347,6 +397,7 @@ def main():
                      "algorithmic_bytes_per_launch": GATEUP_CODE_BYTES + GATEUP_CODEBOOK_BYTES},
         "cpu_baseline": cpu,
         "variants": variants,
+        "chunk_prefill_512": chunk,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
