@@ -391,7 +391,7 @@ def main():
                   "HIP events recorded around each kernel in an eager timed pass of the same steps",
         "eager_tokens_per_s": main_res["tokens_per_s"],
         "kernel_us": main_res["kernel_us"],
-        "roofline": {"bound": "hbm", "kernel": f"k_moe_gateup_{args.dtype}", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": "k_gateup_ws_f32" if args.dtype == "f32" else "k_moe_gateup_f16", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic_from_profiles(args.dtype),
                      "algorithmic_bytes_per_launch": GATEUP_CODE_BYTES + GATEUP_CODEBOOK_BYTES},

@@ -53,7 +53,8 @@ typedef enum {
   RVQ_ERR_ALIGN = 4,       /* a pointer or stride violates the stated alignment */
   RVQ_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returned */
   RVQ_ERR_EXPERT_ID = 6,   /* (device status) an expert id outside [0, num_experts) was seen */
-  RVQ_ERR_HIP = 7          /* a HIP runtime call failed */
+  RVQ_ERR_HIP = 7,         /* a HIP runtime call failed */
+  RVQ_ERR_DEVICE_STALL = 8 /* (device status) a kernel's bounded internal wait gave up; outputs invalid */
 } rvq_status_t;
 
 typedef enum { RVQ_F32 = 0, RVQ_F16 = 1, RVQ_BF16 = 2 } rvq_dtype_t;
@@ -156,13 +157,20 @@ size_t rvq_bank_record_bytes(int32_t hidden, int32_t inter);
  *   y[t] = residual[t] + sum_{i<k} gates[t][i] * down( silu(gate x_t) * (up x_t) )
  * of expert ids[t][i], silu(z) = z / (1 + exp(-z)).
  * T == 1 (decode): table path; compute_dtype RVQ_F32 or RVQ_F16 (table
- * precision; accumulation is fp32); x_dtype RVQ_F32.
+ * precision; accumulation is fp32); x_dtype RVQ_F32 (4-byte aligned).
+ * 2 <= T <= 4096 (chunked prefill): each expert's tokens are gathered and
+ * multiplied against its codes decoded to matrix-core operands;
+ * compute_dtype RVQ_F16 or RVQ_BF16 (operand precision; accumulation fp32);
+ * x_dtype RVQ_BF16 (16-byte aligned); H and I multiples of 64; and
+ * num_experts * (ceil(T/32) + 1) + 1 <= 16384 (the bucketing bitmap).
+ * No events may be passed for T > 1 (RVQ_ERR_SHAPE).
  * ids, gates: device [T][k] (as written by rvq_router_topk); residual: fp32
  * [T][H] or NULL; y: fp32 [T][H] (may alias residual).
  * An id outside [0, num_experts) contributes zero and sets the sticky device
  * status RVQ_ERR_EXPERT_ID in the workspace (see rvq_check_device_status).
- * workspace: 256-byte aligned, >= rvq_moe_layer_workspace_bytes(...), and
- * zero-filled once by rvq_workspace_init before its first use.
+ * workspace: 256-byte aligned, >= rvq_moe_layer_workspace_bytes(...) for
+ * the same T, k and compute_dtype, and zero-filled once by
+ * rvq_workspace_init before its first use.
  * ------------------------------------------------------------------------ */
 size_t rvq_moe_layer_workspace_bytes(const rvq_expert_bank_t *bank, int32_t T, int32_t k, int32_t compute_dtype);
 int rvq_moe_layer_forward(const rvq_expert_bank_t *bank, const void *x, int32_t x_dtype, int32_t T,
@@ -195,8 +203,9 @@ int rvq_rmsnorm(const float *x, int32_t T, int32_t H, float eps, float *out, hip
 int rvq_stream_copy(const void *src, void *dst, size_t nbytes, hipStream_t stream);
 
 /* Synchronises `stream`, returns the sticky device status held in the
- * workspace of rvq_moe_layer_forward (RVQ_OK or RVQ_ERR_EXPERT_ID) and clears
- * it.  Returns RVQ_ERR_HIP if the synchronisation or copy fails. */
+ * workspace of rvq_moe_layer_forward (RVQ_OK, RVQ_ERR_EXPERT_ID, or
+ * RVQ_ERR_DEVICE_STALL if a kernel's bounded wait between its wave roles gave
+ * up, which leaves y invalid) and clears it.  Returns RVQ_ERR_HIP if the synchronisation or copy fails. */
 int rvq_check_device_status(void *workspace, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -48,6 +48,7 @@ const char* rvq_status_string(int status) {
     case RVQ_ERR_WORKSPACE: return "RVQ_ERR_WORKSPACE: workspace too small";
     case RVQ_ERR_EXPERT_ID: return "RVQ_ERR_EXPERT_ID: an expert id outside [0, num_experts) was seen";
     case RVQ_ERR_HIP: return "RVQ_ERR_HIP: a HIP runtime call failed";
+    case RVQ_ERR_DEVICE_STALL: return "RVQ_ERR_DEVICE_STALL: a kernel's bounded internal wait gave up";
     default: return "RVQ: unknown status";
   }
 }

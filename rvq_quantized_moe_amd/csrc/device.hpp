@@ -36,6 +36,7 @@ constexpr int kWaves = kThreads / 64;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16;
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -164,13 +165,14 @@ __device__ __forceinline__ float group_norm2(float v) {
 // ---------------------------------------------------------------------------------------------
 // Stream loop: each lane owns one row of a 64-row block; per slab it loads 48 code bytes as three
 // 16-byte loads and adds the 48 table entries they select.
-template <int BASE>
+// STRIDE: floats between consecutive subtables (256, or more when padded against bank conflicts).
+template <int BASE, int STRIDE = kEntries>
 __device__ __forceinline__ float gather16_f32(const float* lut, u32x4 d, float acc) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const uint32_t v = d[w];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc += lut[(BASE + 4 * w + k) * kEntries + ((v >> (8 * k)) & 0xffu)];
+    for (int k = 0; k < 4; ++k) acc += lut[(BASE + 4 * w + k) * STRIDE + ((v >> (8 * k)) & 0xffu)];
   }
   return acc;
 }
@@ -208,7 +210,7 @@ __device__ __forceinline__ void load_slabs(SlabData& s, const uint8_t* __restric
   }
 }
 
-template <bool F16>
+template <bool F16, int STRIDE = kEntries>
 __device__ __forceinline__ float gather_slabs(const void* lut, const SlabData& s) {
   float acc = 0.f;
   if constexpr (F16) {
@@ -221,9 +223,9 @@ __device__ __forceinline__ float gather_slabs(const void* lut, const SlabData& s
     acc = gather16_f16<80>(t, s.d[5], acc);
   } else {
     const float* t = static_cast<const float*>(lut);
-    acc = gather16_f32<0>(t, s.d[0], acc);
-    acc = gather16_f32<16>(t, s.d[1], acc);
-    acc = gather16_f32<32>(t, s.d[2], acc);
+    acc = gather16_f32<0, STRIDE>(t, s.d[0], acc);
+    acc = gather16_f32<16, STRIDE>(t, s.d[1], acc);
+    acc = gather16_f32<32, STRIDE>(t, s.d[2], acc);
   }
   return acc;
 }

@@ -422,7 +422,8 @@ hipError_t launch_rmsnorm(const float* x, int T, int H, float eps, float* out, h
 
 // =============================================================================================
 // MoE layer, one decode token.
-//   gate/up:  grid k * 2 * nt_in   -> part_gu[slot][m][tile][row]   (rows of gate/up = I)
+//   gate/up:  grid k * 2 * ngu     -> part_gu[slot][m][part][row]   (rows of gate/up = I; ngu = nt_in
+//             partials, one per K-tile, or fewer when a workgroup sums several K-tiles)
 //   down:     grid k * nt_out * P  -> part_d[slot][tile][row]        (rows of down = H)
 //             (each workgroup first rebuilds its 8*G entries of h = silu(g) * u from part_gu)
 //   combine:  y[r] = residual[r] + sum_slot gate[slot] * sum_tile part_d[slot][tile][r]
@@ -463,6 +464,166 @@ __device__ __forceinline__ void k_moe_gateup_body(BankArgs bank, const float* __
   rs.run(lut, out_scale, part_gu + (((int64_t)slot * 2 + m) * nt + tile) * pad_rows(I));
 }
 
+// ---------------------------------------------------------------------------------------------
+// Wave-specialised gate/up kernel (fp32 tables), one 12-wave workgroup per CU.
+//
+// Workgroup b owns ITEMS consecutive 16-group K-tiles of one (expert slot, matrix): gm = b / nchunk,
+// tiles ITEMS (b % nchunk) + [0, ITEMS).  Waves 0-7 stream the 2048-row code tiles through the
+// tables and keep one running sum per row across the items, so each workgroup writes one partial
+// row vector (nchunk partials per row instead of one per K-tile).  Waves 8-11 build the next
+// item's tables into the other half of a double buffer while the streamers gather.  The roles
+// exchange LDS counters with workgroup-scope release/acquire instead of barriers:
+//   built[k%2] += 1 per builder wave when its share of item k's tables is written;
+//                 streamers start item k at built[k%2] >= 4 (floor(k/2) + 1);
+//   done[k%2]  += 1 per streamer wave when it has read item k's tables;
+//                 builders overwrite buffer k%2 (item k >= 2) at done[k%2] >= 8 floor(k/2).
+// The counts are per buffer so a sum cannot be reached early: a builder wave can only get to item
+// k+2 once every streamer is past item k, hence when built[k%2] first reaches its target each
+// builder wave has added exactly floor(k/2)+1 to it (and likewise for done).  Neither role waits on
+// itself, so the waits end; each is still bounded (kSpinLimit polls, after which the kernel records
+// RVQ_ERR_DEVICE_STALL rather than hang).
+//
+// The tables of one item are the product of the 768 x 8 codebook (3 stages x 256 entries) with the
+// 8 x 16 matrix of the tile's x sub-vectors, computed with fp32 MFMAs: builder wave w owns 16-entry
+// table tiles 12w .. 12w+11.  With lane l = 16q + i (q < 4), A holds codebook entry i of the table
+// tile at dims 2q, 2q+1 (one per MFMA), B holds group i's x at the same dims, and D returns
+// entries 4q..4q+3 of group i, stored as one 16-byte LDS write (conflict-free because subtables
+// are kPipeStride = 260 floats apart).  The codebook operands are the same for every item of the
+// workgroup, and every item's x operands are loaded at the start, so builds never wait on memory.
+constexpr int kPipeStreamWaves = 8, kPipeBuildWaves = 4;
+constexpr int kPipeThreads = 64 * (kPipeStreamWaves + kPipeBuildWaves);
+constexpr int kPipeRowBlocks = 32;     // row blocks of a gate/up matrix this kernel handles (I = 2048)
+constexpr int kPipeStride = 260;       // floats between subtables
+constexpr int kPipeMaxItems = 8;
+constexpr int kSpinLimit = 1 << 22;
+constexpr int kStatusStall = 8;        // RVQ_ERR_DEVICE_STALL
+
+__device__ inline bool lds_wait_ge(int* flag, int target) {
+  for (int i = 0; i < kSpinLimit; ++i) {
+    if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return false;
+}
+
+// Compute units of the current device (0 if the query fails), cached per device.
+static int compute_units() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev >= 64) {
+    int n = 0;
+    return hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? n : 0;
+  }
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+template <int ITEMS>
+__global__ __launch_bounds__(kPipeThreads) void k_gateup_ws_f32(BankArgs bank, const float* __restrict__ x,
+                                                               const int32_t* __restrict__ ids,
+                                                               float* __restrict__ part_gu,
+                                                               int32_t* __restrict__ status, int nchunk) {
+  constexpr int BPI = kPipeRowBlocks / kPipeStreamWaves;   // row blocks per streamer wave
+  constexpr int NB = 3;   // row blocks of codes held per wave (deeper measured slower)
+  constexpr int NBLK = ITEMS * BPI;
+  constexpr int TPW = 48 / kPipeBuildWaves;                 // table tiles per builder wave
+  constexpr int64_t kTileBytes = (int64_t)kPipeRowBlocks * kSlabBytes;
+  __shared__ __attribute__((aligned(16))) float lut[2][48 * kPipeStride];
+  __shared__ int built[2], done[2];
+  const int H = bank.H, I = bank.I;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int gm = blockIdx.x / nchunk;                       // slot * 2 + matrix
+  const int t0 = (blockIdx.x - gm * nchunk) * ITEMS;
+  int e = ids[gm >> 1];
+  const bool bad = e < 0 || e >= bank.E;
+  if (bad) e = 0;  // recorded below; this slot's results are never read
+  const bool streamer = wave < kPipeStreamWaves;
+
+  // builder operands are requested before the start barrier, i.e. ahead of the code stream
+  const int bw = wave - kPipeStreamWaves;
+  const int q = lane >> 4, i16 = lane & 15;
+  f32x2 a[TPW], xb[ITEMS];
+  if (!streamer) {
+    const float* cb = bank.cb + ((int64_t)e * 3 + (gm & 1)) * kCodebookFloats;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) a[t] = *reinterpret_cast<const f32x2*>(cb + ((bw * TPW + t) * 16 + i16) * 8 + 2 * q);
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) xb[k] = *reinterpret_cast<const f32x2*>(x + (int64_t)(t0 + k) * 128 + i16 * 8 + 2 * q);
+  } else if (threadIdx.x == 0) {
+    built[0] = 0;
+    built[1] = 0;
+    done[0] = 0;
+    done[1] = 0;
+    if (bad) atomicExch(status, 6 /* RVQ_ERR_EXPERT_ID */);
+  }
+  __syncthreads();
+
+  if (streamer) {
+    // ----------------------------------------------------------------- streamers
+    const uint8_t* codes = bank.codes + (int64_t)e * bank.stride + (int64_t)(gm & 1) * packed_bytes(I, H) +
+                           (int64_t)t0 * kTileBytes;
+    SlabData buf[NB];
+    const uint32_t lane_off = lane * 16;
+    auto load_blk = [&](int i, int s) {
+      const int k = s / BPI, r = s % BPI;
+      load_slabs<false>(buf[i], codes + k * kTileBytes, codes + k * kTileBytes,
+                        (uint32_t)(wave + kPipeStreamWaves * r) * kSlabBytes + lane_off);
+    };
+#pragma unroll
+    for (int i = 0; i < NB; ++i) load_blk(i, i);
+    float acc[BPI];
+#pragma unroll
+    for (int r = 0; r < BPI; ++r) acc[r] = 0.f;
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1));
+#pragma unroll
+      for (int r = 0; r < BPI; ++r) {
+        const int s = k * BPI + r;
+        const float g = gather_slabs<false, kPipeStride>(lut[k & 1], buf[s % NB]);
+        // opaque use: without it the compiler interleaves the row blocks' gathers into one
+        // another and spills
+        asm volatile("" : : "v"(g));
+        acc[r] += g;
+        if (s + NB < NBLK) load_blk(s % NB, s + NB);
+      }
+      if (lane == 0) __hip_atomic_fetch_add(&done[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    float* out = part_gu + (int64_t)blockIdx.x * pad_rows(I);
+#pragma unroll
+    for (int r = 0; r < BPI; ++r) out[(wave + kPipeStreamWaves * r) * kSlabRows + lane] = acc[r];
+    if (!ok && lane == 0) atomicExch(status, kStatusStall);
+  } else {
+    // ----------------------------------------------------------------- builders
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      if (k >= 2) ok &= lds_wait_ge(&done[k & 1], kPipeStreamWaves * (k / 2));
+      // an opaque copy pins this item's products after the wait (otherwise the compiler computes
+      // every item's tables up front and spills them)
+      f32x2 xk = xb[k];
+      asm volatile("" : "+v"(xk));
+      float* L = lut[k & 1];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int ti = bw * TPW + t, st = ti >> 4, e0 = (ti & 15) * 16;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].x, xk.x, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].y, xk.y, d, 0, 0, 0);
+        *reinterpret_cast<f32x4*>(&L[(3 * i16 + st) * kPipeStride + e0 + 4 * q]) = d;
+      }
+      if (lane == 0) __hip_atomic_fetch_add(&built[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if (!ok && lane == 0) atomicExch(status, kStatusStall);
+  }
+}
+
 // gate/up: 4-wave workgroups, three per CU (LDS-bound), so three workgroups' table builds and
 // streams interleave on each CU.
 constexpr int kGateUpThreads = 256;
@@ -482,7 +643,7 @@ __global__ __launch_bounds__(kGateUpThreads) __attribute__((amdgpu_waves_per_eu(
 template <bool F16, int BPW, int NT>
 __device__ __forceinline__ void k_moe_down_body(BankArgs bank, const int32_t* __restrict__ ids,
                                                        const float* __restrict__ part_gu, float* __restrict__ part_d,
-                                                       int nparts) {
+                                                       int nparts, int ngu) {
   constexpr int G = Tile<F16>::kGroups;
   constexpr int V = G * 8;              // entries of h this tile consumes
   constexpr int S = NT / V;             // threads cooperating on one entry's tile sums
@@ -493,7 +654,7 @@ __device__ __forceinline__ void k_moe_down_body(BankArgs bank, const int32_t* __
   const int H = bank.H, I = bank.I;
   const int groups = I / 8;
   const int nt = (int)cdiv(groups, G);
-  const int nt_in = (int)cdiv(H / 8, G);
+  const int nt_in = ngu;   // gate/up partial sums per row
   const int p = blockIdx.x % nparts;
   const int tile = (blockIdx.x / nparts) % nt;
   const int slot = blockIdx.x / (nparts * nt);
@@ -566,14 +727,14 @@ constexpr int kDownThreads = 1024;
 template <int BPW>
 __global__ __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_moe_down_f32(
     BankArgs bank, const int32_t* __restrict__ ids, const float* __restrict__ part_gu, float* __restrict__ part_d,
-    int nparts) {
-  k_moe_down_body<false, BPW, kDownThreads>(bank, ids, part_gu, part_d, nparts);
+    int nparts, int ngu) {
+  k_moe_down_body<false, BPW, kDownThreads>(bank, ids, part_gu, part_d, nparts, ngu);
 }
 template <int BPW>
 __global__ __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_moe_down_f16(
     BankArgs bank, const int32_t* __restrict__ ids, const float* __restrict__ part_gu, float* __restrict__ part_d,
-    int nparts) {
-  k_moe_down_body<true, BPW, kDownThreads>(bank, ids, part_gu, part_d, nparts);
+    int nparts, int ngu) {
+  k_moe_down_body<true, BPW, kDownThreads>(bank, ids, part_gu, part_d, nparts, ngu);
 }
 
 // Gated combine.  Workgroup = 64 rows x 8 waves; wave q sums slots q, q+8, ... over all tiles (loads
@@ -646,9 +807,33 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
     if (ev && err == hipSuccess) err = hipEventRecord(ev[i], stream);
   };
   mark(0);
+  // The wave-specialised gate/up kernel takes fp32 tables, I in (1984, 2048] and whole 16-group
+  // tiles; it sums `chunk` K-tiles per workgroup, chosen to fill the CUs in as few rounds as possible
+  // (ties: the larger chunk, i.e. fewer partials).
+  const int ncu = compute_units();
+  int chunk = 0;
+  if (!f16 && (H / 8) % 16 == 0 && (int)cdiv(I, kSlabRows) == kPipeRowBlocks && ncu > 0) {
+    long best = 0;
+    for (int c = 1; c <= kPipeMaxItems; ++c) {
+      if (w.nt_in % c != 0) continue;
+      const long grid = (long)k * 2 * (w.nt_in / c);
+      const long cost = (grid + ncu - 1) / ncu * c;
+      if (chunk == 0 || cost <= best) best = cost, chunk = c;
+    }
+  }
+  const int ngu = chunk ? w.nt_in / chunk : w.nt_in;
   const int bpw_gu = pick_bpw((int)cdiv(I, kSlabRows), 1, kGateUpThreads / 64);
   const int bpw_d = pick_bpw((int)cdiv(H, kSlabRows), nparts, kDownThreads / 64);
-  if (f16) {
+  if (chunk) {
+    const dim3 grid((unsigned)(k * 2 * ngu));
+    switch (chunk) {
+#define RVQ_WS_CASE(n) \
+  case n: hipLaunchKernelGGL((k_gateup_ws_f32<n>), grid, dim3(kPipeThreads), 0, stream, bank, x, ids, part_gu, status, ngu); break;
+      RVQ_WS_CASE(1) RVQ_WS_CASE(2) RVQ_WS_CASE(3) RVQ_WS_CASE(4)
+      RVQ_WS_CASE(5) RVQ_WS_CASE(6) RVQ_WS_CASE(7) RVQ_WS_CASE(8)
+#undef RVQ_WS_CASE
+    }
+  } else if (f16) {
     RVQ_BPW_DISPATCH(bpw_gu, hipLaunchKernelGGL((k_moe_gateup_f16<B>), dim3(k * 2 * w.nt_in), dim3(kGateUpThreads), 0,
                                                 stream, bank, x, ids, part_gu, status))
   } else {
@@ -658,10 +843,10 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
   mark(1);
   if (f16) {
     RVQ_BPW_DISPATCH(bpw_d, hipLaunchKernelGGL((k_moe_down_f16<B>), dim3(k * w.nt_out * nparts), dim3(kDownThreads), 0,
-                                               stream, bank, ids, part_gu, part_d, nparts))
+                                               stream, bank, ids, part_gu, part_d, nparts, ngu))
   } else {
     RVQ_BPW_DISPATCH(bpw_d, hipLaunchKernelGGL((k_moe_down_f32<B>), dim3(k * w.nt_out * nparts), dim3(kDownThreads), 0,
-                                               stream, bank, ids, part_gu, part_d, nparts))
+                                               stream, bank, ids, part_gu, part_d, nparts, ngu))
   }
   mark(2);
   hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)cdiv(H, 64)), dim3(512), 0, stream, part_d, w.nt_out, H, ids,
