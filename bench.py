@@ -173,9 +173,10 @@ def run_variant(rvq, hip, bank, w, pool, steps, warmup, dtype):
     }
 
 
-def run_graphed(rvq, bank, w, pool, steps, warmup, dtype):
-    """The same step replayed from HIP graphs (one graph per pool token: router top-k + MoE layer),
-    which removes host launch overhead; returns tokens/s over `steps` replays."""
+def run_graphed(rvq, bank, w, pool, steps, warmup, dtype, routed=True):
+    """The step replayed from HIP graphs (one graph per pool token), which removes host launch
+    overhead; returns tokens/s over `steps` replays.  routed: one rvq_moe_decode_routed call (router,
+    top-k inside the gate/up kernel, experts); else rvq_router_topk + rvq_moe_layer_forward."""
     import torch
     dev = pool.device
     ids = torch.empty((1, K), dtype=torch.int32, device=dev)
@@ -189,8 +190,12 @@ def run_graphed(rvq, bank, w, pool, steps, warmup, dtype):
     for j in range(POOL):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
-            rvq.router_topk(w, pool[j], K, ids=ids, gates=gates, logits=logits)
-            rvq.moe_layer_forward(bank, pool[j], ids[0], gates[0], dtype=dtype, y=y, workspace=ws)
+            if routed:
+                rvq.moe_decode_routed(bank, w, pool[j], K, dtype=dtype, y=y, ids=ids[0], gates=gates[0],
+                                      logits=logits[0], workspace=ws)
+            else:
+                rvq.router_topk(w, pool[j], K, ids=ids, gates=gates, logits=logits)
+                rvq.moe_layer_forward(bank, pool[j], ids[0], gates[0], dtype=dtype, y=y, workspace=ws)
         graphs.append(g)
     for i in range(warmup):
         graphs[i % POOL].replay()
@@ -347,6 +352,7 @@ def main():
     main_res = run_variant(rvq, hip, bank, w, pool, args.steps, args.warmup, args.dtype)
     print("[bench] graph replay", file=sys.stderr, flush=True)
     graph_tok_s = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype)
+    graph_two_call = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, routed=False)
     variants = {}
     if not args.no_variants:
         other = "f16" if args.dtype == "f32" else "f32"
@@ -387,11 +393,13 @@ def main():
         "code_frac_of_stream_copy": CODE_BYTES_PER_TOKEN * graph_tok_s / 1e9 / copy_gbps,
         "stream_copy_GBps": copy_gbps,
         "decoded_weights_per_s": WEIGHTS_PER_TOKEN * graph_tok_s,
-        "timing": "value: HIP-graph replay of the step (one graph per pool token); kernel_us and roofline: "
-                  "HIP events recorded around each kernel in an eager timed pass of the same steps",
+        "timing": "value: HIP-graph replay of one rvq_moe_decode_routed step per token (one graph per pool "
+                  "token); kernel_us and roofline: HIP events around each kernel of the two-call form "
+                  "(rvq_router_topk, rvq_moe_layer_forward_timed) in an eager timed pass of the same steps",
+        "graph_two_call_tokens_per_s": graph_two_call,
         "eager_tokens_per_s": main_res["tokens_per_s"],
         "kernel_us": main_res["kernel_us"],
-        "roofline": {"bound": "hbm", "kernel": "k_gateup_ws_f32" if args.dtype == "f32" else "k_moe_gateup_f16", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": "k_table_ws_f32<gate/up>" if args.dtype == "f32" else "k_moe_gateup_f16", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic_from_profiles(args.dtype),
                      "algorithmic_bytes_per_launch": GATEUP_CODE_BYTES + GATEUP_CODEBOOK_BYTES},

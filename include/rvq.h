@@ -130,7 +130,8 @@ int rvq_expert_gemv(const rvq_matrix_t *W, const float *x, int32_t lut_dtype, fl
  * gates = softmax over those k logits (= softmax over all E renormalised to
  * the selected k).
  * w_router: bf16 [E][H]; x: [T][H] of x_dtype RVQ_F32 or RVQ_BF16;
- * ids: int32 [T][k]; gates: fp32 [T][k]; logits: double [T][E] or NULL.
+ * ids: int32 [T][k]; gates: fp32 [T][k]; logits: double [T][E], written
+ * (the selection reads it back).
  * 1 <= k <= E <= 4096, k <= 64, H >= 1, T >= 1.  No workspace.
  * ------------------------------------------------------------------------ */
 int rvq_router_topk(const void *w_router_bf16, const void *x, int32_t x_dtype, int32_t T, int32_t E, int32_t H,
@@ -186,6 +187,23 @@ int rvq_moe_layer_forward_timed(const rvq_expert_bank_t *bank, const void *x, in
                                 const int32_t *ids, const float *gates, int32_t k, const float *residual, float *y,
                                 int32_t compute_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t *events);
+
+/* ------------------------------------------------------------------------
+ * One routed decode step for one token: the router and top-k of
+ * rvq_router_topk (T = 1, x_dtype RVQ_F32) followed by rvq_moe_layer_forward
+ * (T = 1) on the selected experts, with the same results as calling the two.
+ * Where the gate/up kernel can (fp32 tables, the shapes its wave-specialised
+ * form takes, num_experts <= 1024), each of its workgroups takes the top-k
+ * itself instead of a separate selection kernel.
+ * w_router: bf16 [E][H]; x: fp32 [H]; residual: fp32 [H] or NULL; y: fp32
+ * [H] (may alias residual); ids: int32 [k], gates: fp32 [k], logits: fp64
+ * [E]: all written.  compute_dtype: RVQ_F32 or RVQ_F16 (table precision).
+ * workspace: as for rvq_moe_layer_forward with T = 1 and the same k and
+ * compute_dtype.  1 <= k <= min(64, E), E <= 4096.
+ * ------------------------------------------------------------------------ */
+int rvq_moe_decode_routed(const rvq_expert_bank_t *bank, const void *w_router_bf16, const float *x, int32_t k,
+                          const float *residual, float *y, int32_t *ids, float *gates, double *logits,
+                          int32_t compute_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Zero-fill a workspace (with a kernel, so the call can be graph-captured). */
 int rvq_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);

@@ -43,7 +43,7 @@ EXPORTS = [
     "rvq_expert_gemv_workspace_bytes", "rvq_expert_gemv", "rvq_router_topk", "rvq_bank_record_bytes",
     "rvq_moe_layer_workspace_bytes", "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed",
     "rvq_workspace_init", "rvq_rmsnorm", "rvq_stream_copy",
-    "rvq_check_device_status",
+    "rvq_check_device_status", "rvq_moe_decode_routed",
 ]
 
 
@@ -77,9 +77,10 @@ def lib():
         L.rvq_rmsnorm.argtypes = [p, i32, i32, ctypes.c_float, p, p]
         L.rvq_check_device_status.argtypes = [p, p]
         L.rvq_stream_copy.argtypes = [p, p, sz, p]
+        L.rvq_moe_decode_routed.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, p, p, p, p, p, i32, p, sz, p]
         for name in ("rvq_pack_codes", "rvq_lut_build", "rvq_expert_gemv", "rvq_router_topk",
                      "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed", "rvq_workspace_init", "rvq_rmsnorm",
-                     "rvq_check_device_status", "rvq_stream_copy"):
+                     "rvq_check_device_status", "rvq_stream_copy", "rvq_moe_decode_routed"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -325,3 +326,29 @@ def moe_layer_forward(bank, x, ids, gates, residual=None, dtype="f32", y=None, w
         arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(int(e)) for e in events])
         _check(lib().rvq_moe_layer_forward_timed(*args, arr))
     return y
+
+
+def moe_decode_routed(bank, w_router, x, k, residual=None, dtype="f32", y=None, ids=None, gates=None, logits=None,
+                      workspace=None):
+    """One routed decode step: router top-k of w_router (bf16 [E, H]) on x (fp32 [H]), then
+    y = [residual +] sum_i gates[i] * expert_{ids[i]}(x).  Returns (y, ids, gates, logits)."""
+    _dev(w_router, torch.bfloat16, "w_router")
+    _dev(x, torch.float32, "x")
+    E, H = w_router.shape
+    if E != bank.E or H != bank.H:
+        raise ValueError("router shape does not match the bank")
+    dev = x.device
+    d = _table_dtype(dtype)
+    if residual is not None:
+        _dev(residual, torch.float32, "residual")
+    y = torch.empty(H, dtype=torch.float32, device=dev) if y is None else y
+    ids = torch.empty(k, dtype=torch.int32, device=dev) if ids is None else ids
+    gates = torch.empty(k, dtype=torch.float32, device=dev) if gates is None else gates
+    logits = torch.empty(E, dtype=torch.float64, device=dev) if logits is None else logits
+    if workspace is None:
+        workspace = make_moe_workspace(bank, 1, k, d)
+    desc = bank.desc()
+    _check(lib().rvq_moe_decode_routed(ctypes.byref(desc), _ptr(w_router), _ptr(x), k, _ptr(residual), _ptr(y),
+                                       _ptr(ids), _ptr(gates), _ptr(logits), d, _ptr(workspace), workspace.numel(),
+                                       _stream(x)))
+    return y, ids, gates, logits

@@ -183,6 +183,28 @@ int rvq_moe_layer_forward_timed(const rvq_expert_bank_t* bank, const void* x, in
                                 workspace_bytes, stream, events);
 }
 
+int rvq_moe_decode_routed(const rvq_expert_bank_t* bank, const void* w_router_bf16, const float* x, int32_t k,
+                          const float* residual, float* y, int32_t* ids, float* gates, double* logits,
+                          int32_t compute_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_bank(bank);
+  if (st != RVQ_OK) return st;
+  if (!w_router_bf16 || !x || !y || !ids || !gates || !logits || !workspace) return RVQ_ERR_NULL;
+  if (k < 1 || k > kMaxTopK || k > bank->num_experts || bank->num_experts > kMaxExperts) return RVQ_ERR_SHAPE;
+  if (!table_dtype(compute_dtype)) return RVQ_ERR_DTYPE;
+  if (!aligned(workspace, 256) || !aligned(w_router_bf16, 2) || !aligned(x, 4) || !aligned(y, 4) ||
+      !aligned(ids, 4) || !aligned(gates, 4) || !aligned(logits, 8) || (residual && !aligned(residual, 4)))
+    return RVQ_ERR_ALIGN;
+  const bool f16 = compute_dtype == RVQ_F16;
+  if (workspace_bytes < moe_workspace_layout(bank->hidden, bank->inter, k, f16).total) return RVQ_ERR_WORKSPACE;
+  const hipError_t err = launch_router_logits(static_cast<const uint16_t*>(w_router_bf16), x, false, 1,
+                                              bank->num_experts, bank->hidden, logits, stream);
+  if (err != hipSuccess) return RVQ_ERR_HIP;
+  const Route route{logits, ids, gates};
+  return hip_status(launch_moe_decode(bank->codes, bank->codebooks, bank->record_stride, bank->num_experts,
+                                      bank->hidden, bank->inter, x, nullptr, nullptr, k, residual, y, f16, workspace,
+                                      stream, nullptr, &route));
+}
+
 int rvq_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!workspace) return RVQ_ERR_NULL;
   if (!aligned(workspace, 256)) return RVQ_ERR_ALIGN;

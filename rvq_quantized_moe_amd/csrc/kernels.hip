@@ -337,51 +337,86 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 }
 
 // Top-k by (logit desc, id asc): the rank of e is the number of experts that precede it in that
-// order; ranks < k are kept, at position rank.  P consecutive lanes share one expert's comparisons
-// (each compares against every P-th logit; their counts are summed by shuffles).  gates = softmax
-// over the kept logits in fp64, summed by a fixed shuffle tree.
-__global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ logits, int E, int k,
-                                               int32_t* __restrict__ ids, float* __restrict__ gates) {
-  __shared__ double L[kMaxExperts];
-  __shared__ int sel[kMaxTopK];
-  const int t = blockIdx.x;
-  if (threadIdx.x < kMaxTopK) sel[threadIdx.x] = 0;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) L[e] = logits[(int64_t)t * E + e];
-  __syncthreads();
-  int P = (int)(blockDim.x / E);
-  P = P >= 64 ? 64 : P >= 32 ? 32 : P >= 16 ? 16 : P >= 8 ? 8 : P >= 4 ? 4 : P >= 2 ? 2 : 1;
-  const int sub = threadIdx.x % P;
-  const int per_pass = blockDim.x / P;
-  for (int base = 0; base < E; base += per_pass) {
-    const int e = base + threadIdx.x / P;
+// order; ranks < k are kept, at position rank.  Experts are taken 64 to a wave (lane = expert) and
+// the comparisons split into 64-expert blocks of j: wave (b, r) counts, for experts 64b + lane,
+// the j of the blocks r, r + R, ...  A block entirely before expert block b needs only L[j] >= L[e],
+// one entirely after it only L[j] > L[e]; only the diagonal block compares ids.  The partial counts
+// are integers, so adding them (LDS atomics) in any order is exact.  cnt[0..E) must be zero.
+__device__ void topk_ranks(const double* L, int* cnt, int E) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  const int nb = (E + 63) >> 6;                       // expert blocks
+  const int R = nw / nb > 1 ? nw / nb : 1;            // j-ranges per expert block
+  for (int task = wave; task < nb * R; task += nw) {
+    const int b = task / R, r = task - b * R;
+    const int e = b * 64 + lane;
+    const double le = L[e < E ? e : E - 1];
     int rank = 0;
-    if (e < E) {
-      const double le = L[e];
-      for (int j = sub; j < E; j += P) {
-        const double lj = L[j];
-        rank += (lj > le) || (lj == le && j < e);
+    for (int jb = r; jb < nb; jb += R) {
+      const int j0 = jb * 64;
+      const int jn = E - j0 < 64 ? E - j0 : 64;
+      if (jb < b) {
+#pragma unroll 8
+        for (int jj = 0; jj < jn; ++jj) rank += L[j0 + jj] >= le;
+      } else if (jb > b) {
+#pragma unroll 8
+        for (int jj = 0; jj < jn; ++jj) rank += L[j0 + jj] > le;
+      } else {
+#pragma unroll 8
+        for (int jj = 0; jj < jn; ++jj) {
+          const double lj = L[j0 + jj];
+          rank += (lj > le) || (lj == le && jj < lane);
+        }
       }
     }
-    for (int off = 1; off < P; off <<= 1) rank += __shfl_xor(rank, off, 64);
-    if (e < E && sub == 0 && rank < k) sel[rank] = e;
-  }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int i = threadIdx.x;
-    const double m = L[sel[0]];
-    const double ex = i < k ? exp(L[sel[i]] - m) : 0.0;
-    double z = ex;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
-    if (i < k) {
-      ids[(int64_t)t * k + i] = sel[i];
-      gates[(int64_t)t * k + i] = (float)(ex / z);
-    }
+    if (e < E) atomicAdd(&cnt[e], rank);
   }
 }
 
-hipError_t launch_router_topk(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, int k, int32_t* ids,
-                              float* gates, double* logits, hipStream_t stream) {
+// sel[rank] = e for the experts ranked below k.
+__device__ void topk_select(const int* cnt, int E, int k, int* sel) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    if (cnt[e] < k) sel[cnt[e]] = e;
+}
+
+// Called by one whole wave: gates = softmax over the kept logits in fp64 (max subtracted), the
+// denominator summed by a fixed shuffle tree over ranks; writes ids/gates[i] for i < k with
+// want(i) true.
+template <typename Want>
+__device__ void topk_gates(const double* L, const int* sel, int k, int32_t* ids, float* gates, Want want) {
+  const int i = threadIdx.x & 63;
+  const double m = L[sel[0]];
+  const double ex = i < k ? exp(L[sel[i]] - m) : 0.0;
+  double z = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+  if (i < k && want(i)) {
+    ids[i] = sel[i];
+    gates[i] = (float)(ex / z);
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ logits, int E, int k,
+                                               int32_t* __restrict__ ids, float* __restrict__ gates) {
+  __shared__ double L[kMaxExperts];
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int sel[kMaxTopK];
+  const int t = blockIdx.x;
+  if (threadIdx.x < kMaxTopK) sel[threadIdx.x] = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    L[e] = logits[(int64_t)t * E + e];
+    cnt[e] = 0;
+  }
+  __syncthreads();
+  topk_ranks(L, cnt, E);
+  __syncthreads();
+  topk_select(cnt, E, k, sel);
+  __syncthreads();
+  if (threadIdx.x < 64) topk_gates(L, sel, k, ids + (int64_t)t * k, gates + (int64_t)t * k, [](int) { return true; });
+}
+
+hipError_t launch_router_logits(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, double* logits,
+                                hipStream_t stream) {
   const int vec = (H % 8 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0) &&
                   ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
   dim3 grid((unsigned)E, (unsigned)T);
@@ -391,7 +426,12 @@ hipError_t launch_router_topk(const uint16_t* w, const void* x, bool x_bf16, int
   else
     hipLaunchKernelGGL(k_router_logits<float>, grid, dim3(256), 0, stream, w, static_cast<const float*>(x), T, E, H,
                        logits, vec);
-  hipError_t err = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_router_topk(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, int k, int32_t* ids,
+                              float* gates, double* logits, hipStream_t stream) {
+  const hipError_t err = launch_router_logits(w, x, x_bf16, T, E, H, logits, stream);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_topk, dim3((unsigned)T), dim3(1024), 0, stream, logits, E, k, ids, gates);
   return hipGetLastError();
@@ -465,18 +505,22 @@ __device__ __forceinline__ void k_moe_gateup_body(BankArgs bank, const float* __
 }
 
 // ---------------------------------------------------------------------------------------------
-// Wave-specialised gate/up kernel (fp32 tables), one 12-wave workgroup per CU.
+// Wave-specialised table kernels (fp32 tables): one workgroup per CU, NSW streamer waves and 4
+// builder waves.
 //
-// Workgroup b owns ITEMS consecutive 16-group K-tiles of one (expert slot, matrix): gm = b / nchunk,
-// tiles ITEMS (b % nchunk) + [0, ITEMS).  Waves 0-7 stream the 2048-row code tiles through the
-// tables and keep one running sum per row across the items, so each workgroup writes one partial
-// row vector (nchunk partials per row instead of one per K-tile).  Waves 8-11 build the next
-// item's tables into the other half of a double buffer while the streamers gather.  The roles
-// exchange LDS counters with workgroup-scope release/acquire instead of barriers:
+// A workgroup owns ITEMS consecutive 16-group K-tiles of one matrix and a range of NSW * BPI row
+// blocks.  The streamer waves stream those rows' codes through each K-tile's tables in turn and keep
+// one running sum per row, so the workgroup writes one partial row vector.  The builder waves build
+// the next K-tile's tables into the other half of a double buffer while the streamers gather.
+//   gate/up (DOWN = false): workgroup b -> gm = b / nchunk (slot * 2 + matrix), K-tiles
+//            ITEMS (b % nchunk) + [0, ITEMS), all 32 row blocks; partial row vector b of part_gu.
+//   down    (DOWN = true):  workgroup b -> slot, row chunk rc, K-tile chunk kc (kc fastest); its
+//            x operand is h = silu(g) * u, where g and u sum the `ngu` gate and up partials.
+// The roles exchange LDS counters with workgroup-scope release/acquire instead of barriers:
 //   built[k%2] += 1 per builder wave when its share of item k's tables is written;
 //                 streamers start item k at built[k%2] >= 4 (floor(k/2) + 1);
 //   done[k%2]  += 1 per streamer wave when it has read item k's tables;
-//                 builders overwrite buffer k%2 (item k >= 2) at done[k%2] >= 8 floor(k/2).
+//                 builders overwrite buffer k%2 (item k >= 2) at done[k%2] >= NSW floor(k/2).
 // The counts are per buffer so a sum cannot be reached early: a builder wave can only get to item
 // k+2 once every streamer is past item k, hence when built[k%2] first reaches its target each
 // builder wave has added exactly floor(k/2)+1 to it (and likewise for done).  Neither role waits on
@@ -489,12 +533,13 @@ __device__ __forceinline__ void k_moe_gateup_body(BankArgs bank, const float* __
 // tile at dims 2q, 2q+1 (one per MFMA), B holds group i's x at the same dims, and D returns
 // entries 4q..4q+3 of group i, stored as one 16-byte LDS write (conflict-free because subtables
 // are kPipeStride = 260 floats apart).  The codebook operands are the same for every item of the
-// workgroup, and every item's x operands are loaded at the start, so builds never wait on memory.
-constexpr int kPipeStreamWaves = 8, kPipeBuildWaves = 4;
-constexpr int kPipeThreads = 64 * (kPipeStreamWaves + kPipeBuildWaves);
-constexpr int kPipeRowBlocks = 32;     // row blocks of a gate/up matrix this kernel handles (I = 2048)
+// workgroup and are loaded once, before the start barrier.
+constexpr int kPipeBuildWaves = 4;
 constexpr int kPipeStride = 260;       // floats between subtables
 constexpr int kPipeMaxItems = 8;
+constexpr int kPipeMaxGu = 8;          // down: most gate/up partials per row
+constexpr int kGuStreamWaves = 8, kGuBpi = 4;     // gate/up: 32 row blocks (I in (1984, 2048])
+constexpr int kDnStreamWaves = 7, kDnBpi = 4;     // down: row chunks of 28 row blocks
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kStatusStall = 8;        // RVQ_ERR_DEVICE_STALL
 
@@ -522,57 +567,146 @@ static int compute_units() {
   return cache[dev];
 }
 
-template <int ITEMS>
-__global__ __launch_bounds__(kPipeThreads) void k_gateup_ws_f32(BankArgs bank, const float* __restrict__ x,
-                                                               const int32_t* __restrict__ ids,
-                                                               float* __restrict__ part_gu,
-                                                               int32_t* __restrict__ status, int nchunk) {
-  constexpr int BPI = kPipeRowBlocks / kPipeStreamWaves;   // row blocks per streamer wave
-  constexpr int NB = 3;   // row blocks of codes held per wave (deeper measured slower)
+struct PipeArgs {
+  const float* x;         // gate/up: fp32 [H]
+  const float* part_gu;   // down: gate/up partials [k][2][ngu][pad_rows(I)]
+  float* out;             // gate/up: part_gu; down: part_d [k][nkc][pad_rows(H)]
+  int nchunk;             // gate/up: workgroups per matrix; down: K-tile chunks per slot (nkc)
+  int nrc;                // down: row chunks per slot
+  int ngu;                // down: gate/up partials per row
+  // gate/up with routing: when logits is set the workgroup picks its slot's expert itself (the
+  // top-k of logits[0..E)), and the first workgroup of each slot writes ids/gates[slot]
+  const double* logits;
+  int32_t* ids_out;
+  float* gates_out;
+  int k;
+};
+constexpr int kRouteMaxExperts = 1024;
+
+template <bool DOWN, int NSW, int BPI, int ITEMS>
+__global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws_f32(BankArgs bank,
+                                                                             const int32_t* __restrict__ ids,
+                                                                             int32_t* __restrict__ status,
+                                                                             PipeArgs pa) {
+  constexpr int NB = 3;   // row blocks of codes held per streamer wave (deeper measured slower)
   constexpr int NBLK = ITEMS * BPI;
   constexpr int TPW = 48 / kPipeBuildWaves;                 // table tiles per builder wave
-  constexpr int64_t kTileBytes = (int64_t)kPipeRowBlocks * kSlabBytes;
   __shared__ __attribute__((aligned(16))) float lut[2][48 * kPipeStride];
-  __shared__ int built[2], done[2];
+  __shared__ __attribute__((aligned(16))) float hs[DOWN ? ITEMS : 1][128];
+  __shared__ int built[2], done[2], hready;
+  __shared__ double rl[DOWN ? 1 : kRouteMaxExperts];
+  __shared__ int rcnt[DOWN ? 1 : kRouteMaxExperts], rsel[kMaxTopK];
   const int H = bank.H, I = bank.I;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int gm = blockIdx.x / nchunk;                       // slot * 2 + matrix
-  const int t0 = (blockIdx.x - gm * nchunk) * ITEMS;
-  int e = ids[gm >> 1];
+  // geometry of this workgroup
+  int slot, m, t0, rb0;
+  if constexpr (DOWN) {
+    const int kc = blockIdx.x % pa.nchunk;
+    const int rc = (blockIdx.x / pa.nchunk) % pa.nrc;
+    slot = blockIdx.x / (pa.nchunk * pa.nrc);
+    m = 2;
+    t0 = kc * ITEMS;
+    rb0 = rc * NSW * BPI;
+  } else {
+    const int gm = blockIdx.x / pa.nchunk;
+    slot = gm >> 1;
+    m = gm & 1;
+    t0 = (blockIdx.x - gm * pa.nchunk) * ITEMS;
+    rb0 = 0;
+  }
+  const bool streamer = wave < NSW;
+  const int bw = wave - NSW;
+  // down: builder wave bw computes h for items bw, bw + 4, ... (ITEMS <= 8, so at most two): lane l
+  // takes entries l and 64 + l of the item's 128.  The gate/up partials depend on the slot only,
+  // so they are requested first, before the expert id is known.
+  constexpr int HI = DOWN ? (ITEMS + kPipeBuildWaves - 1) / kPipeBuildWaves : 1;
+  constexpr int GU = DOWN ? kPipeMaxGu : 1;
+  float gv[HI][2][GU], uv[HI][2][GU];
+  if constexpr (DOWN) {
+    if (!streamer) {
+      const int64_t Ip = pad_rows(I);
+      const float* pg = pa.part_gu + (int64_t)slot * 2 * pa.ngu * Ip;
+      const float* pu = pg + (int64_t)pa.ngu * Ip;
+#pragma unroll
+      for (int n = 0; n < HI; ++n) {
+        const int k = bw + n * kPipeBuildWaves < ITEMS ? bw + n * kPipeBuildWaves : ITEMS - 1;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int64_t col = (int64_t)(t0 + k) * 128 + hh * 64 + lane;
+#pragma unroll
+          for (int p = 0; p < GU; ++p) {
+            const int pp = p < pa.ngu ? p : 0;
+            gv[n][hh][p] = pg[pp * Ip + col];
+            uv[n][hh][p] = pu[pp * Ip + col];
+          }
+        }
+      }
+    }
+  }
+  int e;
+  if (!DOWN && pa.logits) {
+    // top-k of the router logits, the same computation as k_topk
+    const int E = bank.E;
+    if (threadIdx.x < kMaxTopK) rsel[threadIdx.x] = 0;
+    for (int j = threadIdx.x; j < E; j += blockDim.x) {
+      rl[j] = pa.logits[j];
+      rcnt[j] = 0;
+    }
+    __syncthreads();
+    topk_ranks(rl, rcnt, E);
+    __syncthreads();
+    topk_select(rcnt, E, pa.k, rsel);
+    __syncthreads();
+    e = rsel[slot];
+    if (m == 0 && t0 == 0 && wave == 0)
+      topk_gates(rl, rsel, pa.k, pa.ids_out, pa.gates_out, [&](int i) { return i == slot; });
+  } else {
+    e = ids[slot];
+  }
   const bool bad = e < 0 || e >= bank.E;
-  if (bad) e = 0;  // recorded below; this slot's results are never read
-  const bool streamer = wave < kPipeStreamWaves;
+  if constexpr (DOWN) {
+    if (bad) return;  // the gate/up kernel records the status; combine skips the slot
+  } else {
+    if (bad) e = 0;   // recorded below; this slot's results are never read
+  }
+  const int rows = DOWN ? H : I;
+  const int nrb = (int)cdiv(rows, kSlabRows);
+  const int64_t tile_bytes = (int64_t)nrb * kSlabBytes;
 
-  // builder operands are requested before the start barrier, i.e. ahead of the code stream
-  const int bw = wave - kPipeStreamWaves;
+  // builder operands, requested before the start barrier (ahead of the code stream)
   const int q = lane >> 4, i16 = lane & 15;
-  f32x2 a[TPW], xb[ITEMS];
+  f32x2 a[TPW];
+  f32x2 xb[DOWN ? 1 : ITEMS];
   if (!streamer) {
-    const float* cb = bank.cb + ((int64_t)e * 3 + (gm & 1)) * kCodebookFloats;
+    const float* cb = bank.cb + ((int64_t)e * 3 + m) * kCodebookFloats;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) a[t] = *reinterpret_cast<const f32x2*>(cb + ((bw * TPW + t) * 16 + i16) * 8 + 2 * q);
+    if constexpr (!DOWN) {
 #pragma unroll
-    for (int k = 0; k < ITEMS; ++k) xb[k] = *reinterpret_cast<const f32x2*>(x + (int64_t)(t0 + k) * 128 + i16 * 8 + 2 * q);
+      for (int k = 0; k < ITEMS; ++k)
+        xb[k] = *reinterpret_cast<const f32x2*>(pa.x + (int64_t)(t0 + k) * 128 + i16 * 8 + 2 * q);
+    }
   } else if (threadIdx.x == 0) {
     built[0] = 0;
     built[1] = 0;
     done[0] = 0;
     done[1] = 0;
-    if (bad) atomicExch(status, 6 /* RVQ_ERR_EXPERT_ID */);
+    hready = 0;
+    if (!DOWN && bad) atomicExch(status, 6 /* RVQ_ERR_EXPERT_ID */);
   }
   __syncthreads();
 
   if (streamer) {
     // ----------------------------------------------------------------- streamers
-    const uint8_t* codes = bank.codes + (int64_t)e * bank.stride + (int64_t)(gm & 1) * packed_bytes(I, H) +
-                           (int64_t)t0 * kTileBytes;
+    const uint8_t* codes = bank.codes + (int64_t)e * bank.stride + (int64_t)m * packed_bytes(I, H) +
+                           (int64_t)t0 * tile_bytes + (int64_t)rb0 * kSlabBytes;
     SlabData buf[NB];
     const uint32_t lane_off = lane * 16;
     auto load_blk = [&](int i, int s) {
       const int k = s / BPI, r = s % BPI;
-      load_slabs<false>(buf[i], codes + k * kTileBytes, codes + k * kTileBytes,
-                        (uint32_t)(wave + kPipeStreamWaves * r) * kSlabBytes + lane_off);
+      load_slabs<false>(buf[i], codes + k * tile_bytes, codes + k * tile_bytes,
+                        (uint32_t)(wave + NSW * r) * kSlabBytes + lane_off);
     };
 #pragma unroll
     for (int i = 0; i < NB; ++i) load_blk(i, i);
@@ -595,19 +729,42 @@ __global__ __launch_bounds__(kPipeThreads) void k_gateup_ws_f32(BankArgs bank, c
       }
       if (lane == 0) __hip_atomic_fetch_add(&done[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    float* out = part_gu + (int64_t)blockIdx.x * pad_rows(I);
+    float* out = pa.out + (int64_t)blockIdx.x * pad_rows(rows) + (int64_t)rb0 * kSlabRows;
+    if constexpr (DOWN) out = pa.out + ((int64_t)slot * pa.nchunk + (blockIdx.x % pa.nchunk)) * pad_rows(rows) +
+                              (int64_t)rb0 * kSlabRows;
 #pragma unroll
-    for (int r = 0; r < BPI; ++r) out[(wave + kPipeStreamWaves * r) * kSlabRows + lane] = acc[r];
+    for (int r = 0; r < BPI; ++r) out[(wave + NSW * r) * kSlabRows + lane] = acc[r];
     if (!ok && lane == 0) atomicExch(status, kStatusStall);
   } else {
     // ----------------------------------------------------------------- builders
     bool ok = true;
+    if constexpr (DOWN) {
+#pragma unroll
+      for (int n = 0; n < HI; ++n) {
+        const int k = bw + n * kPipeBuildWaves;
+        if (k >= ITEMS) break;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          float g = 0.f, u = 0.f;
+#pragma unroll
+          for (int p = 0; p < GU; ++p) {
+            g += p < pa.ngu ? gv[n][hh][p] : 0.f;
+            u += p < pa.ngu ? uv[n][hh][p] : 0.f;
+          }
+          hs[k][hh * 64 + lane] = g / (1.f + expf(-g)) * u;
+        }
+      }
+      if (lane == 0) __hip_atomic_fetch_add(&hready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      ok &= lds_wait_ge(&hready, kPipeBuildWaves);
+    }
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
-      if (k >= 2) ok &= lds_wait_ge(&done[k & 1], kPipeStreamWaves * (k / 2));
-      // an opaque copy pins this item's products after the wait (otherwise the compiler computes
-      // every item's tables up front and spills them)
-      f32x2 xk = xb[k];
+      if (k >= 2) ok &= lds_wait_ge(&done[k & 1], NSW * (k / 2));
+      // an opaque copy pins this item's products after the wait (otherwise the compiler may compute
+      // every item's tables up front)
+      f32x2 xk;
+      if constexpr (DOWN) xk = *reinterpret_cast<const f32x2*>(&hs[k][i16 * 8 + 2 * q]);
+      else xk = xb[k];
       asm volatile("" : "+v"(xk));
       float* L = lut[k & 1];
 #pragma unroll
@@ -737,29 +894,32 @@ __global__ __launch_bounds__(kDownThreads) __attribute__((amdgpu_waves_per_eu(4,
   k_moe_down_body<true, BPW, kDownThreads>(bank, ids, part_gu, part_d, nparts, ngu);
 }
 
-// Gated combine.  Workgroup = 64 rows x 8 waves; wave q sums slots q, q+8, ... over all tiles (loads
-// four tiles at a time), then wave 0 adds the 8 partial sums to the residual in a fixed order.
-__global__ __launch_bounds__(512) void k_moe_combine(const float* __restrict__ part_d, int nt, int H,
-                                                     const int32_t* __restrict__ ids, const float* __restrict__ gates,
-                                                     int k, int E, const float* residual, float* y) {
+// Gated combine.  Workgroup = 64 rows x 16 waves; wave q sums slots q, q+16, ... over their
+// `nt` partials (issued 8 at a time, so a slot costs few memory round trips), then wave 0 adds the
+// 16 per-wave sums to the residual in a fixed order.
+constexpr int kCombineWaves = 16;
+__global__ __launch_bounds__(64 * kCombineWaves) void k_moe_combine(const float* __restrict__ part_d, int nt, int H,
+                                                                    const int32_t* __restrict__ ids,
+                                                                    const float* __restrict__ gates, int k, int E,
+                                                                    const float* residual, float* y) {
   const int64_t Hp = pad_rows(H);
-  __shared__ float red[8][64];
+  __shared__ float red[kCombineWaves][64];
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int r = blockIdx.x * 64 + lane;
   float acc = 0.f;
   if (r < H) {
-    for (int slot = q; slot < k; slot += 8) {
+    for (int slot = q; slot < k; slot += kCombineWaves) {
       const int e = ids[slot];
       if (e < 0 || e >= E) continue;
       const float* pd = part_d + (int64_t)slot * nt * Hp + r;
       float s = 0.f;
-      int t = 0;
-      for (; t + 4 <= nt; t += 4) {
-        const float a = pd[t * Hp], b = pd[(t + 1) * Hp];
-        const float c = pd[(t + 2) * Hp], d = pd[(t + 3) * Hp];
-        s += a; s += b; s += c; s += d;
+      for (int t = 0; t < nt; t += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = t + u < nt ? pd[(int64_t)(t + u) * Hp] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
       }
-      for (; t < nt; ++t) s += pd[t * Hp];
       acc = fmaf(gates[slot], s, acc);
     }
   }
@@ -768,7 +928,7 @@ __global__ __launch_bounds__(512) void k_moe_combine(const float* __restrict__ p
   if (q == 0 && r < H) {
     float o = residual ? residual[r] : 0.f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) o += red[w][lane];
+    for (int w = 0; w < kCombineWaves; ++w) o += red[w][lane];
     y[r] = o;
   }
 }
@@ -794,7 +954,7 @@ MoeWorkspace moe_workspace_layout(int H, int I, int k, bool f16) {
 
 hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
                              const float* x, const int32_t* ids, const float* gates, int k, const float* residual,
-                             float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev) {
+                             float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev, const Route* route) {
   const MoeWorkspace w = moe_workspace_layout(H, I, k, f16);
   uint8_t* base = static_cast<uint8_t*>(ws);
   int32_t* status = reinterpret_cast<int32_t*>(base + w.status_off);
@@ -807,28 +967,54 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
     if (ev && err == hipSuccess) err = hipEventRecord(ev[i], stream);
   };
   mark(0);
-  // The wave-specialised gate/up kernel takes fp32 tables, I in (1984, 2048] and whole 16-group
-  // tiles; it sums `chunk` K-tiles per workgroup, chosen to fill the CUs in as few rounds as possible
-  // (ties: the larger chunk, i.e. fewer partials).
+  // The wave-specialised kernels take fp32 tables.  Gate/up needs I in (1984, 2048] and whole
+  // 16-group K-tiles; down needs I a multiple of 128, H a multiple of 28 row blocks, and at most
+  // kPipeMaxGu gate/up partials.  Each sums `c` K-tiles per workgroup, c chosen to fill the CUs in
+  // as few rounds as possible (ties: the larger c, i.e. fewer partials).
   const int ncu = compute_units();
-  int chunk = 0;
-  if (!f16 && (H / 8) % 16 == 0 && (int)cdiv(I, kSlabRows) == kPipeRowBlocks && ncu > 0) {
+  auto pick_chunk = [&](int ntiles, long per_chunk_groups) {
+    int best_c = 0;
     long best = 0;
     for (int c = 1; c <= kPipeMaxItems; ++c) {
-      if (w.nt_in % c != 0) continue;
-      const long grid = (long)k * 2 * (w.nt_in / c);
+      if (ntiles % c != 0) continue;
+      const long grid = per_chunk_groups * (ntiles / c);
       const long cost = (grid + ncu - 1) / ncu * c;
-      if (chunk == 0 || cost <= best) best = cost, chunk = c;
+      if (best_c == 0 || cost <= best) best = cost, best_c = c;
     }
-  }
+    return best_c;
+  };
+  const int chunk = (!f16 && ncu > 0 && (H / 8) % 16 == 0 && (int)cdiv(I, kSlabRows) == kGuStreamWaves * kGuBpi)
+                        ? pick_chunk(w.nt_in, 2L * k)
+                        : 0;
   const int ngu = chunk ? w.nt_in / chunk : w.nt_in;
+  constexpr int kDnRows = kDnStreamWaves * kDnBpi;
+  const int nrb_h = (int)cdiv(H, kSlabRows);
+  const int nrc = nrb_h / kDnRows;
+  const int dchunk = (chunk && I % 128 == 0 && nrb_h % kDnRows == 0 && ngu <= kPipeMaxGu)
+                         ? pick_chunk(w.nt_out, (long)k * nrc)
+                         : 0;
+  const int nparts_d = dchunk ? w.nt_out / dchunk : w.nt_out;
+  // routing: the gate/up kernel takes the top-k itself when it is the wave-specialised one;
+  // otherwise k_topk writes ids/gates first
+  const bool fused_route = route && chunk && E <= kRouteMaxExperts;
+  if (route) {
+    ids = route->ids;
+    gates = route->gates;
+    if (!fused_route)
+      hipLaunchKernelGGL(k_topk, dim3(1), dim3(1024), 0, stream, route->logits, E, k, route->ids, route->gates);
+  }
   const int bpw_gu = pick_bpw((int)cdiv(I, kSlabRows), 1, kGateUpThreads / 64);
   const int bpw_d = pick_bpw((int)cdiv(H, kSlabRows), nparts, kDownThreads / 64);
   if (chunk) {
     const dim3 grid((unsigned)(k * 2 * ngu));
+    const PipeArgs pa{x,       nullptr, part_gu, ngu, 1, 0, fused_route ? route->logits : nullptr,
+                      route ? route->ids : nullptr, route ? route->gates : nullptr, k};
     switch (chunk) {
-#define RVQ_WS_CASE(n) \
-  case n: hipLaunchKernelGGL((k_gateup_ws_f32<n>), grid, dim3(kPipeThreads), 0, stream, bank, x, ids, part_gu, status, ngu); break;
+#define RVQ_WS_CASE(n)                                                                                             \
+  case n:                                                                                                          \
+    hipLaunchKernelGGL((k_table_ws_f32<false, kGuStreamWaves, kGuBpi, n>), grid, dim3(64 * (kGuStreamWaves + 4)), 0, \
+                       stream, bank, ids, status, pa);                                                             \
+    break;
       RVQ_WS_CASE(1) RVQ_WS_CASE(2) RVQ_WS_CASE(3) RVQ_WS_CASE(4)
       RVQ_WS_CASE(5) RVQ_WS_CASE(6) RVQ_WS_CASE(7) RVQ_WS_CASE(8)
 #undef RVQ_WS_CASE
@@ -841,7 +1027,21 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
                                                 stream, bank, x, ids, part_gu, status))
   }
   mark(1);
-  if (f16) {
+  if (dchunk) {
+    const int nkc = w.nt_out / dchunk;
+    const dim3 grid((unsigned)(k * nrc * nkc));
+    const PipeArgs pa{nullptr, part_gu, part_d, nkc, nrc, ngu, nullptr, nullptr, nullptr, k};
+    switch (dchunk) {
+#define RVQ_WS_CASE(n)                                                                                             \
+  case n:                                                                                                          \
+    hipLaunchKernelGGL((k_table_ws_f32<true, kDnStreamWaves, kDnBpi, n>), grid, dim3(64 * (kDnStreamWaves + 4)), 0,  \
+                       stream, bank, ids, status, pa);                                                             \
+    break;
+      RVQ_WS_CASE(1) RVQ_WS_CASE(2) RVQ_WS_CASE(3) RVQ_WS_CASE(4)
+      RVQ_WS_CASE(5) RVQ_WS_CASE(6) RVQ_WS_CASE(7) RVQ_WS_CASE(8)
+#undef RVQ_WS_CASE
+    }
+  } else if (f16) {
     RVQ_BPW_DISPATCH(bpw_d, hipLaunchKernelGGL((k_moe_down_f16<B>), dim3(k * w.nt_out * nparts), dim3(kDownThreads), 0,
                                                stream, bank, ids, part_gu, part_d, nparts, ngu))
   } else {
@@ -849,8 +1049,8 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
                                                stream, bank, ids, part_gu, part_d, nparts, ngu))
   }
   mark(2);
-  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)cdiv(H, 64)), dim3(512), 0, stream, part_d, w.nt_out, H, ids,
-                     gates, k, E, residual, y);
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)cdiv(H, 64)), dim3(64 * kCombineWaves), 0, stream, part_d, nparts_d,
+                     H, ids, gates, k, E, residual, y);
   mark(3);
   const hipError_t last = hipGetLastError();
   return err != hipSuccess ? err : last;

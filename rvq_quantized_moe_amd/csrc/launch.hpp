@@ -31,9 +31,20 @@ hipError_t launch_gemv(const uint8_t* codes, const float* cb, int rows, int cols
 hipError_t launch_router_topk(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, int k, int32_t* ids,
                               float* gates, double* logits, hipStream_t stream);
 hipError_t launch_rmsnorm(const float* x, int T, int H, float eps, float* out, hipStream_t stream);
+hipError_t launch_router_logits(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, double* logits,
+                                hipStream_t stream);
+// Routing inputs of a decode step: the router logits (fp64 [E]) and where the top-k ids/gates go.
+struct Route {
+  const double* logits;
+  int32_t* ids;
+  float* gates;
+};
+// route == nullptr: ids/gates are inputs.  Otherwise ids/gates are ignored and the top-k of
+// route->logits is taken first (inside the gate/up kernel when it can), written to route->ids/gates.
 hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
                              const float* x, const int32_t* ids, const float* gates, int k, const float* residual,
-                             float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev);
+                             float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev,
+                             const Route* route = nullptr);
 
 size_t chunk_workspace_bytes(int E, int H, int I, int T, int k);
 hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,

@@ -150,6 +150,30 @@ def test_moe_validation(L):
     assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 1, None, FAKE, 16, None, FAKE, 0, FAKE, n, s) == NULL
 
 
+def test_routed_decode_validation(L):
+    """Every check of rvq_moe_decode_routed returns before anything is enqueued."""
+    s = None
+    n = L.rvq_moe_layer_workspace_bytes(_bank(), 1, 16, 0)
+    f = L.rvq_moe_decode_routed
+    ok = [FAKE, FAKE, 16, None, FAKE, FAKE, FAKE, FAKE, 0, FAKE, n, s]
+
+    def call(bank=None, **kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(bank if bank is not None else _bank(), *a)
+    assert f(None, *ok) == NULL
+    assert call(a0=None) == NULL                          # router weights
+    assert call(a4=None) == NULL                          # y
+    assert call(a7=None) == NULL                          # logits
+    assert call(_bank(E=0)) == SHAPE
+    assert call(a2=0) == SHAPE and call(a2=65) == SHAPE   # k
+    assert call(a8=2) == DTYPE                            # bf16 tables: no
+    assert call(a7=FAKE + 4) == ALIGN                     # logits are fp64
+    assert call(a9=FAKE + 64) == ALIGN                    # workspace
+    assert call(a10=n - 1) == WS
+
+
 def test_chunk_workspace_and_validation(L):
     """T > 1 selects the chunk path: bf16 tokens, f16 or bf16 tiles."""
     s = None

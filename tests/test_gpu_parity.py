@@ -287,3 +287,48 @@ def test_moe_layer_is_deterministic(layer_bank):
     a = rvq.moe_layer_forward(bank, x, ids[0], gates[0])
     b = rvq.moe_layer_forward(bank, x, ids[0], gates[0])
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_routed_decode_matches_two_calls_and_oracle(layer_bank, dtype):
+    """rvq_moe_decode_routed (top-k taken inside the gate/up kernel for fp32 tables, by the selection
+    kernel for fp16) gives the ids and gates of rvq_router_topk bit for bit, the output of
+    rvq_moe_layer_forward on them bit for bit, and the oracle's layer within tolerance."""
+    bank, bits, w = layer_bank
+    ws = rvq.make_moe_workspace(bank, 1, TOP_K, dtype)
+    cache = {}
+    def get(e):
+        if e not in cache:
+            cache[e] = oracle_expert(synth.SEED_LAYER, 0, e)
+        return cache[e]
+    for t in (2, 3):
+        say(f"routed decode token {t} {dtype}")
+        x = synth.activation_f32(synth.SEED_LAYER, t, HIDDEN)
+        r = synth.activation_f32(synth.SEED_LAYER, 1000 + t, HIDDEN)
+        xd, rd = to_dev(x), to_dev(r)
+        y, ids, gates, logits = rvq.moe_decode_routed(bank, w, xd, TOP_K, residual=rd, dtype=dtype, workspace=ws)
+        ids2, gates2, logits2 = rvq.router_topk(w, xd, TOP_K)
+        y2 = rvq.moe_layer_forward(bank, xd, ids2[0], gates2[0], residual=rd, dtype=dtype, workspace=ws)
+        assert torch.equal(logits, logits2[0])
+        assert torch.equal(ids, ids2[0])
+        assert torch.equal(gates, gates2[0])
+        assert torch.equal(y, y2)
+        y_ref, ids_ref, gates_ref, _ = oracle.moe_layer(get, bits, x, TOP_K, residual=r)
+        assert np.array_equal(ids.cpu().numpy(), ids_ref)
+        np.testing.assert_allclose(gates.cpu().numpy(), gates_ref, rtol=1e-6)
+        assert rel_l2(y.cpu().numpy() - r, y_ref - r) <= TOL[dtype]
+    assert rvq.check_device_status(ws) == 0
+
+
+def test_routed_decode_small_expert_count():
+    """Top-k inside the gate/up kernel with fewer experts than wave lanes, k = 1 and k = E."""
+    E, k_all = 5, 5
+    say("routed decode, 5 experts")
+    bank = upload_bank(synth.SEED_EXPERT, 7, E)
+    bits, w = router(synth.SEED_EXPERT, 7, E, HIDDEN)
+    x = to_dev(synth.activation_f32(synth.SEED_EXPERT, 70, HIDDEN))
+    for k in (1, k_all):
+        y, ids, gates, _ = rvq.moe_decode_routed(bank, w, x, k)
+        ids2, gates2, _ = rvq.router_topk(w, x, k)
+        assert torch.equal(ids, ids2[0]) and torch.equal(gates, gates2[0])
+        assert torch.equal(y, rvq.moe_layer_forward(bank, x, ids2[0], gates2[0]))
