@@ -177,13 +177,13 @@ __device__ __forceinline__ float gather16_f32(const float* lut, u32x4 d, float a
   return acc;
 }
 
-template <int BASE>
+template <int BASE, int STRIDE = kEntries>
 __device__ __forceinline__ float gather16_f16(const f16* lut, u32x4 d, float acc) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const uint32_t v = d[w];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc += (float)lut[(BASE + 4 * w + k) * kEntries + ((v >> (8 * k)) & 0xffu)];
+    for (int k = 0; k < 4; ++k) acc += (float)lut[(BASE + 4 * w + k) * STRIDE + ((v >> (8 * k)) & 0xffu)];
   }
   return acc;
 }
@@ -208,6 +208,24 @@ __device__ __forceinline__ void load_slabs(SlabData& s, const uint8_t* __restric
     s.d[4] = *(b + 64);
     s.d[5] = *(b + 128);
   }
+}
+
+// One slab (16 groups, three 16-byte code words per lane) through tables of either precision.
+template <bool F16, int STRIDE>
+__device__ __forceinline__ float gather_slab1(const void* lut, const SlabData& s) {
+  float acc = 0.f;
+  if constexpr (F16) {
+    const f16* t = static_cast<const f16*>(lut);
+    acc = gather16_f16<0, STRIDE>(t, s.d[0], acc);
+    acc = gather16_f16<16, STRIDE>(t, s.d[1], acc);
+    acc = gather16_f16<32, STRIDE>(t, s.d[2], acc);
+  } else {
+    const float* t = static_cast<const float*>(lut);
+    acc = gather16_f32<0, STRIDE>(t, s.d[0], acc);
+    acc = gather16_f32<16, STRIDE>(t, s.d[1], acc);
+    acc = gather16_f32<32, STRIDE>(t, s.d[2], acc);
+  }
+  return acc;
 }
 
 template <bool F16, int STRIDE = kEntries>

@@ -534,8 +534,14 @@ __device__ __forceinline__ void k_moe_gateup_body(BankArgs bank, const float* __
 // entries 4q..4q+3 of group i, stored as one 16-byte LDS write (conflict-free because subtables
 // are kPipeStride = 260 floats apart).  The codebook operands are the same for every item of the
 // workgroup and are loaded once, before the start barrier.
+//
+// fp16 tables (F16): entries are stored scaled by 2^-e_k, e_k = f16_table_exponent(max |c| max |x_g|)
+// over the codebook and the item's 16 groups (so no entry can overflow), 4 entries per 8-byte
+// write with subtables kPipeStride16 = 264 halves apart; the streamers scale each item's sums by
+// 2^e_k before adding them to the row totals.
 constexpr int kPipeBuildWaves = 4;
 constexpr int kPipeStride = 260;       // floats between subtables
+constexpr int kPipeStride16 = 264;     // halves between subtables (fp16 tables)
 constexpr int kPipeMaxItems = 8;
 constexpr int kPipeMaxGu = 8;          // down: most gate/up partials per row
 constexpr int kGuStreamWaves = 8, kGuBpi = 4;     // gate/up: 32 row blocks (I in (1984, 2048])
@@ -583,17 +589,23 @@ struct PipeArgs {
 };
 constexpr int kRouteMaxExperts = 1024;
 
-template <bool DOWN, int NSW, int BPI, int ITEMS>
-__global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws_f32(BankArgs bank,
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+
+template <bool F16, bool DOWN, int NSW, int BPI, int ITEMS>
+__global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankArgs bank,
                                                                              const int32_t* __restrict__ ids,
                                                                              int32_t* __restrict__ status,
                                                                              PipeArgs pa) {
   constexpr int NB = 3;   // row blocks of codes held per streamer wave (deeper measured slower)
   constexpr int NBLK = ITEMS * BPI;
   constexpr int TPW = 48 / kPipeBuildWaves;                 // table tiles per builder wave
-  __shared__ __attribute__((aligned(16))) float lut[2][48 * kPipeStride];
+  typedef typename Tile<F16>::entry_t T;
+  constexpr int S = F16 ? kPipeStride16 : kPipeStride;
+  __shared__ __attribute__((aligned(16))) T lut[2][48 * S];
   __shared__ __attribute__((aligned(16))) float hs[DOWN ? ITEMS : 1][128];
   __shared__ int built[2], done[2], hready;
+  __shared__ int cmax_bits;            // fp16: max squared codebook-entry norm (bits of a float >= 0)
+  __shared__ float escale[ITEMS];      // fp16: 2^e_k of each item
   __shared__ double rl[DOWN ? 1 : kRouteMaxExperts];
   __shared__ int rcnt[DOWN ? 1 : kRouteMaxExperts], rsel[kMaxTopK];
   const int H = bank.H, I = bank.I;
@@ -693,6 +705,7 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws_f32(B
     done[0] = 0;
     done[1] = 0;
     hready = 0;
+    cmax_bits = 0;
     if (!DOWN && bad) atomicExch(status, 6 /* RVQ_ERR_EXPERT_ID */);
   }
   __syncthreads();
@@ -720,10 +733,11 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws_f32(B
 #pragma unroll
       for (int r = 0; r < BPI; ++r) {
         const int s = k * BPI + r;
-        const float g = gather_slabs<false, kPipeStride>(lut[k & 1], buf[s % NB]);
+        float g = gather_slab1<F16, S>(lut[k & 1], buf[s % NB]);
         // opaque use: without it the compiler interleaves the row blocks' gathers into one
         // another and spills
         asm volatile("" : : "v"(g));
+        if constexpr (F16) g *= escale[k];
         acc[r] += g;
         if (s + NB < NBLK) load_blk(s % NB, s + NB);
       }
@@ -738,6 +752,20 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws_f32(B
   } else {
     // ----------------------------------------------------------------- builders
     bool ok = true;
+    float cmax2 = 0.f;
+    if constexpr (F16) {
+      // squared norm of codebook entry i16 of each table tile: the 4 lanes q hold 2 dims each
+      float v = 0.f;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        float n2 = a[t].x * a[t].x + a[t].y * a[t].y;
+        n2 += __shfl_xor(n2, 16, 64);
+        n2 += __shfl_xor(n2, 32, 64);
+        v = fmaxf(v, n2);
+      }
+      v = wave_max(v);
+      if (lane == 0) atomicMax(&cmax_bits, __float_as_int(v));   // non-negative floats order as ints
+    }
     if constexpr (DOWN) {
 #pragma unroll
       for (int n = 0; n < HI; ++n) {
@@ -754,8 +782,11 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws_f32(B
           hs[k][hh * 64 + lane] = g / (1.f + expf(-g)) * u;
         }
       }
+    }
+    if (DOWN || F16) {
       if (lane == 0) __hip_atomic_fetch_add(&hready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       ok &= lds_wait_ge(&hready, kPipeBuildWaves);
+      if constexpr (F16) cmax2 = __int_as_float(cmax_bits);
     }
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
@@ -766,14 +797,28 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws_f32(B
       if constexpr (DOWN) xk = *reinterpret_cast<const f32x2*>(&hs[k][i16 * 8 + 2 * q]);
       else xk = xb[k];
       asm volatile("" : "+v"(xk));
-      float* L = lut[k & 1];
+      float scale = 1.f;
+      if constexpr (F16) {
+        float n2 = xk.x * xk.x + xk.y * xk.y;   // squared norm of group i16's x
+        n2 += __shfl_xor(n2, 16, 64);
+        n2 += __shfl_xor(n2, 32, 64);
+        const int ex = f16_table_exponent(sqrtf(cmax2) * sqrtf(wave_max(n2)));
+        scale = ldexpf(1.f, -ex);
+        if (bw == 0 && lane == 0) escale[k] = ldexpf(1.f, ex);
+      }
+      T* L = lut[k & 1];
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int ti = bw * TPW + t, st = ti >> 4, e0 = (ti & 15) * 16;
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
         d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].x, xk.x, d, 0, 0, 0);
         d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].y, xk.y, d, 0, 0, 0);
-        *reinterpret_cast<f32x4*>(&L[(3 * i16 + st) * kPipeStride + e0 + 4 * q]) = d;
+        if constexpr (F16) {
+          const half4 hv = {(f16)(d.x * scale), (f16)(d.y * scale), (f16)(d.z * scale), (f16)(d.w * scale)};
+          *reinterpret_cast<half4*>(&L[(3 * i16 + st) * S + e0 + 4 * q]) = hv;
+        } else {
+          *reinterpret_cast<f32x4*>(&L[(3 * i16 + st) * S + e0 + 4 * q]) = d;
+        }
       }
       if (lane == 0) __hip_atomic_fetch_add(&built[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
@@ -945,9 +990,10 @@ MoeWorkspace moe_workspace_layout(int H, int I, int k, bool f16) {
   w.nt_out = (int)cdiv(I / 8, G);
   w.status_off = 0;
   w.part_gu_off = 256;
-  const size_t gu = (size_t)k * 2 * w.nt_in * pad_rows(I) * sizeof(float);
+  // sized for 16-group K-tiles, the most partials any form of the kernels writes
+  const size_t gu = (size_t)k * 2 * cdiv(H / 8, kSlabGroups) * pad_rows(I) * sizeof(float);
   w.part_d_off = w.part_gu_off + ((gu + 255) / 256) * 256;
-  const size_t d = (size_t)k * w.nt_out * pad_rows(H) * sizeof(float);
+  const size_t d = (size_t)k * cdiv(I / 8, kSlabGroups) * pad_rows(H) * sizeof(float);
   w.total = w.part_d_off + ((d + 255) / 256) * 256;
   return w;
 }
@@ -967,7 +1013,7 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
     if (ev && err == hipSuccess) err = hipEventRecord(ev[i], stream);
   };
   mark(0);
-  // The wave-specialised kernels take fp32 tables.  Gate/up needs I in (1984, 2048] and whole
+  // The wave-specialised kernels: gate/up needs I in (1984, 2048] and whole
   // 16-group K-tiles; down needs I a multiple of 128, H a multiple of 28 row blocks, and at most
   // kPipeMaxGu gate/up partials.  Each sums `c` K-tiles per workgroup, c chosen to fill the CUs in
   // as few rounds as possible (ties: the larger c, i.e. fewer partials).
@@ -983,17 +1029,19 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
     }
     return best_c;
   };
-  const int chunk = (!f16 && ncu > 0 && (H / 8) % 16 == 0 && (int)cdiv(I, kSlabRows) == kGuStreamWaves * kGuBpi)
-                        ? pick_chunk(w.nt_in, 2L * k)
+  // (their K-tiles are single slabs of 16 groups for either table precision)
+  const int nt16_in = (int)cdiv(H / 8, kSlabGroups), nt16_out = (int)cdiv(I / 8, kSlabGroups);
+  const int chunk = (ncu > 0 && (H / 8) % 16 == 0 && (int)cdiv(I, kSlabRows) == kGuStreamWaves * kGuBpi)
+                        ? pick_chunk(nt16_in, 2L * k)
                         : 0;
-  const int ngu = chunk ? w.nt_in / chunk : w.nt_in;
+  const int ngu = chunk ? nt16_in / chunk : w.nt_in;
   constexpr int kDnRows = kDnStreamWaves * kDnBpi;
   const int nrb_h = (int)cdiv(H, kSlabRows);
   const int nrc = nrb_h / kDnRows;
   const int dchunk = (chunk && I % 128 == 0 && nrb_h % kDnRows == 0 && ngu <= kPipeMaxGu)
-                         ? pick_chunk(w.nt_out, (long)k * nrc)
+                         ? pick_chunk(nt16_out, (long)k * nrc)
                          : 0;
-  const int nparts_d = dchunk ? w.nt_out / dchunk : w.nt_out;
+  const int nparts_d = dchunk ? nt16_out / dchunk : w.nt_out;
   // routing: the gate/up kernel takes the top-k itself when it is the wave-specialised one;
   // otherwise k_topk writes ids/gates first
   const bool fused_route = route && chunk && E <= kRouteMaxExperts;
@@ -1012,8 +1060,12 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
     switch (chunk) {
 #define RVQ_WS_CASE(n)                                                                                             \
   case n:                                                                                                          \
-    hipLaunchKernelGGL((k_table_ws_f32<false, kGuStreamWaves, kGuBpi, n>), grid, dim3(64 * (kGuStreamWaves + 4)), 0, \
-                       stream, bank, ids, status, pa);                                                             \
+    if (f16)                                                                                                       \
+      hipLaunchKernelGGL((k_table_ws<true, false, kGuStreamWaves, kGuBpi, n>), grid, dim3(64 * (kGuStreamWaves + 4)),  \
+                         0, stream, bank, ids, status, pa);                                                        \
+    else                                                                                                           \
+      hipLaunchKernelGGL((k_table_ws<false, false, kGuStreamWaves, kGuBpi, n>), grid, dim3(64 * (kGuStreamWaves + 4)), \
+                         0, stream, bank, ids, status, pa);                                                        \
     break;
       RVQ_WS_CASE(1) RVQ_WS_CASE(2) RVQ_WS_CASE(3) RVQ_WS_CASE(4)
       RVQ_WS_CASE(5) RVQ_WS_CASE(6) RVQ_WS_CASE(7) RVQ_WS_CASE(8)
@@ -1028,14 +1080,18 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
   }
   mark(1);
   if (dchunk) {
-    const int nkc = w.nt_out / dchunk;
+    const int nkc = nt16_out / dchunk;
     const dim3 grid((unsigned)(k * nrc * nkc));
     const PipeArgs pa{nullptr, part_gu, part_d, nkc, nrc, ngu, nullptr, nullptr, nullptr, k};
     switch (dchunk) {
 #define RVQ_WS_CASE(n)                                                                                             \
   case n:                                                                                                          \
-    hipLaunchKernelGGL((k_table_ws_f32<true, kDnStreamWaves, kDnBpi, n>), grid, dim3(64 * (kDnStreamWaves + 4)), 0,  \
-                       stream, bank, ids, status, pa);                                                             \
+    if (f16)                                                                                                       \
+      hipLaunchKernelGGL((k_table_ws<true, true, kDnStreamWaves, kDnBpi, n>), grid, dim3(64 * (kDnStreamWaves + 4)),   \
+                         0, stream, bank, ids, status, pa);                                                        \
+    else                                                                                                           \
+      hipLaunchKernelGGL((k_table_ws<false, true, kDnStreamWaves, kDnBpi, n>), grid, dim3(64 * (kDnStreamWaves + 4)),  \
+                         0, stream, bank, ids, status, pa);                                                        \
     break;
       RVQ_WS_CASE(1) RVQ_WS_CASE(2) RVQ_WS_CASE(3) RVQ_WS_CASE(4)
       RVQ_WS_CASE(5) RVQ_WS_CASE(6) RVQ_WS_CASE(7) RVQ_WS_CASE(8)
