@@ -35,6 +35,7 @@ WEIGHTS_PER_TOKEN = K * 3 * H * I                         # 704,643,072
 GATEUP_CODE_BYTES = K * 2 * (H * I * 3 // 8)              # 176,160,768 per gate/up launch
 GATEUP_CODEBOOK_BYTES = K * 2 * 3 * 256 * 8 * 4           # 786,432
 DOWN_CODE_BYTES = K * (H * I * 3 // 8)
+LDS_GATHER_RATE = {"f32": 5.97e12, "f16": 6.92e12}             # measured random-gather lookups/s, chip-wide
 KERNEL_SOURCES = ["rvq_quantized_moe_amd/csrc/kernels.hip", "rvq_quantized_moe_amd/csrc/device.hpp"]
 
 
@@ -403,6 +404,11 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic_from_profiles(args.dtype),
                      "algorithmic_bytes_per_launch": GATEUP_CODE_BYTES + GATEUP_CODEBOOK_BYTES},
+        # the table kernels' real ceiling: one LDS lookup per code byte, at the random-gather rate
+        # measured for ds_read_b32 over 256-dword (fp32) or ds_read_u16 over 256-half (fp16) subtables
+        "lds_gather": {"kernel": "gate/up", "lookups_per_s": GATEUP_CODE_BYTES / (gu_us * 1e-6),
+                       "ceiling_lookups_per_s": LDS_GATHER_RATE[args.dtype],
+                       "frac": GATEUP_CODE_BYTES / (gu_us * 1e-6) / LDS_GATHER_RATE[args.dtype]},
         "cpu_baseline": cpu,
         "variants": variants,
         "chunk_prefill_512": chunk,
