@@ -118,44 +118,43 @@ __global__ __launch_bounds__(1024) void k_chunk_bucket(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode of one RVQ group into an MFMA A fragment.  Codes of the 64-row x 16-group tile are staged
-// in LDS in the packed slab order (byte b of row r's 48-byte run at (b/16)*1024 + r*16 + b%16).
+// Decode of one RVQ group into an MFMA A fragment.  Codebooks are held in LDS as fp16 [3][256][8]
+// (12 KiB per matrix) for either tile precision: fp16 tiles sum the three vectors with packed fp16
+// adds; bf16 tiles sum them in fp32 and round once (the fp16 codebook rounding, 2^-11, is far below
+// bf16's 2^-8).
+constexpr int kCbBytes = 3 * 256 * 8 * 2;
+
+__device__ inline void load_codebooks(_Float16* d, const float* __restrict__ cb) {
+  for (int i = threadIdx.x; i < 3 * 256 * 8 / 4; i += blockDim.x) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(cb)[i];
+    d[4 * i] = (_Float16)v.x;
+    d[4 * i + 1] = (_Float16)v.y;
+    d[4 * i + 2] = (_Float16)v.z;
+    d[4 * i + 3] = (_Float16)v.w;
+  }
+}
+
 template <bool F16>
 struct Decoder;
 
-// fp16 tiles: codebooks held in LDS as fp16 [3][256][8]; the group is summed with packed fp16 adds.
 template <>
 struct Decoder<true> {
   typedef half8 frag_t;
-  static constexpr int kCbBytes = 3 * 256 * 8 * 2;
-  __device__ static void load_codebooks(uint8_t* dst, const float* __restrict__ cb) {
-    _Float16* d = reinterpret_cast<_Float16*>(dst);
-    for (int i = threadIdx.x; i < 3 * 256 * 8; i += blockDim.x) d[i] = (_Float16)cb[i];
-  }
-  __device__ static frag_t decode(const uint8_t* cbs, int c0, int c1, int c2) {
+  __device__ static frag_t decode(const _Float16* cbs, uint32_t c) {
     const half8* t = reinterpret_cast<const half8*>(cbs);
-    return t[c0] + t[256 + c1] + t[512 + c2];
+    return t[c & 255u] + t[256 + ((c >> 8) & 255u)] + t[512 + ((c >> 16) & 255u)];
   }
 };
 
-// bf16 tiles: codebooks held in LDS as fp32; the group is summed in fp32 and rounded once.
 template <>
 struct Decoder<false> {
   typedef bf16x8 frag_t;
-  static constexpr int kCbBytes = 3 * 256 * 8 * 4;
-  __device__ static void load_codebooks(uint8_t* dst, const float* __restrict__ cb) {
-    float* d = reinterpret_cast<float*>(dst);
-    for (int i = threadIdx.x; i < 3 * 256 * 8; i += blockDim.x) d[i] = cb[i];
-  }
-  __device__ static frag_t decode(const uint8_t* cbs, int c0, int c1, int c2) {
-    const f32x4* t = reinterpret_cast<const f32x4*>(cbs);
-    const f32x4 a0 = t[2 * c0], a1 = t[2 * c0 + 1];
-    const f32x4 b0 = t[2 * (256 + c1)], b1 = t[2 * (256 + c1) + 1];
-    const f32x4 d0 = t[2 * (512 + c2)], d1 = t[2 * (512 + c2) + 1];
-    const f32x4 s0 = a0 + b0 + d0, s1 = a1 + b1 + d1;
+  __device__ static frag_t decode(const _Float16* cbs, uint32_t c) {
+    const half8* t = reinterpret_cast<const half8*>(cbs);
+    const half8 a = t[c & 255u], b = t[256 + ((c >> 8) & 255u)], d = t[512 + ((c >> 16) & 255u)];
     frag_t f;
-    f[0] = (__bf16)s0.x; f[1] = (__bf16)s0.y; f[2] = (__bf16)s0.z; f[3] = (__bf16)s0.w;
-    f[4] = (__bf16)s1.x; f[5] = (__bf16)s1.y; f[6] = (__bf16)s1.z; f[7] = (__bf16)s1.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (__bf16)((float)a[i] + (float)b[i] + (float)d[i]);
     return f;
   }
 };
@@ -163,30 +162,33 @@ struct Decoder<false> {
 __device__ inline f32x4 mfma16(half8 a, half8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
 
-// Stages one packed slab (64 rows x 16 groups, 3072 bytes) into LDS.
-__device__ inline void stage_slab(uint8_t* dst, const uint8_t* __restrict__ src) {
-  for (int i = threadIdx.x; i < kSlabBytes / 16; i += blockDim.x)
-    reinterpret_cast<u32x4*>(dst)[i] = reinterpret_cast<const u32x4*>(src)[i];
-}
-
-// The three code bytes of group g (0..15) of row r (0..63) of a staged slab.
-__device__ inline void slab_codes(const uint8_t* slab, int r, int g, int& c0, int& c1, int& c2) {
-  const int b = 3 * g;
-  c0 = slab[(b / 16) * 1024 + r * 16 + b % 16];
-  c1 = slab[((b + 1) / 16) * 1024 + r * 16 + (b + 1) % 16];
-  c2 = slab[((b + 2) / 16) * 1024 + r * 16 + (b + 2) % 16];
-}
+// The 48 code bytes of row r of a staged slab (byte b of the row's run at (b/16)*1024 + r*16 + b%16)
+// as 12 dwords, and the three code bytes of group g = 4kk + q (q < 4) within them: the 12-byte
+// window of kk holds groups 4kk .. 4kk+3, group q at bytes 3q .. 3q+2.
+struct RowCodes {
+  uint32_t w[12];
+  __device__ void load(const uint8_t* slab, int r) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(slab + j * 1024 + r * 16);
+      w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
+    }
+  }
+  __device__ uint32_t group(int kk, int q) const {   // c0 | c1 << 8 | c2 << 16
+    const uint64_t lo = (uint64_t)w[3 * kk] | ((uint64_t)w[3 * kk + 1] << 32);
+    const uint64_t hi = (uint64_t)w[3 * kk + 1] | ((uint64_t)w[3 * kk + 2] << 32);
+    return (uint32_t)(q < 2 ? lo >> (24 * q) : hi >> (24 * q - 32));
+  }
+};
 
 // ---------------------------------------------------------------------------------------------
 // Expert GEMM for one 64-row block of NMAT matrices of one expert (NMAT = 2: gate and up, which
-// share the activations; NMAT = 1: down).  Activations for the expert's pairs are staged per
-// 128-column K-tile as 16-bit rows; wave w owns rows [16w, 16w+16) of every matrix.
+// share the activations; NMAT = 1: down).  Wave w owns rows [16w, 16w+16) of every matrix.
 //   acc[m][tb] (lane l, i) = sum_k W_m[row0 + 16w + 4(l/16) + i][k] * act[pair tb*16 + l%16][k]
-template <bool F16, int NMAT>
-struct ExpertTile {
-  typedef typename Decoder<F16>::frag_t frag_t;
-  f32x4 acc[NMAT][4];
-};
+// Per 128-column K-tile, the NMAT code slabs and the activations of up to 64 pairs (16-bit rows)
+// sit in one half of a double buffer in LDS.  The next K-tile's global loads are issued into
+// registers before this tile's MFMAs and written to the other half after them, so one barrier per
+// K-tile separates the halves and the load latency hides behind the compute.
 
 // Activation source for the gate/up product: bf16 token rows of the chunk, gathered by pair.
 struct ActTokens {
@@ -209,111 +211,231 @@ __device__ inline int h_exponent(uint32_t maxbits) {
   return e - 15;        // m * 2^-(e-15) < 2^15 < 65504
 }
 
-template <bool F16>
-__device__ inline void stage_act(uint16_t* xs, const ActTokens& a, int p0, int np, int k0) {
-  // 64 token rows x 128 columns; thread q copies 8 columns (16 bytes) at a time.
-  for (int q = threadIdx.x; q < kChunkTok * (kChunkK / 8); q += blockDim.x) {
-    const int j = q / (kChunkK / 8), c8 = q % (kChunkK / 8);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (j < np && k0 + c8 * 8 < a.K) {
-      const int t = a.pair_token[p0 + j];
-      v = *reinterpret_cast<const u32x4*>(a.x + (int64_t)t * a.K + k0 + c8 * 8);
-      if constexpr (F16) {
-        // bf16 -> fp16 (exact for |x| below the fp16 range)
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// Register staging of one K-tile: thread i < 192 holds 16 bytes of each slab; every thread holds 4
+// 16-byte pieces of the activation tile (64 rows x 16 pieces): piece u covers row (tid + 256u)/16.
+constexpr int kActPieces = kChunkTok * (kChunkK / 8) / 256;   // 4 (256-thread workgroups)
+
+template <bool F16, int NMAT>
+struct StageRegs {
+  u32x4 slab[NMAT];
+  u32x4 act[kActPieces];
+  f32x4 hsrc[kActPieces][2];  // ActH: the fp32 source of each piece
+};
+
+struct TokenRows {  // per pass: the token of each of this thread's activation rows (-1: none)
+  int t[kActPieces];
+};
+
+template <bool F16, int NMAT>
+__device__ inline void stage_issue(StageRegs<F16, NMAT>& s, const uint8_t* const (&mats)[NMAT], int kt, int nrb, int rb,
+                                   const ActTokens& a, const TokenRows& tr, int k0) {
+  if (threadIdx.x < kSlabBytes / 16) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float lo = __uint_as_float(w[r] << 16), hi = __uint_as_float(w[r] & 0xffff0000u);
-          const _Float16 hl = (_Float16)lo, hh = (_Float16)hi;
-          w[r] = (uint32_t)__builtin_bit_cast(uint16_t, hl) | ((uint32_t)__builtin_bit_cast(uint16_t, hh) << 16);
-        }
-        v = u32x4{w[0], w[1], w[2], w[3]};
-      }
-    }
-    *reinterpret_cast<u32x4*>(xs + j * kXStride + c8 * 8) = v;
+    for (int m = 0; m < NMAT; ++m)
+      s.slab[m] = reinterpret_cast<const u32x4*>(mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes)[threadIdx.x];
+  }
+#pragma unroll
+  for (int u = 0; u < kActPieces; ++u) {
+    const int c8 = (threadIdx.x + 256 * u) % (kChunkK / 8);
+    const int t = tr.t[u];
+    s.act[u] = (t >= 0 && k0 + c8 * 8 < a.K) ? *reinterpret_cast<const u32x4*>(a.x + (int64_t)t * a.K + k0 + c8 * 8)
+                                             : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-template <bool F16>
-__device__ inline void stage_act(uint16_t* xs, const ActH& a, int p0, int np, int k0) {
-  for (int q = threadIdx.x; q < kChunkTok * (kChunkK / 8); q += blockDim.x) {
-    const int j = q / (kChunkK / 8), c8 = q % (kChunkK / 8);
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (j < np && k0 + c8 * 8 < a.K) {
-      const float* src = a.h + (int64_t)(p0 + j) * a.K + k0 + c8 * 8;
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(src);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(src + 4);
-      const float v[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      if constexpr (F16) {
-        const float sc = ldexpf(1.f, -h_exponent(a.hmax[p0 + j]));
+template <bool F16, int NMAT>
+__device__ inline void stage_issue(StageRegs<F16, NMAT>& s, const uint8_t* const (&mats)[NMAT], int kt, int nrb, int rb,
+                                   const ActH& a, const TokenRows& tr, int k0) {
+  if (threadIdx.x < kSlabBytes / 16) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const _Float16 lo = (_Float16)(v[2 * r] * sc), hi = (_Float16)(v[2 * r + 1] * sc);
-          w[r] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
-      } else {
+    for (int m = 0; m < NMAT; ++m)
+      s.slab[m] = reinterpret_cast<const u32x4*>(mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes)[threadIdx.x];
+  }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const __bf16 lo = (__bf16)v[2 * r], hi = (__bf16)v[2 * r + 1];
-          w[r] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
-      }
+  for (int u = 0; u < kActPieces; ++u) {
+    const int c8 = (threadIdx.x + 256 * u) % (kChunkK / 8);
+    const int p = tr.t[u];  // pair index for ActH
+    if (p >= 0 && k0 + c8 * 8 < a.K) {
+      const float* src = a.h + (int64_t)p * a.K + k0 + c8 * 8;
+      s.hsrc[u][0] = *reinterpret_cast<const f32x4*>(src);
+      s.hsrc[u][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    } else {
+      s.hsrc[u][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s.hsrc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    *reinterpret_cast<u32x4*>(xs + j * kXStride + c8 * 8) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
-// One workgroup = (expert, 64-row block); loops over the expert's pairs 64 at a time and over K.
+__device__ inline uint32_t pack_h2(float lo, float hi) {
+  const _Float16 l = (_Float16)lo, h = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+__device__ inline uint32_t pack_b2(float lo, float hi) {
+  const __bf16 l = (__bf16)lo, h = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
+template <bool F16, int NMAT>
+__device__ inline void stage_store(const StageRegs<F16, NMAT>& s, uint8_t* code_lds, uint16_t* x_lds, const ActTokens&,
+                                   const float (&)[kActPieces]) {
+  if (threadIdx.x < kSlabBytes / 16) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) reinterpret_cast<u32x4*>(code_lds + m * kSlabBytes)[threadIdx.x] = s.slab[m];
+  }
+#pragma unroll
+  for (int u = 0; u < kActPieces; ++u) {
+    const int q = threadIdx.x + 256 * u, j = q / (kChunkK / 8), c8 = q % (kChunkK / 8);
+    u32x4 v = s.act[u];
+    if constexpr (F16) {  // bf16 -> fp16 (exact for |x| below the fp16 range)
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = pack_h2(__uint_as_float(w[r] << 16), __uint_as_float(w[r] & 0xffff0000u));
+      v = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    *reinterpret_cast<u32x4*>(x_lds + j * kXStride + c8 * 8) = v;
+  }
+}
+
+template <bool F16, int NMAT>
+__device__ inline void stage_store(const StageRegs<F16, NMAT>& s, uint8_t* code_lds, uint16_t* x_lds, const ActH&,
+                                   const float (&sc)[kActPieces]) {
+  if (threadIdx.x < kSlabBytes / 16) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) reinterpret_cast<u32x4*>(code_lds + m * kSlabBytes)[threadIdx.x] = s.slab[m];
+  }
+#pragma unroll
+  for (int u = 0; u < kActPieces; ++u) {
+    const int q = threadIdx.x + 256 * u, j = q / (kChunkK / 8), c8 = q % (kChunkK / 8);
+    const f32x4 a = s.hsrc[u][0], b = s.hsrc[u][1];
+    u32x4 v;
+    if constexpr (F16) {
+      const float f = sc[u];
+      v = u32x4{pack_h2(a.x * f, a.y * f), pack_h2(a.z * f, a.w * f), pack_h2(b.x * f, b.y * f), pack_h2(b.z * f, b.w * f)};
+    } else {
+      v = u32x4{pack_b2(a.x, a.y), pack_b2(a.z, a.w), pack_b2(b.x, b.y), pack_b2(b.z, b.w)};
+    }
+    *reinterpret_cast<u32x4*>(x_lds + j * kXStride + c8 * 8) = v;
+  }
+}
+
+// per pass: which token (gate/up) or pair (down) each activation row of this thread reads
+__device__ inline void pass_rows(TokenRows& tr, float (&sc)[kActPieces], const ActTokens& a, int p0, int np) {
+#pragma unroll
+  for (int u = 0; u < kActPieces; ++u) {
+    const int j = (threadIdx.x + 256 * u) / (kChunkK / 8);
+    tr.t[u] = j < np ? a.pair_token[p0 + j] : -1;
+    sc[u] = 1.f;
+  }
+}
+__device__ inline void pass_rows(TokenRows& tr, float (&sc)[kActPieces], const ActH& a, int p0, int np) {
+#pragma unroll
+  for (int u = 0; u < kActPieces; ++u) {
+    const int j = (threadIdx.x + 256 * u) / (kChunkK / 8);
+    tr.t[u] = j < np ? p0 + j : -1;
+    sc[u] = j < np ? ldexpf(1.f, -h_exponent(a.hmax[p0 + j])) : 1.f;
+  }
+}
+
+// Dynamic LDS of the chunk kernels: NMAT fp16 codebooks, then two buffers, each holding NMAT code
+// slabs and the 64 x kXStride activation tile.  Addressed through this one symbol with integer
+// offsets, so every access is known to be LDS (a pointer picked from an array would turn them into
+// flat accesses, which also count against the global-memory counter).
+extern __shared__ __attribute__((aligned(16))) uint8_t chunk_lds[];
+
+template <int NMAT>
+struct ChunkLds {
+  static constexpr int kBuf = NMAT * kSlabBytes + kChunkTok * kXStride * 2;
+  __device__ static _Float16* cb() { return reinterpret_cast<_Float16*>(chunk_lds); }
+  __device__ static uint8_t* code(int b) { return chunk_lds + NMAT * kCbBytes + b * kBuf; }
+  __device__ static uint16_t* act(int b) {
+    return reinterpret_cast<uint16_t*>(chunk_lds + NMAT * kCbBytes + b * kBuf + NMAT * kSlabBytes);
+  }
+};
+
+// The K loop of one pass over NTB 16-pair blocks.  The body is straight-line code (no branch on the
+// pair count, and the next tile's loads are issued unconditionally: the last iteration re-reads the
+// last tile into the idle buffer), so the compiler's memory-counter waits stay exact and the
+// prefetch is never drained early.
+template <bool F16, int NMAT, int NTB, class Act>
+__device__ inline void k_loop(f32x4 (&acc)[NMAT][4], const uint8_t* const (&mats)[NMAT], int ntile, int nrb, int rb,
+                              const Act& act, const TokenRows& tr, const float (&sc)[kActPieces],
+                              StageRegs<F16, NMAT>& st) {
+  typedef typename Decoder<F16>::frag_t frag_t;
+  typedef ChunkLds<NMAT> L;
+  const _Float16* cb_lds = L::cb();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4;
+  const int r = 16 * wave + (lane & 15);
+  for (int kt = 0; kt < ntile; ++kt) {
+    const int cur = kt & 1;
+    const int nxt = kt + 1 < ntile ? kt + 1 : kt;
+    stage_issue<F16, NMAT>(st, mats, nxt, nrb, rb, act, tr, nxt * kChunkK);
+    RowCodes rc[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) rc[m].load(L::code(cur) + m * kSlabBytes, r);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      frag_t a[NMAT];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) a[m] = Decoder<F16>::decode(cb_lds + m * (kCbBytes / 2), rc[m].group(kk, q));
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        const frag_t b =
+            *reinterpret_cast<const frag_t*>(L::act(cur) + (tb * 16 + (lane & 15)) * kXStride + 32 * kk + 8 * q);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) acc[m][tb] = mfma16(a[m], b, acc[m][tb]);
+      }
+    }
+    stage_store<F16, NMAT>(st, L::code(cur ^ 1), L::act(cur ^ 1), act, sc);
+    __syncthreads();
+  }
+}
+
+// One workgroup = (expert, row blocks [rb0, rb1)): loads the codebooks once, then per 64-row block
+// loops over the expert's pairs 64 at a time and over K.
 template <bool F16, int NMAT, class Act, class Epi>
 __device__ void expert_tile_gemm(const uint8_t* const (&mats)[NMAT], const float* const (&cbs)[NMAT], int K,
-                                 int rb, int nrb, int p_begin, int n_pairs, const Act& act, const Epi& epi,
-                                 uint8_t* smem) {
-  typedef typename Decoder<F16>::frag_t frag_t;
-  constexpr int CB = Decoder<F16>::kCbBytes;
-  uint8_t* cb_lds = smem;                                         // NMAT codebooks
-  uint8_t* code_lds = smem + NMAT * CB;                           // NMAT slabs
-  uint16_t* x_lds = reinterpret_cast<uint16_t*>(code_lds + NMAT * kSlabBytes);
+                                 int rb0, int rb1, int nrb, int p_begin, int n_pairs, const Act& act, const Epi& epi) {
+  typedef ChunkLds<NMAT> L;
+  _Float16* cb_lds = L::cb();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int m = 0; m < NMAT; ++m) Decoder<F16>::load_codebooks(cb_lds + m * CB, cbs[m]);
+  const int q = lane >> 4;
+  for (int m = 0; m < NMAT; ++m) load_codebooks(cb_lds + m * (kCbBytes / 2), cbs[m]);
   const int ntile = (K / 8 + 15) / 16;
+  for (int rb = rb0; rb < rb1; ++rb)
   for (int pb = 0; pb < n_pairs; pb += kChunkTok) {
     const int np = n_pairs - pb < kChunkTok ? n_pairs - pb : kChunkTok;
+    TokenRows tr;
+    float sc[kActPieces];
+    pass_rows(tr, sc, act, p_begin + pb, np);
+    StageRegs<F16, NMAT> st;
+    stage_issue<F16, NMAT>(st, mats, 0, nrb, rb, act, tr, 0);
+    __syncthreads();  // the previous pass is done with both buffers (and the codebooks are stored)
+    stage_store<F16, NMAT>(st, L::code(0), L::act(0), act, sc);
+    __syncthreads();
     f32x4 acc[NMAT][4];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[m][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kt = 0; kt < ntile; ++kt) {
-      __syncthreads();  // previous tile's LDS contents are consumed
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-        stage_slab(code_lds + m * kSlabBytes, mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes);
-      stage_act<F16>(x_lds, act, p_begin + pb, np, kt * kChunkK);
-      __syncthreads();
-      const int r = 16 * wave + (lane & 15);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int g = 4 * kk + (lane >> 4);
-        frag_t a[NMAT];
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-          int c0, c1, c2;
-          slab_codes(code_lds + m * kSlabBytes, r, g, c0, c1, c2);
-          a[m] = Decoder<F16>::decode(cb_lds + m * CB, c0, c1, c2);
-        }
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          if (tb * 16 < np) {
-            const frag_t b =
-                *reinterpret_cast<const frag_t*>(x_lds + (tb * 16 + (lane & 15)) * kXStride + 32 * kk + 8 * (lane >> 4));
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) acc[m][tb] = mfma16(a[m], b, acc[m][tb]);
-          }
-        }
-      }
+    switch ((np + 15) / 16) {
+      case 1: k_loop<F16, NMAT, 1>(acc, mats, ntile, nrb, rb, act, tr, sc, st); break;
+      case 2: k_loop<F16, NMAT, 2>(acc, mats, ntile, nrb, rb, act, tr, sc, st); break;
+      case 3: k_loop<F16, NMAT, 3>(acc, mats, ntile, nrb, rb, act, tr, sc, st); break;
+      default: k_loop<F16, NMAT, 4>(acc, mats, ntile, nrb, rb, act, tr, sc, st); break;
     }
-    epi(acc, p_begin + pb, np, 16 * wave + 4 * (lane >> 4), lane & 15);
+    epi(acc, p_begin + pb, np, rb * kChunkRows + 16 * wave + 4 * q, lane & 15);
   }
+}
+
+// Work index of this workgroup such that consecutive work items run on the same XCD: workgroups
+// are dealt to the 8 XCDs round-robin, so work item w goes to workgroup (w % per) * 8 + w / per.
+// An expert's workgroups then share one L2, which serves its activation rows to all of them.
+// The grid is a multiple of 8; returns -1 for padding workgroups.
+__device__ inline int xcd_major(int nwork) {
+  const int per = gridDim.x >> 3;
+  const int w = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  return w < nwork ? w : -1;
 }
 
 // Gate/up: h[p][row] = silu(g) * u (fp32), and the per-pair max |h| (fp16 tiles scale h by it).
@@ -321,7 +443,7 @@ template <bool F16>
 struct GateUpEpi {
   float* h;
   uint32_t* hmax;
-  int I, row0;
+  int I;
   __device__ void operator()(const f32x4 (&acc)[2][4], int p0, int np, int rloc, int col) const {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
@@ -332,7 +454,7 @@ struct GateUpEpi {
       for (int i = 0; i < 4; ++i) {
         const float g = acc[0][tb][i], u = acc[1][tb][i];
         const float hv = g / (1.f + expf(-g)) * u;
-        h[(int64_t)(p0 + j) * I + row0 + rloc + i] = hv;
+        h[(int64_t)(p0 + j) * I + rloc + i] = hv;
         m = fmaxf(m, fabsf(hv));
       }
       if constexpr (F16) atomicMax(&hmax[p0 + j], __float_as_uint(m));
@@ -345,7 +467,7 @@ template <bool F16>
 struct DownEpi {
   float* y;
   const uint32_t* hmax;
-  int H, row0;
+  int H;
   __device__ void operator()(const f32x4 (&acc)[1][4], int p0, int np, int rloc, int col) const {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
@@ -353,7 +475,7 @@ struct DownEpi {
       if (j >= np) continue;
       const float sc = F16 ? ldexpf(1.f, h_exponent(hmax[p0 + j])) : 1.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[(int64_t)(p0 + j) * H + row0 + rloc + i] = acc[0][tb][i] * sc;
+      for (int i = 0; i < 4; ++i) y[(int64_t)(p0 + j) * H + rloc + i] = acc[0][tb][i] * sc;
     }
   }
 };
@@ -362,11 +484,13 @@ template <bool F16>
 __global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint16_t* __restrict__ x,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ pair_token, float* __restrict__ h,
-                                                      uint32_t* __restrict__ hmax) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem_gu[];
+                                                      uint32_t* __restrict__ hmax, int rpw) {
   const int H = bank.H, I = bank.I;
-  const int nrb = I / kChunkRows;
-  const int e = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+  const int nrb = I / kChunkRows, ngrp = (nrb + rpw - 1) / rpw;
+  const int w = xcd_major(bank.E * ngrp);
+  if (w < 0) return;
+  const int e = w / ngrp, rb0 = (w % ngrp) * rpw;
+  const int rb1 = rb0 + rpw < nrb ? rb0 + rpw : nrb;
   const int p_begin = offsets[e], n_pairs = offsets[e + 1] - p_begin;
   if (n_pairs == 0) return;
   const uint8_t* rec = bank.codes + (int64_t)e * bank.stride;
@@ -374,26 +498,28 @@ __global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint1
   const float* const cbs[2] = {bank.cb + ((int64_t)e * 3 + 0) * kCodebookFloats,
                                bank.cb + ((int64_t)e * 3 + 1) * kCodebookFloats};
   ActTokens act{x, pair_token, H};
-  GateUpEpi<F16> epi{h, hmax, I, rb * kChunkRows};
-  expert_tile_gemm<F16, 2>(mats, cbs, H, rb, nrb, p_begin, n_pairs, act, epi, smem_gu);
+  GateUpEpi<F16> epi{h, hmax, I};
+  expert_tile_gemm<F16, 2>(mats, cbs, H, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
 }
 
 template <bool F16>
 __global__ __launch_bounds__(256) void k_chunk_down(BankArgs bank, const int32_t* __restrict__ offsets,
                                                     const float* __restrict__ h, const uint32_t* __restrict__ hmax,
-                                                    float* __restrict__ y) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem_dn[];
+                                                    float* __restrict__ y, int rpw) {
   const int H = bank.H, I = bank.I;
-  const int nrb = H / kChunkRows;
-  const int e = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+  const int nrb = H / kChunkRows, ngrp = (nrb + rpw - 1) / rpw;
+  const int w = xcd_major(bank.E * ngrp);
+  if (w < 0) return;
+  const int e = w / ngrp, rb0 = (w % ngrp) * rpw;
+  const int rb1 = rb0 + rpw < nrb ? rb0 + rpw : nrb;
   const int p_begin = offsets[e], n_pairs = offsets[e + 1] - p_begin;
   if (n_pairs == 0) return;
   const uint8_t* rec = bank.codes + (int64_t)e * bank.stride;
   const uint8_t* const mats[1] = {rec + 2 * packed_bytes(I, H)};
   const float* const cbs[1] = {bank.cb + ((int64_t)e * 3 + 2) * kCodebookFloats};
   ActH act{h, hmax, I};
-  DownEpi<F16> epi{y, hmax, H, rb * kChunkRows};
-  expert_tile_gemm<F16, 1>(mats, cbs, I, rb, nrb, p_begin, n_pairs, act, epi, smem_dn);
+  DownEpi<F16> epi{y, hmax, H};
+  expert_tile_gemm<F16, 1>(mats, cbs, I, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
 }
 
 // out[t][r] = residual[t][r] + sum_i gates[t][i] * y[pair_pos[t][i]][r]   (fixed order in i)
@@ -413,8 +539,8 @@ __global__ __launch_bounds__(256) void k_chunk_combine(const float* __restrict__
 }
 
 static size_t chunk_smem(bool f16, int nmat) {
-  const size_t cb = f16 ? Decoder<true>::kCbBytes : Decoder<false>::kCbBytes;
-  return nmat * cb + nmat * kSlabBytes + (size_t)kChunkTok * kXStride * 2;
+  (void)f16;
+  return nmat * kCbBytes + 2 * (nmat * kSlabBytes + (size_t)kChunkTok * kXStride * 2);
 }
 
 hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
@@ -433,20 +559,27 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
   const size_t bucket_smem = ((size_t)E * ((T + 31) / 32) + E + 1) * 4;
   hipLaunchKernelGGL(k_chunk_bucket, dim3(1), dim3(1024), bucket_smem, stream, ids, T, k, E, offsets, pair_token,
                      pair_pos, hmax, status);
-  const unsigned g_gu = (unsigned)(E * (I / kChunkRows)), g_dn = (unsigned)(E * (H / kChunkRows));
-  // bf16 tiles keep fp32 codebooks in LDS (over 64 KiB for gate+up): allow the larger allocation
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_chunk_gateup<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)chunk_smem(false, 2));
+  // row blocks per workgroup: the codebooks are loaded once per workgroup
+  const int rpw_gu = 2, rpw_dn = 4;
+  const unsigned g_gu = (unsigned)(cdiv(E * cdiv(I / kChunkRows, rpw_gu), 8) * 8);
+  const unsigned g_dn = (unsigned)(cdiv(E * cdiv(H / kChunkRows, rpw_dn), 8) * 8);
+  // gate+up double-buffers two slabs and the token tile next to two codebooks (over 64 KiB): allow
+  // the larger allocation
+  for (const void* f : {reinterpret_cast<const void*>(k_chunk_gateup<false>),
+                        reinterpret_cast<const void*>(k_chunk_gateup<true>)}) {
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)chunk_smem(f16, 2));
+    if (e != hipSuccess) return e;
+  }
   if (f16) {
     hipLaunchKernelGGL(k_chunk_gateup<true>, dim3(g_gu), dim3(256), chunk_smem(true, 2), stream, bank, x, offsets,
-                       pair_token, h, hmax);
+                       pair_token, h, hmax, rpw_gu);
     hipLaunchKernelGGL(k_chunk_down<true>, dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets, h, hmax,
-                       ybuf);
+                       ybuf, rpw_dn);
   } else {
     hipLaunchKernelGGL(k_chunk_gateup<false>, dim3(g_gu), dim3(256), chunk_smem(false, 2), stream, bank, x, offsets,
-                       pair_token, h, hmax);
+                       pair_token, h, hmax, rpw_gu);
     hipLaunchKernelGGL(k_chunk_down<false>, dim3(g_dn), dim3(256), chunk_smem(false, 1), stream, bank, offsets, h,
-                       hmax, ybuf);
+                       hmax, ybuf, rpw_dn);
   }
   hipLaunchKernelGGL(k_chunk_combine, dim3((unsigned)cdiv(H, 256), (unsigned)T), dim3(256), 0, stream, ybuf, pair_pos,
                      gates, k, H, residual, y);
