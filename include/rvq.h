@@ -205,6 +205,14 @@ int rvq_moe_decode_routed(const rvq_expert_bank_t *bank, const void *w_router_bf
                           const float *residual, float *y, int32_t *ids, float *gates, double *logits,
                           int32_t compute_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Testing aid for the failure path.  Sets how many times each bounded wait
+ * between the wave roles of the table kernels polls before it gives up
+ * (which sets RVQ_ERR_DEVICE_STALL and leaves the output invalid, but lets
+ * every kernel finish).  polls < 0 restores the default (4,194,304, about a
+ * tenth of a second).  Returns the previous value.  Process-wide; affects
+ * launches enqueued after the call. */
+int32_t rvq_set_wait_limit(int32_t polls);
+
 /* Zero-fill a workspace (with a kernel, so the call can be graph-captured). */
 int rvq_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
 

@@ -43,7 +43,7 @@ EXPORTS = [
     "rvq_expert_gemv_workspace_bytes", "rvq_expert_gemv", "rvq_router_topk", "rvq_bank_record_bytes",
     "rvq_moe_layer_workspace_bytes", "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed",
     "rvq_workspace_init", "rvq_rmsnorm", "rvq_stream_copy",
-    "rvq_check_device_status", "rvq_moe_decode_routed",
+    "rvq_check_device_status", "rvq_moe_decode_routed", "rvq_set_wait_limit",
 ]
 
 
@@ -77,6 +77,8 @@ def lib():
         L.rvq_rmsnorm.argtypes = [p, i32, i32, ctypes.c_float, p, p]
         L.rvq_check_device_status.argtypes = [p, p]
         L.rvq_stream_copy.argtypes = [p, p, sz, p]
+        L.rvq_set_wait_limit.argtypes = [i32]
+        L.rvq_set_wait_limit.restype = i32
         L.rvq_moe_decode_routed.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, p, p, p, p, p, i32, p, sz, p]
         for name in ("rvq_pack_codes", "rvq_lut_build", "rvq_expert_gemv", "rvq_router_topk",
                      "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed", "rvq_workspace_init", "rvq_rmsnorm",

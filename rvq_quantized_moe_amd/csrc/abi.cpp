@@ -205,6 +205,8 @@ int rvq_moe_decode_routed(const rvq_expert_bank_t* bank, const void* w_router_bf
                                       stream, nullptr, &route));
 }
 
+int32_t rvq_set_wait_limit(int32_t polls) { return set_wait_limit(polls); }
+
 int rvq_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!workspace) return RVQ_ERR_NULL;
   if (!aligned(workspace, 256)) return RVQ_ERR_ALIGN;

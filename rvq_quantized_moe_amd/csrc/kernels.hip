@@ -549,12 +549,21 @@ constexpr int kDnStreamWaves = 7, kDnBpi = 4;     // down: row chunks of 28 row 
 constexpr int kSpinLimit = 1 << 22;
 constexpr int kStatusStall = 8;        // RVQ_ERR_DEVICE_STALL
 
-__device__ inline bool lds_wait_ge(int* flag, int target) {
-  for (int i = 0; i < kSpinLimit; ++i) {
+__device__ inline bool lds_wait_ge(int* flag, int target, int limit) {
+  for (int i = 0; i < limit; ++i) {
     if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return true;
     __builtin_amdgcn_s_sleep(1);
   }
   return false;
+}
+
+// Polls per bounded wait of the wave-specialised kernels (see rvq_set_wait_limit).
+static int g_wait_limit = kSpinLimit;
+
+int set_wait_limit(int polls) {
+  const int old = g_wait_limit;
+  g_wait_limit = polls < 0 ? kSpinLimit : polls;
+  return old;
 }
 
 // Compute units of the current device (0 if the query fails), cached per device.
@@ -586,6 +595,7 @@ struct PipeArgs {
   int32_t* ids_out;
   float* gates_out;
   int k;
+  int wait_limit;         // polls per bounded wait (kSpinLimit unless a test lowers it)
 };
 constexpr int kRouteMaxExperts = 1024;
 
@@ -729,7 +739,7 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
     bool ok = true;
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
-      ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1));
+      ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1), pa.wait_limit);
 #pragma unroll
       for (int r = 0; r < BPI; ++r) {
         const int s = k * BPI + r;
@@ -785,12 +795,12 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
     }
     if (DOWN || F16) {
       if (lane == 0) __hip_atomic_fetch_add(&hready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      ok &= lds_wait_ge(&hready, kPipeBuildWaves);
+      ok &= lds_wait_ge(&hready, kPipeBuildWaves, pa.wait_limit);
       if constexpr (F16) cmax2 = __int_as_float(cmax_bits);
     }
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
-      if (k >= 2) ok &= lds_wait_ge(&done[k & 1], NSW * (k / 2));
+      if (k >= 2) ok &= lds_wait_ge(&done[k & 1], NSW * (k / 2), pa.wait_limit);
       // an opaque copy pins this item's products after the wait (otherwise the compiler may compute
       // every item's tables up front)
       f32x2 xk;
@@ -1056,7 +1066,7 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
   if (chunk) {
     const dim3 grid((unsigned)(k * 2 * ngu));
     const PipeArgs pa{x,       nullptr, part_gu, ngu, 1, 0, fused_route ? route->logits : nullptr,
-                      route ? route->ids : nullptr, route ? route->gates : nullptr, k};
+                      route ? route->ids : nullptr, route ? route->gates : nullptr, k, g_wait_limit};
     switch (chunk) {
 #define RVQ_WS_CASE(n)                                                                                             \
   case n:                                                                                                          \
@@ -1082,7 +1092,7 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
   if (dchunk) {
     const int nkc = nt16_out / dchunk;
     const dim3 grid((unsigned)(k * nrc * nkc));
-    const PipeArgs pa{nullptr, part_gu, part_d, nkc, nrc, ngu, nullptr, nullptr, nullptr, k};
+    const PipeArgs pa{nullptr, part_gu, part_d, nkc, nrc, ngu, nullptr, nullptr, nullptr, k, g_wait_limit};
     switch (dchunk) {
 #define RVQ_WS_CASE(n)                                                                                             \
   case n:                                                                                                          \

@@ -31,6 +31,8 @@ hipError_t launch_gemv(const uint8_t* codes, const float* cb, int rows, int cols
 hipError_t launch_router_topk(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, int k, int32_t* ids,
                               float* gates, double* logits, hipStream_t stream);
 hipError_t launch_rmsnorm(const float* x, int T, int H, float eps, float* out, hipStream_t stream);
+// Polls per bounded wait inside the wave-specialised kernels; returns the previous value (< 0: default).
+int set_wait_limit(int polls);
 hipError_t launch_router_logits(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, double* logits,
                                 hipStream_t stream);
 // Routing inputs of a decode step: the router logits (fp64 [E]) and where the top-k ids/gates go.

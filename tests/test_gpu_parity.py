@@ -332,3 +332,63 @@ def test_routed_decode_small_expert_count():
         ids2, gates2, _ = rvq.router_topk(w, x, k)
         assert torch.equal(ids, ids2[0]) and torch.equal(gates, gates2[0])
         assert torch.equal(y, rvq.moe_layer_forward(bank, x, ids2[0], gates2[0]))
+
+
+# ---------------------------------------------------------------- other layer shapes
+
+@pytest.mark.parametrize("H,I,E,k", [
+    (256, 128, 8, 4),      # one-K-tile-per-workgroup kernels (gate/up rows != 2048)
+    (264, 200, 6, 3),      # ragged: 33 groups, 200 rows (partial row block), both fallbacks
+    (1024, 2048, 8, 4),    # wave-specialised gate/up, fallback down (16 row blocks of H)
+    (3584, 2048, 4, 2),    # both wave-specialised kernels, 2 row chunks of down
+])
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_moe_layer_other_shapes(H, I, E, k, dtype):
+    say(f"moe layer H={H} I={I} E={E} k={k} {dtype}")
+    seed = synth.SEED_EXPERT ^ (H * 131 + I)
+    bank = upload_bank(seed, 0, E, H, I)
+    bits, w = router(seed, 0, E, H)
+    cache = {}
+    def get(e):
+        if e not in cache:
+            cache[e] = oracle_expert(seed, 0, e, H, I)
+        return cache[e]
+    ws = rvq.make_moe_workspace(bank, 1, k, dtype)
+    for t in (0, 1):
+        x = synth.activation_f32(seed, t, H)
+        r = synth.activation_f32(seed, 100 + t, H)
+        xd, rd = to_dev(x), to_dev(r)
+        ids, gates, _ = rvq.router_topk(w, xd, k)
+        y = rvq.moe_layer_forward(bank, xd, ids[0], gates[0], residual=rd, dtype=dtype, workspace=ws)
+        y_ref, ids_ref, _, _ = oracle.moe_layer(get, bits, x, k, residual=r)
+        assert np.array_equal(ids[0].cpu().numpy(), ids_ref)
+        err = rel_l2(y.cpu().numpy() - r, y_ref - r)
+        say(f"  rel-L2 {err:.3e}")
+        assert err <= TOL[dtype]
+        y2, ids2, gates2, _ = rvq.moe_decode_routed(bank, w, xd, k, residual=rd, dtype=dtype, workspace=ws)
+        assert torch.equal(ids2, ids[0]) and torch.equal(gates2, gates[0]) and torch.equal(y2, y)
+    assert rvq.check_device_status(ws) == 0
+
+
+def test_bounded_waits_give_up_and_report(layer_bank):
+    """Failure path of the wave-specialised kernels, forced from the host: with their bounded waits cut
+    to zero polls they still finish (every access stays in bounds) and the workspace reports
+    RVQ_ERR_DEVICE_STALL; the default limit brings back the exact result."""
+    say("bounded waits cut to zero polls")
+    bank, bits, w = layer_bank
+    L = rvq.lib()
+    x = to_dev(synth.activation_f32(synth.SEED_LAYER, 9, HIDDEN))
+    ids, gates, _ = rvq.router_topk(w, x, TOP_K)
+    ws = rvq.make_moe_workspace(bank, 1, TOP_K, "f32")
+    ref = rvq.moe_layer_forward(bank, x, ids[0], gates[0], workspace=ws)
+    assert rvq.check_device_status(ws) == 0
+    L.rvq_set_wait_limit(0)
+    try:
+        rvq.moe_layer_forward(bank, x, ids[0], gates[0], workspace=ws)
+        st = rvq.check_device_status(ws)
+    finally:
+        L.rvq_set_wait_limit(-1)
+    assert st == 8  # RVQ_ERR_DEVICE_STALL
+    again = rvq.moe_layer_forward(bank, x, ids[0], gates[0], workspace=ws)
+    assert rvq.check_device_status(ws) == 0
+    assert torch.equal(again, ref)
