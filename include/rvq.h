@@ -223,9 +223,9 @@ int rvq_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stre
 int rvq_rmsnorm(const float *x, int32_t T, int32_t H, float eps, float *out, hipStream_t stream);
 
 /* Measurement aid: copies nbytes (multiple of 16) from src to dst (16-byte
- * aligned, non-overlapping) with the same 16-byte global loads the code
- * stream uses, so its duration gives the achievable streaming rate and its
- * memory-traffic counters scale those of the table kernels. */
+ * aligned, non-overlapping) with the same non-temporal 16-byte global loads
+ * the code stream uses, so its duration gives the achievable streaming rate
+ * and its memory-traffic counters scale those of the table kernels. */
 int rvq_stream_copy(const void *src, void *dst, size_t nbytes, hipStream_t stream);
 
 /* Synchronises `stream`, returns the sticky device status held in the

@@ -232,7 +232,7 @@ __device__ inline void stage_issue(StageRegs<F16, NMAT>& s, const uint8_t* const
   if (threadIdx.x < kSlabBytes / 16) {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
-      s.slab[m] = reinterpret_cast<const u32x4*>(mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes)[threadIdx.x];
+      s.slab[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes) + threadIdx.x);
   }
 #pragma unroll
   for (int u = 0; u < kActPieces; ++u) {
@@ -249,7 +249,7 @@ __device__ inline void stage_issue(StageRegs<F16, NMAT>& s, const uint8_t* const
   if (threadIdx.x < kSlabBytes / 16) {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
-      s.slab[m] = reinterpret_cast<const u32x4*>(mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes)[threadIdx.x];
+      s.slab[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes) + threadIdx.x);
   }
 #pragma unroll
   for (int u = 0; u < kActPieces; ++u) {

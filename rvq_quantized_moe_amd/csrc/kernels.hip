@@ -67,8 +67,10 @@ hipError_t launch_zero(void* p, size_t nbytes, hipStream_t stream) {
 __global__ __launch_bounds__(256) void k_stream_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                      int64_t n16) {
   const int64_t stride = (int64_t)gridDim.x * 256;
+  // the same non-temporal 16-byte load as the code stream, so its memory counters calibrate those
+  // of the table kernels
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride)
-    dst[i] = src[i];
+    dst[i] = __builtin_nontemporal_load(src + i);
 }
 
 hipError_t launch_stream_copy(const void* src, void* dst, size_t nbytes, hipStream_t stream) {
