@@ -10,6 +10,9 @@ Prints ONE JSON line.  Roofline: the dominant kernel (gate/up, two thirds of the
 timed with HIP events recorded around it on its own stream inside the timed region; its
 algorithmic bytes per launch are the code bytes of 16 experts' gate and up matrices plus their
 codebooks.  cpu_baseline: the fp64 oracle on a bounded sample of the same workload.
+
+Also reported, not the headline: the 512-token chunked prefill (decode-to-MFMA path), one 256x512
+matvec, one SwiGLU expert per token, and the 92-layer x 64-expert stack decode (97 GB resident).
 """
 import argparse
 import ctypes
@@ -256,6 +259,99 @@ def run_chunk(rvq, hip, bank, w, xt, steps, dtype):
             "mfma_TFLOPs": flops / (moe_ms * 1e-3) / 1e12, "tile_dtype": dtype}
 
 
+def replay_rate(torch, graphs, steps, warmup, before=None):
+    """Replays graphs round-robin (before(i) runs eagerly ahead of replay i); returns seconds per step."""
+    for i in range(warmup):
+        if before:
+            before(i)
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if before:
+            before(i)
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        fn()
+    return g
+
+
+def run_matvec(torch, rvq, dev, steps):
+    """One 256x512 RVQ matvec (fp32 tables): microseconds per call, graph-replayed."""
+    import synth
+    from workloads import MATVEC_COLS, MATVEC_ROWS
+    R, C = MATVEC_ROWS, MATVEC_COLS
+    codes = synth.matrix_codes(synth.SEED_MATVEC, 0, 0, synth.SINGLE, R, C)
+    cb = torch.from_numpy(synth.matrix_codebooks(synth.SEED_MATVEC, 0, 0, synth.SINGLE)).to(dev)
+    packed = rvq.pack_codes(torch.from_numpy(codes).to(dev), R, C)
+    xs = [torch.from_numpy(synth.activation_f32(synth.SEED_MATVEC, t, C)).to(dev) for t in range(8)]
+    y = torch.empty(R, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(rvq.gemv_workspace_bytes(R, C, "f32"), 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    graphs = [capture(torch, lambda x=x: rvq.expert_gemv(packed, cb, R, C, x, "f32", y=y, workspace=ws)) for x in xs]
+    sec = replay_rate(torch, graphs, steps, 20)
+    return {"us_per_call": sec * 1e6, "code_GBps": R * C * 3 / 8 / sec / 1e9}
+
+
+def run_expert(torch, rvq, bank, pool, steps):
+    """One SwiGLU expert (7168/2048, fp32 tables) per token: the layer forward with k = 1, rotating
+    over 32 of the resident experts so that no expert stays cached; microseconds per token."""
+    dev = pool.device
+    ids = [torch.tensor([e], dtype=torch.int32, device=dev) for e in range(0, 256, 8)]
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    y = torch.empty(H, dtype=torch.float32, device=dev)
+    ws = rvq.make_moe_workspace(bank, 1, 1, "f32")
+    torch.cuda.synchronize()
+    graphs = [capture(torch, lambda j=j: rvq.moe_layer_forward(bank, pool[j % POOL], ids[j], one, dtype="f32", y=y,
+                                                               workspace=ws)) for j in range(len(ids))]
+    sec = replay_rate(torch, graphs, steps, 20)
+    status = rvq.check_device_status(ws)
+    if status:
+        raise RuntimeError(rvq.status_string(status))
+    return {"us_per_token": sec * 1e6, "code_GBps": 3 * (H * I * 3 // 8) / sec / 1e9}
+
+
+def run_stack(torch, rvq, dev, dtype):
+    """92-layer stack decode (64 experts per layer, top-16, RMSNorm + residual between layers): 32
+    steps of fresh tokens, each step one graph of 92 x (rmsnorm + routed decode)."""
+    import synth
+    from workloads import RMS_EPS, STACK_STEPS, Stack
+    print("[bench] uploading the 92-layer stack (97 GB of codes)", file=sys.stderr, flush=True)
+    st = Stack(device=dev)
+    xin = torch.empty(H, dtype=torch.float32, device=dev)
+    h = torch.empty(H, dtype=torch.float32, device=dev)
+    n = torch.empty(H, dtype=torch.float32, device=dev)
+    ids = torch.empty(K, dtype=torch.int32, device=dev)
+    gates = torch.empty(K, dtype=torch.float32, device=dev)
+    logits = torch.empty(st.E, dtype=torch.float64, device=dev)
+    ws = rvq.make_moe_workspace(st.banks[0], 1, K, dtype)
+    xs = [torch.from_numpy(synth.activation_f32(synth.SEED_STACK, t, H)).to(dev) for t in range(STACK_STEPS)]
+
+    def step():
+        h.copy_(xin)
+        for l in range(st.L):
+            rvq.rmsnorm(h, RMS_EPS, out=n)
+            rvq.moe_decode_routed(st.banks[l], st.routers[l], n, K, residual=h, dtype=dtype, y=h, ids=ids,
+                                  gates=gates, logits=logits, workspace=ws)
+    torch.cuda.synchronize()
+    g = capture(torch, step)
+    sec = replay_rate(torch, [g], STACK_STEPS * 3, 4, before=lambda i: xin.copy_(xs[i % STACK_STEPS]))
+    status = rvq.check_device_status(ws)
+    if status:
+        raise RuntimeError(rvq.status_string(status))
+    code = st.L * K * 3 * (H * I * 3 // 8)
+    del st
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": 1.0 / sec, "ms_per_token": sec * 1e3, "code_GBps": code / sec / 1e9,
+            "code_frac_of_hbm_peak": code / sec / 1e9 / HBM_PEAK_GBPS, "table_dtype": dtype}
+
+
 def stream_copy_peak(torch, rvq, dev):
     """Read+write GB/s of rvq_stream_copy over 1 GiB (the code stream's load instruction); its
     rocprofv3 FETCH_SIZE/WRITE_SIZE per dispatch (1 GiB each) calibrate the counters."""
@@ -329,6 +425,8 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="skip the other table precision")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-chunk", action="store_true", help="skip the 512-token chunked-prefill measurement")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads (one matvec, one expert, the 92-layer stack)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
@@ -366,6 +464,14 @@ def main():
         xb = np.stack([synth.activation_bf16_bits(synth.SEED_CHUNK, t, H) for t in range(512)])
         xt = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
         chunk = {d: run_chunk(rvq, hip, bank, w, xt, 20, d) for d in ("f16", "bf16")}
+    extra = None
+    if not args.no_extra:
+        print("[bench] one matvec, one expert", file=sys.stderr, flush=True)
+        extra = {"matvec_256x512_f32": run_matvec(torch, rvq, dev, 2000),
+                 "expert_7168x2048_f32": run_expert(torch, rvq, bank, pool, 1000)}
+        del bank
+        torch.cuda.empty_cache()
+        extra["stack_92x64_top16_" + args.dtype] = run_stack(torch, rvq, dev, args.dtype)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -412,6 +518,7 @@ def main():
         "cpu_baseline": cpu,
         "variants": variants,
         "chunk_prefill_512": chunk,
+        "other_workloads": extra,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
