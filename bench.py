@@ -318,15 +318,14 @@ def run_expert(torch, rvq, bank, pool, steps):
 
 
 def run_stack(torch, rvq, dev, dtype):
-    """92-layer stack decode (64 experts per layer, top-16, RMSNorm + residual between layers): 32
-    steps of fresh tokens, each step one graph of 92 x (rmsnorm + routed decode)."""
+    """92-layer stack decode (64 experts per layer, top-16, pre-norm residual blocks): 32 steps of
+    fresh tokens, each step one graph of 92 block decodes (RMSNorm folded into the router)."""
     import synth
     from workloads import RMS_EPS, STACK_STEPS, Stack
     print("[bench] uploading the 92-layer stack (97 GB of codes)", file=sys.stderr, flush=True)
     st = Stack(device=dev)
     xin = torch.empty(H, dtype=torch.float32, device=dev)
     h = torch.empty(H, dtype=torch.float32, device=dev)
-    n = torch.empty(H, dtype=torch.float32, device=dev)
     ids = torch.empty(K, dtype=torch.int32, device=dev)
     gates = torch.empty(K, dtype=torch.float32, device=dev)
     logits = torch.empty(st.E, dtype=torch.float64, device=dev)
@@ -336,9 +335,8 @@ def run_stack(torch, rvq, dev, dtype):
     def step():
         h.copy_(xin)
         for l in range(st.L):
-            rvq.rmsnorm(h, RMS_EPS, out=n)
-            rvq.moe_decode_routed(st.banks[l], st.routers[l], n, K, residual=h, dtype=dtype, y=h, ids=ids,
-                                  gates=gates, logits=logits, workspace=ws)
+            rvq.moe_block_decode(st.banks[l], st.routers[l], h, K, RMS_EPS, dtype=dtype, h_out=h, ids=ids,
+                                 gates=gates, logits=logits, workspace=ws)
     torch.cuda.synchronize()
     g = capture(torch, step)
     sec = replay_rate(torch, [g], STACK_STEPS * 3, 4, before=lambda i: xin.copy_(xs[i % STACK_STEPS]))

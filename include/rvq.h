@@ -205,6 +205,21 @@ int rvq_moe_decode_routed(const rvq_expert_bank_t *bank, const void *w_router_bf
                           const float *residual, float *y, int32_t *ids, float *gates, double *logits,
                           int32_t compute_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * One pre-norm residual MoE block for one token (a layer of the stack):
+ *   n = RMSNorm(h) (unit weight, as rvq_rmsnorm);  h_out = h + MoE(n)
+ * with the router, top-k and expert forward of rvq_moe_decode_routed on n.
+ * Results equal rvq_rmsnorm followed by rvq_moe_decode_routed(x = n,
+ * residual = h) bit for bit: the normalisation is folded into the router
+ * kernel (each of its workgroups forms the same fp64 mean square), which also
+ * stores n for the expert kernels, so no separate normalisation kernel runs.
+ * h, h_out: fp32 [H] (may alias); eps >= 0; other arguments and the
+ * workspace as for rvq_moe_decode_routed (n lives in the workspace).
+ * ------------------------------------------------------------------------ */
+int rvq_moe_block_decode(const rvq_expert_bank_t *bank, const void *w_router_bf16, const float *h, int32_t k,
+                         float eps, float *h_out, int32_t *ids, float *gates, double *logits, int32_t compute_dtype,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Testing aid for the failure path.  Sets how many times each bounded wait
  * between the wave roles of the table kernels polls before it gives up
  * (which sets RVQ_ERR_DEVICE_STALL and leaves the output invalid, but lets

@@ -5,11 +5,13 @@ only for device memory and streams; every step of the path runs in the
 library's HIP kernels.
 """
 from ._lib import (BF16, F16, F32, ExpertBank, RvqError, check_device_status, expert_gemv, gemv_workspace_bytes,
-                   lib, lut_build, make_moe_workspace, moe_decode_routed, moe_layer_forward, moe_workspace_bytes,
+                   lib, lut_build, make_moe_workspace, moe_block_decode, moe_decode_routed, moe_layer_forward,
+                   moe_workspace_bytes,
                    pack_codes,
                    packed_bytes, rmsnorm, router_topk, status_string, stream_copy, workspace_init)
 
 __all__ = ["BF16", "F16", "F32", "ExpertBank", "RvqError", "check_device_status", "expert_gemv",
-           "gemv_workspace_bytes", "lib", "lut_build", "make_moe_workspace", "moe_decode_routed", "moe_layer_forward",
+           "gemv_workspace_bytes", "lib", "lut_build", "make_moe_workspace", "moe_block_decode", "moe_decode_routed",
+           "moe_layer_forward",
            "moe_workspace_bytes", "pack_codes", "packed_bytes", "rmsnorm", "router_topk", "status_string",
            "stream_copy", "workspace_init"]

@@ -43,7 +43,7 @@ EXPORTS = [
     "rvq_expert_gemv_workspace_bytes", "rvq_expert_gemv", "rvq_router_topk", "rvq_bank_record_bytes",
     "rvq_moe_layer_workspace_bytes", "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed",
     "rvq_workspace_init", "rvq_rmsnorm", "rvq_stream_copy",
-    "rvq_check_device_status", "rvq_moe_decode_routed", "rvq_set_wait_limit",
+    "rvq_check_device_status", "rvq_moe_decode_routed", "rvq_set_wait_limit", "rvq_moe_block_decode",
 ]
 
 
@@ -77,12 +77,14 @@ def lib():
         L.rvq_rmsnorm.argtypes = [p, i32, i32, ctypes.c_float, p, p]
         L.rvq_check_device_status.argtypes = [p, p]
         L.rvq_stream_copy.argtypes = [p, p, sz, p]
+        L.rvq_moe_block_decode.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, ctypes.c_float, p, p, p, p, i32, p,
+                                           sz, p]
         L.rvq_set_wait_limit.argtypes = [i32]
         L.rvq_set_wait_limit.restype = i32
         L.rvq_moe_decode_routed.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, p, p, p, p, p, i32, p, sz, p]
         for name in ("rvq_pack_codes", "rvq_lut_build", "rvq_expert_gemv", "rvq_router_topk",
                      "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed", "rvq_workspace_init", "rvq_rmsnorm",
-                     "rvq_check_device_status", "rvq_stream_copy", "rvq_moe_decode_routed"):
+                     "rvq_check_device_status", "rvq_stream_copy", "rvq_moe_decode_routed", "rvq_moe_block_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -354,3 +356,27 @@ def moe_decode_routed(bank, w_router, x, k, residual=None, dtype="f32", y=None, 
                                        _ptr(ids), _ptr(gates), _ptr(logits), d, _ptr(workspace), workspace.numel(),
                                        _stream(x)))
     return y, ids, gates, logits
+
+
+def moe_block_decode(bank, w_router, h, k, eps=1e-6, dtype="f32", h_out=None, ids=None, gates=None, logits=None,
+                     workspace=None):
+    """One pre-norm residual MoE block: h_out = h + MoE(RMSNorm(h)), routed by w_router (bf16 [E, H]).
+    Returns (h_out, ids, gates, logits)."""
+    _dev(w_router, torch.bfloat16, "w_router")
+    _dev(h, torch.float32, "h")
+    E, H = w_router.shape
+    if E != bank.E or H != bank.H:
+        raise ValueError("router shape does not match the bank")
+    dev = h.device
+    d = _table_dtype(dtype)
+    h_out = torch.empty(H, dtype=torch.float32, device=dev) if h_out is None else h_out
+    ids = torch.empty(k, dtype=torch.int32, device=dev) if ids is None else ids
+    gates = torch.empty(k, dtype=torch.float32, device=dev) if gates is None else gates
+    logits = torch.empty(E, dtype=torch.float64, device=dev) if logits is None else logits
+    if workspace is None:
+        workspace = make_moe_workspace(bank, 1, k, d)
+    desc = bank.desc()
+    _check(lib().rvq_moe_block_decode(ctypes.byref(desc), _ptr(w_router), _ptr(h), k, float(eps), _ptr(h_out),
+                                      _ptr(ids), _ptr(gates), _ptr(logits), d, _ptr(workspace), workspace.numel(),
+                                      _stream(h)))
+    return h_out, ids, gates, logits

@@ -205,6 +205,31 @@ int rvq_moe_decode_routed(const rvq_expert_bank_t* bank, const void* w_router_bf
                                       stream, nullptr, &route));
 }
 
+int rvq_moe_block_decode(const rvq_expert_bank_t* bank, const void* w_router_bf16, const float* h, int32_t k,
+                         float eps, float* h_out, int32_t* ids, float* gates, double* logits, int32_t compute_dtype,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_bank(bank);
+  if (st != RVQ_OK) return st;
+  if (!w_router_bf16 || !h || !h_out || !ids || !gates || !logits || !workspace) return RVQ_ERR_NULL;
+  if (k < 1 || k > kMaxTopK || k > bank->num_experts || bank->num_experts > kMaxExperts || !(eps >= 0.f))
+    return RVQ_ERR_SHAPE;
+  if (!table_dtype(compute_dtype)) return RVQ_ERR_DTYPE;
+  if (!aligned(workspace, 256) || !aligned(w_router_bf16, 2) || !aligned(h, 4) || !aligned(h_out, 4) ||
+      !aligned(ids, 4) || !aligned(gates, 4) || !aligned(logits, 8))
+    return RVQ_ERR_ALIGN;
+  const bool f16 = compute_dtype == RVQ_F16;
+  const MoeWorkspace w = moe_workspace_layout(bank->hidden, bank->inter, k, f16);
+  if (workspace_bytes < w.total) return RVQ_ERR_WORKSPACE;
+  float* n = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + w.norm_off);
+  const hipError_t err = launch_router_norm_logits(static_cast<const uint16_t*>(w_router_bf16), h, bank->num_experts,
+                                                   bank->hidden, eps, logits, n, stream);
+  if (err != hipSuccess) return RVQ_ERR_HIP;
+  const Route route{logits, ids, gates};
+  return hip_status(launch_moe_decode(bank->codes, bank->codebooks, bank->record_stride, bank->num_experts,
+                                      bank->hidden, bank->inter, n, nullptr, nullptr, k, h, h_out, f16, workspace,
+                                      stream, nullptr, &route));
+}
+
 int32_t rvq_set_wait_limit(int32_t polls) { return set_wait_limit(polls); }
 
 int rvq_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {

@@ -417,6 +417,64 @@ __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ logits
   if (threadIdx.x < 64) topk_gates(L, sel, k, ids + (int64_t)t * k, gates + (int64_t)t * k, [](int) { return true; });
 }
 
+// Pre-norm router for one token: every workgroup forms inv = 1/sqrt(mean(h^2) + eps) exactly as
+// k_rmsnorm does (same per-thread strides and reduction order, fp64), then the logit of its expert
+// on n = (float)(h * inv), again exactly as k_router_logits reads an fp32 n; workgroup e also writes
+// its slice [e*ceil(H/E), ...) of n for the expert kernels.
+__global__ __launch_bounds__(256) void k_router_norm_logits(const uint16_t* __restrict__ w, const float* __restrict__ h,
+                                                            int E, int H, float eps, double* __restrict__ logits,
+                                                            float* __restrict__ n, int vec) {
+  __shared__ double red[4];
+  __shared__ double red2[4];
+  const int e = blockIdx.x;
+  double ss = 0.0;
+  for (int j = threadIdx.x; j < H; j += 256) ss = fma((double)h[j], (double)h[j], ss);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const double tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const double inv = 1.0 / sqrt(tot / (double)H + (double)eps);
+  const uint16_t* wr = w + (int64_t)e * H;
+  double a0 = 0.0, a1 = 0.0;
+  int h0 = 0;
+  if (vec) {
+    const int n8 = H / 8;
+    for (int q = threadIdx.x; q < n8; q += 256) {
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(wr + q * 8);
+      const f32x4 xa = *reinterpret_cast<const f32x4*>(h + q * 8);
+      const f32x4 xb = *reinterpret_cast<const f32x4*>(h + q * 8 + 4);
+      const float hv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+      double xv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xv[j] = (double)(float)((double)hv[j] * inv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a0 = fma(bf16_to_f64((uint16_t)(wv[j] & 0xffffu)), xv[2 * j], a0);
+        a1 = fma(bf16_to_f64((uint16_t)(wv[j] >> 16)), xv[2 * j + 1], a1);
+      }
+    }
+    h0 = n8 * 8;
+  }
+  for (int j = h0 + threadIdx.x; j < H; j += 256) a0 = fma(bf16_to_f64(wr[j]), (double)(float)((double)h[j] * inv), a0);
+  double acc = a0 + a1;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if ((threadIdx.x & 63) == 0) red2[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) logits[e] = (red2[0] + red2[1]) + (red2[2] + red2[3]);
+  const int per = (H + E - 1) / E;
+  for (int j = e * per + (int)threadIdx.x; j < (e + 1) * per && j < H; j += 256) n[j] = (float)((double)h[j] * inv);
+}
+
+hipError_t launch_router_norm_logits(const uint16_t* w, const float* h, int E, int H, float eps, double* logits,
+                                     float* n, hipStream_t stream) {
+  const int vec = (H % 8 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0) &&
+                  ((reinterpret_cast<uintptr_t>(h) & 15) == 0);
+  hipLaunchKernelGGL(k_router_norm_logits, dim3((unsigned)E), dim3(256), 0, stream, w, h, E, H, eps, logits, n, vec);
+  return hipGetLastError();
+}
+
 hipError_t launch_router_logits(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, double* logits,
                                 hipStream_t stream) {
   const int vec = (H % 8 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0) &&
@@ -1006,7 +1064,8 @@ MoeWorkspace moe_workspace_layout(int H, int I, int k, bool f16) {
   const size_t gu = (size_t)k * 2 * cdiv(H / 8, kSlabGroups) * pad_rows(I) * sizeof(float);
   w.part_d_off = w.part_gu_off + ((gu + 255) / 256) * 256;
   const size_t d = (size_t)k * cdiv(I / 8, kSlabGroups) * pad_rows(H) * sizeof(float);
-  w.total = w.part_d_off + ((d + 255) / 256) * 256;
+  w.norm_off = w.part_d_off + ((d + 255) / 256) * 256;
+  w.total = w.norm_off + ((H * sizeof(float) + 255) / 256) * 256;
   return w;
 }
 

@@ -14,6 +14,7 @@ struct MoeWorkspace {
   size_t status_off;              // int32 sticky device status
   size_t part_gu_off;             // fp32 [k][2][nt_in][I]
   size_t part_d_off;              // fp32 [k][nt_out][H]
+  size_t norm_off;                // fp32 [H]: RMSNorm(h) for the pre-norm block
   size_t total;
 };
 
@@ -33,6 +34,8 @@ hipError_t launch_router_topk(const uint16_t* w, const void* x, bool x_bf16, int
 hipError_t launch_rmsnorm(const float* x, int T, int H, float eps, float* out, hipStream_t stream);
 // Polls per bounded wait inside the wave-specialised kernels; returns the previous value (< 0: default).
 int set_wait_limit(int polls);
+hipError_t launch_router_norm_logits(const uint16_t* w, const float* h, int E, int H, float eps, double* logits,
+                                     float* n, hipStream_t stream);
 hipError_t launch_router_logits(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, double* logits,
                                 hipStream_t stream);
 // Routing inputs of a decode step: the router logits (fp64 [E]) and where the top-k ids/gates go.

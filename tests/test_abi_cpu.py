@@ -125,7 +125,7 @@ def _bank(E=256, H=7168, I=2048, stride=16_515_072, codes=FAKE, cb=FAKE2):
 
 def test_moe_workspace_size(L):
     n = L.rvq_moe_layer_workspace_bytes(_bank(), 1, 16, 0)
-    assert n == 256 + 16 * 2 * 56 * 2048 * 4 + 16 * 16 * 7168 * 4
+    assert n == 256 + 16 * 2 * 56 * 2048 * 4 + 16 * 16 * 7168 * 4 + 7168 * 4   # + RMSNorm(h) of the block
     # partials are sized for 16-group K-tiles whatever the table precision
     assert L.rvq_moe_layer_workspace_bytes(_bank(), 1, 16, 1) == n
     assert L.rvq_moe_layer_workspace_bytes(_bank(), 1, 16, 2) == 0
@@ -172,6 +172,25 @@ def test_routed_decode_validation(L):
     assert call(a8=2) == DTYPE                            # bf16 tables: no
     assert call(a7=FAKE + 4) == ALIGN                     # logits are fp64
     assert call(a9=FAKE + 64) == ALIGN                    # workspace
+    assert call(a10=n - 1) == WS
+
+
+def test_block_decode_validation(L):
+    s = None
+    n = L.rvq_moe_layer_workspace_bytes(_bank(), 1, 16, 0)
+    f = L.rvq_moe_block_decode
+    ok = [FAKE, FAKE, 16, 1e-6, FAKE, FAKE, FAKE, FAKE, 0, FAKE, n, s]
+
+    def call(bank=None, **kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(bank if bank is not None else _bank(), *a)
+    assert f(None, *ok) == NULL
+    assert call(a1=None) == NULL and call(a4=None) == NULL
+    assert call(a3=-1.0) == SHAPE and call(a2=0) == SHAPE
+    assert call(a8=2) == DTYPE
+    assert call(a7=FAKE + 4) == ALIGN
     assert call(a10=n - 1) == WS
 
 

@@ -320,6 +320,42 @@ def test_routed_decode_matches_two_calls_and_oracle(layer_bank, dtype):
     assert rvq.check_device_status(ws) == 0
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_block_decode_matches_norm_then_routed_and_oracle(layer_bank, dtype):
+    """rvq_moe_block_decode (RMSNorm folded into the router kernel) equals rvq_rmsnorm followed by
+    rvq_moe_decode_routed(x = n, residual = h) bit for bit, also in place (h_out aliasing h), and the
+    oracle's pre-norm block within tolerance."""
+    bank, bits, w = layer_bank
+    ws = rvq.make_moe_workspace(bank, 1, TOP_K, dtype)
+    cache = {}
+    def get(e):
+        if e not in cache:
+            cache[e] = oracle_expert(synth.SEED_LAYER, 0, e)
+        return cache[e]
+    for t, scale in ((4, 3.5), (5, 0.02)):
+        say(f"block decode token {t} {dtype}")
+        h = synth.activation_f32(synth.SEED_LAYER, 2000 + t, HIDDEN) * np.float32(scale)
+        hd = to_dev(h)
+        y, ids, gates, logits = rvq.moe_block_decode(bank, w, hd, TOP_K, 1e-6, dtype=dtype, workspace=ws)
+        n = rvq.rmsnorm(hd[None, :], 1e-6)[0]
+        y2, ids2, gates2, logits2 = rvq.moe_decode_routed(bank, w, n, TOP_K, residual=hd, dtype=dtype, workspace=ws)
+        assert torch.equal(logits, logits2) and torch.equal(ids, ids2) and torch.equal(gates, gates2)
+        assert torch.equal(y, y2)
+        hin = hd.clone()
+        y3, ids3, _, _ = rvq.moe_block_decode(bank, w, hin, TOP_K, 1e-6, dtype=dtype, h_out=hin, workspace=ws)
+        assert torch.equal(hin, y) and torch.equal(ids3, ids)
+        n_ref = oracle.rmsnorm(h.astype(np.float64), 1e-6)
+        y_ref, ids_ref, gates_ref, gaps = oracle.moe_layer(get, bits, n_ref, TOP_K, residual=h)
+        # the kernels route on n rounded to fp32, which moves a logit by at most 2^-24 sum |w n|; the
+        # kept experts and their order are then unique while every gap exceeds twice that
+        wf = (np.asarray(bits, dtype=np.uint32).reshape(-1, HIDDEN) << 16).view(np.float32).astype(np.float64)
+        assert min(gaps) > 2.0 * 2.0 ** -24 * float((np.abs(wf) @ np.abs(n_ref)).max())
+        assert np.array_equal(ids.cpu().numpy(), ids_ref)
+        np.testing.assert_allclose(gates.cpu().numpy(), gates_ref, rtol=1e-5)
+        assert rel_l2(y.cpu().numpy() - h, y_ref - h) <= TOL[dtype]
+    assert rvq.check_device_status(ws) == 0
+
+
 def test_routed_decode_small_expert_count():
     """Top-k inside the gate/up kernel with fewer experts than wave lanes, k = 1 and k = E."""
     E, k_all = 5, 5

@@ -9,7 +9,8 @@ WASTE pages describe for their own engine):
     oracle -> GPU only): RMSNorm of the oracle's h_l (rel-L2 <= 1e-6), the router on the oracle's
     n_l (ids bit-exact: both sides accumulate logits in fp64; gates 1e-6), and the MoE output on
     the oracle's n_l, ids and gates (rel-L2 <= 1e-5 with fp32 tables, 2e-3 with fp16 tables).
-  * end-to-end: the GPU runs all 92 layers on its own.  Its ids must equal the oracle's at every
+  * end-to-end: the GPU runs all 92 layers on its own (norm, router, layer as three calls; the
+    fused block call must give the same final h bit for bit).  Its ids must equal the oracle's at every
     layer except where the oracle's own top-k boundary is a near-tie (gap < TAU); after such a
     divergence the step is not compared further.  92 routed layers amplify rounding-level
     differences about 400x (measured below: the oracle's own final h under a one-ulp change of x),
@@ -76,6 +77,15 @@ def gpu_free_step(stack, x, dtype, ws):
     return h.cpu().numpy(), [i.cpu().numpy() for i in ids_all]
 
 
+def gpu_block_step(stack, x, dtype, ws):
+    """The same free run through rvq_moe_block_decode (one call per layer, updated in place)."""
+    h = dev32(x)
+    for l in range(stack.L):
+        rvq.moe_block_decode(stack.banks[l], stack.routers[l], h, TOP_K, RMS_EPS, dtype=dtype, h_out=h,
+                             workspace=ws)
+    return h.cpu().numpy()
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_stack_decode_steps(stack, dtype):
     ws = rvq.make_moe_workspace(stack.banks[0], 1, TOP_K, dtype)
@@ -105,6 +115,7 @@ def test_stack_decode_steps(stack, dtype):
         say(f"  layer-wise MoE output: worst rel-L2 over 92 layers {worst:.3e}")
         say(f"stack step {t} {dtype}: end-to-end GPU")
         h_free, ids_gpu = gpu_free_step(stack, x, dtype, ws)
+        assert np.array_equal(gpu_block_step(stack, x, dtype, ws), h_free)
         diverged = False
         for l in range(stack.L):
             ids_o, gap = trace[l][2], trace[l][4]
