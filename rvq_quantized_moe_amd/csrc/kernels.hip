@@ -286,22 +286,81 @@ __device__ inline double bf16_to_f64(uint16_t b) { return (double)__uint_as_floa
 __device__ inline double x_to_f64(float v) { return (double)v; }
 __device__ inline double x_to_f64(uint16_t v) { return bf16_to_f64(v); }
 
+// Eight x values as loaded (16 or 32 bytes), widened to fp64 only when used, so that a thread can
+// have all of its loads in flight before the first product.
 template <typename XT>
-__device__ __forceinline__ void load8(const XT* p, double (&xv)[8]);
+struct RawX8;
 template <>
-__device__ __forceinline__ void load8<float>(const float* p, double (&xv)[8]) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-  xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w; xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
-}
-template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, double (&xv)[8]) {
-  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    xv[2 * j] = bf16_to_f64((uint16_t)(a[j] & 0xffffu));
-    xv[2 * j + 1] = bf16_to_f64((uint16_t)(a[j] >> 16));
+struct RawX8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
   }
+  __device__ __forceinline__ double get(int j) const { return (double)(j < 4 ? a[j] : b[j - 4]); }
+};
+template <>
+struct RawX8<uint16_t> {
+  u32x4 a;
+  __device__ __forceinline__ void load(const uint16_t* p) { a = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ double get(int j) const {
+    return bf16_to_f64((uint16_t)((j & 1) ? (a[j >> 1] >> 16) : (a[j >> 1] & 0xffffu)));
+  }
+};
+
+constexpr int kRouterUnroll = 4;   // 8-element pieces per thread with loads in flight together
+
+// This thread's part of sum_h w[h] * xf(x[h]) for one router row: pieces q = tid, tid + 256, ...
+// in increasing q, even elements into a0 and odd into a1 (fp64 fma), then a scalar tail into a0.
+// Loads use clamped (always valid) indices and are all issued before the products, which are
+// predicated on the real index; the order of the products is that of the plain loop.
+template <typename XT, typename XF>
+__device__ __forceinline__ double router_dot(const uint16_t* __restrict__ wr, const XT* __restrict__ xr, int H, int vec,
+                                             XF xf) {
+  double a0 = 0.0, a1 = 0.0;
+  int h0 = 0;
+  if (vec) {
+    const int n8 = H / 8;
+    for (int q0 = threadIdx.x; q0 < n8; q0 += 256 * kRouterUnroll) {
+      u32x4 wv[kRouterUnroll];
+      RawX8<XT> xv[kRouterUnroll];
+#pragma unroll
+      for (int u = 0; u < kRouterUnroll; ++u) {
+        const int q = min(q0 + 256 * u, n8 - 1);
+        wv[u] = *reinterpret_cast<const u32x4*>(wr + q * 8);
+        xv[u].load(xr + q * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < kRouterUnroll; ++u) {
+        if (q0 + 256 * u < n8) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            a0 = fma(bf16_to_f64((uint16_t)(wv[u][j] & 0xffffu)), xf(xv[u].get(2 * j)), a0);
+            a1 = fma(bf16_to_f64((uint16_t)(wv[u][j] >> 16)), xf(xv[u].get(2 * j + 1)), a1);
+          }
+        }
+      }
+    }
+    h0 = n8 * 8;
+  }
+  for (int h = h0 + threadIdx.x; h < H; h += 256) a0 = fma(bf16_to_f64(wr[h]), xf(x_to_f64(xr[h])), a0);
+  return a0 + a1;
+}
+
+// This thread's part of sum_h x[h]^2 in fp64: h = tid, tid + 256, ... in increasing order (fma),
+// 16 loads in flight at a time.
+__device__ __forceinline__ double sum_squares(const float* __restrict__ x, int H) {
+  constexpr int U = 16;
+  double ss = 0.0;
+  for (int h0 = threadIdx.x; h0 < H; h0 += 256 * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = x[min(h0 + 256 * u, H - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (h0 + 256 * u < H) ss = fma((double)v[u], (double)v[u], ss);
+  }
+  return ss;
 }
 
 // One workgroup per (expert, token): 256 threads stride over H in 8-element (16/32-byte) pieces
@@ -313,24 +372,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   const int e = blockIdx.x, t = blockIdx.y;
   const uint16_t* wr = w + (int64_t)e * H;
   const XT* xr = x + (int64_t)t * H;
-  double a0 = 0.0, a1 = 0.0;
-  int h0 = 0;
-  if (vec) {
-    const int n8 = H / 8;
-    for (int q = threadIdx.x; q < n8; q += 256) {
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(wr + q * 8);
-      double xv[8];
-      load8<XT>(xr + q * 8, xv);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        a0 = fma(bf16_to_f64((uint16_t)(wv[j] & 0xffffu)), xv[2 * j], a0);
-        a1 = fma(bf16_to_f64((uint16_t)(wv[j] >> 16)), xv[2 * j + 1], a1);
-      }
-    }
-    h0 = n8 * 8;
-  }
-  for (int h = h0 + threadIdx.x; h < H; h += 256) a0 = fma(bf16_to_f64(wr[h]), x_to_f64(xr[h]), a0);
-  double acc = a0 + a1;
+  double acc = router_dot(wr, xr, H, vec, [](double v) { return v; });
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
@@ -427,8 +469,7 @@ __global__ __launch_bounds__(256) void k_router_norm_logits(const uint16_t* __re
   __shared__ double red[4];
   __shared__ double red2[4];
   const int e = blockIdx.x;
-  double ss = 0.0;
-  for (int j = threadIdx.x; j < H; j += 256) ss = fma((double)h[j], (double)h[j], ss);
+  double ss = sum_squares(h, H);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -436,28 +477,7 @@ __global__ __launch_bounds__(256) void k_router_norm_logits(const uint16_t* __re
   const double tot = (red[0] + red[1]) + (red[2] + red[3]);
   const double inv = 1.0 / sqrt(tot / (double)H + (double)eps);
   const uint16_t* wr = w + (int64_t)e * H;
-  double a0 = 0.0, a1 = 0.0;
-  int h0 = 0;
-  if (vec) {
-    const int n8 = H / 8;
-    for (int q = threadIdx.x; q < n8; q += 256) {
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(wr + q * 8);
-      const f32x4 xa = *reinterpret_cast<const f32x4*>(h + q * 8);
-      const f32x4 xb = *reinterpret_cast<const f32x4*>(h + q * 8 + 4);
-      const float hv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-      double xv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xv[j] = (double)(float)((double)hv[j] * inv);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        a0 = fma(bf16_to_f64((uint16_t)(wv[j] & 0xffffu)), xv[2 * j], a0);
-        a1 = fma(bf16_to_f64((uint16_t)(wv[j] >> 16)), xv[2 * j + 1], a1);
-      }
-    }
-    h0 = n8 * 8;
-  }
-  for (int j = h0 + threadIdx.x; j < H; j += 256) a0 = fma(bf16_to_f64(wr[j]), (double)(float)((double)h[j] * inv), a0);
-  double acc = a0 + a1;
+  double acc = router_dot(wr, h, H, vec, [inv](double v) { return (double)(float)(v * inv); });
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if ((threadIdx.x & 63) == 0) red2[threadIdx.x >> 6] = acc;
@@ -503,8 +523,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* x, int H, float ep
   __shared__ double red[4];
   const int64_t t = blockIdx.x;
   const float* xr = x + t * H;
-  double ss = 0.0;
-  for (int h = threadIdx.x; h < H; h += 256) ss = fma((double)xr[h], (double)xr[h], ss);
+  double ss = sum_squares(xr, H);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -1021,11 +1040,14 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_moe_combine(const float*
   __shared__ float red[kCombineWaves][64];
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int r = blockIdx.x * 64 + lane;
+  // every load is issued before the first use: the residual, and per slot the id, the gate and the
+  // partial sums (their addresses do not depend on the id; an invalid id only drops the sum)
+  const float res = (q == 0 && r < H && residual) ? residual[r] : 0.f;
   float acc = 0.f;
   if (r < H) {
     for (int slot = q; slot < k; slot += kCombineWaves) {
       const int e = ids[slot];
-      if (e < 0 || e >= E) continue;
+      const float g = gates[slot];
       const float* pd = part_d + (int64_t)slot * nt * Hp + r;
       float s = 0.f;
       for (int t = 0; t < nt; t += 8) {
@@ -1035,13 +1057,13 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_moe_combine(const float*
 #pragma unroll
         for (int u = 0; u < 8; ++u) s += v[u];
       }
-      acc = fmaf(gates[slot], s, acc);
+      if (e >= 0 && e < E) acc = fmaf(g, s, acc);
     }
   }
   red[q][lane] = acc;
   __syncthreads();
   if (q == 0 && r < H) {
-    float o = residual ? residual[r] : 0.f;
+    float o = res;
 #pragma unroll
     for (int w = 0; w < kCombineWaves; ++w) o += red[w][lane];
     y[r] = o;
