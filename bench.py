@@ -259,6 +259,51 @@ def run_chunk(rvq, hip, bank, w, xt, steps, dtype):
             "mfma_TFLOPs": flops / (moe_ms * 1e-3) / 1e12, "tile_dtype": dtype}
 
 
+def run_small_batch(torch, rvq, bank, w, xt, sizes=(1, 2, 4, 8, 16, 32, 64), reps=10):
+    """Small-batch decode: the first T tokens of the bf16 chunk through the table path
+    (rvq_moe_batch_decode, every token streaming its own experts' codes) and through the chunk path
+    (rvq_moe_layer_forward, T > 1: every touched expert decoded once); tokens/s of the MoE part
+    (routing computed beforehand), eager calls timed between synchronisations."""
+    dev = xt.device
+    res = {"T": list(sizes), "lut_f32_tokens_per_s": [], "lut_f16_tokens_per_s": [], "chunk_f16_tokens_per_s": [],
+           "distinct_experts": []}
+
+    def rate(fn, T):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return T * reps / (time.perf_counter() - t0)
+
+    for T in sizes:
+        xb = xt[:T].contiguous()
+        x32 = xb.float()
+        ids, gates, _ = rvq.router_topk(w, xb, K)
+        res["distinct_experts"].append(int(torch.unique(ids).numel()))
+        y = torch.empty(T, H, dtype=torch.float32, device=dev)
+        for d in ("f32", "f16"):
+            ws = rvq.make_batch_workspace(bank, T, K, d)
+            res[f"lut_{d}_tokens_per_s"].append(
+                rate(lambda: rvq.moe_batch_decode(bank, x32, ids, gates, dtype=d, y=y, workspace=ws), T))
+            status = rvq.check_device_status(ws)
+            if status:
+                raise RuntimeError(rvq.status_string(status))
+            del ws
+        if T > 1:
+            ws = rvq.make_moe_workspace(bank, T, K, "f16")
+            res["chunk_f16_tokens_per_s"].append(
+                rate(lambda: rvq.moe_layer_forward(bank, xb, ids, gates, dtype="f16", y=y, workspace=ws), T))
+            del ws
+        else:
+            res["chunk_f16_tokens_per_s"].append(None)
+    best_lut = [max(a, b) for a, b in zip(res["lut_f32_tokens_per_s"], res["lut_f16_tokens_per_s"])]
+    cross = [T for T, c, l in zip(sizes, res["chunk_f16_tokens_per_s"], best_lut) if c is not None and c > l]
+    res["chunk_faster_from_T"] = cross[0] if cross else None
+    return res
+
+
 def replay_rate(torch, graphs, steps, warmup, before=None):
     """Replays graphs round-robin (before(i) runs eagerly ahead of replay i); returns seconds per step."""
     for i in range(warmup):
@@ -462,6 +507,8 @@ def main():
         xb = np.stack([synth.activation_bf16_bits(synth.SEED_CHUNK, t, H) for t in range(512)])
         xt = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
         chunk = {d: run_chunk(rvq, hip, bank, w, xt, 20, d) for d in ("f16", "bf16")}
+        print("[bench] small-batch decode: table path vs chunk path", file=sys.stderr, flush=True)
+        chunk["small_batch_decode"] = run_small_batch(torch, rvq, bank, w, xt)
     extra = None
     if not args.no_extra:
         print("[bench] one matvec, one expert", file=sys.stderr, flush=True)

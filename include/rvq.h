@@ -220,6 +220,31 @@ int rvq_moe_block_decode(const rvq_expert_bank_t *bank, const void *w_router_bf1
                          float eps, float *h_out, int32_t *ids, float *gates, double *logits, int32_t compute_dtype,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * A small batch of T decode tokens through the table (LUT) path: for every
+ * token t, y[t] = [residual[t] +] sum_i gates[t][i] * expert_{ids[t][i]}(x[t]),
+ * each token with its own partial-dot tables, as in rvq_moe_layer_forward
+ * with T = 1.  The pages' engine decodes one token at a time ("Running a
+ * 2.78-Trillion-Parameter Model on a Laptop", section "Gotcha": no batching)
+ * and reports chunked prefill faster than sequential (news.hada.io topic
+ * 32035, prefill figures); this entry point is the per-token side of that
+ * comparison: its cost grows with T (every token streams its experts' codes),
+ * while the chunk path (rvq_moe_layer_forward, T > 1) decodes each touched
+ * expert once for all its tokens.  The benchmark reports the crossover.
+ * All T tokens run in the same three launches (pair t*k + i is one work item
+ * of the gate/up and down kernels, chunked exactly as for one token), so each
+ * y[t] equals a single-token rvq_moe_layer_forward call bit for bit; shapes
+ * without the wave-specialised kernels run the tokens one after another.
+ * x, residual, y: fp32 [T][H] (y may alias residual); ids: int32 [T][k];
+ * gates: fp32 [T][k]; 1 <= T <= 256; 1 <= k <= 64; table_dtype RVQ_F32 or
+ * RVQ_F16; workspace 256-byte aligned, >= the query below, zero-filled once
+ * by rvq_workspace_init.  Errors as rvq_moe_layer_forward.
+ * ------------------------------------------------------------------------ */
+size_t rvq_moe_batch_decode_workspace_bytes(const rvq_expert_bank_t *bank, int32_t T, int32_t k, int32_t table_dtype);
+int rvq_moe_batch_decode(const rvq_expert_bank_t *bank, const float *x, int32_t T, const int32_t *ids,
+                         const float *gates, int32_t k, const float *residual, float *y, int32_t table_dtype,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Testing aid for the failure path.  Sets how many times each bounded wait
  * between the wave roles of the table kernels polls before it gives up
  * (which sets RVQ_ERR_DEVICE_STALL and leaves the output invalid, but lets

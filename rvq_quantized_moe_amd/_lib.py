@@ -44,6 +44,7 @@ EXPORTS = [
     "rvq_moe_layer_workspace_bytes", "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed",
     "rvq_workspace_init", "rvq_rmsnorm", "rvq_stream_copy",
     "rvq_check_device_status", "rvq_moe_decode_routed", "rvq_set_wait_limit", "rvq_moe_block_decode",
+    "rvq_moe_batch_decode", "rvq_moe_batch_decode_workspace_bytes",
 ]
 
 
@@ -80,11 +81,15 @@ def lib():
         L.rvq_moe_block_decode.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, ctypes.c_float, p, p, p, p, i32, p,
                                            sz, p]
         L.rvq_set_wait_limit.argtypes = [i32]
+        L.rvq_moe_batch_decode.argtypes = [ctypes.POINTER(BankDesc), p, i32, p, p, i32, p, p, i32, p, sz, p]
+        L.rvq_moe_batch_decode_workspace_bytes.argtypes = [ctypes.POINTER(BankDesc), i32, i32, i32]
+        L.rvq_moe_batch_decode_workspace_bytes.restype = sz
         L.rvq_set_wait_limit.restype = i32
         L.rvq_moe_decode_routed.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, p, p, p, p, p, i32, p, sz, p]
         for name in ("rvq_pack_codes", "rvq_lut_build", "rvq_expert_gemv", "rvq_router_topk",
                      "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed", "rvq_workspace_init", "rvq_rmsnorm",
-                     "rvq_check_device_status", "rvq_stream_copy", "rvq_moe_decode_routed", "rvq_moe_block_decode"):
+                     "rvq_check_device_status", "rvq_stream_copy", "rvq_moe_decode_routed", "rvq_moe_block_decode",
+                     "rvq_moe_batch_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -380,3 +385,37 @@ def moe_block_decode(bank, w_router, h, k, eps=1e-6, dtype="f32", h_out=None, id
                                       _ptr(ids), _ptr(gates), _ptr(logits), d, _ptr(workspace), workspace.numel(),
                                       _stream(h)))
     return h_out, ids, gates, logits
+
+
+def make_batch_workspace(bank, T, k=16, dtype="f32"):
+    """Zero-filled workspace for moe_batch_decode with T tokens."""
+    desc = bank.desc()
+    n = lib().rvq_moe_batch_decode_workspace_bytes(ctypes.byref(desc), T, k, _table_dtype(dtype))
+    if n == 0:
+        raise ValueError("unsupported batch decode configuration")
+    ws = torch.empty(n, dtype=torch.uint8, device=bank.codes.device)
+    workspace_init(ws)
+    return ws
+
+
+def moe_batch_decode(bank, x, ids, gates, residual=None, dtype="f32", y=None, workspace=None):
+    """T decode tokens through the table path: x fp32 [T, H], ids int32 [T, k], gates fp32 [T, k];
+    returns y fp32 [T, H] (y[t] as a single-token moe_layer_forward)."""
+    _dev(x, torch.float32, "x")
+    _dev(ids, torch.int32, "ids")
+    _dev(gates, torch.float32, "gates")
+    T, H = x.shape
+    k = ids.shape[1]
+    if H != bank.H or tuple(ids.shape) != (T, k) or tuple(gates.shape) != (T, k):
+        raise ValueError("shape mismatch")
+    if residual is not None:
+        _dev(residual, torch.float32, "residual")
+    d = _table_dtype(dtype)
+    y = torch.empty(T, H, dtype=torch.float32, device=x.device) if y is None else y
+    if workspace is None:
+        workspace = make_batch_workspace(bank, T, k, dtype)
+    desc = bank.desc()
+    _check(lib().rvq_moe_batch_decode(ctypes.byref(desc), _ptr(x), T, _ptr(ids), _ptr(gates), k,
+                                      _ptr(residual) if residual is not None else None, _ptr(y), d, _ptr(workspace),
+                                      workspace.numel(), _stream(x)))
+    return y

@@ -183,6 +183,32 @@ int rvq_moe_layer_forward_timed(const rvq_expert_bank_t* bank, const void* x, in
                                 workspace_bytes, stream, events);
 }
 
+size_t rvq_moe_batch_decode_workspace_bytes(const rvq_expert_bank_t* bank, int32_t T, int32_t k,
+                                            int32_t table_dtype_) {
+  if (!bank || T < 1 || T > kMaxBatchDecode || k < 1 || k > kMaxTopK) return 0;
+  if (!valid_matrix_shape(bank->inter, bank->hidden) || bank->inter % 8 != 0) return 0;
+  if (!table_dtype(table_dtype_)) return 0;
+  return moe_workspace_layout(bank->hidden, bank->inter, T * k, table_dtype_ == RVQ_F16).total;
+}
+
+int rvq_moe_batch_decode(const rvq_expert_bank_t* bank, const float* x, int32_t T, const int32_t* ids,
+                         const float* gates, int32_t k, const float* residual, float* y, int32_t table_dtype_,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_bank(bank);
+  if (st != RVQ_OK) return st;
+  if (!x || !ids || !gates || !y || !workspace) return RVQ_ERR_NULL;
+  if (T < 1 || T > kMaxBatchDecode || k < 1 || k > kMaxTopK) return RVQ_ERR_SHAPE;
+  if (!table_dtype(table_dtype_)) return RVQ_ERR_DTYPE;
+  if (!aligned(workspace, 256) || !aligned(x, 4) || !aligned(y, 4) || !aligned(ids, 4) || !aligned(gates, 4) ||
+      (residual && !aligned(residual, 4)))
+    return RVQ_ERR_ALIGN;
+  const bool f16 = table_dtype_ == RVQ_F16;
+  if (workspace_bytes < moe_workspace_layout(bank->hidden, bank->inter, T * k, f16).total) return RVQ_ERR_WORKSPACE;
+  return hip_status(launch_moe_batch_decode(bank->codes, bank->codebooks, bank->record_stride, bank->num_experts,
+                                            bank->hidden, bank->inter, x, T, ids, gates, k, residual, y, f16,
+                                            workspace, stream));
+}
+
 int rvq_moe_decode_routed(const rvq_expert_bank_t* bank, const void* w_router_bf16, const float* x, int32_t k,
                           const float* residual, float* y, int32_t* ids, float* gates, double* logits,
                           int32_t compute_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {

@@ -784,9 +784,10 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
 #pragma unroll
     for (int t = 0; t < TPW; ++t) a[t] = *reinterpret_cast<const f32x2*>(cb + ((bw * TPW + t) * 16 + i16) * 8 + 2 * q);
     if constexpr (!DOWN) {
+      const float* xt = pa.x + (int64_t)(slot / pa.k) * H;   // slot = token * k + i when batched
 #pragma unroll
       for (int k = 0; k < ITEMS; ++k)
-        xb[k] = *reinterpret_cast<const f32x2*>(pa.x + (int64_t)(t0 + k) * 128 + i16 * 8 + 2 * q);
+        xb[k] = *reinterpret_cast<const f32x2*>(xt + (int64_t)(t0 + k) * 128 + i16 * 8 + 2 * q);
     }
   } else if (threadIdx.x == 0) {
     built[0] = 0;
@@ -1038,6 +1039,13 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_moe_combine(const float*
                                                                     const float* residual, float* y) {
   const int64_t Hp = pad_rows(H);
   __shared__ float red[kCombineWaves][64];
+  // batched decode: token blockIdx.y owns slots [k t, k t + k) and rows t of residual and y
+  const int tok = blockIdx.y;
+  part_d += (int64_t)tok * k * nt * Hp;
+  ids += tok * k;
+  gates += tok * k;
+  if (residual) residual += (int64_t)tok * H;
+  y += (int64_t)tok * H;
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int r = blockIdx.x * 64 + lane;
   // every load is issued before the first use: the residual, and per slot the id, the gate and the
@@ -1091,10 +1099,16 @@ MoeWorkspace moe_workspace_layout(int H, int I, int k, bool f16) {
   return w;
 }
 
-hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
-                             const float* x, const int32_t* ids, const float* gates, int k, const float* residual,
-                             float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev, const Route* route) {
-  const MoeWorkspace w = moe_workspace_layout(H, I, k, f16);
+// T tokens of decode (T = 1 for the single-token entry points).  Pair p = t k + i (token t's i-th
+// expert) is one "slot" of the kernels, which read x, residual and y at row p / k; the chunk sizes
+// are chosen from one token's counts, so every pair is computed exactly as in a single-token call.
+// Shapes without both wave-specialised forms run the tokens one after another.
+static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
+                                const float* x, int T, const int32_t* ids, const float* gates, int k,
+                                const float* residual, float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev,
+                                const Route* route) {
+  const int P = T * k;
+  const MoeWorkspace w = moe_workspace_layout(H, I, P, f16);
   uint8_t* base = static_cast<uint8_t*>(ws);
   int32_t* status = reinterpret_cast<int32_t*>(base + w.status_off);
   float* part_gu = reinterpret_cast<float*>(base + w.part_gu_off);
@@ -1135,6 +1149,15 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
                          ? pick_chunk(nt16_out, (long)k * nrc)
                          : 0;
   const int nparts_d = dchunk ? nt16_out / dchunk : w.nt_out;
+  if (T > 1 && !(chunk && dchunk)) {
+    for (int t = 0; t < T; ++t) {
+      const hipError_t e = decode_tokens(codes, cb, stride, E, H, I, x + (int64_t)t * H, 1, ids + t * k, gates + t * k,
+                                         k, residual ? residual + (int64_t)t * H : nullptr, y + (int64_t)t * H, f16, ws,
+                                         stream, nullptr, nullptr);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   // routing: the gate/up kernel takes the top-k itself when it is the wave-specialised one;
   // otherwise k_topk writes ids/gates first
   const bool fused_route = route && chunk && E <= kRouteMaxExperts;
@@ -1147,7 +1170,7 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
   const int bpw_gu = pick_bpw((int)cdiv(I, kSlabRows), 1, kGateUpThreads / 64);
   const int bpw_d = pick_bpw((int)cdiv(H, kSlabRows), nparts, kDownThreads / 64);
   if (chunk) {
-    const dim3 grid((unsigned)(k * 2 * ngu));
+    const dim3 grid((unsigned)(P * 2 * ngu));
     const PipeArgs pa{x,       nullptr, part_gu, ngu, 1, 0, fused_route ? route->logits : nullptr,
                       route ? route->ids : nullptr, route ? route->gates : nullptr, k, g_wait_limit};
     switch (chunk) {
@@ -1174,7 +1197,7 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
   mark(1);
   if (dchunk) {
     const int nkc = nt16_out / dchunk;
-    const dim3 grid((unsigned)(k * nrc * nkc));
+    const dim3 grid((unsigned)(P * nrc * nkc));
     const PipeArgs pa{nullptr, part_gu, part_d, nkc, nrc, ngu, nullptr, nullptr, nullptr, k, g_wait_limit};
     switch (dchunk) {
 #define RVQ_WS_CASE(n)                                                                                             \
@@ -1198,11 +1221,23 @@ hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stri
                                                stream, bank, ids, part_gu, part_d, nparts, ngu))
   }
   mark(2);
-  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)cdiv(H, 64)), dim3(64 * kCombineWaves), 0, stream, part_d, nparts_d,
-                     H, ids, gates, k, E, residual, y);
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)cdiv(H, 64), (unsigned)T), dim3(64 * kCombineWaves), 0, stream,
+                     part_d, nparts_d, H, ids, gates, k, E, residual, y);
   mark(3);
   const hipError_t last = hipGetLastError();
   return err != hipSuccess ? err : last;
+}
+
+hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
+                             const float* x, const int32_t* ids, const float* gates, int k, const float* residual,
+                             float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev, const Route* route) {
+  return decode_tokens(codes, cb, stride, E, H, I, x, 1, ids, gates, k, residual, y, f16, ws, stream, ev, route);
+}
+
+hipError_t launch_moe_batch_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
+                                   const float* x, int T, const int32_t* ids, const float* gates, int k,
+                                   const float* residual, float* y, bool f16, void* ws, hipStream_t stream) {
+  return decode_tokens(codes, cb, stride, E, H, I, x, T, ids, gates, k, residual, y, f16, ws, stream, nullptr, nullptr);
 }
 
 }  // namespace rvq

@@ -34,6 +34,12 @@ hipError_t launch_router_topk(const uint16_t* w, const void* x, bool x_bf16, int
 hipError_t launch_rmsnorm(const float* x, int T, int H, float eps, float* out, hipStream_t stream);
 // Polls per bounded wait inside the wave-specialised kernels; returns the previous value (< 0: default).
 int set_wait_limit(int polls);
+// T tokens of decode through the table path (x, residual, y: [T][H]; ids, gates: [T][k]); the
+// workspace holds moe_workspace_layout(H, I, T * k, f16).
+hipError_t launch_moe_batch_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
+                                   const float* x, int T, const int32_t* ids, const float* gates, int k,
+                                   const float* residual, float* y, bool f16, void* ws, hipStream_t stream);
+constexpr int kMaxBatchDecode = 256;
 hipError_t launch_router_norm_logits(const uint16_t* w, const float* h, int E, int H, float eps, double* logits,
                                      float* n, hipStream_t stream);
 hipError_t launch_router_logits(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, double* logits,

@@ -151,6 +151,35 @@ def test_moe_validation(L):
     assert L.rvq_moe_layer_forward(_bank(), FAKE, 0, 1, None, FAKE, 16, None, FAKE, 0, FAKE, n, s) == NULL
 
 
+def test_batch_decode_workspace_and_validation(L):
+    """rvq_moe_batch_decode: the workspace holds the decode layout for T * k pairs; every check
+    returns before anything is enqueued."""
+    s = None
+    q = L.rvq_moe_batch_decode_workspace_bytes
+    n = q(_bank(), 4, 16, 0)
+    assert n == 256 + 64 * 2 * 56 * 2048 * 4 + 64 * 16 * 7168 * 4 + 7168 * 4
+    assert q(_bank(), 1, 16, 0) == L.rvq_moe_layer_workspace_bytes(_bank(), 1, 16, 0)
+    assert q(_bank(), 4, 16, 1) == n and q(_bank(), 4, 16, 2) == 0
+    assert q(_bank(), 0, 16, 0) == 0 and q(_bank(), 257, 16, 0) == 0 and q(_bank(), 4, 65, 0) == 0
+    assert q(None, 4, 16, 0) == 0
+    f = L.rvq_moe_batch_decode
+    ok = [FAKE, 4, FAKE, FAKE, 16, None, FAKE, 0, FAKE, n, s]
+
+    def call(bank=None, **kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(bank if bank is not None else _bank(), *a)
+    assert f(None, *ok) == NULL
+    assert call(a0=None) == NULL and call(a2=None) == NULL and call(a6=None) == NULL and call(a8=None) == NULL
+    assert call(_bank(E=0)) == SHAPE
+    assert call(a1=0) == SHAPE and call(a1=257) == SHAPE     # T
+    assert call(a4=0) == SHAPE and call(a4=65) == SHAPE      # k
+    assert call(a7=2) == DTYPE                              # bf16 tables: no
+    assert call(a0=FAKE + 2) == ALIGN and call(a8=FAKE + 64) == ALIGN
+    assert call(a9=n - 1) == WS
+
+
 def test_routed_decode_validation(L):
     """Every check of rvq_moe_decode_routed returns before anything is enqueued."""
     s = None

@@ -356,6 +356,64 @@ def test_block_decode_matches_norm_then_routed_and_oracle(layer_bank, dtype):
     assert rvq.check_device_status(ws) == 0
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_batch_decode_equals_single_token_calls(layer_bank, dtype):
+    """rvq_moe_batch_decode runs T tokens' pairs in the same launches, each chunked as for one token:
+    every row equals a single-token rvq_moe_layer_forward bit for bit (those are checked against the
+    oracle above), y may alias the residual, and the workspace is reusable across batch sizes."""
+    bank, bits, w = layer_bank
+    T = 5
+    say(f"batch decode T={T} {dtype}")
+    X = np.stack([synth.activation_f32(synth.SEED_LAYER, 40 + t, HIDDEN) for t in range(T)])
+    R = np.stack([synth.activation_f32(synth.SEED_LAYER, 1040 + t, HIDDEN) for t in range(T)])
+    xd, rd = to_dev(X), to_dev(R)
+    ids, gates, _ = rvq.router_topk(w, xd, TOP_K)
+    ws = rvq.make_batch_workspace(bank, T, TOP_K, dtype)
+    y = rvq.moe_batch_decode(bank, xd, ids, gates, residual=rd, dtype=dtype, workspace=ws)
+    for t in range(T):
+        y1 = rvq.moe_layer_forward(bank, xd[t], ids[t], gates[t], residual=rd[t], dtype=dtype, workspace=ws)
+        assert torch.equal(y[t], y1), t
+    yin = rd[:3].clone()
+    rvq.moe_batch_decode(bank, xd[:3], ids[:3], gates[:3], residual=yin, dtype=dtype, y=yin, workspace=ws)
+    assert torch.equal(yin, y[:3])
+    assert rvq.check_device_status(ws) == 0
+
+
+@pytest.mark.parametrize("H,I,E,k", [
+    (1024, 2048, 8, 4),    # no wave-specialised down: tokens run one after another
+    (3584, 2048, 4, 2),    # both wave-specialised kernels (one K-tile per workgroup)
+])
+def test_batch_decode_other_shapes(H, I, E, k):
+    say(f"batch decode H={H} I={I} E={E} k={k}")
+    seed = synth.SEED_EXPERT ^ (H * 131 + I)
+    bank = upload_bank(seed, 0, E, H, I)
+    bits, w = router(seed, 0, E, H)
+    T = 3
+    xd = to_dev(np.stack([synth.activation_f32(seed, 200 + t, H) for t in range(T)]))
+    ids, gates, _ = rvq.router_topk(w, xd, k)
+    for dtype in ("f32", "f16"):
+        y = rvq.moe_batch_decode(bank, xd, ids, gates, dtype=dtype)
+        for t in range(T):
+            assert torch.equal(y[t], rvq.moe_layer_forward(bank, xd[t], ids[t], gates[t], dtype=dtype)), (dtype, t)
+
+
+def test_batch_decode_invalid_id_is_skipped(expert_bank):
+    """An id outside [0, E) in one token of a batch sets RVQ_ERR_EXPERT_ID and contributes zero,
+    as in a single-token call; the other tokens are unaffected."""
+    bank = expert_bank
+    say("batch decode with an invalid id")
+    X = to_dev(np.stack([synth.activation_f32(synth.SEED_EXPERT, 60 + t, HIDDEN) for t in range(2)]))
+    ids = torch.tensor([[0, 1], [1, 99]], dtype=torch.int32, device="cuda")
+    gates = torch.tensor([[0.25, 0.75], [0.5, 0.5]], dtype=torch.float32, device="cuda")
+    ws = rvq.make_batch_workspace(bank, 2, 2, "f32")
+    y = rvq.moe_batch_decode(bank, X, ids, gates, workspace=ws)
+    assert rvq.check_device_status(ws) == 6
+    for t in range(2):
+        y1 = rvq.moe_layer_forward(bank, X[t], ids[t], gates[t], workspace=ws)
+        assert torch.equal(y[t], y1)
+    assert rvq.check_device_status(ws) == 6
+
+
 def test_routed_decode_small_expert_count():
     """Top-k inside the gate/up kernel with fewer experts than wave lanes, k = 1 and k = E."""
     E, k_all = 5, 5
