@@ -19,6 +19,9 @@ module marshals numpy arrays and composes the per-layer steps:
                    still matter, so none is dropped)
   moe_layer(x)   = [residual +] sum_i gate_i * expert_{id_i}(x)
   stack step     = for each layer: n = rmsnorm(h); h += moe_layer_l(n)
+  crc32(bytes)   = CRC-32 (IEEE 802.3, reflected, preset and final complement) of a
+                   record's code payload, bit by bit (news.hada.io topic 32035,
+                   disk-streaming architecture section: optional payload crc32)
 
 Parity status of each function (what pins it) is listed in tests/test_oracle_pins.py.
 """
@@ -60,6 +63,8 @@ def _load():
         lib.orc_router_logits.argtypes = [p, p, i64, i64, i64, p, i32]
         lib.orc_topk.argtypes = [p, i64, i64, p, p, p]
         lib.orc_rmsnorm.argtypes = [p, i64, ctypes.c_double, p]
+        lib.orc_crc32.argtypes = [p, i64]
+        lib.orc_crc32.restype = ctypes.c_uint32
         _lib = lib
     return _lib
 
@@ -238,3 +243,10 @@ def moe_chunk(get_expert, router_bits, X, k, residual=None, tokens=None):
     if residual is not None:
         Y += np.asarray(residual, dtype=np.float64)[want]
     return Y, ids, gates
+
+
+def crc32(data):
+    """CRC-32 of a byte buffer (bytes or a uint8 array)."""
+    a = np.ascontiguousarray(np.frombuffer(data, dtype=np.uint8) if isinstance(data, (bytes, bytearray))
+                             else np.asarray(data, dtype=np.uint8).reshape(-1))
+    return int(_load().orc_crc32(a.ctypes.data, a.size))

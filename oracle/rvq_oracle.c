@@ -22,6 +22,9 @@
  *    selected logits (news.hada.io topic 32035, read-ahead section: 16
  *    experts per layer).
  *  - RMSNorm: h / sqrt(mean(h^2) + eps), unit weight.
+ *  - Record check: CRC-32 of an expert record's code payload (news.hada.io
+ *    topic 32035, disk-streaming architecture section: an optional crc32 of
+ *    each record's payload), computed bit by bit from its definition.
  */
 #include <math.h>
 #include <pthread.h>
@@ -228,4 +231,21 @@ void orc_rmsnorm(const double *h, int64_t H, double eps, double *out) {
   for (int64_t k = 0; k < H; ++k) ss += h[k] * h[k];
   double inv = 1.0 / sqrt(ss / (double)H + eps);
   for (int64_t k = 0; k < H; ++k) out[k] = h[k] * inv;
+}
+
+/* ---------------------------------------------------------------- CRC-32
+ * The CRC-32 of IEEE 802.3 (as in zlib and PNG): the message bits, least
+ * significant bit of each byte first, are divided by the generator
+ * x^32 + x^26 + x^23 + x^22 + x^16 + x^12 + x^11 + x^10 + x^8 + x^7 + x^5 +
+ * x^4 + x^2 + x + 1 with the register preset to all ones and the remainder
+ * complemented.  In the bit-reversed register the generator's low 32 terms
+ * read 0xEDB88320, and each message bit is one shift-and-conditional-subtract
+ * step: no table, no combination of partial results. */
+uint32_t orc_crc32(const uint8_t *data, int64_t n) {
+  uint32_t r = 0xFFFFFFFFu;
+  for (int64_t i = 0; i < n; ++i) {
+    r ^= data[i];
+    for (int b = 0; b < 8; ++b) r = (r & 1u) ? (r >> 1) ^ 0xEDB88320u : (r >> 1);
+  }
+  return ~r;
 }

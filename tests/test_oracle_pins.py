@@ -16,6 +16,8 @@ Pinned functions and what pins them:
   router / topk    : numpy matmul on widened bf16, lexsort order, scipy softmax
                      (k = E), gate = 1 at k = 1, exact ties -> lower id
   rmsnorm          : torch rms_norm, closed-form RMS of the output
+  crc32            : the standard check value of CRC-32 ("123456789" -> 0xCBF43926),
+                     zlib.crc32 on random buffers of ragged lengths, single-bit flips
 """
 import json
 import os
@@ -315,3 +317,22 @@ def test_rmsnorm_matches_torch_and_closed_form():
     ms = np.mean(h * h)
     assert abs(np.sqrt(np.mean(out * out)) - np.sqrt(ms / (ms + eps))) < 1e-14
     np.testing.assert_allclose(oracle.rmsnorm(7.0 * h, 0.0), oracle.rmsnorm(h, 0.0), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- CRC-32
+
+def test_crc32_check_value_and_zlib():
+    import zlib
+    assert oracle.crc32(b"123456789") == 0xCBF43926   # the catalogued check value of CRC-32
+    assert oracle.crc32(b"") == 0
+    rng = np.random.default_rng(7)
+    for n in (1, 3, 1023, 1024, 65537, 300001):
+        buf = rng.integers(0, 256, n, dtype=np.uint8)
+        assert oracle.crc32(buf) == zlib.crc32(buf.tobytes()), n
+    # a single flipped bit anywhere changes the value
+    buf = rng.integers(0, 256, 4096, dtype=np.uint8)
+    c = oracle.crc32(buf)
+    for pos in (0, 1000, 4095):
+        b2 = buf.copy()
+        b2[pos] ^= 0x10
+        assert oracle.crc32(b2) != c
