@@ -39,7 +39,7 @@ GATEUP_CODE_BYTES = K * 2 * (H * I * 3 // 8)              # 176,160,768 per gate
 GATEUP_CODEBOOK_BYTES = K * 2 * 3 * 256 * 8 * 4           # 786,432
 DOWN_CODE_BYTES = K * (H * I * 3 // 8)
 LDS_GATHER_RATE = {"f32": 5.97e12, "f16": 6.92e12}             # measured random-gather lookups/s, chip-wide
-KERNEL_SOURCES = ["rvq_quantized_moe_amd/csrc/kernels.hip", "rvq_quantized_moe_amd/csrc/device.hpp"]
+KERNEL_SOURCES = ["rvq_quantized_moe_amd/csrc/kernels.hip", "rvq_quantized_moe_amd/csrc/device.hpp"]   # decode kernels
 
 
 def kernel_source_hash():
@@ -327,6 +327,24 @@ def capture(torch, fn):
     return g
 
 
+def run_crc(torch, rvq, bank, reps=10):
+    """Integrity check of the resident layer bank: CRC-32 of all 256 records' code payloads
+    (4,227,858,432 bytes) per call; GB/s against the HBM peak."""
+    ws = torch.empty(rvq.lib().rvq_bank_crc32_workspace_bytes(ctypes.byref(bank.desc())), dtype=torch.uint8,
+                     device=bank.codes.device)
+    crc = torch.empty(bank.E, dtype=torch.int32, device=bank.codes.device)
+    rvq.bank_crc32(bank, crc=crc, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        rvq.bank_crc32(bank, crc=crc, workspace=ws)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / reps
+    nbytes = bank.E * (2 * bank.gate_bytes + bank.down_bytes)
+    return {"ms_per_bank": sec * 1e3, "GBps": nbytes / sec / 1e9, "frac_of_hbm_peak": nbytes / sec / 1e9 / HBM_PEAK_GBPS,
+            "bytes": nbytes}
+
+
 def run_matvec(torch, rvq, dev, steps):
     """One 256x512 RVQ matvec (fp32 tables): microseconds per call, graph-replayed."""
     import synth
@@ -513,7 +531,8 @@ def main():
     if not args.no_extra:
         print("[bench] one matvec, one expert", file=sys.stderr, flush=True)
         extra = {"matvec_256x512_f32": run_matvec(torch, rvq, dev, 2000),
-                 "expert_7168x2048_f32": run_expert(torch, rvq, bank, pool, 1000)}
+                 "expert_7168x2048_f32": run_expert(torch, rvq, bank, pool, 1000),
+                 "bank_crc32_256x16.5MB": run_crc(torch, rvq, bank)}
         del bank
         torch.cuda.empty_cache()
         extra["stack_92x64_top16_" + args.dtype] = run_stack(torch, rvq, dev, args.dtype)

@@ -245,6 +245,23 @@ int rvq_moe_batch_decode(const rvq_expert_bank_t *bank, const float *x, int32_t 
                          const float *gates, int32_t k, const float *residual, float *y, int32_t table_dtype,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Integrity check of a resident bank (news.hada.io topic 32035, disk-
+ * streaming architecture section: each expert record's payload carries an
+ * optional crc32, checked on request; codebooks carry none).
+ * crc[e] (device uint32 [num_experts], 4-byte aligned) = CRC-32 of IEEE
+ * 802.3 (the zlib / PNG CRC: preset all ones, bits least significant first,
+ * final complement) of expert e's code payload: its gate, up and down
+ * matrices in the packed layout, 2 * rvq_packed_bytes(inter, hidden) +
+ * rvq_packed_bytes(hidden, inter) bytes from codes + e * record_stride.
+ * One pass over the bank at HBM speed; compare against CRCs recorded when
+ * the bank was written.  workspace: 256-byte aligned, >= the query below
+ * (no zero-fill needed).
+ * ------------------------------------------------------------------------ */
+size_t rvq_bank_crc32_workspace_bytes(const rvq_expert_bank_t *bank);
+int rvq_bank_crc32(const rvq_expert_bank_t *bank, uint32_t *crc, void *workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
 /* Testing aid for the failure path.  Sets how many times each bounded wait
  * between the wave roles of the table kernels polls before it gives up
  * (which sets RVQ_ERR_DEVICE_STALL and leaves the output invalid, but lets

@@ -44,7 +44,7 @@ EXPORTS = [
     "rvq_moe_layer_workspace_bytes", "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed",
     "rvq_workspace_init", "rvq_rmsnorm", "rvq_stream_copy",
     "rvq_check_device_status", "rvq_moe_decode_routed", "rvq_set_wait_limit", "rvq_moe_block_decode",
-    "rvq_moe_batch_decode", "rvq_moe_batch_decode_workspace_bytes",
+    "rvq_moe_batch_decode", "rvq_moe_batch_decode_workspace_bytes", "rvq_bank_crc32", "rvq_bank_crc32_workspace_bytes",
 ]
 
 
@@ -84,6 +84,10 @@ def lib():
         L.rvq_moe_batch_decode.argtypes = [ctypes.POINTER(BankDesc), p, i32, p, p, i32, p, p, i32, p, sz, p]
         L.rvq_moe_batch_decode_workspace_bytes.argtypes = [ctypes.POINTER(BankDesc), i32, i32, i32]
         L.rvq_moe_batch_decode_workspace_bytes.restype = sz
+        L.rvq_bank_crc32.argtypes = [ctypes.POINTER(BankDesc), p, p, sz, p]
+        L.rvq_bank_crc32.restype = ctypes.c_int
+        L.rvq_bank_crc32_workspace_bytes.argtypes = [ctypes.POINTER(BankDesc)]
+        L.rvq_bank_crc32_workspace_bytes.restype = sz
         L.rvq_set_wait_limit.restype = i32
         L.rvq_moe_decode_routed.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, p, p, p, p, p, i32, p, sz, p]
         for name in ("rvq_pack_codes", "rvq_lut_build", "rvq_expert_gemv", "rvq_router_topk",
@@ -419,3 +423,19 @@ def moe_batch_decode(bank, x, ids, gates, residual=None, dtype="f32", y=None, wo
                                       _ptr(residual) if residual is not None else None, _ptr(y), d, _ptr(workspace),
                                       workspace.numel(), _stream(x)))
     return y
+
+
+def bank_crc32(bank, crc=None, workspace=None):
+    """CRC-32 of every expert record's code payload: int32 tensor [E] holding the uint32 bit patterns
+    (view as unsigned on the host: .cpu().numpy().view(np.uint32))."""
+    desc = bank.desc()
+    dev = bank.codes.device
+    crc = torch.empty(bank.E, dtype=torch.int32, device=dev) if crc is None else crc
+    if workspace is None:
+        n = lib().rvq_bank_crc32_workspace_bytes(ctypes.byref(desc))
+        if n == 0:
+            raise ValueError("invalid bank")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    _check(lib().rvq_bank_crc32(ctypes.byref(desc), _ptr(crc), _ptr(workspace), workspace.numel(),
+                                _stream(bank.codes)))
+    return crc

@@ -7,7 +7,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librvq.so")
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "chunk.hip"), os.path.join(CSRC, "abi.cpp")]
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "chunk.hip"), os.path.join(CSRC, "verify.hip"),
+           os.path.join(CSRC, "abi.cpp")]
 HEADERS = [os.path.join(CSRC, "device.hpp"), os.path.join(CSRC, "launch.hpp"), os.path.join(ROOT, "include", "rvq.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

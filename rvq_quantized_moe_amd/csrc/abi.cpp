@@ -209,6 +209,22 @@ int rvq_moe_batch_decode(const rvq_expert_bank_t* bank, const float* x, int32_t 
                                             workspace, stream));
 }
 
+size_t rvq_bank_crc32_workspace_bytes(const rvq_expert_bank_t* bank) {
+  if (check_bank(bank) != RVQ_OK) return 0;
+  return crc_workspace_bytes(bank->num_experts, bank->hidden, bank->inter);
+}
+
+int rvq_bank_crc32(const rvq_expert_bank_t* bank, uint32_t* crc, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  const int st = check_bank(bank);
+  if (st != RVQ_OK) return st;
+  if (!crc || !workspace) return RVQ_ERR_NULL;
+  if (!aligned(crc, 4) || !aligned(workspace, 256)) return RVQ_ERR_ALIGN;
+  if (workspace_bytes < crc_workspace_bytes(bank->num_experts, bank->hidden, bank->inter)) return RVQ_ERR_WORKSPACE;
+  return hip_status(launch_bank_crc32(bank->codes, bank->record_stride, bank->num_experts, bank->hidden, bank->inter,
+                                      crc, workspace, stream));
+}
+
 int rvq_moe_decode_routed(const rvq_expert_bank_t* bank, const void* w_router_bf16, const float* x, int32_t k,
                           const float* residual, float* y, int32_t* ids, float* gates, double* logits,
                           int32_t compute_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {

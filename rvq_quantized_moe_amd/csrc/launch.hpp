@@ -40,6 +40,12 @@ hipError_t launch_moe_batch_decode(const uint8_t* codes, const float* cb, int64_
                                    const float* x, int T, const int32_t* ids, const float* gates, int k,
                                    const float* residual, float* y, bool f16, void* ws, hipStream_t stream);
 constexpr int kMaxBatchDecode = 256;
+// CRC-32 of each expert record's code payload (verify.hip); the workspace holds one word per
+// 64 KiB block of every record.
+int64_t crc_payload_bytes(int H, int I);
+size_t crc_workspace_bytes(int E, int H, int I);
+hipError_t launch_bank_crc32(const uint8_t* codes, int64_t stride, int E, int H, int I, uint32_t* crc, void* ws,
+                             hipStream_t stream);
 hipError_t launch_router_norm_logits(const uint16_t* w, const float* h, int E, int H, float eps, double* logits,
                                      float* n, hipStream_t stream);
 hipError_t launch_router_logits(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, double* logits,

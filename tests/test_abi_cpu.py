@@ -180,6 +180,21 @@ def test_batch_decode_workspace_and_validation(L):
     assert call(a9=n - 1) == WS
 
 
+def test_bank_crc32_validation(L):
+    """rvq_bank_crc32: one word per 64 KiB block of every record in the workspace; every check returns
+    before anything is enqueued."""
+    q = L.rvq_bank_crc32_workspace_bytes
+    n = q(_bank())
+    assert n == 256 * 252 * 4   # 256 records; 16,515,072-byte payloads are 252 blocks of 64 KiB
+    assert q(None) == 0 and q(_bank(E=0)) == 0
+    f = L.rvq_bank_crc32
+    assert f(None, FAKE, FAKE, n, None) == NULL
+    assert f(_bank(), None, FAKE, n, None) == NULL and f(_bank(), FAKE, None, n, None) == NULL
+    assert f(_bank(), FAKE + 2, FAKE, n, None) == ALIGN and f(_bank(), FAKE, FAKE + 64, n, None) == ALIGN
+    assert f(_bank(), FAKE, FAKE, n - 1, None) == WS
+    assert f(_bank(E=0), FAKE, FAKE, n, None) == SHAPE
+
+
 def test_routed_decode_validation(L):
     """Every check of rvq_moe_decode_routed returns before anything is enqueued."""
     s = None

@@ -414,6 +414,45 @@ def test_batch_decode_invalid_id_is_skipped(expert_bank):
     assert rvq.check_device_status(ws) == 6
 
 
+def record_payload(bank, e):
+    n = 2 * bank.gate_bytes + bank.down_bytes
+    return bank.codes[e * bank.stride: e * bank.stride + n].cpu().numpy()
+
+
+def test_bank_crc32_matches_oracle(expert_bank):
+    """CRC-32 of each record's packed code payload, bit-exact against the oracle's bitwise CRC of the
+    same bytes; a flipped byte changes only that record's value (and matches the oracle again)."""
+    bank = expert_bank
+    say("bank crc32 (4 experts, 16.5 MB records)")
+    crc = rvq.bank_crc32(bank).cpu().numpy().view(np.uint32)
+    for e in range(bank.E):
+        assert int(crc[e]) == oracle.crc32(record_payload(bank, e)), e
+    pos = 2 * bank.stride + 12_345_679
+    saved = bank.codes[pos].clone()
+    bank.codes[pos] ^= 0x40
+    try:
+        crc2 = rvq.bank_crc32(bank).cpu().numpy().view(np.uint32)
+        assert int(crc2[2]) != int(crc[2]) and int(crc2[2]) == oracle.crc32(record_payload(bank, 2))
+        assert all(int(crc2[e]) == int(crc[e]) for e in (0, 1, 3))
+    finally:
+        bank.codes[pos] = saved
+    torch.cuda.synchronize()
+
+
+def test_bank_crc32_ragged_and_layer(layer_bank):
+    """A shape whose records end in a partial 64 KiB block (72 KiB payloads), and sampled experts of
+    the 256-expert layer bank."""
+    say("bank crc32 ragged shape and layer samples")
+    small = upload_bank(synth.SEED_EXPERT ^ 77, 0, 3, 256, 200)
+    crc = rvq.bank_crc32(small).cpu().numpy().view(np.uint32)
+    for e in range(3):
+        assert int(crc[e]) == oracle.crc32(record_payload(small, e)), e
+    bank = layer_bank[0]
+    crc = rvq.bank_crc32(bank).cpu().numpy().view(np.uint32)
+    for e in (0, 97, 255):
+        assert int(crc[e]) == oracle.crc32(record_payload(bank, e)), e
+
+
 def test_routed_decode_small_expert_count():
     """Top-k inside the gate/up kernel with fewer experts than wave lanes, k = 1 and k = E."""
     E, k_all = 5, 5
