@@ -345,6 +345,55 @@ def run_crc(torch, rvq, bank, reps=10):
             "bytes": nbytes}
 
 
+def run_pool(torch, rvq, bank, w, pool_x, slots_list=(32, 128), tokens=128):
+    """Layer decode with the 256 experts in pinned host memory and `slots` device records as the
+    LRU cache (rvq expert pool): per token, router top-16 on the device, ids to the host, acquire
+    (copies of the missing experts), decode on the slots.  Tokens/s, hit rate and the host-to-device
+    copy rate over the run (copies and decode overlap only through the streams)."""
+    dev = bank.codes.device
+    hc = torch.empty(bank.codes.numel(), dtype=torch.uint8, pin_memory=True)
+    hc.copy_(bank.codes)
+    hb = torch.empty(bank.codebooks.shape, dtype=torch.float32, pin_memory=True)
+    hb.copy_(bank.codebooks)
+    out = {}
+    for slots in slots_list:
+        pool = rvq.ExpertPool(hc, hb, bank.E, bank.H, bank.I, slots, device=dev)
+        ws = rvq.make_moe_workspace(pool.bank, 1, K, "f32")
+        y = torch.empty(H, dtype=torch.float32, device=dev)
+        ids = torch.empty((1, K), dtype=torch.int32, device=dev)
+        gates = torch.empty((1, K), dtype=torch.float32, device=dev)
+        logits = torch.empty((1, E), dtype=torch.float64, device=dev)
+        sd = torch.empty(K, dtype=torch.int32, device=dev)
+
+        def step(t):
+            x = pool_x[t % pool_x.shape[0]]
+            rvq.router_topk(w, x, K, ids=ids, gates=gates, logits=logits)
+            slot_ids = pool.acquire(ids[0].cpu().numpy())
+            sd.copy_(torch.from_numpy(slot_ids), non_blocking=False)
+            rvq.moe_layer_forward(pool.bank, x, sd, gates[0], dtype="f32", y=y, workspace=ws)
+        for t in range(8):
+            step(t)
+        torch.cuda.synchronize()
+        s0 = pool.stats()
+        t0 = time.perf_counter()
+        for t in range(tokens):
+            step(8 + t)
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        s1 = pool.stats()
+        status = rvq.check_device_status(ws)
+        if status:
+            raise RuntimeError(rvq.status_string(status))
+        hits, misses = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
+        out[f"slots_{slots}"] = {"tokens_per_s": tokens / sec, "hit_rate": hits / max(1, hits + misses),
+                                 "misses_per_token": misses / tokens,
+                                 "h2d_GBps": (s1["bytes_copied"] - s0["bytes_copied"]) / sec / 1e9}
+        pool.close()
+        del pool, ws
+    del hc, hb
+    return out
+
+
 def run_matvec(torch, rvq, dev, steps):
     """One 256x512 RVQ matvec (fp32 tables): microseconds per call, graph-replayed."""
     import synth
@@ -533,6 +582,8 @@ def main():
         extra = {"matvec_256x512_f32": run_matvec(torch, rvq, dev, 2000),
                  "expert_7168x2048_f32": run_expert(torch, rvq, bank, pool, 1000),
                  "bank_crc32_256x16.5MB": run_crc(torch, rvq, bank)}
+        print("[bench] expert pool (experts in pinned host memory)", file=sys.stderr, flush=True)
+        extra["layer_decode_expert_pool_host_backed"] = run_pool(torch, rvq, bank, w, pool)
         del bank
         torch.cuda.empty_cache()
         extra["stack_92x64_top16_" + args.dtype] = run_stack(torch, rvq, dev, args.dtype)

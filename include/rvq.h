@@ -262,6 +262,51 @@ size_t rvq_bank_crc32_workspace_bytes(const rvq_expert_bank_t *bank);
 int rvq_bank_crc32(const rvq_expert_bank_t *bank, uint32_t *crc, void *workspace, size_t workspace_bytes,
                    hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Expert pool: experts held in pinned host memory, an LRU set of `slots`
+ * device records as the cache (the pages' engine streams experts from NVMe
+ * into an LRU cache sized to one token's working set and prefetches what the
+ * next layer's router predicts: "Running a 2.78-Trillion-Parameter Model on a
+ * Laptop", Technical Insight; news.hada.io topic 32035, read-ahead and
+ * router-prediction section).  Host DRAM stands in for the NVMe tier here.
+ *
+ * rvq_pool_create: host_codes: num_experts records of record_stride bytes in
+ * the packed layout (as in rvq_expert_bank_t), host_codebooks: fp32
+ * [num_experts][3][3][256][8]; both pinned host memory (hipHostMalloc or a
+ * pinned torch tensor) that outlives the pool.  slot_codes (256-byte aligned,
+ * slots * record_stride bytes) and slot_codebooks (16-byte aligned, fp32
+ * [slots][3][3][256][8]) are device memory the caller owns; an
+ * rvq_expert_bank_t over them with num_experts = slots is the bank that the
+ * decode entry points use with slot ids.  The pool creates one stream of its
+ * own (default priority) for the copies.
+ * rvq_pool_acquire: makes the k experts ids[0..k) (host int32, 1 <= k <=
+ * slots) resident and writes their slot ids to slot_ids (host int32 [k]).
+ * Missing experts are copied (LRU victim among the slots this call does not
+ * use), after all work already enqueued on `stream` (earlier decodes may
+ * still read the victims); `stream` is made to wait for the copies of the
+ * slots it gets, so work enqueued on it afterwards sees them.  The slots
+ * stay valid for work enqueued on `stream` until the next acquire.  Never
+ * blocks the host.
+ * rvq_pool_prefetch: starts copies of the listed experts that are not
+ * resident (look-ahead), into slots that the latest acquire did not hand
+ * out; stops when none is free.  Does not touch any stream but the pool's.
+ * rvq_pool_stats: hits and misses of the acquires (distinct experts per
+ * call), prefetch copies started, bytes copied host to device.
+ * rvq_pool_destroy: waits for the pool's copies, frees its stream and events.
+ * Errors: RVQ_ERR_NULL, RVQ_ERR_SHAPE, RVQ_ERR_ALIGN, RVQ_ERR_EXPERT_ID (an
+ * id outside [0, num_experts): nothing is copied), RVQ_ERR_HIP.  A pool is
+ * not thread-safe: one host thread drives it.
+ * ------------------------------------------------------------------------ */
+typedef struct rvq_expert_pool rvq_expert_pool_t;
+int rvq_pool_create(const void *host_codes, const float *host_codebooks, int64_t record_stride, int32_t num_experts,
+                    int32_t hidden, int32_t inter, void *slot_codes, float *slot_codebooks, int32_t slots,
+                    rvq_expert_pool_t **out);
+int rvq_pool_acquire(rvq_expert_pool_t *pool, const int32_t *ids, int32_t k, int32_t *slot_ids, hipStream_t stream);
+int rvq_pool_prefetch(rvq_expert_pool_t *pool, const int32_t *ids, int32_t k);
+int rvq_pool_stats(const rvq_expert_pool_t *pool, int64_t *hits, int64_t *misses, int64_t *prefetches,
+                   int64_t *bytes_copied);
+int rvq_pool_destroy(rvq_expert_pool_t *pool);
+
 /* Testing aid for the failure path.  Sets how many times each bounded wait
  * between the wave roles of the table kernels polls before it gives up
  * (which sets RVQ_ERR_DEVICE_STALL and leaves the output invalid, but lets

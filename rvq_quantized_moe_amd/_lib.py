@@ -8,6 +8,7 @@ calls raise.
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,6 +46,7 @@ EXPORTS = [
     "rvq_workspace_init", "rvq_rmsnorm", "rvq_stream_copy",
     "rvq_check_device_status", "rvq_moe_decode_routed", "rvq_set_wait_limit", "rvq_moe_block_decode",
     "rvq_moe_batch_decode", "rvq_moe_batch_decode_workspace_bytes", "rvq_bank_crc32", "rvq_bank_crc32_workspace_bytes",
+    "rvq_pool_create", "rvq_pool_acquire", "rvq_pool_prefetch", "rvq_pool_stats", "rvq_pool_destroy",
 ]
 
 
@@ -88,6 +90,15 @@ def lib():
         L.rvq_bank_crc32.restype = ctypes.c_int
         L.rvq_bank_crc32_workspace_bytes.argtypes = [ctypes.POINTER(BankDesc)]
         L.rvq_bank_crc32_workspace_bytes.restype = sz
+        i64 = ctypes.c_int64
+        L.rvq_pool_create.argtypes = [p, p, i64, i32, i32, i32, p, p, i32, ctypes.POINTER(ctypes.c_void_p)]
+        L.rvq_pool_acquire.argtypes = [p, p, i32, p, p]
+        L.rvq_pool_prefetch.argtypes = [p, p, i32]
+        L.rvq_pool_stats.argtypes = [p, p, p, p, p]
+        L.rvq_pool_destroy.argtypes = [p]
+        for name in ("rvq_pool_create", "rvq_pool_acquire", "rvq_pool_prefetch", "rvq_pool_stats",
+                     "rvq_pool_destroy"):
+            getattr(L, name).restype = ctypes.c_int
         L.rvq_set_wait_limit.restype = i32
         L.rvq_moe_decode_routed.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, p, p, p, p, p, i32, p, sz, p]
         for name in ("rvq_pack_codes", "rvq_lut_build", "rvq_expert_gemv", "rvq_router_topk",
@@ -439,3 +450,54 @@ def bank_crc32(bank, crc=None, workspace=None):
     _check(lib().rvq_bank_crc32(ctypes.byref(desc), _ptr(crc), _ptr(workspace), workspace.numel(),
                                 _stream(bank.codes)))
     return crc
+
+
+class ExpertPool:
+    """Experts in pinned host memory with an LRU set of `slots` device records as the cache.
+
+    host_codes: pinned uint8 tensor of num_experts * record_stride bytes (packed records, e.g. a
+    copy of an ExpertBank's codes); host_codebooks: pinned fp32 [num_experts, 3, 3, 256, 8].
+    self.bank is the device bank of the slots: pass it, with the slot ids from acquire(), to the
+    decode functions."""
+
+    def __init__(self, host_codes, host_codebooks, num_experts, hidden, inter, slots, device="cuda",
+                 record_stride=None):
+        if not host_codes.is_pinned() or not host_codebooks.is_pinned():
+            raise ValueError("host_codes and host_codebooks must be pinned host tensors")
+        self.bank = ExpertBank(slots, hidden, inter, device=device, record_stride=record_stride)
+        self.host_codes, self.host_codebooks = host_codes, host_codebooks
+        self.E, self.slots = num_experts, slots
+        if host_codes.numel() < num_experts * self.bank.stride or host_codebooks.numel() < num_experts * 3 * 6144:
+            raise ValueError("host store too small")
+        handle = ctypes.c_void_p()
+        _check(lib().rvq_pool_create(_ptr(host_codes), _ptr(host_codebooks), self.bank.stride, num_experts, hidden,
+                                     inter, _ptr(self.bank.codes), _ptr(self.bank.codebooks), slots,
+                                     ctypes.byref(handle)))
+        self._h = handle
+
+    def acquire(self, ids):
+        """ids: host int sequence [k] -> host int32 slot ids [k]; the current stream waits for copies."""
+        a = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).reshape(-1))
+        out = np.empty(a.size, dtype=np.int32)
+        _check(lib().rvq_pool_acquire(self._h, a.ctypes.data, a.size, out.ctypes.data, _stream(self.bank.codes)))
+        return out
+
+    def prefetch(self, ids):
+        a = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+        _check(lib().rvq_pool_prefetch(self._h, a.ctypes.data, a.size))
+
+    def stats(self):
+        v = [ctypes.c_int64() for _ in range(4)]
+        _check(lib().rvq_pool_stats(self._h, *[ctypes.byref(x) for x in v]))
+        return {"hits": v[0].value, "misses": v[1].value, "prefetches": v[2].value, "bytes_copied": v[3].value}
+
+    def close(self):
+        if self._h:
+            _check(lib().rvq_pool_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,209 @@
+// Expert pool: an LRU set of HBM slots over experts held in pinned host memory (extern "C" entry
+// points of include/rvq.h, "Expert pool" section).
+//
+// The pages' engine keeps only the trunk resident and streams each token's experts from NVMe into
+// an LRU cache held at one token's working set, overlapping the reads with compute and prefetching
+// the experts that the next layer's router, run early on the current residual, predicts
+// ("Running a 2.78-Trillion-Parameter Model on a Laptop", Technical Insight; news.hada.io topic
+// 32035, read-ahead and router-prediction section).  Here host DRAM plays the NVMe role and HBM the
+// RAM cache: records are copied host-to-device by the DMA engines on a stream of the pool's own,
+// and the caller's compute stream waits only for the copies it needs.
+//
+// Ordering without host synchronisation:
+//  * every acquire records an event on the compute stream before returning slots; the kernels of
+//    earlier acquires were enqueued before it, so once the copy stream has waited for it, any slot
+//    that the current acquire does not hand out may be overwritten;
+//  * a slot handed out by the latest acquire may still be read by kernels in flight, so neither a
+//    later prefetch nor anything but the next acquire (after its own event) evicts it;
+//  * a slot's copy records an event on the copy stream; the compute stream waits for it once, the
+//    first time the slot is handed out after the copy.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/rvq.h"
+#include "device.hpp"
+
+struct rvq_expert_pool {
+  const uint8_t* host_codes = nullptr;
+  const float* host_cb = nullptr;
+  int64_t stride = 0, payload = 0;
+  int E = 0, H = 0, I = 0, S = 0;
+  uint8_t* dev_codes = nullptr;
+  float* dev_cb = nullptr;
+  hipStream_t copy = nullptr;
+  hipEvent_t compute_mark = nullptr;     // recorded on the compute stream at each acquire
+  std::vector<int> slot_of;              // [E] slot holding the expert, or -1
+  std::vector<int> expert_in;            // [S] expert held, or -1
+  std::vector<int64_t> last_use;         // [S] index of the acquire that last handed the slot out
+  std::vector<int64_t> stamp;            // [S] recency (larger = more recent)
+  std::vector<hipEvent_t> loaded;        // [S] end of the slot's latest copy
+  std::vector<char> unwaited;            // [S] the compute stream has not yet waited for that copy
+  int64_t acquires = 0, clock = 0;
+  int64_t hits = 0, misses = 0, prefetches = 0, bytes = 0;
+  bool mark_waited = false;              // the copy stream already waits for this acquire's mark
+};
+
+namespace {
+
+constexpr int64_t kCbBytes = 3 * (int64_t)rvq::kCodebookFloats * sizeof(float);   // one expert's codebooks
+
+// Least recently stamped slot that the latest acquire has not handed out (empty slots first); -1 if
+// every slot is in use by it.
+int pick_victim(const rvq_expert_pool& p, int64_t busy_acquire) {
+  int best = -1;
+  for (int s = 0; s < p.S; ++s) {
+    if (p.last_use[s] == busy_acquire) continue;
+    if (p.expert_in[s] < 0) return s;
+    if (best < 0 || p.stamp[s] < p.stamp[best]) best = s;
+  }
+  return best;
+}
+
+// Copies expert e into slot s on the copy stream (after the latest compute mark).
+hipError_t load_slot(rvq_expert_pool& p, int s, int e) {
+  hipError_t err = hipSuccess;
+  if (!p.mark_waited) {
+    err = hipStreamWaitEvent(p.copy, p.compute_mark, 0);
+    if (err != hipSuccess) return err;
+    p.mark_waited = true;
+  }
+  if (p.expert_in[s] >= 0) p.slot_of[p.expert_in[s]] = -1;
+  p.expert_in[s] = e;
+  p.slot_of[e] = s;
+  err = hipMemcpyAsync(p.dev_codes + (int64_t)s * p.stride, p.host_codes + (int64_t)e * p.stride, p.payload,
+                       hipMemcpyHostToDevice, p.copy);
+  if (err == hipSuccess)
+    err = hipMemcpyAsync(reinterpret_cast<uint8_t*>(p.dev_cb) + (int64_t)s * kCbBytes,
+                         reinterpret_cast<const uint8_t*>(p.host_cb) + (int64_t)e * kCbBytes, kCbBytes,
+                         hipMemcpyHostToDevice, p.copy);
+  if (err == hipSuccess) err = hipEventRecord(p.loaded[s], p.copy);
+  p.unwaited[s] = 1;
+  p.bytes += p.payload + kCbBytes;
+  return err;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rvq_pool_create(const void* host_codes, const float* host_codebooks, int64_t record_stride, int32_t num_experts,
+                    int32_t hidden, int32_t inter, void* slot_codes, float* slot_codebooks, int32_t slots,
+                    rvq_expert_pool_t** out) {
+  if (!out) return RVQ_ERR_NULL;
+  *out = nullptr;
+  if (!host_codes || !host_codebooks || !slot_codes || !slot_codebooks) return RVQ_ERR_NULL;
+  const size_t rec = rvq_bank_record_bytes(hidden, inter);
+  if (rec == 0 || num_experts < 1 || slots < 1 || record_stride < (int64_t)rec) return RVQ_ERR_SHAPE;
+  if (record_stride % 256 != 0 || (reinterpret_cast<uintptr_t>(slot_codes) & 255) != 0 ||
+      (reinterpret_cast<uintptr_t>(slot_codebooks) & 15) != 0)
+    return RVQ_ERR_ALIGN;
+  rvq_expert_pool* p = new (std::nothrow) rvq_expert_pool;
+  if (!p) return RVQ_ERR_HIP;
+  p->host_codes = static_cast<const uint8_t*>(host_codes);
+  p->host_cb = host_codebooks;
+  p->stride = record_stride;
+  p->payload = (int64_t)rec;
+  p->E = num_experts;
+  p->H = hidden;
+  p->I = inter;
+  p->S = slots;
+  p->dev_codes = static_cast<uint8_t*>(slot_codes);
+  p->dev_cb = slot_codebooks;
+  p->slot_of.assign(num_experts, -1);
+  p->expert_in.assign(slots, -1);
+  p->last_use.assign(slots, -1);
+  p->stamp.assign(slots, 0);
+  p->unwaited.assign(slots, 0);
+  p->loaded.assign(slots, nullptr);
+  bool ok = hipStreamCreateWithFlags(&p->copy, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&p->compute_mark, hipEventDisableTiming) == hipSuccess;
+  for (int s = 0; ok && s < slots; ++s) ok = hipEventCreateWithFlags(&p->loaded[s], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    rvq_pool_destroy(p);
+    return RVQ_ERR_HIP;
+  }
+  *out = p;
+  return RVQ_OK;
+}
+
+int rvq_pool_destroy(rvq_expert_pool_t* p) {
+  if (!p) return RVQ_ERR_NULL;
+  int st = RVQ_OK;
+  if (p->copy && hipStreamSynchronize(p->copy) != hipSuccess) st = RVQ_ERR_HIP;
+  for (hipEvent_t e : p->loaded)
+    if (e) (void)hipEventDestroy(e);
+  if (p->compute_mark) (void)hipEventDestroy(p->compute_mark);
+  if (p->copy) (void)hipStreamDestroy(p->copy);
+  delete p;
+  return st;
+}
+
+int rvq_pool_acquire(rvq_expert_pool_t* p, const int32_t* ids, int32_t k, int32_t* slot_ids, hipStream_t stream) {
+  if (!p || !ids || !slot_ids) return RVQ_ERR_NULL;
+  if (k < 1 || k > p->S) return RVQ_ERR_SHAPE;
+  for (int i = 0; i < k; ++i)
+    if (ids[i] < 0 || ids[i] >= p->E) return RVQ_ERR_EXPERT_ID;
+  const int64_t a = ++p->acquires;
+  hipError_t err = hipEventRecord(p->compute_mark, stream);
+  if (err != hipSuccess) return RVQ_ERR_HIP;
+  p->mark_waited = false;
+  // resident experts first, so that no eviction below can take a slot this acquire needs
+  for (int i = 0; i < k; ++i) {
+    const int s = p->slot_of[ids[i]];
+    if (s < 0) continue;
+    if (p->last_use[s] != a) ++p->hits;
+    p->last_use[s] = a;
+    p->stamp[s] = ++p->clock;
+  }
+  for (int i = 0; i < k; ++i) {
+    int s = p->slot_of[ids[i]];
+    if (s < 0) {
+      s = pick_victim(*p, a);   // exists: at most k - 1 < S slots carry this acquire's mark
+      ++p->misses;
+      err = load_slot(*p, s, ids[i]);
+      if (err != hipSuccess) return RVQ_ERR_HIP;
+      p->last_use[s] = a;
+      p->stamp[s] = ++p->clock;
+    }
+    slot_ids[i] = s;
+  }
+  for (int i = 0; i < k; ++i) {
+    const int s = slot_ids[i];
+    if (p->unwaited[s]) {
+      if (hipStreamWaitEvent(stream, p->loaded[s], 0) != hipSuccess) return RVQ_ERR_HIP;
+      p->unwaited[s] = 0;
+    }
+  }
+  return RVQ_OK;
+}
+
+int rvq_pool_prefetch(rvq_expert_pool_t* p, const int32_t* ids, int32_t k) {
+  if (!p || !ids) return RVQ_ERR_NULL;
+  if (k < 0) return RVQ_ERR_SHAPE;
+  for (int i = 0; i < k; ++i) {
+    const int e = ids[i];
+    if (e < 0 || e >= p->E) return RVQ_ERR_EXPERT_ID;
+    if (p->slot_of[e] >= 0) continue;
+    const int s = pick_victim(*p, p->acquires);
+    if (s < 0) break;   // every slot is held by the latest acquire
+    if (load_slot(*p, s, e) != hipSuccess) return RVQ_ERR_HIP;
+    p->stamp[s] = ++p->clock;
+    ++p->prefetches;
+  }
+  return RVQ_OK;
+}
+
+int rvq_pool_stats(const rvq_expert_pool_t* p, int64_t* hits, int64_t* misses, int64_t* prefetches,
+                   int64_t* bytes_copied) {
+  if (!p || !hits || !misses || !prefetches || !bytes_copied) return RVQ_ERR_NULL;
+  *hits = p->hits;
+  *misses = p->misses;
+  *prefetches = p->prefetches;
+  *bytes_copied = p->bytes;
+  return RVQ_OK;
+}
+
+}  // extern "C"

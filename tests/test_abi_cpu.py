@@ -195,6 +195,27 @@ def test_bank_crc32_validation(L):
     assert f(_bank(E=0), FAKE, FAKE, n, None) == SHAPE
 
 
+def test_pool_validation(L):
+    """Expert pool entry points: every argument check returns before any HIP call."""
+    out = ctypes.c_void_p()
+    c = L.rvq_pool_create
+    ok = [FAKE, FAKE2, 16_515_072, 32, 7168, 2048, FAKE, FAKE2, 8]
+    assert c(*ok, None) == NULL
+    assert c(None, *ok[1:], ctypes.byref(out)) == NULL
+    assert c(*ok[:6], None, *ok[7:], ctypes.byref(out)) == NULL
+    assert c(*ok[:8], 0, ctypes.byref(out)) == SHAPE                      # no slots
+    assert c(*ok[:3], 0, *ok[4:], ctypes.byref(out)) == SHAPE             # no experts
+    assert c(*ok[:2], 16_515_072 - 256, *ok[3:], ctypes.byref(out)) == SHAPE
+    assert c(*ok[:6], FAKE + 16, *ok[7:], ctypes.byref(out)) == ALIGN     # slot codes 256-aligned
+    assert out.value is None
+    ids = (ctypes.c_int32 * 2)(0, 1)
+    assert L.rvq_pool_acquire(None, ids, 2, ids, None) == NULL
+    assert L.rvq_pool_prefetch(None, ids, 2) == NULL
+    v = ctypes.c_int64()
+    assert L.rvq_pool_stats(None, ctypes.byref(v), ctypes.byref(v), ctypes.byref(v), ctypes.byref(v)) == NULL
+    assert L.rvq_pool_destroy(None) == NULL
+
+
 def test_routed_decode_validation(L):
     """Every check of rvq_moe_decode_routed returns before anything is enqueued."""
     s = None
