@@ -19,6 +19,8 @@ module marshals numpy arrays and composes the per-layer steps:
                    still matter, so none is dropped)
   moe_layer(x)   = [residual +] sum_i gate_i * expert_{id_i}(x)
   stack step     = for each layer: n = rmsnorm(h); h += moe_layer_l(n)
+  rvq_encode(W)  = codes [rows, cols/8, 3] of W by residual (stage-by-stage nearest
+                   entry) quantisation, decisions in fp32 (the decode's inverse)
   crc32(bytes)   = CRC-32 (IEEE 802.3, reflected, preset and final complement) of a
                    record's code payload, bit by bit (news.hada.io topic 32035,
                    disk-streaming architecture section: optional payload crc32)
@@ -63,6 +65,7 @@ def _load():
         lib.orc_router_logits.argtypes = [p, p, i64, i64, i64, p, i32]
         lib.orc_topk.argtypes = [p, i64, i64, p, p, p]
         lib.orc_rmsnorm.argtypes = [p, i64, ctypes.c_double, p]
+        lib.orc_rvq_encode.argtypes = [p, i64, i64, p, p]
         lib.orc_crc32.argtypes = [p, i64]
         lib.orc_crc32.restype = ctypes.c_uint32
         _lib = lib
@@ -250,3 +253,14 @@ def crc32(data):
     a = np.ascontiguousarray(np.frombuffer(data, dtype=np.uint8) if isinstance(data, (bytes, bytearray))
                              else np.asarray(data, dtype=np.uint8).reshape(-1))
     return int(_load().orc_crc32(a.ctypes.data, a.size))
+
+
+def rvq_encode(W, codebooks):
+    """Residual quantisation of W (fp32 [rows, cols]) against codebooks [3, 256, 8] fp32:
+    codes uint8 [rows, cols/8, 3]."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    cb = np.ascontiguousarray(codebooks, dtype=np.float32)
+    rows, cols = W.shape
+    codes = np.empty((rows, cols // 8, 3), dtype=np.uint8)
+    _load().orc_rvq_encode(W.ctypes.data, rows, cols, cb.ctypes.data, codes.ctypes.data)
+    return codes

@@ -22,6 +22,13 @@
  *    selected logits (news.hada.io topic 32035, read-ahead section: 16
  *    experts per layer).
  *  - RMSNorm: h / sqrt(mean(h^2) + eps), unit weight.
+ *  - RVQ encoding (for checking the GPU encoder): each 8-column sub-vector
+ *    is quantised stage by stage, each stage choosing the entry nearest (in
+ *    squared Euclidean distance) to what the earlier stages left, and that
+ *    entry is subtracted: the residual form of the RVQ decode above.  The
+ *    choice is taken in fp32 (distance accumulated over the 8 dims in order,
+ *    no fused operations, ties to the lower index), the precision of the
+ *    kernel that it checks.
  *  - Record check: CRC-32 of an expert record's code payload (news.hada.io
  *    topic 32035, disk-streaming architecture section: an optional crc32 of
  *    each record's payload), computed bit by bit from its definition.
@@ -248,4 +255,34 @@ uint32_t orc_crc32(const uint8_t *data, int64_t n) {
     for (int b = 0; b < 8; ++b) r = (r & 1u) ? (r >> 1) ^ 0xEDB88320u : (r >> 1);
   }
   return ~r;
+}
+
+/* ---------------------------------------------------------------- RVQ encode
+ * W: fp32 [rows][cols] (cols % 8 == 0); cb: fp32 [3][256][8]; codes: [rows][cols/8][3]. */
+void orc_rvq_encode(const float *W, int64_t rows, int64_t cols, const float *cb, uint8_t *codes) {
+  const int64_t G = cols / 8;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t g = 0; g < G; ++g) {
+      float v[8];
+      for (int j = 0; j < 8; ++j) v[j] = W[r * cols + 8 * g + j];
+      for (int s = 0; s < 3; ++s) {
+        const float *C = cb + (int64_t)s * 256 * 8;
+        int best = 0;
+        float best_d = 0.f;
+        for (int c = 0; c < 256; ++c) {
+          float d = 0.f;
+          for (int j = 0; j < 8; ++j) {
+            const float t = v[j] - C[c * 8 + j];
+            const float t2 = t * t;
+            d = d + t2;
+          }
+          if (c == 0 || d < best_d) {
+            best_d = d;
+            best = c;
+          }
+        }
+        for (int j = 0; j < 8; ++j) v[j] = v[j] - C[best * 8 + j];
+        codes[(r * G + g) * 3 + s] = (uint8_t)best;
+      }
+    }
 }

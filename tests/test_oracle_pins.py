@@ -16,6 +16,9 @@ Pinned functions and what pins them:
   router / topk    : numpy matmul on widened bf16, lexsort order, scipy softmax
                      (k = E), gate = 1 at k = 1, exact ties -> lower id
   rmsnorm          : torch rms_norm, closed-form RMS of the output
+  rvq_encode       : the binary-digit encoding built by bit extraction (greedy residual
+                     search must recover it exactly), exact codebook entries with a zero
+                     entry in the later stages, and re-encoding of a decode
   crc32            : the standard check value of CRC-32 ("123456789" -> 0xCBF43926),
                      zlib.crc32 on random buffers of ragged lengths, single-bit flips
 """
@@ -336,3 +339,37 @@ def test_crc32_check_value_and_zlib():
         b2 = buf.copy()
         b2[pos] ^= 0x10
         assert oracle.crc32(b2) != c
+
+
+# ---------------------------------------------------------------- RVQ encoder
+
+def test_rvq_encode_recovers_digit_codes():
+    """With digit codebooks (16, 4, 1) x bits, w = 16a + 4b + c: the nearest stage-0 entry takes
+    bit a in every column (16 + [0, 5] is nearer 16 than 0; [0, 5] nearer 0), and so on down the
+    stages, so the greedy residual search must return exactly the bit-extraction codes."""
+    rng = np.random.default_rng(11)
+    rows, cols = 37, 96
+    W = (16 * rng.integers(0, 2, (rows, cols)) + 4 * rng.integers(0, 2, (rows, cols))
+         + rng.integers(0, 2, (rows, cols))).astype(np.float32)
+    codes = oracle.rvq_encode(W, _digit_codebooks())
+    assert np.array_equal(codes, _digit_encode(W))
+    np.testing.assert_array_equal(oracle.dequant(codes, _digit_codebooks(), rows, cols), W)
+
+
+def test_rvq_encode_exact_entries_and_reencode():
+    rng = np.random.default_rng(12)
+    cb = rng.standard_normal((3, 256, 8)).astype(np.float32) * np.float32(0.5) ** np.arange(3)[:, None, None]
+    cb[1, 77] = 0.0
+    cb[2, 201] = 0.0
+    # a sub-vector equal to a stage-0 entry: that entry, then the zero entries of stages 1 and 2
+    picks = rng.integers(0, 256, 12)
+    W = cb[0, picks].reshape(3, 32)
+    codes = oracle.rvq_encode(W, cb)
+    assert np.array_equal(codes[:, :, 0].reshape(-1), picks)
+    assert np.all(codes[:, :, 1] == 77) and np.all(codes[:, :, 2] == 201)
+    # encoding a decode returns the same codes when every stage's pick is the unique nearest
+    # (stages far apart in scale: 1, 1e-2, 1e-4)
+    cb2 = rng.standard_normal((3, 256, 8)).astype(np.float32) * np.array([1.0, 1e-2, 1e-4], np.float32)[:, None, None]
+    c0 = rng.integers(0, 256, (20, 6, 3)).astype(np.uint8)
+    W2 = oracle.dequant(c0, cb2, 20, 48).astype(np.float32)
+    assert np.array_equal(oracle.rvq_encode(W2, cb2), c0)
