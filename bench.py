@@ -394,6 +394,33 @@ def run_pool(torch, rvq, bank, w, pool_x, slots_list=(32, 128), tokens=128):
     return out
 
 
+# fp32 VALU lane operations per second: MI355X's published fp32 vector peak (157.3 TFLOP/s) counts
+# an FMA as 2 flops, i.e. 78.6 T lane operations/s (256 CUs x 128 lanes per clock x 2.4 GHz); a
+# plain sub, mul, add, compare or select is one lane operation.
+VALU_LANE_OPS_PEAK = 157.3e12 / 2
+
+
+def run_encode(torch, rvq, dev, reps=5):
+    """RVQ encoding of one 2048 x 7168 matrix (residual, stage-by-stage nearest entry, fp32 decisions):
+    weights/s and the VALU rate of its distance arithmetic (3 stages x 256 entries x 8 dims x
+    (sub, mul, add) per sub-vector, plus a compare and two selects per entry)."""
+    import synth
+    rows, cols = I, H
+    cb = torch.from_numpy(synth.matrix_codebooks(synth.SEED_EXPERT, 0, 1, synth.GATE)).to(dev)
+    W = torch.randn(rows, cols, device=dev, generator=torch.Generator(device=dev).manual_seed(3))
+    codes = torch.empty((rows, cols // 8, 3), dtype=torch.uint8, device=dev)
+    rvq.rvq_encode(W, cb, codes=codes)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        rvq.rvq_encode(W, cb, codes=codes)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / reps
+    ops = rows * (cols // 8) * 3 * 256 * (3 * 8 + 3)
+    return {"ms": sec * 1e3, "weights_per_s": rows * cols / sec, "valu_lane_ops_per_s": ops / sec,
+            "frac_of_valu_peak": ops / sec / VALU_LANE_OPS_PEAK}
+
+
 def run_matvec(torch, rvq, dev, steps):
     """One 256x512 RVQ matvec (fp32 tables): microseconds per call, graph-replayed."""
     import synth
@@ -581,7 +608,8 @@ def main():
         print("[bench] one matvec, one expert", file=sys.stderr, flush=True)
         extra = {"matvec_256x512_f32": run_matvec(torch, rvq, dev, 2000),
                  "expert_7168x2048_f32": run_expert(torch, rvq, bank, pool, 1000),
-                 "bank_crc32_256x16.5MB": run_crc(torch, rvq, bank)}
+                 "bank_crc32_256x16.5MB": run_crc(torch, rvq, bank),
+                 "rvq_encode_2048x7168": run_encode(torch, rvq, dev)}
         print("[bench] expert pool (experts in pinned host memory)", file=sys.stderr, flush=True)
         extra["layer_decode_expert_pool_host_backed"] = run_pool(torch, rvq, bank, w, pool)
         del bank

@@ -246,6 +246,21 @@ int rvq_moe_batch_decode(const rvq_expert_bank_t *bank, const float *x, int32_t 
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * RVQ encoding (checkpoint conversion; the pages convert offline, news.hada.io
+ * topic 32035, conversion section): codes[r][g][s] for W fp32 [rows][cols]
+ * (cols % 8 == 0, 16-byte aligned, rows >= 1) against codebooks fp32
+ * [3][256][8] (16-byte aligned), written in the canonical layout
+ * [rows][cols/8][3] (pack with rvq_pack_codes).  Stage by stage, each 8-column
+ * sub-vector takes the entry nearest in squared Euclidean distance to what the
+ * earlier stages left, which is then subtracted; the distance is accumulated in
+ * fp32 over the 8 dims in order with no fused operations and ties go to the
+ * lower index, so the result is reproducible bit for bit.  Codebook fitting is
+ * not part of the library (the pages' codebooks come from training).
+ * ------------------------------------------------------------------------ */
+int rvq_encode(const float *W, int32_t rows, int32_t cols, const float *codebooks, uint8_t *codes,
+               hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Integrity check of a resident bank (news.hada.io topic 32035, disk-
  * streaming architecture section: each expert record's payload carries an
  * optional crc32, checked on request; codebooks carry none).

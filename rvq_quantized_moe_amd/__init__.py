@@ -9,11 +9,11 @@ from ._lib import (BF16, F16, F32, ExpertBank, ExpertPool, RvqError, bank_crc32,
                    moe_decode_routed, moe_layer_forward,
                    moe_workspace_bytes,
                    pack_codes,
-                   packed_bytes, rmsnorm, router_topk, status_string, stream_copy, workspace_init)
+                   packed_bytes, rmsnorm, router_topk, rvq_encode, status_string, stream_copy, workspace_init)
 
 __all__ = ["BF16", "F16", "F32", "ExpertBank", "ExpertPool", "RvqError", "bank_crc32", "check_device_status", "expert_gemv",
            "gemv_workspace_bytes", "lib", "lut_build", "make_batch_workspace", "make_moe_workspace", "moe_batch_decode",
            "moe_block_decode", "moe_decode_routed",
            "moe_layer_forward",
-           "moe_workspace_bytes", "pack_codes", "packed_bytes", "rmsnorm", "router_topk", "status_string",
+           "moe_workspace_bytes", "pack_codes", "packed_bytes", "rmsnorm", "router_topk", "rvq_encode", "status_string",
            "stream_copy", "workspace_init"]

@@ -46,7 +46,7 @@ EXPORTS = [
     "rvq_workspace_init", "rvq_rmsnorm", "rvq_stream_copy",
     "rvq_check_device_status", "rvq_moe_decode_routed", "rvq_set_wait_limit", "rvq_moe_block_decode",
     "rvq_moe_batch_decode", "rvq_moe_batch_decode_workspace_bytes", "rvq_bank_crc32", "rvq_bank_crc32_workspace_bytes",
-    "rvq_pool_create", "rvq_pool_acquire", "rvq_pool_prefetch", "rvq_pool_stats", "rvq_pool_destroy",
+    "rvq_encode", "rvq_pool_create", "rvq_pool_acquire", "rvq_pool_prefetch", "rvq_pool_stats", "rvq_pool_destroy",
 ]
 
 
@@ -86,6 +86,8 @@ def lib():
         L.rvq_moe_batch_decode.argtypes = [ctypes.POINTER(BankDesc), p, i32, p, p, i32, p, p, i32, p, sz, p]
         L.rvq_moe_batch_decode_workspace_bytes.argtypes = [ctypes.POINTER(BankDesc), i32, i32, i32]
         L.rvq_moe_batch_decode_workspace_bytes.restype = sz
+        L.rvq_encode.argtypes = [p, i32, i32, p, p, p]
+        L.rvq_encode.restype = ctypes.c_int
         L.rvq_bank_crc32.argtypes = [ctypes.POINTER(BankDesc), p, p, sz, p]
         L.rvq_bank_crc32.restype = ctypes.c_int
         L.rvq_bank_crc32_workspace_bytes.argtypes = [ctypes.POINTER(BankDesc)]
@@ -501,3 +503,14 @@ class ExpertPool:
             self.close()
         except Exception:
             pass
+
+
+def rvq_encode(W, codebooks, codes=None):
+    """Residual RVQ codes of W (fp32 [rows, cols]) against codebooks fp32 [3, 256, 8]:
+    uint8 [rows, cols/8, 3] (canonical layout)."""
+    _dev(W, torch.float32, "W")
+    _dev(codebooks, torch.float32, "codebooks")
+    rows, cols = W.shape
+    codes = torch.empty((rows, cols // 8, 3), dtype=torch.uint8, device=W.device) if codes is None else codes
+    _check(lib().rvq_encode(_ptr(W), rows, cols, _ptr(codebooks), _ptr(codes), _stream(W)))
+    return codes

@@ -209,6 +209,14 @@ int rvq_moe_batch_decode(const rvq_expert_bank_t* bank, const float* x, int32_t 
                                             workspace, stream));
 }
 
+int rvq_encode(const float* W, int32_t rows, int32_t cols, const float* codebooks, uint8_t* codes,
+               hipStream_t stream) {
+  if (!W || !codebooks || !codes) return RVQ_ERR_NULL;
+  if (rows < 1 || cols < 8 || cols % 8 != 0) return RVQ_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(codebooks, 16)) return RVQ_ERR_ALIGN;
+  return hip_status(launch_rvq_encode(W, rows, cols, codebooks, codes, stream));
+}
+
 size_t rvq_bank_crc32_workspace_bytes(const rvq_expert_bank_t* bank) {
   if (check_bank(bank) != RVQ_OK) return 0;
   return crc_workspace_bytes(bank->num_experts, bank->hidden, bank->inter);

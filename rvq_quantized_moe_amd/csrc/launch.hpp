@@ -40,6 +40,10 @@ hipError_t launch_moe_batch_decode(const uint8_t* codes, const float* cb, int64_
                                    const float* x, int T, const int32_t* ids, const float* gates, int k,
                                    const float* residual, float* y, bool f16, void* ws, hipStream_t stream);
 constexpr int kMaxBatchDecode = 256;
+// Residual RVQ encoding of W fp32 [rows][cols] against codebooks [3][256][8] into canonical codes
+// [rows][cols/8][3] (encode.hip).
+hipError_t launch_rvq_encode(const float* W, int64_t rows, int64_t cols, const float* cb, uint8_t* codes,
+                             hipStream_t stream);
 // CRC-32 of each expert record's code payload (verify.hip); the workspace holds one word per
 // 64 KiB block of every record.
 int64_t crc_payload_bytes(int H, int I);
