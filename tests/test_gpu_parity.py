@@ -504,6 +504,70 @@ def test_rvq_encode_full_size_sampled():
     assert rel_l2(y, oracle.gemv(codes, cb, rows, cols, x)) <= 1e-5
 
 
+def test_graph_replays_match_eager(layer_bank):
+    """The benchmark replays HIP graphs of the decode entry points: every replay, with new inputs
+    copied in eagerly between replays, equals an eager call on the same inputs bit for bit (routed
+    step, pre-norm block in place, and a 3-token batch)."""
+    bank, bits, w = layer_bank
+    say("graph replays vs eager")
+    k = TOP_K
+    ws = rvq.make_moe_workspace(bank, 1, k, "f32")
+    wsb = rvq.make_batch_workspace(bank, 3, k, "f32")
+    xin = torch.empty(HIDDEN, dtype=torch.float32, device="cuda")
+    hblk = torch.empty_like(xin)
+    y = torch.empty_like(xin)
+    ids = torch.empty(k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(k, dtype=torch.float32, device="cuda")
+    logits = torch.empty(LAYER_EXPERTS, dtype=torch.float64, device="cuda")
+    xb = torch.empty(3, HIDDEN, dtype=torch.float32, device="cuda")
+    idsb = torch.empty(3, k, dtype=torch.int32, device="cuda")
+    gatesb = torch.empty(3, k, dtype=torch.float32, device="cuda")
+    yb = torch.empty(3, HIDDEN, dtype=torch.float32, device="cuda")
+
+    def routed():
+        rvq.moe_decode_routed(bank, w, xin, k, y=y, ids=ids, gates=gates, logits=logits, workspace=ws)
+
+    def block():
+        rvq.moe_block_decode(bank, w, hblk, k, 1e-6, h_out=hblk, ids=ids, gates=gates, logits=logits, workspace=ws)
+
+    def batch():
+        rvq.moe_batch_decode(bank, xb, idsb, gatesb, y=yb, workspace=wsb)
+
+    def inputs(t):
+        xs = np.stack([synth.activation_f32(synth.SEED_LAYER, 500 + 4 * t + j, HIDDEN) for j in range(4)])
+        return to_dev(xs)
+    X0 = inputs(0)
+    xin.copy_(X0[0]); hblk.copy_(X0[1]); xb.copy_(X0[1:])
+    ib, gb, _ = rvq.router_topk(w, xb, k)
+    idsb.copy_(ib); gatesb.copy_(gb)
+    routed(); block(); batch()
+    torch.cuda.synchronize()
+    graphs = []
+    for fn in (routed, block, batch):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs.append(g)
+    for t in range(1, 5):
+        X = inputs(t)
+        ib, gb, _ = rvq.router_topk(w, X[1:], k)
+        # eager references on the same inputs
+        ref_y, ref_ids, _, _ = rvq.moe_decode_routed(bank, w, X[0], k, workspace=ws)
+        ref_h, _, _, _ = rvq.moe_block_decode(bank, w, X[1], k, 1e-6, workspace=ws)
+        ref_b = rvq.moe_batch_decode(bank, X[1:], ib, gb, workspace=wsb)
+        xin.copy_(X[0]); hblk.copy_(X[1]); xb.copy_(X[1:]); idsb.copy_(ib); gatesb.copy_(gb)
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref_y) and torch.equal(ids, ref_ids), t
+        graphs[1].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(hblk, ref_h), t
+        graphs[2].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yb, ref_b), t
+    assert rvq.check_device_status(ws) == 0 and rvq.check_device_status(wsb) == 0
+
+
 def test_routed_decode_small_expert_count():
     """Top-k inside the gate/up kernel with fewer experts than wave lanes, k = 1 and k = E."""
     E, k_all = 5, 5
