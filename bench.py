@@ -421,6 +421,79 @@ def run_encode(torch, rvq, dev, reps=5):
             "frac_of_valu_peak": ops / sec / VALU_LANE_OPS_PEAK}
 
 
+def run_stack_pool(torch, rvq, dev, layers=8, slots=128, tokens=12):
+    """Pre-norm stack of 8 layers x 64 experts (8.5 GB of codes) held in pinned host memory behind
+    a pool of `slots` device records, decoded token by token, with and without the pages' router
+    look-ahead: layer l+1's router run on layer l's normalised input (before layer l's MoE), its
+    16 picks, or the 8 highest-ranked, prefetched while layer l decodes.  Tokens/s, pool hit rate, and the fraction of layer l+1's
+    experts that the look-ahead predicted."""
+    import synth
+    from workloads import RMS_EPS, Stack
+    st = Stack(layers=layers, device=dev)
+    E1, stride = st.E, st.banks[0].stride
+    hc = torch.empty(layers * E1 * stride, dtype=torch.uint8, pin_memory=True)
+    hb = torch.empty((layers * E1, 3, 3, 256, 8), dtype=torch.float32, pin_memory=True)
+    for l in range(layers):
+        hc[l * E1 * stride:(l + 1) * E1 * stride].copy_(st.banks[l].codes)
+        hb[l * E1:(l + 1) * E1].copy_(st.banks[l].codebooks)
+    routers = st.routers
+    st.banks = None
+    torch.cuda.empty_cache()
+    xs = [torch.from_numpy(synth.activation_f32(synth.SEED_STACK, t, H)).to(dev) for t in range(tokens + 2)]
+    h = torch.empty(H, dtype=torch.float32, device=dev)
+    n = torch.empty_like(h)
+    sd = torch.empty(K, dtype=torch.int32, device=dev)
+    out = {}
+    for look in (0, K, K // 2):
+        pool = rvq.ExpertPool(hc, hb, layers * E1, H, I, slots, device=dev)
+        ws = rvq.make_moe_workspace(pool.bank, 1, K, "f32")
+        pred = {"hit": 0, "n": 0}
+
+        def token(t):
+            h.copy_(xs[t])
+            nxt = None
+            for l in range(layers):
+                rvq.rmsnorm(h, RMS_EPS, out=n)
+                ids, gates, _ = rvq.router_topk(routers[l], n, K)
+                if look and l + 1 < layers:
+                    p_ids, _, _ = rvq.router_topk(routers[l + 1], n, K)
+                    both = torch.cat([ids[0], p_ids[0]]).cpu().numpy()
+                    cur, pnext = both[:K], both[K:]
+                else:
+                    cur, pnext = ids[0].cpu().numpy(), None
+                if nxt is not None:
+                    pred["hit"] += len(set(nxt.tolist()) & set(cur.tolist()))
+                    pred["n"] += K
+                sd.copy_(torch.from_numpy(pool.acquire(cur + l * E1)))
+                rvq.moe_layer_forward(pool.bank, n, sd, gates[0], residual=h, y=h, dtype="f32", workspace=ws)
+                if pnext is not None:
+                    pool.prefetch(pnext[:look] + (l + 1) * E1)   # the `look` highest-ranked picks
+                nxt = pnext
+        for t in range(2):
+            token(t)
+        torch.cuda.synchronize()
+        s0 = pool.stats()
+        pred["hit"] = pred["n"] = 0
+        t0 = time.perf_counter()
+        for t in range(tokens):
+            token(2 + t)
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        s1 = pool.stats()
+        hits, misses = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
+        key = f"lookahead_top{look}" if look else "no_lookahead"
+        out[key] = {"tokens_per_s": tokens / sec, "ms_per_token": sec / tokens * 1e3,
+                    "hit_rate": hits / max(1, hits + misses),
+                    "h2d_GBps": (s1["bytes_copied"] - s0["bytes_copied"]) / sec / 1e9}
+        if look:
+            out[key]["predicted_fraction"] = pred["hit"] / max(1, pred["n"])
+        pool.close()
+        del pool, ws
+    out["config"] = {"layers": layers, "experts_per_layer": E1, "slots": slots, "host_bytes": int(hc.numel())}
+    del hc, hb
+    return out
+
+
 def run_matvec(torch, rvq, dev, steps):
     """One 256x512 RVQ matvec (fp32 tables): microseconds per call, graph-replayed."""
     import synth
@@ -615,6 +688,8 @@ def main():
         del bank
         torch.cuda.empty_cache()
         extra["stack_92x64_top16_" + args.dtype] = run_stack(torch, rvq, dev, args.dtype)
+        print("[bench] 8-layer stack behind an expert pool, router look-ahead", file=sys.stderr, flush=True)
+        extra["stack_8x64_host_backed_pool"] = run_stack_pool(torch, rvq, dev)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -6,8 +6,9 @@
 // the experts that the next layer's router, run early on the current residual, predicts
 // ("Running a 2.78-Trillion-Parameter Model on a Laptop", Technical Insight; news.hada.io topic
 // 32035, read-ahead and router-prediction section).  Here host DRAM plays the NVMe role and HBM the
-// RAM cache: records are copied host-to-device by the DMA engines on a stream of the pool's own,
-// and the caller's compute stream waits only for the copies it needs.
+// RAM cache: records are copied host-to-device by the DMA engines on streams of the pool's own (one
+// for the copies an acquire needs, one for look-ahead copies, so that a demand copy never queues
+// behind a prefetch), and the caller's compute stream waits only for the copies it needs.
 //
 // Ordering without host synchronisation:
 //  * every acquire records an event on the compute stream before returning slots; the kernels of
@@ -15,8 +16,9 @@
 //    that the current acquire does not hand out may be overwritten;
 //  * a slot handed out by the latest acquire may still be read by kernels in flight, so neither a
 //    later prefetch nor anything but the next acquire (after its own event) evicts it;
-//  * a slot's copy records an event on the copy stream; the compute stream waits for it once, the
-//    first time the slot is handed out after the copy.
+//  * a slot's copy records an event on its copy stream; the compute stream waits for it once, the
+//    first time the slot is handed out after the copy, and the slot's next copy (on either copy
+//    stream) waits for it too.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,7 +35,8 @@ struct rvq_expert_pool {
   int E = 0, H = 0, I = 0, S = 0;
   uint8_t* dev_codes = nullptr;
   float* dev_cb = nullptr;
-  hipStream_t copy = nullptr;
+  hipStream_t copy = nullptr;            // copies an acquire needs
+  hipStream_t ahead = nullptr;           // look-ahead copies (never queued in front of the former)
   hipEvent_t compute_mark = nullptr;     // recorded on the compute stream at each acquire
   std::vector<int> slot_of;              // [E] slot holding the expert, or -1
   std::vector<int> expert_in;            // [S] expert held, or -1
@@ -43,7 +46,7 @@ struct rvq_expert_pool {
   std::vector<char> unwaited;            // [S] the compute stream has not yet waited for that copy
   int64_t acquires = 0, clock = 0;
   int64_t hits = 0, misses = 0, prefetches = 0, bytes = 0;
-  bool mark_waited = false;              // the copy stream already waits for this acquire's mark
+  bool mark_waited[2] = {false, false};  // each copy stream already waits for this acquire's mark
 };
 
 namespace {
@@ -62,24 +65,29 @@ int pick_victim(const rvq_expert_pool& p, int64_t busy_acquire) {
   return best;
 }
 
-// Copies expert e into slot s on the copy stream (after the latest compute mark).
-hipError_t load_slot(rvq_expert_pool& p, int s, int e) {
+// Copies expert e into slot s (after the latest compute mark) on the demand stream, or on the
+// look-ahead stream (lookahead).
+hipError_t load_slot(rvq_expert_pool& p, int s, int e, bool lookahead) {
   hipError_t err = hipSuccess;
-  if (!p.mark_waited) {
-    err = hipStreamWaitEvent(p.copy, p.compute_mark, 0);
+  hipStream_t st = lookahead ? p.ahead : p.copy;
+  if (!p.mark_waited[lookahead]) {
+    err = hipStreamWaitEvent(st, p.compute_mark, 0);
     if (err != hipSuccess) return err;
-    p.mark_waited = true;
+    p.mark_waited[lookahead] = true;
   }
+  // the slot's previous copy may still be in flight on the other copy stream
+  err = hipStreamWaitEvent(st, p.loaded[s], 0);
+  if (err != hipSuccess) return err;
   if (p.expert_in[s] >= 0) p.slot_of[p.expert_in[s]] = -1;
   p.expert_in[s] = e;
   p.slot_of[e] = s;
   err = hipMemcpyAsync(p.dev_codes + (int64_t)s * p.stride, p.host_codes + (int64_t)e * p.stride, p.payload,
-                       hipMemcpyHostToDevice, p.copy);
+                       hipMemcpyHostToDevice, st);
   if (err == hipSuccess)
     err = hipMemcpyAsync(reinterpret_cast<uint8_t*>(p.dev_cb) + (int64_t)s * kCbBytes,
                          reinterpret_cast<const uint8_t*>(p.host_cb) + (int64_t)e * kCbBytes, kCbBytes,
-                         hipMemcpyHostToDevice, p.copy);
-  if (err == hipSuccess) err = hipEventRecord(p.loaded[s], p.copy);
+                         hipMemcpyHostToDevice, st);
+  if (err == hipSuccess) err = hipEventRecord(p.loaded[s], st);
   p.unwaited[s] = 1;
   p.bytes += p.payload + kCbBytes;
   return err;
@@ -119,6 +127,7 @@ int rvq_pool_create(const void* host_codes, const float* host_codebooks, int64_t
   p->unwaited.assign(slots, 0);
   p->loaded.assign(slots, nullptr);
   bool ok = hipStreamCreateWithFlags(&p->copy, hipStreamNonBlocking) == hipSuccess &&
+            hipStreamCreateWithFlags(&p->ahead, hipStreamNonBlocking) == hipSuccess &&
             hipEventCreateWithFlags(&p->compute_mark, hipEventDisableTiming) == hipSuccess;
   for (int s = 0; ok && s < slots; ++s) ok = hipEventCreateWithFlags(&p->loaded[s], hipEventDisableTiming) == hipSuccess;
   if (!ok) {
@@ -133,10 +142,12 @@ int rvq_pool_destroy(rvq_expert_pool_t* p) {
   if (!p) return RVQ_ERR_NULL;
   int st = RVQ_OK;
   if (p->copy && hipStreamSynchronize(p->copy) != hipSuccess) st = RVQ_ERR_HIP;
+  if (p->ahead && hipStreamSynchronize(p->ahead) != hipSuccess) st = RVQ_ERR_HIP;
   for (hipEvent_t e : p->loaded)
     if (e) (void)hipEventDestroy(e);
   if (p->compute_mark) (void)hipEventDestroy(p->compute_mark);
   if (p->copy) (void)hipStreamDestroy(p->copy);
+  if (p->ahead) (void)hipStreamDestroy(p->ahead);
   delete p;
   return st;
 }
@@ -149,7 +160,7 @@ int rvq_pool_acquire(rvq_expert_pool_t* p, const int32_t* ids, int32_t k, int32_
   const int64_t a = ++p->acquires;
   hipError_t err = hipEventRecord(p->compute_mark, stream);
   if (err != hipSuccess) return RVQ_ERR_HIP;
-  p->mark_waited = false;
+  p->mark_waited[0] = p->mark_waited[1] = false;
   // resident experts first, so that no eviction below can take a slot this acquire needs
   for (int i = 0; i < k; ++i) {
     const int s = p->slot_of[ids[i]];
@@ -163,7 +174,7 @@ int rvq_pool_acquire(rvq_expert_pool_t* p, const int32_t* ids, int32_t k, int32_
     if (s < 0) {
       s = pick_victim(*p, a);   // exists: at most k - 1 < S slots carry this acquire's mark
       ++p->misses;
-      err = load_slot(*p, s, ids[i]);
+      err = load_slot(*p, s, ids[i], false);
       if (err != hipSuccess) return RVQ_ERR_HIP;
       p->last_use[s] = a;
       p->stamp[s] = ++p->clock;
@@ -189,7 +200,7 @@ int rvq_pool_prefetch(rvq_expert_pool_t* p, const int32_t* ids, int32_t k) {
     if (p->slot_of[e] >= 0) continue;
     const int s = pick_victim(*p, p->acquires);
     if (s < 0) break;   // every slot is held by the latest acquire
-    if (load_slot(*p, s, e) != hipSuccess) return RVQ_ERR_HIP;
+    if (load_slot(*p, s, e, true) != hipSuccess) return RVQ_ERR_HIP;
     p->stamp[s] = ++p->clock;
     ++p->prefetches;
   }

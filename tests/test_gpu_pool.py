@@ -120,3 +120,69 @@ def test_pool_rejects_bad_ids(store):
         assert pool.stats()["misses"] == 0
     finally:
         pool.close()
+
+
+def test_pool_two_layer_lookahead_matches_resident(store):
+    """The pages' look-ahead on a 2-layer pre-norm stack over the pool (the 24 experts as 2 layers of
+    12): layer 1's router run early on layer 0's normalised input, its picks prefetched while layer
+    0 decodes; the final h equals the all-resident computation bit for bit."""
+    bank, hc, hb, _ = store
+    say("pool: 2-layer stack with router look-ahead")
+    E1, k = 12, 4
+    routers = [router(synth.SEED_EXPERT ^ 0x6, l, E1, HIDDEN)[1] for l in range(2)]
+    pool = rvq.ExpertPool(hc, hb, E_POOL, HIDDEN, INTER, 8)
+    ws = rvq.make_moe_workspace(pool.bank, 1, k, "f32")
+    wsr = rvq.make_moe_workspace(bank, 1, k, "f32")
+    try:
+        for t in range(4):
+            x = torch.from_numpy(synth.activation_f32(synth.SEED_EXPERT ^ 0x6, t, HIDDEN)).cuda()
+            h, href = x.clone(), x.clone()
+            for l in range(2):
+                n = rvq.rmsnorm(h, 1e-6)
+                ids, gates, _ = rvq.router_topk(routers[l], n, k)
+                if l == 0:
+                    pred, _, _ = rvq.router_topk(routers[1], n, k)
+                    pred_h = pred[0].cpu().numpy() + E1
+                slot = pool.acquire(ids[0].cpu().numpy() + l * E1)
+                rvq.moe_layer_forward(pool.bank, n, torch.from_numpy(slot).cuda(), gates[0], residual=h, y=h,
+                                      dtype="f32", workspace=ws)
+                if l == 0:
+                    pool.prefetch(pred_h)
+                nr = rvq.rmsnorm(href, 1e-6)
+                idr, gr, _ = rvq.router_topk(routers[l], nr, k)
+                rvq.moe_layer_forward(bank, nr, idr[0] + l * E1, gr[0], residual=href, y=href, dtype="f32",
+                                      workspace=wsr)
+            assert torch.equal(h, href), t
+        assert pool.stats()["prefetches"] > 0
+    finally:
+        pool.close()
+
+
+def test_pool_evicts_slots_with_lookahead_copies_in_flight(store):
+    """Look-ahead copies run on their own stream; an acquire that right away needs every slot evicts
+    the slots being prefetched into, so its copies must queue behind theirs.  6 slots: acquire 4,
+    prefetch 2 others, acquire 6 new ones at once; every decode equals the resident bank."""
+    bank, hc, hb, w = store
+    say("pool: eviction of slots with look-ahead copies in flight")
+    pool = rvq.ExpertPool(hc, hb, E_POOL, HIDDEN, INTER, 6)
+    ws = rvq.make_moe_workspace(pool.bank, 1, 6, "f32")
+    wsr = rvq.make_moe_workspace(bank, 1, 6, "f32")
+    rng = np.random.default_rng(9)
+    x = torch.from_numpy(synth.activation_f32(synth.SEED_EXPERT ^ 0x5, 77, HIDDEN)).cuda()
+
+    def decode(ids):
+        g = torch.from_numpy(rng.random(len(ids)).astype(np.float32)).cuda()
+        slot = pool.acquire(ids)
+        y = rvq.moe_layer_forward(pool.bank, x, torch.from_numpy(slot).cuda(), g, dtype="f32", workspace=ws)
+        ref = rvq.moe_layer_forward(bank, x, torch.tensor(ids, dtype=torch.int32).cuda(), g, dtype="f32",
+                                    workspace=wsr)
+        assert torch.equal(y, ref), ids
+    try:
+        for r in range(4):
+            perm = rng.permutation(E_POOL)
+            decode(perm[:4])
+            pool.prefetch(perm[4:6])
+            decode(perm[6:12])
+        assert pool.stats()["prefetches"] > 0
+    finally:
+        pool.close()
