@@ -349,15 +349,25 @@ def run_pool(torch, rvq, bank, w, pool_x, slots_list=(32, 128), tokens=128):
     """Layer decode with the 256 experts in pinned host memory and `slots` device records as the
     LRU cache (rvq expert pool): per token, router top-16 on the device, ids to the host, acquire
     (copies of the missing experts), decode on the slots.  Tokens/s, hit rate and the host-to-device
-    copy rate over the run (copies and decode overlap only through the streams)."""
+    copy rate over the run (copies and decode overlap only through the streams).  The same at the
+    largest slot count over a store of expert records (each record's header checked on every read),
+    and with the payload CRC-32 of every copied expert checked on the device as well."""
     dev = bank.codes.device
     hc = torch.empty(bank.codes.numel(), dtype=torch.uint8, pin_memory=True)
     hc.copy_(bank.codes)
     hb = torch.empty(bank.codebooks.shape, dtype=torch.float32, pin_memory=True)
     hb.copy_(bank.codebooks)
+    crcs = rvq.bank_crc32(bank).cpu().numpy().view(np.uint32)
+    rec = rvq.write_records(bank, 0, crcs)
+    big = max(slots_list)
+    variants = [(f"slots_{s}", lambda s=s: rvq.ExpertPool(hc, hb, bank.E, bank.H, bank.I, s, device=dev))
+                for s in slots_list]
+    variants += [(f"records{'_crc_verify' if v else ''}_slots_{big}",
+                  lambda v=v: rvq.ExpertPool.from_records(rec, 0, bank.E, bank.H, bank.I, big, device=dev, verify=v))
+                 for v in (False, True)]
     out = {}
-    for slots in slots_list:
-        pool = rvq.ExpertPool(hc, hb, bank.E, bank.H, bank.I, slots, device=dev)
+    for name, make in variants:
+        pool = make()
         ws = rvq.make_moe_workspace(pool.bank, 1, K, "f32")
         y = torch.empty(H, dtype=torch.float32, device=dev)
         ids = torch.empty((1, K), dtype=torch.int32, device=dev)
@@ -384,13 +394,15 @@ def run_pool(torch, rvq, bank, w, pool_x, slots_list=(32, 128), tokens=128):
         status = rvq.check_device_status(ws)
         if status:
             raise RuntimeError(rvq.status_string(status))
+        if pool.verify_status() != -1:
+            raise RuntimeError("an expert record failed its payload CRC-32")
         hits, misses = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
-        out[f"slots_{slots}"] = {"tokens_per_s": tokens / sec, "hit_rate": hits / max(1, hits + misses),
+        out[name] = {"tokens_per_s": tokens / sec, "hit_rate": hits / max(1, hits + misses),
                                  "misses_per_token": misses / tokens,
                                  "h2d_GBps": (s1["bytes_copied"] - s0["bytes_copied"]) / sec / 1e9}
         pool.close()
         del pool, ws
-    del hc, hb
+    del hc, hb, rec
     return out
 
 

@@ -54,7 +54,8 @@ typedef enum {
   RVQ_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returned */
   RVQ_ERR_EXPERT_ID = 6,   /* (device status) an expert id outside [0, num_experts) was seen */
   RVQ_ERR_HIP = 7,         /* a HIP runtime call failed */
-  RVQ_ERR_DEVICE_STALL = 8 /* (device status) a kernel's bounded internal wait gave up; outputs invalid */
+  RVQ_ERR_DEVICE_STALL = 8, /* (device status) a kernel's bounded internal wait gave up; outputs invalid */
+  RVQ_ERR_RECORD = 9       /* an expert record failed its header check, or its payload its CRC-32 */
 } rvq_status_t;
 
 typedef enum { RVQ_F32 = 0, RVQ_F16 = 1, RVQ_BF16 = 2 } rvq_dtype_t;
@@ -278,6 +279,62 @@ int rvq_bank_crc32(const rvq_expert_bank_t *bank, uint32_t *crc, void *workspace
                    hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Expert records: the self-describing host form of one expert.
+ *
+ * The pages' container stores each expert as one 4 KiB-aligned block holding
+ * gate, up and down next to each other with their RVQ codebooks and a CRC32
+ * header, read with a single read call ("Running a 2.78-Trillion-Parameter
+ * Model on a Laptop", Technical Insight); every read checks the record's
+ * magic, expert id and offset range, so that a truncated or wrongly joined
+ * bank is refused instead of answering with wrong weights, and a crc32 of the
+ * payload is checked on request; codebooks carry no checksum (news.hada.io
+ * topic 32035, disk-streaming architecture section).
+ *
+ * Layout of a record of rvq_record_bytes(hidden, inter) bytes (all integers
+ * little-endian, as the structure below on this ABI):
+ *   [0, 64)            rvq_record_header_t; the rest of the first 4 KiB is 0
+ *   [4096, +73728)     codebooks, fp32 [3 matrices: gate, up, down][3][256][8]
+ *   [77824, +P)        codes, the packed bank record (P = rvq_bank_record_bytes)
+ *   then zero padding to a multiple of 4096.
+ * The header's offsets and sizes state that layout; a reader trusts only
+ * what rvq_record_check has accepted.
+ * ------------------------------------------------------------------------ */
+#define RVQ_RECORD_MAGIC 0x45515652u /* bytes 'R' 'V' 'Q' 'E' */
+#define RVQ_RECORD_VERSION 1u
+
+typedef struct {
+  uint32_t magic;           /* RVQ_RECORD_MAGIC */
+  uint32_t version;         /* RVQ_RECORD_VERSION */
+  int32_t layer;            /* layer of the expert */
+  int32_t expert;           /* expert id within the layer */
+  int32_t hidden, inter;    /* expert shape H, I */
+  int64_t codebook_offset;  /* bytes from the record start */
+  int64_t codebook_bytes;   /* 73,728 */
+  int64_t codes_offset;     /* bytes from the record start */
+  int64_t codes_bytes;      /* rvq_bank_record_bytes(hidden, inter) */
+  uint32_t payload_crc32;   /* CRC-32 (IEEE 802.3, as rvq_bank_crc32) of the codes */
+  uint32_t reserved;        /* 0 */
+} rvq_record_header_t;      /* 64 bytes */
+
+/* Bytes of one record: 77,824 + rvq_bank_record_bytes, rounded up to 4096
+ * (16,592,896 at hidden 7168, inter 2048); 0 for an invalid shape. */
+size_t rvq_record_bytes(int32_t hidden, int32_t inter);
+
+/* Fills *header (host memory) with the standard layout above.
+ * Errors: RVQ_ERR_NULL, RVQ_ERR_SHAPE (invalid shape, negative layer or id). */
+int rvq_record_header_init(rvq_record_header_t *header, int32_t layer, int32_t expert, int32_t hidden,
+                           int32_t inter, uint32_t payload_crc32);
+
+/* The check the pages apply on every read, on a record in HOST memory of
+ * record_bytes bytes: magic and version; layer, expert id and shape equal to
+ * the expected ones; codebook and code sizes those of the shape; both regions
+ * 16-byte aligned, past the header, disjoint and inside the record.  Reads
+ * only the header; returns RVQ_OK or RVQ_ERR_RECORD (RVQ_ERR_NULL, or
+ * RVQ_ERR_SHAPE for an invalid expected shape).  Needs no GPU. */
+int rvq_record_check(const void *record, int64_t record_bytes, int32_t layer, int32_t expert, int32_t hidden,
+                     int32_t inter);
+
+/* ------------------------------------------------------------------------
  * Expert pool: experts held in pinned host memory, an LRU set of `slots`
  * device records as the cache (the pages' engine streams experts from NVMe
  * into an LRU cache sized to one token's working set and prefetches what the
@@ -292,8 +349,9 @@ int rvq_bank_crc32(const rvq_expert_bank_t *bank, uint32_t *crc, void *workspace
  * slots * record_stride bytes) and slot_codebooks (16-byte aligned, fp32
  * [slots][3][3][256][8]) are device memory the caller owns; an
  * rvq_expert_bank_t over them with num_experts = slots is the bank that the
- * decode entry points use with slot ids.  The pool creates one stream of its
- * own (default priority) for the copies.
+ * decode entry points use with slot ids.  The pool creates streams of its
+ * own (default priority): one for the copies acquire needs, one for
+ * look-ahead copies, and with verify (below) one for the payload checks.
  * rvq_pool_acquire: makes the k experts ids[0..k) (host int32, 1 <= k <=
  * slots) resident and writes their slot ids to slot_ids (host int32 [k]).
  * Missing experts are copied (LRU victim among the slots this call does not
@@ -321,6 +379,33 @@ int rvq_pool_prefetch(rvq_expert_pool_t *pool, const int32_t *ids, int32_t k);
 int rvq_pool_stats(const rvq_expert_pool_t *pool, int64_t *hits, int64_t *misses, int64_t *prefetches,
                    int64_t *bytes_copied);
 int rvq_pool_destroy(rvq_expert_pool_t *pool);
+
+/* Pool over a host store of expert records (the layout above): num_experts
+ * records of record_bytes bytes each (>= rvq_record_bytes(hidden, inter),
+ * multiple of 4096) in pinned host memory, record e holding expert e of
+ * `layer`.  Every copy into a slot (acquire miss or prefetch) first checks
+ * that record with rvq_record_check; acquire returns RVQ_ERR_RECORD for a
+ * record that fails, having copied nothing and changed no state, and
+ * prefetch stops at it with RVQ_ERR_RECORD.  slot_stride: bytes between slot
+ * records in slot_codes (multiple of 256, >= rvq_bank_record_bytes).
+ * verify != 0 adds the pages' optional payload check: after each copy the
+ * CRC-32 of the slot's codes is computed on the device, on the pool's check
+ * stream while the next copy proceeds, and compared with the header's (the
+ * compute stream and the slot's next copy wait for the check); a
+ * mismatch is recorded in verify_workspace (device,
+ * rvq_pool_verify_workspace_bytes(hidden, inter) bytes, 256-byte aligned,
+ * owned by the caller; NULL when verify == 0).  The decode still runs on the
+ * copied bytes: the check reports, it does not repair.
+ * rvq_pool_verify_status: waits for the pool's copies and checks, returns
+ * RVQ_ERR_RECORD and the id of an expert whose payload failed (in
+ * *bad_expert, -1 if none) and clears the record, else RVQ_OK; RVQ_OK with
+ * -1 for a pool without verify.  Synchronises the pool's streams. */
+size_t rvq_pool_verify_workspace_bytes(int32_t hidden, int32_t inter);
+int rvq_pool_create_records(const void *host_records, int64_t record_bytes, int32_t layer, int32_t num_experts,
+                            int32_t hidden, int32_t inter, void *slot_codes, float *slot_codebooks,
+                            int64_t slot_stride, int32_t slots, int32_t verify, void *verify_workspace,
+                            size_t verify_workspace_bytes, rvq_expert_pool_t **out);
+int rvq_pool_verify_status(rvq_expert_pool_t *pool, int32_t *bad_expert);
 
 /* Testing aid for the failure path.  Sets how many times each bounded wait
  * between the wave roles of the table kernels polls before it gives up

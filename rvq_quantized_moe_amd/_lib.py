@@ -19,6 +19,7 @@ _DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
 
 RVQ_OK = 0
 RVQ_ERR_EXPERT_ID = 6
+RVQ_ERR_RECORD = 9
 
 
 class RvqError(RuntimeError):
@@ -37,6 +38,15 @@ class BankDesc(ctypes.Structure):
                 ("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32)]
 
 
+class RecordHeader(ctypes.Structure):
+    """The 64-byte header at the start of an expert record (rvq_record_header_t)."""
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32), ("layer", ctypes.c_int32),
+                ("expert", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("codebook_offset", ctypes.c_int64), ("codebook_bytes", ctypes.c_int64),
+                ("codes_offset", ctypes.c_int64), ("codes_bytes", ctypes.c_int64),
+                ("payload_crc32", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
 _lib = None
 
 EXPORTS = [
@@ -47,6 +57,8 @@ EXPORTS = [
     "rvq_check_device_status", "rvq_moe_decode_routed", "rvq_set_wait_limit", "rvq_moe_block_decode",
     "rvq_moe_batch_decode", "rvq_moe_batch_decode_workspace_bytes", "rvq_bank_crc32", "rvq_bank_crc32_workspace_bytes",
     "rvq_encode", "rvq_pool_create", "rvq_pool_acquire", "rvq_pool_prefetch", "rvq_pool_stats", "rvq_pool_destroy",
+    "rvq_record_bytes", "rvq_record_header_init", "rvq_record_check", "rvq_pool_verify_workspace_bytes",
+    "rvq_pool_create_records", "rvq_pool_verify_status",
 ]
 
 
@@ -98,8 +110,18 @@ def lib():
         L.rvq_pool_prefetch.argtypes = [p, p, i32]
         L.rvq_pool_stats.argtypes = [p, p, p, p, p]
         L.rvq_pool_destroy.argtypes = [p]
+        L.rvq_record_bytes.argtypes = [i32, i32]
+        L.rvq_record_bytes.restype = sz
+        L.rvq_record_header_init.argtypes = [ctypes.POINTER(RecordHeader), i32, i32, i32, i32, ctypes.c_uint32]
+        L.rvq_record_check.argtypes = [p, i64, i32, i32, i32, i32]
+        L.rvq_pool_verify_workspace_bytes.argtypes = [i32, i32]
+        L.rvq_pool_verify_workspace_bytes.restype = sz
+        L.rvq_pool_create_records.argtypes = [p, i64, i32, i32, i32, i32, p, p, i64, i32, i32, p, sz,
+                                              ctypes.POINTER(ctypes.c_void_p)]
+        L.rvq_pool_verify_status.argtypes = [p, ctypes.POINTER(i32)]
         for name in ("rvq_pool_create", "rvq_pool_acquire", "rvq_pool_prefetch", "rvq_pool_stats",
-                     "rvq_pool_destroy"):
+                     "rvq_pool_destroy", "rvq_record_header_init", "rvq_record_check", "rvq_pool_create_records",
+                     "rvq_pool_verify_status"):
             getattr(L, name).restype = ctypes.c_int
         L.rvq_set_wait_limit.restype = i32
         L.rvq_moe_decode_routed.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, p, p, p, p, p, i32, p, sz, p]
@@ -477,6 +499,42 @@ class ExpertPool:
                                      ctypes.byref(handle)))
         self._h = handle
 
+    @classmethod
+    def from_records(cls, records, layer, num_experts, hidden, inter, slots, device="cuda", verify=False,
+                     record_bytes_=None):
+        """Pool over a pinned store of expert records (write_records layout); every copy checks its record's
+        header first; verify also checks each copied payload's CRC-32 on the device (see verify_status)."""
+        if not records.is_pinned():
+            raise ValueError("records must be a pinned host tensor")
+        rb = record_bytes_ or record_bytes(hidden, inter)
+        if records.numel() < num_experts * rb:
+            raise ValueError("record store too small")
+        self = cls.__new__(cls)
+        self.bank = ExpertBank(slots, hidden, inter, device=device)
+        self.host_codes, self.host_codebooks = records, None
+        self.E, self.slots = num_experts, slots
+        self.verify_ws = None
+        if verify:
+            n = lib().rvq_pool_verify_workspace_bytes(hidden, inter)
+            self.verify_ws = torch.empty(n, dtype=torch.uint8, device=device)
+        handle = ctypes.c_void_p()
+        _check(lib().rvq_pool_create_records(_ptr(records), rb, layer, num_experts, hidden, inter,
+                                             _ptr(self.bank.codes), _ptr(self.bank.codebooks), self.bank.stride, slots,
+                                             int(bool(verify)), _ptr(self.verify_ws),
+                                             0 if self.verify_ws is None else self.verify_ws.numel(),
+                                             ctypes.byref(handle)))
+        self._h = handle
+        return self
+
+    def verify_status(self):
+        """Waits for the pool's copies; -1 if every verified payload matched its header's CRC-32, else the id
+        of an expert whose payload did not (the record is then cleared)."""
+        bad = ctypes.c_int32(-1)
+        st = lib().rvq_pool_verify_status(self._h, ctypes.byref(bad))
+        if st not in (RVQ_OK, RVQ_ERR_RECORD):
+            _check(st)
+        return bad.value
+
     def acquire(self, ids):
         """ids: host int sequence [k] -> host int32 slot ids [k]; the current stream waits for copies."""
         a = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).reshape(-1))
@@ -503,6 +561,43 @@ class ExpertPool:
             self.close()
         except Exception:
             pass
+
+
+def record_bytes(hidden, inter):
+    return lib().rvq_record_bytes(hidden, inter)
+
+
+def record_header(layer, expert, hidden, inter, payload_crc32):
+    """The 64 header bytes of an expert record in the standard layout."""
+    h = RecordHeader()
+    _check(lib().rvq_record_header_init(ctypes.byref(h), layer, expert, hidden, inter, payload_crc32))
+    return bytes(h)
+
+
+def record_check(record, layer, expert, hidden, inter):
+    """Status of the read-time header check of one record (host uint8 numpy array or CPU tensor)."""
+    if isinstance(record, torch.Tensor):
+        if record.device.type != "cpu" or record.dtype != torch.uint8 or not record.is_contiguous():
+            raise ValueError("record must be a contiguous CPU uint8 tensor")
+        return lib().rvq_record_check(record.data_ptr(), record.numel(), layer, expert, hidden, inter)
+    a = np.ascontiguousarray(record, dtype=np.uint8)
+    return lib().rvq_record_check(a.ctypes.data, a.size, layer, expert, hidden, inter)
+
+
+def write_records(bank, layer, crcs, out=None):
+    """Expert records of every expert of a device ExpertBank (standard layout) in one pinned uint8 tensor
+    of E * record_bytes bytes; crcs: the payload CRC-32 of each expert's codes (e.g. from bank_crc32)."""
+    rb = record_bytes(bank.H, bank.I)
+    out = torch.zeros(bank.E * rb, dtype=torch.uint8, pin_memory=True) if out is None else out
+    codes = bank.codes.view(bank.E, bank.stride)[:, :bank.record_bytes].cpu()
+    cbs = bank.codebooks.reshape(bank.E, -1).cpu().view(torch.uint8)
+    for e in range(bank.E):
+        rec = out[e * rb:(e + 1) * rb]
+        hdr = RecordHeader.from_buffer_copy(record_header(layer, e, bank.H, bank.I, int(crcs[e])))
+        rec[:64] = torch.frombuffer(bytearray(bytes(hdr)), dtype=torch.uint8)
+        rec[hdr.codebook_offset:hdr.codebook_offset + hdr.codebook_bytes] = cbs[e]
+        rec[hdr.codes_offset:hdr.codes_offset + hdr.codes_bytes] = codes[e]
+    return out
 
 
 def rvq_encode(W, codebooks, codes=None):

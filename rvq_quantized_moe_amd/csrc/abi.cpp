@@ -49,6 +49,7 @@ const char* rvq_status_string(int status) {
     case RVQ_ERR_EXPERT_ID: return "RVQ_ERR_EXPERT_ID: an expert id outside [0, num_experts) was seen";
     case RVQ_ERR_HIP: return "RVQ_ERR_HIP: a HIP runtime call failed";
     case RVQ_ERR_DEVICE_STALL: return "RVQ_ERR_DEVICE_STALL: a kernel's bounded internal wait gave up";
+    case RVQ_ERR_RECORD: return "RVQ_ERR_RECORD: an expert record failed its header or payload check";
     default: return "RVQ: unknown status";
   }
 }

@@ -50,6 +50,10 @@ int64_t crc_payload_bytes(int H, int I);
 size_t crc_workspace_bytes(int E, int H, int I);
 hipError_t launch_bank_crc32(const uint8_t* codes, int64_t stride, int E, int H, int I, uint32_t* crc, void* ws,
                              hipStream_t stream);
+// CRC-32 of one record's codes compared on the device with `expect`; a mismatch stores RVQ_ERR_RECORD
+// and `tag` into status[0..1].  ws: crc_workspace_bytes(1, H, I) bytes.
+hipError_t launch_record_crc_check(const uint8_t* codes, int H, int I, uint32_t expect, int32_t tag, int32_t* status,
+                                   void* ws, hipStream_t stream);
 hipError_t launch_router_norm_logits(const uint16_t* w, const float* h, int E, int H, float eps, double* logits,
                                      float* n, hipStream_t stream);
 hipError_t launch_router_logits(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, double* logits,

@@ -19,19 +19,35 @@
 //  * a slot's copy records an event on its copy stream; the compute stream waits for it once, the
 //    first time the slot is handed out after the copy, and the slot's next copy (on either copy
 //    stream) waits for it too.
+//
+// Record stores: the host store may instead hold self-describing expert records (header, codebooks,
+// codes in one 4 KiB-aligned block, as the pages' container does); each record's header is then
+// checked on the host before any copy from it, and with verify on, the CRC-32 of each slot's codes
+// is compared on the device with the header's.  The checks run on a third stream of the pool's, so
+// the copy engine goes on to the next copy meanwhile; the slot's `loaded` event is then recorded
+// after its check.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <new>
 #include <vector>
 
 #include "../../include/rvq.h"
 #include "device.hpp"
+#include "launch.hpp"
 
 struct rvq_expert_pool {
   const uint8_t* host_codes = nullptr;
   const float* host_cb = nullptr;
-  int64_t stride = 0, payload = 0;
+  int64_t stride = 0, payload = 0;       // host record stride; code bytes per expert
+  int64_t slot_stride = 0;               // bytes between slot records in dev_codes
+  const uint8_t* host_records = nullptr; // record store (else host_codes / host_cb)
+  int32_t layer = 0;
+  bool verify = false;
+  uint8_t* verify_ws = nullptr;          // status words, then the CRC workspace of the check stream
+  hipStream_t check = nullptr;           // payload checks (verify only)
+  hipEvent_t copied[2] = {nullptr, nullptr};   // end of the latest copy on each copy stream
   int E = 0, H = 0, I = 0, S = 0;
   uint8_t* dev_codes = nullptr;
   float* dev_cb = nullptr;
@@ -52,6 +68,22 @@ struct rvq_expert_pool {
 namespace {
 
 constexpr int64_t kCbBytes = 3 * (int64_t)rvq::kCodebookFloats * sizeof(float);   // one expert's codebooks
+constexpr int64_t kRecordAlign = 4096;
+constexpr int64_t kHeaderPage = 4096;                   // header + zero fill
+constexpr int64_t kRecordCodesOffset = kHeaderPage + kCbBytes;
+
+// Verify workspace: [0, 256) two int32 status words; then the CRC block partials of one record.
+int64_t verify_ws_bytes(int H, int I) { return 256 + (int64_t)rvq::crc_workspace_bytes(1, H, I); }
+
+const rvq_record_header_t* header_of(const rvq_expert_pool& p, int e) {
+  return reinterpret_cast<const rvq_record_header_t*>(p.host_records + (int64_t)e * p.stride);
+}
+
+// The read-time check of the record holding expert e (record stores only).
+bool record_ok(const rvq_expert_pool& p, int e) {
+  return !p.host_records ||
+         rvq_record_check(p.host_records + (int64_t)e * p.stride, p.stride, p.layer, e, p.H, p.I) == RVQ_OK;
+}
 
 // Least recently stamped slot that the latest acquire has not handed out (empty slots first); -1 if
 // every slot is in use by it.
@@ -81,39 +113,39 @@ hipError_t load_slot(rvq_expert_pool& p, int s, int e, bool lookahead) {
   if (p.expert_in[s] >= 0) p.slot_of[p.expert_in[s]] = -1;
   p.expert_in[s] = e;
   p.slot_of[e] = s;
-  err = hipMemcpyAsync(p.dev_codes + (int64_t)s * p.stride, p.host_codes + (int64_t)e * p.stride, p.payload,
-                       hipMemcpyHostToDevice, st);
+  const uint8_t* src_codes = p.host_codes + (int64_t)e * p.stride;
+  const uint8_t* src_cb = reinterpret_cast<const uint8_t*>(p.host_cb) + (int64_t)e * kCbBytes;
+  uint32_t crc = 0;
+  if (p.host_records) {   // offsets from the header that record_ok accepted
+    const rvq_record_header_t* h = header_of(p, e);
+    src_codes = p.host_records + (int64_t)e * p.stride + h->codes_offset;
+    src_cb = p.host_records + (int64_t)e * p.stride + h->codebook_offset;
+    crc = h->payload_crc32;
+  }
+  uint8_t* dst_codes = p.dev_codes + (int64_t)s * p.slot_stride;
+  err = hipMemcpyAsync(dst_codes, src_codes, p.payload, hipMemcpyHostToDevice, st);
   if (err == hipSuccess)
-    err = hipMemcpyAsync(reinterpret_cast<uint8_t*>(p.dev_cb) + (int64_t)s * kCbBytes,
-                         reinterpret_cast<const uint8_t*>(p.host_cb) + (int64_t)e * kCbBytes, kCbBytes,
+    err = hipMemcpyAsync(reinterpret_cast<uint8_t*>(p.dev_cb) + (int64_t)s * kCbBytes, src_cb, kCbBytes,
                          hipMemcpyHostToDevice, st);
-  if (err == hipSuccess) err = hipEventRecord(p.loaded[s], st);
+  if (err == hipSuccess && p.verify) {   // the check, on its own stream, after this copy
+    err = hipEventRecord(p.copied[lookahead], st);
+    if (err == hipSuccess) err = hipStreamWaitEvent(p.check, p.copied[lookahead], 0);
+    if (err == hipSuccess)
+      err = rvq::launch_record_crc_check(dst_codes, p.H, p.I, crc, e, reinterpret_cast<int32_t*>(p.verify_ws),
+                                         p.verify_ws + 256, p.check);
+    if (err == hipSuccess) err = hipEventRecord(p.loaded[s], p.check);
+  } else if (err == hipSuccess) {
+    err = hipEventRecord(p.loaded[s], st);
+  }
   p.unwaited[s] = 1;
   p.bytes += p.payload + kCbBytes;
   return err;
 }
 
-}  // namespace
-
-extern "C" {
-
-int rvq_pool_create(const void* host_codes, const float* host_codebooks, int64_t record_stride, int32_t num_experts,
-                    int32_t hidden, int32_t inter, void* slot_codes, float* slot_codebooks, int32_t slots,
-                    rvq_expert_pool_t** out) {
-  if (!out) return RVQ_ERR_NULL;
-  *out = nullptr;
-  if (!host_codes || !host_codebooks || !slot_codes || !slot_codebooks) return RVQ_ERR_NULL;
-  const size_t rec = rvq_bank_record_bytes(hidden, inter);
-  if (rec == 0 || num_experts < 1 || slots < 1 || record_stride < (int64_t)rec) return RVQ_ERR_SHAPE;
-  if (record_stride % 256 != 0 || (reinterpret_cast<uintptr_t>(slot_codes) & 255) != 0 ||
-      (reinterpret_cast<uintptr_t>(slot_codebooks) & 15) != 0)
-    return RVQ_ERR_ALIGN;
-  rvq_expert_pool* p = new (std::nothrow) rvq_expert_pool;
-  if (!p) return RVQ_ERR_HIP;
-  p->host_codes = static_cast<const uint8_t*>(host_codes);
-  p->host_cb = host_codebooks;
-  p->stride = record_stride;
-  p->payload = (int64_t)rec;
+// Shared part of the two constructors: the fields already set on p, then the maps, streams, events
+// and (verify) the cleared status words.
+int finish_create(rvq_expert_pool* p, int32_t num_experts, int32_t hidden, int32_t inter, void* slot_codes,
+                  float* slot_codebooks, int32_t slots, rvq_expert_pool_t** out) {
   p->E = num_experts;
   p->H = hidden;
   p->I = inter;
@@ -130,6 +162,14 @@ int rvq_pool_create(const void* host_codes, const float* host_codebooks, int64_t
             hipStreamCreateWithFlags(&p->ahead, hipStreamNonBlocking) == hipSuccess &&
             hipEventCreateWithFlags(&p->compute_mark, hipEventDisableTiming) == hipSuccess;
   for (int s = 0; ok && s < slots; ++s) ok = hipEventCreateWithFlags(&p->loaded[s], hipEventDisableTiming) == hipSuccess;
+  if (ok && p->verify)
+    ok = hipStreamCreateWithFlags(&p->check, hipStreamNonBlocking) == hipSuccess &&
+         hipEventCreateWithFlags(&p->copied[0], hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&p->copied[1], hipEventDisableTiming) == hipSuccess;
+  if (ok && p->verify) {
+    const int32_t zero[2] = {RVQ_OK, -1};
+    ok = hipMemcpy(p->verify_ws, zero, sizeof zero, hipMemcpyHostToDevice) == hipSuccess;
+  }
   if (!ok) {
     rvq_pool_destroy(p);
     return RVQ_ERR_HIP;
@@ -138,13 +178,140 @@ int rvq_pool_create(const void* host_codes, const float* host_codebooks, int64_t
   return RVQ_OK;
 }
 
+bool slots_aligned(const void* slot_codes, const float* slot_codebooks) {
+  return (reinterpret_cast<uintptr_t>(slot_codes) & 255) == 0 && (reinterpret_cast<uintptr_t>(slot_codebooks) & 15) == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rvq_record_bytes(int32_t hidden, int32_t inter) {
+  const size_t codes = rvq_bank_record_bytes(hidden, inter);
+  if (codes == 0) return 0;
+  return (size_t)((kRecordCodesOffset + (int64_t)codes + kRecordAlign - 1) / kRecordAlign * kRecordAlign);
+}
+
+int rvq_record_header_init(rvq_record_header_t* h, int32_t layer, int32_t expert, int32_t hidden, int32_t inter,
+                           uint32_t payload_crc32) {
+  if (!h) return RVQ_ERR_NULL;
+  const size_t codes = rvq_bank_record_bytes(hidden, inter);
+  if (codes == 0 || layer < 0 || expert < 0) return RVQ_ERR_SHAPE;
+  memset(h, 0, sizeof *h);
+  h->magic = RVQ_RECORD_MAGIC;
+  h->version = RVQ_RECORD_VERSION;
+  h->layer = layer;
+  h->expert = expert;
+  h->hidden = hidden;
+  h->inter = inter;
+  h->codebook_offset = kHeaderPage;
+  h->codebook_bytes = kCbBytes;
+  h->codes_offset = kRecordCodesOffset;
+  h->codes_bytes = (int64_t)codes;
+  h->payload_crc32 = payload_crc32;
+  return RVQ_OK;
+}
+
+int rvq_record_check(const void* record, int64_t record_bytes, int32_t layer, int32_t expert, int32_t hidden,
+                     int32_t inter) {
+  if (!record) return RVQ_ERR_NULL;
+  const size_t codes = rvq_bank_record_bytes(hidden, inter);
+  if (codes == 0 || layer < 0 || expert < 0) return RVQ_ERR_SHAPE;
+  rvq_record_header_t h;
+  if (record_bytes < (int64_t)sizeof h) return RVQ_ERR_RECORD;
+  memcpy(&h, record, sizeof h);
+  if (h.magic != RVQ_RECORD_MAGIC || h.version != RVQ_RECORD_VERSION) return RVQ_ERR_RECORD;
+  if (h.layer != layer || h.expert != expert || h.hidden != hidden || h.inter != inter) return RVQ_ERR_RECORD;
+  if (h.codebook_bytes != kCbBytes || h.codes_bytes != (int64_t)codes) return RVQ_ERR_RECORD;
+  // regions: past the header, 16-byte aligned, inside the record (no overflow: sizes are known and
+  // positive, offsets compared before subtracting), and disjoint
+  const auto inside = [&](int64_t off, int64_t n) {
+    return off >= (int64_t)sizeof h && off % 16 == 0 && off <= record_bytes && n <= record_bytes - off;
+  };
+  if (!inside(h.codebook_offset, h.codebook_bytes) || !inside(h.codes_offset, h.codes_bytes)) return RVQ_ERR_RECORD;
+  if (h.codebook_offset < h.codes_offset + h.codes_bytes && h.codes_offset < h.codebook_offset + h.codebook_bytes)
+    return RVQ_ERR_RECORD;
+  return RVQ_OK;
+}
+
+int rvq_pool_create(const void* host_codes, const float* host_codebooks, int64_t record_stride, int32_t num_experts,
+                    int32_t hidden, int32_t inter, void* slot_codes, float* slot_codebooks, int32_t slots,
+                    rvq_expert_pool_t** out) {
+  if (!out) return RVQ_ERR_NULL;
+  *out = nullptr;
+  if (!host_codes || !host_codebooks || !slot_codes || !slot_codebooks) return RVQ_ERR_NULL;
+  const size_t rec = rvq_bank_record_bytes(hidden, inter);
+  if (rec == 0 || num_experts < 1 || slots < 1 || record_stride < (int64_t)rec) return RVQ_ERR_SHAPE;
+  if (record_stride % 256 != 0 || !slots_aligned(slot_codes, slot_codebooks)) return RVQ_ERR_ALIGN;
+  rvq_expert_pool* p = new (std::nothrow) rvq_expert_pool;
+  if (!p) return RVQ_ERR_HIP;
+  p->host_codes = static_cast<const uint8_t*>(host_codes);
+  p->host_cb = host_codebooks;
+  p->stride = record_stride;
+  p->slot_stride = record_stride;
+  p->payload = (int64_t)rec;
+  return finish_create(p, num_experts, hidden, inter, slot_codes, slot_codebooks, slots, out);
+}
+
+size_t rvq_pool_verify_workspace_bytes(int32_t hidden, int32_t inter) {
+  if (rvq_bank_record_bytes(hidden, inter) == 0) return 0;
+  return (size_t)verify_ws_bytes(hidden, inter);
+}
+
+int rvq_pool_create_records(const void* host_records, int64_t record_bytes, int32_t layer, int32_t num_experts,
+                            int32_t hidden, int32_t inter, void* slot_codes, float* slot_codebooks,
+                            int64_t slot_stride, int32_t slots, int32_t verify, void* verify_workspace,
+                            size_t verify_workspace_bytes, rvq_expert_pool_t** out) {
+  if (!out) return RVQ_ERR_NULL;
+  *out = nullptr;
+  if (!host_records || !slot_codes || !slot_codebooks || (verify && !verify_workspace)) return RVQ_ERR_NULL;
+  const size_t rec = rvq_record_bytes(hidden, inter);
+  const size_t payload = rvq_bank_record_bytes(hidden, inter);
+  if (rec == 0 || layer < 0 || num_experts < 1 || slots < 1 || record_bytes < (int64_t)rec ||
+      slot_stride < (int64_t)payload)
+    return RVQ_ERR_SHAPE;
+  if (record_bytes % kRecordAlign != 0 || slot_stride % 256 != 0 || !slots_aligned(slot_codes, slot_codebooks) ||
+      (verify && (reinterpret_cast<uintptr_t>(verify_workspace) & 255) != 0))
+    return RVQ_ERR_ALIGN;
+  if (verify && verify_workspace_bytes < rvq_pool_verify_workspace_bytes(hidden, inter)) return RVQ_ERR_WORKSPACE;
+  rvq_expert_pool* p = new (std::nothrow) rvq_expert_pool;
+  if (!p) return RVQ_ERR_HIP;
+  p->host_records = static_cast<const uint8_t*>(host_records);
+  p->stride = record_bytes;
+  p->slot_stride = slot_stride;
+  p->payload = (int64_t)payload;
+  p->layer = layer;
+  p->verify = verify != 0;
+  p->verify_ws = static_cast<uint8_t*>(verify_workspace);
+  return finish_create(p, num_experts, hidden, inter, slot_codes, slot_codebooks, slots, out);
+}
+
+int rvq_pool_verify_status(rvq_expert_pool_t* p, int32_t* bad_expert) {
+  if (!p || !bad_expert) return RVQ_ERR_NULL;
+  *bad_expert = -1;
+  if (hipStreamSynchronize(p->copy) != hipSuccess || hipStreamSynchronize(p->ahead) != hipSuccess) return RVQ_ERR_HIP;
+  if (!p->verify) return RVQ_OK;
+  if (hipStreamSynchronize(p->check) != hipSuccess) return RVQ_ERR_HIP;
+  int32_t st[2];
+  if (hipMemcpy(st, p->verify_ws, sizeof st, hipMemcpyDeviceToHost) != hipSuccess) return RVQ_ERR_HIP;
+  if (st[0] == RVQ_OK) return RVQ_OK;
+  *bad_expert = st[1];
+  const int32_t zero[2] = {RVQ_OK, -1};
+  if (hipMemcpy(p->verify_ws, zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess) return RVQ_ERR_HIP;
+  return RVQ_ERR_RECORD;
+}
+
 int rvq_pool_destroy(rvq_expert_pool_t* p) {
   if (!p) return RVQ_ERR_NULL;
   int st = RVQ_OK;
   if (p->copy && hipStreamSynchronize(p->copy) != hipSuccess) st = RVQ_ERR_HIP;
   if (p->ahead && hipStreamSynchronize(p->ahead) != hipSuccess) st = RVQ_ERR_HIP;
+  if (p->check && hipStreamSynchronize(p->check) != hipSuccess) st = RVQ_ERR_HIP;
   for (hipEvent_t e : p->loaded)
     if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->copied)
+    if (e) (void)hipEventDestroy(e);
+  if (p->check) (void)hipStreamDestroy(p->check);
   if (p->compute_mark) (void)hipEventDestroy(p->compute_mark);
   if (p->copy) (void)hipStreamDestroy(p->copy);
   if (p->ahead) (void)hipStreamDestroy(p->ahead);
@@ -157,6 +324,8 @@ int rvq_pool_acquire(rvq_expert_pool_t* p, const int32_t* ids, int32_t k, int32_
   if (k < 1 || k > p->S) return RVQ_ERR_SHAPE;
   for (int i = 0; i < k; ++i)
     if (ids[i] < 0 || ids[i] >= p->E) return RVQ_ERR_EXPERT_ID;
+  for (int i = 0; i < k; ++i)   // every record this call would read, before any state changes
+    if (p->slot_of[ids[i]] < 0 && !record_ok(*p, ids[i])) return RVQ_ERR_RECORD;
   const int64_t a = ++p->acquires;
   hipError_t err = hipEventRecord(p->compute_mark, stream);
   if (err != hipSuccess) return RVQ_ERR_HIP;
@@ -198,6 +367,7 @@ int rvq_pool_prefetch(rvq_expert_pool_t* p, const int32_t* ids, int32_t k) {
     const int e = ids[i];
     if (e < 0 || e >= p->E) return RVQ_ERR_EXPERT_ID;
     if (p->slot_of[e] >= 0) continue;
+    if (!record_ok(*p, e)) return RVQ_ERR_RECORD;
     const int s = pick_victim(*p, p->acquires);
     if (s < 0) break;   // every slot is held by the latest acquire
     if (load_slot(*p, s, e, true) != hipSuccess) return RVQ_ERR_HIP;

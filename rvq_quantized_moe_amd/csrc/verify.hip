@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/rvq.h"
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -111,9 +112,12 @@ __global__ __launch_bounds__(256) void k_crc_blocks(const uint8_t* __restrict__ 
   if (lane == 0) blk[w] = r;
 }
 
-// One wave per record: fold its blocks, then the preset register and the final complement.
+// One wave per record: fold its blocks, then the preset register and the final complement.  With a
+// status word the CRC is not stored but compared with `expect`: a mismatch stores the record-error
+// code and `tag` into status[0..1].
 __global__ __launch_bounds__(64) void k_crc_finish(const uint32_t* __restrict__ blk, int64_t nspans, int nblocks,
-                                                   uint32_t* __restrict__ crc, CrcConsts cc) {
+                                                   uint32_t* __restrict__ crc, CrcConsts cc, uint32_t expect,
+                                                   int32_t tag, int32_t* __restrict__ status) {
   const int e = blockIdx.x, lane = threadIdx.x;
   uint32_t acc = 0;
   for (int b = lane; b < nblocks; b += 64) {
@@ -122,7 +126,15 @@ __global__ __launch_bounds__(64) void k_crc_finish(const uint32_t* __restrict__ 
     acc ^= gf_mul(blk[(int64_t)e * nblocks + b], shift_spans(after, cc.pow2));
   }
   acc = wave_xor(acc);
-  if (lane == 0) crc[e] = ~(acc ^ gf_mul(0xFFFFFFFFu, shift_spans(nspans, cc.pow2)));
+  if (lane == 0) {
+    const uint32_t c = ~(acc ^ gf_mul(0xFFFFFFFFu, shift_spans(nspans, cc.pow2)));
+    if (!status) {
+      crc[e] = c;
+    } else if (c != expect) {
+      status[0] = RVQ_ERR_RECORD;
+      status[1] = tag;
+    }
+  }
 }
 
 static CrcConsts crc_consts() {
@@ -143,8 +155,8 @@ size_t crc_workspace_bytes(int E, int H, int I) {
   return (size_t)((E * nblocks * 4 + 255) / 256 * 256);
 }
 
-hipError_t launch_bank_crc32(const uint8_t* codes, int64_t stride, int E, int H, int I, uint32_t* crc, void* ws,
-                             hipStream_t stream) {
+static hipError_t crc_records(const uint8_t* codes, int64_t stride, int E, int H, int I, uint32_t* crc, void* ws,
+                              uint32_t expect, int32_t tag, int32_t* status, hipStream_t stream) {
   static const CrcConsts cc = crc_consts();
   const int64_t payload = crc_payload_bytes(H, I);   // a multiple of the 3072-byte slab, so of kCrcSpan
   const int64_t nspans = payload / kCrcSpan;
@@ -153,8 +165,19 @@ hipError_t launch_bank_crc32(const uint8_t* codes, int64_t stride, int E, int H,
   const int64_t waves = (int64_t)E * nblocks;
   hipLaunchKernelGGL(k_crc_blocks, dim3((unsigned)cdiv(waves, 4)), dim3(256), 0, stream, codes, stride, nspans, nblocks,
                      E, blk, cc);
-  hipLaunchKernelGGL(k_crc_finish, dim3((unsigned)E), dim3(64), 0, stream, blk, nspans, nblocks, crc, cc);
+  hipLaunchKernelGGL(k_crc_finish, dim3((unsigned)E), dim3(64), 0, stream, blk, nspans, nblocks, crc, cc, expect, tag,
+                     status);
   return hipGetLastError();
+}
+
+hipError_t launch_bank_crc32(const uint8_t* codes, int64_t stride, int E, int H, int I, uint32_t* crc, void* ws,
+                             hipStream_t stream) {
+  return crc_records(codes, stride, E, H, I, crc, ws, 0, 0, nullptr, stream);
+}
+
+hipError_t launch_record_crc_check(const uint8_t* codes, int H, int I, uint32_t expect, int32_t tag, int32_t* status,
+                                   void* ws, hipStream_t stream) {
+  return crc_records(codes, 0, 1, H, I, nullptr, ws, expect, tag, status, stream);
 }
 
 }  // namespace rvq

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(8):
+    for s in range(10):
         txt = rvq.status_string(s)
         assert txt.startswith("RVQ_")
     assert "unknown" in rvq.status_string(99)
@@ -326,3 +326,122 @@ def test_stream_copy_validation(L):
     assert L.rvq_stream_copy(FAKE, FAKE2, 17, s) == SHAPE
     assert L.rvq_stream_copy(FAKE + 4, FAKE2, 16, s) == ALIGN
     assert L.rvq_stream_copy(FAKE, FAKE2, 0, s) == OK
+
+
+# ---- expert records (host-only: header layout and the read-time check) ----
+REC_H, REC_I = 256, 128        # small shape: packed codes 36,864 B, record exactly 114,688 B (no padding)
+RECORD = 9
+
+
+def _spec_header(layer, expert, H, I, crc, codes_bytes):
+    """The header as the documented layout states it, packed independently of the library."""
+    import struct
+    return struct.pack("<IIiiiiqqqqII", 0x45515652, 1, layer, expert, H, I, 4096, 73728, 4096 + 73728, codes_bytes,
+                       crc, 0)
+
+
+def _record(layer=3, expert=5, crc=0xDEADBEEF):
+    rb = rvq.record_bytes(REC_H, REC_I)
+    rec = np.zeros(rb, dtype=np.uint8)
+    rec[:64] = np.frombuffer(rvq.record_header(layer, expert, REC_H, REC_I, crc), dtype=np.uint8)
+    return rec
+
+
+def test_record_layout_matches_the_documented_header(L):
+    cb = L.rvq_bank_record_bytes(REC_H, REC_I)
+    assert cb == 36864
+    assert rvq.record_bytes(REC_H, REC_I) == 114688
+    assert rvq.record_bytes(7168, 2048) == 16_592_896 == 4051 * 4096
+    assert rvq.record_bytes(7168, 2048) - 77824 == L.rvq_bank_record_bytes(7168, 2048)
+    assert ctypes.sizeof(rvq.RecordHeader) == 64
+    assert rvq.record_header(3, 5, REC_H, REC_I, 0xDEADBEEF) == _spec_header(3, 5, REC_H, REC_I, 0xDEADBEEF, cb)
+    assert rvq.record_header(91, 255, 7168, 2048, 1) == _spec_header(91, 255, 7168, 2048, 1, 16_515_072)
+    h = rvq.RecordHeader()
+    assert L.rvq_record_header_init(None, 0, 0, REC_H, REC_I, 0) == NULL
+    assert L.rvq_record_header_init(ctypes.byref(h), -1, 0, REC_H, REC_I, 0) == SHAPE
+    assert L.rvq_record_header_init(ctypes.byref(h), 0, -1, REC_H, REC_I, 0) == SHAPE
+    assert L.rvq_record_header_init(ctypes.byref(h), 0, 0, REC_H, 12, 0) == SHAPE
+    assert rvq.record_bytes(REC_H, 12) == 0
+
+
+def test_record_check_accepts_the_standard_record(L):
+    rec = _record()
+    assert rvq.record_check(rec, 3, 5, REC_H, REC_I) == OK
+    # the check reads the header only: payload bytes and the CRC field are not its business
+    rec[4096:] = 0xA5
+    assert rvq.record_check(rec, 3, 5, REC_H, REC_I) == OK
+    # a record longer than the layout needs (padding after the codes) is fine
+    assert rvq.record_check(np.concatenate([rec, np.zeros(4096, np.uint8)]), 3, 5, REC_H, REC_I) == OK
+
+
+def test_record_check_refuses_wrong_identity_and_truncation(L):
+    rec = _record()
+    assert rvq.record_check(rec, 4, 5, REC_H, REC_I) == RECORD          # another layer's record
+    assert rvq.record_check(rec, 3, 6, REC_H, REC_I) == RECORD          # wrongly joined: expert 5 in slot 6
+    assert rvq.record_check(rec, 3, 5, 512, REC_I) == RECORD            # another shape
+    assert rvq.record_check(rec[:-1], 3, 5, REC_H, REC_I) == RECORD     # truncated by one byte
+    assert rvq.record_check(rec[:4096], 3, 5, REC_H, REC_I) == RECORD   # header page only
+    assert rvq.record_check(rec[:63], 3, 5, REC_H, REC_I) == RECORD     # not even a header
+    assert rvq.record_check(np.zeros_like(rec), 3, 5, REC_H, REC_I) == RECORD
+    assert L.rvq_record_check(None, rec.size, 3, 5, REC_H, REC_I) == NULL
+    assert rvq.record_check(rec, -1, 5, REC_H, REC_I) == SHAPE
+    assert rvq.record_check(rec, 3, 5, REC_H, 12) == SHAPE
+
+
+def test_record_check_refuses_every_single_bit_flip_of_the_checked_fields(L):
+    """At a record with no padding every field the check reads is pinned: flipping any one of the 448
+    bits of the first 56 bytes (magic .. codes_bytes) is refused; the CRC and reserved words are not
+    checked here."""
+    rec = _record()
+    for byte in range(64):
+        for bit in range(8):
+            r = rec.copy()
+            r[byte] ^= np.uint8(1 << bit)
+            want = RECORD if byte < 56 else OK
+            assert rvq.record_check(r, 3, 5, REC_H, REC_I) == want, (byte, bit)
+
+
+def test_record_check_offset_range_edge_cases(L):
+    import struct
+    cb = L.rvq_bank_record_bytes(REC_H, REC_I)
+    rb = rvq.record_bytes(REC_H, REC_I)
+
+    def with_offsets(cb_off, codes_off, size=rb):
+        r = np.zeros(size, dtype=np.uint8)
+        r[:64] = np.frombuffer(struct.pack("<IIiiiiqqqqII", 0x45515652, 1, 3, 5, REC_H, REC_I, cb_off, 73728,
+                                           codes_off, cb, 0, 0), dtype=np.uint8)
+        return rvq.record_check(r, 3, 5, REC_H, REC_I)
+    assert with_offsets(4096, 77824) == OK
+    assert with_offsets(64, 64 + 73728) == OK                   # packed right after the header
+    assert with_offsets(64 + cb, 64) == OK                      # codes first, then codebooks
+    assert with_offsets(48, 77824) == RECORD                    # over the header
+    assert with_offsets(4096, 77824 - 16) == RECORD             # regions overlap by 16 bytes
+    assert with_offsets(4096, rb - cb + 16) == RECORD           # codes run 16 bytes past the end
+    assert with_offsets(4096, 2 ** 62) == RECORD                # offset far out (no overflow)
+    assert with_offsets(4096, -4096) == RECORD                  # negative offset
+    assert with_offsets(2 ** 63 - 16, 77824) == RECORD          # offset + size would overflow
+    assert with_offsets(4104, 77824) == RECORD                  # not 16-byte aligned
+
+
+def test_record_pool_validation(L):
+    out = ctypes.c_void_p()
+    c = L.rvq_pool_create_records
+    rb = rvq.record_bytes(7168, 2048)
+    vw = L.rvq_pool_verify_workspace_bytes(7168, 2048)
+    assert vw >= 256 + 2 * 256 and vw % 256 == 0
+    assert L.rvq_pool_verify_workspace_bytes(7168, 12) == 0
+    ok = [FAKE, rb, 0, 32, 7168, 2048, FAKE, FAKE2, 16_515_072, 8, 1, FAKE2 + 0x100000, vw]
+    assert c(*ok, None) == NULL
+    assert c(None, *ok[1:], ctypes.byref(out)) == NULL
+    assert c(*ok[:11], None, vw, ctypes.byref(out)) == NULL                  # verify without a workspace
+    assert c(*ok[:1], rb - 4096, *ok[2:], ctypes.byref(out)) == SHAPE        # records shorter than the layout
+    assert c(*ok[:1], rb + 256, *ok[2:], ctypes.byref(out)) == ALIGN         # record stride not 4 KiB
+    assert c(*ok[:2], -1, *ok[3:], ctypes.byref(out)) == SHAPE               # negative layer
+    assert c(*ok[:9], 0, *ok[10:], ctypes.byref(out)) == SHAPE               # no slots
+    assert c(*ok[:8], 16_515_072 - 256, *ok[9:], ctypes.byref(out)) == SHAPE  # slot stride below the payload
+    assert c(*ok[:8], 16_515_072 + 16, *ok[9:], ctypes.byref(out)) == ALIGN   # slot stride not 256
+    assert c(*ok[:11], FAKE2 + 0x100010, vw, ctypes.byref(out)) == ALIGN      # workspace alignment
+    assert c(*ok[:12], vw - 1, ctypes.byref(out)) == WS
+    assert out.value is None
+    bad = ctypes.c_int32()
+    assert L.rvq_pool_verify_status(None, ctypes.byref(bad)) == NULL

@@ -1,12 +1,14 @@
 """Expert pool (experts in pinned host memory, an LRU set of device slots): decoding through the
 pool's slots gives the all-resident result bit for bit, and the hit/miss accounting follows the
-LRU policy, computed independently here."""
+LRU policy, computed independently here.  Over a store of expert records, every read checks the
+record's header and, with verify on, the payload's CRC-32 against the oracle's."""
 import sys
 
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import rvq_quantized_moe_amd as rvq
 import synth
 from workloads import HIDDEN, INTER, router, upload_bank
@@ -186,3 +188,122 @@ def test_pool_evicts_slots_with_lookahead_copies_in_flight(store):
         assert pool.stats()["prefetches"] > 0
     finally:
         pool.close()
+
+
+REC_LAYER = 17
+
+
+@pytest.fixture(scope="module")
+def records(store):
+    """The 24 experts as records of layer 17, header CRCs computed by the oracle from the packed codes."""
+    bank = store[0]
+    say("write the pool's experts as records")
+    codes = bank.codes.view(E_POOL, bank.stride)[:, :bank.record_bytes].cpu().numpy()
+    crcs = [oracle.crc32(codes[e]) for e in range(E_POOL)]
+    return rvq.write_records(bank, REC_LAYER, crcs), crcs
+
+
+def _decode_both(pool, bank, ids, x, ws, wsr, rng):
+    g = torch.from_numpy(rng.random(len(ids)).astype(np.float32)).cuda()
+    slot = pool.acquire(ids)
+    y = rvq.moe_layer_forward(pool.bank, x, torch.from_numpy(slot).cuda(), g, dtype="f32", workspace=ws)
+    ref = rvq.moe_layer_forward(bank, x, torch.tensor(np.asarray(ids), dtype=torch.int32).cuda(), g, dtype="f32",
+                                workspace=wsr)
+    return y, ref
+
+
+@pytest.mark.parametrize("verify", [False, True])
+def test_record_pool_matches_resident_bank(store, records, verify):
+    """Slots filled from records (header checked on every read; with verify, each payload's CRC-32 too)
+    decode exactly as the resident bank; clean records report no CRC failure."""
+    bank = store[0]
+    rec, _ = records
+    say(f"record pool verify={verify}")
+    pool = rvq.ExpertPool.from_records(rec, REC_LAYER, E_POOL, HIDDEN, INTER, 6, verify=verify)
+    ws = rvq.make_moe_workspace(pool.bank, 1, 4, "f32")
+    wsr = rvq.make_moe_workspace(bank, 1, 4, "f32")
+    rng = np.random.default_rng(11)
+    x = torch.from_numpy(synth.activation_f32(synth.SEED_EXPERT ^ 0x5, 91, HIDDEN)).cuda()
+    try:
+        for r in range(5):
+            perm = rng.permutation(E_POOL)
+            y, ref = _decode_both(pool, bank, perm[:4], x, ws, wsr, rng)
+            assert torch.equal(y, ref), r
+            pool.prefetch(perm[4:6])
+        assert pool.verify_status() == -1
+        assert pool.stats()["misses"] > 0
+    finally:
+        pool.close()
+
+
+def test_record_pool_refuses_bad_headers(store, records):
+    """A record with a damaged magic, one carrying another expert's header (a wrongly joined store) and
+    one whose code offset runs past its end are refused on read: the acquire that needs them copies
+    nothing and changes no state; other records still load."""
+    bank = store[0]
+    rec, _ = records
+    rb = rvq.record_bytes(HIDDEN, INTER)
+    say("record pool: damaged headers")
+    saved = {e: rec[e * rb:e * rb + 64].clone() for e in (3, 7, 9)}
+    rec[3 * rb] ^= 0xFF                                                   # magic
+    rec[7 * rb:7 * rb + 64] = rec[8 * rb:8 * rb + 64]                     # expert 8's header in record 7
+    hdr = rvq.RecordHeader.from_buffer_copy(bytes(rec[9 * rb:9 * rb + 64].numpy()))
+    hdr.codes_offset = rb - hdr.codes_bytes + 4096                        # past the record's end
+    rec[9 * rb:9 * rb + 64] = torch.frombuffer(bytearray(bytes(hdr)), dtype=torch.uint8)
+    pool = rvq.ExpertPool.from_records(rec, REC_LAYER, E_POOL, HIDDEN, INTER, 6)
+    ws = rvq.make_moe_workspace(pool.bank, 1, 4, "f32")
+    wsr = rvq.make_moe_workspace(bank, 1, 4, "f32")
+    rng = np.random.default_rng(12)
+    x = torch.from_numpy(synth.activation_f32(synth.SEED_EXPERT ^ 0x5, 92, HIDDEN)).cuda()
+    try:
+        for bad in (3, 7, 9):
+            with pytest.raises(rvq.RvqError) as ei:
+                pool.acquire([0, bad])
+            assert ei.value.status == rvq._lib.RVQ_ERR_RECORD
+        assert pool.stats() == {"hits": 0, "misses": 0, "prefetches": 0, "bytes_copied": 0}
+        y, ref = _decode_both(pool, bank, [0, 1, 2, 8], x, ws, wsr, rng)
+        assert torch.equal(y, ref)
+        with pytest.raises(rvq.RvqError):
+            pool.prefetch([4, 7, 5])   # copies 4, stops at 7
+        assert pool.stats()["prefetches"] == 1
+        y, ref = _decode_both(pool, bank, [4, 1, 10, 11], x, ws, wsr, rng)
+        assert torch.equal(y, ref)
+        assert pool.stats()["hits"] == 2
+    finally:
+        pool.close()
+        for e, h in saved.items():
+            rec[e * rb:e * rb + 64] = h
+
+
+def test_record_pool_verify_reports_a_corrupt_payload(store, records):
+    """One flipped byte in expert 5's codes (header intact, CRC of the clean payload): the header check
+    passes, the device CRC check on the copy stream reports expert 5, once; loads of clean records
+    report nothing; a pool without verify does not check."""
+    bank = store[0]
+    rec, crcs = records
+    rb = rvq.record_bytes(HIDDEN, INTER)
+    hdr = rvq.RecordHeader.from_buffer_copy(bytes(rec[5 * rb:5 * rb + 64].numpy()))
+    pos = 5 * rb + hdr.codes_offset + 1_234_567
+    say("record pool: corrupt payload under verify")
+    rec[pos] ^= 0x10
+    try:
+        pool = rvq.ExpertPool.from_records(rec, REC_LAYER, E_POOL, HIDDEN, INTER, 4, verify=True)
+        try:
+            pool.acquire([1, 2])
+            assert pool.verify_status() == -1
+            pool.acquire([5, 6])
+            assert pool.verify_status() == 5
+            assert pool.verify_status() == -1   # reported once, then cleared
+            pool.prefetch([7])
+            pool.acquire([7, 8])
+            assert pool.verify_status() == -1
+        finally:
+            pool.close()
+        plain = rvq.ExpertPool.from_records(rec, REC_LAYER, E_POOL, HIDDEN, INTER, 4, verify=False)
+        try:
+            plain.acquire([5])
+            assert plain.verify_status() == -1
+        finally:
+            plain.close()
+    finally:
+        rec[pos] ^= 0x10
