@@ -24,6 +24,10 @@ module marshals numpy arrays and composes the per-layer steps:
   crc32(bytes)   = CRC-32 (IEEE 802.3, reflected, preset and final complement) of a
                    record's code payload, bit by bit (news.hada.io topic 32035,
                    disk-streaming architecture section: optional payload crc32)
+  rvq_fit(W)     = codebooks [3, 256, 8] and codes of W by residual k-means: per stage,
+                   Lloyd iterations from given initial sub-vectors (nearest entry as in
+                   rvq_encode; means in fp64 over runs of 2048 sub-vectors, then across
+                   runs, in ascending order), then the stage's codes and its residual
 
 Parity status of each function (what pins it) is listed in tests/test_oracle_pins.py.
 """
@@ -67,6 +71,8 @@ def _load():
         lib.orc_rmsnorm.argtypes = [p, i64, ctypes.c_double, p]
         lib.orc_rvq_encode.argtypes = [p, i64, i64, p, p]
         lib.orc_crc32.argtypes = [p, i64]
+        lib.orc_rvq_fit.argtypes = [p, i64, i64, i32, p, p, p, i32]
+        lib.orc_rvq_fit.restype = None
         lib.orc_crc32.restype = ctypes.c_uint32
         _lib = lib
     return _lib
@@ -264,3 +270,20 @@ def rvq_encode(W, codebooks):
     codes = np.empty((rows, cols // 8, 3), dtype=np.uint8)
     _load().orc_rvq_encode(W.ctypes.data, rows, cols, cb.ctypes.data, codes.ctypes.data)
     return codes
+
+
+def rvq_fit(W, iters, init_idx, threads=None):
+    """Residual k-means codebooks of W (fp32 [rows, cols]): iters Lloyd iterations per stage from the
+    residual sub-vectors init_idx[s] (int [3, 256], row-major sub-vector indices).  Returns
+    (codebooks fp32 [3, 256, 8], codes uint8 [rows, cols/8, 3])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    rows, cols = W.shape
+    init = np.ascontiguousarray(init_idx, dtype=np.int32).reshape(3, 256)
+    n = rows * (cols // 8)
+    if init.min() < 0 or init.max() >= n:
+        raise ValueError("init_idx out of range")
+    cb = np.empty((3, 256, 8), dtype=np.float32)
+    codes = np.empty((rows, cols // 8, 3), dtype=np.uint8)
+    _load().orc_rvq_fit(W.ctypes.data, rows, cols, int(iters), init.ctypes.data, cb.ctypes.data, codes.ctypes.data,
+                        int(threads or min(16, os.cpu_count() or 1)))
+    return cb, codes

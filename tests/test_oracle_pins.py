@@ -373,3 +373,130 @@ def test_rvq_encode_exact_entries_and_reencode():
     c0 = rng.integers(0, 256, (20, 6, 3)).astype(np.uint8)
     W2 = oracle.dequant(c0, cb2, 20, 48).astype(np.float32)
     assert np.array_equal(oracle.rvq_encode(W2, cb2), c0)
+
+
+# ---------------------------------------------------------------- RVQ codebook fit (residual k-means)
+
+def _lattice_data(seed):
+    """Sub-vectors S0[c0] + S1[c1] + S2[c2] over the full product of 256 x 8 x 5 entries, shuffled.
+    S0: 1024 x distinct integer vectors (clusters far apart); S1 = {+-v1..+-v4} (components +-8, +-16),
+    S2 = {0, +-u1, +-u2} (components +-0.5, +-1): both of mean zero, so each stage's clusters have
+    their stage entry as exact mean, and every value and sum is exact in fp32 and fp64."""
+    rng = np.random.default_rng(seed)
+    S0 = set()
+    while len(S0) < 256:
+        S0.add(tuple(rng.integers(-3, 4, 8)))
+    S0 = 1024.0 * np.array(sorted(S0), dtype=np.float64)
+    v = rng.choice([-16.0, -8.0, 8.0, 16.0], size=(4, 8))
+    S1 = np.concatenate([v, -v])
+    u = rng.choice([-1.0, -0.5, 0.5, 1.0], size=(2, 8))
+    S2 = np.concatenate([np.zeros((1, 8)), u, -u])
+    assert len({tuple(r) for r in S1}) == 8 and len({tuple(r) for r in S2}) == 5
+    digits = np.array([(a, b, c) for a in range(256) for b in range(8) for c in range(5)])
+    digits = digits[rng.permutation(len(digits))]
+    X = S0[digits[:, 0]] + S1[digits[:, 1]] + S2[digits[:, 2]]
+    return X.astype(np.float32).reshape(160, 512), digits, (S0, S1, S2)
+
+
+def _first_with(digits, **want):
+    cols = {"s0": 0, "s1": 1, "s2": 2}
+    m = np.ones(len(digits), bool)
+    for k, v in want.items():
+        m &= digits[:, cols[k]] == v
+    return int(np.flatnonzero(m)[0])
+
+
+@pytest.mark.parametrize("iters", [1, 3])
+def test_rvq_fit_recovers_a_separated_balanced_lattice(iters):
+    """Stage 0 starts each centroid at a member away from its cluster's centre (S0[k] + v1 + u1) and
+    must reach the exact centre in one Lloyd iteration (the mean of 40 members); stages 1 and 2
+    start at residuals equal to their entries (repeated over the 256 centroids, the copies with higher
+    index staying empty), which only the correct residual makes exact.  Codes = the digits, and the
+    fitted codebooks rebuild every sub-vector exactly."""
+    W, digits, (S0, S1, S2) = _lattice_data(21)
+    init = np.zeros((3, 256), np.int32)
+    for c in range(256):
+        init[0, c] = _first_with(digits, s0=c, s1=0, s2=1)
+        init[1, c] = _first_with(digits, s1=c % 8, s2=0)
+        init[2, c] = _first_with(digits, s2=c % 5)
+    cb, codes = oracle.rvq_fit(W, iters, init)
+    assert np.array_equal(cb[0], S0.astype(np.float32))
+    assert np.array_equal(cb[1], S1[np.arange(256) % 8].astype(np.float32))
+    assert np.array_equal(cb[2], S2[np.arange(256) % 5].astype(np.float32))
+    assert np.array_equal(codes.reshape(-1, 3), digits)
+    rebuilt = (cb[0][codes[..., 0]] + cb[1][codes[..., 1]] + cb[2][codes[..., 2]]).reshape(W.shape)
+    assert np.array_equal(rebuilt, W)
+    # no iteration: the centroids are the chosen sub-vectors themselves
+    cb0, _ = oracle.rvq_fit(W, 0, init)
+    assert np.array_equal(cb0[0], W.reshape(-1, 8)[init[0]])
+
+
+def _gauss_fit_input(seed, rows=125, cols=320, dup=40):
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((rows, cols)).astype(np.float32)
+    n = rows * cols // 8
+    init = np.stack([rng.choice(n, 256, replace=False) for _ in range(3)]).astype(np.int32)
+    init[0, 256 - dup:] = init[0, :dup]          # repeated starts: those copies begin empty
+    return W, init
+
+
+@pytest.mark.parametrize("K", [1, 2, 5])
+def test_rvq_fit_update_is_the_mean_of_the_previous_assignment(K):
+    """Lloyd's update, checked against an exact sum: the stage-0 centroids after K iterations are the
+    means (math.fsum, correctly rounded, within one fp32 ulp) of the sub-vectors that the last
+    assignment of a (K-1)-iteration run gave them; a centroid without members keeps its value."""
+    import math
+    W, init = _gauss_fit_input(5)
+    X = W.reshape(-1, 8).astype(np.float64)
+    cbp, codesp = oracle.rvq_fit(W, K - 1, init)
+    cb, _ = oracle.rvq_fit(W, K, init)
+    a = codesp.reshape(-1, 3)[:, 0]
+    empty = 0
+    for c in range(256):
+        m = np.flatnonzero(a == c)
+        if len(m) == 0:
+            empty += 1
+            assert np.array_equal(cb[0, c], cbp[0, c])
+            continue
+        exact = np.array([math.fsum(X[m, j]) / len(m) for j in range(8)], dtype=np.float32)
+        ulp = np.spacing(np.abs(exact))
+        assert np.all(np.abs(cb[0, c] - exact) <= ulp), c
+    if K == 1:
+        assert empty >= 40   # the repeated starts lose every tie to their lower-index twins
+
+
+def test_rvq_fit_initialises_each_stage_from_its_residual():
+    """With no iteration, stage s's centroids are the sub-vectors init[s] of what stages < s left
+    (residual formed in fp32 from the earlier stages' codes and centroids)."""
+    W, init = _gauss_fit_input(6)
+    cb, codes = oracle.rvq_fit(W, 0, init)
+    R = W.reshape(-1, 8).copy()
+    c = codes.reshape(-1, 3)
+    for s in range(3):
+        assert np.array_equal(cb[s], R[init[s]]), s
+        R = R - cb[s][c[:, s]]
+
+
+def test_rvq_fit_codes_are_the_encoding_with_the_fitted_codebooks():
+    """The last assignment of each stage is the residual encoder's decision (pinned above): the fit's
+    codes equal rvq_encode of W with the fitted codebooks, bit for bit."""
+    W, init = _gauss_fit_input(7)
+    cb, codes = oracle.rvq_fit(W, 4, init)
+    assert np.array_equal(codes, oracle.rvq_encode(W, cb))
+
+
+def test_rvq_fit_distortion_never_increases():
+    """Lloyd's monotonicity: the stage-0 squared error does not grow with the iteration count, and
+    the three-stage error is far below stage 0's."""
+    W, init = _gauss_fit_input(8)
+    X = W.reshape(-1, 8).astype(np.float64)
+    prev = None
+    for it in range(7):
+        cb, codes = oracle.rvq_fit(W, it, init)
+        c = codes.reshape(-1, 3)
+        d0 = float(np.sum((X - cb[0][c[:, 0]]) ** 2))
+        if prev is not None:
+            assert d0 <= prev * (1 + 1e-6), it
+        prev = d0
+    d3 = float(np.sum((X - cb[0][c[:, 0]] - cb[1][c[:, 1]] - cb[2][c[:, 2]]) ** 2))
+    assert d3 < 0.5 * d0
