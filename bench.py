@@ -433,6 +433,31 @@ def run_encode(torch, rvq, dev, reps=5):
             "frac_of_valu_peak": ops / sec / VALU_LANE_OPS_PEAK}
 
 
+def run_fit(torch, rvq, dev, iters=8, reps=2):
+    """Codebook fitting of one 2048 x 7168 matrix (residual k-means, `iters` Lloyd iterations per stage
+    from random starts): ms per matrix, weights/s, the VALU rate of its nearest-entry passes
+    (3 x (iters + 1) passes of 256 entries x (3 x 8 + 3) lane operations per sub-vector), and the
+    relative squared error of the three-stage reconstruction (Gaussian weights)."""
+    rows, cols = I, H
+    n = rows * cols // 8
+    W = 0.02 * torch.randn(rows, cols, device=dev, generator=torch.Generator(device=dev).manual_seed(4))
+    init = np.random.default_rng(4).choice(n, (3, 256)).astype(np.int32)
+    ws = torch.empty(rvq.lib().rvq_fit_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
+    cb, codes = rvq.rvq_fit(W, iters, init, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        rvq.rvq_fit(W, iters, init, codebooks=cb, codes=codes, workspace=ws)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / reps
+    ops = 3 * (iters + 1) * n * 256 * (3 * 8 + 3)
+    c = codes.reshape(-1, 3).long()
+    rec = (cb[0][c[:, 0]] + cb[1][c[:, 1]] + cb[2][c[:, 2]]).reshape(rows, cols)
+    rel = float(((rec.double() - W.double()) ** 2).sum() / (W.double() ** 2).sum())
+    return {"iters": iters, "ms": sec * 1e3, "weights_per_s": rows * cols / sec,
+            "assign_valu_lane_ops_per_s": ops / sec, "rel_sq_error": rel}
+
+
 def run_stack_pool(torch, rvq, dev, layers=8, slots=128, tokens=12):
     """Pre-norm stack of 8 layers x 64 experts (8.5 GB of codes) held in pinned host memory behind
     a pool of `slots` device records, decoded token by token, with and without the pages' router
@@ -694,7 +719,8 @@ def main():
         extra = {"matvec_256x512_f32": run_matvec(torch, rvq, dev, 2000),
                  "expert_7168x2048_f32": run_expert(torch, rvq, bank, pool, 1000),
                  "bank_crc32_256x16.5MB": run_crc(torch, rvq, bank),
-                 "rvq_encode_2048x7168": run_encode(torch, rvq, dev)}
+                 "rvq_encode_2048x7168": run_encode(torch, rvq, dev),
+                 "rvq_fit_2048x7168": run_fit(torch, rvq, dev)}
         print("[bench] expert pool (experts in pinned host memory)", file=sys.stderr, flush=True)
         extra["layer_decode_expert_pool_host_backed"] = run_pool(torch, rvq, bank, w, pool)
         del bank

@@ -255,11 +255,46 @@ int rvq_moe_batch_decode(const rvq_expert_bank_t *bank, const float *x, int32_t 
  * sub-vector takes the entry nearest in squared Euclidean distance to what the
  * earlier stages left, which is then subtracted; the distance is accumulated in
  * fp32 over the 8 dims in order with no fused operations and ties go to the
- * lower index, so the result is reproducible bit for bit.  Codebook fitting is
- * not part of the library (the pages' codebooks come from training).
+ * lower index, so the result is reproducible bit for bit.  The codebooks
+ * themselves can be fitted with rvq_fit (below).
  * ------------------------------------------------------------------------ */
 int rvq_encode(const float *W, int32_t rows, int32_t cols, const float *codebooks, uint8_t *codes,
                hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Codebook fitting: the three stage codebooks of a matrix and its codes.
+ *
+ * The pages' codebooks come from their offline converter (K3's experts were
+ * trained for the format; news.hada.io topic 32035, conversion section names
+ * an encoder without its method).  The plainest fit of the residual form
+ * ("Running a 2.78-Trillion-Parameter Model on a Laptop", Technical Insight:
+ * 3 stages x 256 entries x 8 dims) is computed: residual k-means.  For stage
+ * s = 0, 1, 2: the 256 centroids start at the sub-vectors init_idx[s][c] of
+ * what stages < s left (stage 0: W); `iters` Lloyd iterations follow, each
+ * assigning every sub-vector to its nearest centroid (exactly the decision of
+ * rvq_encode: fp32 squared distance, no fused operations, ties to the lower
+ * index) and replacing every centroid that has members by their mean (one
+ * with none keeps its value); then every sub-vector is assigned once more,
+ * that is its stage-s code, and its centroid is subtracted (fp32).  The mean
+ * is an fp64 sum in a fixed order: within each run of 2048 consecutive
+ * sub-vectors (row-major sub-vector index r*(cols/8) + g) over its members in
+ * ascending index, then the run sums in ascending run order; divided by the
+ * member count, rounded to fp32.  So the result is reproducible bit for bit,
+ * and codes equal rvq_encode(W, codebooks).
+ *
+ * W: fp32 [rows][cols] (device, 4-byte aligned, not modified); cols % 8 == 0,
+ * rows * cols / 8 <= INT32_MAX.  init_idx: HOST int32 [3][256], each in
+ * [0, rows*cols/8) (random starts are the caller's: pass them in).
+ * 0 <= iters <= 10000.  codebooks out: fp32 [3][256][8] (16-byte aligned);
+ * codes out: uint8 [rows][cols/8][3] canonical.  workspace: device,
+ * 256-byte aligned, rvq_fit_workspace_bytes(rows, cols) bytes (about 41
+ * bytes per sub-vector: the residual, the current assignment, the run sums).
+ * Errors: RVQ_ERR_NULL, RVQ_ERR_SHAPE (shape, iters, or an index out of
+ * range), RVQ_ERR_ALIGN, RVQ_ERR_WORKSPACE, RVQ_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+size_t rvq_fit_workspace_bytes(int32_t rows, int32_t cols);
+int rvq_fit(const float *W, int32_t rows, int32_t cols, int32_t iters, const int32_t *init_idx, float *codebooks,
+            uint8_t *codes, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Integrity check of a resident bank (news.hada.io topic 32035, disk-

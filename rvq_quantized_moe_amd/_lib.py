@@ -58,7 +58,7 @@ EXPORTS = [
     "rvq_moe_batch_decode", "rvq_moe_batch_decode_workspace_bytes", "rvq_bank_crc32", "rvq_bank_crc32_workspace_bytes",
     "rvq_encode", "rvq_pool_create", "rvq_pool_acquire", "rvq_pool_prefetch", "rvq_pool_stats", "rvq_pool_destroy",
     "rvq_record_bytes", "rvq_record_header_init", "rvq_record_check", "rvq_pool_verify_workspace_bytes",
-    "rvq_pool_create_records", "rvq_pool_verify_status",
+    "rvq_pool_create_records", "rvq_pool_verify_status", "rvq_fit_workspace_bytes", "rvq_fit",
 ]
 
 
@@ -100,6 +100,10 @@ def lib():
         L.rvq_moe_batch_decode_workspace_bytes.restype = sz
         L.rvq_encode.argtypes = [p, i32, i32, p, p, p]
         L.rvq_encode.restype = ctypes.c_int
+        L.rvq_fit_workspace_bytes.argtypes = [i32, i32]
+        L.rvq_fit_workspace_bytes.restype = sz
+        L.rvq_fit.argtypes = [p, i32, i32, i32, p, p, p, p, sz, p]
+        L.rvq_fit.restype = ctypes.c_int
         L.rvq_bank_crc32.argtypes = [ctypes.POINTER(BankDesc), p, p, sz, p]
         L.rvq_bank_crc32.restype = ctypes.c_int
         L.rvq_bank_crc32_workspace_bytes.argtypes = [ctypes.POINTER(BankDesc)]
@@ -609,3 +613,23 @@ def rvq_encode(W, codebooks, codes=None):
     codes = torch.empty((rows, cols // 8, 3), dtype=torch.uint8, device=W.device) if codes is None else codes
     _check(lib().rvq_encode(_ptr(W), rows, cols, _ptr(codebooks), _ptr(codes), _stream(W)))
     return codes
+
+
+def rvq_fit(W, iters, init_idx, codebooks=None, codes=None, workspace=None):
+    """Residual k-means codebooks of W (fp32 [rows, cols], device): iters Lloyd iterations per stage from
+    the residual sub-vectors init_idx (host int [3, 256]).  Returns (codebooks fp32 [3, 256, 8],
+    codes uint8 [rows, cols/8, 3]); the codes equal rvq_encode(W, codebooks)."""
+    _dev(W, torch.float32, "W")
+    rows, cols = W.shape
+    dev = W.device
+    init = np.ascontiguousarray(np.asarray(init_idx, dtype=np.int32).reshape(3, 256))
+    codebooks = torch.empty((3, 256, 8), dtype=torch.float32, device=dev) if codebooks is None else codebooks
+    codes = torch.empty((rows, cols // 8, 3), dtype=torch.uint8, device=dev) if codes is None else codes
+    if workspace is None:
+        n = lib().rvq_fit_workspace_bytes(rows, cols)
+        if n == 0:
+            raise ValueError("invalid shape")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    _check(lib().rvq_fit(_ptr(W), rows, cols, int(iters), init.ctypes.data, _ptr(codebooks), _ptr(codes),
+                         _ptr(workspace), workspace.numel(), _stream(W)))
+    return codebooks, codes

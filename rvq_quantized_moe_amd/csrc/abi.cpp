@@ -218,6 +218,28 @@ int rvq_encode(const float* W, int32_t rows, int32_t cols, const float* codebook
   return hip_status(launch_rvq_encode(W, rows, cols, codebooks, codes, stream));
 }
 
+static bool fit_shape_ok(int32_t rows, int32_t cols) {
+  if (rows < 1 || cols < 8 || cols % 8 != 0) return false;
+  return (int64_t)rows * (cols / 8) <= INT32_MAX;   // sub-vector indices are int32
+}
+
+size_t rvq_fit_workspace_bytes(int32_t rows, int32_t cols) {
+  if (!fit_shape_ok(rows, cols)) return 0;
+  return fit_workspace_bytes((int64_t)rows * (cols / 8));
+}
+
+int rvq_fit(const float* W, int32_t rows, int32_t cols, int32_t iters, const int32_t* init_idx, float* codebooks,
+            uint8_t* codes, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!W || !init_idx || !codebooks || !codes || !workspace) return RVQ_ERR_NULL;
+  if (!fit_shape_ok(rows, cols) || iters < 0 || iters > kMaxFitIters) return RVQ_ERR_SHAPE;
+  const int64_t N = (int64_t)rows * (cols / 8);
+  for (int i = 0; i < 3 * 256; ++i)
+    if (init_idx[i] < 0 || init_idx[i] >= N) return RVQ_ERR_SHAPE;
+  if (!aligned(W, 4) || !aligned(codebooks, 16) || !aligned(workspace, 256)) return RVQ_ERR_ALIGN;
+  if (workspace_bytes < fit_workspace_bytes(N)) return RVQ_ERR_WORKSPACE;
+  return hip_status(launch_rvq_fit(W, rows, cols, iters, init_idx, codebooks, codes, workspace, stream));
+}
+
 size_t rvq_bank_crc32_workspace_bytes(const rvq_expert_bank_t* bank) {
   if (check_bank(bank) != RVQ_OK) return 0;
   return crc_workspace_bytes(bank->num_experts, bank->hidden, bank->inter);

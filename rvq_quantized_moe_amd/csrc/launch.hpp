@@ -40,8 +40,13 @@ hipError_t launch_moe_batch_decode(const uint8_t* codes, const float* cb, int64_
                                    const float* x, int T, const int32_t* ids, const float* gates, int k,
                                    const float* residual, float* y, bool f16, void* ws, hipStream_t stream);
 constexpr int kMaxBatchDecode = 256;
+constexpr int kMaxFitIters = 10000;   // Lloyd iterations per stage accepted by rvq_fit
 // Residual RVQ encoding of W fp32 [rows][cols] against codebooks [3][256][8] into canonical codes
 // [rows][cols/8][3] (encode.hip).
+// Residual k-means fit of a matrix's stage codebooks (starts: host int32 [3][256], each < rows*cols/8).
+size_t fit_workspace_bytes(int64_t N);
+hipError_t launch_rvq_fit(const float* W, int64_t rows, int64_t cols, int iters, const int32_t* starts, float* cb,
+                          uint8_t* codes, void* ws, hipStream_t stream);
 hipError_t launch_rvq_encode(const float* W, int64_t rows, int64_t cols, const float* cb, uint8_t* codes,
                              hipStream_t stream);
 // CRC-32 of each expert record's code payload (verify.hip); the workspace holds one word per

@@ -445,3 +445,28 @@ def test_record_pool_validation(L):
     assert out.value is None
     bad = ctypes.c_int32()
     assert L.rvq_pool_verify_status(None, ctypes.byref(bad)) == NULL
+
+
+def test_fit_workspace_and_validation(L):
+    ws = L.rvq_fit_workspace_bytes(2048, 7168)
+    n = 2048 * 896
+    runs = -(-n // 2048)
+    assert ws == n * 32 + n + runs * 2048 * 8 + runs * 256 * 4
+    assert L.rvq_fit_workspace_bytes(0, 8) == 0 and L.rvq_fit_workspace_bytes(4, 12) == 0
+    assert L.rvq_fit_workspace_bytes(2 ** 30, 2 ** 30) == 0                # more sub-vectors than int32 indices
+    init = (ctypes.c_int32 * 768)(*([0] * 768))
+    f = L.rvq_fit
+    ok = [FAKE, 64, 512, 3, init, FAKE2, FAKE, FAKE2 + 0x100000, L.rvq_fit_workspace_bytes(64, 512), None]
+    assert f(None, *ok[1:]) == NULL
+    assert f(*ok[:4], None, *ok[5:]) == NULL
+    assert f(*ok[:7], None, *ok[8:]) == NULL
+    assert f(*ok[:3], -1, *ok[4:]) == SHAPE
+    assert f(*ok[:3], 10001, *ok[4:]) == SHAPE
+    assert f(FAKE, 64, 500, *ok[3:]) == SHAPE
+    bad = (ctypes.c_int32 * 768)(*([0] * 767 + [64 * 64]))               # one start past the last sub-vector
+    assert f(*ok[:4], bad, *ok[5:]) == SHAPE
+    neg = (ctypes.c_int32 * 768)(*([-1] + [0] * 767))
+    assert f(*ok[:4], neg, *ok[5:]) == SHAPE
+    assert f(*ok[:5], FAKE2 + 4, *ok[6:]) == ALIGN                         # codebooks 16-aligned
+    assert f(*ok[:7], FAKE2 + 0x100010, *ok[8:]) == ALIGN                  # workspace 256-aligned
+    assert f(*ok[:8], ok[8] - 1, None) == WS
