@@ -139,35 +139,80 @@ __global__ __launch_bounds__(256) void k_fit_assign(float* __restrict__ R, int64
 }
 
 // Run b's per-centroid sums: thread c adds, in ascending index, the residuals of the run's sub-vectors
-// assigned to c.  part[(c * 8 + d) * nruns + b] (fp64), cnt[c * nruns + b].
+// assigned to c.  Wave w holds centroids 64w .. 64w+63, so of every code only the wave it names does
+// any work: the wave reads 16 codes at a time (one broadcast LDS read, made scalar), finds its own
+// codes four bytes per scalar test, and visits those in order, the named lane adding the residual.
+// (A per-lane test of every code is bound by the CU's one scalar unit: nine scalar instructions per
+// code and wave.)  part[(c * 8 + d) * nruns + b] (fp64), cnt[c * nruns + b].
 __global__ __launch_bounds__(256) void k_fit_partial(const float* __restrict__ R, int64_t N,
                                                      const uint8_t* __restrict__ cur, int nruns,
                                                      double* __restrict__ part, int32_t* __restrict__ cnt) {
   __shared__ __attribute__((aligned(16))) float Rb[kFitChunk * 8];
-  __shared__ uint16_t code[kFitChunk];
+  __shared__ __attribute__((aligned(16))) uint8_t code[kFitChunk];
   const int c = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  // the wave's top two code bits in every byte (wave-uniform, so the scan below is scalar)
+  const uint32_t mine = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 0x40404040u;
   double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int n = 0;
   const int64_t run0 = (int64_t)blockIdx.x * kFitRun;
   for (int h = 0; h < kFitRun; h += kFitChunk) {
+    const int64_t left = N - (run0 + h);
+    if (left <= 0) break;   // uniform across the workgroup
+    const int nvalid = left < kFitChunk ? (int)left : kFitChunk;
     __syncthreads();   // the previous chunk has been read
-    for (int q = threadIdx.x; q < kFitChunk; q += 256) {
-      const int64_t i = run0 + h + q;
-      if (i < N) {
-        code[q] = cur[i];
+    {
+      // 4 sub-vectors per thread, loads first (indices clamped to the last one: entries past nvalid
+      // are staged but never read as members)
+      constexpr int kPer = kFitChunk / 256;
+      uint8_t cv[kPer];
+      f32x4 lo[kPer], hi[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        int64_t i = run0 + h + u * 256 + threadIdx.x;
+        i = i < N ? i : N - 1;
+        cv[u] = cur[i];
         const f32x4* src = reinterpret_cast<const f32x4*>(R + i * 8);
-        reinterpret_cast<f32x4*>(Rb)[2 * q] = src[0];
-        reinterpret_cast<f32x4*>(Rb)[2 * q + 1] = src[1];
-      } else {
-        code[q] = 0xFFFF;   // past the end: nobody's member
+        lo[u] = src[0];
+        hi[u] = src[1];
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int q = u * 256 + threadIdx.x;
+        code[q] = cv[u];
+        reinterpret_cast<f32x4*>(Rb)[2 * q] = lo[u];
+        reinterpret_cast<f32x4*>(Rb)[2 * q + 1] = hi[u];
       }
     }
     __syncthreads();
-    for (int j = 0; j < kFitChunk; ++j) {
-      if (code[j] == c) {
-        ++n;
+    for (int j16 = 0; j16 < nvalid; j16 += 16) {
+      const u32x4 w4 = *reinterpret_cast<const u32x4*>(code + j16);
 #pragma unroll
-        for (int d = 0; d < 8; ++d) s[d] += (double)Rb[j * 8 + d];
+      for (int q = 0; q < 4; ++q) {
+      const int j0 = j16 + 4 * q;
+      const uint32_t word = __builtin_amdgcn_readfirstlane(w4[q]);
+      // bit 7 of byte k of m is set iff code j0+k has this wave's top two bits
+      const uint32_t u = ~(word ^ mine);
+      uint32_t m = u & (u << 1) & 0x80808080u;
+      while (m) {
+        const int k = __builtin_ctz(m) >> 3;
+        m &= m - 1;
+        const int j = j0 + k;
+        if (j >= nvalid) break;
+        if (lane == (int)((word >> (8 * k)) & 63u)) {
+          ++n;
+          const f32x4 lo = reinterpret_cast<const f32x4*>(Rb)[2 * j];
+          const f32x4 hi = reinterpret_cast<const f32x4*>(Rb)[2 * j + 1];
+          s[0] += (double)lo.x;
+          s[1] += (double)lo.y;
+          s[2] += (double)lo.z;
+          s[3] += (double)lo.w;
+          s[4] += (double)hi.x;
+          s[5] += (double)hi.y;
+          s[6] += (double)hi.z;
+          s[7] += (double)hi.w;
+        }
+      }
       }
     }
   }
@@ -177,13 +222,15 @@ __global__ __launch_bounds__(256) void k_fit_partial(const float* __restrict__ R
 }
 
 // Thread (c, d): the run sums in run order, then the mean (a centroid without members keeps its value).
-__global__ __launch_bounds__(256) void k_fit_reduce(const double* __restrict__ part, const int32_t* __restrict__ cnt,
-                                                    int nruns, float* __restrict__ C) {
-  const int t = blockIdx.x * 256 + threadIdx.x;   // 2048 threads
+// 2048 threads in workgroups of one wave, so that the serial sums spread over 32 CUs, each with many
+// loads in flight.
+__global__ __launch_bounds__(64) void k_fit_reduce(const double* __restrict__ part, const int32_t* __restrict__ cnt,
+                                                   int nruns, float* __restrict__ C) {
+  const int t = blockIdx.x * 64 + threadIdx.x;   // 2048 threads
   const int c = t >> 3;
   const double* p = part + (int64_t)t * nruns;
   const int32_t* q = cnt + (int64_t)c * nruns;
-  constexpr int kAhead = 16;
+  constexpr int kAhead = 32;
   double s = 0.0;
   int64_t n = 0;
   int b = 0;
@@ -237,7 +284,7 @@ hipError_t launch_rvq_fit(const float* W, int64_t rows, int64_t cols, int iters,
     for (int it = 0; it < iters; ++it) {
       hipLaunchKernelGGL(k_fit_assign, dim3(g), dim3(256), 0, stream, R, N, C, cur, nullptr, s);
       hipLaunchKernelGGL(k_fit_partial, dim3((unsigned)nr), dim3(256), 0, stream, R, N, cur, nr, part, cnt);
-      hipLaunchKernelGGL(k_fit_reduce, dim3(8), dim3(256), 0, stream, part, cnt, nr, C);
+      hipLaunchKernelGGL(k_fit_reduce, dim3(32), dim3(64), 0, stream, part, cnt, nr, C);
     }
     hipLaunchKernelGGL(k_fit_assign, dim3(g), dim3(256), 0, stream, R, N, C, cur, codes, s);
   }
