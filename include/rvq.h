@@ -386,7 +386,8 @@ int rvq_record_check(const void *record, int64_t record_bytes, int32_t layer, in
  * rvq_expert_bank_t over them with num_experts = slots is the bank that the
  * decode entry points use with slot ids.  The pool creates streams of its
  * own (default priority): one for the copies acquire needs, one for
- * look-ahead copies, and with verify (below) one for the payload checks.
+ * look-ahead copies, and with verify (below) one per copy stream for the
+ * payload checks.
  * rvq_pool_acquire: makes the k experts ids[0..k) (host int32, 1 <= k <=
  * slots) resident and writes their slot ids to slot_ids (host int32 [k]).
  * Missing experts are copied (LRU victim among the slots this call does not
@@ -424,9 +425,10 @@ int rvq_pool_destroy(rvq_expert_pool_t *pool);
  * prefetch stops at it with RVQ_ERR_RECORD.  slot_stride: bytes between slot
  * records in slot_codes (multiple of 256, >= rvq_bank_record_bytes).
  * verify != 0 adds the pages' optional payload check: after each copy the
- * CRC-32 of the slot's codes is computed on the device, on the pool's check
- * stream while the next copy proceeds, and compared with the header's (the
- * compute stream and the slot's next copy wait for the check); a
+ * CRC-32 of the slot's codes is computed on the device, on a check stream of
+ * the pool's (one per copy stream) while the next copy proceeds, and compared
+ * with the header's (the compute stream and the slot's next copy wait for
+ * the check); a
  * mismatch is recorded in verify_workspace (device,
  * rvq_pool_verify_workspace_bytes(hidden, inter) bytes, 256-byte aligned,
  * owned by the caller; NULL when verify == 0).  The decode still runs on the

@@ -23,9 +23,10 @@
 // Record stores: the host store may instead hold self-describing expert records (header, codebooks,
 // codes in one 4 KiB-aligned block, as the pages' container does); each record's header is then
 // checked on the host before any copy from it, and with verify on, the CRC-32 of each slot's codes
-// is compared on the device with the header's.  The checks run on a third stream of the pool's, so
-// the copy engine goes on to the next copy meanwhile; the slot's `loaded` event is then recorded
-// after its check.
+// is compared on the device with the header's.  The checks run on streams of the pool's own (one
+// per copy stream, so that a demand copy's check never waits behind a look-ahead copy), and the copy
+// engine goes on to the next copy meanwhile; the slot's `loaded` event is then recorded after its
+// check.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -45,8 +46,8 @@ struct rvq_expert_pool {
   const uint8_t* host_records = nullptr; // record store (else host_codes / host_cb)
   int32_t layer = 0;
   bool verify = false;
-  uint8_t* verify_ws = nullptr;          // status words, then the CRC workspace of the check stream
-  hipStream_t check = nullptr;           // payload checks (verify only)
+  uint8_t* verify_ws = nullptr;          // status words, then the CRC workspace of each check stream
+  hipStream_t check[2] = {nullptr, nullptr};   // payload checks after demand / look-ahead copies
   hipEvent_t copied[2] = {nullptr, nullptr};   // end of the latest copy on each copy stream
   int E = 0, H = 0, I = 0, S = 0;
   uint8_t* dev_codes = nullptr;
@@ -72,8 +73,10 @@ constexpr int64_t kRecordAlign = 4096;
 constexpr int64_t kHeaderPage = 4096;                   // header + zero fill
 constexpr int64_t kRecordCodesOffset = kHeaderPage + kCbBytes;
 
-// Verify workspace: [0, 256) two int32 status words; then the CRC block partials of one record.
-int64_t verify_ws_bytes(int H, int I) { return 256 + (int64_t)rvq::crc_workspace_bytes(1, H, I); }
+// Verify workspace: [0, 256) two int32 status words; then, per check stream, the CRC block partials
+// of one record.
+int64_t crc_region_bytes(int H, int I) { return (int64_t)rvq::crc_workspace_bytes(1, H, I); }
+int64_t verify_ws_bytes(int H, int I) { return 256 + 2 * crc_region_bytes(H, I); }
 
 const rvq_record_header_t* header_of(const rvq_expert_pool& p, int e) {
   return reinterpret_cast<const rvq_record_header_t*>(p.host_records + (int64_t)e * p.stride);
@@ -129,11 +132,12 @@ hipError_t load_slot(rvq_expert_pool& p, int s, int e, bool lookahead) {
                          hipMemcpyHostToDevice, st);
   if (err == hipSuccess && p.verify) {   // the check, on its own stream, after this copy
     err = hipEventRecord(p.copied[lookahead], st);
-    if (err == hipSuccess) err = hipStreamWaitEvent(p.check, p.copied[lookahead], 0);
+    hipStream_t ck = p.check[lookahead];
+    if (err == hipSuccess) err = hipStreamWaitEvent(ck, p.copied[lookahead], 0);
     if (err == hipSuccess)
       err = rvq::launch_record_crc_check(dst_codes, p.H, p.I, crc, e, reinterpret_cast<int32_t*>(p.verify_ws),
-                                         p.verify_ws + 256, p.check);
-    if (err == hipSuccess) err = hipEventRecord(p.loaded[s], p.check);
+                                         p.verify_ws + 256 + lookahead * crc_region_bytes(p.H, p.I), ck);
+    if (err == hipSuccess) err = hipEventRecord(p.loaded[s], ck);
   } else if (err == hipSuccess) {
     err = hipEventRecord(p.loaded[s], st);
   }
@@ -163,7 +167,8 @@ int finish_create(rvq_expert_pool* p, int32_t num_experts, int32_t hidden, int32
             hipEventCreateWithFlags(&p->compute_mark, hipEventDisableTiming) == hipSuccess;
   for (int s = 0; ok && s < slots; ++s) ok = hipEventCreateWithFlags(&p->loaded[s], hipEventDisableTiming) == hipSuccess;
   if (ok && p->verify)
-    ok = hipStreamCreateWithFlags(&p->check, hipStreamNonBlocking) == hipSuccess &&
+    ok = hipStreamCreateWithFlags(&p->check[0], hipStreamNonBlocking) == hipSuccess &&
+         hipStreamCreateWithFlags(&p->check[1], hipStreamNonBlocking) == hipSuccess &&
          hipEventCreateWithFlags(&p->copied[0], hipEventDisableTiming) == hipSuccess &&
          hipEventCreateWithFlags(&p->copied[1], hipEventDisableTiming) == hipSuccess;
   if (ok && p->verify) {
@@ -291,7 +296,8 @@ int rvq_pool_verify_status(rvq_expert_pool_t* p, int32_t* bad_expert) {
   *bad_expert = -1;
   if (hipStreamSynchronize(p->copy) != hipSuccess || hipStreamSynchronize(p->ahead) != hipSuccess) return RVQ_ERR_HIP;
   if (!p->verify) return RVQ_OK;
-  if (hipStreamSynchronize(p->check) != hipSuccess) return RVQ_ERR_HIP;
+  if (hipStreamSynchronize(p->check[0]) != hipSuccess || hipStreamSynchronize(p->check[1]) != hipSuccess)
+    return RVQ_ERR_HIP;
   int32_t st[2];
   if (hipMemcpy(st, p->verify_ws, sizeof st, hipMemcpyDeviceToHost) != hipSuccess) return RVQ_ERR_HIP;
   if (st[0] == RVQ_OK) return RVQ_OK;
@@ -306,12 +312,14 @@ int rvq_pool_destroy(rvq_expert_pool_t* p) {
   int st = RVQ_OK;
   if (p->copy && hipStreamSynchronize(p->copy) != hipSuccess) st = RVQ_ERR_HIP;
   if (p->ahead && hipStreamSynchronize(p->ahead) != hipSuccess) st = RVQ_ERR_HIP;
-  if (p->check && hipStreamSynchronize(p->check) != hipSuccess) st = RVQ_ERR_HIP;
+  for (hipStream_t c : p->check)
+    if (c && hipStreamSynchronize(c) != hipSuccess) st = RVQ_ERR_HIP;
   for (hipEvent_t e : p->loaded)
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->copied)
     if (e) (void)hipEventDestroy(e);
-  if (p->check) (void)hipStreamDestroy(p->check);
+  for (hipStream_t c : p->check)
+    if (c) (void)hipStreamDestroy(c);
   if (p->compute_mark) (void)hipEventDestroy(p->compute_mark);
   if (p->copy) (void)hipStreamDestroy(p->copy);
   if (p->ahead) (void)hipStreamDestroy(p->ahead);

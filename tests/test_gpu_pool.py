@@ -277,15 +277,18 @@ def test_record_pool_refuses_bad_headers(store, records):
 
 def test_record_pool_verify_reports_a_corrupt_payload(store, records):
     """One flipped byte in expert 5's codes (header intact, CRC of the clean payload): the header check
-    passes, the device CRC check on the copy stream reports expert 5, once; loads of clean records
-    report nothing; a pool without verify does not check."""
+    passes, the device CRC check after the demand copy reports expert 5, once; loads of clean records
+    report nothing; a flipped last byte of expert 9, copied by look-ahead, is reported by the other
+    check stream; a pool without verify does not check."""
     bank = store[0]
     rec, crcs = records
     rb = rvq.record_bytes(HIDDEN, INTER)
     hdr = rvq.RecordHeader.from_buffer_copy(bytes(rec[5 * rb:5 * rb + 64].numpy()))
     pos = 5 * rb + hdr.codes_offset + 1_234_567
+    pos9 = 9 * rb + hdr.codes_offset + hdr.codes_bytes - 1   # the last payload byte, copied ahead
     say("record pool: corrupt payload under verify")
     rec[pos] ^= 0x10
+    rec[pos9] ^= 0x01
     try:
         pool = rvq.ExpertPool.from_records(rec, REC_LAYER, E_POOL, HIDDEN, INTER, 4, verify=True)
         try:
@@ -297,6 +300,8 @@ def test_record_pool_verify_reports_a_corrupt_payload(store, records):
             pool.prefetch([7])
             pool.acquire([7, 8])
             assert pool.verify_status() == -1
+            pool.prefetch([9])                    # checked on the look-ahead side
+            assert pool.verify_status() == 9
         finally:
             pool.close()
         plain = rvq.ExpertPool.from_records(rec, REC_LAYER, E_POOL, HIDDEN, INTER, 4, verify=False)
@@ -307,3 +312,4 @@ def test_record_pool_verify_reports_a_corrupt_payload(store, records):
             plain.close()
     finally:
         rec[pos] ^= 0x10
+        rec[pos9] ^= 0x01
