@@ -71,6 +71,13 @@ def test_chunk_crowded_experts_and_residual(dtype):
     assert err <= TOL[dtype]
 
 
+def test_chunk_at_max_tokens():
+    """The largest chunk accepted (4096 tokens; 8 experts, so about 1000 pairs per expert)."""
+    say("chunk E=8 H=256 I=128 T=4096 k=2 f16")
+    err = run_case(0xC4, 8, 256, 128, 4096, 2, "f16")[0]
+    assert err <= TOL["f16"]
+
+
 def test_chunk_is_deterministic():
     say("chunk determinism")
     _, bank, y, ids, gates, xt = run_case(0xC3, 16, 256, 128, 48, 3, "f16")

@@ -126,7 +126,8 @@ def test_gemv_is_deterministic():
 
 # ---------------------------------------------------------------- router
 
-@pytest.mark.parametrize("E,H,k", [(LAYER_EXPERTS, HIDDEN, TOP_K), (64, HIDDEN, TOP_K), (300, 1000, 7), (16, 64, 16)])
+@pytest.mark.parametrize("E,H,k", [(LAYER_EXPERTS, HIDDEN, TOP_K), (64, HIDDEN, TOP_K), (300, 1000, 7), (16, 64, 16),
+                                   (4096, 512, 64)])   # the largest expert count and k accepted
 def test_router_topk_matches_oracle(E, H, k):
     say(f"router E={E} H={H} k={k}")
     bits, w = router(synth.SEED_LAYER, 0, E, H)
@@ -397,6 +398,23 @@ def test_batch_decode_other_shapes(H, I, E, k):
             assert torch.equal(y[t], rvq.moe_layer_forward(bank, xd[t], ids[t], gates[t], dtype=dtype)), (dtype, t)
 
 
+def test_batch_decode_at_max_tokens(layer_bank):
+    """The largest batch (256 tokens x top-16 = 4096 pairs in one set of launches): sampled rows equal
+    single-token calls bit for bit."""
+    bank, bits, w = layer_bank
+    T = 256
+    say(f"batch decode T={T} f16")
+    X = np.stack([synth.activation_f32(synth.SEED_LAYER, 3000 + t, HIDDEN) for t in range(T)])
+    xd = to_dev(X)
+    ids, gates, _ = rvq.router_topk(w, xd, TOP_K)
+    ws = rvq.make_batch_workspace(bank, T, TOP_K, "f16")
+    y = rvq.moe_batch_decode(bank, xd, ids, gates, dtype="f16", workspace=ws)
+    for t in (0, 1, 100, 254, 255):
+        y1 = rvq.moe_layer_forward(bank, xd[t], ids[t], gates[t], dtype="f16", workspace=ws)
+        assert torch.equal(y[t], y1), t
+    assert rvq.check_device_status(ws) == 0
+
+
 def test_batch_decode_invalid_id_is_skipped(expert_bank):
     """An id outside [0, E) in one token of a batch sets RVQ_ERR_EXPERT_ID and contributes zero,
     as in a single-token call; the other tokens are unaffected."""
@@ -589,6 +607,8 @@ def test_routed_decode_small_expert_count():
     (264, 200, 6, 3),      # ragged: 33 groups, 200 rows (partial row block), both fallbacks
     (1024, 2048, 8, 4),    # wave-specialised gate/up, fallback down (16 row blocks of H)
     (3584, 2048, 4, 2),    # both wave-specialised kernels, 2 row chunks of down
+    (256, 128, 64, 64),    # the largest k: every expert selected
+    (1024, 2048, 64, 64),  # the largest k through the wave-specialised gate/up (and its in-kernel ranking)
 ])
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_moe_layer_other_shapes(H, I, E, k, dtype):
