@@ -23,11 +23,14 @@
  *
  * Conventions for every entry point:
  *  - Data pointers are DEVICE pointers unless stated otherwise; the caller
- *    owns every buffer.  The library never allocates, frees or synchronises,
- *    except rvq_check_device_status, which synchronises `stream`.
+ *    owns every buffer.  The library never allocates device memory.  It does
+ *    not synchronise, except rvq_check_device_status (which synchronises
+ *    `stream`) and the expert pool's verify_status and destroy (which wait for
+ *    the pool's own streams); the expert pool is the one object the library
+ *    creates (host memory, streams and events of its own, freed by destroy).
  *  - Work is enqueued on `stream` (0 = the null stream).  Calls on distinct
- *    streams with distinct workspaces may run concurrently; the library has no
- *    global mutable state.
+ *    streams with distinct workspaces may run concurrently; the library's
+ *    only global mutable state is the testing aid rvq_set_wait_limit.
  *  - Return value: RVQ_OK (0) or an rvq_status_t error.  Every host-visible
  *    argument is validated before anything is enqueued: a call that returns an
  *    error other than RVQ_ERR_HIP has enqueued nothing.
