@@ -139,20 +139,24 @@ __global__ __launch_bounds__(256) void k_fit_assign(float* __restrict__ R, int64
 }
 
 // Run b's per-centroid sums: thread c adds, in ascending index, the residuals of the run's sub-vectors
-// assigned to c.  Wave w holds centroids 64w .. 64w+63, so of every code only the wave it names does
-// any work: the wave reads 16 codes at a time (one broadcast LDS read, made scalar), finds its own
-// codes four bytes per scalar test, and visits those in order, the named lane adding the residual.
-// (A per-lane test of every code is bound by the CU's one scalar unit: nine scalar instructions per
-// code and wave.)  part[(c * 8 + d) * nruns + b] (fp64), cnt[c * nruns + b].
+// assigned to c.  Each 1024-sub-vector chunk of the run is staged in LDS and its indices are sorted by
+// code, stably, so that thread c then walks exactly its own members in index order:
+//  * count per code (LDS integer atomics: exact in any order) and an exclusive scan: off[c];
+//  * four sub-chunks of 256 in index order; in each, wave w (64 consecutive sub-vectors) finds for
+//    every lane the lanes below it with the same code (8 ballots, one per code bit) and writes its
+//    per-code counts, and a sub-vector's slot is off[c] + (earlier sub-chunks' count of c) +
+//    (earlier waves' count of c) + (same-code lanes below it);
+//  * thread c adds its members' residuals (8 fp64 sums) from off[c] on.
+// part[(c * 8 + d) * nruns + b] (fp64), cnt[c * nruns + b].
 __global__ __launch_bounds__(256) void k_fit_partial(const float* __restrict__ R, int64_t N,
                                                      const uint8_t* __restrict__ cur, int nruns,
                                                      double* __restrict__ part, int32_t* __restrict__ cnt) {
   __shared__ __attribute__((aligned(16))) float Rb[kFitChunk * 8];
-  __shared__ __attribute__((aligned(16))) uint8_t code[kFitChunk];
+  __shared__ uint16_t order[kFitChunk];   // chunk-local indices, grouped by code, ascending within a code
+  __shared__ int count[256], off[256], base[256];
+  __shared__ int whist[4][256];
   const int c = threadIdx.x;
-  const int lane = threadIdx.x & 63;
-  // the wave's top two code bits in every byte (wave-uniform, so the scan below is scalar)
-  const uint32_t mine = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 0x40404040u;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int n = 0;
   const int64_t run0 = (int64_t)blockIdx.x * kFitRun;
@@ -161,17 +165,19 @@ __global__ __launch_bounds__(256) void k_fit_partial(const float* __restrict__ R
     if (left <= 0) break;   // uniform across the workgroup
     const int nvalid = left < kFitChunk ? (int)left : kFitChunk;
     __syncthreads();   // the previous chunk has been read
+    count[c] = 0;
+    base[c] = 0;
+    // stage: 4 sub-vectors per thread, loads first (indices clamped to the last one; entries past
+    // nvalid are staged but take no slot)
+    constexpr int kPer = kFitChunk / 256;
+    int code[kPer];
     {
-      // 4 sub-vectors per thread, loads first (indices clamped to the last one: entries past nvalid
-      // are staged but never read as members)
-      constexpr int kPer = kFitChunk / 256;
-      uint8_t cv[kPer];
       f32x4 lo[kPer], hi[kPer];
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
         int64_t i = run0 + h + u * 256 + threadIdx.x;
         i = i < N ? i : N - 1;
-        cv[u] = cur[i];
+        code[u] = cur[i];
         const f32x4* src = reinterpret_cast<const f32x4*>(R + i * 8);
         lo[u] = src[0];
         hi[u] = src[1];
@@ -179,41 +185,70 @@ __global__ __launch_bounds__(256) void k_fit_partial(const float* __restrict__ R
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
         const int q = u * 256 + threadIdx.x;
-        code[q] = cv[u];
         reinterpret_cast<f32x4*>(Rb)[2 * q] = lo[u];
         reinterpret_cast<f32x4*>(Rb)[2 * q + 1] = hi[u];
       }
     }
     __syncthreads();
-    for (int j16 = 0; j16 < nvalid; j16 += 16) {
-      const u32x4 w4 = *reinterpret_cast<const u32x4*>(code + j16);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-      const int j0 = j16 + 4 * q;
-      const uint32_t word = __builtin_amdgcn_readfirstlane(w4[q]);
-      // bit 7 of byte k of m is set iff code j0+k has this wave's top two bits
-      const uint32_t u = ~(word ^ mine);
-      uint32_t m = u & (u << 1) & 0x80808080u;
-      while (m) {
-        const int k = __builtin_ctz(m) >> 3;
-        m &= m - 1;
-        const int j = j0 + k;
-        if (j >= nvalid) break;
-        if (lane == (int)((word >> (8 * k)) & 63u)) {
-          ++n;
-          const f32x4 lo = reinterpret_cast<const f32x4*>(Rb)[2 * j];
-          const f32x4 hi = reinterpret_cast<const f32x4*>(Rb)[2 * j + 1];
-          s[0] += (double)lo.x;
-          s[1] += (double)lo.y;
-          s[2] += (double)lo.z;
-          s[3] += (double)lo.w;
-          s[4] += (double)hi.x;
-          s[5] += (double)hi.y;
-          s[6] += (double)hi.z;
-          s[7] += (double)hi.w;
-        }
+    for (int u = 0; u < kPer; ++u)
+      if (u * 256 + threadIdx.x < nvalid) atomicAdd(&count[code[u]], 1);
+    __syncthreads();
+    if (wave == 0) {   // exclusive scan of the 256 counts: lane l holds codes 4l .. 4l+3
+      const int c0 = count[4 * lane], c1 = count[4 * lane + 1], c2 = count[4 * lane + 2], c3 = count[4 * lane + 3];
+      int incl = c0 + c1 + c2 + c3;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
       }
+      const int ex = incl - (c0 + c1 + c2 + c3);
+      off[4 * lane] = ex;
+      off[4 * lane + 1] = ex + c0;
+      off[4 * lane + 2] = ex + c0 + c1;
+      off[4 * lane + 3] = ex + c0 + c1 + c2;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int q = u * 256 + threadIdx.x;
+      const bool valid = q < nvalid;
+      const int v = valid ? code[u] : 256;   // past the end: a code no lane shares with a valid one
+      uint64_t peers = ~0ull;
+#pragma unroll
+      for (int bit = 0; bit < 9; ++bit) {
+        const uint64_t m = __ballot((v >> bit) & 1);
+        peers &= ((v >> bit) & 1) ? m : ~m;
       }
+      const int below = __popcll(peers & ((1ull << lane) - 1ull));
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) whist[w2][c] = 0;
+      __syncthreads();
+      if (valid && below == 0) whist[wave][v] = __popcll(peers);
+      __syncthreads();
+      if (valid) {
+        int slot = off[v] + base[v] + below;
+        for (int w2 = 0; w2 < wave; ++w2) slot += whist[w2][v];
+        order[slot] = (uint16_t)q;
+      }
+      __syncthreads();
+      base[c] += whist[0][c] + whist[1][c] + whist[2][c] + whist[3][c];
+      __syncthreads();
+    }
+    // thread c: its members in index order
+    const int m0 = off[c], m1 = off[c] + count[c];
+    n += m1 - m0;
+    for (int i = m0; i < m1; ++i) {
+      const int j = order[i];
+      const f32x4 lo = reinterpret_cast<const f32x4*>(Rb)[2 * j];
+      const f32x4 hi = reinterpret_cast<const f32x4*>(Rb)[2 * j + 1];
+      s[0] += (double)lo.x;
+      s[1] += (double)lo.y;
+      s[2] += (double)lo.z;
+      s[3] += (double)lo.w;
+      s[4] += (double)hi.x;
+      s[5] += (double)hi.y;
+      s[6] += (double)hi.z;
+      s[7] += (double)hi.w;
     }
   }
 #pragma unroll
