@@ -774,6 +774,9 @@ def main():
         "chunk_prefill_512": chunk,
         "other_workloads": extra,
         "kernel_source_sha256_16": kernel_source_hash(),
+        "device": {"name": torch.cuda.get_device_name(dev), "arch": torch.cuda.get_device_properties(dev).gcnArchName,
+                   "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
+                   "hip": torch.version.hip, "torch": torch.__version__},
     }
     print(json.dumps(line), flush=True)
 
