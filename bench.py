@@ -177,10 +177,11 @@ def run_variant(rvq, hip, bank, w, pool, steps, warmup, dtype):
     }
 
 
-def run_graphed(rvq, bank, w, pool, steps, warmup, dtype, routed=True):
+def run_graphed(rvq, bank, w, pool, steps, warmup, dtype, routed=True, stats=None):
     """The step replayed from HIP graphs (one graph per pool token), which removes host launch
     overhead; returns tokens/s over `steps` replays.  routed: one rvq_moe_decode_routed call (router,
-    top-k inside the gate/up kernel, experts); else rvq_router_topk + rvq_moe_layer_forward."""
+    top-k inside the gate/up kernel, experts); else rvq_router_topk + rvq_moe_layer_forward.
+    stats (dict): filled with p10/p50/p90 of the per-replay time (µs) from a second pass."""
     import torch
     dev = pool.device
     ids = torch.empty((1, K), dtype=torch.int32, device=dev)
@@ -209,6 +210,8 @@ def run_graphed(rvq, bank, w, pool, steps, warmup, dtype, routed=True):
         graphs[i % POOL].replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if stats is not None:
+        stats.update(percentiles(replay_step_us(torch, graphs, min(steps, 256))))
     status = rvq.check_device_status(ws)
     if status:
         raise RuntimeError(rvq.status_string(status))
@@ -318,6 +321,26 @@ def replay_rate(torch, graphs, steps, warmup, before=None):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
+
+
+def replay_step_us(torch, graphs, steps, before=None):
+    """Per-replay durations (µs, sorted) from events recorded around each replay on the current
+    stream (where replay launches); a separate pass from the rate measurement, whose loop has no
+    events in it."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        if before:
+            before(i)
+        evs[i][0].record()
+        graphs[i % len(graphs)].replay()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+
+
+def percentiles(us):
+    return {"p10": float(np.percentile(us, 10)), "p50": float(np.percentile(us, 50)),
+            "p90": float(np.percentile(us, 90))}
 
 
 def capture(torch, fn):
@@ -589,6 +612,7 @@ def run_stack(torch, rvq, dev, dtype):
     torch.cuda.synchronize()
     g = capture(torch, step)
     sec = replay_rate(torch, [g], STACK_STEPS * 3, 4, before=lambda i: xin.copy_(xs[i % STACK_STEPS]))
+    per_token = percentiles(replay_step_us(torch, [g], STACK_STEPS * 3, before=lambda i: xin.copy_(xs[i % STACK_STEPS])))
     status = rvq.check_device_status(ws)
     if status:
         raise RuntimeError(rvq.status_string(status))
@@ -596,7 +620,8 @@ def run_stack(torch, rvq, dev, dtype):
     del st
     torch.cuda.empty_cache()
     return {"tokens_per_s": 1.0 / sec, "ms_per_token": sec * 1e3, "code_GBps": code / sec / 1e9,
-            "code_frac_of_hbm_peak": code / sec / 1e9 / HBM_PEAK_GBPS, "table_dtype": dtype}
+            "code_frac_of_hbm_peak": code / sec / 1e9 / HBM_PEAK_GBPS, "table_dtype": dtype,
+            "token_us_32x3": per_token}
 
 
 def stream_copy_peak(torch, rvq, dev):
@@ -695,7 +720,8 @@ def main():
     print(f"[bench] timing {args.steps} steps ({args.dtype} tables)", file=sys.stderr, flush=True)
     main_res = run_variant(rvq, hip, bank, w, pool, args.steps, args.warmup, args.dtype)
     print("[bench] graph replay", file=sys.stderr, flush=True)
-    graph_tok_s = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype)
+    step_pct = {}
+    graph_tok_s = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, stats=step_pct)
     graph_two_call = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, routed=False)
     variants = {}
     if not args.no_variants:
@@ -741,6 +767,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": 1e3 / graph_tok_s,
+        "step_us": step_pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
