@@ -201,6 +201,94 @@ struct SlabData {
   u32x4 d[6];
 };
 
+// ---------------------------------------------------------------------------------------------
+// Skewed fp32 tables (the wave-specialised kernels).  The 64 lanes of a wave (one row each) gather
+// from 48 subtables of 256 entries.  Read plainly, all lanes of an instruction share one subtable,
+// so the 32 lanes of an LDS pass land on random banks (three to four passes' worth of conflicts
+// per instruction).  Here entry c of table column j sits at byte 256 c + 4 j, so a column lies in
+// one bank (j mod 32) whatever c is.  In step i, lane l reads column (l + i) mod 32 (subtables
+// 0..31) and, for i = 32 + j, column 32 + (l + j) mod 16 + 16 ((l / 16) mod 2) (subtables 32..47,
+// stored twice, at columns 32..47 and 48..63): the 32 lanes of every pass read 32 distinct banks.
+// A lane thus needs its row's 48 code bytes in a rotated order: the first 32 left by l mod 32, the
+// last 16 by l mod 16 (a select network over the dwords, v_alignbyte within them: about one VALU
+// instruction per lookup); each lookup's address is then one v_perm (code byte above the lane's
+// column offset).
+constexpr int kSkewCols = 64;
+constexpr int kSkewWords = kSkewCols * kEntries;   // 16384 floats (64 KiB) per table
+
+// Per lane: the column offset (4 j) of each step; per wave: which lanes rotate by 1, 2 and 4 dwords
+// (first 32 bytes) and by 1 and 2 dwords (last 16), as lane masks, and the byte shifts.
+struct SkewLane {
+  uint32_t col[48];
+  uint64_t mA1, mA2, mA4, mB1, mB2;
+  uint32_t shA, shB;
+  __device__ __forceinline__ void init(int lane) {
+    const int la = lane & 31, lb = lane & 15, hb = (lane >> 4) & 1;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) col[i] = 4u * (uint32_t)((la + i) & 31);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) col[32 + j] = 4u * (uint32_t)(32 + ((lb + j) & 15) + 16 * hb);
+    mA1 = __ballot((la >> 2) & 1);
+    mA2 = __ballot((la >> 3) & 1);
+    mA4 = __ballot((la >> 4) & 1);
+    mB1 = __ballot((lb >> 2) & 1);
+    mB2 = __ballot((lb >> 3) & 1);
+    shA = (uint32_t)(la & 3);
+    shB = (uint32_t)(lb & 3);
+  }
+};
+
+// b where the lane's bit of m is set, else a: one v_cndmask (issued as written, so the rotation
+// below stays one select per dword per stage).
+__device__ __forceinline__ uint32_t lane_select(uint32_t a, uint32_t b, uint64_t m) {
+  uint32_t d;
+  asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "s"(m));
+  return d;
+}
+
+// w[0..N) rotated left by whole dwords (the stages whose masks hold this lane), then by sh bytes.
+template <int N>
+__device__ __forceinline__ void rotate_stage(uint32_t (&w)[N], int bit, uint64_t m) {
+  uint32_t t[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) t[q] = lane_select(w[q], w[(q + bit) % N], m);
+#pragma unroll
+  for (int q = 0; q < N; ++q) w[q] = t[q];
+}
+template <int N>
+__device__ __forceinline__ void rotate_bytes_tail(uint32_t (&w)[N], uint32_t sh) {
+  uint32_t t[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) t[q] = __builtin_amdgcn_alignbyte(w[(q + 1) % N], w[q], sh);
+#pragma unroll
+  for (int q = 0; q < N; ++q) w[q] = t[q];
+}
+
+// One row block's 48 lookups through a skewed table (lut: the table's first byte; the lane's codes
+// in s.d[0..2] as loaded).
+__device__ __forceinline__ float gather_skew(const float* lut, const SlabData& s, const SkewLane& sl) {
+  uint32_t lo[8] = {s.d[0][0], s.d[0][1], s.d[0][2], s.d[0][3], s.d[1][0], s.d[1][1], s.d[1][2], s.d[1][3]};
+  uint32_t hi[4] = {s.d[2][0], s.d[2][1], s.d[2][2], s.d[2][3]};
+  rotate_stage<8>(lo, 1, sl.mA1);
+  rotate_stage<8>(lo, 2, sl.mA2);
+  rotate_stage<8>(lo, 4, sl.mA4);
+  rotate_bytes_tail<8>(lo, sl.shA);
+  rotate_stage<4>(hi, 1, sl.mB1);
+  rotate_stage<4>(hi, 2, sl.mB2);
+  rotate_bytes_tail<4>(hi, sl.shB);
+  const uint32_t r[12] = {lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7], hi[0], hi[1], hi[2], hi[3]};
+  const char* t = reinterpret_cast<const char*>(lut);
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 48; ++i) {
+    // bytes: [0] = column offset, [1] = code byte i, [2], [3] = 0  ->  256 c + 4 j
+    const uint32_t sel = 0x0c0c0000u | ((uint32_t)(4 + (i & 3)) << 8);
+    const uint32_t a = __builtin_amdgcn_perm(r[i >> 2], sl.col[i], sel);
+    acc += *reinterpret_cast<const float*>(t + a);
+  }
+  return acc;
+}
+
 // Loads one row block (48 code bytes per lane, or 96 with fp16 tables) of slab base(s) s0/s1 at
 // byte offset `off` (< 4 GiB; lane part included): uniform 64-bit base + 32-bit lane offset, so
 // the address costs one VGPR.

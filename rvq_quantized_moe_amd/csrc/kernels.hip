@@ -690,7 +690,8 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
   constexpr int TPW = 48 / kPipeBuildWaves;                 // table tiles per builder wave
   typedef typename Tile<F16>::entry_t T;
   constexpr int S = F16 ? kPipeStride16 : kPipeStride;
-  __shared__ __attribute__((aligned(16))) T lut[2][48 * S];
+  // fp32: skewed 64-column tables (see SkewLane); fp16: 48 subtables S halves apart
+  __shared__ __attribute__((aligned(16))) T lut[2][F16 ? 48 * S : kSkewWords];
   __shared__ __attribute__((aligned(16))) float hs[DOWN ? ITEMS : 1][128];
   __shared__ int built[2], done[2], hready;
   __shared__ int cmax_bits;            // fp16: max squared codebook-entry norm (bits of a float >= 0)
@@ -804,34 +805,61 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
     // ----------------------------------------------------------------- streamers
     const uint8_t* codes = bank.codes + (int64_t)e * bank.stride + (int64_t)m * packed_bytes(I, H) +
                            (int64_t)t0 * tile_bytes + (int64_t)rb0 * kSlabBytes;
-    SlabData buf[NB];
-    const uint32_t lane_off = lane * 16;
-    auto load_blk = [&](int i, int s) {
-      const int k = s / BPI, r = s % BPI;
-      load_slabs<false>(buf[i], codes + k * tile_bytes, codes + k * tile_bytes,
-                        (uint32_t)(wave + NSW * r) * kSlabBytes + lane_off);
-    };
-#pragma unroll
-    for (int i = 0; i < NB; ++i) load_blk(i, i);
     float acc[BPI];
 #pragma unroll
     for (int r = 0; r < BPI; ++r) acc[r] = 0.f;
     bool ok = true;
+    if constexpr (F16) {
+      SlabData buf[NB];
+      const uint32_t lane_off = lane * 16;
+      auto load_blk = [&](int i, int s) {
+        const int k = s / BPI, r = s % BPI;
+        load_slabs<false>(buf[i], codes + k * tile_bytes, codes + k * tile_bytes,
+                          (uint32_t)(wave + NSW * r) * kSlabBytes + lane_off);
+      };
 #pragma unroll
-    for (int k = 0; k < ITEMS; ++k) {
-      ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1), pa.wait_limit);
+      for (int i = 0; i < NB; ++i) load_blk(i, i);
 #pragma unroll
-      for (int r = 0; r < BPI; ++r) {
-        const int s = k * BPI + r;
-        float g = gather_slab1<F16, S>(lut[k & 1], buf[s % NB]);
-        // opaque use: without it the compiler interleaves the row blocks' gathers into one
-        // another and spills
-        asm volatile("" : : "v"(g));
-        if constexpr (F16) g *= escale[k];
-        acc[r] += g;
-        if (s + NB < NBLK) load_blk(s % NB, s + NB);
+      for (int k = 0; k < ITEMS; ++k) {
+        ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1), pa.wait_limit);
+#pragma unroll
+        for (int r = 0; r < BPI; ++r) {
+          const int s = k * BPI + r;
+          float g = gather_slab1<F16, S>(lut[k & 1], buf[s % NB]);
+          // opaque use: without it the compiler interleaves the row blocks' gathers into one
+          // another and spills
+          asm volatile("" : : "v"(g));
+          g *= escale[k];
+          acc[r] += g;
+          if (s + NB < NBLK) load_blk(s % NB, s + NB);
+        }
+        if (lane == 0) __hip_atomic_fetch_add(&done[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
-      if (lane == 0) __hip_atomic_fetch_add(&done[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+      SlabData buf[NB];
+      const uint32_t lane_off = lane * 16;
+      SkewLane sl;
+      sl.init(lane);
+      auto load_blk = [&](int i, int s) {
+        const int k = s / BPI, r = s % BPI;
+        load_slabs<false>(buf[i], codes + k * tile_bytes, codes + k * tile_bytes,
+                          (uint32_t)(wave + NSW * r) * kSlabBytes + lane_off);
+      };
+#pragma unroll
+      for (int i = 0; i < NB; ++i) load_blk(i, i);
+#pragma unroll
+      for (int k = 0; k < ITEMS; ++k) {
+        ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1), pa.wait_limit);
+#pragma unroll
+        for (int r = 0; r < BPI; ++r) {
+          const int s = k * BPI + r;
+          float g = gather_skew(lut[k & 1], buf[s % NB], sl);
+          asm volatile("" : : "v"(g));
+          acc[r] += g;
+          if (s + NB < NBLK) load_blk(s % NB, s + NB);
+        }
+        if (lane == 0) __hip_atomic_fetch_add(&done[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
     }
     float* out = pa.out + (int64_t)blockIdx.x * pad_rows(rows) + (int64_t)rb0 * kSlabRows;
     if constexpr (DOWN) out = pa.out + ((int64_t)slot * pa.nchunk + (blockIdx.x % pa.nchunk)) * pad_rows(rows) +
@@ -907,7 +935,19 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
           const half4 hv = {(f16)(d.x * scale), (f16)(d.y * scale), (f16)(d.z * scale), (f16)(d.w * scale)};
           *reinterpret_cast<half4*>(&L[(3 * i16 + st) * S + e0 + 4 * q]) = hv;
         } else {
-          *reinterpret_cast<f32x4*>(&L[(3 * i16 + st) * S + e0 + 4 * q]) = d;
+          // skewed layout: entry c of subtable k at word 64 c + k; subtables 32..47 also at k + 16
+          const int k = 3 * i16 + st, c0 = e0 + 4 * q;
+          float* col = L + kSkewCols * c0 + k;
+          col[0] = d.x;
+          col[kSkewCols] = d.y;
+          col[2 * kSkewCols] = d.z;
+          col[3 * kSkewCols] = d.w;
+          if (k >= 32) {
+            col[16] = d.x;
+            col[kSkewCols + 16] = d.y;
+            col[2 * kSkewCols + 16] = d.z;
+            col[3 * kSkewCols + 16] = d.w;
+          }
         }
       }
       if (lane == 0) __hip_atomic_fetch_add(&built[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
