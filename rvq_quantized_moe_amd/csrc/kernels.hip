@@ -380,47 +380,101 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   if (threadIdx.x == 0) logits[(int64_t)t * E + e] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// Top-k by (logit desc, id asc): the rank of e is the number of experts that precede it in that
-// order; ranks < k are kept, at position rank.  Experts are taken 64 to a wave (lane = expert) and
-// the comparisons split into 64-expert blocks of j: wave (b, r) counts, for experts 64b + lane,
-// the j of the blocks r, r + R, ...  A block entirely before expert block b needs only L[j] >= L[e],
-// one entirely after it only L[j] > L[e]; only the diagonal block compares ids.  The partial counts
-// are integers, so adding them (LDS atomics) in any order is exact.  cnt[0..E) must be zero.
-__device__ void topk_ranks(const double* L, int* cnt, int E) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nw = blockDim.x >> 6;
-  const int nb = (E + 63) >> 6;                       // expert blocks
-  const int R = nw / nb > 1 ? nw / nb : 1;            // j-ranges per expert block
-  for (int task = wave; task < nb * R; task += nw) {
-    const int b = task / R, r = task - b * R;
-    const int e = b * 64 + lane;
-    const double le = L[e < E ? e : E - 1];
-    int rank = 0;
-    for (int jb = r; jb < nb; jb += R) {
-      const int j0 = jb * 64;
-      const int jn = E - j0 < 64 ? E - j0 : 64;
-      if (jb < b) {
-#pragma unroll 8
-        for (int jj = 0; jj < jn; ++jj) rank += L[j0 + jj] >= le;
-      } else if (jb > b) {
-#pragma unroll 8
-        for (int jj = 0; jj < jn; ++jj) rank += L[j0 + jj] > le;
-      } else {
-#pragma unroll 8
-        for (int jj = 0; jj < jn; ++jj) {
-          const double lj = L[j0 + jj];
-          rank += (lj > le) || (lj == le && jj < lane);
-        }
-      }
-    }
-    if (e < E) atomicAdd(&cnt[e], rank);
+// Top-k by (logit desc, id asc), by one workgroup; every thread calls it.  A full ranking compares
+// all E^2 pairs in fp64; here it runs in two passes:
+//  (a) g[e] = #{j in e's 64-expert block : L[j] > L[e]} (strict, one compare per pair, E * 64 pairs);
+//  (b) the candidates are the experts with g < k.  Every expert of global rank < k is one (its
+//      count within the block is at most its rank), and every expert ahead of such an expert has
+//      smaller rank, so is one too;
+//  (c) each candidate's rank among the candidates by (logit desc, id asc) is then its global rank
+//      whenever that is below k, and a candidate of global rank >= k has the true top k ahead of
+//      it, so its rank among candidates is >= k as well.  sel[rank] = id for ranks < k.
+// Each task of (a) and (c) compares its 64 lanes with 16 values read at once (the passes are bound
+// by LDS latency, not by the compares).  The partial counts are integers added with LDS atomics:
+// exact in any order.  Candidates take list slots in atomic order, which changes nothing, as (c)
+// orders them by logit and id alone.
+// On entry (see topk_prepare): L holds the E logits and -inf up to E rounded to 64; g and crank are
+// zero; cl and cid hold -inf and INT_MAX (the padding that (c) compares against); *ncand is zero.
+struct TopkScratch {
+  int* g;
+  int* crank;
+  int* cid;
+  double* cl;
+  int* ncand;
+};
+constexpr int kTopkChunk = 16;
+__device__ __forceinline__ int topk_pad(int E) { return (E + 63) & ~63; }
+
+// Writes the state topk_select expects; src(e) gives logit e.  Every thread calls it; a barrier
+// must follow.
+template <typename Src>
+__device__ void topk_prepare(double* L, int E, const TopkScratch& ts, Src src) {
+  if (threadIdx.x == 0) *ts.ncand = 0;
+  for (int e = threadIdx.x; e < topk_pad(E); e += blockDim.x) {
+    L[e] = e < E ? src(e) : -INFINITY;
+    ts.g[e] = 0;
+    ts.crank[e] = 0;
+    ts.cid[e] = INT_MAX;
+    ts.cl[e] = -INFINITY;
   }
 }
 
-// sel[rank] = e for the experts ranked below k.
-__device__ void topk_select(const int* cnt, int E, int k, int* sel) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    if (cnt[e] < k) sel[cnt[e]] = e;
+__device__ void topk_select(const double* L, int E, int k, const TopkScratch& ts, int* sel) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  constexpr int Q = 64 / kTopkChunk;
+  const int nb = topk_pad(E) >> 6;
+  for (int task = wave; task < nb * Q; task += nw) {
+    const int b = task / Q, q = task - b * Q;
+    const int e = b * 64 + lane;
+    const double le = L[e];
+    const double* Lj = L + b * 64 + q * kTopkChunk;
+    double v[kTopkChunk];
+#pragma unroll
+    for (int u = 0; u < kTopkChunk; ++u) v[u] = Lj[u];
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < kTopkChunk; ++u) c += v[u] > le;
+    if (e < E) atomicAdd(&ts.g[e], c);
+  }
+  __syncthreads();
+  for (int e0 = wave * 64; e0 < nb * 64; e0 += nw * 64) {
+    const int e = e0 + lane;
+    const bool cand = e < E && ts.g[e] < k;
+    const uint64_t m = __ballot(cand);
+    int base = 0;
+    if (lane == 0 && m) base = atomicAdd(ts.ncand, __popcll(m));
+    base = __shfl(base, 0, 64);
+    if (cand) {
+      const int p = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      ts.cid[p] = e;
+      ts.cl[p] = L[e];
+    }
+  }
+  __syncthreads();
+  const int C = __builtin_amdgcn_readfirstlane(*ts.ncand);
+  const int ncb = (C + 63) >> 6, nq = (C + kTopkChunk - 1) / kTopkChunk;
+  for (int task = wave; task < ncb * nq; task += nw) {
+    const int b = task / nq, q = task - b * nq;
+    const int i = b * 64 + lane;
+    const int ii = i < C ? i : C - 1;
+    const int ei = ts.cid[ii];
+    const double li = ts.cl[ii];
+    double v[kTopkChunk];
+    int id[kTopkChunk];
+#pragma unroll
+    for (int u = 0; u < kTopkChunk; ++u) {
+      v[u] = ts.cl[q * kTopkChunk + u];
+      id[u] = ts.cid[q * kTopkChunk + u];
+    }
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < kTopkChunk; ++u) c += (v[u] > li) || (v[u] == li && id[u] < ei);
+    if (i < C) atomicAdd(&ts.crank[i], c);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < C; i += blockDim.x)
+    if (ts.crank[i] < k) sel[ts.crank[i]] = ts.cid[i];
 }
 
 // Called by one whole wave: gates = softmax over the kept logits in fp64 (max subtracted), the
@@ -442,19 +496,15 @@ __device__ void topk_gates(const double* L, const int* sel, int k, int32_t* ids,
 
 __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ logits, int E, int k,
                                                int32_t* __restrict__ ids, float* __restrict__ gates) {
-  __shared__ double L[kMaxExperts];
-  __shared__ int cnt[kMaxExperts];
-  __shared__ int sel[kMaxTopK];
+  __shared__ double L[kMaxExperts], cl[kMaxExperts];
+  __shared__ int g[kMaxExperts], crank[kMaxExperts], cid[kMaxExperts];
+  __shared__ int sel[kMaxTopK], ncand;
   const int t = blockIdx.x;
   if (threadIdx.x < kMaxTopK) sel[threadIdx.x] = 0;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    L[e] = logits[(int64_t)t * E + e];
-    cnt[e] = 0;
-  }
+  const TopkScratch ts{g, crank, cid, cl, &ncand};
+  topk_prepare(L, E, ts, [&](int e) { return logits[(int64_t)t * E + e]; });
   __syncthreads();
-  topk_ranks(L, cnt, E);
-  __syncthreads();
-  topk_select(cnt, E, k, sel);
+  topk_select(L, E, k, ts, sel);
   __syncthreads();
   if (threadIdx.x < 64) topk_gates(L, sel, k, ids + (int64_t)t * k, gates + (int64_t)t * k, [](int) { return true; });
 }
@@ -696,8 +746,8 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
   __shared__ int built[2], done[2], hready;
   __shared__ int cmax_bits;            // fp16: max squared codebook-entry norm (bits of a float >= 0)
   __shared__ float escale[ITEMS];      // fp16: 2^e_k of each item
-  __shared__ double rl[DOWN ? 1 : kRouteMaxExperts];
-  __shared__ int rcnt[DOWN ? 1 : kRouteMaxExperts], rsel[kMaxTopK];
+  __shared__ int rsel[kMaxTopK];
+  static_assert(DOWN || sizeof(lut) >= 28 * kRouteMaxExperts + 4, "top-k scratch must fit in the table buffers");
   const int H = bank.H, I = bank.I;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -748,17 +798,20 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
   }
   int e;
   if (!DOWN && pa.logits) {
-    // top-k of the router logits, the same computation as k_topk
+    // top-k of the router logits, the same computation as k_topk.  Its scratch lies in the table
+    // buffers, which nothing writes before the start barrier below; every read of it comes first.
     const int E = bank.E;
+    char* scr = reinterpret_cast<char*>(&lut[0][0]);
+    double* rl = reinterpret_cast<double*>(scr);
+    const TopkScratch ts{reinterpret_cast<int*>(scr + 16 * kRouteMaxExperts),
+                         reinterpret_cast<int*>(scr + 20 * kRouteMaxExperts),
+                         reinterpret_cast<int*>(scr + 24 * kRouteMaxExperts),
+                         reinterpret_cast<double*>(scr + 8 * kRouteMaxExperts),
+                         reinterpret_cast<int*>(scr + 28 * kRouteMaxExperts)};
     if (threadIdx.x < kMaxTopK) rsel[threadIdx.x] = 0;
-    for (int j = threadIdx.x; j < E; j += blockDim.x) {
-      rl[j] = pa.logits[j];
-      rcnt[j] = 0;
-    }
+    topk_prepare(rl, E, ts, [&](int j) { return pa.logits[j]; });
     __syncthreads();
-    topk_ranks(rl, rcnt, E);
-    __syncthreads();
-    topk_select(rcnt, E, pa.k, rsel);
+    topk_select(rl, E, pa.k, ts, rsel);
     __syncthreads();
     e = rsel[slot];
     if (m == 0 && t0 == 0 && wave == 0)

@@ -290,6 +290,39 @@ def test_moe_layer_is_deterministic(layer_bank):
     assert torch.equal(a, b)
 
 
+def test_topk_ties_across_blocks(layer_bank):
+    """Top-k of 256 logits with many exact ties inside and across the 64-expert blocks of the
+    selection (router rows repeated with period 37, and a group of rows set to the largest one):
+    rvq_router_topk equals the oracle's order (logit desc, lower id first) for k = 1, 16, 64, and the
+    top-k inside the gate/up kernel (rvq_moe_decode_routed, fp32 tables) gives the same ids and gates."""
+    say("top-k ties across blocks (256 experts)")
+    bank, bits0, _ = layer_bank
+    E = LAYER_EXPERTS
+    bits = bits0.copy()
+    for j in range(37, E):
+        bits[j] = bits[j % 37]
+    x = synth.activation_f32(synth.SEED_LAYER, 41, HIDDEN)
+    lo = oracle.router_logits(bits, x[None, :])[0]
+    top = int(np.argmax(lo))
+    for j in (3, 70, 130, 200, 255):
+        bits[j] = bits[top]              # ties at the top, in four different blocks
+    w = to_dev(bits.view(np.int16)).view(torch.bfloat16)
+    xd = to_dev(x)
+    lo = oracle.router_logits(bits, x[None, :])[0]
+    assert len(np.unique(lo)) == 37
+    for k in (1, 16, 64):
+        ids, gates, logits = rvq.router_topk(w, xd, k)
+        ids_o, gates_o, _ = oracle.topk(lo, k)
+        assert np.array_equal(ids[0].cpu().numpy(), ids_o), k
+        np.testing.assert_allclose(gates[0].cpu().numpy(), gates_o, rtol=1e-6)
+    ws = rvq.make_moe_workspace(bank, 1, TOP_K, "f32")
+    y, ids_r, gates_r, _ = rvq.moe_decode_routed(bank, w, xd, TOP_K, dtype="f32", workspace=ws)
+    ids2, gates2, _ = rvq.router_topk(w, xd, TOP_K)
+    assert torch.equal(ids_r, ids2[0]) and torch.equal(gates_r, gates2[0])
+    assert torch.equal(y, rvq.moe_layer_forward(bank, xd, ids2[0], gates2[0], dtype="f32", workspace=ws))
+    assert rvq.check_device_status(ws) == 0
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_routed_decode_matches_two_calls_and_oracle(layer_bank, dtype):
     """rvq_moe_decode_routed (top-k taken inside the gate/up kernel for fp32 tables, by the selection
