@@ -33,6 +33,7 @@ METRIC = "MoE-layer decode tokens/s + code-byte HBM GB/s (% of peak), batch 1, t
 HBM_PEAK_GBPS = 8000.0
 E, H, I, K = 256, 7168, 2048, 16
 POOL = 64
+STEPS_PER_GRAPH = 8        # decode steps captured in one HIP graph
 CODE_BYTES_PER_TOKEN = K * 3 * (H * I * 3 // 8)          # 264,241,152
 WEIGHTS_PER_TOKEN = K * 3 * H * I                         # 704,643,072
 GATEUP_CODE_BYTES = K * 2 * (H * I * 3 // 8)              # 176,160,768 per gate/up launch
@@ -179,11 +180,14 @@ def run_variant(rvq, hip, bank, w, pool, steps, warmup, dtype):
     }
 
 
-def run_graphed(rvq, bank, w, pool, steps, warmup, dtype, routed=True, stats=None):
-    """The step replayed from HIP graphs (one graph per pool token), which removes host launch
-    overhead; returns tokens/s over `steps` replays.  routed: one rvq_moe_decode_routed call (router,
-    top-k inside the gate/up kernel, experts); else rvq_router_topk + rvq_moe_layer_forward.
-    stats (dict): filled with p10/p50/p90 of the per-replay time (µs) from a second pass."""
+def run_graphed(rvq, bank, w, pool, steps, warmup, dtype, routed=True, stats=None, per_graph=1):
+    """The step replayed from HIP graphs, which removes host launch overhead; returns tokens/s over
+    `steps` decode steps.  Each graph holds per_graph consecutive steps (pool tokens j*per_graph ..),
+    one after another on one stream, as the layers of a token follow one another inside one graph
+    in a full model; per_graph = 1 adds one graph launch (about 10 µs of idle GPU) to every step.
+    routed: one rvq_moe_decode_routed call per step (router, top-k inside the gate/up kernel,
+    experts); else rvq_router_topk + rvq_moe_layer_forward.  stats (dict): filled with p10/p50/p90
+    of the per-step time (µs: each replay's time / per_graph) from a second pass."""
     import torch
     dev = pool.device
     ids = torch.empty((1, K), dtype=torch.int32, device=dev)
@@ -192,33 +196,36 @@ def run_graphed(rvq, bank, w, pool, steps, warmup, dtype, routed=True, stats=Non
     y = torch.empty(H, dtype=torch.float32, device=dev)
     ws = rvq.make_moe_workspace(bank, 1, K, dtype)
     torch.cuda.synchronize()
+    assert POOL % per_graph == 0
     graphs = []
     side = torch.cuda.Stream()
-    for j in range(POOL):
+    for j0 in range(0, POOL, per_graph):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
-            if routed:
-                rvq.moe_decode_routed(bank, w, pool[j], K, dtype=dtype, y=y, ids=ids[0], gates=gates[0],
-                                      logits=logits[0], workspace=ws)
-            else:
-                rvq.router_topk(w, pool[j], K, ids=ids, gates=gates, logits=logits)
-                rvq.moe_layer_forward(bank, pool[j], ids[0], gates[0], dtype=dtype, y=y, workspace=ws)
+            for j in range(j0, j0 + per_graph):
+                if routed:
+                    rvq.moe_decode_routed(bank, w, pool[j], K, dtype=dtype, y=y, ids=ids[0], gates=gates[0],
+                                          logits=logits[0], workspace=ws)
+                else:
+                    rvq.router_topk(w, pool[j], K, ids=ids, gates=gates, logits=logits)
+                    rvq.moe_layer_forward(bank, pool[j], ids[0], gates[0], dtype=dtype, y=y, workspace=ws)
         graphs.append(g)
-    for i in range(warmup):
-        graphs[i % POOL].replay()
+    replays = max(1, steps // per_graph)
+    for i in range(max(1, warmup // per_graph)):
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % POOL].replay()
+    for i in range(replays):
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if stats is not None:
-        stats.update(percentiles(replay_step_us(torch, graphs, min(steps, 256))))
+        stats.update(percentiles([u / per_graph for u in replay_step_us(torch, graphs, min(replays, 256))]))
     status = rvq.check_device_status(ws)
     if status:
         raise RuntimeError(rvq.status_string(status))
     del graphs
-    return steps / (t1 - t0)
+    return replays * per_graph / (t1 - t0)
 
 
 def run_chunk(rvq, hip, bank, w, xt, steps, dtype):
@@ -723,14 +730,19 @@ def main():
     main_res = run_variant(rvq, hip, bank, w, pool, args.steps, args.warmup, args.dtype)
     print("[bench] graph replay", file=sys.stderr, flush=True)
     step_pct = {}
-    graph_tok_s = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, stats=step_pct)
-    graph_two_call = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, routed=False)
+    graph_tok_s = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, stats=step_pct,
+                              per_graph=STEPS_PER_GRAPH)
+    one_step_pct = {}
+    graph_one_step = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, stats=one_step_pct)
+    graph_two_call = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, routed=False,
+                                 per_graph=STEPS_PER_GRAPH)
     variants = {}
     if not args.no_variants:
         other = "f16" if args.dtype == "f32" else "f32"
         print(f"[bench] timing {args.steps} steps ({other} tables)", file=sys.stderr, flush=True)
         variants[other] = run_variant(rvq, hip, bank, w, pool, args.steps, args.warmup, other)
-        variants[other]["graph_replay_tokens_per_s"] = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, other)
+        variants[other]["graph_replay_tokens_per_s"] = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, other,
+                                                                   per_graph=STEPS_PER_GRAPH)
     chunk = None
     if not args.no_chunk:
         print("[bench] chunked prefill (512 tokens)", file=sys.stderr, flush=True)
@@ -783,18 +795,23 @@ def main():
         "code_frac_of_stream_copy": CODE_BYTES_PER_TOKEN * graph_tok_s / 1e9 / copy_gbps,
         "stream_copy_GBps": copy_gbps,
         "decoded_weights_per_s": WEIGHTS_PER_TOKEN * graph_tok_s,
-        "timing": "value: HIP-graph replay of one rvq_moe_decode_routed step per token (one graph per pool "
-                  "token); kernel_us and roofline: HIP events around each kernel of the two-call form "
-                  "(rvq_router_topk, rvq_moe_layer_forward_timed) in an eager timed pass of the same steps",
+        "timing": f"value: HIP-graph replays, each graph holding {STEPS_PER_GRAPH} consecutive decode steps "
+                  "(one rvq_moe_decode_routed call per token, pool tokens in order), as the layers of a token "
+                  "run inside one graph in a full model; graph_one_step_per_graph_tokens_per_s: one graph per "
+                  "step, which adds one graph launch to every step; kernel_us and roofline: HIP events around "
+                  "each kernel of the two-call form (rvq_router_topk, rvq_moe_layer_forward_timed) in an eager "
+                  "timed pass of the same steps",
+        "graph_one_step_per_graph_tokens_per_s": graph_one_step,
+        "step_us_one_step_per_graph": one_step_pct,
         "graph_two_call_tokens_per_s": graph_two_call,
         "eager_tokens_per_s": main_res["tokens_per_s"],
         "kernel_us": main_res["kernel_us"],
-        "roofline": {"bound": "hbm", "kernel": "k_table_ws_f32<gate/up>" if args.dtype == "f32" else "k_moe_gateup_f16", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": "k_table_ws_f32<gate/up>" if args.dtype == "f32" else "k_table_ws_f16<gate/up>", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic_from_profiles(args.dtype),
                      "algorithmic_bytes_per_launch": GATEUP_CODE_BYTES + GATEUP_CODEBOOK_BYTES},
-        # the table kernels' real ceiling: one LDS lookup per code byte, at the random-gather rate
-        # measured for ds_read_b32 over 256-dword (fp32) or ds_read_u16 over 256-half (fp16) subtables
+        # the table kernels' LDS ceiling: one lookup per code byte, at the gather rate measured for the
+        # table layout (skewed fp32 columns, or random ds_read_u16 over 256-half fp16 subtables)
         "lds_gather": {"kernel": "gate/up", "lookups_per_s": GATEUP_CODE_BYTES / (gu_us * 1e-6),
                        "ceiling_lookups_per_s": LDS_GATHER_RATE[args.dtype],
                        "frac": GATEUP_CODE_BYTES / (gu_us * 1e-6) / LDS_GATHER_RATE[args.dtype]},
