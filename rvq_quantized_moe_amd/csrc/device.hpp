@@ -266,7 +266,10 @@ __device__ __forceinline__ void rotate_bytes_tail(uint32_t (&w)[N], uint32_t sh)
 
 // One row block's 48 lookups through a skewed table (lut: the table's first byte; the lane's codes
 // in s.d[0..2] as loaded).
-__device__ __forceinline__ float gather_skew(const float* lut, const SlabData& s, const SkewLane& sl) {
+// F16: the table holds fp16 entries in one half of each 32-bit word (t already points at that
+// half), and two lookups are added at a time with v_dot2 against (1, 1).
+template <bool F16>
+__device__ __forceinline__ float gather_skew(const char* t, const SlabData& s, const SkewLane& sl) {
   uint32_t lo[8] = {s.d[0][0], s.d[0][1], s.d[0][2], s.d[0][3], s.d[1][0], s.d[1][1], s.d[1][2], s.d[1][3]};
   uint32_t hi[4] = {s.d[2][0], s.d[2][1], s.d[2][2], s.d[2][3]};
   rotate_stage<8>(lo, 1, sl.mA1);
@@ -277,14 +280,22 @@ __device__ __forceinline__ float gather_skew(const float* lut, const SlabData& s
   rotate_stage<4>(hi, 2, sl.mB2);
   rotate_bytes_tail<4>(hi, sl.shB);
   const uint32_t r[12] = {lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7], hi[0], hi[1], hi[2], hi[3]};
-  const char* t = reinterpret_cast<const char*>(lut);
+  // bytes: [0] = column offset, [1] = code byte i, [2], [3] = 0  ->  256 c + 4 j
+  auto addr = [&](int i) {
+    return __builtin_amdgcn_perm(r[i >> 2], sl.col[i], 0x0c0c0000u | ((uint32_t)(4 + (i & 3)) << 8));
+  };
   float acc = 0.f;
+  if constexpr (F16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-  for (int i = 0; i < 48; ++i) {
-    // bytes: [0] = column offset, [1] = code byte i, [2], [3] = 0  ->  256 c + 4 j
-    const uint32_t sel = 0x0c0c0000u | ((uint32_t)(4 + (i & 3)) << 8);
-    const uint32_t a = __builtin_amdgcn_perm(r[i >> 2], sl.col[i], sel);
-    acc += *reinterpret_cast<const float*>(t + a);
+    for (int i = 0; i < 48; i += 2) {
+      const h2 p = {*reinterpret_cast<const _Float16*>(t + addr(i)), *reinterpret_cast<const _Float16*>(t + addr(i + 1))};
+      acc = __builtin_amdgcn_fdot2(p, one, acc, false);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 48; ++i) acc += *reinterpret_cast<const float*>(t + addr(i));
   }
   return acc;
 }

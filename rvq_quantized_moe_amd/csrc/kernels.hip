@@ -660,17 +660,16 @@ __device__ __forceinline__ void k_moe_gateup_body(BankArgs bank, const float* __
 // 8 x 16 matrix of the tile's x sub-vectors, computed with fp32 MFMAs: builder wave w owns 16-entry
 // table tiles 12w .. 12w+11.  With lane l = 16q + i (q < 4), A holds codebook entry i of the table
 // tile at dims 2q, 2q+1 (one per MFMA), B holds group i's x at the same dims, and D returns
-// entries 4q..4q+3 of group i, stored as one 16-byte LDS write (conflict-free because subtables
-// are kPipeStride = 260 floats apart).  The codebook operands are the same for every item of the
-// workgroup and are loaded once, before the start barrier.
+// entries 4q..4q+3 of group i, written to rows 4q..4q+3 of the subtable's column of the skewed
+// layout (see SkewLane; subtables 32..47 twice).  The codebook operands are the same for every
+// item of the workgroup and are loaded once, before the start barrier.
 //
 // fp16 tables (F16): entries are stored scaled by 2^-e_k, e_k = f16_table_exponent(max |c| max |x_g|)
-// over the codebook and the item's 16 groups (so no entry can overflow), 4 entries per 8-byte
-// write with subtables kPipeStride16 = 264 halves apart; the streamers scale each item's sums by
-// 2^e_k before adding them to the row totals.
+// over the codebook and the item's 16 groups (so no entry can overflow); the streamers scale each
+// item's sums by 2^e_k before adding them to the row totals.  The two fp16 tables share one skewed
+// array of 32-bit words, table k & 1 in half k & 1 of each word: the lookups keep the fp32
+// layout's addresses (and its conflict-free banks), and both tables take 64 KiB.
 constexpr int kPipeBuildWaves = 4;
-constexpr int kPipeStride = 260;       // floats between subtables
-constexpr int kPipeStride16 = 264;     // halves between subtables (fp16 tables)
 constexpr int kPipeMaxItems = 8;
 constexpr int kPipeMaxGu = 8;          // down: most gate/up partials per row
 constexpr int kGuStreamWaves = 8, kGuBpi = 4;     // gate/up: 32 row blocks (I in (1984, 2048])
@@ -738,10 +737,12 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
   constexpr int NB = 3;   // row blocks of codes held per streamer wave (deeper measured slower)
   constexpr int NBLK = ITEMS * BPI;
   constexpr int TPW = 48 / kPipeBuildWaves;                 // table tiles per builder wave
-  typedef typename Tile<F16>::entry_t T;
-  constexpr int S = F16 ? kPipeStride16 : kPipeStride;
   // fp32: skewed 64-column tables (see SkewLane); fp16: 48 subtables S halves apart
-  __shared__ __attribute__((aligned(16))) T lut[2][F16 ? 48 * S : kSkewWords];
+  __shared__ __attribute__((aligned(16))) float lut[F16 ? 1 : 2][kSkewWords];
+  // item k's table: fp32, buffer k & 1; fp16, half k & 1 of every word of the one buffer
+  auto table = [&](int k) -> char* {
+    return F16 ? reinterpret_cast<char*>(&lut[0][0]) + 2 * (k & 1) : reinterpret_cast<char*>(&lut[k & 1][0]);
+  };
   __shared__ __attribute__((aligned(16))) float hs[DOWN ? ITEMS : 1][128];
   __shared__ int built[2], done[2], hready;
   __shared__ int cmax_bits;            // fp16: max squared codebook-entry norm (bits of a float >= 0)
@@ -862,57 +863,32 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
 #pragma unroll
     for (int r = 0; r < BPI; ++r) acc[r] = 0.f;
     bool ok = true;
-    if constexpr (F16) {
-      SlabData buf[NB];
-      const uint32_t lane_off = lane * 16;
-      auto load_blk = [&](int i, int s) {
-        const int k = s / BPI, r = s % BPI;
-        load_slabs<false>(buf[i], codes + k * tile_bytes, codes + k * tile_bytes,
-                          (uint32_t)(wave + NSW * r) * kSlabBytes + lane_off);
-      };
+    SlabData buf[NB];
+    const uint32_t lane_off = lane * 16;
+    SkewLane sl;
+    sl.init(lane);
+    auto load_blk = [&](int i, int s) {
+      const int k = s / BPI, r = s % BPI;
+      load_slabs<false>(buf[i], codes + k * tile_bytes, codes + k * tile_bytes,
+                        (uint32_t)(wave + NSW * r) * kSlabBytes + lane_off);
+    };
 #pragma unroll
-      for (int i = 0; i < NB; ++i) load_blk(i, i);
+    for (int i = 0; i < NB; ++i) load_blk(i, i);
 #pragma unroll
-      for (int k = 0; k < ITEMS; ++k) {
-        ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1), pa.wait_limit);
+    for (int k = 0; k < ITEMS; ++k) {
+      ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1), pa.wait_limit);
 #pragma unroll
-        for (int r = 0; r < BPI; ++r) {
-          const int s = k * BPI + r;
-          float g = gather_slab1<F16, S>(lut[k & 1], buf[s % NB]);
-          // opaque use: without it the compiler interleaves the row blocks' gathers into one
-          // another and spills
-          asm volatile("" : : "v"(g));
-          g *= escale[k];
-          acc[r] += g;
-          if (s + NB < NBLK) load_blk(s % NB, s + NB);
-        }
-        if (lane == 0) __hip_atomic_fetch_add(&done[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      for (int r = 0; r < BPI; ++r) {
+        const int s = k * BPI + r;
+        float g = gather_skew<F16>(table(k), buf[s % NB], sl);
+        // opaque use: without it the compiler interleaves the row blocks' gathers into one another
+        // and spills
+        asm volatile("" : : "v"(g));
+        if constexpr (F16) g *= escale[k];
+        acc[r] += g;
+        if (s + NB < NBLK) load_blk(s % NB, s + NB);
       }
-    } else {
-      SlabData buf[NB];
-      const uint32_t lane_off = lane * 16;
-      SkewLane sl;
-      sl.init(lane);
-      auto load_blk = [&](int i, int s) {
-        const int k = s / BPI, r = s % BPI;
-        load_slabs<false>(buf[i], codes + k * tile_bytes, codes + k * tile_bytes,
-                          (uint32_t)(wave + NSW * r) * kSlabBytes + lane_off);
-      };
-#pragma unroll
-      for (int i = 0; i < NB; ++i) load_blk(i, i);
-#pragma unroll
-      for (int k = 0; k < ITEMS; ++k) {
-        ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1), pa.wait_limit);
-#pragma unroll
-        for (int r = 0; r < BPI; ++r) {
-          const int s = k * BPI + r;
-          float g = gather_skew(lut[k & 1], buf[s % NB], sl);
-          asm volatile("" : : "v"(g));
-          acc[r] += g;
-          if (s + NB < NBLK) load_blk(s % NB, s + NB);
-        }
-        if (lane == 0) __hip_atomic_fetch_add(&done[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
+      if (lane == 0) __hip_atomic_fetch_add(&done[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     float* out = pa.out + (int64_t)blockIdx.x * pad_rows(rows) + (int64_t)rb0 * kSlabRows;
     if constexpr (DOWN) out = pa.out + ((int64_t)slot * pa.nchunk + (blockIdx.x % pa.nchunk)) * pad_rows(rows) +
@@ -977,25 +953,31 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
         scale = ldexpf(1.f, -ex);
         if (bw == 0 && lane == 0) escale[k] = ldexpf(1.f, ex);
       }
-      T* L = lut[k & 1];
+      char* L = table(k);
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int ti = bw * TPW + t, st = ti >> 4, e0 = (ti & 15) * 16;
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
         d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].x, xk.x, d, 0, 0, 0);
         d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t].y, xk.y, d, 0, 0, 0);
+        // skewed layout: entry c of subtable j at word 64 c + j; subtables 32..47 also at j + 16
+        const int j = 3 * i16 + st, c0 = e0 + 4 * q;
         if constexpr (F16) {
-          const half4 hv = {(f16)(d.x * scale), (f16)(d.y * scale), (f16)(d.z * scale), (f16)(d.w * scale)};
-          *reinterpret_cast<half4*>(&L[(3 * i16 + st) * S + e0 + 4 * q]) = hv;
+          _Float16* col = reinterpret_cast<_Float16*>(L) + 2 * (kSkewCols * c0 + j);   // half k & 1 of the word
+          const _Float16 h[4] = {(_Float16)(d.x * scale), (_Float16)(d.y * scale), (_Float16)(d.z * scale),
+                                 (_Float16)(d.w * scale)};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            col[2 * kSkewCols * u] = h[u];
+            if (j >= 32) col[2 * kSkewCols * u + 32] = h[u];
+          }
         } else {
-          // skewed layout: entry c of subtable k at word 64 c + k; subtables 32..47 also at k + 16
-          const int k = 3 * i16 + st, c0 = e0 + 4 * q;
-          float* col = L + kSkewCols * c0 + k;
+          float* col = reinterpret_cast<float*>(L) + kSkewCols * c0 + j;
           col[0] = d.x;
           col[kSkewCols] = d.y;
           col[2 * kSkewCols] = d.z;
           col[3 * kSkewCols] = d.w;
-          if (k >= 32) {
+          if (j >= 32) {
             col[16] = d.x;
             col[kSkewCols + 16] = d.y;
             col[2 * kSkewCols + 16] = d.z;
