@@ -39,9 +39,10 @@ WEIGHTS_PER_TOKEN = K * 3 * H * I                         # 704,643,072
 GATEUP_CODE_BYTES = K * 2 * (H * I * 3 // 8)              # 176,160,768 per gate/up launch
 GATEUP_CODEBOOK_BYTES = K * 2 * 3 * 256 * 8 * 4           # 786,432
 DOWN_CODE_BYTES = K * (H * I * 3 // 8)
-# chip-wide lookups/s of the LDS gather each table layout allows, measured with the same per-lookup
-# code: fp32 tables in the skewed layout (32 distinct banks per pass), fp16 tables read at random
-LDS_GATHER_RATE = {"f32": 11.2e12, "f16": 6.92e12}
+# chip-wide lookups/s of the LDS gather the skewed table layout allows (32 distinct banks per pass),
+# measured with 32-bit reads and the kernel's per-lookup code; the fp16 tables use the same layout
+# and addresses with 16-bit reads, which take the same passes (this figure is assumed for them)
+LDS_GATHER_RATE = {"f32": 11.2e12, "f16": 11.2e12}
 KERNEL_SOURCES = ["rvq_quantized_moe_amd/csrc/kernels.hip", "rvq_quantized_moe_amd/csrc/device.hpp"]   # decode kernels
 
 
@@ -810,8 +811,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic_from_profiles(args.dtype),
                      "algorithmic_bytes_per_launch": GATEUP_CODE_BYTES + GATEUP_CODEBOOK_BYTES},
-        # the table kernels' LDS ceiling: one lookup per code byte, at the gather rate measured for the
-        # table layout (skewed fp32 columns, or random ds_read_u16 over 256-half fp16 subtables)
+        # the table kernels' LDS ceiling: one lookup per code byte, at the skewed layout's gather rate
         "lds_gather": {"kernel": "gate/up", "lookups_per_s": GATEUP_CODE_BYTES / (gu_us * 1e-6),
                        "ceiling_lookups_per_s": LDS_GATHER_RATE[args.dtype],
                        "frac": GATEUP_CODE_BYTES / (gu_us * 1e-6) / LDS_GATHER_RATE[args.dtype]},

@@ -320,24 +320,6 @@ __device__ __forceinline__ void load_slabs(SlabData& s, const uint8_t* __restric
   }
 }
 
-// One slab (16 groups, three 16-byte code words per lane) through tables of either precision.
-template <bool F16, int STRIDE>
-__device__ __forceinline__ float gather_slab1(const void* lut, const SlabData& s) {
-  float acc = 0.f;
-  if constexpr (F16) {
-    const f16* t = static_cast<const f16*>(lut);
-    acc = gather16_f16<0, STRIDE>(t, s.d[0], acc);
-    acc = gather16_f16<16, STRIDE>(t, s.d[1], acc);
-    acc = gather16_f16<32, STRIDE>(t, s.d[2], acc);
-  } else {
-    const float* t = static_cast<const float*>(lut);
-    acc = gather16_f32<0, STRIDE>(t, s.d[0], acc);
-    acc = gather16_f32<16, STRIDE>(t, s.d[1], acc);
-    acc = gather16_f32<32, STRIDE>(t, s.d[2], acc);
-  }
-  return acc;
-}
-
 template <bool F16, int STRIDE = kEntries>
 __device__ __forceinline__ float gather_slabs(const void* lut, const SlabData& s) {
   float acc = 0.f;
