@@ -545,10 +545,93 @@ hipError_t launch_router_norm_logits(const uint16_t* w, const float* h, int E, i
   return hipGetLastError();
 }
 
+// Router logits of several tokens: workgroup (b, c) computes experts ET b .. ET b + ET-1 for tokens
+// TT c .. TT c + TT-1, so each router row is read once per TT tokens and each token row once per ET
+// experts.  Every (expert, token) sum takes exactly the steps of k_router_logits (router_dot's
+// pieces q = tid, tid + 256, ... in increasing q, even elements into a0 and odd into a1, fp64
+// fma; then a0 + a1, the same shuffle tree and the same four-wave sum), so the logits are those
+// of one token at a time, bit for bit.  Needs H % 8 == 0 and 16-byte aligned rows; out-of-range
+// experts and tokens load a valid row and are not written.
+template <typename XT, int ET, int TT>
+__global__ __launch_bounds__(256) void k_router_logits_tiles(const uint16_t* __restrict__ w, const XT* __restrict__ x,
+                                                             int T, int E, int H, double* __restrict__ logits) {
+  constexpr int U = 2;   // pieces per thread with loads in flight together
+  __shared__ double red[ET * TT][4];
+  const int e0 = blockIdx.x * ET, t0 = blockIdx.y * TT;
+  const uint16_t* wr[ET];
+  const XT* xr[TT];
+#pragma unroll
+  for (int i = 0; i < ET; ++i) wr[i] = w + (int64_t)min(e0 + i, E - 1) * H;
+#pragma unroll
+  for (int t = 0; t < TT; ++t) xr[t] = x + (int64_t)min(t0 + t, T - 1) * H;
+  double a0[ET][TT], a1[ET][TT];
+#pragma unroll
+  for (int i = 0; i < ET; ++i)
+#pragma unroll
+    for (int t = 0; t < TT; ++t) a0[i][t] = a1[i][t] = 0.0;
+  const int n8 = H / 8;
+  for (int q0 = threadIdx.x; q0 < n8; q0 += 256 * U) {
+    u32x4 wv[U][ET];
+    RawX8<XT> xv[U][TT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = min(q0 + 256 * u, n8 - 1);
+#pragma unroll
+      for (int i = 0; i < ET; ++i) wv[u][i] = *reinterpret_cast<const u32x4*>(wr[i] + q * 8);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) xv[u][t].load(xr[t] + q * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (q0 + 256 * u < n8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int i = 0; i < ET; ++i) {
+            const double we = bf16_to_f64((uint16_t)(wv[u][i][j] & 0xffffu));
+            const double wo = bf16_to_f64((uint16_t)(wv[u][i][j] >> 16));
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+              a0[i][t] = fma(we, xv[u][t].get(2 * j), a0[i][t]);
+              a1[i][t] = fma(wo, xv[u][t].get(2 * j + 1), a1[i][t]);
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < ET; ++i)
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      double acc = a0[i][t] + a1[i][t];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      if ((threadIdx.x & 63) == 0) red[i * TT + t][threadIdx.x >> 6] = acc;
+    }
+  __syncthreads();
+  if (threadIdx.x < ET * TT) {
+    const int i = threadIdx.x / TT, t = threadIdx.x % TT;
+    const double* r = red[threadIdx.x];
+    if (e0 + i < E && t0 + t < T) logits[(int64_t)(t0 + t) * E + e0 + i] = (r[0] + r[1]) + (r[2] + r[3]);
+  }
+}
+constexpr int kRouterTileE = 4, kRouterTileT = 4;
+
 hipError_t launch_router_logits(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, double* logits,
                                 hipStream_t stream) {
   const int vec = (H % 8 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0) &&
                   ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  if (T > 1 && vec) {
+    const dim3 tiles((unsigned)cdiv(E, kRouterTileE), (unsigned)cdiv(T, kRouterTileT));
+    if (x_bf16)
+      hipLaunchKernelGGL((k_router_logits_tiles<uint16_t, kRouterTileE, kRouterTileT>), tiles, dim3(256), 0, stream, w,
+                         static_cast<const uint16_t*>(x), T, E, H, logits);
+    else
+      hipLaunchKernelGGL((k_router_logits_tiles<float, kRouterTileE, kRouterTileT>), tiles, dim3(256), 0, stream, w,
+                         static_cast<const float*>(x), T, E, H, logits);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)E, (unsigned)T);
   if (x_bf16)
     hipLaunchKernelGGL(k_router_logits<uint16_t>, grid, dim3(256), 0, stream, w, static_cast<const uint16_t*>(x), T,

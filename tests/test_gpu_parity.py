@@ -156,6 +156,32 @@ def test_router_bf16_tokens():
         np.testing.assert_allclose(gates[t].cpu().numpy(), gates_o, rtol=1e-6)
 
 
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("E,H,T", [(37, 7168, 7), (256, 264, 5), (8, 7168, 64)])
+def test_router_tiles_equal_one_token(x_dtype, E, H, T):
+    """Several tokens at once (4-expert x 4-token tiles) give every token the logits, ids and gates
+    of a one-token call bit for bit, with experts and tokens ragged against the tiles, and agree
+    with the oracle's fp64 logits to rounding."""
+    say(f"router tiles E={E} H={H} T={T} {x_dtype}")
+    bits = synth.router_bf16_bits(0x7A ^ E, 0, E, H)
+    w = to_dev(bits.view(np.int16)).view(torch.bfloat16)
+    if x_dtype == "f32":
+        X = np.stack([synth.activation_f32(0x7A, t, H) for t in range(T)])
+        Xd, Xo = to_dev(X), X.astype(np.float64)
+    else:
+        Xb = np.stack([synth.activation_bf16_bits(0x7A, t, H) for t in range(T)])
+        Xd = to_dev(Xb.view(np.int16)).view(torch.bfloat16)
+        Xo = (Xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    k = min(16, E)
+    ids, gates, logits = rvq.router_topk(w, Xd, k)
+    for t in range(T):
+        ids1, gates1, logits1 = rvq.router_topk(w, Xd[t], k)
+        assert torch.equal(logits[t], logits1[0]), t
+        assert torch.equal(ids[t], ids1[0]) and torch.equal(gates[t], gates1[0]), t
+    lo = oracle.router_logits(bits, Xo)
+    np.testing.assert_allclose(logits.cpu().numpy(), lo, rtol=1e-12, atol=1e-12 * np.abs(lo).max())
+
+
 def test_router_exact_ties_and_edge_k():
     say("router ties")
     E, H = 12, 32
