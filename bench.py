@@ -565,7 +565,8 @@ def run_stack_pool(torch, rvq, dev, layers=8, slots=128, tokens=12):
 
 
 def run_matvec(torch, rvq, dev, steps):
-    """One 256x512 RVQ matvec (fp32 tables): microseconds per call, graph-replayed."""
+    """One 256x512 RVQ matvec (fp32 tables): microseconds per call, from a graph of 8 calls (and from
+    one graph per call, beside it)."""
     import synth
     from workloads import MATVEC_COLS, MATVEC_ROWS
     R, C = MATVEC_ROWS, MATVEC_COLS
@@ -576,14 +577,20 @@ def run_matvec(torch, rvq, dev, steps):
     y = torch.empty(R, dtype=torch.float32, device=dev)
     ws = torch.empty(max(rvq.gemv_workspace_bytes(R, C, "f32"), 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-    graphs = [capture(torch, lambda x=x: rvq.expert_gemv(packed, cb, R, C, x, "f32", y=y, workspace=ws)) for x in xs]
-    sec = replay_rate(torch, graphs, steps, 20)
-    return {"us_per_call": sec * 1e6, "code_GBps": R * C * 3 / 8 / sec / 1e9}
+    one = [capture(torch, lambda x=x: rvq.expert_gemv(packed, cb, R, C, x, "f32", y=y, workspace=ws)) for x in xs]
+    sec1 = replay_rate(torch, one, steps, 20)
+    # the 8 calls in one graph, one after another (as in a full model's graph)
+    def calls():
+        for x in xs:
+            rvq.expert_gemv(packed, cb, R, C, x, "f32", y=y, workspace=ws)
+    sec = replay_rate(torch, [capture(torch, calls)], max(1, steps // len(xs)), 3) / len(xs)
+    return {"us_per_call": sec * 1e6, "code_GBps": R * C * 3 / 8 / sec / 1e9, "us_per_call_one_per_graph": sec1 * 1e6}
 
 
 def run_expert(torch, rvq, bank, pool, steps):
     """One SwiGLU expert (7168/2048, fp32 tables) per token: the layer forward with k = 1, rotating
-    over 32 of the resident experts so that no expert stays cached; microseconds per token."""
+    over 32 of the resident experts so that no expert stays cached; microseconds per token, from
+    graphs of STEPS_PER_GRAPH tokens (and from one graph per token, beside it)."""
     dev = pool.device
     ids = [torch.tensor([e], dtype=torch.int32, device=dev) for e in range(0, 256, 8)]
     one = torch.ones(1, dtype=torch.float32, device=dev)
@@ -592,11 +599,18 @@ def run_expert(torch, rvq, bank, pool, steps):
     torch.cuda.synchronize()
     graphs = [capture(torch, lambda j=j: rvq.moe_layer_forward(bank, pool[j % POOL], ids[j], one, dtype="f32", y=y,
                                                                workspace=ws)) for j in range(len(ids))]
-    sec = replay_rate(torch, graphs, steps, 20)
+    sec1 = replay_rate(torch, graphs, steps, 20)
+    # STEPS_PER_GRAPH tokens in one graph, one after another (as in a full model's graph)
+    def tokens(j0):
+        for j in range(j0, j0 + STEPS_PER_GRAPH):
+            rvq.moe_layer_forward(bank, pool[j % POOL], ids[j], one, dtype="f32", y=y, workspace=ws)
+    multi = [capture(torch, lambda j0=j0: tokens(j0)) for j0 in range(0, len(ids), STEPS_PER_GRAPH)]
+    sec = replay_rate(torch, multi, max(1, steps // STEPS_PER_GRAPH), 3) / STEPS_PER_GRAPH
     status = rvq.check_device_status(ws)
     if status:
         raise RuntimeError(rvq.status_string(status))
-    return {"us_per_token": sec * 1e6, "code_GBps": 3 * (H * I * 3 // 8) / sec / 1e9}
+    return {"us_per_token": sec * 1e6, "code_GBps": 3 * (H * I * 3 // 8) / sec / 1e9,
+            "us_per_token_one_per_graph": sec1 * 1e6}
 
 
 def run_stack(torch, rvq, dev, dtype):
