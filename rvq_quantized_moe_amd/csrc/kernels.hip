@@ -807,6 +807,7 @@ struct PipeArgs {
   float* gates_out;
   int k;
   int wait_limit;         // polls per bounded wait (kSpinLimit unless a test lowers it)
+  int gu_stride;          // down: partials stored per (slot, matrix) in part_gu (>= ngu)
 };
 constexpr int kRouteMaxExperts = 1024;
 
@@ -862,8 +863,8 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
   if constexpr (DOWN) {
     if (!streamer) {
       const int64_t Ip = pad_rows(I);
-      const float* pg = pa.part_gu + (int64_t)slot * 2 * pa.ngu * Ip;
-      const float* pu = pg + (int64_t)pa.ngu * Ip;
+      const float* pg = pa.part_gu + (int64_t)slot * 2 * pa.gu_stride * Ip;
+      const float* pu = pg + (int64_t)pa.gu_stride * Ip;
 #pragma unroll
       for (int n = 0; n < HI; ++n) {
         const int k = bw + n * kPipeBuildWaves < ITEMS ? bw + n * kPipeBuildWaves : ITEMS - 1;
@@ -1257,6 +1258,26 @@ MoeWorkspace moe_workspace_layout(int H, int I, int k, bool f16) {
   return w;
 }
 
+// Sums the gate/up partials of each (slot, matrix) row into partial 0, in ascending partial order
+// (the order the down kernel's prologue adds them in), so that down reads one partial per row.  In
+// place: each element is read and written by one thread.  part_gu: [P][2][stride][Ip].
+__global__ __launch_bounds__(256) void k_sum_gu_partials(float* __restrict__ part_gu, int ngu, int stride, int64_t Ip) {
+  constexpr int U = 32;   // partials in flight per thread
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= Ip) return;
+  float* p = part_gu + (int64_t)blockIdx.y * stride * Ip + i;
+  float s = 0.f;
+  for (int p0 = 0; p0 < ngu; p0 += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = p0 + u < ngu ? p[(int64_t)(p0 + u) * Ip] : 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (p0 + u < ngu) s += v[u];
+  }
+  p[0] = s;
+}
+
 // T tokens of decode (T = 1 for the single-token entry points).  Pair p = t k + i (token t's i-th
 // expert) is one "slot" of the kernels, which read x, residual and y at row p / k; the chunk sizes
 // are chosen from one token's counts, so every pair is computed exactly as in a single-token call.
@@ -1303,7 +1324,10 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
   constexpr int kDnRows = kDnStreamWaves * kDnBpi;
   const int nrb_h = (int)cdiv(H, kSlabRows);
   const int nrc = nrb_h / kDnRows;
-  const int dchunk = (chunk && I % 128 == 0 && nrb_h % kDnRows == 0 && ngu <= kPipeMaxGu)
+  // more gate/up partials than the down prologue reads (few slots: gate/up took few K-tiles per
+  // workgroup to fill the CUs) are first summed into one
+  const bool sum_gu = chunk && ngu > kPipeMaxGu;
+  const int dchunk = (chunk && I % 128 == 0 && nrb_h % kDnRows == 0)
                          ? pick_chunk(nt16_out, (long)k * nrc)
                          : 0;
   const int nparts_d = dchunk ? nt16_out / dchunk : w.nt_out;
@@ -1330,7 +1354,7 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
   if (chunk) {
     const dim3 grid((unsigned)(P * 2 * ngu));
     const PipeArgs pa{x,       nullptr, part_gu, ngu, 1, 0, fused_route ? route->logits : nullptr,
-                      route ? route->ids : nullptr, route ? route->gates : nullptr, k, g_wait_limit};
+                      route ? route->ids : nullptr, route ? route->gates : nullptr, k, g_wait_limit, 0};
     switch (chunk) {
 #define RVQ_WS_CASE(n)                                                                                             \
   case n:                                                                                                          \
@@ -1354,9 +1378,13 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
   }
   mark(1);
   if (dchunk) {
+    if (sum_gu)
+      hipLaunchKernelGGL(k_sum_gu_partials, dim3((unsigned)cdiv(pad_rows(I), 256), (unsigned)(P * 2)), dim3(256), 0,
+                         stream, part_gu, ngu, ngu, (int64_t)pad_rows(I));
     const int nkc = nt16_out / dchunk;
     const dim3 grid((unsigned)(P * nrc * nkc));
-    const PipeArgs pa{nullptr, part_gu, part_d, nkc, nrc, ngu, nullptr, nullptr, nullptr, k, g_wait_limit};
+    const PipeArgs pa{nullptr, part_gu, part_d, nkc, nrc, sum_gu ? 1 : ngu, nullptr, nullptr, nullptr, k,
+                      g_wait_limit, ngu};
     switch (dchunk) {
 #define RVQ_WS_CASE(n)                                                                                             \
   case n:                                                                                                          \
