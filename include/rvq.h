@@ -184,9 +184,11 @@ int rvq_moe_layer_forward(const rvq_expert_bank_t *bank, const void *x, int32_t 
 
 /* Same as rvq_moe_layer_forward, and records events[0..3] on `stream`
  * around its kernels: [0] before the gate/up table kernel, [1] between it
- * and the SwiGLU+down kernel, [2] before the gated combine, [3] after it, so
- * a caller can time each kernel with hipEventElapsedTime.  events: host array
- * of 4 caller-created events (none NULL). */
+ * and the SwiGLU+down stage (with few experts, k = 1 for instance, that stage
+ * first sums the gate/up partial sums in a small kernel of its own), [2]
+ * before the gated combine, [3] after it, so a caller can time each stage
+ * with hipEventElapsedTime.  events: host array of 4 caller-created events
+ * (none NULL). */
 int rvq_moe_layer_forward_timed(const rvq_expert_bank_t *bank, const void *x, int32_t x_dtype, int32_t T,
                                 const int32_t *ids, const float *gates, int32_t k, const float *residual, float *y,
                                 int32_t compute_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream,
