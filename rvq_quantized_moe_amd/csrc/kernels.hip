@@ -957,7 +957,7 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
                         (uint32_t)(wave + NSW * r) * kSlabBytes + lane_off);
     };
 #pragma unroll
-    for (int i = 0; i < NB; ++i) load_blk(i, i);
+    for (int i = 0; i < NB && i < NBLK; ++i) load_blk(i, i);   // never past the workgroup's blocks
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
       ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1), pa.wait_limit);
@@ -1321,15 +1321,27 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
                         ? pick_chunk(nt16_in, 2L * k)
                         : 0;
   const int ngu = chunk ? nt16_in / chunk : w.nt_in;
-  constexpr int kDnRows = kDnStreamWaves * kDnBpi;
+  // down: row chunks of kDnBpi row blocks per streamer wave, or of one when few slots would leave
+  // CUs idle (only with 1 or 2 K-tiles per workgroup).  Only the rows a workgroup takes change, never
+  // the K-tiles it sums, so every result is the same either way.  The work estimate is rounds x
+  // K-tiles x row blocks per wave; ties keep kDnBpi.
   const int nrb_h = (int)cdiv(H, kSlabRows);
-  const int nrc = nrb_h / kDnRows;
+  int dn_bpi = kDnBpi;
+  int nrc = nrb_h / (kDnStreamWaves * kDnBpi);
   // more gate/up partials than the down prologue reads (few slots: gate/up took few K-tiles per
   // workgroup to fill the CUs) are first summed into one
   const bool sum_gu = chunk && ngu > kPipeMaxGu;
-  const int dchunk = (chunk && I % 128 == 0 && nrb_h % kDnRows == 0)
-                         ? pick_chunk(nt16_out, (long)k * nrc)
-                         : 0;
+  const int dchunk = (chunk && I % 128 == 0 && nrb_h % (kDnStreamWaves * kDnBpi) == 0)
+                   ? pick_chunk(nt16_out, (long)k * nrc)
+                   : 0;
+  if (dchunk && dchunk <= 2 && ncu > 0) {   // one token's counts only (see above)
+    const int nrc1 = nrb_h / kDnStreamWaves;
+    auto cost = [&](int rows_per_wave, int chunks) {
+      const long grid = (long)k * chunks * (nt16_out / dchunk);
+      return (grid + ncu - 1) / ncu * dchunk * rows_per_wave;
+    };
+    if (cost(1, nrc1) < cost(kDnBpi, nrc)) dn_bpi = 1, nrc = nrc1;
+  }
   const int nparts_d = dchunk ? nt16_out / dchunk : w.nt_out;
   if (T > 1 && !(chunk && dchunk)) {
     for (int t = 0; t < T; ++t) {
@@ -1385,7 +1397,20 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
     const dim3 grid((unsigned)(P * nrc * nkc));
     const PipeArgs pa{nullptr, part_gu, part_d, nkc, nrc, sum_gu ? 1 : ngu, nullptr, nullptr, nullptr, k,
                       g_wait_limit, ngu};
-    switch (dchunk) {
+    if (dn_bpi == 1) {
+#define RVQ_WS_CASE1(n)                                                                                            \
+  case n:                                                                                                          \
+    if (f16)                                                                                                       \
+      hipLaunchKernelGGL((k_table_ws<true, true, kDnStreamWaves, 1, n>), grid, dim3(64 * (kDnStreamWaves + 4)), 0,   \
+                         stream, bank, ids, status, pa);                                                           \
+    else                                                                                                           \
+      hipLaunchKernelGGL((k_table_ws<false, true, kDnStreamWaves, 1, n>), grid, dim3(64 * (kDnStreamWaves + 4)), 0,  \
+                         stream, bank, ids, status, pa);                                                           \
+    break;
+      switch (dchunk) { RVQ_WS_CASE1(1) RVQ_WS_CASE1(2) }
+#undef RVQ_WS_CASE1
+    } else {
+      switch (dchunk) {
 #define RVQ_WS_CASE(n)                                                                                             \
   case n:                                                                                                          \
     if (f16)                                                                                                       \
@@ -1395,9 +1420,10 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
       hipLaunchKernelGGL((k_table_ws<false, true, kDnStreamWaves, kDnBpi, n>), grid, dim3(64 * (kDnStreamWaves + 4)),  \
                          0, stream, bank, ids, status, pa);                                                        \
     break;
-      RVQ_WS_CASE(1) RVQ_WS_CASE(2) RVQ_WS_CASE(3) RVQ_WS_CASE(4)
-      RVQ_WS_CASE(5) RVQ_WS_CASE(6) RVQ_WS_CASE(7) RVQ_WS_CASE(8)
+        RVQ_WS_CASE(1) RVQ_WS_CASE(2) RVQ_WS_CASE(3) RVQ_WS_CASE(4)
+        RVQ_WS_CASE(5) RVQ_WS_CASE(6) RVQ_WS_CASE(7) RVQ_WS_CASE(8)
 #undef RVQ_WS_CASE
+      }
     }
   } else if (f16) {
     RVQ_BPW_DISPATCH(bpw_d, hipLaunchKernelGGL((k_moe_down_f16<B>), dim3(k * w.nt_out * nparts), dim3(kDownThreads), 0,
