@@ -1300,9 +1300,9 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
   };
   mark(0);
   // The wave-specialised kernels: gate/up needs I in (1984, 2048] and whole
-  // 16-group K-tiles; down needs I a multiple of 128, H a multiple of 28 row blocks, and at most
-  // kPipeMaxGu gate/up partials.  Each sums `c` K-tiles per workgroup, c chosen to fill the CUs in
-  // as few rounds as possible (ties: the larger c, i.e. fewer partials).
+  // 16-group K-tiles; down needs I a multiple of 128 and H a multiple of 28 row blocks (more than
+  // kPipeMaxGu gate/up partials are summed into one first).  Each sums `c` K-tiles per workgroup,
+  // c chosen to fill the CUs in as few rounds as possible (ties: the larger c, i.e. fewer partials).
   const int ncu = compute_units();
   auto pick_chunk = [&](int ntiles, long per_chunk_groups) {
     int best_c = 0;
