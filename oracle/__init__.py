@@ -17,17 +17,19 @@ module marshals numpy arrays and composes the per-layer steps:
                    router-prediction section: 16 expert ids chosen per layer;
                    the starlog page, "Technical Insight": low-ranked experts
                    still matter, so none is dropped)
-  moe_layer(x)   = [residual +] sum_i gate_i * expert_{id_i}(x)
+  moe_mix(x)     = [residual +] sum_i gate_i * expert_{id_i}(x) for given ids and gates
+  moe_layer(x)   = route(x), then moe_mix
   stack step     = for each layer: n = rmsnorm(h); h += moe_layer_l(n)
   rvq_encode(W)  = codes [rows, cols/8, 3] of W by residual (stage-by-stage nearest
-                   entry) quantisation, decisions in fp32 (the decode's inverse)
+                   entry) quantisation, distances and residuals in fp64 (the decode's
+                   inverse); optionally each decision's best and second-best distance
   crc32(bytes)   = CRC-32 (IEEE 802.3, reflected, preset and final complement) of a
                    record's code payload, bit by bit (news.hada.io topic 32035,
                    disk-streaming architecture section: optional payload crc32)
   rvq_fit(W)     = codebooks [3, 256, 8] and codes of W by residual k-means: per stage,
                    Lloyd iterations from given initial sub-vectors (nearest entry as in
-                   rvq_encode; means in fp64 over runs of 2048 sub-vectors, then across
-                   runs, in ascending order), then the stage's codes and its residual
+                   rvq_encode; each mean one fp64 sum over its members in ascending
+                   index), then the stage's codes and its residual
 
 Parity status of each function (what pins it) is listed in tests/test_oracle_pins.py.
 """
@@ -69,7 +71,7 @@ def _load():
         lib.orc_router_logits.argtypes = [p, p, i64, i64, i64, p, i32]
         lib.orc_topk.argtypes = [p, i64, i64, p, p, p]
         lib.orc_rmsnorm.argtypes = [p, i64, ctypes.c_double, p]
-        lib.orc_rvq_encode.argtypes = [p, i64, i64, p, p]
+        lib.orc_rvq_encode.argtypes = [p, i64, i64, p, p, p]
         lib.orc_crc32.argtypes = [p, i64]
         lib.orc_rvq_fit.argtypes = [p, i64, i64, i32, p, p, p, i32]
         lib.orc_rvq_fit.restype = None
@@ -207,6 +209,19 @@ def rmsnorm(h, eps=1e-6):
     return out
 
 
+def moe_mix(get_expert, x, ids, gates, residual=None, rowsel=None):
+    """[residual +] sum_i gates[i] * expert_{ids[i]}(x) for given ids and gates, in slot order (fp64)."""
+    x = np.asarray(x, dtype=np.float64)
+    y = None
+    for e, g in zip(np.asarray(ids).reshape(-1), np.asarray(gates, dtype=np.float64).reshape(-1)):
+        yi = expert(get_expert(int(e)), x, rowsel)
+        y = g * yi if y is None else y + g * yi
+    if residual is not None:
+        r = np.asarray(residual, dtype=np.float64)
+        y = y + (r if rowsel is None else r[np.asarray(rowsel)])
+    return y
+
+
 def moe_layer(get_expert, router_bits, x, k, residual=None, rowsel=None):
     """One decode token through one MoE layer.
 
@@ -215,14 +230,7 @@ def moe_layer(get_expert, router_bits, x, k, residual=None, rowsel=None):
     x = np.asarray(x, dtype=np.float64)
     logits = router_logits(router_bits, x[None, :])[0]
     ids, gates, gaps = topk(logits, k)
-    y = None
-    for i in range(k):
-        yi = expert(get_expert(int(ids[i])), x, rowsel)
-        y = gates[i] * yi if y is None else y + gates[i] * yi
-    if residual is not None:
-        r = np.asarray(residual, dtype=np.float64)
-        y = y + (r if rowsel is None else r[np.asarray(rowsel)])
-    return y, ids, gates, gaps
+    return moe_mix(get_expert, x, ids, gates, residual, rowsel), ids, gates, gaps
 
 
 def moe_chunk(get_expert, router_bits, X, k, residual=None, tokens=None):
@@ -261,15 +269,18 @@ def crc32(data):
     return int(_load().orc_crc32(a.ctypes.data, a.size))
 
 
-def rvq_encode(W, codebooks):
+def rvq_encode(W, codebooks, margins=False):
     """Residual quantisation of W (fp32 [rows, cols]) against codebooks [3, 256, 8] fp32:
-    codes uint8 [rows, cols/8, 3]."""
+    codes uint8 [rows, cols/8, 3].  With margins=True also returns fp64 [rows, cols/8, 3, 3]:
+    per decision (best distance, second-best distance, squared norm of the stage's input)."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     cb = np.ascontiguousarray(codebooks, dtype=np.float32)
     rows, cols = W.shape
     codes = np.empty((rows, cols // 8, 3), dtype=np.uint8)
-    _load().orc_rvq_encode(W.ctypes.data, rows, cols, cb.ctypes.data, codes.ctypes.data)
-    return codes
+    m = np.empty((rows, cols // 8, 3, 3), dtype=np.float64) if margins else None
+    _load().orc_rvq_encode(W.ctypes.data, rows, cols, cb.ctypes.data, codes.ctypes.data,
+                           None if m is None else m.ctypes.data)
+    return (codes, m) if margins else codes
 
 
 def rvq_fit(W, iters, init_idx, threads=None):

@@ -26,23 +26,27 @@
  *    is quantised stage by stage, each stage choosing the entry nearest (in
  *    squared Euclidean distance) to what the earlier stages left, and that
  *    entry is subtracted: the residual form of the RVQ decode above.  The
- *    choice is taken in fp32 (distance accumulated over the 8 dims in order,
- *    no fused operations, ties to the lower index), the precision of the
- *    kernel that it checks.
+ *    plain definition, in double precision: the fp32 weights and entries are
+ *    widened, differences, squares, sums and the residual are fp64; exact
+ *    ties go to the lower index.  Beside each code it can report the best and
+ *    second-best squared distances and the squared norm of the residual the
+ *    stage was applied to, so that a caller can tell a decision taken in a
+ *    lower precision from a wrong one (two entries within rounding of each
+ *    other are both correct answers).
  *  - Record check: CRC-32 of an expert record's code payload (news.hada.io
  *    topic 32035, disk-streaming architecture section: an optional crc32 of
  *    each record's payload), computed bit by bit from its definition.
  *  - Codebook fitting (the converter's side of the RVQ form; the pages name
  *    the offline conversion but not its method): residual k-means.  Stage by
- *    stage, 256 centroids start at the residual sub-vectors the caller names,
- *    then Lloyd iterations: every sub-vector goes to its nearest centroid (the
- *    encoding decision above), every centroid with members becomes their mean
- *    (a centroid without members keeps its value); after the last iteration
- *    the sub-vectors are assigned once more, those codes are the stage's
- *    codes, and the chosen centroids are subtracted.  The mean's sum is taken
- *    in fp64 in a stated order: within each run of 2048 consecutive sub-vector
- *    indices over its members in ascending index, then the run sums in
- *    ascending run order; divided by the member count and rounded to fp32.
+ *    stage, 256 centroids start at the residual sub-vectors the caller names
+ *    (rounded to fp32, the codebooks' type), then Lloyd iterations: every
+ *    sub-vector goes to its nearest centroid (the encoding decision above, in
+ *    fp64), every centroid with members becomes their mean (a centroid without
+ *    members keeps its value); after the last iteration the sub-vectors are
+ *    assigned once more, those codes are the stage's codes, and the chosen
+ *    centroids are subtracted (fp64 residual).  The mean is one fp64 sum over
+ *    the members in ascending sub-vector index, divided by the member count
+ *    and rounded to fp32.
  */
 #include <math.h>
 #include <pthread.h>
@@ -268,32 +272,54 @@ uint32_t orc_crc32(const uint8_t *data, int64_t n) {
   return ~r;
 }
 
-/* ---------------------------------------------------------------- RVQ encode
- * W: fp32 [rows][cols] (cols % 8 == 0); cb: fp32 [3][256][8]; codes: [rows][cols/8][3]. */
-void orc_rvq_encode(const float *W, int64_t rows, int64_t cols, const float *cb, uint8_t *codes) {
+/* ---------------------------------------------------------------- RVQ encode */
+/* Nearest entry of C (fp32 [256][8]) to v (fp64): squared distances in fp64, ties to the lower
+ * index.  d_best / d_second receive the smallest and second-smallest distances. */
+static int nearest_entry(const double *v, const float *C, double *d_best, double *d_second) {
+  int best = 0;
+  double b1 = INFINITY, b2 = INFINITY;
+  for (int c = 0; c < 256; ++c) {
+    double d = 0.0;
+    for (int j = 0; j < 8; ++j) {
+      const double t = v[j] - (double)C[c * 8 + j];
+      d += t * t;
+    }
+    if (d < b1) {
+      b2 = b1;
+      b1 = d;
+      best = c;
+    } else if (d < b2) {
+      b2 = d;
+    }
+  }
+  if (d_best) *d_best = b1;
+  if (d_second) *d_second = b2;
+  return best;
+}
+
+/* W: fp32 [rows][cols] (cols % 8 == 0); cb: fp32 [3][256][8]; codes: [rows][cols/8][3].
+ * margins (or NULL): fp64 [rows][cols/8][3][3] = (best distance, second-best distance, squared norm
+ * of the residual the stage was applied to) for every decision. */
+void orc_rvq_encode(const float *W, int64_t rows, int64_t cols, const float *cb, uint8_t *codes,
+                    double *margins) {
   const int64_t G = cols / 8;
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t g = 0; g < G; ++g) {
-      float v[8];
-      for (int j = 0; j < 8; ++j) v[j] = W[r * cols + 8 * g + j];
+      double v[8];
+      for (int j = 0; j < 8; ++j) v[j] = (double)W[r * cols + 8 * g + j];
       for (int s = 0; s < 3; ++s) {
         const float *C = cb + (int64_t)s * 256 * 8;
-        int best = 0;
-        float best_d = 0.f;
-        for (int c = 0; c < 256; ++c) {
-          float d = 0.f;
-          for (int j = 0; j < 8; ++j) {
-            const float t = v[j] - C[c * 8 + j];
-            const float t2 = t * t;
-            d = d + t2;
-          }
-          if (c == 0 || d < best_d) {
-            best_d = d;
-            best = c;
-          }
-        }
-        for (int j = 0; j < 8; ++j) v[j] = v[j] - C[best * 8 + j];
+        double d1, d2, vv = 0.0;
+        for (int j = 0; j < 8; ++j) vv += v[j] * v[j];
+        const int best = nearest_entry(v, C, &d1, &d2);
+        for (int j = 0; j < 8; ++j) v[j] = v[j] - (double)C[best * 8 + j];
         codes[(r * G + g) * 3 + s] = (uint8_t)best;
+        if (margins) {
+          double *m = margins + ((r * G + g) * 3 + s) * 3;
+          m[0] = d1;
+          m[1] = d2;
+          m[2] = vv;
+        }
       }
     }
 }
@@ -301,69 +327,42 @@ void orc_rvq_encode(const float *W, int64_t rows, int64_t cols, const float *cb,
 /* ---------------------------------------------------------------- RVQ codebook fit
  * W: fp32 [rows][cols]; init: [3][256] sub-vector indices (row-major sub-vector order,
  * each in [0, rows*cols/8)); cb out: fp32 [3][256][8]; codes out: [rows][cols/8][3]. */
-#define FIT_RUN 2048
-
-static int nearest_entry(const float *v, const float *C) {   /* fp32, no fusion, ties low */
-  int best = 0;
-  float best_d = 0.f;
-  for (int c = 0; c < 256; ++c) {
-    float d = 0.f;
-    for (int j = 0; j < 8; ++j) {
-      const float t = v[j] - C[c * 8 + j];
-      const float t2 = t * t;
-      d = d + t2;
-    }
-    if (c == 0 || d < best_d) {
-      best_d = d;
-      best = c;
-    }
-  }
-  return best;
-}
-
-typedef struct { const float *R; const float *C; int32_t *code; } assign_ctx;
+typedef struct { const double *R; const float *C; int32_t *code; } assign_ctx;
 
 static void assign_range(void *p, int64_t lo, int64_t hi) {
   assign_ctx *a = (assign_ctx *)p;
-  for (int64_t i = lo; i < hi; ++i) a->code[i] = nearest_entry(a->R + i * 8, a->C);
+  for (int64_t i = lo; i < hi; ++i) a->code[i] = nearest_entry(a->R + i * 8, a->C, 0, 0);
 }
 
 void orc_rvq_fit(const float *W, int64_t rows, int64_t cols, int iters, const int32_t *init, float *cb,
                  uint8_t *codes, int threads) {
   const int64_t N = rows * (cols / 8);
-  float *R = (float *)malloc((size_t)N * 8 * sizeof(float));   /* what the earlier stages left */
+  double *R = (double *)malloc((size_t)N * 8 * sizeof(double));   /* what the earlier stages left */
   int32_t *code = (int32_t *)malloc((size_t)N * sizeof(int32_t));
-  memcpy(R, W, (size_t)N * 8 * sizeof(float));                  /* sub-vector i = W[8i .. 8i+8) */
+  for (int64_t i = 0; i < N * 8; ++i) R[i] = (double)W[i];       /* sub-vector i = W[8i .. 8i+8) */
   for (int s = 0; s < 3; ++s) {
     float *C = cb + (int64_t)s * 256 * 8;
     for (int c = 0; c < 256; ++c)
-      for (int j = 0; j < 8; ++j) C[c * 8 + j] = R[(int64_t)init[s * 256 + c] * 8 + j];
+      for (int j = 0; j < 8; ++j) C[c * 8 + j] = (float)R[(int64_t)init[s * 256 + c] * 8 + j];
     assign_ctx a = {R, C, code};
     for (int it = 0; it <= iters; ++it) {
       parallel_for(N, threads, assign_range, &a);
       if (it == iters) break;
-      double tot[256][8];
+      double sum[256][8];
       int64_t n[256];
-      memset(tot, 0, sizeof tot);
+      memset(sum, 0, sizeof sum);
       memset(n, 0, sizeof n);
-      for (int64_t r0 = 0; r0 < N; r0 += FIT_RUN) {
-        double run[256][8];
-        memset(run, 0, sizeof run);
-        const int64_t r1 = r0 + FIT_RUN < N ? r0 + FIT_RUN : N;
-        for (int64_t i = r0; i < r1; ++i) {
-          n[code[i]] += 1;
-          for (int j = 0; j < 8; ++j) run[code[i]][j] += (double)R[i * 8 + j];
-        }
-        for (int c = 0; c < 256; ++c)
-          for (int j = 0; j < 8; ++j) tot[c][j] += run[c][j];
+      for (int64_t i = 0; i < N; ++i) {
+        n[code[i]] += 1;
+        for (int j = 0; j < 8; ++j) sum[code[i]][j] += R[i * 8 + j];
       }
       for (int c = 0; c < 256; ++c)
         if (n[c] > 0)
-          for (int j = 0; j < 8; ++j) C[c * 8 + j] = (float)(tot[c][j] / (double)n[c]);
+          for (int j = 0; j < 8; ++j) C[c * 8 + j] = (float)(sum[c][j] / (double)n[c]);
     }
     for (int64_t i = 0; i < N; ++i) {
       codes[i * 3 + s] = (uint8_t)code[i];
-      for (int j = 0; j < 8; ++j) R[i * 8 + j] = R[i * 8 + j] - C[code[i] * 8 + j];
+      for (int j = 0; j < 8; ++j) R[i * 8 + j] = R[i * 8 + j] - (double)C[code[i] * 8 + j];
     }
   }
   free(code);

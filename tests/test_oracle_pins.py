@@ -16,9 +16,19 @@ Pinned functions and what pins them:
   router / topk    : numpy matmul on widened bf16, lexsort order, scipy softmax
                      (k = E), gate = 1 at k = 1, exact ties -> lower id
   rmsnorm          : torch rms_norm, closed-form RMS of the output
+  gemv_batch /     : T tokens at once equal T one-token calls bit for bit (each token's
+  expert_batch       sums are independent of the others)
+  moe_chunk        : token by token equal to moe_layer (routing, gates, residual), with
+                     several tokens on one expert, a token subset, and k = 1
   rvq_encode       : the binary-digit encoding built by bit extraction (greedy residual
                      search must recover it exactly), exact codebook entries with a zero
-                     entry in the later stages, and re-encoding of a decode
+                     entry in the later stages, re-encoding of a decode, numpy brute force
+                     of every decision along the path, exact ties -> lower index, and the
+                     reported margins (best, second-best distance, input norm)
+  rvq_fit          : exact recovery of a separated balanced lattice, Lloyd's update against
+                     math.fsum means of the previous assignment, starts taken from the
+                     residual, codes = rvq_encode with the fitted codebooks, monotone
+                     stage-0 distortion
   crc32            : the standard check value of CRC-32 ("123456789" -> 0xCBF43926),
                      zlib.crc32 on random buffers of ragged lengths, single-bit flips
 """
@@ -309,6 +319,52 @@ def test_moe_layer_k1_and_duplicate_experts():
     np.testing.assert_allclose(yr - r, y3, rtol=1e-13, atol=1e-12)
 
 
+def test_gemv_and_expert_batch_equal_single_token_calls():
+    """Several tokens at once give each token exactly what a one-token call gives (the oracle's
+    per-token sums do not depend on the other tokens); row selection keeps that."""
+    H, I = 96, 40
+    ex = _small_expert(13, 3, H, I)
+    X = np.stack([synth.activation_f32(13, t, H).astype(np.float64) for t in range(5)])
+    X[2] *= -3.0
+    codes, cb = ex["gate"]
+    Yg = oracle.gemv_batch(codes, cb, I, H, X)
+    Ye = oracle.expert_batch(ex, X)
+    sel = np.array([0, 17, 95, 3])
+    Yes = oracle.expert_batch(ex, X, rowsel=sel)
+    for t in range(X.shape[0]):
+        assert np.array_equal(Yg[t], oracle.gemv(codes, cb, I, H, X[t]))
+        assert np.array_equal(Ye[t], oracle.expert(ex, X[t]))
+        assert np.array_equal(Yes[t], Ye[t][sel])
+    # and the batch form is the dense product on the dequantised weights
+    np.testing.assert_allclose(Yg, X @ oracle.dequant(codes, cb, I, H).T, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("E,k", [(6, 3), (8, 1), (5, 5)])
+def test_moe_chunk_equals_moe_layer_token_by_token(E, k):
+    """The chunk form (experts rebuilt once, applied to all their tokens, pairs scattered back with
+    their gates) gives each token moe_layer's output: same ids and gates, same sum up to the order of
+    the fp64 additions; with few experts every expert serves several tokens, and a token subset
+    returns those rows only."""
+    H, I, T = 64, 32, 7
+    experts = {e: _small_expert(17, e, H, I) for e in range(E)}
+    get = lambda e: experts[e]
+    bits = synth.router_bf16_bits(17, 0, E, H)
+    X = np.stack([synth.activation_f32(17, 100 + t, H).astype(np.float64) for t in range(T)])
+    R = np.stack([synth.activation_f32(17, 200 + t, H).astype(np.float64) for t in range(T)])
+    for residual in (None, R):
+        Y, ids, gates = oracle.moe_chunk(get, bits, X, k, residual=residual)
+        for t in range(T):
+            y1, ids1, g1, _ = oracle.moe_layer(get, bits, X[t], k, residual=None if residual is None else R[t])
+            assert np.array_equal(ids[t], ids1) and np.array_equal(gates[t], g1)
+            np.testing.assert_allclose(Y[t], y1, rtol=1e-13, atol=1e-12 * np.abs(y1).max())
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    assert counts.max() >= 2          # some expert serves several tokens
+    sub = np.array([5, 0, 3])
+    Ys, _, _ = oracle.moe_chunk(get, bits, X, k, residual=R, tokens=sub)
+    Yall, _, _ = oracle.moe_chunk(get, bits, X, k, residual=R)
+    np.testing.assert_allclose(Ys, Yall[sub], rtol=1e-13, atol=1e-12 * np.abs(Yall).max())
+
+
 # ---------------------------------------------------------------- RMSNorm
 
 def test_rmsnorm_matches_torch_and_closed_form():
@@ -373,6 +429,43 @@ def test_rvq_encode_exact_entries_and_reencode():
     c0 = rng.integers(0, 256, (20, 6, 3)).astype(np.uint8)
     W2 = oracle.dequant(c0, cb2, 20, 48).astype(np.float32)
     assert np.array_equal(oracle.rvq_encode(W2, cb2), c0)
+
+
+def test_rvq_encode_brute_force_and_margins():
+    """Every decision against a numpy brute force along the oracle's own path (all 256 distances of
+    the fp64 residual, the first index of the minimum), and the reported margins: the best and
+    second-best distance and the input's squared norm at each stage."""
+    rng = np.random.default_rng(14)
+    cb = (rng.standard_normal((3, 256, 8)) * np.array([1.0, 0.5, 0.25])[:, None, None]).astype(np.float32)
+    W = rng.standard_normal((9, 64)).astype(np.float32)
+    codes, m = oracle.rvq_encode(W, cb, margins=True)
+    V = W.reshape(-1, 8).astype(np.float64)
+    C = codes.reshape(-1, 3)
+    M = m.reshape(-1, 3, 3)
+    for s in range(3):
+        D = ((V[:, None, :] - cb[s].astype(np.float64)[None]) ** 2).sum(axis=2)
+        best = np.argmin(D, axis=1)
+        assert np.array_equal(C[:, s], best), s
+        Ds = np.sort(D, axis=1)
+        np.testing.assert_allclose(M[:, s, 0], Ds[:, 0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(M[:, s, 1], Ds[:, 1], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(M[:, s, 2], (V ** 2).sum(axis=1), rtol=1e-12)
+        V = V - cb[s][best].astype(np.float64)
+    assert np.array_equal(oracle.rvq_encode(W, cb), codes)
+
+
+def test_rvq_encode_exact_tie_takes_lower_index():
+    """Two entries at exactly the same distance (mirror images about the sub-vector): the lower
+    index wins, at every stage, and the reported gap is exactly zero."""
+    cb = np.full((3, 256, 8), 100.0, dtype=np.float32)
+    for s in range(3):
+        cb[s, 200] = 1.0
+        cb[s, 31] = -1.0            # |0 - 1| == |0 - (-1)|: a tie between entries 31 and 200
+    W = np.zeros((1, 8), dtype=np.float32)
+    codes, m = oracle.rvq_encode(W, cb, margins=True)
+    # stage 0 picks 31 (lower index); the residual is then +1, nearest entry 200 (distance 0)
+    assert codes[0, 0, 0] == 31 and m[0, 0, 0, 0] == m[0, 0, 0, 1] == 8.0
+    assert codes[0, 0, 1] == 200 and m[0, 0, 1, 0] == 0.0
 
 
 # ---------------------------------------------------------------- RVQ codebook fit (residual k-means)
@@ -466,15 +559,16 @@ def test_rvq_fit_update_is_the_mean_of_the_previous_assignment(K):
 
 
 def test_rvq_fit_initialises_each_stage_from_its_residual():
-    """With no iteration, stage s's centroids are the sub-vectors init[s] of what stages < s left
-    (residual formed in fp32 from the earlier stages' codes and centroids)."""
+    """With no iteration, stage s's centroids are the sub-vectors init[s] of what stages < s left,
+    rounded to fp32 (the residual itself is exact: formed in fp64 from the earlier stages' codes and
+    centroids, numpy here)."""
     W, init = _gauss_fit_input(6)
     cb, codes = oracle.rvq_fit(W, 0, init)
-    R = W.reshape(-1, 8).copy()
+    R = W.reshape(-1, 8).astype(np.float64)
     c = codes.reshape(-1, 3)
     for s in range(3):
-        assert np.array_equal(cb[s], R[init[s]]), s
-        R = R - cb[s][c[:, s]]
+        assert np.array_equal(cb[s], R[init[s]].astype(np.float32)), s
+        R = R - cb[s][c[:, s]].astype(np.float64)
 
 
 def test_rvq_fit_codes_are_the_encoding_with_the_fitted_codebooks():
