@@ -2,9 +2,13 @@
 into MFMA operands, grouped expert GEMMs, gated combine; against the fp64 oracle.
 
 Tile precision and bound: fp16 tiles (weights summed in fp16 from fp16 codebooks, h scaled per pair
-by a power of two) must meet rel-L2 <= 2e-3.  bf16 tiles (weights and h rounded to bf16, 8-bit
-significand) carry about 2^-9/sqrt(3) relative error per operand; three chained products give
-~3e-3, so they are reported against 2e-3 and held to the derived bound 6e-3.
+by a power of two) must meet rel-L2 <= 2e-3.  bf16 tiles round the weights and h to bf16 (8-bit
+significand).  One such rounding of a value with a log-uniform significand has relative standard
+deviation 2^-7 * sqrt(E[(1/m)^2]) / sqrt(12) = 2^-7 * 0.736 / 3.46 = 1.66e-3 (m in [1, 2)); the
+output sees four independent ones in a chain (gate weights, up weights, h, down weights; x is bf16
+already), each carried into the output at about its own relative size because the sums average
+independent errors, so rel-L2 ~ sqrt(4) * 1.66e-3 = 3.3e-3 (measured 3.3e-3).  bf16 is held to 4e-3,
+1.2x that expectation; it is also reported against 2e-3, which only the fp16 tiles meet.
 """
 import sys
 
@@ -18,7 +22,7 @@ import synth
 from workloads import CHUNK_TOKENS, HIDDEN, INTER, LAYER_EXPERTS, TOP_K, oracle_expert, rel_l2, router, upload_bank
 
 pytestmark = pytest.mark.gpu
-TOL = {"f16": 2e-3, "bf16": 6e-3}
+TOL = {"f16": 2e-3, "bf16": 4e-3}
 
 
 def say(msg):

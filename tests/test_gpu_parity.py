@@ -14,6 +14,7 @@ import torch
 import oracle
 import rvq_quantized_moe_amd as rvq
 import synth
+from quant_checks import compare_with_oracle_codes
 from workloads import (HIDDEN, INTER, LAYER_EXPERTS, MATVEC_COLS, MATVEC_ROWS, TOP_K, oracle_expert, pack_spec,
                        rel_l2, router, upload_bank)
 
@@ -279,6 +280,31 @@ def layer_bank():
     return bank, bits, w
 
 
+def _layer_oracle_getter(seed=None, H=HIDDEN, I=INTER):
+    seed = synth.SEED_LAYER if seed is None else seed
+    cache = {}
+
+    def get(e):
+        if e not in cache:
+            cache[e] = oracle_expert(seed, 0, e, H, I)
+        return cache[e]
+    return get
+
+
+def _rows_match_oracle(get, bits, X, R, y, ids, gates, tokens, k, dtype):
+    """Rows `tokens` of a batch output against the oracle's layer, token by token: the same ids, gates
+    to 1e-6, and the MoE part (output minus residual) within the table precision's tolerance."""
+    for t in tokens:
+        r = None if R is None else R[t]
+        y_ref, ids_ref, gates_ref, _ = oracle.moe_layer(get, bits, X[t], k, residual=r)
+        assert np.array_equal(ids[t], ids_ref), t
+        np.testing.assert_allclose(gates[t], gates_ref, rtol=1e-6)
+        base = 0.0 if r is None else r
+        err = rel_l2(y[t] - base, y_ref - base)
+        say(f"  token {t}: rel-L2 {err:.3e} against the oracle")
+        assert err <= TOL[dtype], t
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_moe_layer_decode(layer_bank, dtype):
     bank, bits, w = layer_bank
@@ -419,8 +445,9 @@ def test_block_decode_matches_norm_then_routed_and_oracle(layer_bank, dtype):
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_batch_decode_equals_single_token_calls(layer_bank, dtype):
     """rvq_moe_batch_decode runs T tokens' pairs in the same launches, each chunked as for one token:
-    every row equals a single-token rvq_moe_layer_forward bit for bit (those are checked against the
-    oracle above), y may alias the residual, and the workspace is reusable across batch sizes."""
+    rows 0 and T-1 against the oracle's layer, every row equal to a single-token
+    rvq_moe_layer_forward bit for bit, y may alias the residual, and the workspace is reusable across
+    batch sizes."""
     bank, bits, w = layer_bank
     T = 5
     say(f"batch decode T={T} {dtype}")
@@ -430,6 +457,8 @@ def test_batch_decode_equals_single_token_calls(layer_bank, dtype):
     ids, gates, _ = rvq.router_topk(w, xd, TOP_K)
     ws = rvq.make_batch_workspace(bank, T, TOP_K, dtype)
     y = rvq.moe_batch_decode(bank, xd, ids, gates, residual=rd, dtype=dtype, workspace=ws)
+    _rows_match_oracle(_layer_oracle_getter(), bits, X, R, y.cpu().numpy(), ids.cpu().numpy(),
+                       gates.cpu().numpy(), (0, T - 1), TOP_K, dtype)
     for t in range(T):
         y1 = rvq.moe_layer_forward(bank, xd[t], ids[t], gates[t], residual=rd[t], dtype=dtype, workspace=ws)
         assert torch.equal(y[t], y1), t
@@ -437,6 +466,26 @@ def test_batch_decode_equals_single_token_calls(layer_bank, dtype):
     rvq.moe_batch_decode(bank, xd[:3], ids[:3], gates[:3], residual=yin, dtype=dtype, y=yin, workspace=ws)
     assert torch.equal(yin, y[:3])
     assert rvq.check_device_status(ws) == 0
+
+
+@pytest.mark.parametrize("k,T", [(1, 6), (2, 4)])
+def test_batch_decode_few_experts_per_token(layer_bank, k, T):
+    """k = 1 and k = 2 on the 256-expert layer: few pairs per token, so gate/up leaves more partial
+    sums per row than the down kernel reads (the partial-sum kernel runs) and the down kernel may take
+    one row block per streamer wave.  Every row against the oracle, and bit-equal to single-token
+    calls."""
+    bank, bits, w = layer_bank
+    X = np.stack([synth.activation_f32(synth.SEED_LAYER, 4000 + 10 * k + t, HIDDEN) for t in range(T)])
+    xd = to_dev(X)
+    ids, gates, _ = rvq.router_topk(w, xd, k)
+    get = _layer_oracle_getter()
+    for dtype in ("f32", "f16"):
+        say(f"batch decode T={T} k={k} {dtype}")
+        y = rvq.moe_batch_decode(bank, xd, ids, gates, dtype=dtype)
+        _rows_match_oracle(get, bits, X, None, y.cpu().numpy(), ids.cpu().numpy(), gates.cpu().numpy(),
+                           range(T), k, dtype)
+        for t in range(T):
+            assert torch.equal(y[t], rvq.moe_layer_forward(bank, xd[t], ids[t], gates[t], dtype=dtype)), t
 
 
 @pytest.mark.parametrize("H,I,E,k", [
@@ -449,17 +498,21 @@ def test_batch_decode_other_shapes(H, I, E, k):
     bank = upload_bank(seed, 0, E, H, I)
     bits, w = router(seed, 0, E, H)
     T = 3
-    xd = to_dev(np.stack([synth.activation_f32(seed, 200 + t, H) for t in range(T)]))
+    X = np.stack([synth.activation_f32(seed, 200 + t, H) for t in range(T)])
+    xd = to_dev(X)
     ids, gates, _ = rvq.router_topk(w, xd, k)
+    get = _layer_oracle_getter(seed, H, I)
     for dtype in ("f32", "f16"):
         y = rvq.moe_batch_decode(bank, xd, ids, gates, dtype=dtype)
+        _rows_match_oracle(get, bits, X, None, y.cpu().numpy(), ids.cpu().numpy(), gates.cpu().numpy(),
+                           range(T), k, dtype)
         for t in range(T):
             assert torch.equal(y[t], rvq.moe_layer_forward(bank, xd[t], ids[t], gates[t], dtype=dtype)), (dtype, t)
 
 
 def test_batch_decode_at_max_tokens(layer_bank):
-    """The largest batch (256 tokens x top-16 = 4096 pairs in one set of launches): sampled rows equal
-    single-token calls bit for bit."""
+    """The largest batch (256 tokens x top-16 = 4096 pairs in one set of launches): two rows against
+    the oracle, sampled rows equal single-token calls bit for bit."""
     bank, bits, w = layer_bank
     T = 256
     say(f"batch decode T={T} f16")
@@ -468,6 +521,8 @@ def test_batch_decode_at_max_tokens(layer_bank):
     ids, gates, _ = rvq.router_topk(w, xd, TOP_K)
     ws = rvq.make_batch_workspace(bank, T, TOP_K, "f16")
     y = rvq.moe_batch_decode(bank, xd, ids, gates, dtype="f16", workspace=ws)
+    _rows_match_oracle(_layer_oracle_getter(), bits, X, None, y.cpu().numpy(), ids.cpu().numpy(),
+                       gates.cpu().numpy(), (1, 254), TOP_K, "f16")
     for t in (0, 1, 100, 254, 255):
         y1 = rvq.moe_layer_forward(bank, xd[t], ids[t], gates[t], dtype="f16", workspace=ws)
         assert torch.equal(y[t], y1), t
@@ -545,9 +600,11 @@ def _digit_setup(rows, cols, seed):
 
 @pytest.mark.parametrize("rows,cols", [(256, 512), (100, 264), (1, 8)])
 def test_rvq_encode_matches_oracle(rows, cols):
-    """GPU residual encoding equals the oracle's fp32 decisions bit for bit (weights near the code
-    lattice, as from a decode plus noise, and plain Gaussian weights); the digit case recovers the
-    codes built by bit extraction."""
+    """GPU residual encoding (fp32 decisions) against the oracle's fp64 decisions: every group equal
+    except where the oracle's best and second-best distances lie within the fp32 rounding bound of
+    each other, and those groups are nearest-entry picks along their own path (quant_checks.py).
+    Weights near the code lattice (a decode plus noise) and plain Gaussian weights; the digit case
+    recovers the codes built by bit extraction exactly."""
     say(f"rvq encode {rows}x{cols}")
     cb = synth.matrix_codebooks(synth.SEED_MATVEC, 0, 0, synth.SINGLE)
     rng = np.random.default_rng(rows * 31 + cols)
@@ -557,15 +614,17 @@ def test_rvq_encode_matches_oracle(rows, cols):
     cbd = to_dev(cb)
     for W in (W1, W2):
         got = rvq.rvq_encode(to_dev(W), cbd).cpu().numpy()
-        assert np.array_equal(got, oracle.rvq_encode(W, cb))
+        want, margins = oracle.rvq_encode(W, cb, margins=True)
+        flipped = compare_with_oracle_codes(W, cb, got, want, margins)
+        assert flipped <= max(1, got.size // 3000)
     Wd, cbdig, codes = _digit_setup(rows, cols, rows + cols)
     assert np.array_equal(rvq.rvq_encode(to_dev(Wd), to_dev(cbdig)).cpu().numpy(), codes)
 
 
 def test_rvq_encode_full_size_sampled():
-    """A 2048 x 7168 gate matrix (decode of its codes plus noise): sampled rows against the oracle,
-    and the round trip through the packed decode path (encode -> pack -> table GEMV) against the
-    oracle's GEMV of the recovered codes."""
+    """A 2048 x 7168 gate matrix (decode of its codes plus noise): sampled rows against the oracle (as
+    above), and the round trip through the packed decode path (encode -> pack -> table GEMV) against
+    the oracle's GEMV of the recovered codes."""
     say("rvq encode 2048x7168")
     rows, cols = INTER, HIDDEN
     ex = synth.Expert(synth.SEED_EXPERT, 0, 1, HIDDEN, INTER)
@@ -574,7 +633,8 @@ def test_rvq_encode_full_size_sampled():
     W = (oracle.dequant(ex.codes(synth.GATE), cb, rows, cols) + 0.02 * rng.standard_normal((rows, cols))).astype(np.float32)
     codes = rvq.rvq_encode(to_dev(W), to_dev(cb)).cpu().numpy()
     for r in (0, 1, 777, 2047):
-        assert np.array_equal(codes[r:r + 1], oracle.rvq_encode(W[r:r + 1], cb)), r
+        want, margins = oracle.rvq_encode(W[r:r + 1], cb, margins=True)
+        assert compare_with_oracle_codes(W[r:r + 1], cb, codes[r:r + 1], want, margins) <= 1, r
     x = synth.activation_f32(synth.SEED_EXPERT, 3, cols)
     packed = rvq.pack_codes(torch.from_numpy(codes).cuda(), rows, cols)
     y = rvq.expert_gemv(packed, to_dev(cb), rows, cols, to_dev(x), "f32").cpu().numpy()

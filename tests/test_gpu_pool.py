@@ -11,10 +11,27 @@ import torch
 import oracle
 import rvq_quantized_moe_amd as rvq
 import synth
-from workloads import HIDDEN, INTER, router, upload_bank
+from workloads import HIDDEN, INTER, oracle_expert, rel_l2, router, upload_bank
 
 pytestmark = pytest.mark.gpu
 E_POOL = 24
+SEED_POOL = synth.SEED_EXPERT ^ 0x5
+_ORACLE_EXPERTS = {}
+
+
+def oracle_get(e):
+    """The pool's experts as the oracle sees them, regenerated from their seeds (never read back)."""
+    if e not in _ORACLE_EXPERTS:
+        _ORACLE_EXPERTS[e] = oracle_expert(SEED_POOL, 0, e)
+    return _ORACLE_EXPERTS[e]
+
+
+def assert_matches_oracle(y, x, ids, gates):
+    """A pool decode against the oracle's mix of the same experts and gates (fp32 tables: 1e-5)."""
+    y_ref = oracle.moe_mix(oracle_get, np.asarray(x, dtype=np.float64), np.asarray(ids), np.asarray(gates))
+    err = rel_l2(y, y_ref)
+    say(f"  rel-L2 {err:.3e} against the oracle")
+    assert err <= 1e-5
 
 
 def say(msg):
@@ -68,21 +85,23 @@ def lru_model(slots, events):
 @pytest.fixture(scope="module")
 def store():
     say(f"upload {E_POOL} experts and copy them to pinned host memory")
-    bank = upload_bank(synth.SEED_EXPERT ^ 0x5, 0, E_POOL)
+    bank = upload_bank(SEED_POOL, 0, E_POOL)
     hc = torch.empty(bank.codes.numel(), dtype=torch.uint8, pin_memory=True)
     hc.copy_(bank.codes)
     hb = torch.empty(bank.codebooks.shape, dtype=torch.float32, pin_memory=True)
     hb.copy_(bank.codebooks)
-    bits, w = router(synth.SEED_EXPERT ^ 0x5, 0, E_POOL, HIDDEN)
+    bits, w = router(SEED_POOL, 0, E_POOL, HIDDEN)
     return bank, hc, hb, w
 
 
 @pytest.mark.parametrize("slots,k,prefetch", [(10, 4, False), (4, 4, False), (12, 4, True)])
 def test_pool_decode_matches_resident_bank(store, slots, k, prefetch):
     """slots = k evicts on almost every step (copies must wait for the previous step's kernels);
-    with prefetch the next token's experts are copied while the current one decodes."""
+    with prefetch the next token's experts are copied while the current one decodes.  Every decode
+    equals the resident bank bit for bit; the first and last against the oracle's routed layer."""
     bank, hc, hb, w = store
     say(f"pool slots={slots} k={k} prefetch={prefetch}")
+    bits = synth.router_bf16_bits(SEED_POOL, 0, E_POOL, HIDDEN)
     pool = rvq.ExpertPool(hc, hb, E_POOL, HIDDEN, INTER, slots)
     ws = rvq.make_moe_workspace(bank, 1, k, "f32")
     wsp = rvq.make_moe_workspace(pool.bank, 1, k, "f32")
@@ -102,6 +121,10 @@ def test_pool_decode_matches_resident_bank(store, slots, k, prefetch):
                 events.append(("prefetch", [int(e) for e in host_ids[t + 1]]))
             ref = rvq.moe_layer_forward(bank, xs[t], ids[0], gates[0], dtype="f32", workspace=ws)
             assert torch.equal(y, ref), t
+            if t in (0, len(xs) - 1):
+                y_ref, ids_ref, g_ref, _ = oracle.moe_layer(oracle_get, bits, xs[t].cpu().numpy(), k)
+                assert np.array_equal(host_ids[t], ids_ref)
+                assert rel_l2(y.cpu().numpy(), y_ref) <= 1e-5, t
         st = pool.stats()
         hits, misses, pre = lru_model(slots, events)
         assert (st["hits"], st["misses"], st["prefetches"]) == (hits, misses, pre)
@@ -203,19 +226,22 @@ def records(store):
     return rvq.write_records(bank, REC_LAYER, crcs), crcs
 
 
-def _decode_both(pool, bank, ids, x, ws, wsr, rng):
+def _decode_both(pool, bank, ids, x, ws, wsr, rng, check_oracle=False):
     g = torch.from_numpy(rng.random(len(ids)).astype(np.float32)).cuda()
     slot = pool.acquire(ids)
     y = rvq.moe_layer_forward(pool.bank, x, torch.from_numpy(slot).cuda(), g, dtype="f32", workspace=ws)
     ref = rvq.moe_layer_forward(bank, x, torch.tensor(np.asarray(ids), dtype=torch.int32).cuda(), g, dtype="f32",
                                 workspace=wsr)
+    if check_oracle:
+        assert_matches_oracle(y.cpu().numpy(), x.cpu().numpy(), ids, g.cpu().numpy())
     return y, ref
 
 
 @pytest.mark.parametrize("verify", [False, True])
 def test_record_pool_matches_resident_bank(store, records, verify):
     """Slots filled from records (header checked on every read; with verify, each payload's CRC-32 too)
-    decode exactly as the resident bank; clean records report no CRC failure."""
+    decode exactly as the resident bank, and the first and last decodes match the oracle's mix of
+    the same experts and gates; clean records report no CRC failure."""
     bank = store[0]
     rec, _ = records
     say(f"record pool verify={verify}")
@@ -227,7 +253,7 @@ def test_record_pool_matches_resident_bank(store, records, verify):
     try:
         for r in range(5):
             perm = rng.permutation(E_POOL)
-            y, ref = _decode_both(pool, bank, perm[:4], x, ws, wsr, rng)
+            y, ref = _decode_both(pool, bank, perm[:4], x, ws, wsr, rng, check_oracle=r in (0, 4))
             assert torch.equal(y, ref), r
             pool.prefetch(perm[4:6])
         assert pool.verify_status() == -1

@@ -4,17 +4,21 @@ layers, no attention): the HIP path against the fp64 oracle.
   h <- x_t;  for each layer l:  n = rmsnorm(h);  (ids, gates) = route_l(n);  h <- h + MoE_l(n)
 
 Checks per decode step (the layer-by-layer comparison against an independent reference that the
-WASTE pages describe for their own engine):
+WASTE pages describe for their own engine), on 4 of the 32 steps:
   * layer-wise: each GPU layer is given the oracle's own inputs for that layer (inputs flow
     oracle -> GPU only): RMSNorm of the oracle's h_l (rel-L2 <= 1e-6), the router on the oracle's
     n_l (ids bit-exact: both sides accumulate logits in fp64; gates 1e-6), and the MoE output on
     the oracle's n_l, ids and gates (rel-L2 <= 1e-5 with fp32 tables, 2e-3 with fp16 tables).
   * end-to-end: the GPU runs all 92 layers on its own (norm, router, layer as three calls; the
-    fused block call must give the same final h bit for bit).  Its ids must equal the oracle's at every
-    layer except where the oracle's own top-k boundary is a near-tie (gap < TAU); after such a
-    divergence the step is not compared further.  92 routed layers amplify rounding-level
-    differences about 400x (measured below: the oracle's own final h under a one-ulp change of x),
-    so the end-to-end drift is reported and held to a sanity limit only.
+    fused block call must give the same final h bit for bit).  At layer l its router input n_l
+    differs from the oracle's by rounding drift, and no logit can move by more than
+    D_l = max_e ||w_e|| * ||n_gpu - n_oracle|| (Cauchy-Schwarz; the fp64 sums add ~1e-13).  So the
+    GPU's ids must equal the oracle's, except that two experts may be ordered differently where their
+    oracle logits are less than 2 D_l apart (an in-set reorder: counted, the step goes on), and the set
+    may differ where the oracle's top-k boundary gap is below 2 D_l (counted; the step is compared no
+    further).  92 routed layers amplify rounding-level differences about 400x (measured below: the
+    oracle's own final h under a one-ulp change of x), so the drift of h is reported, at the end or
+    at the layer where the set first differs, and held to a sanity limit.
 """
 import sys
 
@@ -29,9 +33,9 @@ from workloads import RMS_EPS, TOP_K, Stack, rel_l2
 
 pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-5, "f16": 2e-3}
-# Largest oracle logit gap at which the free-running GPU may order experts differently.
-TAU = {"f32": 1e-3, "f16": 5e-2}
 SANITY = {"f32": 1e-3, "f16": 5e-2}
+STEPS = (0, 9, 20, 31)
+_TRACES = {}
 
 
 def say(msg):
@@ -49,7 +53,8 @@ def stack():
 
 
 def oracle_step(stack, x):
-    """The oracle's trajectory: per layer (h_in, n, ids, gates, boundary gap, MoE output); final h."""
+    """The oracle's trajectory: per layer (h_in, n, ids, gates, boundary gap, MoE output, logits);
+    final h."""
     h = np.asarray(x, dtype=np.float64)
     trace = []
     for l in range(stack.L):
@@ -61,20 +66,35 @@ def oracle_step(stack, x):
                 cache[e] = stack.oracle_expert(l, e)
             return cache[e]
         y, ids, gates, gaps = oracle.moe_layer(get, stack.router_bits[l], n, TOP_K)
-        trace.append((h, n, ids, gates, gaps[0], y))
+        logits = oracle.router_logits(stack.router_bits[l], n[None, :])[0]
+        trace.append((h, n, ids, gates, gaps[0], y, logits))
         h = h + y
     return h, trace
 
 
+def oracle_trace(stack, t):
+    if t not in _TRACES:
+        x = synth.activation_f32(synth.SEED_STACK, t, stack.H)
+        say(f"stack step {t}: oracle trajectory")
+        _TRACES[t] = (x,) + oracle_step(stack, x)
+    return _TRACES[t]
+
+
+def router_row_norms(stack, l):
+    w = (np.asarray(stack.router_bits[l], dtype=np.uint32).reshape(stack.E, stack.H) << 16).view(np.float32)
+    return np.sqrt((w.astype(np.float64) ** 2).sum(axis=1))
+
+
 def gpu_free_step(stack, x, dtype, ws):
+    """The GPU's own run: final h, and per layer (h_in, n, ids)."""
     h = dev32(x)
-    ids_all = []
+    per_layer = []
     for l in range(stack.L):
         n = rvq.rmsnorm(h, RMS_EPS)
         ids, gates, _ = rvq.router_topk(stack.routers[l], n, TOP_K)
+        per_layer.append((h.cpu().numpy(), n.cpu().numpy(), ids[0].cpu().numpy()))
         h = rvq.moe_layer_forward(stack.banks[l], n, ids[0], gates[0], residual=h, dtype=dtype, workspace=ws)
-        ids_all.append(ids[0])
-    return h.cpu().numpy(), [i.cpu().numpy() for i in ids_all]
+    return h.cpu().numpy(), per_layer
 
 
 def gpu_block_step(stack, x, dtype, ws):
@@ -86,22 +106,41 @@ def gpu_block_step(stack, x, dtype, ws):
     return h.cpu().numpy()
 
 
+def compare_routes(ids_g, ids_o, logits_o, bound):
+    """'same', 'reordered' or 'set' (see the module docstring); asserts every difference lies within
+    the bound on the logits' movement."""
+    if np.array_equal(ids_g, ids_o):
+        return "same"
+    if set(ids_g.tolist()) == set(ids_o.tolist()):
+        pos_o = {e: i for i, e in enumerate(ids_o.tolist())}
+        for i in range(len(ids_g)):
+            for j in range(i + 1, len(ids_g)):
+                a, b = int(ids_g[i]), int(ids_g[j])
+                if pos_o[a] > pos_o[b]:   # ordered the other way by the oracle
+                    assert abs(logits_o[a] - logits_o[b]) < 2 * bound, (a, b, logits_o[a] - logits_o[b], bound)
+        return "reordered"
+    order = np.lexsort((np.arange(len(logits_o)), -logits_o))
+    k = len(ids_o)
+    gap = logits_o[order[k - 1]] - logits_o[order[k]]
+    assert gap < 2 * bound, (ids_g, ids_o, gap, bound)
+    return "set"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_stack_decode_steps(stack, dtype):
     ws = rvq.make_moe_workspace(stack.banks[0], 1, TOP_K, dtype)
-    flips = 0
-    for t in (0, 1):
-        x = synth.activation_f32(synth.SEED_STACK, t, stack.H)
-        say(f"stack step {t} {dtype}: oracle trajectory")
-        h_ref, trace = oracle_step(stack, x)
-        if t == 0 and dtype == "f32":
+    wn = [router_row_norms(stack, l).max() for l in range(stack.L)]
+    counts = {"reordered": 0, "set": 0}
+    for t in STEPS:
+        x, h_ref, trace = oracle_trace(stack, t)
+        if t == STEPS[0] and dtype == "f32":
             sign = np.where(synth.uniform_bytes(0x51, 1, stack.H) & 1, 1.0, -1.0)
             xp = np.nextafter(x, (x.astype(np.float64) + sign).astype(np.float32))
             h_p, _ = oracle_step(stack, xp)
             say(f"  oracle sensitivity to a 1-ulp input change: final h rel-L2 {rel_l2(h_p, h_ref):.3e}")
         say(f"stack step {t} {dtype}: layer-wise GPU on the oracle's inputs")
         worst = 0.0
-        for l, (h_in, n, ids, gates, gap, y) in enumerate(trace):
+        for l, (h_in, n, ids, gates, gap, y, _) in enumerate(trace):
             n_gpu = rvq.rmsnorm(dev32(h_in), RMS_EPS).cpu().numpy()
             assert rel_l2(n_gpu, n) <= 1e-6, l
             ids_g, gates_g, _ = rvq.router_topk(stack.routers[l], dev32(n), TOP_K)
@@ -114,22 +153,26 @@ def test_stack_decode_steps(stack, dtype):
             assert err <= TOL[dtype], (l, err)
         say(f"  layer-wise MoE output: worst rel-L2 over 92 layers {worst:.3e}")
         say(f"stack step {t} {dtype}: end-to-end GPU")
-        h_free, ids_gpu = gpu_free_step(stack, x, dtype, ws)
+        h_free, per_layer = gpu_free_step(stack, x, dtype, ws)
         assert np.array_equal(gpu_block_step(stack, x, dtype, ws), h_free)
-        diverged = False
+        where, drift = stack.L, None
         for l in range(stack.L):
-            ids_o, gap = trace[l][2], trace[l][4]
-            if not np.array_equal(ids_gpu[l], ids_o):
-                same_set = set(ids_gpu[l].tolist()) == set(ids_o.tolist())
-                assert same_set or gap < TAU[dtype], (l, ids_gpu[l], ids_o, gap)
-                if not same_set:
-                    flips += 1
-                    diverged = True
-                    say(f"  layer {l}: top-k boundary near-tie (oracle gap {gap:.2e}); rest of step not compared")
-                    break
-        if not diverged:
+            h_g, n_g, ids_g = per_layer[l]
+            h_o, n_o, ids_o, logits_o = trace[l][0], trace[l][1], trace[l][2], trace[l][6]
+            bound = wn[l] * float(np.linalg.norm(n_g.astype(np.float64) - n_o)) + 1e-12
+            kind = compare_routes(ids_g, ids_o, logits_o, bound)
+            if kind == "reordered":
+                counts["reordered"] += 1
+                say(f"  layer {l}: in-set reorder within 2 D_l = {2 * bound:.2e}")
+            elif kind == "set":
+                counts["set"] += 1
+                where, drift = l, rel_l2(h_g, h_o)
+                say(f"  layer {l}: top-k set differs at an oracle boundary gap below 2 D_l = {2 * bound:.2e}; "
+                    f"drift of h entering it {drift:.3e}; rest of step not compared")
+                break
+        if drift is None:
             drift = rel_l2(h_free, h_ref)
             say(f"  end-to-end final h rel-L2 {drift:.3e} (drift)")
-            assert drift <= SANITY[dtype]
+        assert drift <= SANITY[dtype], (t, where, drift)
     assert rvq.check_device_status(ws) == 0
-    say(f"  near-tie divergences: {flips}")
+    say(f"  {dtype}: in-set reorders {counts['reordered']}, set changes {counts['set']} over {len(STEPS)} steps")
