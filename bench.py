@@ -181,14 +181,50 @@ def run_variant(rvq, hip, bank, w, pool, steps, warmup, dtype):
     }
 
 
+MIN_TIMED_S = 0.1          # a timed region shorter than this is extended (and the line says so)
+
+
+def timed_replays(torch, graphs, steps_per_replay, steps, warmup_replays, before=None):
+    """Replays `graphs` round-robin, back to back, for at least `steps` decode steps and at least
+    MIN_TIMED_S of wall clock (a first pass of the requested length calibrates the count).  One event is
+    recorded between consecutive replays inside the timed loop, so the per-replay intervals and the
+    wall clock come from the same replays.  Returns (steps timed, seconds, per-step µs intervals)."""
+    for i in range(warmup_replays):
+        if before:
+            before(i)
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+
+    def timed(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        evs[0].record()
+        for i in range(n):
+            if before:
+                before(i)
+            graphs[i % len(graphs)].replay()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        return sec, [evs[i].elapsed_time(evs[i + 1]) * 1e3 / steps_per_replay for i in range(n)]
+
+    n = max(1, -(-steps // steps_per_replay))
+    sec, us = timed(n)
+    if sec < MIN_TIMED_S:
+        n = max(n, int(np.ceil(n * MIN_TIMED_S / max(sec, 1e-6) * 1.05)))
+        sec, us = timed(n)
+    return n * steps_per_replay, sec, us
+
+
 def run_graphed(rvq, bank, w, pool, steps, warmup, dtype, routed=True, stats=None, per_graph=1):
-    """The step replayed from HIP graphs, which removes host launch overhead; returns tokens/s over
-    `steps` decode steps.  Each graph holds per_graph consecutive steps (pool tokens j*per_graph ..),
-    one after another on one stream, as the layers of a token follow one another inside one graph
-    in a full model; per_graph = 1 adds one graph launch (about 10 µs of idle GPU) to every step.
-    routed: one rvq_moe_decode_routed call per step (router, top-k inside the gate/up kernel,
-    experts); else rvq_router_topk + rvq_moe_layer_forward.  stats (dict): filled with p10/p50/p90
-    of the per-step time (µs: each replay's time / per_graph) from a second pass."""
+    """The step replayed from HIP graphs, which removes host launch overhead; returns (tokens/s, steps
+    timed).  Each graph holds per_graph consecutive steps (pool tokens j*per_graph ..), one after
+    another on one stream, as the layers of a token follow one another inside one graph in a full
+    model; per_graph = 1 adds one graph launch (about 10 µs of idle GPU) to every step.  routed: one
+    rvq_moe_decode_routed call per step (router, top-k inside the gate/up kernel, experts); else
+    rvq_router_topk + rvq_moe_layer_forward.  stats (dict): filled with p10/p50/p90 of the per-step
+    time (µs: each replay's event interval / per_graph) from the same timed replays."""
     import torch
     dev = pool.device
     ids = torch.empty((1, K), dtype=torch.int32, device=dev)
@@ -211,22 +247,15 @@ def run_graphed(rvq, bank, w, pool, steps, warmup, dtype, routed=True, stats=Non
                     rvq.router_topk(w, pool[j], K, ids=ids, gates=gates, logits=logits)
                     rvq.moe_layer_forward(bank, pool[j], ids[0], gates[0], dtype=dtype, y=y, workspace=ws)
         graphs.append(g)
-    replays = max(1, steps // per_graph)
-    for i in range(max(1, warmup // per_graph)):
-        graphs[i % len(graphs)].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(replays):
-        graphs[i % len(graphs)].replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    n, sec, us = timed_replays(torch, graphs, per_graph, steps, max(1, -(-warmup // per_graph)))
     if stats is not None:
-        stats.update(percentiles([u / per_graph for u in replay_step_us(torch, graphs, min(replays, 256))]))
+        stats.update(percentiles(us))
+        stats["mean"] = float(np.mean(us))
     status = rvq.check_device_status(ws)
     if status:
         raise RuntimeError(rvq.status_string(status))
     del graphs
-    return replays * per_graph / (t1 - t0)
+    return n / sec, n
 
 
 def run_chunk(rvq, hip, bank, w, xt, steps, dtype):
@@ -318,7 +347,7 @@ def run_small_batch(torch, rvq, bank, w, xt, sizes=(1, 2, 4, 8, 16, 32, 64), rep
 
 
 def replay_rate(torch, graphs, steps, warmup, before=None):
-    """Replays graphs round-robin (before(i) runs eagerly ahead of replay i); returns seconds per step."""
+    """Replays graphs round-robin (before(i) runs eagerly ahead of replay i); returns seconds per replay."""
     for i in range(warmup):
         if before:
             before(i)
@@ -331,21 +360,6 @@ def replay_rate(torch, graphs, steps, warmup, before=None):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
-
-
-def replay_step_us(torch, graphs, steps, before=None):
-    """Per-replay durations (µs, sorted) from events recorded around each replay on the current
-    stream (where replay launches); a separate pass from the rate measurement, whose loop has no
-    events in it."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        if before:
-            before(i)
-        evs[i][0].record()
-        graphs[i % len(graphs)].replay()
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    return sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
 
 
 def percentiles(us):
@@ -635,8 +649,9 @@ def run_stack(torch, rvq, dev, dtype):
                                  gates=gates, logits=logits, workspace=ws)
     torch.cuda.synchronize()
     g = capture(torch, step)
-    sec = replay_rate(torch, [g], STACK_STEPS * 3, 4, before=lambda i: xin.copy_(xs[i % STACK_STEPS]))
-    per_token = percentiles(replay_step_us(torch, [g], STACK_STEPS * 3, before=lambda i: xin.copy_(xs[i % STACK_STEPS])))
+    n, total, us = timed_replays(torch, [g], 1, STACK_STEPS * 3, 4, before=lambda i: xin.copy_(xs[i % STACK_STEPS]))
+    sec = total / n
+    per_token = percentiles(us)
     status = rvq.check_device_status(ws)
     if status:
         raise RuntimeError(rvq.status_string(status))
@@ -645,7 +660,7 @@ def run_stack(torch, rvq, dev, dtype):
     torch.cuda.empty_cache()
     return {"tokens_per_s": 1.0 / sec, "ms_per_token": sec * 1e3, "code_GBps": code / sec / 1e9,
             "code_frac_of_hbm_peak": code / sec / 1e9 / HBM_PEAK_GBPS, "table_dtype": dtype,
-            "token_us_32x3": per_token}
+            "tokens_timed": n, "token_us": per_token}
 
 
 def stream_copy_peak(torch, rvq, dev):
@@ -666,6 +681,22 @@ def stream_copy_peak(torch, rvq, dev):
     dt = (time.perf_counter() - t0) / reps
     del a, b
     return 2 * n / dt / 1e9
+
+
+def stream_read_peak(torch, rvq, bank, reps=10):
+    """Read-only GB/s of rvq_stream_read over the resident bank's 4.23 GB of codes (the code stream's
+    load instruction, nothing written): the achievable rate of the table kernels' bound."""
+    sink = torch.zeros(1, dtype=torch.int32, device=bank.codes.device)
+    src = bank.codes[:bank.E * bank.stride]
+    for _ in range(2):
+        rvq.stream_read(src, sink)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        rvq.stream_read(src, sink)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    return src.numel() / dt / 1e9
 
 
 def cpu_baseline(budget_s):
@@ -739,25 +770,27 @@ def main():
     _, w = router(synth.SEED_LAYER, 0, E, H, device=dev)
     pool = torch.from_numpy(np.stack([synth.activation_f32(synth.SEED_LAYER, t, H) for t in range(POOL)])).to(dev)
     hip = Hip()
-    print("[bench] stream copy peak", file=sys.stderr, flush=True)
+    print("[bench] stream copy and read peaks", file=sys.stderr, flush=True)
     copy_gbps = stream_copy_peak(torch, rvq, dev)
+    read_gbps = stream_read_peak(torch, rvq, bank)
     print(f"[bench] timing {args.steps} steps ({args.dtype} tables)", file=sys.stderr, flush=True)
-    main_res = run_variant(rvq, hip, bank, w, pool, args.steps, args.warmup, args.dtype)
+    kernel_steps = max(args.steps, 200)   # per-kernel event timings: at least 200 samples
+    main_res = run_variant(rvq, hip, bank, w, pool, kernel_steps, args.warmup, args.dtype)
     print("[bench] graph replay", file=sys.stderr, flush=True)
     step_pct = {}
-    graph_tok_s = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, stats=step_pct,
-                              per_graph=STEPS_PER_GRAPH)
+    graph_tok_s, steps_timed = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, stats=step_pct,
+                                           per_graph=STEPS_PER_GRAPH)
     one_step_pct = {}
-    graph_one_step = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, stats=one_step_pct)
-    graph_two_call = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, routed=False,
-                                 per_graph=STEPS_PER_GRAPH)
+    graph_one_step, _ = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, stats=one_step_pct)
+    graph_two_call, _ = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, args.dtype, routed=False,
+                                    per_graph=STEPS_PER_GRAPH)
     variants = {}
     if not args.no_variants:
         other = "f16" if args.dtype == "f32" else "f32"
         print(f"[bench] timing {args.steps} steps ({other} tables)", file=sys.stderr, flush=True)
-        variants[other] = run_variant(rvq, hip, bank, w, pool, args.steps, args.warmup, other)
+        variants[other] = run_variant(rvq, hip, bank, w, pool, kernel_steps, args.warmup, other)
         variants[other]["graph_replay_tokens_per_s"] = run_graphed(rvq, bank, w, pool, args.steps, args.warmup, other,
-                                                                   per_graph=STEPS_PER_GRAPH)
+                                                                   per_graph=STEPS_PER_GRAPH)[0]
     chunk = None
     if not args.no_chunk:
         print("[bench] chunked prefill (512 tokens)", file=sys.stderr, flush=True)
@@ -793,10 +826,12 @@ def main():
         "value": graph_tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps_timed,
+        "steps_requested": args.steps,
         "warmup": args.warmup,
         "ms_per_step": 1e3 / graph_tok_s,
         "step_us": step_pct,
+        "value_from_step_us_mean": 1e6 / step_pct["mean"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -807,15 +842,20 @@ def main():
                    "resident_code_bytes": E * 3 * (H * I * 3 // 8), "token_pool": POOL},
         "code_GBps": CODE_BYTES_PER_TOKEN * graph_tok_s / 1e9,
         "code_frac_of_hbm_peak": CODE_BYTES_PER_TOKEN * graph_tok_s / 1e9 / HBM_PEAK_GBPS,
-        "code_frac_of_stream_copy": CODE_BYTES_PER_TOKEN * graph_tok_s / 1e9 / copy_gbps,
+        "code_frac_of_stream_read": CODE_BYTES_PER_TOKEN * graph_tok_s / 1e9 / read_gbps,
+        "stream_read_GBps": read_gbps,
         "stream_copy_GBps": copy_gbps,
         "decoded_weights_per_s": WEIGHTS_PER_TOKEN * graph_tok_s,
         "timing": f"value: HIP-graph replays, each graph holding {STEPS_PER_GRAPH} consecutive decode steps "
                   "(one rvq_moe_decode_routed call per token, pool tokens in order), as the layers of a token "
-                  "run inside one graph in a full model; graph_one_step_per_graph_tokens_per_s: one graph per "
-                  "step, which adds one graph launch to every step; kernel_us and roofline: HIP events around "
-                  "each kernel of the two-call form (rvq_router_topk, rvq_moe_layer_forward_timed) in an eager "
-                  "timed pass of the same steps",
+                  "run inside one graph in a full model, replayed back to back for the requested steps or, if "
+                  f"those take under {MIN_TIMED_S * 1e3:.0f} ms, for as many more as reach it (steps = steps "
+                  "timed); step_us: the same replays' event intervals / steps per graph; "
+                  "graph_one_step_per_graph_tokens_per_s: one graph per step, which adds one graph launch to "
+                  "every step; kernel_us and roofline: HIP events around each kernel of the two-call form "
+                  f"(rvq_router_topk, rvq_moe_layer_forward_timed) in an eager pass of {kernel_steps} steps; "
+                  "stream_read_GBps: rvq_stream_read over the resident bank's codes (read only, the code "
+                  "stream's loads)",
         "graph_one_step_per_graph_tokens_per_s": graph_one_step,
         "step_us_one_step_per_graph": one_step_pct,
         "graph_two_call_tokens_per_s": graph_two_call,

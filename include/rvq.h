@@ -28,9 +28,9 @@
  *    `stream`) and the expert pool's verify_status and destroy (which wait for
  *    the pool's own streams); the expert pool is the one object the library
  *    creates (host memory, streams and events of its own, freed by destroy).
- *  - Work is enqueued on `stream` (0 = the null stream).  Calls on distinct
- *    streams with distinct workspaces may run concurrently; the library's
- *    only global mutable state is the testing aid rvq_set_wait_limit.
+ *  - Work is enqueued on `stream` (0 = the null stream).  The library keeps no
+ *    global mutable state: calls on distinct streams with distinct workspaces
+ *    may run concurrently (the expert pool is an object of the caller's).
  *  - Return value: RVQ_OK (0) or an rvq_status_t error.  Every host-visible
  *    argument is validated before anything is enqueued: a call that returns an
  *    error other than RVQ_ERR_HIP has enqueued nothing.
@@ -132,10 +132,16 @@ int rvq_expert_gemv(const rvq_matrix_t *W, const float *x, int32_t lut_dtype, fl
  * (bf16 x fp32 products are exact in fp64), then the k experts with the
  * largest logits in the order (logit descending, expert id ascending) and
  * gates = softmax over those k logits (= softmax over all E renormalised to
- * the selected k).
+ * the selected k).  The pages fix only that 16 experts are chosen per layer
+ * and that none of them is dropped (news.hada.io topic 32035, read-ahead and
+ * router-prediction section; "Running a 2.78-Trillion-Parameter Model on a
+ * Laptop", Technical Insight); the linear router without bias, the tie order
+ * and the renormalised softmax gates are this library's reading, the
+ * plainest router consistent with them.
  * w_router: bf16 [E][H]; x: [T][H] of x_dtype RVQ_F32 or RVQ_BF16;
- * ids: int32 [T][k]; gates: fp32 [T][k]; logits: double [T][E], written
- * (the selection reads it back).
+ * ids: int32 [T][k]; gates: fp32 [T][k]; logits: double [T][E], written, and
+ * required (not NULL): the selection kernel reads the logits back from it, and
+ * the call takes no workspace to hold them otherwise.
  * 1 <= k <= E <= 4096, k <= 64, H >= 1, T >= 1.  No workspace.
  * ------------------------------------------------------------------------ */
 int rvq_router_topk(const void *w_router_bf16, const void *x, int32_t x_dtype, int32_t T, int32_t E, int32_t H,
@@ -175,7 +181,9 @@ size_t rvq_bank_record_bytes(int32_t hidden, int32_t inter);
  * status RVQ_ERR_EXPERT_ID in the workspace (see rvq_check_device_status).
  * workspace: 256-byte aligned, >= rvq_moe_layer_workspace_bytes(...) for
  * the same T, k and compute_dtype, and zero-filled once by
- * rvq_workspace_init before its first use.
+ * rvq_workspace_init before its first use: its header holds the sticky device
+ * status (and, for T == 1, the wait limit below), which must start at zero;
+ * the rest needs no initialisation.
  * ------------------------------------------------------------------------ */
 size_t rvq_moe_layer_workspace_bytes(const rvq_expert_bank_t *bank, int32_t T, int32_t k, int32_t compute_dtype);
 int rvq_moe_layer_forward(const rvq_expert_bank_t *bank, const void *x, int32_t x_dtype, int32_t T,
@@ -449,19 +457,29 @@ int rvq_pool_create_records(const void *host_records, int64_t record_bytes, int3
                             size_t verify_workspace_bytes, rvq_expert_pool_t **out);
 int rvq_pool_verify_status(rvq_expert_pool_t *pool, int32_t *bad_expert);
 
-/* Testing aid for the failure path.  Sets how many times each bounded wait
- * between the wave roles of the table kernels polls before it gives up
- * (which sets RVQ_ERR_DEVICE_STALL and leaves the output invalid, but lets
- * every kernel finish).  polls < 0 restores the default (4,194,304, about a
- * tenth of a second).  Returns the previous value.  Process-wide; affects
- * launches enqueued after the call. */
-int32_t rvq_set_wait_limit(int32_t polls);
-
-/* Zero-fill a workspace (with a kernel, so the call can be graph-captured). */
+/* Zero-fill a workspace (with a kernel, so the call can be graph-captured).
+ * This also resets the wait limit below to the default. */
 int rvq_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Testing aid for the failure path of the T == 1 table kernels (decode,
+ * routed decode, pre-norm block, batch decode).  Stores in the header of
+ * `workspace` how many times each bounded wait between the kernels' wave
+ * roles polls before it gives up (which sets RVQ_ERR_DEVICE_STALL in that
+ * workspace's status and leaves the output invalid, but lets every kernel
+ * finish).  polls < 0 restores the default (4,194,304, about a tenth of a
+ * second).  Enqueued on `stream` (a one-thread kernel, graph-capturable);
+ * applies to kernels that use this workspace and run after it.  The value
+ * lives in the workspace, not in the library: other workspaces are not
+ * affected.  workspace: 256-byte aligned, >= 256 bytes.  Errors: RVQ_ERR_NULL,
+ * RVQ_ERR_ALIGN, RVQ_ERR_WORKSPACE, RVQ_ERR_SHAPE (polls == INT32_MAX). */
+int rvq_workspace_set_wait_limit(void *workspace, size_t workspace_bytes, int32_t polls, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * RMSNorm with unit weight: out[t] = x[t] / sqrt(mean(x[t]^2) + eps).
+ * The pages mention norms only inside the model's trunk and give no formula;
+ * this normalisation is the one the stacked-layer decode puts between MoE
+ * layers (pre-norm residual blocks, see rvq_moe_block_decode), a reading of
+ * this library, not a passage of the pages.
  * x, out: fp32 [T][H] (may alias).  T >= 1, H >= 1, eps >= 0.
  * ------------------------------------------------------------------------ */
 int rvq_rmsnorm(const float *x, int32_t T, int32_t H, float eps, float *out, hipStream_t stream);
@@ -471,6 +489,13 @@ int rvq_rmsnorm(const float *x, int32_t T, int32_t H, float eps, float *out, hip
  * the code stream uses, so its duration gives the achievable streaming rate
  * and its memory-traffic counters scale those of the table kernels. */
 int rvq_stream_copy(const void *src, void *dst, size_t nbytes, hipStream_t stream);
+
+/* Measurement aid: reads nbytes (multiple of 16) from src (16-byte aligned)
+ * with the same non-temporal 16-byte global loads as the code stream and
+ * writes nothing but, in practice never, one word to sink (device uint32): its
+ * duration gives the achievable read-only streaming rate, the bound of the
+ * table kernels' code stream. */
+int rvq_stream_read(const void *src, size_t nbytes, uint32_t *sink, hipStream_t stream);
 
 /* Synchronises `stream`, returns the sticky device status held in the
  * workspace of rvq_moe_layer_forward (RVQ_OK, RVQ_ERR_EXPERT_ID, or

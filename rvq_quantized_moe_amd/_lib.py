@@ -18,6 +18,7 @@ F32, F16, BF16 = 0, 1, 2
 _DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
 
 RVQ_OK = 0
+RVQ_ERR_WORKSPACE = 5
 RVQ_ERR_EXPERT_ID = 6
 RVQ_ERR_RECORD = 9
 
@@ -53,8 +54,8 @@ EXPORTS = [
     "rvq_status_string", "rvq_packed_bytes", "rvq_pack_codes", "rvq_lut_build",
     "rvq_expert_gemv_workspace_bytes", "rvq_expert_gemv", "rvq_router_topk", "rvq_bank_record_bytes",
     "rvq_moe_layer_workspace_bytes", "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed",
-    "rvq_workspace_init", "rvq_rmsnorm", "rvq_stream_copy",
-    "rvq_check_device_status", "rvq_moe_decode_routed", "rvq_set_wait_limit", "rvq_moe_block_decode",
+    "rvq_workspace_init", "rvq_rmsnorm", "rvq_stream_copy", "rvq_stream_read",
+    "rvq_check_device_status", "rvq_moe_decode_routed", "rvq_workspace_set_wait_limit", "rvq_moe_block_decode",
     "rvq_moe_batch_decode", "rvq_moe_batch_decode_workspace_bytes", "rvq_bank_crc32", "rvq_bank_crc32_workspace_bytes",
     "rvq_encode", "rvq_pool_create", "rvq_pool_acquire", "rvq_pool_prefetch", "rvq_pool_stats", "rvq_pool_destroy",
     "rvq_record_bytes", "rvq_record_header_init", "rvq_record_check", "rvq_pool_verify_workspace_bytes",
@@ -92,9 +93,10 @@ def lib():
         L.rvq_rmsnorm.argtypes = [p, i32, i32, ctypes.c_float, p, p]
         L.rvq_check_device_status.argtypes = [p, p]
         L.rvq_stream_copy.argtypes = [p, p, sz, p]
+        L.rvq_stream_read.argtypes = [p, sz, p, p]
         L.rvq_moe_block_decode.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, ctypes.c_float, p, p, p, p, i32, p,
                                            sz, p]
-        L.rvq_set_wait_limit.argtypes = [i32]
+        L.rvq_workspace_set_wait_limit.argtypes = [p, sz, i32, p]
         L.rvq_moe_batch_decode.argtypes = [ctypes.POINTER(BankDesc), p, i32, p, p, i32, p, p, i32, p, sz, p]
         L.rvq_moe_batch_decode_workspace_bytes.argtypes = [ctypes.POINTER(BankDesc), i32, i32, i32]
         L.rvq_moe_batch_decode_workspace_bytes.restype = sz
@@ -127,12 +129,11 @@ def lib():
                      "rvq_pool_destroy", "rvq_record_header_init", "rvq_record_check", "rvq_pool_create_records",
                      "rvq_pool_verify_status"):
             getattr(L, name).restype = ctypes.c_int
-        L.rvq_set_wait_limit.restype = i32
         L.rvq_moe_decode_routed.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, p, p, p, p, p, i32, p, sz, p]
         for name in ("rvq_pack_codes", "rvq_lut_build", "rvq_expert_gemv", "rvq_router_topk",
                      "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed", "rvq_workspace_init", "rvq_rmsnorm",
                      "rvq_check_device_status", "rvq_stream_copy", "rvq_moe_decode_routed", "rvq_moe_block_decode",
-                     "rvq_moe_batch_decode"):
+                     "rvq_moe_batch_decode", "rvq_workspace_set_wait_limit", "rvq_stream_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -266,8 +267,20 @@ def stream_copy(src, dst):
     _check(lib().rvq_stream_copy(_ptr(src), _ptr(dst), n, _stream(src)))
 
 
+def stream_read(src, sink):
+    """Reads src (a device tensor, 16-byte multiple) with the code stream's load instruction; sink:
+    a one-word int32 device tensor that is (in practice never) written."""
+    n = src.numel() * src.element_size()
+    _check(lib().rvq_stream_read(_ptr(src), n, _ptr(sink), _stream(src)))
+
+
 def workspace_init(ws):
-    _check(lib().rvq_workspace_init(_ptr(ws), ws.numel(), _stream(ws)))
+    _check(lib().rvq_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(ws)))
+
+
+def set_wait_limit(ws, polls):
+    """Polls per bounded wait of the table kernels that use workspace `ws` (< 0: the default)."""
+    _check(lib().rvq_workspace_set_wait_limit(_ptr(ws), ws.numel() * ws.element_size(), int(polls), _stream(ws)))
 
 
 def check_device_status(ws):

@@ -303,7 +303,14 @@ int rvq_moe_block_decode(const rvq_expert_bank_t* bank, const void* w_router_bf1
                                       stream, nullptr, &route));
 }
 
-int32_t rvq_set_wait_limit(int32_t polls) { return set_wait_limit(polls); }
+int rvq_workspace_set_wait_limit(void* workspace, size_t workspace_bytes, int32_t polls, hipStream_t stream) {
+  if (!workspace) return RVQ_ERR_NULL;
+  if (!aligned(workspace, 256)) return RVQ_ERR_ALIGN;
+  if (workspace_bytes < 256) return RVQ_ERR_WORKSPACE;
+  if (polls == INT32_MAX) return RVQ_ERR_SHAPE;
+  const int32_t word = polls < 0 ? 0 : polls + 1;
+  return hip_status(launch_set_word(static_cast<int32_t*>(workspace) + kWaitLimitWord, word, stream));
+}
 
 int rvq_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!workspace) return RVQ_ERR_NULL;
@@ -318,6 +325,14 @@ int rvq_stream_copy(const void* src, void* dst, size_t nbytes, hipStream_t strea
   if (!aligned(src, 16) || !aligned(dst, 16)) return RVQ_ERR_ALIGN;
   if (nbytes == 0) return RVQ_OK;
   return hip_status(launch_stream_copy(src, dst, nbytes, stream));
+}
+
+int rvq_stream_read(const void* src, size_t nbytes, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink) return RVQ_ERR_NULL;
+  if (nbytes % 16 != 0) return RVQ_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return RVQ_ERR_ALIGN;
+  if (nbytes == 0) return RVQ_OK;
+  return hip_status(launch_stream_read(src, nbytes, sink, stream));
 }
 
 int rvq_rmsnorm(const float* x, int32_t T, int32_t H, float eps, float* out, hipStream_t stream) {

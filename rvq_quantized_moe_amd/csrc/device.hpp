@@ -8,17 +8,22 @@
 // Quantization (RVQ)"; "Running a 2.78-Trillion-Parameter Model on a Laptop:
 // Inside WASTE's NVMe-Streaming Engine", section "Technical Insight".)
 //
-// GPU mapping (one workgroup = 256 threads = 4 wave64):
-//  * A workgroup owns one K-tile (16 groups with fp32 tables, 32 with fp16) of
-//    one matrix.  It builds that tile's tables in LDS: thread c computes entry c
-//    of all 3*groups subtables (48 KiB either way, so 3 workgroups fit a CU).
-//  * Within a tile the table index of a code byte is simply its byte position
-//    b = 3*g + s inside the row's run for the tile, so the stream loop never
-//    decodes (g, s): byte b of the lane's registers reads subtable b at a
-//    compile-time LDS offset, and the address VGPR is just code << 2 (or << 1).
-//  * Codes are streamed in the packed layout: one 16-byte load per lane, 64
-//    lanes = 1 KiB contiguous per load instruction, each lane owning one row, so
-//    a row's partial sum for the tile needs no cross-lane reduction.
+// GPU mapping.  Two families of table kernels use the helpers below.
+//  * One-K-tile kernels (the single-matrix GEMV with kThreads = 512 threads = 8 waves; the fallback
+//    MoE gate/up with 256 threads and down with 1024): a workgroup owns one K-tile (16 groups with
+//    fp32 tables, 32 with fp16) of one matrix and builds that tile's plain tables in LDS
+//    (kLutBytes = 48 KiB either way): thread c computes entry c of the 3 x groups subtables
+//    (build_tile), then its waves stream row blocks through them (RowStream).  Within a tile the table
+//    index of a code byte is its byte position b = 3g + s in the row's run, so the stream loop never
+//    decodes (g, s).
+//  * Wave-specialised kernels (k_table_ws in kernels.hip, the decode path's gate/up and down): one
+//    workgroup per CU with NSW streamer waves and 4 builder waves (12 waves for gate/up, 11 for
+//    down), several K-tiles per workgroup, tables double-buffered in the skewed 64 KiB layout below
+//    (128 KiB for fp32 tables, one shared 64 KiB array for fp16), built with MFMAs while the
+//    streamers gather from the other buffer.
+//  * Codes are streamed in the packed layout: one 16-byte load per lane, 64 lanes = 1 KiB
+//    contiguous per load instruction, each lane owning one row, so a row's partial sum for a tile
+//    needs no cross-lane reduction.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -67,7 +72,7 @@ template <> struct Tile<true> {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Reductions over one workgroup of 4 waves (fixed order: deterministic).
+// Reductions over one workgroup (fixed order: deterministic).
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));

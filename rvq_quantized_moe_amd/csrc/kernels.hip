@@ -83,6 +83,38 @@ hipError_t launch_stream_copy(const void* src, void* dst, size_t nbytes, hipStre
   return hipGetLastError();
 }
 
+// Read-only stream with the same loads: each thread folds its 16-byte pieces into one word, stored
+// only if it equals a value no input produces in practice, so the loads cannot be dropped and the
+// kernel writes (almost) nothing.  Four loads in flight per thread.
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4* __restrict__ src, int64_t n16,
+                                                     uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+hipError_t launch_stream_read(const void* src, size_t nbytes, uint32_t* sink, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(nbytes / 16);
+  int64_t grid = cdiv(n16, 256 * 4);
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(k_stream_read, dim3((unsigned)grid), dim3(256), 0, stream, static_cast<const u32x4*>(src), n16,
+                     sink);
+  return hipGetLastError();
+}
+
 // =============================================================================================
 // Standalone partial-dot tables lut[g][s][c] for all groups of x (global memory output).
 // Block b builds groups [b*G, b*G+G) with G = Tile<F16>::kGroups.  fp16: one exponent for the
@@ -768,13 +800,18 @@ __device__ inline bool lds_wait_ge(int* flag, int target, int limit) {
   return false;
 }
 
-// Polls per bounded wait of the wave-specialised kernels (see rvq_set_wait_limit).
-static int g_wait_limit = kSpinLimit;
+// Polls per bounded wait of the wave-specialised kernels: word kWaitLimitWord of the workspace
+// header holds 0 for the default (kSpinLimit) or polls + 1 (set by rvq_workspace_set_wait_limit).
+__device__ inline int wait_polls(const int32_t* header) {
+  const int32_t w = header[kWaitLimitWord];
+  return w <= 0 ? kSpinLimit : w - 1;
+}
 
-int set_wait_limit(int polls) {
-  const int old = g_wait_limit;
-  g_wait_limit = polls < 0 ? kSpinLimit : polls;
-  return old;
+__global__ void k_set_word(int32_t* p, int32_t v) { *p = v; }
+
+hipError_t launch_set_word(int32_t* p, int32_t v, hipStream_t stream) {
+  hipLaunchKernelGGL(k_set_word, dim3(1), dim3(1), 0, stream, p, v);
+  return hipGetLastError();
 }
 
 // Compute units of the current device (0 if the query fails), cached per device.
@@ -806,7 +843,6 @@ struct PipeArgs {
   int32_t* ids_out;
   float* gates_out;
   int k;
-  int wait_limit;         // polls per bounded wait (kSpinLimit unless a test lowers it)
   int gu_stride;          // down: partials stored per (slot, matrix) in part_gu (>= ngu)
 };
 constexpr int kRouteMaxExperts = 1024;
@@ -836,6 +872,7 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
   const int H = bank.H, I = bank.I;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  const int wait_limit = wait_polls(status);   // status points at the workspace header
   // geometry of this workgroup
   int slot, m, t0, rb0;
   if constexpr (DOWN) {
@@ -960,7 +997,7 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
     for (int i = 0; i < NB && i < NBLK; ++i) load_blk(i, i);   // never past the workgroup's blocks
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
-      ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1), pa.wait_limit);
+      ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1), wait_limit);
 #pragma unroll
       for (int r = 0; r < BPI; ++r) {
         const int s = k * BPI + r;
@@ -1016,12 +1053,12 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
     }
     if (DOWN || F16) {
       if (lane == 0) __hip_atomic_fetch_add(&hready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      ok &= lds_wait_ge(&hready, kPipeBuildWaves, pa.wait_limit);
+      ok &= lds_wait_ge(&hready, kPipeBuildWaves, wait_limit);
       if constexpr (F16) cmax2 = __int_as_float(cmax_bits);
     }
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
-      if (k >= 2) ok &= lds_wait_ge(&done[k & 1], NSW * (k / 2), pa.wait_limit);
+      if (k >= 2) ok &= lds_wait_ge(&done[k & 1], NSW * (k / 2), wait_limit);
       // an opaque copy pins this item's products after the wait (otherwise the compiler may compute
       // every item's tables up front)
       f32x2 xk;
@@ -1366,7 +1403,7 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
   if (chunk) {
     const dim3 grid((unsigned)(P * 2 * ngu));
     const PipeArgs pa{x,       nullptr, part_gu, ngu, 1, 0, fused_route ? route->logits : nullptr,
-                      route ? route->ids : nullptr, route ? route->gates : nullptr, k, g_wait_limit, 0};
+                      route ? route->ids : nullptr, route ? route->gates : nullptr, k, 0};
     switch (chunk) {
 #define RVQ_WS_CASE(n)                                                                                             \
   case n:                                                                                                          \
@@ -1395,8 +1432,7 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
                          stream, part_gu, ngu, ngu, (int64_t)pad_rows(I));
     const int nkc = nt16_out / dchunk;
     const dim3 grid((unsigned)(P * nrc * nkc));
-    const PipeArgs pa{nullptr, part_gu, part_d, nkc, nrc, sum_gu ? 1 : ngu, nullptr, nullptr, nullptr, k,
-                      g_wait_limit, ngu};
+    const PipeArgs pa{nullptr, part_gu, part_d, nkc, nrc, sum_gu ? 1 : ngu, nullptr, nullptr, nullptr, k, ngu};
     if (dn_bpi == 1) {
 #define RVQ_WS_CASE1(n)                                                                                            \
   case n:                                                                                                          \

@@ -25,6 +25,7 @@ size_t gemv_workspace_bytes(int rows, int cols, bool f16);
 hipError_t launch_pack(const uint8_t* src, int rows, int cols, uint8_t* dst, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t nbytes, hipStream_t stream);
 hipError_t launch_stream_copy(const void* src, void* dst, size_t nbytes, hipStream_t stream);
+hipError_t launch_stream_read(const void* src, size_t nbytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_lut_build(const float* x, int cols, const float* cb, bool f16, void* lut, int32_t* log2_scale,
                             hipStream_t stream);
 hipError_t launch_gemv(const uint8_t* codes, const float* cb, int rows, int cols, const float* x, bool f16, float* y,
@@ -32,8 +33,10 @@ hipError_t launch_gemv(const uint8_t* codes, const float* cb, int rows, int cols
 hipError_t launch_router_topk(const uint16_t* w, const void* x, bool x_bf16, int T, int E, int H, int k, int32_t* ids,
                               float* gates, double* logits, hipStream_t stream);
 hipError_t launch_rmsnorm(const float* x, int T, int H, float eps, float* out, hipStream_t stream);
-// Polls per bounded wait inside the wave-specialised kernels; returns the previous value (< 0: default).
-int set_wait_limit(int polls);
+// Word of the decode workspace header (int32 index) holding the polls per bounded wait of the
+// wave-specialised kernels: 0 = the default, else polls + 1.  Word 0 is the sticky status.
+constexpr int kWaitLimitWord = 1;
+hipError_t launch_set_word(int32_t* p, int32_t v, hipStream_t stream);
 // T tokens of decode through the table path (x, residual, y: [T][H]; ids, gates: [T][k]); the
 // workspace holds moe_workspace_layout(H, I, T * k, f16).
 hipError_t launch_moe_batch_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,

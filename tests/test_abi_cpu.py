@@ -290,6 +290,10 @@ def test_misc_validation(L):
     assert L.rvq_workspace_init(None, 16, s) == NULL
     assert L.rvq_workspace_init(FAKE + 8, 16, s) == ALIGN
     assert L.rvq_check_device_status(None, s) == NULL
+    assert L.rvq_workspace_set_wait_limit(None, 256, 0, s) == NULL
+    assert L.rvq_workspace_set_wait_limit(FAKE + 8, 256, 0, s) == ALIGN
+    assert L.rvq_workspace_set_wait_limit(FAKE, 255, 0, s) == WS
+    assert L.rvq_workspace_set_wait_limit(FAKE, 256, 2 ** 31 - 1, s) == SHAPE
 
 
 def test_validator_fuzz(L):

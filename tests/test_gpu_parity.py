@@ -759,23 +759,27 @@ def test_moe_layer_other_shapes(H, I, E, k, dtype):
 
 def test_bounded_waits_give_up_and_report(layer_bank):
     """Failure path of the wave-specialised kernels, forced from the host: with their bounded waits cut
-    to zero polls they still finish (every access stays in bounds) and the workspace reports
-    RVQ_ERR_DEVICE_STALL; the default limit brings back the exact result."""
+    to zero polls in one workspace they still finish (every access stays in bounds) and that workspace
+    reports RVQ_ERR_DEVICE_STALL, while a second workspace used in between keeps the default and gives
+    the exact result; the default limit then brings back the exact result in the first as well."""
     say("bounded waits cut to zero polls")
     bank, bits, w = layer_bank
-    L = rvq.lib()
     x = to_dev(synth.activation_f32(synth.SEED_LAYER, 9, HIDDEN))
     ids, gates, _ = rvq.router_topk(w, x, TOP_K)
     ws = rvq.make_moe_workspace(bank, 1, TOP_K, "f32")
+    other = rvq.make_moe_workspace(bank, 1, TOP_K, "f32")
     ref = rvq.moe_layer_forward(bank, x, ids[0], gates[0], workspace=ws)
     assert rvq.check_device_status(ws) == 0
-    L.rvq_set_wait_limit(0)
-    try:
-        rvq.moe_layer_forward(bank, x, ids[0], gates[0], workspace=ws)
-        st = rvq.check_device_status(ws)
-    finally:
-        L.rvq_set_wait_limit(-1)
-    assert st == 8  # RVQ_ERR_DEVICE_STALL
+    rvq.set_wait_limit(ws, 0)
+    rvq.moe_layer_forward(bank, x, ids[0], gates[0], workspace=ws)
+    assert rvq.check_device_status(ws) == 8  # RVQ_ERR_DEVICE_STALL
+    assert torch.equal(rvq.moe_layer_forward(bank, x, ids[0], gates[0], workspace=other), ref)
+    assert rvq.check_device_status(other) == 0
+    rvq.set_wait_limit(ws, -1)
     again = rvq.moe_layer_forward(bank, x, ids[0], gates[0], workspace=ws)
     assert rvq.check_device_status(ws) == 0
     assert torch.equal(again, ref)
+    rvq.set_wait_limit(ws, 0)
+    rvq.workspace_init(ws)              # a zero-filled header is the default limit again
+    assert torch.equal(rvq.moe_layer_forward(bank, x, ids[0], gates[0], workspace=ws), ref)
+    assert rvq.check_device_status(ws) == 0
