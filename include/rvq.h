@@ -220,6 +220,32 @@ int rvq_moe_decode_routed(const rvq_expert_bank_t *bank, const void *w_router_bf
                           int32_t compute_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * rvq_moe_decode_routed without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture that may not call
+ * hipMalloc, tight serving loops, harnesses that forbid allocation).  Same
+ * kernels, same results bit for bit; the gate/up and down partial sums live
+ * in a static array of the library, 24 MiB (25,165,824 bytes) per GPU, held
+ * from the library's first use on that GPU until the process ends.  The call
+ * allocates nothing: no hipMalloc, hipFree or allocating library routine.
+ * Its layout must fit: the layout of rvq_moe_layer_workspace_bytes(bank, 1,
+ * k, compute_dtype) (22,050,560 bytes at hidden 7168, inter 2048, k = 16) may
+ * not exceed 24 MiB, else RVQ_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU shares that GPU's array: two calls that overlap on
+ * one GPU (on different streams) race and give undefined results; calls
+ * ordered on one stream, or on streams ordered by events, are safe.
+ * status: DEVICE int32[2] (at least 8 bytes, 256-byte aligned), zero-filled
+ * by the caller before its first use: word 0 collects the sticky device
+ * status as a workspace header does (read and clear it with
+ * rvq_check_device_status(status, stream)), word 1 is the wait limit (0 = the
+ * default; a status buffer of 256 bytes may be passed to
+ * rvq_workspace_set_wait_limit).  Other arguments as for
+ * rvq_moe_decode_routed.
+ * ------------------------------------------------------------------------ */
+int rvq_moe_decode_routed_scratch(const rvq_expert_bank_t *bank, const void *w_router_bf16, const float *x, int32_t k,
+                                  const float *residual, float *y, int32_t *ids, float *gates, double *logits,
+                                  int32_t compute_dtype, int32_t *status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * One pre-norm residual MoE block for one token (a layer of the stack):
  *   n = RMSNorm(h) (unit weight, as rvq_rmsnorm);  h_out = h + MoE(n)
  * with the router, top-k and expert forward of rvq_moe_decode_routed on n.

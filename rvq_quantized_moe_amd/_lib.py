@@ -60,6 +60,7 @@ EXPORTS = [
     "rvq_encode", "rvq_pool_create", "rvq_pool_acquire", "rvq_pool_prefetch", "rvq_pool_stats", "rvq_pool_destroy",
     "rvq_record_bytes", "rvq_record_header_init", "rvq_record_check", "rvq_pool_verify_workspace_bytes",
     "rvq_pool_create_records", "rvq_pool_verify_status", "rvq_fit_workspace_bytes", "rvq_fit",
+    "rvq_moe_decode_routed_scratch",
 ]
 
 
@@ -130,10 +131,12 @@ def lib():
                      "rvq_pool_verify_status"):
             getattr(L, name).restype = ctypes.c_int
         L.rvq_moe_decode_routed.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, p, p, p, p, p, i32, p, sz, p]
+        L.rvq_moe_decode_routed_scratch.argtypes = [ctypes.POINTER(BankDesc), p, p, i32, p, p, p, p, p, i32, p, p]
         for name in ("rvq_pack_codes", "rvq_lut_build", "rvq_expert_gemv", "rvq_router_topk",
                      "rvq_moe_layer_forward", "rvq_moe_layer_forward_timed", "rvq_workspace_init", "rvq_rmsnorm",
                      "rvq_check_device_status", "rvq_stream_copy", "rvq_moe_decode_routed", "rvq_moe_block_decode",
-                     "rvq_moe_batch_decode", "rvq_workspace_set_wait_limit", "rvq_stream_read"):
+                     "rvq_moe_batch_decode", "rvq_workspace_set_wait_limit", "rvq_stream_read",
+                     "rvq_moe_decode_routed_scratch"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -8,7 +8,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librvq.so")
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "chunk.hip"), os.path.join(CSRC, "verify.hip"),
-           os.path.join(CSRC, "encode.hip"),
+           os.path.join(CSRC, "encode.hip"), os.path.join(CSRC, "scratch.hip"),
            os.path.join(CSRC, "abi.cpp"), os.path.join(CSRC, "pool.cpp")]
 HEADERS = [os.path.join(CSRC, "device.hpp"), os.path.join(CSRC, "launch.hpp"), os.path.join(ROOT, "include", "rvq.h")]
 

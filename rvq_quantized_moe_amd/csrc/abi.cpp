@@ -278,6 +278,25 @@ int rvq_moe_decode_routed(const rvq_expert_bank_t* bank, const void* w_router_bf
                                       stream, nullptr, &route));
 }
 
+int rvq_moe_decode_routed_scratch(const rvq_expert_bank_t* bank, const void* w_router_bf16, const float* x, int32_t k,
+                                  const float* residual, float* y, int32_t* ids, float* gates, double* logits,
+                                  int32_t compute_dtype, int32_t* status, hipStream_t stream) {
+  int st = check_bank(bank);
+  if (st != RVQ_OK) return st;
+  if (!w_router_bf16 || !x || !y || !ids || !gates || !logits || !status) return RVQ_ERR_NULL;
+  if (k < 1 || k > kMaxTopK || k > bank->num_experts || bank->num_experts > kMaxExperts) return RVQ_ERR_SHAPE;
+  if (!table_dtype(compute_dtype)) return RVQ_ERR_DTYPE;
+  if (!aligned(status, 256) || !aligned(w_router_bf16, 2) || !aligned(x, 4) || !aligned(y, 4) || !aligned(ids, 4) ||
+      !aligned(gates, 4) || !aligned(logits, 8) || (residual && !aligned(residual, 4)))
+    return RVQ_ERR_ALIGN;
+  const bool f16 = compute_dtype == RVQ_F16;
+  if (moe_workspace_layout(bank->hidden, bank->inter, k, f16).total > kScratchBytes) return RVQ_ERR_WORKSPACE;
+  return hip_status(launch_moe_decode_routed_scratch(bank->codes, bank->codebooks, bank->record_stride,
+                                                     bank->num_experts, bank->hidden, bank->inter,
+                                                     static_cast<const uint16_t*>(w_router_bf16), x, k, residual, y,
+                                                     ids, gates, logits, f16, status, stream));
+}
+
 int rvq_moe_block_decode(const rvq_expert_bank_t* bank, const void* w_router_bf16, const float* h, int32_t k,
                          float eps, float* h_out, int32_t* ids, float* gates, double* logits, int32_t compute_dtype,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {

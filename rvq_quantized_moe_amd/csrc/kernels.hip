@@ -1319,14 +1319,15 @@ __global__ __launch_bounds__(256) void k_sum_gu_partials(float* __restrict__ par
 // expert) is one "slot" of the kernels, which read x, residual and y at row p / k; the chunk sizes
 // are chosen from one token's counts, so every pair is computed exactly as in a single-token call.
 // Shapes without both wave-specialised forms run the tokens one after another.
+// status_hdr: where the status and wait-limit words are (the workspace header when null).
 static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
                                 const float* x, int T, const int32_t* ids, const float* gates, int k,
                                 const float* residual, float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev,
-                                const Route* route) {
+                                const Route* route, int32_t* status_hdr = nullptr) {
   const int P = T * k;
   const MoeWorkspace w = moe_workspace_layout(H, I, P, f16);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  int32_t* status = reinterpret_cast<int32_t*>(base + w.status_off);
+  int32_t* status = status_hdr ? status_hdr : reinterpret_cast<int32_t*>(base + w.status_off);
   float* part_gu = reinterpret_cast<float*>(base + w.part_gu_off);
   float* part_d = reinterpret_cast<float*>(base + w.part_d_off);
   BankArgs bank{codes, cb, stride, E, H, I};
@@ -1384,7 +1385,7 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
     for (int t = 0; t < T; ++t) {
       const hipError_t e = decode_tokens(codes, cb, stride, E, H, I, x + (int64_t)t * H, 1, ids + t * k, gates + t * k,
                                          k, residual ? residual + (int64_t)t * H : nullptr, y + (int64_t)t * H, f16, ws,
-                                         stream, nullptr, nullptr);
+                                         stream, nullptr, nullptr, status_hdr);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -1478,8 +1479,10 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
 
 hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
                              const float* x, const int32_t* ids, const float* gates, int k, const float* residual,
-                             float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev, const Route* route) {
-  return decode_tokens(codes, cb, stride, E, H, I, x, 1, ids, gates, k, residual, y, f16, ws, stream, ev, route);
+                             float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev, const Route* route,
+                             int32_t* status_hdr) {
+  return decode_tokens(codes, cb, stride, E, H, I, x, 1, ids, gates, k, residual, y, f16, ws, stream, ev, route,
+                       status_hdr);
 }
 
 hipError_t launch_moe_batch_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,

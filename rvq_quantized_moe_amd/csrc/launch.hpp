@@ -74,10 +74,20 @@ struct Route {
 };
 // route == nullptr: ids/gates are inputs.  Otherwise ids/gates are ignored and the top-k of
 // route->logits is taken first (inside the gate/up kernel when it can), written to route->ids/gates.
+// status_hdr: the status and wait-limit words, when they are not the workspace's header (the
+// static-scratch variant keeps them in caller memory).
 hipError_t launch_moe_decode(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
                              const float* x, const int32_t* ids, const float* gates, int k, const float* residual,
                              float* y, bool f16, void* ws, hipStream_t stream, hipEvent_t* ev,
-                             const Route* route = nullptr);
+                             const Route* route = nullptr, int32_t* status_hdr = nullptr);
+
+// Routed decode through the library's static per-device scratch array (scratch.hip): no workspace
+// argument, nothing allocated.  kScratchBytes bounds the layout moe_workspace_layout(H, I, k, f16).
+constexpr size_t kScratchBytes = (size_t)24 << 20;
+hipError_t launch_moe_decode_routed_scratch(const uint8_t* codes, const float* cb, int64_t stride, int E, int H,
+                                            int I, const uint16_t* w_router, const float* x, int k,
+                                            const float* residual, float* y, int32_t* ids, float* gates,
+                                            double* logits, bool f16, int32_t* status, hipStream_t stream);
 
 size_t chunk_workspace_bytes(int E, int H, int I, int T, int k);
 hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,

@@ -281,6 +281,21 @@ def test_chunk_workspace_and_validation(L):
     del ok
 
 
+def test_scratch_decode_validation(L):
+    """The no-workspace routed decode: its arguments are checked as rvq_moe_decode_routed's, its status
+    words must be given (256-byte aligned), and a layout past the static array (24 MiB) is refused."""
+    s = None
+    b = _bank(E=256)
+    args = lambda **kw: (kw.get("bank", b), FAKE, FAKE, kw.get("k", 16), None, FAKE, FAKE, FAKE, FAKE,
+                         kw.get("dtype", 0), kw.get("status", FAKE), s)
+    assert L.rvq_moe_decode_routed_scratch(*args(status=None)) == NULL
+    assert L.rvq_moe_decode_routed_scratch(*args(status=FAKE + 4)) == ALIGN
+    assert L.rvq_moe_decode_routed_scratch(*args(dtype=2)) == DTYPE
+    assert L.rvq_moe_decode_routed_scratch(*args(k=0)) == SHAPE
+    assert L.rvq_moe_decode_routed_scratch(*args(k=64)) == WS          # 7168/2048 at k = 64: 88 MB of partials
+    assert L.rvq_moe_layer_workspace_bytes(b, 1, 16, 0) <= 24 << 20     # the layer decode's k = 16 fits
+
+
 def test_misc_validation(L):
     s = None
     assert L.rvq_rmsnorm(None, 1, 8, 1e-6, FAKE, s) == NULL
