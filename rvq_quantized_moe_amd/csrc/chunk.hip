@@ -11,6 +11,9 @@
 // B[8(l/16) .. +7][l%16]; D[4(l/16)+i][l%16] in its 4 accumulators.  One RVQ group (8 consecutive
 // input columns of one weight row) is exactly one lane's A fragment, so a lane decodes its group
 // (three codebook vectors summed) into registers and issues the MFMA; no weight tile is written.
+// Which K columns form an MFMA step is free as long as A and B agree: in a 16-group K-tile, step kk
+// gives lane slice q group 4q + kk, so a lane's four groups are 12 consecutive code bytes of its row
+// (three aligned dwords), and each codebook address is one byte-select shift of a code dword.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -30,12 +33,13 @@ constexpr int kChunkK = 128;              // K columns per staged tile (16 group
 constexpr int kXStride = kChunkK + 8;     // staged token row length in 16-bit elements (pad: banks)
 
 struct ChunkWs {
-  size_t status_off, offsets_off, pair_token_off, pair_pos_off, hmax_off, h_off, y_off, total;
+  size_t status_off, offsets_off, pair_token_off, pair_pos_off, hmax_off, h_off, y_off, x16_off, h16_off, total;
 };
 
 // Workspace layout of the chunk path (all 256-byte aligned):
 //   status int32 | offsets int32[E+1] | pair_token int32[P] | pair_pos int32[T*k]
 //   | hmax uint32[P] (bit pattern of max|h| per pair) | h fp32 [P][I] | y fp32 [P][H]
+//   | x16 fp16 [T][H] (the chunk in fp16, for fp16 tiles) | h16 16-bit [P][I] (h as the down operand)
 ChunkWs chunk_ws_layout(int E, int H, int I, int T, int k) {
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t P = (size_t)T * k;
@@ -47,7 +51,9 @@ ChunkWs chunk_ws_layout(int E, int H, int I, int T, int k) {
   w.hmax_off = w.pair_pos_off + up(P * 4);
   w.h_off = w.hmax_off + up(P * 4);
   w.y_off = w.h_off + up(P * (size_t)I * 4);
-  w.total = w.y_off + up(P * (size_t)H * 4);
+  w.x16_off = w.y_off + up(P * (size_t)H * 4);
+  w.h16_off = w.x16_off + up((size_t)T * H * 2);
+  w.total = w.h16_off + up(P * (size_t)I * 2);
   return w;
 }
 
@@ -134,24 +140,54 @@ __device__ inline void load_codebooks(_Float16* d, const float* __restrict__ cb)
   }
 }
 
+// LDS accesses by absolute address: each chunk kernel's LDS is the one dynamic array chunk_lds (no
+// static LDS), which therefore starts at LDS address 0 (checked at kernel entry: lds_at_zero), so an
+// address is an offset into it and constant parts go into the instruction's offset field.
+extern __shared__ __attribute__((aligned(16))) uint8_t chunk_lds[];
+typedef __attribute__((address_space(3))) const half8 lds_half8;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+__device__ __forceinline__ half8 lds_h8(uint32_t a) { return *(lds_half8*)(uintptr_t)a; }
+__device__ __forceinline__ uint32_t lds_w(uint32_t a) { return *(lds_u32*)(uintptr_t)a; }
+__device__ __forceinline__ bool lds_at_zero() {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)chunk_lds == 0u;
+}
+
+// 16 * (byte b of d), b a constant: one v_lshlrev_b32 whose source is the byte (SDWA byte select), the
+// byte offset of a 16-byte codebook entry.
+__device__ __forceinline__ uint32_t byte_x16(uint32_t d, int b) {
+  uint32_t r;
+  switch (b) {
+    case 0: asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(d)); break;
+    case 1: asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(d)); break;
+    case 2: asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(d)); break;
+    default: asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(d)); break;
+  }
+  return r;
+}
+
+// Stage s's entry of group kk (of the four in a lane's 12 code bytes d[0..2]): byte 3kk + s.
+__device__ __forceinline__ uint32_t code_off(const uint32_t (&d)[3], int kk, int st) {
+  const int b = 3 * kk + st;
+  return byte_x16(d[b >> 2], b & 3);
+}
+
 template <bool F16>
 struct Decoder;
 
+// cb: LDS address of the matrix's codebooks (stage s at cb + 4096 s); o0..o2: entry byte offsets.
 template <>
 struct Decoder<true> {
   typedef half8 frag_t;
-  __device__ static frag_t decode(const _Float16* cbs, uint32_t c) {
-    const half8* t = reinterpret_cast<const half8*>(cbs);
-    return t[c & 255u] + t[256 + ((c >> 8) & 255u)] + t[512 + ((c >> 16) & 255u)];
+  __device__ static frag_t decode(uint32_t cb, uint32_t o0, uint32_t o1, uint32_t o2) {
+    return lds_h8(o0 + cb) + lds_h8(o1 + cb + 4096) + lds_h8(o2 + cb + 8192);
   }
 };
 
 template <>
 struct Decoder<false> {
   typedef bf16x8 frag_t;
-  __device__ static frag_t decode(const _Float16* cbs, uint32_t c) {
-    const half8* t = reinterpret_cast<const half8*>(cbs);
-    const half8 a = t[c & 255u], b = t[256 + ((c >> 8) & 255u)], d = t[512 + ((c >> 16) & 255u)];
+  __device__ static frag_t decode(uint32_t cb, uint32_t o0, uint32_t o1, uint32_t o2) {
+    const half8 a = lds_h8(o0 + cb), b = lds_h8(o1 + cb + 4096), d = lds_h8(o2 + cb + 8192);
     frag_t f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = (__bf16)((float)a[i] + (float)b[i] + (float)d[i]);
@@ -161,45 +197,22 @@ struct Decoder<false> {
 
 __device__ inline f32x4 mfma16(half8 a, half8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
-
-// The 48 code bytes of row r of a staged slab (byte b of the row's run at (b/16)*1024 + r*16 + b%16)
-// as 12 dwords, and the three code bytes of group g = 4kk + q (q < 4) within them: the 12-byte
-// window of kk holds groups 4kk .. 4kk+3, group q at bytes 3q .. 3q+2.
-struct RowCodes {
-  uint32_t w[12];
-  __device__ void load(const uint8_t* slab, int r) {
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(slab + j * 1024 + r * 16);
-      w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
-    }
-  }
-  __device__ uint32_t group(int kk, int q) const {   // c0 | c1 << 8 | c2 << 16
-    const uint64_t lo = (uint64_t)w[3 * kk] | ((uint64_t)w[3 * kk + 1] << 32);
-    const uint64_t hi = (uint64_t)w[3 * kk + 1] | ((uint64_t)w[3 * kk + 2] << 32);
-    return (uint32_t)(q < 2 ? lo >> (24 * q) : hi >> (24 * q - 32));
-  }
-};
+__device__ inline f32x4 mfma16(bf16x8 a, half8 b, f32x4 c) { return mfma16(a, __builtin_bit_cast(bf16x8, b), c); }
 
 // ---------------------------------------------------------------------------------------------
 // Expert GEMM for one 64-row block of NMAT matrices of one expert (NMAT = 2: gate and up, which
 // share the activations; NMAT = 1: down).  Wave w owns rows [16w, 16w+16) of every matrix.
 //   acc[m][tb] (lane l, i) = sum_k W_m[row0 + 16w + 4(l/16) + i][k] * act[pair tb*16 + l%16][k]
-// Per 128-column K-tile, the NMAT code slabs and the activations of up to 64 pairs (16-bit rows)
-// sit in one half of a double buffer in LDS.  The next K-tile's global loads are issued into
-// registers before this tile's MFMAs and written to the other half after them, so one barrier per
-// K-tile separates the halves and the load latency hides behind the compute.
+// Per 128-column K-tile, the NMAT code slabs and the 16-bit activations of up to 64 pairs sit in
+// one half of a double buffer in LDS.  The next K-tile's global loads are issued into registers
+// before this tile's MFMAs and written to the other half after them, so one barrier per K-tile
+// separates the halves and the load latency hides behind the compute.
 
-// Activation source for the gate/up product: bf16 token rows of the chunk, gathered by pair.
-struct ActTokens {
-  const uint16_t* x;      // bf16 [T][K]
-  const int32_t* pair_token;
-  int K;
-};
-// Activation source for the down product: fp32 h rows [P][K] (per pair), scaled by 2^-e for fp16.
-struct ActH {
-  const float* h;
-  const uint32_t* hmax;
+// Activation rows of a product, already 16-bit (the MFMA operand type): the chunk's tokens
+// gathered by pair (gate/up: rowmap = pair -> token) or the pairs' h (down: rowmap = null).
+struct Act16 {
+  const uint16_t* src;      // [rows][K]
+  const int32_t* rowmap;
   int K;
 };
 
@@ -215,20 +228,19 @@ __device__ inline int h_exponent(uint32_t maxbits) {
 // 16-byte pieces of the activation tile (64 rows x 16 pieces): piece u covers row (tid + 256u)/16.
 constexpr int kActPieces = kChunkTok * (kChunkK / 8) / 256;   // 4 (256-thread workgroups)
 
-template <bool F16, int NMAT>
+template <int NMAT>
 struct StageRegs {
   u32x4 slab[NMAT];
   u32x4 act[kActPieces];
-  f32x4 hsrc[kActPieces][2];  // ActH: the fp32 source of each piece
 };
 
-struct TokenRows {  // per pass: the token of each of this thread's activation rows (-1: none)
+struct TokenRows {  // per pass: the source row of each of this thread's activation rows (-1: none)
   int t[kActPieces];
 };
 
-template <bool F16, int NMAT>
-__device__ inline void stage_issue(StageRegs<F16, NMAT>& s, const uint8_t* const (&mats)[NMAT], int kt, int nrb, int rb,
-                                   const ActTokens& a, const TokenRows& tr, int k0) {
+template <int NMAT>
+__device__ inline void stage_issue(StageRegs<NMAT>& s, const uint8_t* const (&mats)[NMAT], int kt, int nrb, int rb,
+                                   const Act16& a, const TokenRows& tr, int k0) {
   if (threadIdx.x < kSlabBytes / 16) {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
@@ -238,31 +250,8 @@ __device__ inline void stage_issue(StageRegs<F16, NMAT>& s, const uint8_t* const
   for (int u = 0; u < kActPieces; ++u) {
     const int c8 = (threadIdx.x + 256 * u) % (kChunkK / 8);
     const int t = tr.t[u];
-    s.act[u] = (t >= 0 && k0 + c8 * 8 < a.K) ? *reinterpret_cast<const u32x4*>(a.x + (int64_t)t * a.K + k0 + c8 * 8)
+    s.act[u] = (t >= 0 && k0 + c8 * 8 < a.K) ? *reinterpret_cast<const u32x4*>(a.src + (int64_t)t * a.K + k0 + c8 * 8)
                                              : u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-template <bool F16, int NMAT>
-__device__ inline void stage_issue(StageRegs<F16, NMAT>& s, const uint8_t* const (&mats)[NMAT], int kt, int nrb, int rb,
-                                   const ActH& a, const TokenRows& tr, int k0) {
-  if (threadIdx.x < kSlabBytes / 16) {
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-      s.slab[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes) + threadIdx.x);
-  }
-#pragma unroll
-  for (int u = 0; u < kActPieces; ++u) {
-    const int c8 = (threadIdx.x + 256 * u) % (kChunkK / 8);
-    const int p = tr.t[u];  // pair index for ActH
-    if (p >= 0 && k0 + c8 * 8 < a.K) {
-      const float* src = a.h + (int64_t)p * a.K + k0 + c8 * 8;
-      s.hsrc[u][0] = *reinterpret_cast<const f32x4*>(src);
-      s.hsrc[u][1] = *reinterpret_cast<const f32x4*>(src + 4);
-    } else {
-      s.hsrc[u][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      s.hsrc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
   }
 }
 
@@ -275,9 +264,8 @@ __device__ inline uint32_t pack_b2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
 }
 
-template <bool F16, int NMAT>
-__device__ inline void stage_store(const StageRegs<F16, NMAT>& s, uint8_t* code_lds, uint16_t* x_lds, const ActTokens&,
-                                   const float (&)[kActPieces]) {
+template <int NMAT>
+__device__ inline void stage_store(const StageRegs<NMAT>& s, uint8_t* code_lds, uint16_t* x_lds) {
   if (threadIdx.x < kSlabBytes / 16) {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) reinterpret_cast<u32x4*>(code_lds + m * kSlabBytes)[threadIdx.x] = s.slab[m];
@@ -285,63 +273,21 @@ __device__ inline void stage_store(const StageRegs<F16, NMAT>& s, uint8_t* code_
 #pragma unroll
   for (int u = 0; u < kActPieces; ++u) {
     const int q = threadIdx.x + 256 * u, j = q / (kChunkK / 8), c8 = q % (kChunkK / 8);
-    u32x4 v = s.act[u];
-    if constexpr (F16) {  // bf16 -> fp16 (exact for |x| below the fp16 range)
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = pack_h2(__uint_as_float(w[r] << 16), __uint_as_float(w[r] & 0xffff0000u));
-      v = u32x4{w[0], w[1], w[2], w[3]};
-    }
-    *reinterpret_cast<u32x4*>(x_lds + j * kXStride + c8 * 8) = v;
+    *reinterpret_cast<u32x4*>(x_lds + j * kXStride + c8 * 8) = s.act[u];
   }
 }
 
-template <bool F16, int NMAT>
-__device__ inline void stage_store(const StageRegs<F16, NMAT>& s, uint8_t* code_lds, uint16_t* x_lds, const ActH&,
-                                   const float (&sc)[kActPieces]) {
-  if (threadIdx.x < kSlabBytes / 16) {
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) reinterpret_cast<u32x4*>(code_lds + m * kSlabBytes)[threadIdx.x] = s.slab[m];
-  }
-#pragma unroll
-  for (int u = 0; u < kActPieces; ++u) {
-    const int q = threadIdx.x + 256 * u, j = q / (kChunkK / 8), c8 = q % (kChunkK / 8);
-    const f32x4 a = s.hsrc[u][0], b = s.hsrc[u][1];
-    u32x4 v;
-    if constexpr (F16) {
-      const float f = sc[u];
-      v = u32x4{pack_h2(a.x * f, a.y * f), pack_h2(a.z * f, a.w * f), pack_h2(b.x * f, b.y * f), pack_h2(b.z * f, b.w * f)};
-    } else {
-      v = u32x4{pack_b2(a.x, a.y), pack_b2(a.z, a.w), pack_b2(b.x, b.y), pack_b2(b.z, b.w)};
-    }
-    *reinterpret_cast<u32x4*>(x_lds + j * kXStride + c8 * 8) = v;
-  }
-}
-
-// per pass: which token (gate/up) or pair (down) each activation row of this thread reads
-__device__ inline void pass_rows(TokenRows& tr, float (&sc)[kActPieces], const ActTokens& a, int p0, int np) {
+// per pass: which source row each activation row of this thread reads
+__device__ inline void pass_rows(TokenRows& tr, const Act16& a, int p0, int np) {
 #pragma unroll
   for (int u = 0; u < kActPieces; ++u) {
     const int j = (threadIdx.x + 256 * u) / (kChunkK / 8);
-    tr.t[u] = j < np ? a.pair_token[p0 + j] : -1;
-    sc[u] = 1.f;
-  }
-}
-__device__ inline void pass_rows(TokenRows& tr, float (&sc)[kActPieces], const ActH& a, int p0, int np) {
-#pragma unroll
-  for (int u = 0; u < kActPieces; ++u) {
-    const int j = (threadIdx.x + 256 * u) / (kChunkK / 8);
-    tr.t[u] = j < np ? p0 + j : -1;
-    sc[u] = j < np ? ldexpf(1.f, -h_exponent(a.hmax[p0 + j])) : 1.f;
+    tr.t[u] = j < np ? (a.rowmap ? a.rowmap[p0 + j] : p0 + j) : -1;
   }
 }
 
 // Dynamic LDS of the chunk kernels: NMAT fp16 codebooks, then two buffers, each holding NMAT code
-// slabs and the 64 x kXStride activation tile.  Addressed through this one symbol with integer
-// offsets, so every access is known to be LDS (a pointer picked from an array would turn them into
-// flat accesses, which also count against the global-memory counter).
-extern __shared__ __attribute__((aligned(16))) uint8_t chunk_lds[];
-
+// slabs and the 64 x kXStride activation tile.
 template <int NMAT>
 struct ChunkLds {
   static constexpr int kBuf = NMAT * kSlabBytes + kChunkTok * kXStride * 2;
@@ -350,52 +296,70 @@ struct ChunkLds {
   __device__ static uint16_t* act(int b) {
     return reinterpret_cast<uint16_t*>(chunk_lds + NMAT * kCbBytes + b * kBuf + NMAT * kSlabBytes);
   }
+  // the same as LDS addresses
+  static constexpr uint32_t code_addr(int b) { return NMAT * kCbBytes + b * kBuf; }
+  static constexpr uint32_t act_addr(int b) { return NMAT * kCbBytes + b * kBuf + NMAT * kSlabBytes; }
 };
 
 // The K loop of one pass over NTB 16-pair blocks.  The body is straight-line code (no branch on the
 // pair count, and the next tile's loads are issued unconditionally: the last iteration re-reads the
 // last tile into the idle buffer), so the compiler's memory-counter waits stay exact and the
 // prefetch is never drained early.
-template <bool F16, int NMAT, int NTB, class Act>
+template <bool F16, int NMAT, int NTB>
 __device__ inline void k_loop(f32x4 (&acc)[NMAT][4], const uint8_t* const (&mats)[NMAT], int ntile, int nrb, int rb,
-                              const Act& act, const TokenRows& tr, const float (&sc)[kActPieces],
-                              StageRegs<F16, NMAT>& st) {
+                              const Act16& act, const TokenRows& tr, StageRegs<NMAT>& st) {
   typedef typename Decoder<F16>::frag_t frag_t;
   typedef ChunkLds<NMAT> L;
-  const _Float16* cb_lds = L::cb();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4;
   const int r = 16 * wave + (lane & 15);
+  // the lane's 12 code bytes (12q .. 12q+11 of row r's 48-byte run: groups 4q .. 4q+3) are three
+  // dwords of a staged slab (byte b of the run at (b/16)*1024 + 16r + b%16), and its B operand rows
+  // start at pair lane%16, columns 32q (of the group 4q + kk at step kk)
+  uint32_t coff[2][3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int b = 12 * q + 4 * i;
+    const uint32_t o = (uint32_t)((b >> 4) * 1024 + r * 16 + (b & 15));
+    coff[0][i] = L::code_addr(0) + o;
+    coff[1][i] = L::code_addr(1) + o;
+  }
+  const uint32_t bo = (uint32_t)(((lane & 15) * kXStride + 32 * q) * 2);
+  const uint32_t boff[2] = {L::act_addr(0) + bo, L::act_addr(1) + bo};
   for (int kt = 0; kt < ntile; ++kt) {
     const int cur = kt & 1;
     const int nxt = kt + 1 < ntile ? kt + 1 : kt;
-    stage_issue<F16, NMAT>(st, mats, nxt, nrb, rb, act, tr, nxt * kChunkK);
-    RowCodes rc[NMAT];
+    stage_issue<NMAT>(st, mats, nxt, nrb, rb, act, tr, nxt * kChunkK);
+    uint32_t d[NMAT][3];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) rc[m].load(L::code(cur) + m * kSlabBytes, r);
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int i = 0; i < 3; ++i) d[m][i] = lds_w((cur ? coff[1][i] : coff[0][i]) + m * kSlabBytes);
+    const uint32_t ba = cur ? boff[1] : boff[0];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       frag_t a[NMAT];
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) a[m] = Decoder<F16>::decode(cb_lds + m * (kCbBytes / 2), rc[m].group(kk, q));
+      for (int m = 0; m < NMAT; ++m)
+        a[m] = Decoder<F16>::decode((uint32_t)(m * kCbBytes), code_off(d[m], kk, 0), code_off(d[m], kk, 1),
+                                    code_off(d[m], kk, 2));
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
-        const frag_t b =
-            *reinterpret_cast<const frag_t*>(L::act(cur) + (tb * 16 + (lane & 15)) * kXStride + 32 * kk + 8 * q);
+        const half8 b = lds_h8(ba + (uint32_t)((tb * 16 * kXStride + 8 * kk) * 2));
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) acc[m][tb] = mfma16(a[m], b, acc[m][tb]);
       }
     }
-    stage_store<F16, NMAT>(st, L::code(cur ^ 1), L::act(cur ^ 1), act, sc);
+    stage_store<NMAT>(st, L::code(cur ^ 1), L::act(cur ^ 1));
     __syncthreads();
   }
 }
 
 // One workgroup = (expert, row blocks [rb0, rb1)): loads the codebooks once, then per 64-row block
 // loops over the expert's pairs 64 at a time and over K.
-template <bool F16, int NMAT, class Act, class Epi>
+template <bool F16, int NMAT, class Epi>
 __device__ void expert_tile_gemm(const uint8_t* const (&mats)[NMAT], const float* const (&cbs)[NMAT], int K,
-                                 int rb0, int rb1, int nrb, int p_begin, int n_pairs, const Act& act, const Epi& epi) {
+                                 int rb0, int rb1, int nrb, int p_begin, int n_pairs, const Act16& act, const Epi& epi) {
   typedef ChunkLds<NMAT> L;
   _Float16* cb_lds = L::cb();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -406,12 +370,11 @@ __device__ void expert_tile_gemm(const uint8_t* const (&mats)[NMAT], const float
   for (int pb = 0; pb < n_pairs; pb += kChunkTok) {
     const int np = n_pairs - pb < kChunkTok ? n_pairs - pb : kChunkTok;
     TokenRows tr;
-    float sc[kActPieces];
-    pass_rows(tr, sc, act, p_begin + pb, np);
-    StageRegs<F16, NMAT> st;
-    stage_issue<F16, NMAT>(st, mats, 0, nrb, rb, act, tr, 0);
+    pass_rows(tr, act, p_begin + pb, np);
+    StageRegs<NMAT> st;
+    stage_issue<NMAT>(st, mats, 0, nrb, rb, act, tr, 0);
     __syncthreads();  // the previous pass is done with both buffers (and the codebooks are stored)
-    stage_store<F16, NMAT>(st, L::code(0), L::act(0), act, sc);
+    stage_store<NMAT>(st, L::code(0), L::act(0));
     __syncthreads();
     f32x4 acc[NMAT][4];
 #pragma unroll
@@ -419,10 +382,10 @@ __device__ void expert_tile_gemm(const uint8_t* const (&mats)[NMAT], const float
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[m][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
     switch ((np + 15) / 16) {
-      case 1: k_loop<F16, NMAT, 1>(acc, mats, ntile, nrb, rb, act, tr, sc, st); break;
-      case 2: k_loop<F16, NMAT, 2>(acc, mats, ntile, nrb, rb, act, tr, sc, st); break;
-      case 3: k_loop<F16, NMAT, 3>(acc, mats, ntile, nrb, rb, act, tr, sc, st); break;
-      default: k_loop<F16, NMAT, 4>(acc, mats, ntile, nrb, rb, act, tr, sc, st); break;
+      case 1: k_loop<F16, NMAT, 1>(acc, mats, ntile, nrb, rb, act, tr, st); break;
+      case 2: k_loop<F16, NMAT, 2>(acc, mats, ntile, nrb, rb, act, tr, st); break;
+      case 3: k_loop<F16, NMAT, 3>(acc, mats, ntile, nrb, rb, act, tr, st); break;
+      default: k_loop<F16, NMAT, 4>(acc, mats, ntile, nrb, rb, act, tr, st); break;
     }
     epi(acc, p_begin + pb, np, rb * kChunkRows + 16 * wave + 4 * q, lane & 15);
   }
@@ -480,11 +443,20 @@ struct DownEpi {
   }
 };
 
+// An LDS layout other than the one the kernels address absolutely cannot happen (chunk_lds is their
+// only LDS); if it ever did, the kernel reports it instead of computing.
+__device__ inline bool chunk_lds_ok(int32_t* status) {
+  if (lds_at_zero()) return true;
+  if (threadIdx.x == 0) atomicExch(status, 8 /* RVQ_ERR_DEVICE_STALL: outputs invalid */);
+  return false;
+}
+
 template <bool F16>
-__global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint16_t* __restrict__ x16,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ pair_token, float* __restrict__ h,
-                                                      uint32_t* __restrict__ hmax, int rpw) {
+                                                      uint32_t* __restrict__ hmax, int rpw, int32_t* __restrict__ status) {
+  if (!chunk_lds_ok(status)) return;
   const int H = bank.H, I = bank.I;
   const int nrb = I / kChunkRows, ngrp = (nrb + rpw - 1) / rpw;
   const int w = xcd_major(bank.E * ngrp);
@@ -497,15 +469,16 @@ __global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint1
   const uint8_t* const mats[2] = {rec, rec + packed_bytes(I, H)};
   const float* const cbs[2] = {bank.cb + ((int64_t)e * 3 + 0) * kCodebookFloats,
                                bank.cb + ((int64_t)e * 3 + 1) * kCodebookFloats};
-  ActTokens act{x, pair_token, H};
+  const Act16 act{x16, pair_token, H};
   GateUpEpi<F16> epi{h, hmax, I};
   expert_tile_gemm<F16, 2>(mats, cbs, H, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
 }
 
 template <bool F16>
 __global__ __launch_bounds__(256) void k_chunk_down(BankArgs bank, const int32_t* __restrict__ offsets,
-                                                    const float* __restrict__ h, const uint32_t* __restrict__ hmax,
-                                                    float* __restrict__ y, int rpw) {
+                                                    const uint16_t* __restrict__ h16, const uint32_t* __restrict__ hmax,
+                                                    float* __restrict__ y, int rpw, int32_t* __restrict__ status) {
+  if (!chunk_lds_ok(status)) return;
   const int H = bank.H, I = bank.I;
   const int nrb = H / kChunkRows, ngrp = (nrb + rpw - 1) / rpw;
   const int w = xcd_major(bank.E * ngrp);
@@ -517,9 +490,42 @@ __global__ __launch_bounds__(256) void k_chunk_down(BankArgs bank, const int32_t
   const uint8_t* rec = bank.codes + (int64_t)e * bank.stride;
   const uint8_t* const mats[1] = {rec + 2 * packed_bytes(I, H)};
   const float* const cbs[1] = {bank.cb + ((int64_t)e * 3 + 2) * kCodebookFloats};
-  ActH act{h, hmax, I};
+  const Act16 act{h16, nullptr, I};
   DownEpi<F16> epi{y, hmax, H};
   expert_tile_gemm<F16, 1>(mats, cbs, I, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
+}
+
+// fp16 copy of the chunk's bf16 tokens, for fp16 tiles (exact for |x| inside the fp16 range): done
+// once here instead of in every workgroup that stages the tokens.  8 elements per thread.
+__global__ __launch_bounds__(256) void k_chunk_x16(const uint16_t* __restrict__ x, int64_t n8,
+                                                   uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(x + 8 * i);
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) w[r] = pack_h2(__uint_as_float(w[r] << 16), __uint_as_float(w[r] & 0xffff0000u));
+  *reinterpret_cast<u32x4*>(out + 8 * i) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// h as the down product's operand: fp16 tiles take fp16(h * 2^-e(p)), e(p) from the pair's max |h|
+// (so no entry overflows; the down epilogue multiplies by 2^e(p)); bf16 tiles take bf16(h).
+// 8 elements per thread (I is a multiple of 64, so a piece lies in one pair's row).
+template <bool F16>
+__global__ __launch_bounds__(256) void k_chunk_h16(const float* __restrict__ h, const uint32_t* __restrict__ hmax,
+                                                   int I, int64_t n8, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(h + 8 * i);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(h + 8 * i + 4);
+  u32x4 v;
+  if constexpr (F16) {
+    const float f = ldexpf(1.f, -h_exponent(hmax[(8 * i) / I]));
+    v = u32x4{pack_h2(a.x * f, a.y * f), pack_h2(a.z * f, a.w * f), pack_h2(b.x * f, b.y * f), pack_h2(b.z * f, b.w * f)};
+  } else {
+    v = u32x4{pack_b2(a.x, a.y), pack_b2(a.z, a.w), pack_b2(b.x, b.y), pack_b2(b.z, b.w)};
+  }
+  *reinterpret_cast<u32x4*>(out + 8 * i) = v;
 }
 
 // out[t][r] = residual[t][r] + sum_i gates[t][i] * y[pair_pos[t][i]][r]   (fixed order in i)
@@ -555,10 +561,16 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
   uint32_t* hmax = reinterpret_cast<uint32_t*>(base + w.hmax_off);
   float* h = reinterpret_cast<float*>(base + w.h_off);
   float* ybuf = reinterpret_cast<float*>(base + w.y_off);
+  uint16_t* x16 = reinterpret_cast<uint16_t*>(base + w.x16_off);
+  uint16_t* h16 = reinterpret_cast<uint16_t*>(base + w.h16_off);
   BankArgs bank{codes, cb, stride, E, H, I};
   const size_t bucket_smem = ((size_t)E * ((T + 31) / 32) + E + 1) * 4;
   hipLaunchKernelGGL(k_chunk_bucket, dim3(1), dim3(1024), bucket_smem, stream, ids, T, k, E, offsets, pair_token,
                      pair_pos, hmax, status);
+  // the gate/up operand: the tokens themselves (bf16 tiles) or their fp16 copy
+  const int64_t nx8 = (int64_t)T * H / 8;
+  if (f16) hipLaunchKernelGGL(k_chunk_x16, dim3((unsigned)cdiv(nx8, 256)), dim3(256), 0, stream, x, nx8, x16);
+  const uint16_t* xg = f16 ? x16 : x;
   // row blocks per workgroup: the codebooks are loaded once per workgroup
   const int rpw_gu = 2, rpw_dn = 4;
   const unsigned g_gu = (unsigned)(cdiv(E * cdiv(I / kChunkRows, rpw_gu), 8) * 8);
@@ -570,16 +582,19 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
     const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)chunk_smem(f16, 2));
     if (e != hipSuccess) return e;
   }
+  const int64_t nh8 = (int64_t)T * k * I / 8;
   if (f16) {
-    hipLaunchKernelGGL(k_chunk_gateup<true>, dim3(g_gu), dim3(256), chunk_smem(true, 2), stream, bank, x, offsets,
-                       pair_token, h, hmax, rpw_gu);
-    hipLaunchKernelGGL(k_chunk_down<true>, dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets, h, hmax,
-                       ybuf, rpw_dn);
+    hipLaunchKernelGGL(k_chunk_gateup<true>, dim3(g_gu), dim3(256), chunk_smem(true, 2), stream, bank, xg, offsets,
+                       pair_token, h, hmax, rpw_gu, status);
+    hipLaunchKernelGGL(k_chunk_h16<true>, dim3((unsigned)cdiv(nh8, 256)), dim3(256), 0, stream, h, hmax, I, nh8, h16);
+    hipLaunchKernelGGL(k_chunk_down<true>, dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets, h16,
+                       hmax, ybuf, rpw_dn, status);
   } else {
-    hipLaunchKernelGGL(k_chunk_gateup<false>, dim3(g_gu), dim3(256), chunk_smem(false, 2), stream, bank, x, offsets,
-                       pair_token, h, hmax, rpw_gu);
-    hipLaunchKernelGGL(k_chunk_down<false>, dim3(g_dn), dim3(256), chunk_smem(false, 1), stream, bank, offsets, h,
-                       hmax, ybuf, rpw_dn);
+    hipLaunchKernelGGL(k_chunk_gateup<false>, dim3(g_gu), dim3(256), chunk_smem(false, 2), stream, bank, xg, offsets,
+                       pair_token, h, hmax, rpw_gu, status);
+    hipLaunchKernelGGL(k_chunk_h16<false>, dim3((unsigned)cdiv(nh8, 256)), dim3(256), 0, stream, h, hmax, I, nh8, h16);
+    hipLaunchKernelGGL(k_chunk_down<false>, dim3(g_dn), dim3(256), chunk_smem(false, 1), stream, bank, offsets, h16,
+                       hmax, ybuf, rpw_dn, status);
   }
   hipLaunchKernelGGL(k_chunk_combine, dim3((unsigned)cdiv(H, 256), (unsigned)T), dim3(256), 0, stream, ybuf, pair_pos,
                      gates, k, H, residual, y);
