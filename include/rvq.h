@@ -207,7 +207,7 @@ int rvq_moe_layer_forward_timed(const rvq_expert_bank_t *bank, const void *x, in
  * rvq_router_topk (T = 1, x_dtype RVQ_F32) followed by rvq_moe_layer_forward
  * (T = 1) on the selected experts, with the same results as calling the two.
  * Where the gate/up kernel can (fp32 tables, the shapes its wave-specialised
- * form takes, num_experts <= 1024), each of its workgroups takes the top-k
+ * form takes, num_experts <= 768), each of its workgroups takes the top-k
  * itself instead of a separate selection kernel.
  * w_router: bf16 [E][H]; x: fp32 [H]; residual: fp32 [H] or NULL; y: fp32
  * [H] (may alias residual); ids: int32 [k], gates: fp32 [k], logits: fp64

@@ -412,8 +412,8 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   if (threadIdx.x == 0) logits[(int64_t)t * E + e] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// Top-k by (logit desc, id asc), by one workgroup; every thread calls it.  A full ranking compares
-// all E^2 pairs in fp64; here it runs in two passes:
+// Top-k by (logit desc, id asc), by one workgroup; every thread calls it.  With a thread per expert
+// it is topk_rank below; with more experts than threads it runs in two passes:
 //  (a) g[e] = #{j in e's 64-expert block : L[j] > L[e]} (strict, one compare per pair, E * 64 pairs);
 //  (b) the candidates are the experts with g < k.  Every expert of global rank < k is one (its
 //      count within the block is at most its rank), and every expert ahead of such an expert has
@@ -425,33 +425,168 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 // by LDS latency, not by the compares).  The partial counts are integers added with LDS atomics:
 // exact in any order.  Candidates take list slots in atomic order, which changes nothing, as (c)
 // orders them by logit and id alone.
-// On entry (see topk_prepare): L holds the E logits and -inf up to E rounded to 64; g and crank are
-// zero; cl and cid hold -inf and INT_MAX (the padding that (c) compares against); *ncand is zero.
+// On entry (see topk_prepare): L holds the E logits and -inf up to E rounded to 64 (Ep); g and
+// crank are zero; cl and cid hold -inf and INT_MAX (the padding that (c) compares against); ncand[0]
+// and ncand[1] are zero.  With Ep <= blockDim also: key, the keys below (0 for padding); ckey zero;
+// skey[s] = key[s Ep / 64] (s < 64, a sample); hist zero.
 struct TopkScratch {
-  int* g;
-  int* crank;
-  int* cid;
-  double* cl;
-  int* ncand;
+  int* g;            // [Ep]
+  int* crank;        // [Ep]
+  int* cid;          // [Ep]
+  double* cl;        // [Ep]
+  int* ncand;        // [2]
+  uint32_t* key;     // [Ep], 16-byte aligned (one-pass form only, as the rest of this list)
+  uint32_t* ckey;    // [Ep], 16-byte aligned
+  uint32_t* skey;    // [64], 16-byte aligned
+  int* hist;         // [kMaxTopK]
 };
 constexpr int kTopkChunk = 16;
 __device__ __forceinline__ int topk_pad(int E) { return (E + 63) & ~63; }
+
+// Order-preserving 32-bit image of a logit rounded to fp32, -0 taken as +0 (x + 0.0 is +0 for
+// x = -0 and x otherwise): rounding to nearest is monotone, so key(a) > key(b) implies a > b and
+// key(a) < key(b) implies a < b; equal keys decide nothing.  Finite and infinite logits map above 0,
+// the key of the padding.
+__device__ __forceinline__ uint32_t topk_key(double l) {
+  const uint32_t b = __float_as_uint((float)(l + 0.0));
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
 
 // Writes the state topk_select expects; src(e) gives logit e.  Every thread calls it; a barrier
 // must follow.
 template <typename Src>
 __device__ void topk_prepare(double* L, int E, const TopkScratch& ts, Src src) {
-  if (threadIdx.x == 0) *ts.ncand = 0;
-  for (int e = threadIdx.x; e < topk_pad(E); e += blockDim.x) {
-    L[e] = e < E ? src(e) : -INFINITY;
+  const int Ep = topk_pad(E);
+  const bool one = Ep <= (int)blockDim.x;
+  if (threadIdx.x < 2) ts.ncand[threadIdx.x] = 0;
+  if (one && threadIdx.x < kMaxTopK) ts.hist[threadIdx.x] = 0;
+  const int S = Ep >> 6;   // sample stride
+  for (int e = threadIdx.x; e < Ep; e += blockDim.x) {
+    const double l = e < E ? src(e) : -INFINITY;
+    L[e] = l;
     ts.g[e] = 0;
     ts.crank[e] = 0;
     ts.cid[e] = INT_MAX;
     ts.cl[e] = -INFINITY;
+    if (one) {
+      const uint32_t key = e < E ? topk_key(l) : 0u;
+      ts.key[e] = key;
+      ts.ckey[e] = 0u;
+      if (e % S == 0) ts.skey[e / S] = key;
+    }
+  }
+}
+
+// Experts with a thread each (Ep <= blockDim, blockDim >= 256).  The rank of e is
+// #{j : L[j] > L[e], or L[j] = L[e] and j < e}; ranks are counted on the keys (above), and the
+// fp64 logits and ids decide only between equal keys.
+//  (1) tau = the k-th largest key of the sample skey (each sample key's count of greater sample
+//      keys, then the smallest key among the samples with fewer than k above them).  At least k
+//      keys are >= tau, so every expert of rank < k has a key >= tau.
+//  (2) the candidates are the experts with key >= tau (about k E / 64 of them for unordered
+//      logits; all E at worst), compacted in atomic order, which nothing below depends on.
+//  (3) each candidate's count of greater candidate keys: every key above a candidate's belongs to
+//      a candidate, so this is its count of greater keys overall, its rank unless another key
+//      equals its own.  Thread (i, p) counts part p of the candidates (16 keys per step, the same
+//      for the whole wave, so every read is a broadcast); the parts add with LDS atomics, exact.
+//  (4) candidates with count c < k claim sel[c] and count themselves at c; equal keys share one c,
+//      so a second claimant flags a tie, and then each claimant of such a c (rare) adds the
+//      candidates of its key that come first by fp64 logit, then id, and claims that slot instead.
+//      A candidate with c >= k has rank >= k either way.
+__device__ void topk_rank(const double* L, int E, int k, const TopkScratch& ts, int* sel) {
+  const int Ep = topk_pad(E);
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  if (wave < 4) {   // (1): wave w compares every sample key with sample keys 16 w .. 16 w + 15
+    const uint32_t ks = ts.skey[lane];
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(ts.skey + 16 * wave + 4 * u);
+      c += (int)(kv.x > ks) + (int)(kv.y > ks) + (int)(kv.z > ks) + (int)(kv.w > ks);
+    }
+    atomicAdd(&ts.g[lane], c);
+  }
+  __syncthreads();
+  uint32_t tau = ts.g[lane] < k ? ts.skey[lane] : 0xffffffffu;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)tau, off, 64);
+    tau = o < tau ? o : tau;
+  }
+  if (t < Ep) {   // (2): whole waves (Ep is a multiple of 64)
+    const uint32_t ke = ts.key[t];
+    const bool cand = t < E && ke >= tau;
+    const uint64_t m = __ballot(cand);
+    int base = 0;
+    if (lane == 0 && m) base = atomicAdd(ts.ncand, __popcll(m));
+    base = __shfl(base, 0, 64);
+    if (cand) {
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      ts.cid[pos] = t;
+      ts.ckey[pos] = ke;
+      ts.cl[pos] = L[t];
+    }
+  }
+  __syncthreads();
+  const int C = __builtin_amdgcn_readfirstlane(*ts.ncand);
+  const int Cp = (C + 63) & ~63;   // <= Ep <= blockDim; ckey is zero from C on
+  const int np = __builtin_amdgcn_readfirstlane((int)blockDim.x / Cp);
+  const int p = __builtin_amdgcn_readfirstlane(t / Cp);   // the same for a wave
+  const int i = t - p * Cp;
+  if (p < np && i < C) {   // (3)
+    const int span = __builtin_amdgcn_readfirstlane(((Cp + np - 1) / np + 15) & ~15);
+    const int j0 = p * span, j1 = j0 + span < Cp ? j0 + span : Cp;
+    const uint32_t ki = ts.ckey[i];
+    int c = 0;
+    for (int j = j0; j < j1; j += 16) {
+      u32x4 kv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kv[u] = *reinterpret_cast<const u32x4*>(ts.ckey + j + 4 * u);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        c += (int)(kv[u].x > ki) + (int)(kv[u].y > ki) + (int)(kv[u].z > ki) + (int)(kv[u].w > ki);
+    }
+    if (np == 1) ts.crank[i] = c;
+    else atomicAdd(&ts.crank[i], c);
+  }
+  __syncthreads();
+  for (int c = t; c < C; c += blockDim.x) {   // (4)
+    const int r = ts.crank[c];
+    if (r < k) {
+      sel[r] = ts.cid[c];
+      if (atomicAdd(&ts.hist[r], 1) > 0) ts.ncand[1] = 1;
+    }
+  }
+  __syncthreads();
+  if (ts.ncand[1]) {   // the same for every thread
+    for (int c = t; c < C; c += blockDim.x) {
+      const int r0 = ts.crank[c];
+      if (r0 < k && ts.hist[r0] > 1) {
+        const uint32_t kc = ts.ckey[c];
+        const double lc = ts.cl[c];
+        const int ic = ts.cid[c];
+        int r = r0;
+        for (int j0 = 0; j0 < Cp; j0 += 4) {   // keys 4 at a time; logits and ids only on a match
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(ts.ckey + j0);
+          const uint32_t kk[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int j = j0 + u;
+            if (kk[u] == kc && j != c) r += (ts.cl[j] > lc) || (ts.cl[j] == lc && ts.cid[j] < ic);
+          }
+        }
+        if (r < k) sel[r] = ic;
+      }
+    }
   }
 }
 
 __device__ void topk_select(const double* L, int E, int k, const TopkScratch& ts, int* sel) {
+  if (topk_pad(E) <= (int)blockDim.x) {
+    topk_rank(L, E, k, ts, sel);
+    return;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
   constexpr int Q = 64 / kTopkChunk;
@@ -530,10 +665,12 @@ __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ logits
                                                int32_t* __restrict__ ids, float* __restrict__ gates) {
   __shared__ double L[kMaxExperts], cl[kMaxExperts];
   __shared__ int g[kMaxExperts], crank[kMaxExperts], cid[kMaxExperts];
-  __shared__ int sel[kMaxTopK], ncand;
+  // the one-pass form's arrays (Ep <= the 1024 threads)
+  __shared__ __attribute__((aligned(16))) uint32_t key[1024], ckey[1024], skey[64];
+  __shared__ int sel[kMaxTopK], hist[kMaxTopK], ncand[2];
   const int t = blockIdx.x;
   if (threadIdx.x < kMaxTopK) sel[threadIdx.x] = 0;
-  const TopkScratch ts{g, crank, cid, cl, &ncand};
+  const TopkScratch ts{g, crank, cid, cl, ncand, key, ckey, skey, hist};
   topk_prepare(L, E, ts, [&](int e) { return logits[(int64_t)t * E + e]; });
   __syncthreads();
   topk_select(L, E, k, ts, sel);
@@ -845,7 +982,7 @@ struct PipeArgs {
   int k;
   int gu_stride;          // down: partials stored per (slot, matrix) in part_gu (>= ngu)
 };
-constexpr int kRouteMaxExperts = 1024;
+constexpr int kRouteMaxExperts = 64 * (kGuStreamWaves + kPipeBuildWaves);   // a thread per expert
 
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
@@ -868,7 +1005,8 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
   __shared__ int cmax_bits;            // fp16: max squared codebook-entry norm (bits of a float >= 0)
   __shared__ float escale[ITEMS];      // fp16: 2^e_k of each item
   __shared__ int rsel[kMaxTopK];
-  static_assert(DOWN || sizeof(lut) >= 28 * kRouteMaxExperts + 4, "top-k scratch must fit in the table buffers");
+  static_assert(DOWN || sizeof(lut) >= 36 * kRouteMaxExperts + 512 + 4 * kMaxTopK, "top-k scratch must fit in the table buffers");
+  static_assert(DOWN || 64 * (NSW + kPipeBuildWaves) >= kRouteMaxExperts, "the top-k takes a thread per expert");
   const int H = bank.H, I = bank.I;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -891,9 +1029,14 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
   }
   const bool streamer = wave < NSW;
   const int bw = wave - NSW;
+  // The loads of the prologue are issued in the order their results are needed: the expert id (or
+  // this thread's router logit), then the operands that do not depend on the expert.  A wait for a
+  // vector load also waits for every vector load issued before it.
+  const bool route = !DOWN && pa.logits;
+  const int e_given = route ? 0 : ids[slot];
+  const double logit = route && (int)threadIdx.x < bank.E ? pa.logits[threadIdx.x] : 0.0;
   // down: builder wave bw computes h for items bw, bw + 4, ... (ITEMS <= 8, so at most two): lane l
-  // takes entries l and 64 + l of the item's 128.  The gate/up partials depend on the slot only,
-  // so they are requested first, before the expert id is known.
+  // takes entries l and 64 + l of the item's 128.  The gate/up partials depend on the slot only.
   constexpr int HI = DOWN ? (ITEMS + kPipeBuildWaves - 1) / kPipeBuildWaves : 1;
   constexpr int GU = DOWN ? kPipeMaxGu : 1;
   float gv[HI][2][GU], uv[HI][2][GU];
@@ -918,20 +1061,34 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
       }
     }
   }
+  // gate/up builders: this item range's x sub-vectors do not depend on the expert, so they are
+  // requested first, ahead of the top-k
+  f32x2 xb[DOWN ? 1 : ITEMS];
+  const int q = lane >> 4, i16 = lane & 15;
+  if constexpr (!DOWN) {
+    if (!streamer) {
+      const float* xt = pa.x + (int64_t)(slot / pa.k) * H;   // slot = token * k + i when batched
+#pragma unroll
+      for (int k = 0; k < ITEMS; ++k)
+        xb[k] = *reinterpret_cast<const f32x2*>(xt + (int64_t)(t0 + k) * 128 + i16 * 8 + 2 * q);
+    }
+  }
   int e;
-  if (!DOWN && pa.logits) {
+  if (route) {
     // top-k of the router logits, the same computation as k_topk.  Its scratch lies in the table
     // buffers, which nothing writes before the start barrier below; every read of it comes first.
     const int E = bank.E;
     char* scr = reinterpret_cast<char*>(&lut[0][0]);
     double* rl = reinterpret_cast<double*>(scr);
-    const TopkScratch ts{reinterpret_cast<int*>(scr + 16 * kRouteMaxExperts),
-                         reinterpret_cast<int*>(scr + 20 * kRouteMaxExperts),
-                         reinterpret_cast<int*>(scr + 24 * kRouteMaxExperts),
-                         reinterpret_cast<double*>(scr + 8 * kRouteMaxExperts),
-                         reinterpret_cast<int*>(scr + 28 * kRouteMaxExperts)};
+    constexpr int R = kRouteMaxExperts;   // a multiple of 64: every array below is 16-byte aligned
+    const TopkScratch ts{reinterpret_cast<int*>(scr + 16 * R), reinterpret_cast<int*>(scr + 20 * R),
+                         reinterpret_cast<int*>(scr + 24 * R), reinterpret_cast<double*>(scr + 8 * R),
+                         reinterpret_cast<int*>(scr + 36 * R + 256), reinterpret_cast<uint32_t*>(scr + 28 * R),
+                         reinterpret_cast<uint32_t*>(scr + 32 * R), reinterpret_cast<uint32_t*>(scr + 36 * R),
+                         reinterpret_cast<int*>(scr + 36 * R + 512)};
     if (threadIdx.x < kMaxTopK) rsel[threadIdx.x] = 0;
-    topk_prepare(rl, E, ts, [&](int j) { return pa.logits[j]; });
+    // a thread per expert (E <= kRouteMaxExperts = the workgroup size): logit j is thread j's
+    topk_prepare(rl, E, ts, [&](int) { return logit; });
     __syncthreads();
     topk_select(rl, E, pa.k, ts, rsel);
     __syncthreads();
@@ -939,7 +1096,7 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
     if (m == 0 && t0 == 0 && wave == 0)
       topk_gates(rl, rsel, pa.k, pa.ids_out, pa.gates_out, [&](int i) { return i == slot; });
   } else {
-    e = ids[slot];
+    e = e_given;
   }
   const bool bad = e < 0 || e >= bank.E;
   if constexpr (DOWN) {
@@ -951,20 +1108,13 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
   const int nrb = (int)cdiv(rows, kSlabRows);
   const int64_t tile_bytes = (int64_t)nrb * kSlabBytes;
 
-  // builder operands, requested before the start barrier (ahead of the code stream)
-  const int q = lane >> 4, i16 = lane & 15;
+  // the codebook operands of the builders, requested before the start barrier (ahead of the code
+  // stream)
   f32x2 a[TPW];
-  f32x2 xb[DOWN ? 1 : ITEMS];
   if (!streamer) {
     const float* cb = bank.cb + ((int64_t)e * 3 + m) * kCodebookFloats;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) a[t] = *reinterpret_cast<const f32x2*>(cb + ((bw * TPW + t) * 16 + i16) * 8 + 2 * q);
-    if constexpr (!DOWN) {
-      const float* xt = pa.x + (int64_t)(slot / pa.k) * H;   // slot = token * k + i when batched
-#pragma unroll
-      for (int k = 0; k < ITEMS; ++k)
-        xb[k] = *reinterpret_cast<const f32x2*>(xt + (int64_t)(t0 + k) * 128 + i16 * 8 + 2 * q);
-    }
   } else if (threadIdx.x == 0) {
     built[0] = 0;
     built[1] = 0;
@@ -1021,6 +1171,16 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
     // ----------------------------------------------------------------- builders
     bool ok = true;
     float cmax2 = 0.f;
+    if constexpr (DOWN) {
+      // opaque copies: without them the compiler starts these sums before the expert id's load, and
+      // the id, with it the whole prologue, waits for the partials
+#pragma unroll
+      for (int n = 0; n < HI; ++n)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int p = 0; p < GU; ++p) asm volatile("" : "+v"(gv[n][hh][p]), "+v"(uv[n][hh][p]));
+    }
     if constexpr (F16) {
       // squared norm of codebook entry i16 of each table tile: the 4 lanes q hold 2 dims each
       float v = 0.f;

@@ -375,6 +375,70 @@ def test_topk_ties_across_blocks(layer_bank):
     assert rvq.check_device_status(ws) == 0
 
 
+def near_tie_router(bits0, x, h0, gaps):
+    """Router rows, copies of the top row of bits0 on x, raised by gaps[i] bf16 ulps at element h0
+    (positive there), at ids 10, 100, 200, ...: their logits differ by a few ulps of w[h0] times x[h0]."""
+    lo = oracle.router_logits(bits0, x[None, :])[0]
+    top = int(np.argmax(lo))
+    bits = bits0.copy()
+    ids = [j for j in (10, 100, 200, 250) if j != top][:len(gaps)]
+    for j, d in zip(ids, gaps):
+        bits[j] = bits[top]
+        bits[j, h0] = bits[top, h0] + d
+    return bits, ids, top
+
+
+def test_topk_orders_logits_equal_in_fp32_by_fp64(layer_bank):
+    """Logits that round to the same fp32 value but differ in fp64 keep their fp64 order, not their
+    id order: the selection compares 32-bit keys of the fp32-rounded logits first and must decide
+    equal keys in fp64 (then by id).  Copies of the top router row at three ids, the later ones
+    raised at one element by 1 and 2 bf16 ulps times a small x there, so the larger logits sit at the
+    larger ids; rvq_router_topk (one-pass ranks for E = 256, two passes for
+    E = 4096) and the routed decode's in-kernel top-k must give the oracle's order."""
+    say("top-k: logits equal in fp32, distinct in fp64")
+    bank, bits0, _ = layer_bank
+    x = synth.activation_f32(synth.SEED_LAYER, 43, HIDDEN)
+    lo0 = oracle.router_logits(bits0, x[None, :])[0]
+    top = int(np.argmax(lo0))
+    row = (bits0[top].astype(np.uint32) << 16).view(np.float32)
+    h0 = int(np.flatnonzero((row > 0) & (np.abs(x) > 0))[-1])
+    found = ids_t = None
+    for scale in 2.0 ** -np.arange(8, 40):
+        xs = x.copy()
+        xs[h0] = np.float32(scale)
+        bits, ids_t, _ = near_tie_router(bits0, xs, h0, [0, 1, 2])
+        lo = oracle.router_logits(bits, xs[None, :])[0]
+        l = lo[ids_t]
+        if l[0] < l[1] < l[2] and len(set(np.float32(l).tolist())) == 1 and np.float32(l[0]) == np.float32(lo[top]):
+            found = (xs, bits, lo, ids_t)
+            break
+    assert found is not None
+    xs, bits, lo, ids_t = found
+    xd = to_dev(xs)
+    w = to_dev(bits.view(np.int16)).view(torch.bfloat16)
+    for k in (1, 2, 4, 16):
+        ids, gates, logits = rvq.router_topk(w, xd, k)
+        ids_o, gates_o, _ = oracle.topk(lo, k)
+        assert np.array_equal(ids[0].cpu().numpy(), ids_o), (k, ids[0].cpu().numpy(), ids_o)
+        np.testing.assert_allclose(gates[0].cpu().numpy(), gates_o, rtol=1e-6)
+    assert list(oracle.topk(lo, 2)[0]) == ids_t[:0:-1]   # the larger logits at the larger ids come first
+    ws = rvq.make_moe_workspace(bank, 1, TOP_K, "f32")
+    y, ids_r, gates_r, _ = rvq.moe_decode_routed(bank, w, xd, TOP_K, dtype="f32", workspace=ws)
+    ids_o, gates_o, _ = oracle.topk(lo, TOP_K)
+    assert np.array_equal(ids_r.cpu().numpy(), ids_o)
+    np.testing.assert_allclose(gates_r.cpu().numpy(), gates_o, rtol=1e-6)
+    assert rvq.check_device_status(ws) == 0
+    # 4096 experts (the two-pass form): the same 256 rows repeated, near-ties at the top of each copy
+    big = np.concatenate([bits] * 16)
+    wb = to_dev(big.view(np.int16)).view(torch.bfloat16)
+    lb = oracle.router_logits(big, xs[None, :])[0]
+    for k in (3, 16, 64):
+        ids, gates, _ = rvq.router_topk(wb, xd, k)
+        ids_o, gates_o, _ = oracle.topk(lb, k)
+        assert np.array_equal(ids[0].cpu().numpy(), ids_o), k
+        np.testing.assert_allclose(gates[0].cpu().numpy(), gates_o, rtol=1e-6)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_routed_decode_matches_two_calls_and_oracle(layer_bank, dtype):
     """rvq_moe_decode_routed (top-k taken inside the gate/up kernel for fp32 tables, by the selection
