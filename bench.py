@@ -340,6 +340,18 @@ def run_small_batch(torch, rvq, bank, w, xt, sizes=(1, 2, 4, 8, 16, 32, 64), rep
             del ws
         else:
             res["chunk_f16_tokens_per_s"].append(None)
+    # one expert per token, 256 tokens: the table path's batched form with the most pairs per expert
+    # slot count and down's row split chosen from all pairs
+    xb = xt[:256].contiguous()
+    ids1, gates1, _ = rvq.router_topk(w, xb, 1)
+    y1 = torch.empty(256, H, dtype=torch.float32, device=dev)
+    ws = rvq.make_batch_workspace(bank, 256, 1, "f32")
+    res["k1_T256_lut_f32_tokens_per_s"] = rate(
+        lambda: rvq.moe_batch_decode(bank, xb.float(), ids1, gates1, dtype="f32", y=y1, workspace=ws), 256)
+    status = rvq.check_device_status(ws)
+    if status:
+        raise RuntimeError(rvq.status_string(status))
+    del ws
     best_lut = [max(a, b) for a, b in zip(res["lut_f32_tokens_per_s"], res["lut_f16_tokens_per_s"])]
     cross = [T for T, c, l in zip(sizes, res["chunk_f16_tokens_per_s"], best_lut) if c is not None and c > l]
     res["chunk_faster_from_T"] = cross[0] if cross else None

@@ -1476,8 +1476,9 @@ __global__ __launch_bounds__(256) void k_sum_gu_partials(float* __restrict__ par
 }
 
 // T tokens of decode (T = 1 for the single-token entry points).  Pair p = t k + i (token t's i-th
-// expert) is one "slot" of the kernels, which read x, residual and y at row p / k; the chunk sizes
-// are chosen from one token's counts, so every pair is computed exactly as in a single-token call.
+// expert) is one "slot" of the kernels, which read x, residual and y at row p / k; the K-tile chunk
+// sizes are chosen from one token's counts, so every pair sums the same K-tiles in the same order as
+// in a single-token call (down's row split may differ with the pair count; it changes no sum).
 // Shapes without both wave-specialised forms run the tokens one after another.
 // status_hdr: where the status and wait-limit words are (the workspace header when null).
 static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
@@ -1519,10 +1520,10 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
                         ? pick_chunk(nt16_in, 2L * k)
                         : 0;
   const int ngu = chunk ? nt16_in / chunk : w.nt_in;
-  // down: row chunks of kDnBpi row blocks per streamer wave, or of one when few slots would leave
+  // down: row chunks of kDnBpi row blocks per streamer wave, or of one when few pairs would leave
   // CUs idle (only with 1 or 2 K-tiles per workgroup).  Only the rows a workgroup takes change, never
-  // the K-tiles it sums, so every result is the same either way.  The work estimate is rounds x
-  // K-tiles x row blocks per wave; ties keep kDnBpi.
+  // the K-tiles it sums, so every result is the same either way, and the choice is made from all P
+  // pairs of the call.  The work estimate is rounds x K-tiles x row blocks per wave; ties keep kDnBpi.
   const int nrb_h = (int)cdiv(H, kSlabRows);
   int dn_bpi = kDnBpi;
   int nrc = nrb_h / (kDnStreamWaves * kDnBpi);
@@ -1532,10 +1533,10 @@ static hipError_t decode_tokens(const uint8_t* codes, const float* cb, int64_t s
   const int dchunk = (chunk && I % 128 == 0 && nrb_h % (kDnStreamWaves * kDnBpi) == 0)
                    ? pick_chunk(nt16_out, (long)k * nrc)
                    : 0;
-  if (dchunk && dchunk <= 2 && ncu > 0) {   // one token's counts only (see above)
+  if (dchunk && dchunk <= 2 && ncu > 0) {
     const int nrc1 = nrb_h / kDnStreamWaves;
     auto cost = [&](int rows_per_wave, int chunks) {
-      const long grid = (long)k * chunks * (nt16_out / dchunk);
+      const long grid = (long)P * chunks * (nt16_out / dchunk);
       return (grid + ncu - 1) / ncu * dchunk * rows_per_wave;
     };
     if (cost(1, nrc1) < cost(kDnBpi, nrc)) dn_bpi = 1, nrc = nrc1;

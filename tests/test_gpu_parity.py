@@ -532,22 +532,25 @@ def test_batch_decode_equals_single_token_calls(layer_bank, dtype):
     assert rvq.check_device_status(ws) == 0
 
 
-@pytest.mark.parametrize("k,T", [(1, 6), (2, 4)])
+@pytest.mark.parametrize("k,T", [(1, 6), (2, 4), (1, 48)])
 def test_batch_decode_few_experts_per_token(layer_bank, k, T):
     """k = 1 and k = 2 on the 256-expert layer: few pairs per token, so gate/up leaves more partial
     sums per row than the down kernel reads (the partial-sum kernel runs) and the down kernel may take
-    one row block per streamer wave.  Every row against the oracle, and bit-equal to single-token
-    calls."""
+    one row block per streamer wave.  With 48 one-expert tokens the batch has pairs enough for down's
+    four-block row split while a single-token call takes one row block per wave: the rows differ, the
+    sums must not.  Rows against the oracle (all of them, or 6 of the 48), and every row bit-equal to
+    single-token calls."""
     bank, bits, w = layer_bank
     X = np.stack([synth.activation_f32(synth.SEED_LAYER, 4000 + 10 * k + t, HIDDEN) for t in range(T)])
     xd = to_dev(X)
     ids, gates, _ = rvq.router_topk(w, xd, k)
     get = _layer_oracle_getter()
+    rows = range(T) if T <= 8 else (0, 1, 17, 30, 46, 47)
     for dtype in ("f32", "f16"):
         say(f"batch decode T={T} k={k} {dtype}")
         y = rvq.moe_batch_decode(bank, xd, ids, gates, dtype=dtype)
         _rows_match_oracle(get, bits, X, None, y.cpu().numpy(), ids.cpu().numpy(), gates.cpu().numpy(),
-                           range(T), k, dtype)
+                           rows, k, dtype)
         for t in range(T):
             assert torch.equal(y[t], rvq.moe_layer_forward(bank, xd[t], ids[t], gates[t], dtype=dtype)), t
 

@@ -15,6 +15,9 @@ Pinned functions and what pins them:
                      zero input, k=1 mixing
   router / topk    : numpy matmul on widened bf16, lexsort order, scipy softmax
                      (k = E), gate = 1 at k = 1, exact ties -> lower id
+  moe_layer /      : k = 1 is the one expert, identical experts give that expert (gates sum to 1),
+  moe_mix            the residual added once, and each expert weighed by its own gate (experts
+                     with disjoint output coordinates against scipy's softmax of the kept logits)
   rmsnorm          : torch rms_norm, closed-form RMS of the output
   gemv_batch /     : T tokens at once equal T one-token calls bit for bit (each token's
   expert_batch       sums are independent of the others)
@@ -317,6 +320,42 @@ def test_moe_layer_k1_and_duplicate_experts():
     yr, _, _, _ = oracle.moe_layer(lambda e: experts[e], bits, x, 3, residual=r)
     y3, _, _, _ = oracle.moe_layer(lambda e: experts[e], bits, x, 3)
     np.testing.assert_allclose(yr - r, y3, rtol=1e-13, atol=1e-12)
+
+
+def test_moe_layer_weighs_each_expert_by_its_own_gate():
+    """Experts whose outputs live on disjoint coordinates: expert e's down matrix has one nonzero
+    row, row e (every other row's codes select all-zero entries), so coordinate e of the layer's
+    output is gate(e) * expert_e(x)[e] for a selected e and 0 otherwise.  The gates come from scipy's
+    softmax over the kept logits and the selection from numpy's lexsort of the logits, so a gate
+    applied to another rank's expert, a dropped or repeated expert, or a wrong normalisation fails."""
+    H, I, E, k = 64, 32, 12, 5
+    bits = synth.router_bf16_bits(13, 0, E, H)
+    x = synth.activation_f32(13, 0, H).astype(np.float64)
+    experts = {}
+    for e in range(E):
+        ex = _small_expert(13, e, H, I)
+        dc, dcb = ex["down"]
+        dc = np.array(dc, dtype=np.uint8).reshape(H, I // 8, 3)
+        dcb = np.array(dcb, dtype=np.float32).reshape(3, 256, 8)
+        dcb[:, 0, :] = 0.0                                  # entry 0 of every stage is the zero vector
+        keep = dc[e].copy()
+        dc[:] = 0
+        dc[e] = np.where(keep == 0, 1, keep)                # row e: nonzero entries only
+        ex["down"] = (dc, dcb)
+        experts[e] = ex
+    y, ids, gates, _ = oracle.moe_layer(lambda e: experts[e], bits, x, k)
+    L = oracle.router_logits(bits, x[None, :])[0]
+    order = np.lexsort((np.arange(E), -L))[:k]
+    assert np.array_equal(np.sort(ids), np.sort(order))
+    g = scipy.special.softmax(L[order])
+    for e in range(E):
+        own = oracle.expert(experts[e], x)
+        assert np.count_nonzero(own) == 1 and own[e] != 0.0
+        if e in order:
+            want = g[list(order).index(e)] * own[e]
+            assert abs(y[e] - want) <= 1e-13 * abs(want), (e, y[e], want)
+        else:
+            assert y[e] == 0.0
 
 
 def test_gemv_and_expert_batch_equal_single_token_calls():
