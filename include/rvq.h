@@ -36,6 +36,10 @@
  *    error other than RVQ_ERR_HIP has enqueued nothing.
  *  - Descriptor structs are read during the call only.
  *  - Sizes are element counts unless named *_bytes.
+ *  - Every sum is taken in a fixed order, so results repeat bit for bit on a
+ *    given device.  How the table kernels split K into partial sums is chosen
+ *    from the device's compute-unit count (to fill it), so a device with
+ *    another count may round differently, within the stated tolerances.
  */
 #ifndef RVQ_H_
 #define RVQ_H_

@@ -893,10 +893,11 @@ __device__ __forceinline__ void k_moe_gateup_body(BankArgs bank, const float* __
 // blocks.  The streamer waves stream those rows' codes through each K-tile's tables in turn and keep
 // one running sum per row, so the workgroup writes one partial row vector.  The builder waves build
 // the next K-tile's tables into the other half of a double buffer while the streamers gather.
-//   gate/up (DOWN = false): workgroup b -> gm = b / nchunk (slot * 2 + matrix), K-tiles
+//   gate/up (DOWN = false): work item b -> gm = b / nchunk (slot * 2 + matrix), K-tiles
 //            ITEMS (b % nchunk) + [0, ITEMS), all 32 row blocks; partial row vector b of part_gu.
-//   down    (DOWN = true):  workgroup b -> slot, row chunk rc, K-tile chunk kc (kc fastest); its
+//   down    (DOWN = true):  work item b -> slot, row chunk rc, K-tile chunk kc (kc fastest); its
 //            x operand is h = silu(g) * u, where g and u sum the `ngu` gate and up partials.
+// (Work items are dealt to workgroups XCD by XCD; see the geometry below.)
 // The roles exchange LDS counters with workgroup-scope release/acquire instead of barriers:
 //   built[k%2] += 1 per builder wave when its share of item k's tables is written;
 //                 streamers start item k at built[k%2] >= 4 (floor(k/2) + 1);
@@ -1011,20 +1012,25 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wait_limit = wait_polls(status);   // status points at the workspace header
-  // geometry of this workgroup
+  // geometry of this workgroup.  Work item wi: the hardware deals workgroups to the 8 XCDs in turn,
+  // so consecutive items are given to workgroups on one XCD (when the grid is a multiple of 8): the
+  // workgroups of one slot and matrix then share an L2, which fetches their codebook (and, for
+  // down, their gate/up partial sums) once.  Only where items run changes, never what they compute.
+  const int nwg = (int)gridDim.x;
+  const int wi = (nwg & 7) == 0 ? (int)(blockIdx.x & 7) * (nwg >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
   int slot, m, t0, rb0;
   if constexpr (DOWN) {
-    const int kc = blockIdx.x % pa.nchunk;
-    const int rc = (blockIdx.x / pa.nchunk) % pa.nrc;
-    slot = blockIdx.x / (pa.nchunk * pa.nrc);
+    const int kc = wi % pa.nchunk;
+    const int rc = (wi / pa.nchunk) % pa.nrc;
+    slot = wi / (pa.nchunk * pa.nrc);
     m = 2;
     t0 = kc * ITEMS;
     rb0 = rc * NSW * BPI;
   } else {
-    const int gm = blockIdx.x / pa.nchunk;
+    const int gm = wi / pa.nchunk;
     slot = gm >> 1;
     m = gm & 1;
-    t0 = (blockIdx.x - gm * pa.nchunk) * ITEMS;
+    t0 = (wi - gm * pa.nchunk) * ITEMS;
     rb0 = 0;
   }
   const bool streamer = wave < NSW;
@@ -1161,8 +1167,8 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
       }
       if (lane == 0) __hip_atomic_fetch_add(&done[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    float* out = pa.out + (int64_t)blockIdx.x * pad_rows(rows) + (int64_t)rb0 * kSlabRows;
-    if constexpr (DOWN) out = pa.out + ((int64_t)slot * pa.nchunk + (blockIdx.x % pa.nchunk)) * pad_rows(rows) +
+    float* out = pa.out + (int64_t)wi * pad_rows(rows) + (int64_t)rb0 * kSlabRows;
+    if constexpr (DOWN) out = pa.out + ((int64_t)slot * pa.nchunk + (wi % pa.nchunk)) * pad_rows(rows) +
                               (int64_t)rb0 * kSlabRows;
 #pragma unroll
     for (int r = 0; r < BPI; ++r) out[(wave + NSW * r) * kSlabRows + lane] = acc[r];
