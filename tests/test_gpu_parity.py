@@ -441,9 +441,9 @@ def test_topk_orders_logits_equal_in_fp32_by_fp64(layer_bank):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_routed_decode_matches_two_calls_and_oracle(layer_bank, dtype):
-    """rvq_moe_decode_routed (top-k taken inside the gate/up kernel for fp32 tables, by the selection
-    kernel for fp16) gives the ids and gates of rvq_router_topk bit for bit, the output of
-    rvq_moe_layer_forward on them bit for bit, and the oracle's layer within tolerance."""
+    """rvq_moe_decode_routed (top-k taken inside the gate/up kernel, for fp32 and fp16 tables) gives
+    the ids and gates of rvq_router_topk bit for bit, the output of rvq_moe_layer_forward on them bit
+    for bit, and the oracle's layer within tolerance."""
     bank, bits, w = layer_bank
     ws = rvq.make_moe_workspace(bank, 1, TOP_K, dtype)
     cache = {}
