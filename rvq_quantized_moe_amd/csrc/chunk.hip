@@ -174,20 +174,17 @@ __device__ __forceinline__ uint32_t code_off(const uint32_t (&d)[3], int kk, int
 template <bool F16>
 struct Decoder;
 
-// cb: LDS address of the matrix's codebooks (stage s at cb + 4096 s); o0..o2: entry byte offsets.
+// The three stage vectors of a group (read from LDS) summed into the A fragment.
 template <>
 struct Decoder<true> {
   typedef half8 frag_t;
-  __device__ static frag_t decode(uint32_t cb, uint32_t o0, uint32_t o1, uint32_t o2) {
-    return lds_h8(o0 + cb) + lds_h8(o1 + cb + 4096) + lds_h8(o2 + cb + 8192);
-  }
+  __device__ static frag_t sum(half8 a, half8 b, half8 d) { return a + b + d; }
 };
 
 template <>
 struct Decoder<false> {
   typedef bf16x8 frag_t;
-  __device__ static frag_t decode(uint32_t cb, uint32_t o0, uint32_t o1, uint32_t o2) {
-    const half8 a = lds_h8(o0 + cb), b = lds_h8(o1 + cb + 4096), d = lds_h8(o2 + cb + 8192);
+  __device__ static frag_t sum(half8 a, half8 b, half8 d) {
     frag_t f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = (__bf16)((float)a[i] + (float)b[i] + (float)d[i]);
@@ -336,19 +333,29 @@ __device__ inline void k_loop(f32x4 (&acc)[NMAT][4], const uint8_t* const (&mats
 #pragma unroll
       for (int i = 0; i < 3; ++i) d[m][i] = lds_w((cur ? coff[1][i] : coff[0][i]) + m * kSlabBytes);
     const uint32_t ba = cur ? boff[1] : boff[0];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      frag_t a[NMAT];
+    // step kk's LDS reads (three codebook vectors per matrix, one B fragment per pair block) are
+    // issued before step kk - 1's sums and MFMAs, so two steps' reads are in flight at a time
+    half8 E[2][NMAT][3], Bq[2][NTB];
+    auto fetch = [&](int kk, half8 (&e)[NMAT][3], half8 (&bq)[NTB]) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
-        a[m] = Decoder<F16>::decode((uint32_t)(m * kCbBytes), code_off(d[m], kk, 0), code_off(d[m], kk, 1),
-                                    code_off(d[m], kk, 2));
 #pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) {
-        const half8 b = lds_h8(ba + (uint32_t)((tb * 16 * kXStride + 8 * kk) * 2));
+        for (int st = 0; st < 3; ++st) e[m][st] = lds_h8((uint32_t)(m * kCbBytes + 4096 * st) + code_off(d[m], kk, st));
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) acc[m][tb] = mfma16(a[m], b, acc[m][tb]);
-      }
+      for (int tb = 0; tb < NTB; ++tb) bq[tb] = lds_h8(ba + (uint32_t)((tb * 16 * kXStride + 8 * kk) * 2));
+    };
+    fetch(0, E[0], Bq[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = kk & 1;
+      if (kk + 1 < 4) fetch(kk + 1, E[c ^ 1], Bq[c ^ 1]);
+      frag_t a[NMAT];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) a[m] = Decoder<F16>::sum(E[c][m][0], E[c][m][1], E[c][m][2]);
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) acc[m][tb] = mfma16(a[m], Bq[c][tb], acc[m][tb]);
     }
     stage_store<NMAT>(st, L::code(cur ^ 1), L::act(cur ^ 1));
     __syncthreads();
