@@ -221,8 +221,10 @@ __device__ inline int h_exponent(uint32_t maxbits) {
   return e - 15;        // m * 2^-(e-15) < 2^15 < 65504
 }
 
-// Register staging of one K-tile: thread i < 192 holds 16 bytes of each slab; every thread holds 4
-// 16-byte pieces of the activation tile (64 rows x 16 pieces): piece u covers row (tid + 256u)/16.
+// Register staging of one K-tile: thread i < 192 holds 16 bytes of each slab; every thread holds up
+// to 4 16-byte pieces of the activation tile (64 rows x 16 pieces): piece u covers row (tid + 256u)/16,
+// so piece u is exactly pair block u (rows 16u .. 16u+15).  A pass over NTB pair blocks stages
+// pieces u < NTB only: the MFMAs read no other rows.
 constexpr int kActPieces = kChunkTok * (kChunkK / 8) / 256;   // 4 (256-thread workgroups)
 
 template <int NMAT>
@@ -235,7 +237,7 @@ struct TokenRows {  // per pass: the source row of each of this thread's activat
   int t[kActPieces];
 };
 
-template <int NMAT>
+template <int NMAT, int NTB>
 __device__ inline void stage_issue(StageRegs<NMAT>& s, const uint8_t* const (&mats)[NMAT], int kt, int nrb, int rb,
                                    const Act16& a, const TokenRows& tr, int k0) {
   if (threadIdx.x < kSlabBytes / 16) {
@@ -244,7 +246,7 @@ __device__ inline void stage_issue(StageRegs<NMAT>& s, const uint8_t* const (&ma
       s.slab[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes) + threadIdx.x);
   }
 #pragma unroll
-  for (int u = 0; u < kActPieces; ++u) {
+  for (int u = 0; u < NTB; ++u) {
     const int c8 = (threadIdx.x + 256 * u) % (kChunkK / 8);
     const int t = tr.t[u];
     s.act[u] = (t >= 0 && k0 + c8 * 8 < a.K) ? *reinterpret_cast<const u32x4*>(a.src + (int64_t)t * a.K + k0 + c8 * 8)
@@ -261,14 +263,14 @@ __device__ inline uint32_t pack_b2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
 }
 
-template <int NMAT>
+template <int NMAT, int NTB>
 __device__ inline void stage_store(const StageRegs<NMAT>& s, uint8_t* code_lds, uint16_t* x_lds) {
   if (threadIdx.x < kSlabBytes / 16) {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) reinterpret_cast<u32x4*>(code_lds + m * kSlabBytes)[threadIdx.x] = s.slab[m];
   }
 #pragma unroll
-  for (int u = 0; u < kActPieces; ++u) {
+  for (int u = 0; u < NTB; ++u) {
     const int q = threadIdx.x + 256 * u, j = q / (kChunkK / 8), c8 = q % (kChunkK / 8);
     *reinterpret_cast<u32x4*>(x_lds + j * kXStride + c8 * 8) = s.act[u];
   }
@@ -304,9 +306,14 @@ struct ChunkLds {
 // prefetch is never drained early.
 template <bool F16, int NMAT, int NTB>
 __device__ inline void k_loop(f32x4 (&acc)[NMAT][4], const uint8_t* const (&mats)[NMAT], int ntile, int nrb, int rb,
-                              const Act16& act, const TokenRows& tr, StageRegs<NMAT>& st) {
+                              const Act16& act, const TokenRows& tr) {
   typedef typename Decoder<F16>::frag_t frag_t;
   typedef ChunkLds<NMAT> L;
+  StageRegs<NMAT> st;
+  stage_issue<NMAT, NTB>(st, mats, 0, nrb, rb, act, tr, 0);
+  __syncthreads();  // the previous pass is done with both buffers (and the codebooks are stored)
+  stage_store<NMAT, NTB>(st, L::code(0), L::act(0));
+  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4;
   const int r = 16 * wave + (lane & 15);
@@ -326,7 +333,7 @@ __device__ inline void k_loop(f32x4 (&acc)[NMAT][4], const uint8_t* const (&mats
   for (int kt = 0; kt < ntile; ++kt) {
     const int cur = kt & 1;
     const int nxt = kt + 1 < ntile ? kt + 1 : kt;
-    stage_issue<NMAT>(st, mats, nxt, nrb, rb, act, tr, nxt * kChunkK);
+    stage_issue<NMAT, NTB>(st, mats, nxt, nrb, rb, act, tr, nxt * kChunkK);
     uint32_t d[NMAT][3];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
@@ -357,7 +364,7 @@ __device__ inline void k_loop(f32x4 (&acc)[NMAT][4], const uint8_t* const (&mats
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) acc[m][tb] = mfma16(a[m], Bq[c][tb], acc[m][tb]);
     }
-    stage_store<NMAT>(st, L::code(cur ^ 1), L::act(cur ^ 1));
+    stage_store<NMAT, NTB>(st, L::code(cur ^ 1), L::act(cur ^ 1));
     __syncthreads();
   }
 }
@@ -378,21 +385,16 @@ __device__ void expert_tile_gemm(const uint8_t* const (&mats)[NMAT], const float
     const int np = n_pairs - pb < kChunkTok ? n_pairs - pb : kChunkTok;
     TokenRows tr;
     pass_rows(tr, act, p_begin + pb, np);
-    StageRegs<NMAT> st;
-    stage_issue<NMAT>(st, mats, 0, nrb, rb, act, tr, 0);
-    __syncthreads();  // the previous pass is done with both buffers (and the codebooks are stored)
-    stage_store<NMAT>(st, L::code(0), L::act(0));
-    __syncthreads();
     f32x4 acc[NMAT][4];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[m][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
     switch ((np + 15) / 16) {
-      case 1: k_loop<F16, NMAT, 1>(acc, mats, ntile, nrb, rb, act, tr, st); break;
-      case 2: k_loop<F16, NMAT, 2>(acc, mats, ntile, nrb, rb, act, tr, st); break;
-      case 3: k_loop<F16, NMAT, 3>(acc, mats, ntile, nrb, rb, act, tr, st); break;
-      default: k_loop<F16, NMAT, 4>(acc, mats, ntile, nrb, rb, act, tr, st); break;
+      case 1: k_loop<F16, NMAT, 1>(acc, mats, ntile, nrb, rb, act, tr); break;
+      case 2: k_loop<F16, NMAT, 2>(acc, mats, ntile, nrb, rb, act, tr); break;
+      case 3: k_loop<F16, NMAT, 3>(acc, mats, ntile, nrb, rb, act, tr); break;
+      default: k_loop<F16, NMAT, 4>(acc, mats, ntile, nrb, rb, act, tr); break;
     }
     epi(acc, p_begin + pb, np, rb * kChunkRows + 16 * wave + 4 * q, lane & 15);
   }
