@@ -375,6 +375,32 @@ def test_topk_ties_across_blocks(layer_bank):
     assert rvq.check_device_status(ws) == 0
 
 
+def test_topk_all_logits_equal(layer_bank):
+    """All 256 router rows equal, so all logits are equal: every expert is a candidate with the same
+    key, and the selection's exact fixup of equal keys decides the whole order (by id alone: ids
+    0 .. k-1, each gate 1/k, as the oracle gives), for fp32 and fp16 tables; the two-call form agrees
+    bit for bit."""
+    say("top-k: all logits equal")
+    bank, bits0, _ = layer_bank
+    bits = np.repeat(bits0[:1], LAYER_EXPERTS, axis=0)
+    x = synth.activation_f32(synth.SEED_LAYER, 47, HIDDEN)
+    lo = oracle.router_logits(bits, x[None, :])[0]
+    assert len(np.unique(lo)) == 1
+    ids_o, gates_o, _ = oracle.topk(lo, TOP_K)
+    assert list(ids_o) == list(range(TOP_K))
+    w = to_dev(bits.view(np.int16)).view(torch.bfloat16)
+    xd = to_dev(x)
+    for dtype in ("f32", "f16"):
+        ws = rvq.make_moe_workspace(bank, 1, TOP_K, dtype)
+        y, ids_r, gates_r, _ = rvq.moe_decode_routed(bank, w, xd, TOP_K, dtype=dtype, workspace=ws)
+        assert np.array_equal(ids_r.cpu().numpy(), ids_o), dtype
+        np.testing.assert_allclose(gates_r.cpu().numpy(), gates_o, rtol=1e-6)
+        ids2, gates2, _ = rvq.router_topk(w, xd, TOP_K)
+        assert torch.equal(ids_r, ids2[0]) and torch.equal(gates_r, gates2[0])
+        assert torch.equal(y, rvq.moe_layer_forward(bank, xd, ids2[0], gates2[0], dtype=dtype, workspace=ws))
+        assert rvq.check_device_status(ws) == 0
+
+
 def near_tie_router(bits0, x, h0, gaps):
     """Router rows, copies of the top row of bits0 on x, raised by gaps[i] bf16 ulps at element h0
     (positive there), at ids 10, 100, 200, ...: their logits differ by a few ulps of w[h0] times x[h0]."""
@@ -795,6 +821,8 @@ def test_routed_decode_small_expert_count():
     (3584, 2048, 4, 2),    # both wave-specialised kernels, 2 row chunks of down
     (256, 128, 64, 64),    # the largest k: every expert selected
     (1024, 2048, 64, 64),  # the largest k through the wave-specialised gate/up (and its in-kernel ranking)
+    (256, 2048, 300, 16),  # in-kernel top-k over a ragged expert count (300: 4 whole waves and a part)
+    (128, 2048, 768, 16),  # the most experts the in-kernel top-k takes (a thread per expert)
 ])
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_moe_layer_other_shapes(H, I, E, k, dtype):
