@@ -429,7 +429,13 @@ struct GateUpEpi {
         h[(int64_t)(p0 + j) * I + rloc + i] = hv;
         m = fmaxf(m, fabsf(hv));
       }
-      if constexpr (F16) atomicMax(&hmax[p0 + j], __float_as_uint(m));
+      if constexpr (F16) {
+        // the four lanes of this pair column (lanes col, col + 16, col + 32, col + 48; the same j, so
+        // all present or all skipped) agree on their maximum first: one atomic per column and wave
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if ((threadIdx.x & 63) < 16) atomicMax(&hmax[p0 + j], __float_as_uint(m));
+      }
     }
   }
 };
