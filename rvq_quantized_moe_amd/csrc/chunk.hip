@@ -66,8 +66,7 @@ size_t chunk_workspace_bytes(int E, int H, int I, int T, int k) { return chunk_w
 // every position are deterministic.
 __global__ __launch_bounds__(1024) void k_chunk_bucket(const int32_t* __restrict__ ids, int T, int k, int E,
                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ pair_token,
-                                                       int32_t* __restrict__ pair_pos, uint32_t* __restrict__ hmax,
-                                                       int32_t* __restrict__ status) {
+                                                       int32_t* __restrict__ pair_pos, int32_t* __restrict__ status) {
   extern __shared__ uint32_t sm[];
   const int words = (T + 31) / 32;
   uint32_t* bitmap = sm;                       // [E][words]
@@ -79,7 +78,6 @@ __global__ __launch_bounds__(1024) void k_chunk_bucket(const int32_t* __restrict
   for (int p = threadIdx.x; p < P; p += blockDim.x) {
     const int t = p / k;
     const int e = ids[p];
-    hmax[p] = 0u;
     if (e < 0 || e >= E) {
       atomicExch(status, 6 /* RVQ_ERR_EXPERT_ID */);
       continue;
@@ -410,31 +408,19 @@ __device__ inline int xcd_major(int nwork) {
   return w < nwork ? w : -1;
 }
 
-// Gate/up: h[p][row] = silu(g) * u (fp32), and the per-pair max |h| (fp16 tiles scale h by it).
-template <bool F16>
+// Gate/up: h[p][row] = silu(g) * u (fp32).
 struct GateUpEpi {
   float* h;
-  uint32_t* hmax;
   int I;
   __device__ void operator()(const f32x4 (&acc)[2][4], int p0, int np, int rloc, int col) const {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int j = tb * 16 + col;
       if (j >= np) continue;
-      float m = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float g = acc[0][tb][i], u = acc[1][tb][i];
-        const float hv = g / (1.f + expf(-g)) * u;
-        h[(int64_t)(p0 + j) * I + rloc + i] = hv;
-        m = fmaxf(m, fabsf(hv));
-      }
-      if constexpr (F16) {
-        // the four lanes of this pair column (lanes col, col + 16, col + 32, col + 48; the same j, so
-        // all present or all skipped) agree on their maximum first: one atomic per column and wave
-        m = fmaxf(m, __shfl_xor(m, 16, 64));
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-        if ((threadIdx.x & 63) < 16) atomicMax(&hmax[p0 + j], __float_as_uint(m));
+        h[(int64_t)(p0 + j) * I + rloc + i] = g / (1.f + expf(-g)) * u;
       }
     }
   }
@@ -470,7 +456,7 @@ template <bool F16>
 __global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint16_t* __restrict__ x16,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ pair_token, float* __restrict__ h,
-                                                      uint32_t* __restrict__ hmax, int rpw, int32_t* __restrict__ status) {
+                                                      int rpw, int32_t* __restrict__ status) {
   if (!chunk_lds_ok(status)) return;
   const int H = bank.H, I = bank.I;
   const int nrb = I / kChunkRows, ngrp = (nrb + rpw - 1) / rpw;
@@ -485,7 +471,7 @@ __global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint1
   const float* const cbs[2] = {bank.cb + ((int64_t)e * 3 + 0) * kCodebookFloats,
                                bank.cb + ((int64_t)e * 3 + 1) * kCodebookFloats};
   const Act16 act{x16, pair_token, H};
-  GateUpEpi<F16> epi{h, hmax, I};
+  GateUpEpi epi{h, I};
   expert_tile_gemm<F16, 2>(mats, cbs, H, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
 }
 
@@ -523,24 +509,43 @@ __global__ __launch_bounds__(256) void k_chunk_x16(const uint16_t* __restrict__ 
   *reinterpret_cast<u32x4*>(out + 8 * i) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// h as the down product's operand: fp16 tiles take fp16(h * 2^-e(p)), e(p) from the pair's max |h|
-// (so no entry overflows; the down epilogue multiplies by 2^e(p)); bf16 tiles take bf16(h).
-// 8 elements per thread (I is a multiple of 64, so a piece lies in one pair's row).
+// h as the down product's operand, one workgroup per pair: fp16 tiles take fp16(h * 2^-e(p)), e(p)
+// from the pair's max |h| (so no entry overflows; the down epilogue multiplies by 2^e(p)), written
+// to hmax for it; bf16 tiles take bf16(h).  8 elements per thread and step (I is a multiple of 64).
 template <bool F16>
-__global__ __launch_bounds__(256) void k_chunk_h16(const float* __restrict__ h, const uint32_t* __restrict__ hmax,
-                                                   int I, int64_t n8, uint16_t* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = *reinterpret_cast<const f32x4*>(h + 8 * i);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(h + 8 * i + 4);
-  u32x4 v;
+__global__ __launch_bounds__(256) void k_chunk_h16(const float* __restrict__ h, uint32_t* __restrict__ hmax, int I,
+                                                   uint16_t* __restrict__ out) {
+  const int64_t p = blockIdx.x;
+  const float* hp = h + p * I;
+  uint16_t* op = out + p * I;
+  float f = 1.f;
   if constexpr (F16) {
-    const float f = ldexpf(1.f, -h_exponent(hmax[(8 * i) / I]));
-    v = u32x4{pack_h2(a.x * f, a.y * f), pack_h2(a.z * f, a.w * f), pack_h2(b.x * f, b.y * f), pack_h2(b.z * f, b.w * f)};
-  } else {
-    v = u32x4{pack_b2(a.x, a.y), pack_b2(a.z, a.w), pack_b2(b.x, b.y), pack_b2(b.z, b.w)};
+    __shared__ float red[4];
+    float m = 0.f;
+    for (int c = threadIdx.x * 8; c < I; c += 256 * 8) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(hp + c);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(hp + c + 4);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (threadIdx.x == 0) hmax[p] = __float_as_uint(m);
+    f = ldexpf(1.f, -h_exponent(__float_as_uint(m)));
   }
-  *reinterpret_cast<u32x4*>(out + 8 * i) = v;
+  for (int c = threadIdx.x * 8; c < I; c += 256 * 8) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(hp + c);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(hp + c + 4);
+    u32x4 v;
+    if constexpr (F16)
+      v = u32x4{pack_h2(a.x * f, a.y * f), pack_h2(a.z * f, a.w * f), pack_h2(b.x * f, b.y * f), pack_h2(b.z * f, b.w * f)};
+    else
+      v = u32x4{pack_b2(a.x, a.y), pack_b2(a.z, a.w), pack_b2(b.x, b.y), pack_b2(b.z, b.w)};
+    *reinterpret_cast<u32x4*>(op + c) = v;
+  }
 }
 
 // out[t][r] = residual[t][r] + sum_i gates[t][i] * y[pair_pos[t][i]][r]   (fixed order in i)
@@ -581,7 +586,7 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
   BankArgs bank{codes, cb, stride, E, H, I};
   const size_t bucket_smem = ((size_t)E * ((T + 31) / 32) + E + 1) * 4;
   hipLaunchKernelGGL(k_chunk_bucket, dim3(1), dim3(1024), bucket_smem, stream, ids, T, k, E, offsets, pair_token,
-                     pair_pos, hmax, status);
+                     pair_pos, status);
   // the gate/up operand: the tokens themselves (bf16 tiles) or their fp16 copy
   const int64_t nx8 = (int64_t)T * H / 8;
   if (f16) hipLaunchKernelGGL(k_chunk_x16, dim3((unsigned)cdiv(nx8, 256)), dim3(256), 0, stream, x, nx8, x16);
@@ -597,17 +602,17 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
     const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)chunk_smem(f16, 2));
     if (e != hipSuccess) return e;
   }
-  const int64_t nh8 = (int64_t)T * k * I / 8;
+  const int64_t P = (int64_t)T * k;
   if (f16) {
     hipLaunchKernelGGL(k_chunk_gateup<true>, dim3(g_gu), dim3(256), chunk_smem(true, 2), stream, bank, xg, offsets,
-                       pair_token, h, hmax, rpw_gu, status);
-    hipLaunchKernelGGL(k_chunk_h16<true>, dim3((unsigned)cdiv(nh8, 256)), dim3(256), 0, stream, h, hmax, I, nh8, h16);
+                       pair_token, h, rpw_gu, status);
+    hipLaunchKernelGGL(k_chunk_h16<true>, dim3((unsigned)P), dim3(256), 0, stream, h, hmax, I, h16);
     hipLaunchKernelGGL(k_chunk_down<true>, dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets, h16,
                        hmax, ybuf, rpw_dn, status);
   } else {
     hipLaunchKernelGGL(k_chunk_gateup<false>, dim3(g_gu), dim3(256), chunk_smem(false, 2), stream, bank, xg, offsets,
-                       pair_token, h, hmax, rpw_gu, status);
-    hipLaunchKernelGGL(k_chunk_h16<false>, dim3((unsigned)cdiv(nh8, 256)), dim3(256), 0, stream, h, hmax, I, nh8, h16);
+                       pair_token, h, rpw_gu, status);
+    hipLaunchKernelGGL(k_chunk_h16<false>, dim3((unsigned)P), dim3(256), 0, stream, h, hmax, I, h16);
     hipLaunchKernelGGL(k_chunk_down<false>, dim3(g_dn), dim3(256), chunk_smem(false, 1), stream, bank, offsets, h16,
                        hmax, ybuf, rpw_dn, status);
   }
