@@ -396,9 +396,11 @@ __device__ inline void k_loop(f32x4 (&acc)[NMAT][4], const uint8_t* const (&mats
   }
 }
 
-// One workgroup = (expert, row blocks [rb0, rb1)): loads the codebooks once, then per 64-row block
-// loops over the expert's pairs 64 at a time and over K.
-template <bool F16, int NMAT, class Epi>
+// One workgroup = (expert, row blocks [rb0, rb1)): loads the codebooks once, then per RBS row blocks
+// loops over the expert's pairs 64 at a time and over K.  Matrix m's slab of step rb is at
+// mats[m] + (kt * nrb + rb) * kSlabBytes: RBS = 2 with mats = {W, W + one slab} takes row blocks rb
+// and rb + 1 of one matrix W as the two products of a step (they share the staged activations).
+template <bool F16, int NMAT, class Epi, int RBS = 1>
 __device__ void expert_tile_gemm(const uint8_t* const (&mats)[NMAT], const float* const (&cbs)[NMAT], int K,
                                  int rb0, int rb1, int nrb, int p_begin, int n_pairs, const Act16& act, const Epi& epi) {
   typedef ChunkLds<NMAT> L;
@@ -407,7 +409,7 @@ __device__ void expert_tile_gemm(const uint8_t* const (&mats)[NMAT], const float
   const int q = lane >> 4;
   for (int m = 0; m < NMAT; ++m) load_codebooks(cb_lds + m * (kCbBytes / 2), cbs[m]);
   const int ntile = (K / 8 + 15) / 16;
-  for (int rb = rb0; rb < rb1; ++rb)
+  for (int rb = rb0; rb < rb1; rb += RBS)
   for (int pb = 0; pb < n_pairs; pb += kChunkTok) {
     const int np = n_pairs - pb < kChunkTok ? n_pairs - pb : kChunkTok;
     TokenRows tr;
@@ -455,20 +457,23 @@ struct GateUpEpi {
   }
 };
 
-// Down: y[p][row] = acc * 2^e(p) (undoing the fp16 scale of h).
-template <bool F16>
+// Down: y[p][row] = acc * 2^e(p) (undoing the fp16 scale of h).  NB products of consecutive row
+// blocks (NB = 2: a step of two row blocks of the down matrix).
+template <bool F16, int NB>
 struct DownEpi {
   float* y;
   const uint32_t* hmax;
   int H;
-  __device__ void operator()(const f32x4 (&acc)[1][4], int p0, int np, int rloc, int col) const {
+  __device__ void operator()(const f32x4 (&acc)[NB][4], int p0, int np, int rloc, int col) const {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int j = tb * 16 + col;
       if (j >= np) continue;
       const float sc = F16 ? ldexpf(1.f, h_exponent(hmax[p0 + j])) : 1.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[(int64_t)(p0 + j) * H + rloc + i] = acc[0][tb][i] * sc;
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[(int64_t)(p0 + j) * H + rloc + b * kChunkRows + i] = acc[b][tb][i] * sc;
     }
   }
 };
@@ -504,7 +509,8 @@ __global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint1
   expert_tile_gemm<F16, 2>(mats, cbs, H, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
 }
 
-template <bool F16>
+// PAIR: two row blocks per step (an even number of row blocks, groups of rpw even).
+template <bool F16, bool PAIR>
 __global__ __launch_bounds__(256) void k_chunk_down(BankArgs bank, const int32_t* __restrict__ offsets,
                                                     const uint16_t* __restrict__ h16, const uint32_t* __restrict__ hmax,
                                                     float* __restrict__ y, int rpw, int32_t* __restrict__ status) {
@@ -517,12 +523,20 @@ __global__ __launch_bounds__(256) void k_chunk_down(BankArgs bank, const int32_t
   const int rb1 = rb0 + rpw < nrb ? rb0 + rpw : nrb;
   const int p_begin = offsets[e], n_pairs = offsets[e + 1] - p_begin;
   if (n_pairs == 0) return;
-  const uint8_t* rec = bank.codes + (int64_t)e * bank.stride;
-  const uint8_t* const mats[1] = {rec + 2 * packed_bytes(I, H)};
-  const float* const cbs[1] = {bank.cb + ((int64_t)e * 3 + 2) * kCodebookFloats};
+  const uint8_t* down = bank.codes + (int64_t)e * bank.stride + 2 * packed_bytes(I, H);
+  const float* cb = bank.cb + ((int64_t)e * 3 + 2) * kCodebookFloats;
   const Act16 act{h16, nullptr, I};
-  DownEpi<F16> epi{y, hmax, H};
-  expert_tile_gemm<F16, 1>(mats, cbs, I, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
+  if constexpr (PAIR) {
+    const uint8_t* const mats[2] = {down, down + kSlabBytes};
+    const float* const cbs[2] = {cb, cb};
+    DownEpi<F16, 2> epi{y, hmax, H};
+    expert_tile_gemm<F16, 2, DownEpi<F16, 2>, 2>(mats, cbs, I, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
+  } else {
+    const uint8_t* const mats[1] = {down};
+    const float* const cbs[1] = {cb};
+    DownEpi<F16, 1> epi{y, hmax, H};
+    expert_tile_gemm<F16, 1>(mats, cbs, I, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
+  }
 }
 
 // fp16 copy of the chunk's bf16 tokens, for fp16 tiles (exact for |x| inside the fp16 range): done
@@ -624,10 +638,14 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
   const int rpw_gu = 2, rpw_dn = 4;
   const unsigned g_gu = (unsigned)(cdiv(E * cdiv(I / kChunkRows, rpw_gu), 8) * 8);
   const unsigned g_dn = (unsigned)(cdiv(E * cdiv(H / kChunkRows, rpw_dn), 8) * 8);
-  // gate+up double-buffers two slabs and the token tile next to two codebooks (over 64 KiB): allow
-  // the larger allocation
+  // down takes two row blocks per step when their number is even (rpw_dn is even, so every group
+  // then is too); gate+up, and down in pairs, double-buffer two slabs and the token tile next to two
+  // codebooks (over 64 KiB): allow the larger allocation
+  const bool pair_dn = (H / kChunkRows) % 2 == 0;
   for (const void* f : {reinterpret_cast<const void*>(k_chunk_gateup<false>),
-                        reinterpret_cast<const void*>(k_chunk_gateup<true>)}) {
+                        reinterpret_cast<const void*>(k_chunk_gateup<true>),
+                        reinterpret_cast<const void*>(k_chunk_down<false, true>),
+                        reinterpret_cast<const void*>(k_chunk_down<true, true>)}) {
     const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)chunk_smem(f16, 2));
     if (e != hipSuccess) return e;
   }
@@ -636,14 +654,22 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
     hipLaunchKernelGGL(k_chunk_gateup<true>, dim3(g_gu), dim3(256), chunk_smem(true, 2), stream, bank, xg, offsets,
                        pair_token, h, rpw_gu, status);
     hipLaunchKernelGGL(k_chunk_h16<true>, dim3((unsigned)P), dim3(256), 0, stream, h, hmax, I, h16);
-    hipLaunchKernelGGL(k_chunk_down<true>, dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets, h16,
-                       hmax, ybuf, rpw_dn, status);
+    if (pair_dn)
+      hipLaunchKernelGGL((k_chunk_down<true, true>), dim3(g_dn), dim3(256), chunk_smem(true, 2), stream, bank, offsets,
+                         h16, hmax, ybuf, rpw_dn, status);
+    else
+      hipLaunchKernelGGL((k_chunk_down<true, false>), dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets,
+                         h16, hmax, ybuf, rpw_dn, status);
   } else {
     hipLaunchKernelGGL(k_chunk_gateup<false>, dim3(g_gu), dim3(256), chunk_smem(false, 2), stream, bank, xg, offsets,
                        pair_token, h, rpw_gu, status);
     hipLaunchKernelGGL(k_chunk_h16<false>, dim3((unsigned)P), dim3(256), 0, stream, h, hmax, I, h16);
-    hipLaunchKernelGGL(k_chunk_down<false>, dim3(g_dn), dim3(256), chunk_smem(false, 1), stream, bank, offsets, h16,
-                       hmax, ybuf, rpw_dn, status);
+    if (pair_dn)
+      hipLaunchKernelGGL((k_chunk_down<false, true>), dim3(g_dn), dim3(256), chunk_smem(false, 2), stream, bank,
+                         offsets, h16, hmax, ybuf, rpw_dn, status);
+    else
+      hipLaunchKernelGGL((k_chunk_down<false, false>), dim3(g_dn), dim3(256), chunk_smem(false, 1), stream, bank,
+                         offsets, h16, hmax, ybuf, rpw_dn, status);
   }
   hipLaunchKernelGGL(k_chunk_combine, dim3((unsigned)cdiv(H, 256), (unsigned)T), dim3(256), 0, stream, ybuf, pair_pos,
                      gates, k, H, residual, y);

@@ -75,6 +75,15 @@ def test_chunk_crowded_experts_and_residual(dtype):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_chunk_odd_row_block_count(dtype):
+    """H = 192: three 64-row blocks of the down matrix, so down takes one row block per step (an even
+    count takes two, as in the other cases); K = 192 also leaves a partial K-tile for gate/up."""
+    say(f"chunk E=8 H=192 I=128 T=40 k=2 {dtype}")
+    err = run_case(0xC5, 8, 192, 128, 40, 2, dtype, residual=True)[0]
+    assert err <= TOL[dtype]
+
+
 def test_chunk_at_max_tokens():
     """The largest chunk accepted (4096 tokens; 8 experts, so about 1000 pairs per expert)."""
     say("chunk E=8 H=256 I=128 T=4096 k=2 f16")
