@@ -599,10 +599,20 @@ __global__ __launch_bounds__(256) void k_chunk_combine(const float* __restrict__
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= H) return;
   float acc = residual ? residual[(int64_t)t * H + r] : 0.f;
-  for (int i = 0; i < k; ++i) {
-    const int p = pair_pos[t * k + i];
-    if (p < 0) continue;
-    acc = fmaf(gates[t * k + i], y[(int64_t)p * H + r], acc);
+  // eight pairs' loads issued together (a dropped pair reads row 0, which exists, and is then
+  // skipped), the sums still added in slot order
+  for (int i0 = 0; i0 < k; i0 += 8) {
+    int p[8];
+    float g[8], v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      p[u] = i0 + u < k ? pair_pos[t * k + i0 + u] : -1;
+      g[u] = i0 + u < k ? gates[t * k + i0 + u] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = y[(int64_t)(p[u] < 0 ? 0 : p[u]) * H + r];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = p[u] < 0 ? acc : fmaf(g[u], v[u], acc);
   }
   out[(int64_t)t * H + r] = acc;
 }
