@@ -75,49 +75,92 @@ __global__ __launch_bounds__(1024) void k_chunk_bucket(const int32_t* __restrict
   for (int i = threadIdx.x; i < E * words; i += blockDim.x) bitmap[i] = 0u;
   for (int i = threadIdx.x; i <= E; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
-  for (int p = threadIdx.x; p < P; p += blockDim.x) {
-    const int t = p / k;
-    const int e = ids[p];
-    if (e < 0 || e >= E) {
-      atomicExch(status, 6 /* RVQ_ERR_EXPERT_ID */);
-      continue;
+  // each thread's pairs 8 at a time, their ids loaded together (one memory round trip per 8)
+  constexpr int kBatch = 8;
+  for (int p0 = threadIdx.x; p0 < P; p0 += kBatch * blockDim.x) {
+    int eb[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = p0 + u * blockDim.x;
+      eb[u] = p < P ? ids[p] : 0;
     }
-    atomicOr(&bitmap[(size_t)e * words + t / 32], 1u << (t % 32));
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = p0 + u * blockDim.x;
+      if (p >= P) continue;
+      const int t = p / k, e = eb[u];
+      if (e < 0 || e >= E) {
+        atomicExch(status, 6 /* RVQ_ERR_EXPERT_ID */);
+        continue;
+      }
+      atomicOr(&bitmap[(size_t)e * words + t / 32], 1u << (t % 32));
+    }
   }
   __syncthreads();
-  // counts per expert, then an exclusive prefix (one thread: E <= 4096 additions)
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int c = 0;
-    for (int w = 0; w < words; ++w) c += __popc(bitmap[(size_t)e * words + w]);
-    cnt[e] = c;
+  // counts per expert and their exclusive prefix: thread i takes experts [i per, (i + 1) per)
+  // (per <= 4: E <= 4096 and 1024 threads), a shuffle scan within each wave, the 16 wave totals
+  // through LDS.  Integer sums: exact in any grouping.
+  __shared__ int wsum[1024 / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int per = (E + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int e0 = threadIdx.x * per;
+  int c[4];
+  int own = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int cc = 0;
+    if (j < per && e0 + j < E)
+      for (int w = 0; w < words; ++w) cc += __popc(bitmap[(size_t)(e0 + j) * words + w]);
+    c[j] = cc;
+    own += cc;
   }
+  int incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = cnt[e];
-      cnt[e] = run;
-      offsets[e] = run;
-      run += c;
+  int run = incl - own;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j < per && e0 + j < E) {
+      cnt[e0 + j] = run;
+      offsets[e0 + j] = run;
+      run += c[j];
     }
+  }
+  if (threadIdx.x == blockDim.x - 1) {   // the last thread's running sum is the total
     cnt[E] = run;
     offsets[E] = run;
   }
   __syncthreads();
-  for (int p = threadIdx.x; p < P; p += blockDim.x) {
-    const int t = p / k;
-    const int e = ids[p];
-    if (e < 0 || e >= E) {
-      pair_pos[p] = -1;
-      continue;
+  for (int p0 = threadIdx.x; p0 < P; p0 += kBatch * blockDim.x) {
+    int eb[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = p0 + u * blockDim.x;
+      eb[u] = p < P ? ids[p] : 0;
     }
-    const uint32_t* row = bitmap + (size_t)e * words;
-    int r = 0;
-    for (int w = 0; w < t / 32; ++w) r += __popc(row[w]);
-    r += __popc(row[t / 32] & ((1u << (t % 32)) - 1u));
-    const int pos = cnt[e] + r;
-    pair_token[pos] = t;
-    pair_pos[p] = pos;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = p0 + u * blockDim.x;
+      if (p >= P) continue;
+      const int t = p / k, e = eb[u];
+      if (e < 0 || e >= E) {
+        pair_pos[p] = -1;
+        continue;
+      }
+      const uint32_t* row = bitmap + (size_t)e * words;
+      int r = 0;
+      for (int w = 0; w < t / 32; ++w) r += __popc(row[w]);
+      r += __popc(row[t / 32] & ((1u << (t % 32)) - 1u));
+      const int pos = cnt[e] + r;
+      pair_token[pos] = t;
+      pair_pos[p] = pos;
+    }
   }
 }
 
