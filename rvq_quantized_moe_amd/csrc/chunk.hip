@@ -26,6 +26,7 @@ namespace rvq {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kChunkRows = 64;            // weight rows per workgroup (one packed row block)
 constexpr int kChunkTok = 64;             // tokens per MFMA pass (4 blocks of 16)
@@ -38,7 +39,7 @@ struct ChunkWs {
 
 // Workspace layout of the chunk path (all 256-byte aligned):
 //   status int32 | offsets int32[E+1] | pair_token int32[P] | pair_pos int32[T*k]
-//   | hmax uint32[P] (bit pattern of max|h| per pair) | h fp32 [P][I] | y fp32 [P][H]
+//   | hmax uint32[P] (bit pattern of max|h| per pair) | h fp32 [P][I] (fp16 tiles) | y fp32 [P][H]
 //   | x16 fp16 [T][H] (the chunk in fp16, for fp16 tiles) | h16 16-bit [P][I] (h as the down operand)
 ChunkWs chunk_ws_layout(int E, int H, int I, int T, int k) {
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
@@ -482,19 +483,28 @@ __device__ inline int xcd_major(int nwork) {
   return w < nwork ? w : -1;
 }
 
-// Gate/up: h[p][row] = silu(g) * u (fp32).
+// Gate/up: h[p][row] = silu(g) * u.  fp16 tiles: fp32 h (k_chunk_h16 scales it per pair); bf16
+// tiles: bf16(h) straight into the down operand (the same rounding k_chunk_h16 would apply).
+template <bool F16>
 struct GateUpEpi {
   float* h;
+  uint16_t* h16;
   int I;
   __device__ void operator()(const f32x4 (&acc)[2][4], int p0, int np, int rloc, int col) const {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int j = tb * 16 + col;
       if (j >= np) continue;
+      float hv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float g = acc[0][tb][i], u = acc[1][tb][i];
-        h[(int64_t)(p0 + j) * I + rloc + i] = g / (1.f + expf(-g)) * u;
+        hv[i] = g / (1.f + expf(-g)) * u;
+      }
+      if constexpr (F16) {
+        *reinterpret_cast<f32x4*>(h + (int64_t)(p0 + j) * I + rloc) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+      } else {
+        *reinterpret_cast<u32x2*>(h16 + (int64_t)(p0 + j) * I + rloc) = u32x2{pack_b2(hv[0], hv[1]), pack_b2(hv[2], hv[3])};
       }
     }
   }
@@ -533,7 +543,7 @@ template <bool F16>
 __global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint16_t* __restrict__ x16,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ pair_token, float* __restrict__ h,
-                                                      int rpw, int32_t* __restrict__ status) {
+                                                      uint16_t* __restrict__ h16, int rpw, int32_t* __restrict__ status) {
   if (!chunk_lds_ok(status)) return;
   const int H = bank.H, I = bank.I;
   const int nrb = I / kChunkRows, ngrp = (nrb + rpw - 1) / rpw;
@@ -548,7 +558,7 @@ __global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint1
   const float* const cbs[2] = {bank.cb + ((int64_t)e * 3 + 0) * kCodebookFloats,
                                bank.cb + ((int64_t)e * 3 + 1) * kCodebookFloats};
   const Act16 act{x16, pair_token, H};
-  GateUpEpi epi{h, I};
+  GateUpEpi<F16> epi{h, h16, I};
   expert_tile_gemm<F16, 2>(mats, cbs, H, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
 }
 
@@ -595,42 +605,35 @@ __global__ __launch_bounds__(256) void k_chunk_x16(const uint16_t* __restrict__ 
   *reinterpret_cast<u32x4*>(out + 8 * i) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// h as the down product's operand, one workgroup per pair: fp16 tiles take fp16(h * 2^-e(p)), e(p)
-// from the pair's max |h| (so no entry overflows; the down epilogue multiplies by 2^e(p)), written
-// to hmax for it; bf16 tiles take bf16(h).  8 elements per thread and step (I is a multiple of 64).
-template <bool F16>
+// h as the fp16 tiles' down operand, one workgroup per pair: fp16(h * 2^-e(p)), e(p) from the pair's
+// max |h| (so no entry overflows; the down epilogue multiplies by 2^e(p)), written to hmax for it.
+// 8 elements per thread and step (I is a multiple of 64).  (bf16 tiles take bf16(h) from the gate/up
+// epilogue directly.)
 __global__ __launch_bounds__(256) void k_chunk_h16(const float* __restrict__ h, uint32_t* __restrict__ hmax, int I,
                                                    uint16_t* __restrict__ out) {
   const int64_t p = blockIdx.x;
   const float* hp = h + p * I;
   uint16_t* op = out + p * I;
-  float f = 1.f;
-  if constexpr (F16) {
-    __shared__ float red[4];
-    float m = 0.f;
-    for (int c = threadIdx.x * 8; c < I; c += 256 * 8) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(hp + c);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(hp + c + 4);
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    if (threadIdx.x == 0) hmax[p] = __float_as_uint(m);
-    f = ldexpf(1.f, -h_exponent(__float_as_uint(m)));
-  }
+  __shared__ float red[4];
+  float m = 0.f;
   for (int c = threadIdx.x * 8; c < I; c += 256 * 8) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(hp + c);
     const f32x4 b = *reinterpret_cast<const f32x4*>(hp + c + 4);
-    u32x4 v;
-    if constexpr (F16)
-      v = u32x4{pack_h2(a.x * f, a.y * f), pack_h2(a.z * f, a.w * f), pack_h2(b.x * f, b.y * f), pack_h2(b.z * f, b.w * f)};
-    else
-      v = u32x4{pack_b2(a.x, a.y), pack_b2(a.z, a.w), pack_b2(b.x, b.y), pack_b2(b.z, b.w)};
-    *reinterpret_cast<u32x4*>(op + c) = v;
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (threadIdx.x == 0) hmax[p] = __float_as_uint(m);
+  const float f = ldexpf(1.f, -h_exponent(__float_as_uint(m)));
+  for (int c = threadIdx.x * 8; c < I; c += 256 * 8) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(hp + c);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(hp + c + 4);
+    *reinterpret_cast<u32x4*>(op + c) =
+        u32x4{pack_h2(a.x * f, a.y * f), pack_h2(a.z * f, a.w * f), pack_h2(b.x * f, b.y * f), pack_h2(b.z * f, b.w * f)};
   }
 }
 
@@ -705,8 +708,8 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
   const int64_t P = (int64_t)T * k;
   if (f16) {
     hipLaunchKernelGGL(k_chunk_gateup<true>, dim3(g_gu), dim3(256), chunk_smem(true, 2), stream, bank, xg, offsets,
-                       pair_token, h, rpw_gu, status);
-    hipLaunchKernelGGL(k_chunk_h16<true>, dim3((unsigned)P), dim3(256), 0, stream, h, hmax, I, h16);
+                       pair_token, h, h16, rpw_gu, status);
+    hipLaunchKernelGGL(k_chunk_h16, dim3((unsigned)P), dim3(256), 0, stream, h, hmax, I, h16);
     if (pair_dn)
       hipLaunchKernelGGL((k_chunk_down<true, true>), dim3(g_dn), dim3(256), chunk_smem(true, 2), stream, bank, offsets,
                          h16, hmax, ybuf, rpw_dn, status);
@@ -715,8 +718,7 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
                          h16, hmax, ybuf, rpw_dn, status);
   } else {
     hipLaunchKernelGGL(k_chunk_gateup<false>, dim3(g_gu), dim3(256), chunk_smem(false, 2), stream, bank, xg, offsets,
-                       pair_token, h, rpw_gu, status);
-    hipLaunchKernelGGL(k_chunk_h16<false>, dim3((unsigned)P), dim3(256), 0, stream, h, hmax, I, h16);
+                       pair_token, h, h16, rpw_gu, status);
     if (pair_dn)
       hipLaunchKernelGGL((k_chunk_down<false, true>), dim3(g_dn), dim3(256), chunk_smem(false, 2), stream, bank,
                          offsets, h16, hmax, ybuf, rpw_dn, status);
