@@ -521,10 +521,12 @@ int rvq_rmsnorm(const float *x, int32_t T, int32_t H, float eps, float *out, hip
 int rvq_stream_copy(const void *src, void *dst, size_t nbytes, hipStream_t stream);
 
 /* Measurement aid: reads nbytes (multiple of 16) from src (16-byte aligned)
- * with the same non-temporal 16-byte global loads as the code stream and
- * writes nothing but, in practice never, one word to sink (device uint32): its
- * duration gives the achievable read-only streaming rate, the bound of the
- * table kernels' code stream. */
+ * with the same non-temporal 16-byte global loads as the code stream (one
+ * workgroup per compute unit, each reading one contiguous part with 64 KiB per
+ * compute unit in flight, the fastest read pattern measured) and writes nothing
+ * but, in practice never, one word to sink (device uint32): its duration gives
+ * the achievable read-only streaming rate, the bound of the table kernels' code
+ * stream. */
 int rvq_stream_read(const void *src, size_t nbytes, uint32_t *sink, hipStream_t stream);
 
 /* Synchronises `stream`, returns the sticky device status held in the
