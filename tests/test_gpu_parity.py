@@ -878,3 +878,18 @@ def test_bounded_waits_give_up_and_report(layer_bank):
     rvq.workspace_init(ws)              # a zero-filled header is the default limit again
     assert torch.equal(rvq.moe_layer_forward(bank, x, ids[0], gates[0], workspace=ws), ref)
     assert rvq.check_device_status(ws) == 0
+
+def test_stream_read_reference_sizes():
+    """rvq_stream_read (the bench's read-rate reference: one workgroup per CU over a contiguous part,
+    16 loads in flight per thread) on sizes that do not split evenly: parts ending inside a batch of
+    loads, fewer 16-byte pieces than a workgroup's threads, and more workgroups than the CUs could
+    each fill.  It writes nothing but its sink word, which no input here can reach (all-zero and
+    all-ones data fold to 0)."""
+    say("stream read reference sizes")
+    for nbytes in (16, 4096, 65536 + 48, (1 << 20) + 16 * 37, 48 << 20):
+        for fill in (0, 255):
+            src = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+            sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+            rvq.stream_read(src, sink)
+            torch.cuda.synchronize()
+            assert int(sink.item()) == 7, (nbytes, fill)
