@@ -766,8 +766,8 @@ def main():
                     help="skip the other workloads (one matvec, one expert, the 92-layer stack)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the sharded design is described in DESIGN.md, not run)", file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the row-split sharding is designed, not run)", file=sys.stderr)
         sys.exit(2)
 
     import torch
