@@ -1159,9 +1159,19 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
     };
 #pragma unroll
     for (int i = 0; i < NB && i < NBLK; ++i) load_blk(i, i);   // never past the workgroup's blocks
+    // Wave priority follows the finishing order of the previous item.  Two streamer waves share
+    // each SIMD, and the SIMD's arbiter favours the older one, so without this the younger half
+    // falls behind item by item and streams the workgroup's last blocks alone, with half the
+    // loads in flight.  The later half of an item's finishers runs the next item at a higher
+    // priority; the earlier half at the lowest.  Only the issue order changes.
+    int pos = 0;   // lane 0: this wave's place among the item's finishers
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
       ok &= lds_wait_ge(&built[k & 1], kPipeBuildWaves * (k / 2 + 1), wait_limit);
+      if (k > 0) {
+        if (__builtin_amdgcn_readfirstlane(pos) < NSW / 2) __builtin_amdgcn_s_setprio(0);
+        else __builtin_amdgcn_s_setprio(2);
+      }
 #pragma unroll
       for (int r = 0; r < BPI; ++r) {
         const int s = k * BPI + r;
@@ -1173,7 +1183,8 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
         acc[r] += g;
         if (s + NB < NBLK) load_blk(s % NB, s + NB);
       }
-      if (lane == 0) __hip_atomic_fetch_add(&done[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (lane == 0)
+        pos = __hip_atomic_fetch_add(&done[k & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP) - NSW * (k / 2);
     }
     float* out = pa.out + (int64_t)wi * pad_rows(rows) + (int64_t)rb0 * kSlabRows;
     if constexpr (DOWN) out = pa.out + ((int64_t)slot * pa.nchunk + (wi % pa.nchunk)) * pad_rows(rows) +
