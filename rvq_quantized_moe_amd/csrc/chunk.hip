@@ -187,9 +187,7 @@ __device__ inline void load_codebooks(_Float16* d, const float* __restrict__ cb)
 // address is an offset into it and constant parts go into the instruction's offset field.
 extern __shared__ __attribute__((aligned(16))) uint8_t chunk_lds[];
 typedef __attribute__((address_space(3))) const half8 lds_half8;
-typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 __device__ __forceinline__ half8 lds_h8(uint32_t a) { return *(lds_half8*)(uintptr_t)a; }
-__device__ __forceinline__ uint32_t lds_w(uint32_t a) { return *(lds_u32*)(uintptr_t)a; }
 __device__ __forceinline__ bool lds_at_zero() {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)chunk_lds == 0u;
 }
@@ -271,10 +269,11 @@ __device__ inline f32x4 mfma16(bf16x8 a, half8 b, f32x4 c) { return mfma16(a, __
 // Expert GEMM for one 64-row block of NMAT matrices of one expert (NMAT = 2: gate and up, which
 // share the activations; NMAT = 1: down).  Wave w owns rows [16w, 16w+16) of every matrix.
 //   acc[m][tb] (lane l, i) = sum_k W_m[row0 + 16w + 4(l/16) + i][k] * act[pair tb*16 + l%16][k]
-// Per 128-column K-tile, the NMAT code slabs and the 16-bit activations of up to 64 pairs sit in
-// one half of a double buffer in LDS.  The next K-tile's global loads are issued into registers
-// before this tile's MFMAs and written to the other half after them, so one barrier per K-tile
-// separates the halves and the load latency hides behind the compute.
+// Per 128-column K-tile, the 16-bit activations of up to 64 pairs sit in one half of a double
+// buffer in LDS.  The next K-tile's activation loads are issued into registers before this tile's
+// MFMAs and written to the other half after them, so one barrier per K-tile separates the halves
+// and the load latency hides behind the compute.  Codes do not pass through LDS: each lane loads
+// its own 12 code bytes per matrix (three dwords) one K-tile ahead.
 
 // Activation rows of a product, already 16-bit (the MFMA operand type): the chunk's tokens
 // gathered by pair (gate/up: rowmap = pair -> token) or the pairs' h (down: rowmap = null).
@@ -292,15 +291,13 @@ __device__ inline int h_exponent(uint32_t maxbits) {
   return e - 15;        // m * 2^-(e-15) < 2^15 < 65504
 }
 
-// Register staging of one K-tile: thread i < 192 holds 16 bytes of each slab; every thread holds up
-// to 4 16-byte pieces of the activation tile (64 rows x 16 pieces): piece u covers row (tid + 256u)/16,
-// so piece u is exactly pair block u (rows 16u .. 16u+15).  A pass over NTB pair blocks stages
-// pieces u < NTB only: the MFMAs read no other rows.
+// Register staging of one K-tile's activations: every thread holds up to 4 16-byte pieces of the
+// tile (64 rows x 16 pieces): piece u covers row (tid + 256u)/16, so piece u is exactly pair block u
+// (rows 16u .. 16u+15).  A pass over NTB pair blocks stages pieces u < NTB only: the MFMAs read no
+// other rows.
 constexpr int kActPieces = kChunkTok * (kChunkK / 8) / 256;   // 4 (256-thread workgroups)
 
-template <int NMAT>
 struct StageRegs {
-  u32x4 slab[NMAT];
   u32x4 act[kActPieces];
 };
 
@@ -308,14 +305,8 @@ struct TokenRows {  // per pass: the source row of each of this thread's activat
   int t[kActPieces];
 };
 
-template <int NMAT, int NTB>
-__device__ inline void stage_issue(StageRegs<NMAT>& s, const uint8_t* const (&mats)[NMAT], int kt, int nrb, int rb,
-                                   const Act16& a, const TokenRows& tr, int k0) {
-  if (threadIdx.x < kSlabBytes / 16) {
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-      s.slab[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes) + threadIdx.x);
-  }
+template <int NTB>
+__device__ inline void stage_issue(StageRegs& s, const Act16& a, const TokenRows& tr, int k0) {
 #pragma unroll
   for (int u = 0; u < NTB; ++u) {
     const int c8 = (threadIdx.x + 256 * u) % (kChunkK / 8);
@@ -334,12 +325,8 @@ __device__ inline uint32_t pack_b2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
 }
 
-template <int NMAT, int NTB>
-__device__ inline void stage_store(const StageRegs<NMAT>& s, uint8_t* code_lds, uint16_t* x_lds) {
-  if (threadIdx.x < kSlabBytes / 16) {
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) reinterpret_cast<u32x4*>(code_lds + m * kSlabBytes)[threadIdx.x] = s.slab[m];
-  }
+template <int NTB>
+__device__ inline void stage_store(const StageRegs& s, uint16_t* x_lds) {
 #pragma unroll
   for (int u = 0; u < NTB; ++u) {
     const int q = threadIdx.x + 256 * u, j = q / (kChunkK / 8), c8 = q % (kChunkK / 8);
@@ -356,19 +343,13 @@ __device__ inline void pass_rows(TokenRows& tr, const Act16& a, int p0, int np) 
   }
 }
 
-// Dynamic LDS of the chunk kernels: NMAT fp16 codebooks, then two buffers, each holding NMAT code
-// slabs and the 64 x kXStride activation tile.
+// Dynamic LDS of the chunk kernels: NMAT fp16 codebooks, then two 64 x kXStride activation tiles.
 template <int NMAT>
 struct ChunkLds {
-  static constexpr int kBuf = NMAT * kSlabBytes + kChunkTok * kXStride * 2;
+  static constexpr int kBuf = kChunkTok * kXStride * 2;
   __device__ static _Float16* cb() { return reinterpret_cast<_Float16*>(chunk_lds); }
-  __device__ static uint8_t* code(int b) { return chunk_lds + NMAT * kCbBytes + b * kBuf; }
-  __device__ static uint16_t* act(int b) {
-    return reinterpret_cast<uint16_t*>(chunk_lds + NMAT * kCbBytes + b * kBuf + NMAT * kSlabBytes);
-  }
-  // the same as LDS addresses
-  static constexpr uint32_t code_addr(int b) { return NMAT * kCbBytes + b * kBuf; }
-  static constexpr uint32_t act_addr(int b) { return NMAT * kCbBytes + b * kBuf + NMAT * kSlabBytes; }
+  __device__ static uint16_t* act(int b) { return reinterpret_cast<uint16_t*>(chunk_lds + NMAT * kCbBytes + b * kBuf); }
+  static constexpr uint32_t act_addr(int b) { return NMAT * kCbBytes + b * kBuf; }   // the same as an LDS address
 };
 
 // The K loop of one pass over NTB 16-pair blocks.  The body is straight-line code (no branch on the
@@ -380,36 +361,50 @@ __device__ inline void k_loop(f32x4 (&acc)[NMAT][4], const uint8_t* const (&mats
                               const Act16& act, const TokenRows& tr) {
   typedef typename Decoder<F16>::frag_t frag_t;
   typedef ChunkLds<NMAT> L;
-  StageRegs<NMAT> st;
-  stage_issue<NMAT, NTB>(st, mats, 0, nrb, rb, act, tr, 0);
-  __syncthreads();  // the previous pass is done with both buffers (and the codebooks are stored)
-  stage_store<NMAT, NTB>(st, L::code(0), L::act(0));
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4;
   const int r = 16 * wave + (lane & 15);
   // the lane's 12 code bytes (12q .. 12q+11 of row r's 48-byte run: groups 4q .. 4q+3) are three
-  // dwords of a staged slab (byte b of the run at (b/16)*1024 + 16r + b%16), and its B operand rows
-  // start at pair lane%16, columns 32q (of the group 4q + kk at step kk)
-  uint32_t coff[2][3];
+  // dwords of the row block's slab in the bank (byte b of the run at (b/16)*1024 + 16r + b%16), read
+  // once, straight into registers; its B operand rows start at pair lane%16, columns 32q (of the
+  // group 4q + kk at step kk)
+  uint32_t coff[3];
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     const int b = 12 * q + 4 * i;
-    const uint32_t o = (uint32_t)((b >> 4) * 1024 + r * 16 + (b & 15));
-    coff[0][i] = L::code_addr(0) + o;
-    coff[1][i] = L::code_addr(1) + o;
+    coff[i] = (uint32_t)((b >> 4) * 1024 + r * 16 + (b & 15));
   }
+  auto load_codes = [&](uint32_t (&d)[NMAT][3], int kt) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        d[m][i] = __builtin_nontemporal_load(
+            reinterpret_cast<const uint32_t*>(mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes + coff[i]));
+  };
+  uint32_t dn[NMAT][3];   // the codes of the next K-tile
+  load_codes(dn, 0);
+  StageRegs st;
+  stage_issue<NTB>(st, act, tr, 0);
+  __syncthreads();  // the previous pass is done with both buffers (and the codebooks are stored)
+  stage_store<NTB>(st, L::act(0));
+  __syncthreads();
   const uint32_t bo = (uint32_t)(((lane & 15) * kXStride + 32 * q) * 2);
   const uint32_t boff[2] = {L::act_addr(0) + bo, L::act_addr(1) + bo};
   for (int kt = 0; kt < ntile; ++kt) {
     const int cur = kt & 1;
     const int nxt = kt + 1 < ntile ? kt + 1 : kt;
-    stage_issue<NMAT, NTB>(st, mats, nxt, nrb, rb, act, tr, nxt * kChunkK);
     uint32_t d[NMAT][3];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int i = 0; i < 3; ++i) d[m][i] = lds_w((cur ? coff[1][i] : coff[0][i]) + m * kSlabBytes);
+      for (int i = 0; i < 3; ++i) d[m][i] = dn[m][i];
+    // the next K-tile's loads: activations (written to LDS at the end of this tile, the wait for
+    // them leaves the code loads issued after them in flight), then codes, held in place here:
+    // left to itself the scheduler sinks them to the end of the tile, where they arrive late
+    stage_issue<NTB>(st, act, tr, nxt * kChunkK);
+    load_codes(dn, nxt);
+    __builtin_amdgcn_sched_barrier(0);
     const uint32_t ba = cur ? boff[1] : boff[0];
     // step kk's LDS reads (three codebook vectors per matrix, one B fragment per pair block) are
     // issued before step kk - 1's sums and MFMAs, so two steps' reads are in flight at a time
@@ -435,7 +430,7 @@ __device__ inline void k_loop(f32x4 (&acc)[NMAT][4], const uint8_t* const (&mats
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) acc[m][tb] = mfma16(a[m], Bq[c][tb], acc[m][tb]);
     }
-    stage_store<NMAT, NTB>(st, L::code(cur ^ 1), L::act(cur ^ 1));
+    stage_store<NTB>(st, L::act(cur ^ 1));
     __syncthreads();
   }
 }
@@ -665,7 +660,7 @@ __global__ __launch_bounds__(256) void k_chunk_combine(const float* __restrict__
 
 static size_t chunk_smem(bool f16, int nmat) {
   (void)f16;
-  return nmat * kCbBytes + 2 * (nmat * kSlabBytes + (size_t)kChunkTok * kXStride * 2);
+  return nmat * kCbBytes + 2 * ((size_t)kChunkTok * kXStride * 2);
 }
 
 hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
