@@ -435,18 +435,17 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 // orders them by logit and id alone.
 // On entry (see topk_prepare): L holds the E logits and -inf up to E rounded to 64 (Ep); g and
 // crank are zero; cl and cid hold -inf and INT_MAX (the padding that (c) compares against); ncand[0]
-// and ncand[1] are zero.  With Ep <= blockDim also: key, the keys below (0 for padding); ckey zero;
-// skey[s] = key[s Ep / 64] (s < 64, a sample); hist zero.
+// is zero.  With Ep <= blockDim also: key, the keys below (0 for padding); ckey zero;
+// skey[s] = key[s Ep / 64] (s < 64, a sample).
 struct TopkScratch {
   int* g;            // [Ep]
   int* crank;        // [Ep]
   int* cid;          // [Ep]
   double* cl;        // [Ep]
-  int* ncand;        // [2]
+  int* ncand;        // [1]
   uint32_t* key;     // [Ep], 16-byte aligned (one-pass form only, as the rest of this list)
   uint32_t* ckey;    // [Ep], 16-byte aligned
   uint32_t* skey;    // [64], 16-byte aligned
-  int* hist;         // [kMaxTopK]
 };
 constexpr int kTopkChunk = 16;
 __device__ __forceinline__ int topk_pad(int E) { return (E + 63) & ~63; }
@@ -466,8 +465,7 @@ template <typename Src>
 __device__ void topk_prepare(double* L, int E, const TopkScratch& ts, Src src) {
   const int Ep = topk_pad(E);
   const bool one = Ep <= (int)blockDim.x;
-  if (threadIdx.x < 2) ts.ncand[threadIdx.x] = 0;
-  if (one && threadIdx.x < kMaxTopK) ts.hist[threadIdx.x] = 0;
+  if (threadIdx.x == 0) ts.ncand[0] = 0;
   const int S = Ep >> 6;   // sample stride
   for (int e = threadIdx.x; e < Ep; e += blockDim.x) {
     const double l = e < E ? src(e) : -INFINITY;
@@ -493,14 +491,13 @@ __device__ void topk_prepare(double* L, int E, const TopkScratch& ts, Src src) {
 //      keys are >= tau, so every expert of rank < k has a key >= tau.
 //  (2) the candidates are the experts with key >= tau (about k E / 64 of them for unordered
 //      logits; all E at worst), compacted in atomic order, which nothing below depends on.
-//  (3) each candidate's count of greater candidate keys: every key above a candidate's belongs to
-//      a candidate, so this is its count of greater keys overall, its rank unless another key
-//      equals its own.  Thread (i, p) counts part p of the candidates (16 keys per step, the same
-//      for the whole wave, so every read is a broadcast); the parts add with LDS atomics, exact.
-//  (4) candidates with count c < k claim sel[c] and count themselves at c; equal keys share one c,
-//      so a second claimant flags a tie, and then each claimant of such a c (rare) adds the
-//      candidates of its key that come first by fp64 logit, then id, and claims that slot instead.
-//      A candidate with c >= k has rank >= k either way.
+//  (3) each candidate's rank: its count of greater candidate keys (every key above a candidate's
+//      belongs to a candidate, so this is its count of greater keys overall), plus the candidates
+//      of an equal key that come first by fp64 logit, then id.  Thread (i, p) counts part p of the
+//      candidates (16 keys per step, the same for the whole wave, so every read is a broadcast;
+//      equal keys are counted on the way, and only a part holding another candidate's equal key,
+//      which is rare, compares logits and ids); the parts add with LDS atomics, exact.
+//  (4) the ranks are distinct, so each candidate of rank r < k writes sel[r].
 __device__ void topk_rank(const double* L, int E, int k, const TopkScratch& ts, int* sel) {
   const int Ep = topk_pad(E);
   const int t = threadIdx.x, lane = t & 63;
@@ -546,14 +543,23 @@ __device__ void topk_rank(const double* L, int E, int k, const TopkScratch& ts, 
     const int span = __builtin_amdgcn_readfirstlane(((Cp + np - 1) / np + 15) & ~15);
     const int j0 = p * span, j1 = j0 + span < Cp ? j0 + span : Cp;
     const uint32_t ki = ts.ckey[i];
-    int c = 0;
+    int c = 0, eq = 0;
     for (int j = j0; j < j1; j += 16) {
       u32x4 kv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) kv[u] = *reinterpret_cast<const u32x4*>(ts.ckey + j + 4 * u);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u) {
         c += (int)(kv[u].x > ki) + (int)(kv[u].y > ki) + (int)(kv[u].z > ki) + (int)(kv[u].w > ki);
+        eq += (int)(kv[u].x == ki) + (int)(kv[u].y == ki) + (int)(kv[u].z == ki) + (int)(kv[u].w == ki);
+      }
+    }
+    if (i >= j0 && i < j1) --eq;   // its own key
+    if (eq > 0) {   // another candidate of this part has the same key: the fp64 logit, then the id
+      const double li = ts.cl[i];
+      const int ei = ts.cid[i];
+      for (int j = j0; j < j1; ++j)
+        if (j != i && ts.ckey[j] == ki) c += (int)((ts.cl[j] > li) || (ts.cl[j] == li && ts.cid[j] < ei));
     }
     if (np == 1) ts.crank[i] = c;
     else atomicAdd(&ts.crank[i], c);
@@ -561,32 +567,7 @@ __device__ void topk_rank(const double* L, int E, int k, const TopkScratch& ts, 
   __syncthreads();
   for (int c = t; c < C; c += blockDim.x) {   // (4)
     const int r = ts.crank[c];
-    if (r < k) {
-      sel[r] = ts.cid[c];
-      if (atomicAdd(&ts.hist[r], 1) > 0) ts.ncand[1] = 1;
-    }
-  }
-  __syncthreads();
-  if (ts.ncand[1]) {   // the same for every thread
-    for (int c = t; c < C; c += blockDim.x) {
-      const int r0 = ts.crank[c];
-      if (r0 < k && ts.hist[r0] > 1) {
-        const uint32_t kc = ts.ckey[c];
-        const double lc = ts.cl[c];
-        const int ic = ts.cid[c];
-        int r = r0;
-        for (int j0 = 0; j0 < Cp; j0 += 4) {   // keys 4 at a time; logits and ids only on a match
-          const u32x4 kv = *reinterpret_cast<const u32x4*>(ts.ckey + j0);
-          const uint32_t kk[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int j = j0 + u;
-            if (kk[u] == kc && j != c) r += (ts.cl[j] > lc) || (ts.cl[j] == lc && ts.cid[j] < ic);
-          }
-        }
-        if (r < k) sel[r] = ic;
-      }
-    }
+    if (r < k) sel[r] = ts.cid[c];
   }
 }
 
@@ -675,10 +656,10 @@ __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ logits
   __shared__ int g[kMaxExperts], crank[kMaxExperts], cid[kMaxExperts];
   // the one-pass form's arrays (Ep <= the 1024 threads)
   __shared__ __attribute__((aligned(16))) uint32_t key[1024], ckey[1024], skey[64];
-  __shared__ int sel[kMaxTopK], hist[kMaxTopK], ncand[2];
+  __shared__ int sel[kMaxTopK], ncand[1];
   const int t = blockIdx.x;
   if (threadIdx.x < kMaxTopK) sel[threadIdx.x] = 0;
-  const TopkScratch ts{g, crank, cid, cl, ncand, key, ckey, skey, hist};
+  const TopkScratch ts{g, crank, cid, cl, ncand, key, ckey, skey};
   topk_prepare(L, E, ts, [&](int e) { return logits[(int64_t)t * E + e]; });
   __syncthreads();
   topk_select(L, E, k, ts, sel);
@@ -1014,7 +995,7 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
   __shared__ int cmax_bits;            // fp16: max squared codebook-entry norm (bits of a float >= 0)
   __shared__ float escale[ITEMS];      // fp16: 2^e_k of each item
   __shared__ int rsel[kMaxTopK];
-  static_assert(DOWN || sizeof(lut) >= 36 * kRouteMaxExperts + 512 + 4 * kMaxTopK, "top-k scratch must fit in the table buffers");
+  static_assert(DOWN || sizeof(lut) >= 36 * kRouteMaxExperts + 512, "top-k scratch must fit in the table buffers");
   static_assert(DOWN || 64 * (NSW + kPipeBuildWaves) >= kRouteMaxExperts, "the top-k takes a thread per expert");
   const int H = bank.H, I = bank.I;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1098,8 +1079,7 @@ __global__ __launch_bounds__(64 * (NSW + kPipeBuildWaves)) void k_table_ws(BankA
     const TopkScratch ts{reinterpret_cast<int*>(scr + 16 * R), reinterpret_cast<int*>(scr + 20 * R),
                          reinterpret_cast<int*>(scr + 24 * R), reinterpret_cast<double*>(scr + 8 * R),
                          reinterpret_cast<int*>(scr + 36 * R + 256), reinterpret_cast<uint32_t*>(scr + 28 * R),
-                         reinterpret_cast<uint32_t*>(scr + 32 * R), reinterpret_cast<uint32_t*>(scr + 36 * R),
-                         reinterpret_cast<int*>(scr + 36 * R + 512)};
+                         reinterpret_cast<uint32_t*>(scr + 32 * R), reinterpret_cast<uint32_t*>(scr + 36 * R)};
     if (threadIdx.x < kMaxTopK) rsel[threadIdx.x] = 0;
     // a thread per expert (E <= kRouteMaxExperts = the workgroup size): logit j is thread j's
     topk_prepare(rl, E, ts, [&](int) { return logit; });
