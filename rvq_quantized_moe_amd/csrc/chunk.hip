@@ -686,12 +686,13 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
   if (f16) hipLaunchKernelGGL(k_chunk_x16, dim3((unsigned)cdiv(nx8, 256)), dim3(256), 0, stream, x, nx8, x16);
   const uint16_t* xg = f16 ? x16 : x;
   // row blocks per workgroup: the codebooks are loaded once per workgroup
-  const int rpw_gu = 2, rpw_dn = 4;
+  constexpr int rpw_gu = 2, rpw_dn = 4;
+  static_assert(rpw_dn % 2 == 0, "paired down steps need an even number of row blocks per group");
   const unsigned g_gu = (unsigned)(cdiv(E * cdiv(I / kChunkRows, rpw_gu), 8) * 8);
   const unsigned g_dn = (unsigned)(cdiv(E * cdiv(H / kChunkRows, rpw_dn), 8) * 8);
   // down takes two row blocks per step when their number is even (rpw_dn is even, so every group
-  // then is too); gate+up, and down in pairs, double-buffer two slabs and the token tile next to two
-  // codebooks (over 64 KiB): allow the larger allocation
+  // then is too); gate+up, and down in pairs, hold two codebooks next to the double-buffered token
+  // tile: the attribute allows that allocation whatever the default limit
   const bool pair_dn = (H / kChunkRows) % 2 == 0;
   for (const void* f : {reinterpret_cast<const void*>(k_chunk_gateup<false>),
                         reinterpret_cast<const void*>(k_chunk_gateup<true>),
