@@ -29,7 +29,9 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kChunkRows = 64;            // weight rows per workgroup (one packed row block)
-constexpr int kChunkTok = 64;             // tokens per MFMA pass (4 blocks of 16)
+constexpr int kChunkTok = 48;             // pairs per MFMA pass (3 blocks of 16; 2 of the 256 experts of a
+                                          // 512-token top-16 chunk take a second pass)
+constexpr int kChunkBlocks = kChunkTok / 16;
 constexpr int kChunkK = 128;              // K columns per staged tile (16 groups = one packed slab)
 constexpr int kXStride = kChunkK + 8;     // staged token row length in 16-bit elements (pad: banks)
 
@@ -269,7 +271,7 @@ __device__ inline f32x4 mfma16(bf16x8 a, half8 b, f32x4 c) { return mfma16(a, __
 // Expert GEMM for one 64-row block of NMAT matrices of one expert (NMAT = 2: gate and up, which
 // share the activations; NMAT = 1: down).  Wave w owns rows [16w, 16w+16) of every matrix.
 //   acc[m][tb] (lane l, i) = sum_k W_m[row0 + 16w + 4(l/16) + i][k] * act[pair tb*16 + l%16][k]
-// Per 128-column K-tile, the 16-bit activations of up to 64 pairs sit in one half of a double
+// Per 128-column K-tile, the 16-bit activations of up to 48 pairs sit in one half of a double
 // buffer in LDS.  The next K-tile's activation loads are issued into registers before this tile's
 // MFMAs and written to the other half after them, so one barrier per K-tile separates the halves
 // and the load latency hides behind the compute.  Codes do not pass through LDS: each lane loads
@@ -291,11 +293,12 @@ __device__ inline int h_exponent(uint32_t maxbits) {
   return e - 15;        // m * 2^-(e-15) < 2^15 < 65504
 }
 
-// Register staging of one K-tile's activations: every thread holds up to 4 16-byte pieces of the
-// tile (64 rows x 16 pieces): piece u covers row (tid + 256u)/16, so piece u is exactly pair block u
+// Register staging of one K-tile's activations: every thread holds up to 3 16-byte pieces of the
+// tile (48 rows x 16 pieces): piece u covers row (tid + 256u)/16, so piece u is exactly pair block u
 // (rows 16u .. 16u+15).  A pass over NTB pair blocks stages pieces u < NTB only: the MFMAs read no
 // other rows.
-constexpr int kActPieces = kChunkTok * (kChunkK / 8) / 256;   // 4 (256-thread workgroups)
+constexpr int kActPieces = kChunkTok * (kChunkK / 8) / 256;   // 3 (256-thread workgroups)
+static_assert(kActPieces == kChunkBlocks, "staging piece u is pair block u");
 
 struct StageRegs {
   u32x4 act[kActPieces];
@@ -343,24 +346,25 @@ __device__ inline void pass_rows(TokenRows& tr, const Act16& a, int p0, int np) 
   }
 }
 
-// Dynamic LDS of the chunk kernels: NMAT fp16 codebooks, then two 64 x kXStride activation tiles.
-template <int NMAT>
+// Dynamic LDS of the chunk kernels: NCB fp16 codebooks (NCB = 1 where the products of a step share
+// one, as down's two row blocks do), then two kChunkTok x kXStride activation tiles.
+template <int NCB>
 struct ChunkLds {
   static constexpr int kBuf = kChunkTok * kXStride * 2;
   __device__ static _Float16* cb() { return reinterpret_cast<_Float16*>(chunk_lds); }
-  __device__ static uint16_t* act(int b) { return reinterpret_cast<uint16_t*>(chunk_lds + NMAT * kCbBytes + b * kBuf); }
-  static constexpr uint32_t act_addr(int b) { return NMAT * kCbBytes + b * kBuf; }   // the same as an LDS address
+  __device__ static uint16_t* act(int b) { return reinterpret_cast<uint16_t*>(chunk_lds + NCB * kCbBytes + b * kBuf); }
+  static constexpr uint32_t act_addr(int b) { return NCB * kCbBytes + b * kBuf; }   // the same as an LDS address
 };
 
 // The K loop of one pass over NTB 16-pair blocks.  The body is straight-line code (no branch on the
 // pair count, and the next tile's loads are issued unconditionally: the last iteration re-reads the
 // last tile into the idle buffer), so the compiler's memory-counter waits stay exact and the
 // prefetch is never drained early.
-template <bool F16, int NMAT, int NTB>
-__device__ inline void k_loop(f32x4 (&acc)[NMAT][4], const uint8_t* const (&mats)[NMAT], int ntile, int nrb, int rb,
+template <bool F16, int NMAT, int NTB, int NCB>
+__device__ inline void k_loop(f32x4 (&acc)[NMAT][kChunkBlocks], const uint8_t* const (&mats)[NMAT], int ntile, int nrb, int rb,
                               const Act16& act, const TokenRows& tr) {
   typedef typename Decoder<F16>::frag_t frag_t;
-  typedef ChunkLds<NMAT> L;
+  typedef ChunkLds<NCB> L;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4;
   const int r = 16 * wave + (lane & 15);
@@ -413,7 +417,8 @@ __device__ inline void k_loop(f32x4 (&acc)[NMAT][4], const uint8_t* const (&mats
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int st = 0; st < 3; ++st) e[m][st] = lds_h8((uint32_t)(m * kCbBytes + 4096 * st) + code_off(d[m], kk, st));
+        for (int st = 0; st < 3; ++st)
+          e[m][st] = lds_h8((uint32_t)((m * NCB / NMAT) * kCbBytes + 4096 * st) + code_off(d[m], kk, st));
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) bq[tb] = lds_h8(ba + (uint32_t)((tb * 16 * kXStride + 8 * kk) * 2));
     };
@@ -436,33 +441,33 @@ __device__ inline void k_loop(f32x4 (&acc)[NMAT][4], const uint8_t* const (&mats
 }
 
 // One workgroup = (expert, row blocks [rb0, rb1)): loads the codebooks once, then per RBS row blocks
-// loops over the expert's pairs 64 at a time and over K.  Matrix m's slab of step rb is at
+// loops over the expert's pairs kChunkTok at a time and over K.  Matrix m's slab of step rb is at
 // mats[m] + (kt * nrb + rb) * kSlabBytes: RBS = 2 with mats = {W, W + one slab} takes row blocks rb
 // and rb + 1 of one matrix W as the two products of a step (they share the staged activations).
-template <bool F16, int NMAT, class Epi, int RBS = 1>
+template <bool F16, int NMAT, class Epi, int RBS = 1, int NCB = NMAT>
 __device__ void expert_tile_gemm(const uint8_t* const (&mats)[NMAT], const float* const (&cbs)[NMAT], int K,
                                  int rb0, int rb1, int nrb, int p_begin, int n_pairs, const Act16& act, const Epi& epi) {
-  typedef ChunkLds<NMAT> L;
+  typedef ChunkLds<NCB> L;
   _Float16* cb_lds = L::cb();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4;
-  for (int m = 0; m < NMAT; ++m) load_codebooks(cb_lds + m * (kCbBytes / 2), cbs[m]);
+  for (int m = 0; m < NCB; ++m) load_codebooks(cb_lds + m * (kCbBytes / 2), cbs[m * NMAT / NCB]);
   const int ntile = (K / 8 + 15) / 16;
   for (int rb = rb0; rb < rb1; rb += RBS)
   for (int pb = 0; pb < n_pairs; pb += kChunkTok) {
     const int np = n_pairs - pb < kChunkTok ? n_pairs - pb : kChunkTok;
     TokenRows tr;
     pass_rows(tr, act, p_begin + pb, np);
-    f32x4 acc[NMAT][4];
+    f32x4 acc[NMAT][kChunkBlocks];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) acc[m][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tb = 0; tb < kChunkBlocks; ++tb) acc[m][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    static_assert(kChunkBlocks == 3, "one case per pair-block count");
     switch ((np + 15) / 16) {
-      case 1: k_loop<F16, NMAT, 1>(acc, mats, ntile, nrb, rb, act, tr); break;
-      case 2: k_loop<F16, NMAT, 2>(acc, mats, ntile, nrb, rb, act, tr); break;
-      case 3: k_loop<F16, NMAT, 3>(acc, mats, ntile, nrb, rb, act, tr); break;
-      default: k_loop<F16, NMAT, 4>(acc, mats, ntile, nrb, rb, act, tr); break;
+      case 1: k_loop<F16, NMAT, 1, NCB>(acc, mats, ntile, nrb, rb, act, tr); break;
+      case 2: k_loop<F16, NMAT, 2, NCB>(acc, mats, ntile, nrb, rb, act, tr); break;
+      default: k_loop<F16, NMAT, kChunkBlocks, NCB>(acc, mats, ntile, nrb, rb, act, tr); break;
     }
     epi(acc, p_begin + pb, np, rb * kChunkRows + 16 * wave + 4 * q, lane & 15);
   }
@@ -485,9 +490,9 @@ struct GateUpEpi {
   float* h;
   uint16_t* h16;
   int I;
-  __device__ void operator()(const f32x4 (&acc)[2][4], int p0, int np, int rloc, int col) const {
+  __device__ void operator()(const f32x4 (&acc)[2][kChunkBlocks], int p0, int np, int rloc, int col) const {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int tb = 0; tb < kChunkBlocks; ++tb) {
       const int j = tb * 16 + col;
       if (j >= np) continue;
       float hv[4];
@@ -512,9 +517,9 @@ struct DownEpi {
   float* y;
   const uint32_t* hmax;
   int H;
-  __device__ void operator()(const f32x4 (&acc)[NB][4], int p0, int np, int rloc, int col) const {
+  __device__ void operator()(const f32x4 (&acc)[NB][kChunkBlocks], int p0, int np, int rloc, int col) const {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int tb = 0; tb < kChunkBlocks; ++tb) {
       const int j = tb * 16 + col;
       if (j >= np) continue;
       const float sc = F16 ? ldexpf(1.f, h_exponent(hmax[p0 + j])) : 1.f;
@@ -578,7 +583,7 @@ __global__ __launch_bounds__(256) void k_chunk_down(BankArgs bank, const int32_t
     const uint8_t* const mats[2] = {down, down + kSlabBytes};
     const float* const cbs[2] = {cb, cb};
     DownEpi<F16, 2> epi{y, hmax, H};
-    expert_tile_gemm<F16, 2, DownEpi<F16, 2>, 2>(mats, cbs, I, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
+    expert_tile_gemm<F16, 2, DownEpi<F16, 2>, 2, 1>(mats, cbs, I, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
   } else {
     const uint8_t* const mats[1] = {down};
     const float* const cbs[1] = {cb};
@@ -658,9 +663,9 @@ __global__ __launch_bounds__(256) void k_chunk_combine(const float* __restrict__
   out[(int64_t)t * H + r] = acc;
 }
 
-static size_t chunk_smem(bool f16, int nmat) {
+static size_t chunk_smem(bool f16, int ncb) {   // ncb codebooks in LDS
   (void)f16;
-  return nmat * kCbBytes + 2 * ((size_t)kChunkTok * kXStride * 2);
+  return ncb * kCbBytes + 2 * ((size_t)kChunkTok * kXStride * 2);
 }
 
 hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t stride, int E, int H, int I,
@@ -707,7 +712,7 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
                        pair_token, h, h16, rpw_gu, status);
     hipLaunchKernelGGL(k_chunk_h16, dim3((unsigned)P), dim3(256), 0, stream, h, hmax, I, h16);
     if (pair_dn)
-      hipLaunchKernelGGL((k_chunk_down<true, true>), dim3(g_dn), dim3(256), chunk_smem(true, 2), stream, bank, offsets,
+      hipLaunchKernelGGL((k_chunk_down<true, true>), dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets,
                          h16, hmax, ybuf, rpw_dn, status);
     else
       hipLaunchKernelGGL((k_chunk_down<true, false>), dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets,
@@ -716,7 +721,7 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
     hipLaunchKernelGGL(k_chunk_gateup<false>, dim3(g_gu), dim3(256), chunk_smem(false, 2), stream, bank, xg, offsets,
                        pair_token, h, h16, rpw_gu, status);
     if (pair_dn)
-      hipLaunchKernelGGL((k_chunk_down<false, true>), dim3(g_dn), dim3(256), chunk_smem(false, 2), stream, bank,
+      hipLaunchKernelGGL((k_chunk_down<false, true>), dim3(g_dn), dim3(256), chunk_smem(false, 1), stream, bank,
                          offsets, h16, hmax, ybuf, rpw_dn, status);
     else
       hipLaunchKernelGGL((k_chunk_down<false, false>), dim3(g_dn), dim3(256), chunk_smem(false, 1), stream, bank,
