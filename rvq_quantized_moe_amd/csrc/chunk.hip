@@ -691,7 +691,7 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
   if (f16) hipLaunchKernelGGL(k_chunk_x16, dim3((unsigned)cdiv(nx8, 256)), dim3(256), 0, stream, x, nx8, x16);
   const uint16_t* xg = f16 ? x16 : x;
   // row blocks per workgroup: the codebooks are loaded once per workgroup
-  constexpr int rpw_gu = 2, rpw_dn = 4;
+  constexpr int rpw_gu = 1, rpw_dn = 4;
   static_assert(rpw_dn % 2 == 0, "paired down steps need an even number of row blocks per group");
   const unsigned g_gu = (unsigned)(cdiv(E * cdiv(I / kChunkRows, rpw_gu), 8) * 8);
   const unsigned g_dn = (unsigned)(cdiv(E * cdiv(H / kChunkRows, rpw_dn), 8) * 8);
