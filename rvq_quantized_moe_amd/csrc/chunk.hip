@@ -485,26 +485,30 @@ __device__ inline int xcd_major(int nwork) {
 
 // Gate/up: h[p][row] = silu(g) * u.  fp16 tiles: fp32 h (k_chunk_h16 scales it per pair); bf16
 // tiles: bf16(h) straight into the down operand (the same rounding k_chunk_h16 would apply).
-template <bool F16>
-struct GateUpEpi {
+template <bool F16, int NB>
+struct GateUpEpi {   // products {gate rb .. rb+NB-1, up rb .. rb+NB-1}: h of NB consecutive row blocks
   float* h;
   uint16_t* h16;
   int I;
-  __device__ void operator()(const f32x4 (&acc)[2][kChunkBlocks], int p0, int np, int rloc, int col) const {
+  __device__ void operator()(const f32x4 (&acc)[2 * NB][kChunkBlocks], int p0, int np, int rloc, int col) const {
 #pragma unroll
     for (int tb = 0; tb < kChunkBlocks; ++tb) {
       const int j = tb * 16 + col;
       if (j >= np) continue;
-      float hv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float g = acc[0][tb][i], u = acc[1][tb][i];
-        hv[i] = g / (1.f + expf(-g)) * u;
-      }
-      if constexpr (F16) {
-        *reinterpret_cast<f32x4*>(h + (int64_t)(p0 + j) * I + rloc) = f32x4{hv[0], hv[1], hv[2], hv[3]};
-      } else {
-        *reinterpret_cast<u32x2*>(h16 + (int64_t)(p0 + j) * I + rloc) = u32x2{pack_b2(hv[0], hv[1]), pack_b2(hv[2], hv[3])};
+      for (int b = 0; b < NB; ++b) {
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float g = acc[b][tb][i], u = acc[NB + b][tb][i];
+          hv[i] = g / (1.f + expf(-g)) * u;
+        }
+        const int r = rloc + b * kChunkRows;
+        if constexpr (F16) {
+          *reinterpret_cast<f32x4*>(h + (int64_t)(p0 + j) * I + r) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+        } else {
+          *reinterpret_cast<u32x2*>(h16 + (int64_t)(p0 + j) * I + r) = u32x2{pack_b2(hv[0], hv[1]), pack_b2(hv[2], hv[3])};
+        }
       }
     }
   }
@@ -539,7 +543,9 @@ __device__ inline bool chunk_lds_ok(int32_t* status) {
   return false;
 }
 
-template <bool F16>
+// PAIR: two row blocks of gate and up per step, four products sharing each B fragment (an even
+// number of row blocks, groups of rpw even).
+template <bool F16, bool PAIR>
 __global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint16_t* __restrict__ x16,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ pair_token, float* __restrict__ h,
@@ -553,13 +559,22 @@ __global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint1
   const int rb1 = rb0 + rpw < nrb ? rb0 + rpw : nrb;
   const int p_begin = offsets[e], n_pairs = offsets[e + 1] - p_begin;
   if (n_pairs == 0) return;
-  const uint8_t* rec = bank.codes + (int64_t)e * bank.stride;
-  const uint8_t* const mats[2] = {rec, rec + packed_bytes(I, H)};
-  const float* const cbs[2] = {bank.cb + ((int64_t)e * 3 + 0) * kCodebookFloats,
-                               bank.cb + ((int64_t)e * 3 + 1) * kCodebookFloats};
+  const uint8_t* gate = bank.codes + (int64_t)e * bank.stride;
+  const uint8_t* up = gate + packed_bytes(I, H);
+  const float* gcb = bank.cb + ((int64_t)e * 3 + 0) * kCodebookFloats;
+  const float* ucb = bank.cb + ((int64_t)e * 3 + 1) * kCodebookFloats;
   const Act16 act{x16, pair_token, H};
-  GateUpEpi<F16> epi{h, h16, I};
-  expert_tile_gemm<F16, 2>(mats, cbs, H, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
+  if constexpr (PAIR) {
+    const uint8_t* const mats[4] = {gate, gate + kSlabBytes, up, up + kSlabBytes};
+    const float* const cbs[4] = {gcb, gcb, ucb, ucb};
+    GateUpEpi<F16, 2> epi{h, h16, I};
+    expert_tile_gemm<F16, 4, GateUpEpi<F16, 2>, 2, 2>(mats, cbs, H, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
+  } else {
+    const uint8_t* const mats[2] = {gate, up};
+    const float* const cbs[2] = {gcb, ucb};
+    GateUpEpi<F16, 1> epi{h, h16, I};
+    expert_tile_gemm<F16, 2>(mats, cbs, H, rb0, rb1, nrb, p_begin, n_pairs, act, epi);
+  }
 }
 
 // PAIR: two row blocks per step (an even number of row blocks, groups of rpw even).
@@ -691,16 +706,18 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
   if (f16) hipLaunchKernelGGL(k_chunk_x16, dim3((unsigned)cdiv(nx8, 256)), dim3(256), 0, stream, x, nx8, x16);
   const uint16_t* xg = f16 ? x16 : x;
   // row blocks per workgroup: the codebooks are loaded once per workgroup
-  constexpr int rpw_gu = 1, rpw_dn = 4;
-  static_assert(rpw_dn % 2 == 0, "paired down steps need an even number of row blocks per group");
+  constexpr int rpw_gu = 2, rpw_dn = 4;
+  static_assert(rpw_gu % 2 == 0 && rpw_dn % 2 == 0, "paired steps need an even number of row blocks per group");
   const unsigned g_gu = (unsigned)(cdiv(E * cdiv(I / kChunkRows, rpw_gu), 8) * 8);
   const unsigned g_dn = (unsigned)(cdiv(E * cdiv(H / kChunkRows, rpw_dn), 8) * 8);
   // down takes two row blocks per step when their number is even (rpw_dn is even, so every group
   // then is too); gate+up, and down in pairs, hold two codebooks next to the double-buffered token
   // tile: the attribute allows that allocation whatever the default limit
-  const bool pair_dn = (H / kChunkRows) % 2 == 0;
-  for (const void* f : {reinterpret_cast<const void*>(k_chunk_gateup<false>),
-                        reinterpret_cast<const void*>(k_chunk_gateup<true>),
+  const bool pair_dn = (H / kChunkRows) % 2 == 0, pair_gu = (I / kChunkRows) % 2 == 0;
+  for (const void* f : {reinterpret_cast<const void*>(k_chunk_gateup<false, false>),
+                        reinterpret_cast<const void*>(k_chunk_gateup<true, false>),
+                        reinterpret_cast<const void*>(k_chunk_gateup<false, true>),
+                        reinterpret_cast<const void*>(k_chunk_gateup<true, true>),
                         reinterpret_cast<const void*>(k_chunk_down<false, true>),
                         reinterpret_cast<const void*>(k_chunk_down<true, true>)}) {
     const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)chunk_smem(f16, 2));
@@ -708,8 +725,12 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
   }
   const int64_t P = (int64_t)T * k;
   if (f16) {
-    hipLaunchKernelGGL(k_chunk_gateup<true>, dim3(g_gu), dim3(256), chunk_smem(true, 2), stream, bank, xg, offsets,
-                       pair_token, h, h16, rpw_gu, status);
+    if (pair_gu)
+      hipLaunchKernelGGL((k_chunk_gateup<true, true>), dim3(g_gu), dim3(256), chunk_smem(true, 2), stream, bank, xg,
+                         offsets, pair_token, h, h16, rpw_gu, status);
+    else
+      hipLaunchKernelGGL((k_chunk_gateup<true, false>), dim3(g_gu), dim3(256), chunk_smem(true, 2), stream, bank, xg,
+                         offsets, pair_token, h, h16, rpw_gu, status);
     hipLaunchKernelGGL(k_chunk_h16, dim3((unsigned)P), dim3(256), 0, stream, h, hmax, I, h16);
     if (pair_dn)
       hipLaunchKernelGGL((k_chunk_down<true, true>), dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets,
@@ -718,8 +739,12 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
       hipLaunchKernelGGL((k_chunk_down<true, false>), dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets,
                          h16, hmax, ybuf, rpw_dn, status);
   } else {
-    hipLaunchKernelGGL(k_chunk_gateup<false>, dim3(g_gu), dim3(256), chunk_smem(false, 2), stream, bank, xg, offsets,
-                       pair_token, h, h16, rpw_gu, status);
+    if (pair_gu)
+      hipLaunchKernelGGL((k_chunk_gateup<false, true>), dim3(g_gu), dim3(256), chunk_smem(false, 2), stream, bank, xg,
+                         offsets, pair_token, h, h16, rpw_gu, status);
+    else
+      hipLaunchKernelGGL((k_chunk_gateup<false, false>), dim3(g_gu), dim3(256), chunk_smem(false, 2), stream, bank, xg,
+                         offsets, pair_token, h, h16, rpw_gu, status);
     if (pair_dn)
       hipLaunchKernelGGL((k_chunk_down<false, true>), dim3(g_dn), dim3(256), chunk_smem(false, 1), stream, bank,
                          offsets, h16, hmax, ybuf, rpw_dn, status);

@@ -76,11 +76,13 @@ def test_chunk_crowded_experts_and_residual(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_chunk_odd_row_block_count(dtype):
-    """H = 192: three 64-row blocks of the down matrix, so down takes one row block per step (an even
-    count takes two, as in the other cases); K = 192 also leaves a partial K-tile for gate/up."""
-    say(f"chunk E=8 H=192 I=128 T=40 k=2 {dtype}")
-    err = run_case(0xC5, 8, 192, 128, 40, 2, dtype, residual=True)[0]
+@pytest.mark.parametrize("H,I", [(192, 128), (128, 192)])
+def test_chunk_odd_row_block_count(dtype, H, I):
+    """Three 64-row blocks: H = 192 makes down take one row block per step, I = 192 makes gate/up take
+    one row block of each matrix per step (an even count takes two, as in the other cases); a K of 192
+    also leaves a partial K-tile (gate/up for H = 192, down for I = 192)."""
+    say(f"chunk E=8 H={H} I={I} T=40 k=2 {dtype}")
+    err = run_case(0xC5, 8, H, I, 40, 2, dtype, residual=True)[0]
     assert err <= TOL[dtype]
 
 
