@@ -378,13 +378,14 @@ __device__ inline void k_loop(f32x4 (&acc)[NMAT][kChunkBlocks], const uint8_t* c
     const int b = 12 * q + 4 * i;
     coff[i] = (uint32_t)((b >> 4) * 1024 + r * 16 + (b & 15));
   }
+  // ordinary loads: each 16-byte unit of a slab is read by up to three of the wave's dword loads,
+  // and with non-temporal loads the L2 fetched its line again for each (8 % more HBM reads)
   auto load_codes = [&](uint32_t (&d)[NMAT][3], int kt) {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int i = 0; i < 3; ++i)
-        d[m][i] = __builtin_nontemporal_load(
-            reinterpret_cast<const uint32_t*>(mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes + coff[i]));
+        d[m][i] = *reinterpret_cast<const uint32_t*>(mats[m] + ((int64_t)kt * nrb + rb) * kSlabBytes + coff[i]);
   };
   uint32_t dn[NMAT][3];   // the codes of the next K-tile
   load_codes(dn, 0);
