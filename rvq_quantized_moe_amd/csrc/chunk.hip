@@ -268,8 +268,9 @@ __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) { return __builtin_a
 __device__ inline f32x4 mfma16(bf16x8 a, half8 b, f32x4 c) { return mfma16(a, __builtin_bit_cast(bf16x8, b), c); }
 
 // ---------------------------------------------------------------------------------------------
-// Expert GEMM for one 64-row block of NMAT matrices of one expert (NMAT = 2: gate and up, which
-// share the activations; NMAT = 1: down).  Wave w owns rows [16w, 16w+16) of every matrix.
+// Expert GEMM for NMAT products of one expert that share the activations: 64-row blocks of its
+// matrices (gate/up: two row blocks of gate and of up, NMAT = 4, or one of each, NMAT = 2; down: two
+// row blocks, NMAT = 2, or one).  Wave w owns rows [16w, 16w+16) of every product's block.
 //   acc[m][tb] (lane l, i) = sum_k W_m[row0 + 16w + 4(l/16) + i][k] * act[pair tb*16 + l%16][k]
 // Per 128-column K-tile, the 16-bit activations of up to 48 pairs sit in one half of a double
 // buffer in LDS.  The next K-tile's activation loads are issued into registers before this tile's
