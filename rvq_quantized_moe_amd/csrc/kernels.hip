@@ -677,6 +677,61 @@ __global__ __launch_bounds__(256) void k_router_norm_logits(const uint16_t* __re
   __shared__ double red[4];
   __shared__ double red2[4];
   const int e = blockIdx.x;
+  const int per = (H + E - 1) / E;
+  constexpr int SU = 32;   // h values per thread for the sum of squares in one round of loads
+  if (vec && H <= 256 * SU && H / 8 <= 256 * kRouterUnroll && per <= 256) {
+    // The same sums in the same order as below, with every load issued before the first product:
+    // the sum of squares's values (h = tid + 256 u), the router row's and h's 8-element pieces
+    // (q = tid + 256 u, as router_dot), and the element of n this thread writes.  One round trip
+    // to memory instead of four.
+    const int tid = threadIdx.x;
+    const uint16_t* wr = w + (int64_t)e * H;
+    const int n8 = H / 8;
+    float v[SU];
+#pragma unroll
+    for (int u = 0; u < SU; ++u) v[u] = h[min(tid + 256 * u, H - 1)];
+    u32x4 wv[kRouterUnroll];
+    RawX8<float> xv[kRouterUnroll];
+#pragma unroll
+    for (int u = 0; u < kRouterUnroll; ++u) {
+      const int q = min(tid + 256 * u, n8 - 1);
+      wv[u] = *reinterpret_cast<const u32x4*>(wr + q * 8);
+      xv[u].load(h + q * 8);
+    }
+    const int jn = min(e * per + tid, H - 1);
+    const bool own = tid < per && e * per + tid < H;
+    const float hn = h[jn];
+    __builtin_amdgcn_sched_barrier(0);   // every load above is issued before the first product
+    double ss = 0.0;
+#pragma unroll
+    for (int u = 0; u < SU; ++u)
+      if (tid + 256 * u < H) ss = fma((double)v[u], (double)v[u], ss);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const double tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const double inv = 1.0 / sqrt(tot / (double)H + (double)eps);
+    double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+    for (int u = 0; u < kRouterUnroll; ++u) {
+      if (tid + 256 * u < n8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a0 = fma(bf16_to_f64((uint16_t)(wv[u][j] & 0xffffu)), (double)(float)(xv[u].get(2 * j) * inv), a0);
+          a1 = fma(bf16_to_f64((uint16_t)(wv[u][j] >> 16)), (double)(float)(xv[u].get(2 * j + 1) * inv), a1);
+        }
+      }
+    }
+    double acc = a0 + a1;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if ((tid & 63) == 0) red2[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) logits[e] = (red2[0] + red2[1]) + (red2[2] + red2[3]);
+    if (own) n[jn] = (float)((double)hn * inv);
+    return;
+  }
   double ss = sum_squares(h, H);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
@@ -691,7 +746,6 @@ __global__ __launch_bounds__(256) void k_router_norm_logits(const uint16_t* __re
   if ((threadIdx.x & 63) == 0) red2[threadIdx.x >> 6] = acc;
   __syncthreads();
   if (threadIdx.x == 0) logits[e] = (red2[0] + red2[1]) + (red2[2] + red2[3]);
-  const int per = (H + E - 1) / E;
   for (int j = e * per + (int)threadIdx.x; j < (e + 1) * per && j < H; j += 256) n[j] = (float)((double)h[j] * inv);
 }
 
