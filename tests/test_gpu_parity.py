@@ -812,6 +812,28 @@ def test_routed_decode_small_expert_count():
         assert torch.equal(y, rvq.moe_layer_forward(bank, x, ids2[0], gates2[0]))
 
 
+def test_block_decode_few_experts_and_unaligned_h():
+    """The norm-folding router's loop form (taken when a workgroup writes more than 256 elements of
+    n, here 1434 with 5 experts, and when h is not 16-byte aligned) equals rvq_rmsnorm followed by
+    the routed decode bit for bit, as its one-round form does on the full layer."""
+    E, k = 5, 3
+    say("block decode, 5 experts, h aligned and offset by one float")
+    bank = upload_bank(synth.SEED_EXPERT, 7, E)
+    _, w = router(synth.SEED_EXPERT, 7, E, HIDDEN)
+    ws = rvq.make_moe_workspace(bank, 1, k, "f32")
+    buf = torch.empty(HIDDEN + 4, dtype=torch.float32, device="cuda")
+    h = torch.from_numpy(synth.activation_f32(synth.SEED_EXPERT, 71, HIDDEN))
+    for off in (0, 1):
+        hd = buf[off:off + HIDDEN]
+        hd.copy_(h)
+        y, ids, gates, logits = rvq.moe_block_decode(bank, w, hd, k, 1e-6, workspace=ws)
+        n = rvq.rmsnorm(hd[None, :], 1e-6)[0]
+        y2, ids2, gates2, logits2 = rvq.moe_decode_routed(bank, w, n, k, residual=hd, workspace=ws)
+        assert torch.equal(logits, logits2) and torch.equal(ids, ids2) and torch.equal(gates, gates2), off
+        assert torch.equal(y, y2), off
+    assert rvq.check_device_status(ws) == 0
+
+
 # ---------------------------------------------------------------- other layer shapes
 
 @pytest.mark.parametrize("H,I,E,k", [
