@@ -36,11 +36,11 @@ constexpr int kChunkK = 128;              // K columns per staged tile (16 group
 constexpr int kXStride = kChunkK + 8;     // staged token row length in 16-bit elements (pad: banks)
 
 struct ChunkWs {
-  size_t status_off, offsets_off, pair_token_off, pair_pos_off, hmax_off, h_off, y_off, x16_off, h16_off, total;
+  size_t status_off, offsets_off, order_off, pair_token_off, pair_pos_off, hmax_off, h_off, y_off, x16_off, h16_off, total;
 };
 
 // Workspace layout of the chunk path (all 256-byte aligned):
-//   status int32 | offsets int32[E+1] | pair_token int32[P] | pair_pos int32[T*k]
+//   status int32 | offsets int32[E+1] | order int32[E] | pair_token int32[P] | pair_pos int32[T*k]
 //   | hmax uint32[P] (bit pattern of max|h| per pair) | h fp32 [P][I] (fp16 tiles) | y fp32 [P][H]
 //   | x16 fp16 [T][H] (the chunk in fp16, for fp16 tiles) | h16 16-bit [P][I] (h as the down operand)
 ChunkWs chunk_ws_layout(int E, int H, int I, int T, int k) {
@@ -49,7 +49,8 @@ ChunkWs chunk_ws_layout(int E, int H, int I, int T, int k) {
   ChunkWs w;
   w.status_off = 0;
   w.offsets_off = 256;
-  w.pair_token_off = w.offsets_off + up((size_t)(E + 1) * 4);
+  w.order_off = w.offsets_off + up((size_t)(E + 1) * 4);
+  w.pair_token_off = w.order_off + up((size_t)E * 4);
   w.pair_pos_off = w.pair_token_off + up(P * 4);
   w.hmax_off = w.pair_pos_off + up(P * 4);
   w.h_off = w.hmax_off + up(P * 4);
@@ -66,9 +67,13 @@ size_t chunk_workspace_bytes(int E, int H, int I, int T, int k) { return chunk_w
 // Bucketing (one workgroup).  Pair (t, i) = token t's i-th selected expert e.  Pairs of expert e
 // are placed at offsets[e] + (number of earlier tokens that also selected e): a per-expert token
 // bitmap in LDS answers that with popcounts, so the order (token ascending within an expert) and
-// every position are deterministic.
+// every position are deterministic.  It also writes the order in which the expert kernels take the
+// experts: by pair count, the largest first (in steps of 4 pairs, all counts from 252 up together),
+// so that the longest work items start first.  Within a step the order is that of the atomics; it
+// decides only when and where a work item runs, never what it computes.
 __global__ __launch_bounds__(1024) void k_chunk_bucket(const int32_t* __restrict__ ids, int T, int k, int E,
-                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ pair_token,
+                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ order,
+                                                       int32_t* __restrict__ pair_token,
                                                        int32_t* __restrict__ pair_pos, int32_t* __restrict__ status) {
   extern __shared__ uint32_t sm[];
   const int words = (T + 31) / 32;
@@ -139,7 +144,32 @@ __global__ __launch_bounds__(1024) void k_chunk_bucket(const int32_t* __restrict
     cnt[E] = run;
     offsets[E] = run;
   }
+  __shared__ int obase[64], ofill[64];
+  if (threadIdx.x < 64) {
+    obase[threadIdx.x] = 0;
+    ofill[threadIdx.x] = 0;
+  }
   __syncthreads();
+  auto bin_of = [](int cc) { return 63 - (cc >> 2 < 63 ? cc >> 2 : 63); };
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j < per && e0 + j < E) atomicAdd(&obase[bin_of(c[j])], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int s = 0;
+    for (int b = 0; b < 64; ++b) {
+      const int n = obase[b];
+      obase[b] = s;
+      s += n;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j < per && e0 + j < E) {
+      const int b = bin_of(c[j]);
+      order[obase[b] + atomicAdd(&ofill[b], 1)] = e0 + j;
+    }
   for (int p0 = threadIdx.x; p0 < P; p0 += kBatch * blockDim.x) {
     int eb[kBatch];
 #pragma unroll
@@ -485,6 +515,25 @@ __device__ inline int xcd_major(int nwork) {
   return w < nwork ? w : -1;
 }
 
+// This workgroup's expert and row-block group.  When the experts split evenly over the 8 XCDs, XCD
+// x takes the experts of order ranks x, x + 8, x + 16, ... in rank order (the heaviest first on
+// every XCD, and each XCD's share of the heavy ones even), all ngrp groups of one expert together;
+// otherwise the experts in id order, XCD-major.  Returns false for padding workgroups.
+__device__ inline bool chunk_work(const int32_t* __restrict__ order, int E, int ngrp, int& e, int& grp) {
+  if ((E & 7) == 0) {
+    const int li = (int)(blockIdx.x >> 3);
+    if (li >= (E >> 3) * ngrp) return false;
+    grp = li % ngrp;
+    e = order[(li / ngrp) * 8 + (int)(blockIdx.x & 7)];
+    return true;
+  }
+  const int w = xcd_major(E * ngrp);
+  if (w < 0) return false;
+  e = w / ngrp;
+  grp = w % ngrp;
+  return true;
+}
+
 // Gate/up: h[p][row] = silu(g) * u.  fp16 tiles: fp32 h (k_chunk_h16 scales it per pair); bf16
 // tiles: bf16(h) straight into the down operand (the same rounding k_chunk_h16 would apply).
 template <bool F16, int NB>
@@ -550,14 +599,15 @@ __device__ inline bool chunk_lds_ok(int32_t* status) {
 template <bool F16, bool PAIR>
 __global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint16_t* __restrict__ x16,
                                                       const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ order,
                                                       const int32_t* __restrict__ pair_token, float* __restrict__ h,
                                                       uint16_t* __restrict__ h16, int rpw, int32_t* __restrict__ status) {
   if (!chunk_lds_ok(status)) return;
   const int H = bank.H, I = bank.I;
   const int nrb = I / kChunkRows, ngrp = (nrb + rpw - 1) / rpw;
-  const int w = xcd_major(bank.E * ngrp);
-  if (w < 0) return;
-  const int e = w / ngrp, rb0 = (w % ngrp) * rpw;
+  int e, grp;
+  if (!chunk_work(order, bank.E, ngrp, e, grp)) return;
+  const int rb0 = grp * rpw;
   const int rb1 = rb0 + rpw < nrb ? rb0 + rpw : nrb;
   const int p_begin = offsets[e], n_pairs = offsets[e + 1] - p_begin;
   if (n_pairs == 0) return;
@@ -582,14 +632,15 @@ __global__ __launch_bounds__(256) void k_chunk_gateup(BankArgs bank, const uint1
 // PAIR: two row blocks per step (an even number of row blocks, groups of rpw even).
 template <bool F16, bool PAIR>
 __global__ __launch_bounds__(256) void k_chunk_down(BankArgs bank, const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ order,
                                                     const uint16_t* __restrict__ h16, const uint32_t* __restrict__ hmax,
                                                     float* __restrict__ y, int rpw, int32_t* __restrict__ status) {
   if (!chunk_lds_ok(status)) return;
   const int H = bank.H, I = bank.I;
   const int nrb = H / kChunkRows, ngrp = (nrb + rpw - 1) / rpw;
-  const int w = xcd_major(bank.E * ngrp);
-  if (w < 0) return;
-  const int e = w / ngrp, rb0 = (w % ngrp) * rpw;
+  int e, grp;
+  if (!chunk_work(order, bank.E, ngrp, e, grp)) return;
+  const int rb0 = grp * rpw;
   const int rb1 = rb0 + rpw < nrb ? rb0 + rpw : nrb;
   const int p_begin = offsets[e], n_pairs = offsets[e + 1] - p_begin;
   if (n_pairs == 0) return;
@@ -692,6 +743,7 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
   uint8_t* base = static_cast<uint8_t*>(ws);
   int32_t* status = reinterpret_cast<int32_t*>(base + w.status_off);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + w.offsets_off);
+  int32_t* order = reinterpret_cast<int32_t*>(base + w.order_off);
   int32_t* pair_token = reinterpret_cast<int32_t*>(base + w.pair_token_off);
   int32_t* pair_pos = reinterpret_cast<int32_t*>(base + w.pair_pos_off);
   uint32_t* hmax = reinterpret_cast<uint32_t*>(base + w.hmax_off);
@@ -701,8 +753,13 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
   uint16_t* h16 = reinterpret_cast<uint16_t*>(base + w.h16_off);
   BankArgs bank{codes, cb, stride, E, H, I};
   const size_t bucket_smem = ((size_t)E * ((T + 31) / 32) + E + 1) * 4;
-  hipLaunchKernelGGL(k_chunk_bucket, dim3(1), dim3(1024), bucket_smem, stream, ids, T, k, E, offsets, pair_token,
-                     pair_pos, status);
+  {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chunk_bucket),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bucket_smem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_chunk_bucket, dim3(1), dim3(1024), bucket_smem, stream, ids, T, k, E, offsets, order,
+                     pair_token, pair_pos, status);
   // the gate/up operand: the tokens themselves (bf16 tiles) or their fp16 copy
   const int64_t nx8 = (int64_t)T * H / 8;
   if (f16) hipLaunchKernelGGL(k_chunk_x16, dim3((unsigned)cdiv(nx8, 256)), dim3(256), 0, stream, x, nx8, x16);
@@ -729,30 +786,30 @@ hipError_t launch_moe_chunk(const uint8_t* codes, const float* cb, int64_t strid
   if (f16) {
     if (pair_gu)
       hipLaunchKernelGGL((k_chunk_gateup<true, true>), dim3(g_gu), dim3(256), chunk_smem(true, 2), stream, bank, xg,
-                         offsets, pair_token, h, h16, rpw_gu, status);
+                         offsets, order, pair_token, h, h16, rpw_gu, status);
     else
       hipLaunchKernelGGL((k_chunk_gateup<true, false>), dim3(g_gu), dim3(256), chunk_smem(true, 2), stream, bank, xg,
-                         offsets, pair_token, h, h16, rpw_gu, status);
+                         offsets, order, pair_token, h, h16, rpw_gu, status);
     hipLaunchKernelGGL(k_chunk_h16, dim3((unsigned)P), dim3(256), 0, stream, h, hmax, I, h16);
     if (pair_dn)
-      hipLaunchKernelGGL((k_chunk_down<true, true>), dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets,
+      hipLaunchKernelGGL((k_chunk_down<true, true>), dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets, order,
                          h16, hmax, ybuf, rpw_dn, status);
     else
-      hipLaunchKernelGGL((k_chunk_down<true, false>), dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets,
+      hipLaunchKernelGGL((k_chunk_down<true, false>), dim3(g_dn), dim3(256), chunk_smem(true, 1), stream, bank, offsets, order,
                          h16, hmax, ybuf, rpw_dn, status);
   } else {
     if (pair_gu)
       hipLaunchKernelGGL((k_chunk_gateup<false, true>), dim3(g_gu), dim3(256), chunk_smem(false, 2), stream, bank, xg,
-                         offsets, pair_token, h, h16, rpw_gu, status);
+                         offsets, order, pair_token, h, h16, rpw_gu, status);
     else
       hipLaunchKernelGGL((k_chunk_gateup<false, false>), dim3(g_gu), dim3(256), chunk_smem(false, 2), stream, bank, xg,
-                         offsets, pair_token, h, h16, rpw_gu, status);
+                         offsets, order, pair_token, h, h16, rpw_gu, status);
     if (pair_dn)
       hipLaunchKernelGGL((k_chunk_down<false, true>), dim3(g_dn), dim3(256), chunk_smem(false, 1), stream, bank,
-                         offsets, h16, hmax, ybuf, rpw_dn, status);
+                         offsets, order, h16, hmax, ybuf, rpw_dn, status);
     else
       hipLaunchKernelGGL((k_chunk_down<false, false>), dim3(g_dn), dim3(256), chunk_smem(false, 1), stream, bank,
-                         offsets, h16, hmax, ybuf, rpw_dn, status);
+                         offsets, order, h16, hmax, ybuf, rpw_dn, status);
   }
   hipLaunchKernelGGL(k_chunk_combine, dim3((unsigned)cdiv(H, 256), (unsigned)T), dim3(256), 0, stream, ybuf, pair_pos,
                      gates, k, H, residual, y);
