@@ -515,16 +515,18 @@ __device__ inline int xcd_major(int nwork) {
   return w < nwork ? w : -1;
 }
 
-// This workgroup's expert and row-block group.  When the experts split evenly over the 8 XCDs, XCD
-// x takes the experts of order ranks x, x + 8, x + 16, ... in rank order (the heaviest first on
-// every XCD, and each XCD's share of the heavy ones even), all ngrp groups of one expert together;
-// otherwise the experts in id order, XCD-major.  Returns false for padding workgroups.
+// This workgroup's expert and row-block group.  When the experts split evenly over the 8 XCDs, the
+// order ranks are dealt out in groups of 8, one per XCD, forwards in even groups and backwards in
+// odd ones: each XCD takes its experts in rank order (the heaviest first) and the XCDs' totals
+// stay close.  All ngrp groups of one expert run together on one XCD.  Otherwise the experts go in
+// id order, XCD-major.  Returns false for padding workgroups.
 __device__ inline bool chunk_work(const int32_t* __restrict__ order, int E, int ngrp, int& e, int& grp) {
   if ((E & 7) == 0) {
     const int li = (int)(blockIdx.x >> 3);
     if (li >= (E >> 3) * ngrp) return false;
+    const int g = li / ngrp, x = (int)(blockIdx.x & 7);
     grp = li % ngrp;
-    e = order[(li / ngrp) * 8 + (int)(blockIdx.x & 7)];
+    e = order[g * 8 + ((g & 1) ? 7 - x : x)];
     return true;
   }
   const int w = xcd_major(E * ngrp);
