@@ -266,9 +266,10 @@ def test_chunk_workspace_and_validation(L):
     n = L.rvq_moe_layer_workspace_bytes(_bank(), T, k, 1)
     P = T * k
     up = lambda v: (v + 255) // 256 * 256
-    # status, expert offsets, pair token/position/h-scale, h (fp32), y rows (fp32), the tokens and h
-    # as the tiles' 16-bit operands
-    assert n == 256 + up((E + 1) * 4) + 3 * up(P * 4) + up(P * I * 4) + up(P * H * 4) + up(T * H * 2) + up(P * I * 2)
+    # status, expert offsets, the expert order, pair token/position/h-scale, h (fp32), y rows (fp32),
+    # the tokens and h as the tiles' 16-bit operands
+    assert n == (256 + up((E + 1) * 4) + up(E * 4) + 3 * up(P * 4) + up(P * I * 4) + up(P * H * 4) + up(T * H * 2)
+                 + up(P * I * 2))
     assert L.rvq_moe_layer_workspace_bytes(_bank(), T, k, 2) == n
     assert L.rvq_moe_layer_workspace_bytes(_bank(), T, k, 0) == 0          # fp32 tiles: no
     assert L.rvq_moe_layer_workspace_bytes(_bank(), 5000, k, 1) == 0       # too many tokens
