@@ -86,6 +86,15 @@ def test_chunk_odd_row_block_count(dtype, H, I):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_chunk_expert_count_not_a_multiple_of_8(dtype):
+    """12 experts: the expert kernels take the experts in id order, XCD-major (the deal by pair count
+    needs the experts to split evenly over the 8 XCDs), with the same results."""
+    say(f"chunk E=12 H=256 I=128 T=40 k=3 {dtype}")
+    err = run_case(0xC6, 12, 256, 128, 40, 3, dtype, residual=True)[0]
+    assert err <= TOL[dtype]
+
+
 def test_chunk_at_max_tokens():
     """The largest chunk accepted (4096 tokens; 8 experts, so about 1000 pairs per expert)."""
     say("chunk E=8 H=256 I=128 T=4096 k=2 f16")
