@@ -95,6 +95,15 @@ def test_chunk_expert_count_not_a_multiple_of_8(dtype):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_chunk_smallest(dtype):
+    """The smallest chunk (2 tokens, top-2 of 16 experts): at most 4 experts have a pair, the other
+    work items end at once, and each pass holds one or two pairs of a 16-pair block."""
+    say(f"chunk E=16 H=256 I=128 T=2 k=2 {dtype}")
+    err = run_case(0xC7, 16, 256, 128, 2, 2, dtype, residual=True)[0]
+    assert err <= TOL[dtype]
+
+
 def test_chunk_at_max_tokens():
     """The largest chunk accepted (4096 tokens; 8 experts, so about 1000 pairs per expert)."""
     say("chunk E=8 H=256 I=128 T=4096 k=2 f16")
