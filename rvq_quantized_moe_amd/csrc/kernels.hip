@@ -326,6 +326,43 @@ __device__ inline double bf16_to_f64(uint16_t b) { return (double)__uint_as_floa
 __device__ inline double x_to_f64(float v) { return (double)v; }
 __device__ inline double x_to_f64(uint16_t v) { return bf16_to_f64(v); }
 
+// Sum over the 64 lanes of a wave (every lane active), equal at every lane, bit for bit, to
+//   for (off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64)
+// without lane permutes through the LDS unit.  The xor-32 and xor-16 partners come from the permlane
+// swaps (each half of the double swapped with itself); after those two steps a lane's value depends
+// only on its place in its row of 16 lanes, so rotating the row by 8, 4, 2 and 1 lanes (DPP) reads
+// a lane holding exactly the value of the xor-8, -4, -2 and -1 partner.  a + b equals b + a, so
+// every lane adds the same two values as in the shuffle form, step by step.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  const unsigned lane = __lane_id();
+  {
+    const unsigned lo = (unsigned)__double2loint(v), hi = (unsigned)__double2hiint(v);
+    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const bool up = lane & 32u;   // its partner's value: first result on lanes 32..63, second below
+    v += __hiloint2double((int)(up ? b[0] : b[1]), (int)(up ? a[0] : a[1]));
+  }
+  {
+    const unsigned lo = (unsigned)__double2loint(v), hi = (unsigned)__double2hiint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const bool odd = lane & 16u;   // first result on the odd rows, second on the even ones
+    v += __hiloint2double((int)(odd ? b[0] : b[1]), (int)(odd ? a[0] : a[1]));
+  }
+#define RVQ_ROW_ROR_ADD(n)                                                                              \
+  {                                                                                                     \
+    const int lo = __double2loint(v), hi = __double2hiint(v);                                           \
+    v += __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, 0x120 + (n), 0xF, 0xF, false),            \
+                          __builtin_amdgcn_update_dpp(0, lo, 0x120 + (n), 0xF, 0xF, false));           \
+  }
+  RVQ_ROW_ROR_ADD(8)
+  RVQ_ROW_ROR_ADD(4)
+  RVQ_ROW_ROR_ADD(2)
+  RVQ_ROW_ROR_ADD(1)
+#undef RVQ_ROW_ROR_ADD
+  return v;
+}
+
 // Eight x values as loaded (16 or 32 bytes), widened to fp64 only when used, so that a thread can
 // have all of its loads in flight before the first product.
 template <typename XT>
@@ -413,8 +450,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   const uint16_t* wr = w + (int64_t)e * H;
   const XT* xr = x + (int64_t)t * H;
   double acc = router_dot(wr, xr, H, vec, [](double v) { return v; });
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  acc = wave_sum_f64(acc);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
   if (threadIdx.x == 0) logits[(int64_t)t * E + e] = (red[0] + red[1]) + (red[2] + red[3]);
@@ -642,8 +678,7 @@ __device__ void topk_gates(const double* L, const int* sel, int k, int32_t* ids,
   const double m = L[sel[0]];
   const double ex = i < k ? exp(L[sel[i]] - m) : 0.0;
   double z = ex;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+  z = wave_sum_f64(z);
   if (i < k && want(i)) {
     ids[i] = sel[i];
     gates[i] = (float)(ex / z);
@@ -706,8 +741,7 @@ __global__ __launch_bounds__(256) void k_router_norm_logits(const uint16_t* __re
 #pragma unroll
     for (int u = 0; u < SU; ++u)
       if (tid + 256 * u < H) ss = fma((double)v[u], (double)v[u], ss);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    ss = wave_sum_f64(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     const double tot = (red[0] + red[1]) + (red[2] + red[3]);
@@ -724,8 +758,7 @@ __global__ __launch_bounds__(256) void k_router_norm_logits(const uint16_t* __re
       }
     }
     double acc = a0 + a1;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    acc = wave_sum_f64(acc);
     if ((tid & 63) == 0) red2[tid >> 6] = acc;
     __syncthreads();
     if (tid == 0) logits[e] = (red2[0] + red2[1]) + (red2[2] + red2[3]);
@@ -733,16 +766,14 @@ __global__ __launch_bounds__(256) void k_router_norm_logits(const uint16_t* __re
     return;
   }
   double ss = sum_squares(h, H);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  ss = wave_sum_f64(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const double tot = (red[0] + red[1]) + (red[2] + red[3]);
   const double inv = 1.0 / sqrt(tot / (double)H + (double)eps);
   const uint16_t* wr = w + (int64_t)e * H;
   double acc = router_dot(wr, h, H, vec, [inv](double v) { return (double)(float)(v * inv); });
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  acc = wave_sum_f64(acc);
   if ((threadIdx.x & 63) == 0) red2[threadIdx.x >> 6] = acc;
   __syncthreads();
   if (threadIdx.x == 0) logits[e] = (red2[0] + red2[1]) + (red2[2] + red2[3]);
@@ -817,8 +848,7 @@ __global__ __launch_bounds__(256) void k_router_logits_tiles(const uint16_t* __r
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       double acc = a0[i][t] + a1[i][t];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      acc = wave_sum_f64(acc);
       if ((threadIdx.x & 63) == 0) red[i * TT + t][threadIdx.x >> 6] = acc;
     }
   __syncthreads();
@@ -869,8 +899,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* x, int H, float ep
   const int64_t t = blockIdx.x;
   const float* xr = x + t * H;
   double ss = sum_squares(xr, H);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  ss = wave_sum_f64(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const double tot = (red[0] + red[1]) + (red[2] + red[3]);
